@@ -1,0 +1,10 @@
+"""Float64 CPU oracle for relative-position-bias attention (test infrastructure only).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg use this
+package; the product path never imports it.
+"""
+from .relbias_oracle import (MODE_NONE, MODE_TABLE, MODE_RPROJ, attention, bias_matrix,
+                             decode, prefill, visible_mask)
+
+__all__ = ["MODE_NONE", "MODE_TABLE", "MODE_RPROJ", "attention", "bias_matrix", "decode",
+           "prefill", "visible_mask"]

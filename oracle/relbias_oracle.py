@@ -1,0 +1,209 @@
+"""Reference oracle for causal attention with a learned relative-position bias.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+CPU-baseline leg of the benchmark may import this module.  The product path
+(the HIP library and its Python binding) never calls it, and it shares no
+code with that path.
+
+What it computes (plain definition, float64, no tiling, no online softmax):
+
+  For batch b, query head h (kv head g = floor(h / G)), query row i, key j:
+    delta_ij = qpos[i] - kpos[j]
+    visible_ij  <=>  delta_ij >= 0  and  (window == 0  or  delta_ij < window)
+    beta(h, i, delta) = 0                          if mode == NONE or delta >= bias_range
+                      = table[h, delta]            if mode == TABLE
+                      = sum_f r[b,i,h,f] E[h,f,delta]   if mode == RPROJ
+    s_ij = scale * <q[b,i,h,:], k[b,j,g,:]> + beta(h, i, delta_ij)
+    o[b,i,h,:] = sum_{visible j} softmax_j(s_ij) v[b,j,g,:]
+    lse[b,h,i] = log sum_{visible j} exp(s_ij)
+
+Sources (pages on learned relative-position bias attention):
+  * "Learned Relative-Position Bias" (codewithdark concepts page), section
+    "Standard Relative Bias (T5-style)": scores are q.k / sqrt(d) plus a bias
+    that depends on the distance i-j; section "Inkling's Input-Dependent
+    Version (Conceptual)": local layers use the bias below a 512 distance,
+    global layers below 1024 and a zero bias (content-only, NoPE) beyond.
+  * "Thinking Machines dropped RoPE" (wpnews essay), the five numbered steps
+    of the Inkling bias: per-token, per-head coefficients (step 1) weight a
+    bank of learned distance functions (step 2); the curve is read at the
+    query-key distance (step 3), forced to zero outside the hard-coded range
+    and for keys ahead of the query (step 4), and added to the score before
+    the softmax next to the causal mask (step 5).  The code listing on that
+    page reads the curve of the *query* row at distance i-j and zeroes
+    distances < 0 and >= the range.
+  * Same essay, section "Option 3: position as a bias to the attention": the
+    T5 form is a learned table indexed by distance, shared by all tokens.
+
+Readings where the pages are silent or garbled (each is pinned by a test):
+  * the bias is added after the content scale, not multiplied by it;
+  * the window keeps keys with 0 <= delta < window (window keys including the
+    query itself); window == 0 means no window (full causal);
+  * the bias applies for 0 <= delta < bias_range and is exactly 0 at
+    delta == bias_range;
+  * the table is causal only (no negative-offset half, no buckets);
+  * the bank E is per head ([Hq, R, bias_range]); the page's head-shared bank
+    is the special case E[h] == E for every h;
+  * GQA: query head h reads kv head floor(h / G), G = Hq / Hkv.
+
+Inputs are taken as stored (bf16 / fp32 values upcast to float64).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+MODE_NONE = 0
+MODE_TABLE = 1
+MODE_RPROJ = 2
+
+_MODES = {"none": MODE_NONE, "table": MODE_TABLE, "rproj": MODE_RPROJ,
+          MODE_NONE: MODE_NONE, MODE_TABLE: MODE_TABLE, MODE_RPROJ: MODE_RPROJ}
+
+
+def _f64(x):
+    """Upcast a numpy array or a torch tensor (any dtype, any device) to float64 numpy."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: bf16 has no numpy dtype, go through float64
+        import torch  # local import: the oracle itself only needs numpy
+        return x.detach().to(device="cpu", dtype=torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def visible_mask(qpos, kpos, window):
+    """Boolean [Sq, Sk]: key j visible to query i (causal, optional sliding window).
+
+    Causal: keys ahead of the query are masked ("Thinking Machines dropped RoPE",
+    step 4 and step 5).  Window: "Learned Relative-Position Bias", section
+    "Hybrid Attention Interaction" (local layers use a 512 window); read here
+    as 0 <= delta < window.
+    """
+    qpos = np.asarray(qpos, dtype=np.int64)
+    kpos = np.asarray(kpos, dtype=np.int64)
+    delta = qpos[:, None] - kpos[None, :]
+    vis = delta >= 0
+    if window:
+        vis &= delta < window
+    return vis
+
+
+def bias_matrix(mode, qpos, kpos, bias_range, h, *, table=None, r_rows=None, E=None):
+    """Bias beta[i, j] for query head h, float64 [Sq, Sk].
+
+    mode TABLE: table[h, delta] (T5 style; "Learned Relative-Position Bias",
+    section "Standard Relative Bias (T5-style)", causal half only).
+    mode RPROJ: sum_f r_rows[i, f] * E[h, f, delta], i.e. the query token's
+    curve read at the distance ("Thinking Machines dropped RoPE", steps 2-3 and
+    the code listing).  r_rows is r[b, :, h, :] for the query rows, [Sq, R].
+    Both: zero for delta < 0 and delta >= bias_range (same essay, step 4).
+    """
+    mode = _MODES[mode]
+    qpos = np.asarray(qpos, dtype=np.int64)
+    kpos = np.asarray(kpos, dtype=np.int64)
+    delta = qpos[:, None] - kpos[None, :]
+    out = np.zeros(delta.shape, dtype=np.float64)
+    if mode == MODE_NONE:
+        return out
+    inband = (delta >= 0) & (delta < bias_range)
+    idx = np.clip(delta, 0, bias_range - 1)
+    if mode == MODE_TABLE:
+        row = _f64(table)[h]                       # [bias_range]
+        vals = row[idx]
+    else:
+        curves = _f64(r_rows) @ _f64(E)[h]         # [Sq, R] @ [R, bias_range] -> [Sq, bias_range]
+        vals = np.take_along_axis(curves, idx, axis=1)
+    out[inband] = vals[inband]
+    return out
+
+
+def attention(q, k, v, *, qpos, kpos, scale, window=0, bias_range=0, mode="none",
+              table=None, r=None, E=None, rows=None, row_block=512):
+    """Plain definition of relative-position-bias attention, float64.
+
+    q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D]; r [B, Sq, Hq, R] (RPROJ);
+    table [Hq, bias_range] (TABLE); E [Hq, R, bias_range] (RPROJ).
+    qpos [Sq], kpos [Sk]: integer token positions.
+    rows: optional 1-D array of query-row indices to evaluate (others skipped).
+    Returns (o [B, len(rows), Hq, D], lse [B, Hq, len(rows)]) in float64.
+
+    Formula: "Learned Relative-Position Bias", section "Standard Relative Bias
+    (T5-style)" (score = scaled content term + distance bias), with the bias of
+    "Thinking Machines dropped RoPE", steps 1-5.  The softmax is the ordinary
+    max-subtracted one over the visible keys of each row.
+    """
+    mode = _MODES[mode]
+    q64, k64, v64 = _f64(q), _f64(k), _f64(v)
+    B, Sq, Hq, D = q64.shape
+    Hkv = k64.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    qpos = np.asarray(qpos, dtype=np.int64)
+    kpos = np.asarray(kpos, dtype=np.int64)
+    rows = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    r64 = _f64(r) if mode == MODE_RPROJ else None
+    tab64 = _f64(table) if mode == MODE_TABLE else None
+    E64 = _f64(E) if mode == MODE_RPROJ else None
+    n = len(rows)
+    o = np.zeros((B, n, Hq, D), dtype=np.float64)
+    lse = np.zeros((B, Hq, n), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            kk = k64[b, :, g, :]                   # [Sk, D]
+            vv = v64[b, :, g, :]
+            # keep one row block's [rows, keys] arrays near 8M elements
+            step = max(1, min(row_block, (8 << 20) // max(1, kk.shape[0])))
+            for s0 in range(0, n, step):
+                rr = rows[s0:s0 + step]
+                qq = q64[b, rr, h, :]              # [n_r, D]
+                logits = scale * (qq @ kk.T)       # [n_r, Sk]
+                beta = bias_matrix(mode, qpos[rr], kpos, bias_range, h, table=tab64,
+                                   r_rows=None if r64 is None else r64[b, rr, h, :], E=E64)
+                logits = logits + beta
+                vis = visible_mask(qpos[rr], kpos, window)
+                logits = np.where(vis, logits, -np.inf)
+                m = logits.max(axis=1, keepdims=True)
+                if not np.all(np.isfinite(m)):
+                    raise ValueError("a query row sees no key")
+                p = np.exp(logits - m)
+                l = p.sum(axis=1, keepdims=True)
+                o[b, s0:s0 + len(rr), h, :] = (p @ vv) / l
+                lse[b, h, s0:s0 + len(rr)] = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def prefill(q, k, v, *, scale, window=0, bias_range=0, mode="none", table=None, r=None,
+            E=None, rows=None, row_block=512):
+    """Prefill: query i and key j sit at positions i and j (one sequence per batch row)."""
+    S = q.shape[1]
+    pos = np.arange(S, dtype=np.int64)
+    return attention(q, k, v, qpos=pos, kpos=pos, scale=scale, window=window,
+                     bias_range=bias_range, mode=mode, table=table, r=r, E=E, rows=rows,
+                     row_block=row_block)
+
+
+def decode(q, k_cache, v_cache, kv_len, *, scale, window=0, bias_range=0, mode="none",
+           table=None, r=None, E=None, batch=None):
+    """Single-token decode against a KV cache.
+
+    q [B, Hq, D] is the newest token, at position kv_len - 1; the cache already
+    holds that token's own key/value at index kv_len - 1 (rows >= kv_len are
+    ignored).  r [B, Hq, R] is that token's coefficients.  batch: optional list
+    of batch indices to evaluate.  Returns (o [nb, Hq, D], lse [nb, Hq]).
+    """
+    bidx = range(q.shape[0]) if batch is None else list(batch)
+    qpos = np.array([kv_len - 1], dtype=np.int64)
+    kpos = np.arange(kv_len, dtype=np.int64)
+    outs, lses = [], []
+    for b in bidx:
+        qb = q[b:b + 1][:, None]                    # [1, 1, Hq, D]
+        kb = k_cache[b:b + 1, :kv_len]
+        vb = v_cache[b:b + 1, :kv_len]
+        rb = None if r is None else r[b:b + 1][:, None]
+        o, l = attention(qb, kb, vb, qpos=qpos, kpos=kpos, scale=scale, window=window,
+                         bias_range=bias_range, mode=mode, table=table, r=rb, E=E)
+        outs.append(o[0, 0])
+        lses.append(l[0, :, 0])
+    return np.stack(outs), np.stack(lses)
+
