@@ -1,0 +1,124 @@
+/*
+ * relbias_attn.h - C ABI of the relative-position-bias attention library (MI355X, gfx950).
+ *
+ * The operation (both entry points): causal softmax attention whose logits
+ * carry an additive bias that depends on the query-key distance
+ *     delta = pos(query) - pos(key),
+ *     s = scale * <q, k> + beta(h, query, delta),   o = softmax(s) @ v,
+ * with keys visible iff 0 <= delta and (window == 0 or delta < window), and
+ * beta = 0 for delta >= bias_range ("Learned Relative-Position Bias",
+ * section "Standard Relative Bias (T5-style)" for the scaled content term plus
+ * a distance bias, section "Inkling's Input-Dependent Version (Conceptual)"
+ * for the 512 / 1024 ranges and the content-only tail; "Thinking Machines
+ * dropped RoPE", steps 1-5, for the input-dependent bias and the hard zero
+ * outside the range).  The bias is added after `scale`, it is not scaled.
+ *
+ * Bias modes:
+ *   RBA_BIAS_NONE   beta = 0 (content only).
+ *   RBA_BIAS_TABLE  beta = table[h, delta]: a learned per-head table indexed by
+ *                   distance, T5 style ("Thinking Machines dropped RoPE",
+ *                   section "Option 3: position as a bias to the attention").
+ *   RBA_BIAS_RPROJ  beta = sum_{f<R} r[token, h, f] * E[h, f, delta]: the query
+ *                   token's coefficients (output of the fourth projection,
+ *                   "Inkling 975B MoE architecture deep dive", section "No RoPE?
+ *                   No Problem?") weighting a bank of R learned distance curves
+ *                   ("Thinking Machines dropped RoPE", steps 1-3).  A bank shared
+ *                   by all heads is the case E[h] == E for every h.
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates nothing, keeps no state other than a thread-local error
+ *     message, and may be called from several threads.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
+ *     default stream) and is asynchronous: outputs are valid once the stream
+ *     has reached the call.  Nothing synchronises.
+ *   - Tensors are dense and row-major with the last index innermost, as in
+ *     the shapes below.  q, k, v, o (and the caches) must be 16-byte aligned.
+ *   - GQA: query head h reads kv head h / (Hq / Hkv); Hq must be a multiple
+ *     of Hkv.
+ *   - Return value: RBA_OK, or an error code with nothing launched
+ *     (RBA_EINVAL: invalid argument; RBA_ENOTSUP: valid but outside the
+ *     supported set).  RBA_EHIP reports a HIP error seen at launch time.
+ *     relbias_attn_last_error() gives the message of the calling thread's
+ *     last non-OK status.
+ *   - Supported set: dtype RBA_BF16 with D in {64, 128}; dtype RBA_F32 with
+ *     D in {32, 64, 128}; 1 <= R <= 16; bias_range <= 1048576.
+ *   - Empty problems (B == 0 or S == 0) return RBA_OK and launch nothing.
+ */
+#ifndef RELBIAS_ATTN_H
+#define RELBIAS_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { RBA_OK = 0, RBA_EINVAL = 1, RBA_ENOTSUP = 2, RBA_EHIP = 3 } rba_status_t;
+typedef enum { RBA_F32 = 0, RBA_BF16 = 1 } rba_dtype_t;
+typedef enum { RBA_BIAS_NONE = 0, RBA_BIAS_TABLE = 1, RBA_BIAS_RPROJ = 2 } rba_bias_mode_t;
+
+/*
+ * Prefill: every token of B sequences of length S attends to its own
+ * sequence; query i and key j sit at positions i and j.
+ *
+ *   dtype       RBA_BF16 or RBA_F32: element type of q, k, v, o and r.
+ *   q           [B, S, Hq, D]
+ *   k, v        [B, S, Hkv, D]
+ *   o           [B, S, Hq, D]  (written)
+ *   lse         [B, Hq, S] fp32 natural-log sum-exp of each row (written), or NULL.
+ *   window      0 = full causal; else key j is visible to query i iff 0 <= i-j < window.
+ *   bias_range  bias applied iff 0 <= i-j < bias_range (ignored for RBA_BIAS_NONE).
+ *   mode        rba_bias_mode_t.
+ *   table       RBA_BIAS_TABLE: [Hq, bias_range] fp32; else ignored (may be NULL).
+ *   r           RBA_BIAS_RPROJ: [B, S, Hq, R] of dtype; else ignored.
+ *   E           RBA_BIAS_RPROJ: [Hq, R, bias_range] fp32; else ignored.
+ *   R           RBA_BIAS_RPROJ: number of curves, 1..16.
+ *   scale       multiplier of q.k (typically 1/sqrt(D)); the bias is not scaled.
+ *   stream      hipStream_t.
+ */
+int relbias_attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int S, int Hq, int Hkv, int D, int window, int bias_range, int mode,
+                     const float* table, const void* r, const float* E, int R, float scale,
+                     void* stream);
+
+/*
+ * Bytes of device workspace relbias_attn_decode needs for these sizes
+ * (0 when a single pass writes the output directly).  Pure host function.
+ */
+size_t relbias_attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int kv_len, int window);
+
+/*
+ * Single-token decode against a contiguous KV cache (one new query per sequence).
+ * The cache already holds the new token's own key/value at row kv_len-1; the
+ * query sits at position kv_len-1 and key row j at position j (rows >= kv_len
+ * are not read).  Attention, window and bias are as in relbias_attn_fwd.
+ *
+ *   q           [B, Hq, D]
+ *   k_cache     [B, L_max, Hkv, D]; v_cache the same.  1 <= kv_len <= L_max.
+ *   o           [B, Hq, D] (written); lse [B, Hq] fp32 or NULL.
+ *   r           RBA_BIAS_RPROJ: [B, Hq, R] of dtype (coefficients of the new token).
+ *   table, E, R, scale: as in relbias_attn_fwd.
+ *   workspace   device scratch of at least relbias_attn_decode_workspace_size(...)
+ *               bytes (may be NULL when that size is 0); contents on entry are
+ *               ignored.  Calls that share one workspace must be ordered on one stream.
+ *   Supported: dtype RBA_BF16 with D in {64, 128}, and dtype RBA_F32 with D in {32, 64, 128}.
+ */
+int relbias_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                        void* o, float* lse, int B, int L_max, int kv_len, int Hq, int Hkv, int D,
+                        int window, int bias_range, int mode, const float* table, const void* r,
+                        const float* E, int R, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Message for the calling thread's last non-OK status ("" if none).  The pointer
+ * stays valid until the next call on the same thread. */
+const char* relbias_attn_last_error(void);
+
+/* Library version string, e.g. "relbias_attn 0.1 gfx950". */
+const char* relbias_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RELBIAS_ATTN_H */

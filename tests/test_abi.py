@@ -1,0 +1,128 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects invalid arguments in host code before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_attention_learned_amd as rba
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "relbias_attn.h")
+
+EINVAL, ENOTSUP = rba.RBA_EINVAL, rba.RBA_ENOTSUP
+BF16, F32 = 1, 0
+P = 4096  # a 16-byte aligned dummy address; never dereferenced (validation fails first)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rba.library_path()):
+        from transformer_attention_learned_amd.build import build_library
+        build_library()
+    return rba.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(relbias_attn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == {"relbias_attn_fwd", "relbias_attn_decode",
+                          "relbias_attn_decode_workspace_size", "relbias_attn_last_error",
+                          "relbias_attn_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert "gfx950" in rba.version()
+
+
+def _fwd(lib, **kw):
+    a = dict(dtype=BF16, q=P, k=P, v=P, o=P, lse=None, B=1, S=16, Hq=4, Hkv=2, D=128, window=0,
+             bias_range=8, mode=0, table=None, r=None, E=None, R=0, scale=0.1, stream=None)
+    a.update(kw)
+    return lib.relbias_attn_fwd(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
+                                a["S"], a["Hq"], a["Hkv"], a["D"], a["window"], a["bias_range"],
+                                a["mode"], a["table"], a["r"], a["E"], a["R"], a["scale"],
+                                a["stream"])
+
+
+def _dec(lib, **kw):
+    a = dict(dtype=BF16, q=P, k=P, v=P, o=P, lse=None, B=2, L=100, kv_len=50, Hq=8, Hkv=2, D=128,
+             window=0, bias_range=8, mode=0, table=None, r=None, E=None, R=0, scale=0.1, ws=None,
+             wsb=0, stream=None)
+    a.update(kw)
+    return lib.relbias_attn_decode(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
+                                   a["L"], a["kv_len"], a["Hq"], a["Hkv"], a["D"], a["window"],
+                                   a["bias_range"], a["mode"], a["table"], a["r"], a["E"], a["R"],
+                                   a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(dtype=7), EINVAL, "dtype"),
+    (dict(Hq=6, Hkv=4), EINVAL, "multiple"),
+    (dict(Hkv=0), EINVAL, "Hkv"),
+    (dict(window=-1), EINVAL, "window"),
+    (dict(mode=5), EINVAL, "mode"),
+    (dict(D=96), ENOTSUP, "head_dim"),
+    (dict(dtype=F32, D=48), ENOTSUP, "head_dim"),
+    (dict(mode=1, table=None), EINVAL, "table"),
+    (dict(mode=1, table=P, bias_range=0), EINVAL, "bias_range"),
+    (dict(mode=2, r=P, E=P, R=17), ENOTSUP, "R="),
+    (dict(mode=2, r=P, E=P, R=0), ENOTSUP, "R="),
+    (dict(mode=2, r=None, E=P, R=8), EINVAL, "r and E"),
+    (dict(mode=2, r=P, E=P + 2, R=8), EINVAL, "E is not"),
+    (dict(q=None), EINVAL, "non-NULL"),
+    (dict(o=P + 8), EINVAL, "aligned"),
+    (dict(B=-1), EINVAL, "B="),
+    (dict(scale=float("nan")), EINVAL, "scale"),
+    (dict(mode=1, table=P, bias_range=(1 << 20) + 1), ENOTSUP, "bias_range"),
+])
+def test_fwd_rejects(lib, kw, code, needle):
+    assert _fwd(lib, **kw) == code
+    assert needle in rba.last_error()
+
+
+def test_fwd_empty_is_a_noop(lib):
+    assert _fwd(lib, B=0) == 0
+    assert _fwd(lib, S=0, q=None, k=None, v=None, o=None) == 0
+    assert rba.last_error() == ""
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(kv_len=0), EINVAL, "kv_len"),
+    (dict(kv_len=101), EINVAL, "kv_len"),
+    (dict(Hq=66, Hkv=1), ENOTSUP, "Hq/Hkv"),
+    (dict(k=None), EINVAL, "non-NULL"),
+    (dict(v=P + 4), EINVAL, "aligned"),
+    (dict(D=32), ENOTSUP, "head_dim"),
+    (dict(mode=2, r=P, E=P, R=0), ENOTSUP, "R="),
+])
+def test_decode_rejects(lib, kw, code, needle):
+    assert _dec(lib, **kw) == code
+    assert needle in rba.last_error()
+
+
+def test_decode_workspace_policy(lib):
+    # long caches are split and need a workspace; short (or windowed) ones do not
+    n = rba.decode_workspace_size(64, 32, 8, 128, 65536, 0)
+    assert n > 0 and n % (32 * 64 * (128 + 2) * 4) == 0
+    assert rba.decode_workspace_size(64, 32, 8, 128, 65536, 512) == 0
+    assert rba.decode_workspace_size(1, 1, 1, 64, 10, 0) == 0
+    # a split decode without (enough) workspace is rejected before any launch
+    st = _dec(lib, B=64, Hq=32, Hkv=8, L=65536, kv_len=65536)
+    assert st == EINVAL and "workspace" in rba.last_error()
+    st = _dec(lib, B=64, Hq=32, Hkv=8, L=65536, kv_len=65536, ws=P, wsb=n - 4)
+    assert st == EINVAL and "too small" in rba.last_error()
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    """The binding never falls back to another implementation when the library is absent."""
+    monkeypatch.setattr(rba, "_LIB", None)
+    monkeypatch.setattr(rba, "library_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        rba.load_library()

@@ -1,0 +1,214 @@
+"""Relative-position-bias attention on MI355X (gfx950): Python binding of librelbias_attn.so.
+
+The binding only marshals arguments (shapes, dtypes, device pointers, the
+current HIP stream) into the C ABI declared in include/relbias_attn.h; every
+step of the computation runs in the library's HIP kernels.  PyTorch supplies
+device memory and streams.  If the library is not built, every call raises.
+
+  fwd(q, k, v, ...)                      prefill, q [B,S,Hq,D], k/v [B,S,Hkv,D]
+  decode(q, k_cache, v_cache, kv_len, ...)  one new token per sequence
+  decode_workspace_size(...)             scratch bytes decode needs
+
+Bias modes: "none", "table" (table [Hq, bias_range] fp32) and "rproj"
+(r [.., Hq, R] in the activation dtype, E [Hq, R, bias_range] fp32).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["fwd", "decode", "decode_workspace_size", "last_error", "version", "library_path",
+           "load_library", "RBA_OK", "RBA_EINVAL", "RBA_ENOTSUP", "RBA_EHIP", "MODES",
+           "LibraryError"]
+
+RBA_OK, RBA_EINVAL, RBA_ENOTSUP, RBA_EHIP = 0, 1, 2, 3
+RBA_F32, RBA_BF16 = 0, 1
+MODES = {"none": 0, "table": 1, "rproj": 2}
+
+_LIB = None
+
+
+class LibraryError(RuntimeError):
+    """A non-OK status from the C ABI (the message is relbias_attn_last_error())."""
+
+    def __init__(self, status, message):
+        super().__init__(f"[status {status}] {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "librelbias_attn.so")
+
+
+def load_library():
+    """Load librelbias_attn.so (built in-tree); raise if it is missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built: run `python -m transformer_attention_learned_amd.build` "
+            "(hipcc, gfx950) first; there is no fallback implementation")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.relbias_attn_fwd.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp, i,
+                                     f, vp]
+    lib.relbias_attn_fwd.restype = i
+    lib.relbias_attn_decode.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp, vp,
+                                        vp, i, f, vp, sz, vp]
+    lib.relbias_attn_decode.restype = i
+    lib.relbias_attn_decode_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.relbias_attn_decode_workspace_size.restype = sz
+    lib.relbias_attn_last_error.argtypes = []
+    lib.relbias_attn_last_error.restype = ctypes.c_char_p
+    lib.relbias_attn_version.argtypes = []
+    lib.relbias_attn_version.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def last_error() -> str:
+    return load_library().relbias_attn_last_error().decode()
+
+
+def version() -> str:
+    return load_library().relbias_attn_version().decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_id(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return RBA_BF16
+    if t.dtype == torch.float32:
+        return RBA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+
+
+def _check(t, name, *, dtype=None, ndim=None, device=None):
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream_handle(device, stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _bias_args(mode, table, r, E, Hq, act_dtype, dev):
+    import torch
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    R = 0
+    if m == 1:
+        if table is None:
+            raise ValueError("mode 'table' needs table [Hq, bias_range]")
+        _check(table, "table", dtype=torch.float32, ndim=2, device=dev)
+    elif m == 2:
+        if r is None or E is None:
+            raise ValueError("mode 'rproj' needs r and E")
+        _check(E, "E", dtype=torch.float32, ndim=3, device=dev)
+        _check(r, "r", dtype=act_dtype, device=dev)
+        R = int(E.shape[1])
+        if r.shape[-1] != R or r.shape[-2] != Hq:
+            raise ValueError(f"r must end in [Hq={Hq}, R={R}], got {tuple(r.shape)}")
+    return m, R
+
+
+def fwd(q, k, v, *, window=0, bias_range=0, mode="none", table=None, r=None, E=None,
+        scale=None, out=None, lse=None, return_lse=False, stream=None):
+    """Prefill attention with a relative-position bias (relbias_attn_fwd).
+
+    q [B,S,Hq,D], k/v [B,S,Hkv,D] (bf16 or fp32, contiguous, on one GPU).
+    Returns o [B,S,Hq,D] (and lse [B,Hq,S] fp32 when return_lse or lse is given).
+    """
+    import torch
+    lib = load_library()
+    dev = q.device
+    _check(q, "q", ndim=4)
+    _check(k, "k", dtype=q.dtype, ndim=4, device=dev)
+    _check(v, "v", dtype=q.dtype, ndim=4, device=dev)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, S, Hkv, D) or tuple(v.shape) != (B, S, Hkv, D):
+        raise ValueError(f"k/v must be [B,S,Hkv,D] = {(B, S, Hkv, D)}")
+    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev)
+    if m == 2 and tuple(r.shape) != (B, S, Hq, R):
+        raise ValueError(f"r must be [B,S,Hq,R] = {(B, S, Hq, R)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", dtype=q.dtype, ndim=4, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    _check(lse, "lse", dtype=torch.float32, device=dev)
+    st = lib.relbias_attn_fwd(_dtype_id(q), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                              B, S, Hq, Hkv, D, int(window), int(bias_range), m,
+                              _ptr(table if m == 1 else None), _ptr(r if m == 2 else None),
+                              _ptr(E if m == 2 else None), R, float(scale),
+                              _stream_handle(dev, stream))
+    if st != RBA_OK:
+        raise LibraryError(st, last_error())
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_workspace_size(B, Hq, Hkv, D, kv_len, window=0) -> int:
+    return int(load_library().relbias_attn_decode_workspace_size(B, Hq, Hkv, D, kv_len, window))
+
+
+def decode(q, k_cache, v_cache, kv_len, *, window=0, bias_range=0, mode="none", table=None,
+           r=None, E=None, scale=None, out=None, lse=None, workspace=None, return_lse=False,
+           stream=None):
+    """One decode step (relbias_attn_decode): q [B,Hq,D] at position kv_len-1.
+
+    k_cache/v_cache [B,L_max,Hkv,D]; rows [0, kv_len) are valid and row kv_len-1
+    holds the new token.  workspace: optional uint8 device buffer (allocated
+    here when needed and not given).
+    """
+    import torch
+    lib = load_library()
+    dev = q.device
+    _check(q, "q", ndim=3)
+    _check(k_cache, "k_cache", dtype=q.dtype, ndim=4, device=dev)
+    _check(v_cache, "v_cache", dtype=q.dtype, ndim=4, device=dev)
+    B, Hq, D = q.shape
+    L_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, L_max, Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache/v_cache must be [B,L_max,Hkv,D] matching q")
+    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev)
+    if m == 2 and tuple(r.shape) != (B, Hq, R):
+        raise ValueError(f"r must be [B,Hq,R] = {(B, Hq, R)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = lib.relbias_attn_decode_workspace_size(B, Hq, Hkv, D, int(kv_len), int(window))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.relbias_attn_decode(_dtype_id(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                 _ptr(lse), B, L_max, int(kv_len), Hq, Hkv, D, int(window),
+                                 int(bias_range), m, _ptr(table if m == 1 else None),
+                                 _ptr(r if m == 2 else None), _ptr(E if m == 2 else None), R,
+                                 float(scale), _ptr(workspace), wbytes,
+                                 _stream_handle(dev, stream))
+    if st != RBA_OK:
+        raise LibraryError(st, last_error())
+    return (out, lse) if (return_lse or lse is not None) else out

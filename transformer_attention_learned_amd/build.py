@@ -1,0 +1,75 @@
+"""Build the HIP library librelbias_attn.so for gfx950 (in-tree, with hipcc).
+
+Usage: python -m transformer_attention_learned_amd.build   (or build_library()).
+Compiles every source under csrc/ with hipcc --offload-arch=gfx950 and links
+one shared library next to this file.  A GPU is not needed to build.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "librelbias_attn.so")
+
+SOURCES = ["api.cpp", "fwd_bf16.hip", "attn_f32.hip", "decode_bf16.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def _flags():
+    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
+            # no packed-fp32 VALU instructions in device code
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
+
+
+def _compile(src: str, verbose: bool) -> str:
+    out = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", out] + _flags()
+    if src.endswith(".cpp"):
+        cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", out] + _flags()
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                     if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{msgs}")
+    if verbose and msgs.strip():
+        print(msgs, flush=True)
+    return out
+
+
+def build_library(verbose: bool = False) -> str:
+    """Compile all sources and link librelbias_attn.so; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build_library(verbose="-v" in sys.argv))

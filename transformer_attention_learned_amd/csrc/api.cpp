@@ -1,0 +1,248 @@
+// C ABI of the relative-position-bias attention library: argument validation
+// (pure host code, before any HIP call) and dispatch to the gfx950 kernels.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "relbias_attn.h"
+#include "rba_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return RBA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+constexpr int kMaxBiasRange = 1 << 20;
+
+// Checks shared by prefill and decode.  Returns RBA_OK or an error code.
+int check_common(const char* fn, int dtype, int Hq, int Hkv, int D, int window, int bias_range,
+                 int mode, const float* table, const void* r, const float* E, int R, float scale) {
+  if (dtype != RBA_F32 && dtype != RBA_BF16) return fail(RBA_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  if (Hq < 1 || Hkv < 1) return fail(RBA_EINVAL, "%s: Hq=%d and Hkv=%d must be >= 1", fn, Hq, Hkv);
+  if (Hq % Hkv) return fail(RBA_EINVAL, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+  if (window < 0) return fail(RBA_EINVAL, "%s: window=%d must be >= 0 (0 = full causal)", fn, window);
+  if (mode != RBA_BIAS_NONE && mode != RBA_BIAS_TABLE && mode != RBA_BIAS_RPROJ)
+    return fail(RBA_EINVAL, "%s: unknown bias mode %d", fn, mode);
+  if (!std::isfinite(scale)) return fail(RBA_EINVAL, "%s: scale is not finite", fn);
+  if (dtype == RBA_BF16 && D != 64 && D != 128)
+    return fail(RBA_ENOTSUP, "%s: bf16 supports head_dim 64 or 128, got %d", fn, D);
+  if (dtype == RBA_F32 && D != 32 && D != 64 && D != 128)
+    return fail(RBA_ENOTSUP, "%s: f32 supports head_dim 32, 64 or 128, got %d", fn, D);
+  if (mode != RBA_BIAS_NONE) {
+    if (bias_range < 1) return fail(RBA_EINVAL, "%s: bias_range=%d must be >= 1 with a bias", fn, bias_range);
+    if (bias_range > kMaxBiasRange)
+      return fail(RBA_ENOTSUP, "%s: bias_range=%d exceeds %d", fn, bias_range, kMaxBiasRange);
+  }
+  if (mode == RBA_BIAS_TABLE) {
+    if (!table) return fail(RBA_EINVAL, "%s: table mode needs a table pointer", fn);
+    if (!aligned_to(table, 4)) return fail(RBA_EINVAL, "%s: table is not 4-byte aligned", fn);
+  }
+  if (mode == RBA_BIAS_RPROJ) {
+    if (R < 1 || R > 16) return fail(RBA_ENOTSUP, "%s: R=%d outside 1..16", fn, R);
+    if (!r || !E) return fail(RBA_EINVAL, "%s: rproj mode needs r and E pointers", fn);
+    if (!aligned_to(E, 4)) return fail(RBA_EINVAL, "%s: E is not 4-byte aligned", fn);
+    if (!aligned_to(r, dtype == RBA_F32 ? 4 : 2)) return fail(RBA_EINVAL, "%s: r is misaligned", fn);
+  }
+  return RBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* relbias_attn_last_error(void) { return g_err.c_str(); }
+
+const char* relbias_attn_version(void) { return "relbias_attn 0.1 gfx950"; }
+
+int relbias_attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int S, int Hq, int Hkv, int D, int window, int bias_range, int mode,
+                     const float* table, const void* r, const float* E, int R, float scale,
+                     void* stream) {
+  const char* fn = "relbias_attn_fwd";
+  if (B < 0 || S < 0) return fail(RBA_EINVAL, "%s: B=%d and S=%d must be >= 0", fn, B, S);
+  int st = check_common(fn, dtype, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale);
+  if (st != RBA_OK) return st;
+  if (B == 0 || S == 0) return ok();
+  if (!q || !k || !v || !o) return fail(RBA_EINVAL, "%s: q, k, v and o must be non-NULL", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(RBA_EINVAL, "%s: q, k, v and o must be 16-byte aligned", fn);
+  if (lse && !aligned_to(lse, 4)) return fail(RBA_EINVAL, "%s: lse is not 4-byte aligned", fn);
+  const long long rows = static_cast<long long>(B) * S;
+  if (rows * Hq * D >= (1LL << 40)) return fail(RBA_ENOTSUP, "%s: problem too large", fn);
+  if (static_cast<long long>(S) * 1 > (1LL << 30)) return fail(RBA_ENOTSUP, "%s: S too large", fn);
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == RBA_BF16) {
+    const int G = Hq / Hkv;
+    const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
+    const long long rows_wg = 32LL * (4 / hpw);
+    const long long nblk = ((S + rows_wg - 1) / rows_wg) * (Hq / hpw) * static_cast<long long>(B);
+    if (nblk > 0x7fffffffLL) return fail(RBA_ENOTSUP, "%s: grid too large", fn);
+    rba::FwdArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.o = static_cast<uint16_t*>(o);
+    a.lse = lse;
+    a.table = table;
+    a.r = static_cast<const uint16_t*>(r);
+    a.E = E;
+    a.B = B;
+    a.S = S;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = G;
+    a.window = window;
+    a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
+    a.R = mode == RBA_BIAS_RPROJ ? R : 0;
+    a.c_qk = scale * rba::kLog2e;
+    e = rba::launch_fwd_bf16(a, D, mode, hs);
+  } else {
+    rba::F32Args a{};
+    a.q = static_cast<const float*>(q);
+    a.k = static_cast<const float*>(k);
+    a.v = static_cast<const float*>(v);
+    a.o = static_cast<float*>(o);
+    a.lse = lse;
+    a.table = table;
+    a.r = static_cast<const float*>(r);
+    a.E = E;
+    a.B = B;
+    a.Sq = S;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.D = D;
+    a.kv_rows = S;
+    a.Lk = S;
+    a.q_pos0 = 0;
+    a.window = window;
+    a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
+    a.mode = mode;
+    a.R = mode == RBA_BIAS_RPROJ ? R : 0;
+    a.scale = scale;
+    e = rba::launch_attn_f32(a, hs);
+  }
+  if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+size_t relbias_attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int kv_len, int window) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || kv_len <= 0 || window < 0) return 0;
+  int ns = 1, kpw = 0;
+  rba::decode_split(B, Hkv, kv_len, window, &ns, &kpw);
+  if (ns <= 1) return 0;
+  return static_cast<size_t>(B) * Hq * ns * (D + 2) * sizeof(float);
+}
+
+int relbias_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                        void* o, float* lse, int B, int L_max, int kv_len, int Hq, int Hkv, int D,
+                        int window, int bias_range, int mode, const float* table, const void* r,
+                        const float* E, int R, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const char* fn = "relbias_attn_decode";
+  if (B < 0) return fail(RBA_EINVAL, "%s: B=%d must be >= 0", fn, B);
+  int st = check_common(fn, dtype, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale);
+  if (st != RBA_OK) return st;
+  if (B == 0) return ok();
+  if (L_max < 1 || kv_len < 1 || kv_len > L_max)
+    return fail(RBA_EINVAL, "%s: need 1 <= kv_len (%d) <= L_max (%d)", fn, kv_len, L_max);
+  if (!q || !k_cache || !v_cache || !o)
+    return fail(RBA_EINVAL, "%s: q, k_cache, v_cache and o must be non-NULL", fn);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(RBA_EINVAL, "%s: q, caches and o must be 16-byte aligned", fn);
+  if (lse && !aligned_to(lse, 4)) return fail(RBA_EINVAL, "%s: lse is not 4-byte aligned", fn);
+  const int G = Hq / Hkv;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == RBA_BF16) {
+    if (G > 32) return fail(RBA_ENOTSUP, "%s: bf16 decode supports Hq/Hkv <= 32, got %d", fn, G);
+    int ns = 1, kpw = 64;
+    rba::decode_split(B, Hkv, kv_len, window, &ns, &kpw);
+    const size_t need = relbias_attn_decode_workspace_size(B, Hq, Hkv, D, kv_len, window);
+    if (need > 0) {
+      if (!workspace) return fail(RBA_EINVAL, "%s: workspace of %zu bytes required, got NULL", fn, need);
+      if (workspace_bytes < need)
+        return fail(RBA_EINVAL, "%s: workspace too small (%zu < %zu bytes)", fn, workspace_bytes, need);
+      if (!aligned_to(workspace, 4)) return fail(RBA_EINVAL, "%s: workspace is not 4-byte aligned", fn);
+    }
+    if (Hkv > 65535 || B > 65535) return fail(RBA_ENOTSUP, "%s: grid too large", fn);
+    rba::DecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k_cache);
+    a.v = static_cast<const uint16_t*>(v_cache);
+    a.o = static_cast<uint16_t*>(o);
+    a.lse = lse;
+    a.table = table;
+    a.r = static_cast<const uint16_t*>(r);
+    a.E = E;
+    a.ws = static_cast<float*>(workspace);
+    a.B = B;
+    a.L_max = L_max;
+    a.kv_len = kv_len;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = G;
+    a.window = window;
+    a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
+    a.R = mode == RBA_BIAS_RPROJ ? R : 0;
+    a.key_begin = window ? (kv_len > window ? kv_len - window : 0) : 0;
+    a.n_split = ns;
+    a.keys_per_wave = kpw;
+    a.c_qk = scale * rba::kLog2e;
+    e = rba::launch_decode_bf16(a, D, mode, hs);
+  } else {
+    rba::F32Args a{};
+    a.q = static_cast<const float*>(q);
+    a.k = static_cast<const float*>(k_cache);
+    a.v = static_cast<const float*>(v_cache);
+    a.o = static_cast<float*>(o);
+    a.lse = lse;
+    a.table = table;
+    a.r = static_cast<const float*>(r);
+    a.E = E;
+    a.B = B;
+    a.Sq = 1;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = G;
+    a.D = D;
+    a.kv_rows = L_max;
+    a.Lk = kv_len;
+    a.q_pos0 = kv_len - 1;
+    a.window = window;
+    a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
+    a.mode = mode;
+    a.R = mode == RBA_BIAS_RPROJ ? R : 0;
+    a.scale = scale;
+    e = rba::launch_attn_f32(a, hs);
+  }
+  if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,313 @@
+// Single-token decode with a relative-position bias, bf16 KV cache, gfx950.
+//
+// One new query per sequence at position kv_len - 1 attends to cache rows
+// [max(0, kv_len - window), kv_len).  Only the last bias_range rows carry a
+// bias; every older row is content-only (the NoPE tail of global layers,
+// "Learned Relative-Position Bias", section "Inkling's Input-Dependent Version
+// (Conceptual)"), so only the chunk holding those rows evaluates it.
+//
+// The step is bound by streaming K and V from HBM.  Grid = (split, kv head,
+// batch); each of the 4 waves of a workgroup streams its own contiguous run of
+// cache rows, 64 at a time:
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16, the K rows loaded straight from
+//     global memory into the A operand (16 bytes per lane, no LDS), the G query
+//     heads of the kv head as B-operand columns;
+//   * V is staged in a wave-private LDS tile, transposed, and O^T = V^T P^T
+//     runs on the same MFMA with P kept in registers;
+//   * the 4 waves merge (max / sum-exp) through LDS; with several splits the
+//     workgroup writes an unnormalised partial that a second kernel combines.
+
+#include "rba_device.h"
+#include "rba_internal.h"
+
+namespace rba {
+
+namespace {
+
+constexpr int TK = 64;
+
+__device__ __forceinline__ int vt_pos(int x) {
+  return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
+  constexpr int VST = TK + 8;
+  constexpr int NC = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int VT_ELEMS = D * VST;  // per wave (bf16)
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * VT_ELEMS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ln = lane & 31;
+  const int lh = lane >> 5;
+  const int split = blockIdx.x;
+  const int hkv = blockIdx.y;
+  const int b = blockIdx.z;
+  const int G = a.G;
+  const int h = hkv * G + ln;            // query head of this lane's column (valid if ln < G)
+  const bool col_live = ln < G;
+
+  const size_t kv_row = static_cast<size_t>(a.Hkv) * D;
+  const uint16_t* kbase = a.k + static_cast<size_t>(b) * a.L_max * kv_row + static_cast<size_t>(hkv) * D;
+  const uint16_t* vbase = a.v + static_cast<size_t>(b) * a.L_max * kv_row + static_cast<size_t>(hkv) * D;
+  const int qpos = a.kv_len - 1;
+
+  // This wave's rows.
+  const int w_beg = a.key_begin + (split * 4 + wave) * a.keys_per_wave;
+  const int w_end = min(a.kv_len, w_beg + a.keys_per_wave);
+
+  bf16x8 qf[NC];
+  {
+    const uint16_t* qp = a.q + (static_cast<size_t>(b) * a.Hq + (col_live ? h : 0)) * D + 8 * lh;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (col_live) v = ld16(qp + 16 * c);
+      qf[c] = as_bf16x8(v);
+    }
+  }
+  float rv[16];
+  if (MODE == 2) {
+    const uint16_t* rp = a.r + (static_cast<size_t>(b) * a.Hq + (col_live ? h : 0)) * a.R;
+#pragma unroll
+    for (int f = 0; f < 16; ++f) rv[f] = (col_live && f < a.R) ? bf16_to_f32(rp[f]) * kLog2e : 0.f;
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+
+  uint16_t* vt = smem + wave * VT_ELEMS;
+  const float NEG_INF = -INFINITY;
+
+  for (int tk0 = w_beg; tk0 < w_end; tk0 += TK) {
+    // V tile -> LDS (transposed), 4 keys x 8 dims per item.
+    __builtin_amdgcn_wave_barrier();
+    for (int item = lane; item < (TK / 4) * (D / 8); item += 64) {
+      const int kg = item & 15;
+      const int dg = item >> 4;
+      u32x4 rows[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int key = tk0 + 4 * kg + s;
+        rows[s] = u32x4{0u, 0u, 0u, 0u};
+        if (key < w_end) rows[s] = ld16(vbase + static_cast<size_t>(key) * kv_row + 8 * dg);
+      }
+      const int pos = vt_pos(4 * kg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1;
+        const int sh = (e & 1) * 16;
+        const uint32_t k0 = (rows[0][w] >> sh) & 0xffffu;
+        const uint32_t k1 = (rows[1][w] >> sh) & 0xffffu;
+        const uint32_t k2 = (rows[2][w] >> sh) & 0xffffu;
+        const uint32_t k3 = (rows[3][w] >> sh) & 0xffffu;
+        st8(vt + (8 * dg + e) * VST + pos, u32x2{k0 | (k1 << 16), k2 | (k3 << 16)});
+      }
+    }
+    // S^T = K Q^T, K straight from global memory.
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+      const int key = tk0 + 32 * kb + ln;
+      const uint16_t* kp = kbase + static_cast<size_t>(key) * kv_row + 8 * lh;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (key < w_end) v = ld16(kp + 16 * c);
+        sacc[kb] = mfma32(as_bf16x8(v), qf[c], sacc[kb]);
+      }
+    }
+    float mx = NEG_INF;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = tk0 + 32 * kb + 8 * (i >> 2) + 4 * lh + (i & 3);
+        const int d = qpos - key;
+        float s = sacc[kb][i] * a.c_qk;
+        if (MODE != 0 && d < a.bias_range && key < w_end && col_live) {
+          if (MODE == 1) {
+            s += a.table[static_cast<size_t>(h) * a.bias_range + d] * kLog2e;
+          } else {
+            const float* Eh = a.E + static_cast<size_t>(h) * a.R * a.bias_range + d;
+            float bsum = 0.f;
+#pragma unroll
+            for (int f = 0; f < 16; ++f)
+              if (f < a.R) bsum = fmaf(rv[f], Eh[static_cast<size_t>(f) * a.bias_range], bsum);
+            s += bsum;
+          }
+        }
+        if (key >= w_end) s = NEG_INF;
+        sacc[kb][i] = s;
+        mx = fmaxf(mx, s);
+      }
+    }
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float psum = 0.f;
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        uint32_t w[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float p0 = fast_exp2(sacc[kb][8 * kk + 2 * jj] - m_use);
+          const float p1 = fast_exp2(sacc[kb][8 * kk + 2 * jj + 1] - m_use);
+          psum += p0 + p1;
+          w[jj] = pack_bf16x2(p0, p1);
+        }
+        pf[kb][kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 vf = as_bf16x8(ld16(vt + (32 * db + ln) * VST + 32 * kb + 16 * kk + 8 * lh));
+          oacc[db] = mfma32(vf, pf[kb][kk], oacc[db]);
+        }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // ---- merge the 4 waves through LDS (reusing the V^T area) ---------------------------
+  const float l_tot = l_run + xor32(l_run);
+  __syncthreads();
+  float* mb = reinterpret_cast<float*>(smem);           // [4][G][D] partial acc
+  float* ml = mb + 4 * G * D;                           // [4][G][2] (m, l)
+  if (col_live) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int d = 32 * db + 8 * (i >> 2) + 4 * lh + (i & 3);
+        mb[(wave * G + ln) * D + d] = oacc[db][i];
+      }
+    if (lh == 0) {
+      ml[(wave * G + ln) * 2 + 0] = m_run;
+      ml[(wave * G + ln) * 2 + 1] = l_tot;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int n = idx / D;
+    const int d = idx % D;
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[(w * G + n) * 2]);
+    const float Mu = (M == NEG_INF) ? 0.f : M;
+    float acc = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float sc = fast_exp2(ml[(w * G + n) * 2] - Mu);
+      acc += sc * mb[(w * G + n) * D + d];
+      l += sc * ml[(w * G + n) * 2 + 1];
+    }
+    const int hh = hkv * G + n;
+    if (a.n_split == 1) {
+      a.o[(static_cast<size_t>(b) * a.Hq + hh) * D + d] = f32_to_bf16(acc / l);
+      if (d == 0 && a.lse) a.lse[static_cast<size_t>(b) * a.Hq + hh] = (M + fast_log2(l)) * kLn2;
+    } else {
+      float* wp = a.ws + ((static_cast<size_t>(b) * a.Hq + hh) * a.n_split + split) * (D + 2);
+      wp[d] = acc;
+      if (d == 0) {
+        wp[D] = M;
+        wp[D + 1] = l;
+      }
+    }
+  }
+}
+
+// Combine the split partials of one (batch, head): o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+template <int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+  const int bh = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* wp = a.ws + static_cast<size_t>(bh) * a.n_split * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, wp[s * (D + 2) + D]);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float acc = 0.f, l = 0.f;
+  for (int s = 0; s < a.n_split; ++s) {
+    const float sc = fast_exp2(wp[s * (D + 2) + D] - Mu);
+    acc += sc * wp[s * (D + 2) + d];
+    l += sc * wp[s * (D + 2) + D + 1];
+  }
+  a.o[static_cast<size_t>(bh) * D + d] = f32_to_bf16(acc / l);
+  if (d == 0 && a.lse) a.lse[bh] = (M + fast_log2(l)) * kLn2;
+}
+
+template <int D, int MODE>
+hipError_t launch_d(DecodeArgs a, hipStream_t s) {
+  const dim3 grid(a.n_split, a.Hkv, a.B);
+  hipLaunchKernelGGL((decode_bf16_kernel<D, MODE>), grid, dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_split == 1) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+void decode_split(int B, int Hkv, int kv_len, int window, int* n_split, int* keys_per_wave) {
+  const int key_begin = window ? (kv_len > window ? kv_len - window : 0) : 0;
+  const long long n_vis = static_cast<long long>(kv_len) - key_begin;
+  const long long pairs = static_cast<long long>(B) * Hkv;
+  long long ns = 1;
+  if (n_vis > 1024) {
+    const long long target_wg = 1024;
+    ns = (target_wg + pairs - 1) / pairs;
+    const long long max_ns = (n_vis + 4 * TK - 1) / (4 * TK);
+    if (ns > max_ns) ns = max_ns;
+    if (ns < 1) ns = 1;
+  }
+  long long kpw = (n_vis + 4 * ns - 1) / (4 * ns);
+  kpw = (kpw + TK - 1) / TK * TK;
+  if (kpw < TK) kpw = TK;
+  ns = (n_vis + 4 * kpw - 1) / (4 * kpw);
+  if (ns < 1) ns = 1;
+  *n_split = static_cast<int>(ns);
+  *keys_per_wave = static_cast<int>(kpw);
+}
+
+hipError_t launch_decode_bf16(DecodeArgs a, int D, int mode, hipStream_t s) {
+  if (D == 128) {
+    switch (mode) {
+      case 0: return launch_d<128, 0>(a, s);
+      case 1: return launch_d<128, 1>(a, s);
+      default: return launch_d<128, 2>(a, s);
+    }
+  }
+  switch (mode) {
+    case 0: return launch_d<64, 0>(a, s);
+    case 1: return launch_d<64, 1>(a, s);
+    default: return launch_d<64, 2>(a, s);
+  }
+}
+
+}  // namespace rba

@@ -1,0 +1,81 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels.
+// Not installed; the public interface is include/relbias_attn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rba {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Prefill arguments (bf16 MFMA path).  Strides are implied by the dense shapes
+// q/o [B,S,Hq,D], k/v [B,S,Hkv,D], r [B,S,Hq,R], lse [B,Hq,S].
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  const float* table;   // [Hq, bias_range]
+  const uint16_t* r;    // [B, S, Hq, R]
+  const float* E;       // [Hq, R, bias_range]
+  int B, S, Hq, Hkv, G;
+  int window;           // 0 = full causal
+  int bias_range;
+  int R;
+  int hpw;              // query heads per workgroup (they share one kv head)
+  int rows_wg;          // query rows per workgroup
+  int n_qtiles;         // ceil(S / rows_wg)
+  int n_hgroups;        // Hq / hpw
+  int longest_first;    // schedule query tiles with the most keys first
+  float c_qk;           // scale * log2(e)
+};
+
+// Generic fp32 attention (VALU): queries at positions q_pos0 + i, keys at
+// positions 0..Lk-1 read from rows of a [B, kv_rows, Hkv, D] buffer.
+struct F32Args {
+  const float* q;       // [B, Sq, Hq, D]
+  const float* k;       // [B, kv_rows, Hkv, D]
+  const float* v;
+  float* o;             // [B, Sq, Hq, D]
+  float* lse;           // [B, Hq, Sq] or null
+  const float* table;
+  const float* r;       // [B, Sq, Hq, R]
+  const float* E;
+  int B, Sq, Hq, Hkv, G, D;
+  int kv_rows;          // row count of the k/v buffers per batch entry (L_max or S)
+  int Lk;               // keys 0..Lk-1 exist
+  int q_pos0;           // position of query 0
+  int window, bias_range, mode, R;
+  float scale;
+};
+
+// Decode arguments (bf16 MFMA path).
+struct DecodeArgs {
+  const uint16_t* q;    // [B, Hq, D]
+  const uint16_t* k;    // [B, L_max, Hkv, D]
+  const uint16_t* v;
+  uint16_t* o;          // [B, Hq, D]
+  float* lse;           // [B, Hq] or null
+  const float* table;
+  const uint16_t* r;    // [B, Hq, R]
+  const float* E;
+  float* ws;            // partials [B, Hq, n_part, D + 2] (unnormalised acc, m, l) or null
+  int B, L_max, kv_len, Hq, Hkv, G;
+  int window, bias_range, R;
+  int key_begin;        // first visible key (kv_len - window, clamped at 0)
+  int n_split;          // workgroups per (b, kv head); each has 4 waves
+  int keys_per_wave;    // multiple of 64
+  float c_qk;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int D, int mode, hipStream_t s);
+hipError_t launch_attn_f32(const F32Args& a, hipStream_t s);
+hipError_t launch_decode_bf16(DecodeArgs a, int D, int mode, hipStream_t s);
+
+// Decode split policy, shared by the workspace-size query and the launcher.
+void decode_split(int B, int Hkv, int kv_len, int window, int* n_split, int* keys_per_wave);
+
+}  // namespace rba
