@@ -58,10 +58,18 @@ def assert_parity(got, ref, dtype, what=""):
 
 
 def assert_lse(got, ref, dtype, what=""):
-    tol = 1e-5 if dtype == "f32" else 2e-3
-    err = float(np.abs(np.asarray(got, np.float64) - ref).max()) if ref.size else 0.0
-    _say(f"    lse {what}: max_abs={err:.3e}")
-    assert err <= tol, (what, err)
+    """The log-sum-exp is held to the same bar as the output.
+
+    On the bf16 path the row sum adds the bf16-rounded probabilities (the same
+    ones the P.V product uses) and the r.E bias uses a bf16 copy of E, so lse
+    carries errors of order 2^-9 (about 2e-3 in natural log units per source).
+    """
+    max_abs, rel = _errs(got, ref)
+    _say(f"    lse {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    if dtype == "f32":
+        assert max_abs <= F32_TOL, (what, max_abs)
+    else:
+        assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, (what, max_abs, rel)
 
 
 def _t2np(t):

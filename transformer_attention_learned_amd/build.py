@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librelbias_attn.so")
 
-SOURCES = ["api.cpp", "fwd_bf16.hip", "attn_f32.hip", "decode_bf16.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_bf16_fast.hip", "attn_f32.hip", "decode_bf16.hip"]
 ARCH = "gfx950"
 
 
@@ -35,6 +35,8 @@ def _flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
             # no packed-fp32 VALU instructions in device code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in architectural VGPRs (the softmax rescales them with VALU ops)
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 

@@ -390,6 +390,10 @@ hipError_t launch_mode(const FwdArgs& a, int mode, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a0, int D, int mode, hipStream_t s) {
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(a0.table) & 15u) == 0 &&
+                      (reinterpret_cast<uintptr_t>(a0.E) & 15u) == 0;
+  if (vec_ok && fwd_fast_lds_bytes(D, a0.G, mode, a0.bias_range, a0.R, a0.c_qk) >= 0)
+    return launch_fwd_bf16_fast(a0, mode, s);
   FwdArgs a = a0;
   a.hpw = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0 ? 2 : 1);
   if (D == 128) return launch_mode<128, 1>(a, mode, s);

@@ -1,0 +1,606 @@
+// Prefill, fast path for head_dim 128 and GQA groups of 4k query heads (gfx950).
+//
+// Same operation as the generic prefill kernel (scaled q.k plus a bias read at
+// the distance i - j, zero at and beyond the range, causal / sliding window;
+// "Thinking Machines dropped RoPE", steps 3-5 and the kernel-cost section),
+// organised for MFMA throughput:
+//
+//   * workgroup = 4 waves = the 4 query heads of one GQA group over the same
+//     64 query rows; each wave owns 64 rows (two 32-row MFMA blocks), so every
+//     16-byte K or V fragment read from LDS feeds two MFMAs (8 LDS bytes per
+//     logit for K and V together);
+//   * K/V tiles of 64 keys, double-buffered in LDS; the tile after next is
+//     fetched into registers while the current one is in use (V transposed on
+//     its way to LDS);
+//   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: each lane owns
+//     one query row, P stays in registers;
+//   * the key loop is a two-stage software pipeline over 32-key steps: the
+//     S MFMAs of step j+1 are issued next to the exp / pack of step j, and the
+//     P.V MFMAs of step j next to the row max of step j+1, so the matrix cores
+//     and the vector ALUs work at the same time;
+//   * bias and mask enter through the MFMA accumulator: the S accumulator of a
+//     step starts at bias / scale (or -inf where a key is not visible), so
+//     scale * (q.k + bias / scale) = scale * q.k + bias comes out of the MFMA
+//     and the softmax needs no per-element fix-up; steps with neither bias nor
+//     mask start at zero;
+//   * online softmax with lazy rescaling: the running max only moves when a
+//     row's max grows by more than 2^8, so the O rescale is rare;
+//   * table bias: the group's table rows sit in LDS and are read at the
+//     distance in the steps that reach below the range;
+//   * input-dependent bias r_i . E[h, :, delta]: E (bf16) for the group's heads
+//     is staged in LDS once per workgroup; the curve of a 32x32 block over its
+//     63 distances is two 32-distance curve blocks (one MFMA each, K = the R
+//     features) written to a per-wave LDS buffer whose rows are skewed by the
+//     query index, so that the diagonal read delta = c + n - m is four
+//     contiguous values per 8-byte read; with the ring variant consecutive key
+//     blocks share one curve block;
+//   * steps outside the window are skipped by the mask; steps beyond the bias
+//     range are content-only (the NoPE tail of global layers).
+
+#include <cstdlib>
+
+#include "rba_device.h"
+#include "rba_internal.h"
+
+namespace rba {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int BN = 64;            // keys per tile
+constexpr int NC = D / 16;        // K = 16 chunks of the head dim
+constexpr int NDB = D / 32;       // 32-wide head-dim blocks of O^T
+constexpr int KST = D + 8;        // K tile row stride (bf16)
+constexpr int VST = BN + 8;       // V^T tile row stride (bf16)
+constexpr int RST = 68;           // curve buffer row stride (bf16)
+constexpr int ROWS_WG = 64;       // query rows per workgroup
+constexpr float kRescale = 8.f;   // lazy rescale threshold (log2 units)
+
+constexpr int KS_BYTES = BN * KST * 2;
+constexpr int VT_BYTES = D * VST * 2;
+constexpr int BUF_BYTES = KS_BYTES + VT_BYTES;
+constexpr int RING_BYTES_PER_QB = 32 * RST * 2;
+
+// QB 32-row query blocks per wave; 8 / QB waves = 4 heads x (2 / QB) row halves.
+
+__device__ __forceinline__ int vt_pos(int x) {
+  return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// MODE 0 none, 1 table, 2 r.E; EF = features per distance in the staged E (8 or 16);
+// RING: one curve buffer per query block, shared by consecutive key blocks.
+template <int MODE, int EF, bool RING, int QB>
+__global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bias_off, int ring_off) {
+  constexpr int NT = 512 / QB;      // threads per workgroup
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ln = lane & 31;
+  const int lh = lane >> 5;
+
+  const int per_q = a.n_hgroups * a.B;
+  int qt = blockIdx.x / per_q;
+  const int rem = blockIdx.x - qt * per_q;
+  const int hg = rem % a.n_hgroups;
+  const int b = rem / a.n_hgroups;
+  if (a.longest_first) qt = a.n_qtiles - 1 - qt;
+
+  const int S = a.S;
+  const int W = a.window;
+  const int Rb = a.bias_range;
+  const int i0 = qt * ROWS_WG;
+  const int h = hg * 4 + (wave & 3);
+  const int i0w = i0 + 32 * QB * (wave >> 2);   // first row of this wave
+  const int hkv = h / a.G;
+  const int row_last = min(S, i0 + ROWS_WG) - 1;
+  const int kmin = W ? max(0, i0 - W + 1) : 0;
+  const int t_begin = kmin / BN;
+  const int ntiles = row_last / BN - t_begin + 1;
+  const int nsteps = 2 * ntiles;
+
+  const float cqk = a.c_qk;              // scale * log2(e)
+  const float inv_scale = kLog2e / cqk;  // bias -> accumulator units (bias / scale)
+
+  const size_t q_row = static_cast<size_t>(a.Hq) * D;
+  const size_t kv_row = static_cast<size_t>(a.Hkv) * D;
+  const uint16_t* kbase = a.k + static_cast<size_t>(b) * S * kv_row + static_cast<size_t>(hkv) * D;
+  const uint16_t* vbase = a.v + static_cast<size_t>(b) * S * kv_row + static_cast<size_t>(hkv) * D;
+
+  // ---- K/V staging: 64 keys x 128 dims of K and of V per tile.  K: 1024 chunks of 16 B,
+  // row-major; V: 256 items of 4 keys x 8 dims, transposed.  With 256 threads each thread
+  // takes 4 K chunks and one V item; with 512 threads half take K, half take V.
+  u32x4 kreg[4], vreg[4];
+  const bool v_thread = (NT == 256) || (tid >= 256);
+  const bool k_thread = (NT == 256) || (tid < 256);
+  const int vt_id = tid & 255;
+  const int v_kg = vt_id & 15;
+  const int v_dg = vt_id >> 4;
+  auto load_tile = [&](int tk0) {
+    if (k_thread) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int key = tk0 + it * 16 + (vt_id >> 4);
+        kreg[it] = u32x4{0u, 0u, 0u, 0u};
+        if (key < S) kreg[it] = ld16(kbase + static_cast<size_t>(key) * kv_row + 8 * (vt_id & 15));
+      }
+    }
+    if (v_thread) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int key = tk0 + 4 * v_kg + s;
+        vreg[s] = u32x4{0u, 0u, 0u, 0u};
+        if (key < S) vreg[s] = ld16(vbase + static_cast<size_t>(key) * kv_row + 8 * v_dg);
+      }
+    }
+    if (QB == 2) {   // 1 wave per SIMD: park the staged tile in the accumulation registers
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        asm volatile("" : "+a"(kreg[it]));
+        asm volatile("" : "+a"(vreg[it]));
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t* Ks = reinterpret_cast<uint16_t*>(smem + buf * BUF_BYTES);
+    uint16_t* Vt = reinterpret_cast<uint16_t*>(smem + buf * BUF_BYTES + KS_BYTES);
+    if (k_thread) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) st16(Ks + (it * 16 + (vt_id >> 4)) * KST + 8 * (vt_id & 15), kreg[it]);
+    }
+    if (v_thread) {
+      const int pos = vt_pos(4 * v_kg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+        const uint32_t p01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
+        const uint32_t p23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);
+        st8(Vt + (8 * v_dg + e) * VST + pos, u32x2{p01, p23});
+      }
+    }
+  };
+
+  // first tile in flight while the bias parameters are staged
+  load_tile(t_begin * BN);
+
+  // ---- stage the group's bias parameters in LDS, in accumulator units (bias / scale) ------
+  if (MODE == 1) {
+    // the 4 table rows of the group are contiguous in memory and in LDS: [hw][delta]
+    float4* tab4 = reinterpret_cast<float4*>(smem + bias_off);
+    const float4* src4 = reinterpret_cast<const float4*>(a.table + static_cast<size_t>(hg) * 4 * Rb);
+    for (int base = tid; base < Rb; base += 4 * NT) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (base + NT * u < Rb) v[u] = src4[base + NT * u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (base + NT * u < Rb)
+          tab4[base + NT * u] = float4{v[u].x * inv_scale, v[u].y * inv_scale, v[u].z * inv_scale,
+                                        v[u].w * inv_scale};
+    }
+  }
+  if (MODE == 2) {
+    uint16_t* e2 = reinterpret_cast<uint16_t*>(smem + bias_off);
+    const int R = a.R;
+    const float* Eg = a.E + static_cast<size_t>(hg) * 4 * R * Rb;
+    // element (hw, f, d) of E -> e2[(hw * Rb + d) * EF + f]; 4 consecutive d per float4
+    const int per_hw = EF * Rb / 4;
+    const int nvec = 4 * per_hw;
+    for (int base = tid; base < nvec; base += NT * 4) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int vi = base + NT * u;
+        const int hw = vi / per_hw;
+        const int rr = vi - hw * per_hw;
+        const int f = rr / (Rb / 4);
+        v[u] = float4{0.f, 0.f, 0.f, 0.f};
+        if (vi < nvec && f < R)
+          v[u] = reinterpret_cast<const float4*>(Eg + (static_cast<size_t>(hw) * R + f) * Rb)[rr - f * (Rb / 4)];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int vi = base + NT * u;
+        if (vi >= nvec) continue;
+        const int hw = vi / per_hw;
+        const int rr = vi - hw * per_hw;
+        const int f = rr / (Rb / 4);
+        const int d = 4 * (rr - f * (Rb / 4));
+        uint16_t* dst = e2 + (hw * Rb + d) * EF + f;
+        dst[0] = f32_to_bf16(v[u].x * inv_scale);
+        dst[EF] = f32_to_bf16(v[u].y * inv_scale);
+        dst[2 * EF] = f32_to_bf16(v[u].z * inv_scale);
+        dst[3 * EF] = f32_to_bf16(v[u].w * inv_scale);
+      }
+    }
+  }
+
+  // ---- per-wave constants -------------------------------------------------------------------
+  bf16x8 qf[QB][NC];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = i0w + 32 * qb + ln;
+    const uint16_t* qp = a.q + (static_cast<size_t>(b) * S + row) * q_row + static_cast<size_t>(h) * D + 8 * lh;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row < S) v = ld16(qp + 16 * c);
+      qf[qb][c] = as_bf16x8(v);
+    }
+  }
+  // The query fragments are only ever MFMA operands: keep them in the accumulation
+  // registers so the architectural VGPRs stay free for O and the softmax.
+  if (QB == 2) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) asm volatile("" : "+a"(qf[qb][c]));
+  }
+  bf16x8 rf[QB];
+  if (MODE == 2) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = i0w + 32 * qb + ln;
+      const uint16_t* rp = a.r + ((static_cast<size_t>(b) * S + row) * a.Hq + h) * a.R;
+      const int f0 = (EF == 16) ? 8 * lh : 0;
+      const bool live = row < S && (EF == 16 || lh == 0);
+      uint32_t w[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int f = f0 + 2 * jj;
+        const uint32_t lo = (live && f < a.R) ? rp[f] : 0u;
+        const uint32_t hi = (live && f + 1 < a.R) ? rp[f + 1] : 0u;
+        w[jj] = lo | (hi << 16);
+      }
+      rf[qb] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+    }
+  }
+
+  float m_run[QB], l_run[QB];
+  f32x16 oacc[QB][NDB];
+  int ring_lo[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+    ring_lo[qb] = 0x7fffffff;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[qb][db][i] = 0.f;
+  }
+
+  const float NEG_INF = -INFINITY;
+  const float* tabw = (MODE == 1) ? reinterpret_cast<const float*>(smem + bias_off) + (wave & 3) * Rb : nullptr;
+  const uint16_t* e2w = (MODE == 2) ? reinterpret_cast<const uint16_t*>(smem + bias_off) + (wave & 3) * Rb * EF : nullptr;
+  uint16_t* ring = (MODE == 2) ? reinterpret_cast<uint16_t*>(smem + ring_off) + wave * (RING ? QB : 1) * 32 * RST : nullptr;
+
+  // Accumulator start values of step js for query block qb: bias / scale where the
+  // key is visible and in band, 0 where visible and beyond the band, -inf elsewhere.
+  auto step_init = [&](int js, int qb) -> f32x16 {
+    f32x16 init;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) init[i] = 0.f;
+    const int j0 = (t_begin + (js >> 1)) * BN + 32 * (js & 1);
+    const int c = (i0w + 32 * qb) - j0;                // delta = c + n - m
+    bool on = (c + 31 >= 0) && (j0 < S) && (i0w + 32 * qb < S);
+    if (W) on = on && (c - 31 < W);
+    const bool edge = !on || (c - 31 < 0) || (W && c + 31 >= W);
+    const bool inband = on && (MODE != 0) && (c - 31 < Rb);
+    if (MODE == 1 && inband) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = 8 * (i >> 2) + 4 * lh + (i & 3);
+        const int d = c + ln - m;
+        const float tv = tabw[min(max(d, 0), Rb - 1)];
+        init[i] = (d >= 0 && d < Rb) ? tv : 0.f;
+      }
+    }
+    if (MODE == 2 && inband) {
+      uint16_t* rg = ring + (RING ? qb : 0) * 32 * RST;
+      const int gam = c >> 5;
+      auto curve_block = [&](int beta) {
+        const int dl = 32 * beta + 1 + ln;
+        u32x4 ev = {0u, 0u, 0u, 0u};
+        if ((EF == 16 || lh == 0) && dl >= 0 && dl < Rb) ev = ld16(e2w + dl * EF + 8 * lh);
+        f32x16 cacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) cacc[i] = 0.f;
+        cacc = mfma32(as_bf16x8(ev), rf[qb], cacc);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int sidx = 8 * (i >> 2) + 4 * lh + (i & 3);
+          const int col = (32 * beta + 1 + sidx - ln + 3) & 63;
+          rg[ln * RST + col] = f32_to_bf16(cacc[i]);
+        }
+      };
+      if (!RING || ring_lo[qb] != gam) curve_block(gam);
+      curve_block(gam - 1);
+      if (RING) ring_lo[qb] = gam - 1;
+      wave_sync_lds();
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int m0 = 8 * g4 + 4 * lh;
+        const u32x2 w = ld8(rg + ln * RST + ((c - m0) & 63));
+        // element k of the run holds key m0 + 3 - k
+        init[4 * g4 + 3] = __uint_as_float(w[0] << 16);
+        init[4 * g4 + 2] = __uint_as_float(w[0] & 0xffff0000u);
+        init[4 * g4 + 1] = __uint_as_float(w[1] << 16);
+        init[4 * g4 + 0] = __uint_as_float(w[1] & 0xffff0000u);
+      }
+      wave_sync_lds();
+    }
+    if (edge) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = 8 * (i >> 2) + 4 * lh + (i & 3);
+        const int d = c + ln - m;
+        if (!on || d < 0 || (W && d >= W)) init[i] = NEG_INF;
+      }
+    }
+    return init;
+  };
+
+  auto k_frag = [&](int js, int c) -> bf16x8 {
+    const uint16_t* Ks = reinterpret_cast<const uint16_t*>(smem + ((js >> 1) & 1) * BUF_BYTES);
+    return as_bf16x8(ld16(Ks + (32 * (js & 1) + ln) * KST + 16 * c + 8 * lh));
+  };
+  auto v_frag = [&](int js, int idx) -> bf16x8 {   // idx = 2 * db + kk
+    const uint16_t* Vt = reinterpret_cast<const uint16_t*>(smem + ((js >> 1) & 1) * BUF_BYTES + KS_BYTES);
+    return as_bf16x8(ld16(Vt + (32 * (idx >> 1) + ln) * VST + 32 * (js & 1) + 16 * (idx & 1) + 8 * lh));
+  };
+  // S^T of step js accumulated onto `acc`; the K fragment of chunk c+1 is read before
+  // the MFMAs of chunk c.
+  auto step_scores = [&](int js, f32x16 (&acc)[QB]) {
+    bf16x8 kf = k_frag(js, 0);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      bf16x8 kn = kf;
+      if (c + 1 < NC) kn = k_frag(js, c + 1);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) acc[qb] = mfma32(kf, qf[qb][c], acc[qb]);
+      kf = kn;
+    }
+  };
+  // O^T += V^T P^T for step js.
+  auto step_pv = [&](int js, const bf16x8 (&pf)[QB][2]) {
+    bf16x8 vf = v_frag(js, 0);
+#pragma unroll
+    for (int idx = 0; idx < 2 * NDB; ++idx) {
+      bf16x8 vn = vf;
+      if (idx + 1 < 2 * NDB) vn = v_frag(js, idx + 1);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) oacc[qb][idx >> 1] = mfma32(vf, pf[qb][idx & 1], oacc[qb][idx >> 1]);
+      vf = vn;
+    }
+  };
+  // Probabilities of a step (bf16, packed for the P.V MFMA) and the running row sums.
+  auto step_probs = [&](const f32x16 (&acc)[QB], const float (&m_use)[QB], bf16x8 (&pf)[QB][2]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float psum = l_run[qb];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        uint32_t w[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float p0 = fast_exp2(fmaf(acc[qb][8 * kk + 2 * jj], cqk, -m_use[qb]));
+          const float p1 = fast_exp2(fmaf(acc[qb][8 * kk + 2 * jj + 1], cqk, -m_use[qb]));
+          w[jj] = pack_bf16x2(p0, p1);
+          psum = sum_bf16x2(w[jj], psum);
+        }
+        pf[qb][kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+      }
+      l_run[qb] = psum;
+    }
+  };
+  // Row max of a step in log2 units (both halves of the lane pair).
+  auto step_rowmax = [&](const f32x16 (&acc)[QB], float (&mx)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float v = fmaxf(fmaxf(acc[qb][0], acc[qb][1]), acc[qb][2]);
+#pragma unroll
+      for (int i = 3; i < 15; i += 2) v = fmaxf(fmaxf(v, acc[qb][i]), acc[qb][i + 1]);
+      v = fmaxf(v, acc[qb][15]);
+      mx[qb] = pair_max(v) * cqk;
+    }
+  };
+  // Lazy rescale: move the running max only when a row grew by more than 2^kRescale.
+  auto rescale = [&](const float (&mx)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const bool need = mx[qb] > m_run[qb] + kRescale;
+      if (__any(need)) {
+        const float alpha = need ? fast_exp2(m_run[qb] - mx[qb]) : 1.f;
+        if (need) m_run[qb] = mx[qb];
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
+      }
+    }
+  };
+
+  // ---- prologue: tile 0 in buffer 0, tile 1 in flight, scores of step 0 ------------------------
+  store_tile(0);
+  if (ntiles > 1) load_tile((t_begin + 1) * BN);
+  __syncthreads();
+
+  f32x16 sacc[QB];
+  {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) sacc[qb] = step_init(0, qb);
+    step_scores(0, sacc);
+    float mx[QB];
+    step_rowmax(sacc, mx);
+    rescale(mx);
+  }
+
+  // ---- steady state: two straight-line stages per 32-key step ----------------------------------
+  for (int js = 0; js + 1 < nsteps; ++js) {
+    const int tl = js >> 1;
+    if ((js & 1) == 0 && tl + 1 < ntiles) {
+      __syncthreads();                      // everyone is done with the buffer of tile tl-1
+      store_tile((tl + 1) & 1);
+      if (tl + 2 < ntiles) load_tile((t_begin + tl + 2) * BN);
+    }
+    if ((js & 1) == 1 && tl + 1 < ntiles) __syncthreads();   // tile tl+1 is in LDS
+
+    f32x16 snext[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) snext[qb] = step_init(js + 1, qb);
+    float m_use[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m_use[qb] = (m_run[qb] == NEG_INF) ? 0.f : m_run[qb];
+
+    // stage 1: S MFMAs of step js+1 interleaved with the exp / pack of step js
+    bf16x8 pf[QB][2];
+    step_scores(js + 1, snext);
+    step_probs(sacc, m_use, pf);
+#pragma unroll
+    for (int g = 0; g < NC; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);  // VALU / transcendental
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) asm volatile("" : "+v"(snext[qb]));
+
+    // stage 2: P.V MFMAs of step js interleaved with the row max of step js+1
+    float mx[QB];
+    step_pv(js, pf);
+    step_rowmax(snext, mx);
+#pragma unroll
+    for (int g = 0; g < 2 * NDB; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(oacc[qb][db]));
+
+    rescale(mx);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) sacc[qb] = snext[qb];
+  }
+
+  // ---- last step --------------------------------------------------------------------------------
+  {
+    float m_use[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) m_use[qb] = (m_run[qb] == NEG_INF) ? 0.f : m_run[qb];
+    bf16x8 pf[QB][2];
+    step_probs(sacc, m_use, pf);
+    step_pv(nsteps - 1, pf);
+  }
+
+  // ---- epilogue ------------------------------------------------------------------------------
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = i0w + 32 * qb + ln;
+    const float lt = pair_sum(l_run[qb]);
+    if (row >= S) continue;
+    const float inv = 1.f / lt;
+    uint16_t* op = a.o + (static_cast<size_t>(b) * S + row) * q_row + static_cast<size_t>(h) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * db + 8 * g4 + 4 * lh;
+        const f32x16& acc = oacc[qb][db];
+        st8(op + d, u32x2{pack_bf16x2(acc[4 * g4] * inv, acc[4 * g4 + 1] * inv),
+                          pack_bf16x2(acc[4 * g4 + 2] * inv, acc[4 * g4 + 3] * inv)});
+      }
+    if (a.lse && lh == 0)
+      a.lse[(static_cast<size_t>(b) * a.Hq + h) * S + row] = (m_run[qb] + fast_log2(lt)) * kLn2;
+  }
+}
+
+int bias_bytes(int mode, int Rb, int R) {
+  if (mode == 1) return 4 * Rb * 4;
+  if (mode == 2) return 4 * Rb * (R > 8 ? 16 : 8) * 2;
+  return 0;
+}
+
+// one curve buffer per wave, or per (wave, query block) with the ring; 8 / QB waves
+int ring_bytes(int mode, bool ring, int QB) {
+  return mode == 2 ? (8 / QB) * (ring ? QB : 1) * RING_BYTES_PER_QB : 0;
+}
+
+constexpr int kMaxLds = 160 * 1024;
+
+int lds_total(int mode, int Rb, int R, bool ring, int QB) {
+  return 2 * BUF_BYTES + bias_bytes(mode, Rb, R) + ring_bytes(mode, ring, QB);
+}
+
+template <int MODE, int EF, bool RING, int QB>
+hipError_t launch_fast(FwdArgs a, hipStream_t s) {
+  a.hpw = 4;
+  a.rows_wg = ROWS_WG;
+  a.n_qtiles = (a.S + ROWS_WG - 1) / ROWS_WG;
+  a.n_hgroups = a.Hq / 4;
+  a.longest_first = (a.window == 0 || a.window > ROWS_WG) ? 1 : 0;
+  const int bias_off = 2 * BUF_BYTES;
+  const int ring_off = bias_off + bias_bytes(MODE, a.bias_range, a.R);
+  const int total = ring_off + ring_bytes(MODE, RING, QB);
+  const long long nblk = static_cast<long long>(a.n_qtiles) * a.n_hgroups * a.B;
+  if (nblk <= 0) return hipSuccess;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_fast_kernel<MODE, EF, RING, QB>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((fwd_fast_kernel<MODE, EF, RING, QB>), dim3(static_cast<unsigned>(nblk)), dim3(512 / QB), total, s,
+                     a, bias_off, ring_off);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// LDS bytes the fast kernel needs, or -1 when the shape is outside its domain.
+int fwd_fast_lds_bytes(int D_, int G, int mode, int Rb, int R, float scale) {
+  if (D_ != D || G % 4 != 0 || !(scale > 0.f)) return -1;
+  if (mode != 0 && Rb % 4 != 0) return -1;
+  const int need = lds_total(mode, Rb, R, false, 2);
+  return need <= kMaxLds ? need : -1;
+}
+
+namespace {
+template <int QB>
+hipError_t launch_fast_qb(const FwdArgs& a, int mode, hipStream_t s) {
+  switch (mode) {
+    case 0: return launch_fast<0, 8, false, QB>(a, s);
+    case 1: return launch_fast<1, 8, false, QB>(a, s);
+    default:
+      if (a.R > 8) return launch_fast<2, 16, false, QB>(a, s);
+      if (lds_total(2, a.bias_range, a.R, true, QB) <= kMaxLds) return launch_fast<2, 8, true, QB>(a, s);
+      return launch_fast<2, 8, false, QB>(a, s);
+  }
+}
+}  // namespace
+
+hipError_t launch_fwd_bf16_fast(const FwdArgs& a, int mode, hipStream_t s) {
+  static const int rows_per_wave = [] {
+    const char* e = getenv("RBA_FAST_ROWS_PER_WAVE");
+    return (e && atoi(e) == 64) ? 64 : 32;
+  }();
+  // 8 waves of 32 rows unless their per-wave curve buffers do not fit next to the staged E
+  const bool fits8 = lds_total(mode, a.bias_range, a.R, false, 1) <= kMaxLds;
+  return (rows_per_wave == 64 || !fits8) ? launch_fast_qb<2>(a, mode, s) : launch_fast_qb<1>(a, mode, s);
+}
+
+}  // namespace rba

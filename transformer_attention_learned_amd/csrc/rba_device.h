@@ -22,8 +22,19 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> one packed pair of bf16 (round to nearest even), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// acc + lo(x) + hi(x) for a packed bf16 pair x (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float sum_bf16x2(uint32_t x, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x),
+                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -31,6 +42,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 
 // D = A * B + C on a 32x32 output tile, K = 16 bf16 (fp32 accumulate).
 // Lane l holds A row (l % 32) and B column (l % 32), 8 K-elements each; the
@@ -45,7 +57,18 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Max / sum with the lane 32 apart (the two halves of a 32x32 MFMA column).
+// Value of the lane 32 apart (the two halves of a 32x32 MFMA column).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// max / sum over the lane pair (l, l ^ 32) with v_permlane32_swap: both results of the
+// swap hold {x[l % 32], x[l % 32 + 32]} in every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 }  // namespace rba

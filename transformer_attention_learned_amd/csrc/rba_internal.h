@@ -72,6 +72,10 @@ struct DecodeArgs {
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int D, int mode, hipStream_t s);
+// Fast prefill path (head_dim 128, Hq/Hkv a multiple of 4): LDS bytes it needs, or -1
+// when the shape is outside its domain; and its launcher.
+int fwd_fast_lds_bytes(int D, int G, int mode, int bias_range, int R, float scale);
+hipError_t launch_fwd_bf16_fast(const FwdArgs& a, int mode, hipStream_t s);
 hipError_t launch_attn_f32(const F32Args& a, hipStream_t s);
 hipError_t launch_decode_bf16(DecodeArgs a, int D, int mode, hipStream_t s);
 
