@@ -37,7 +37,9 @@
 //   * steps outside the window are skipped by the mask; steps beyond the bias
 //     range are content-only (the NoPE tail of global layers).
 
-#include <cstdlib>
+#ifndef RBA_SCHED
+#define RBA_SCHED 0   // MFMA / VALU interleave pattern of the pipelined steps (0: compiler default)
+#endif
 
 #include "rba_device.h"
 #include "rba_internal.h"
@@ -75,7 +77,8 @@ __device__ __forceinline__ void wave_sync_lds() {
 
 // MODE 0 none, 1 table, 2 r.E; EF = features per distance in the staged E (8 or 16);
 // RING: one curve buffer per query block, shared by consecutive key blocks.
-template <int MODE, int EF, bool RING, int QB>
+// ESTAGE: E is staged in LDS (bf16); otherwise the curve MFMA reads fp32 E from global memory.
+template <int MODE, int EF, bool RING, int QB, bool ESTAGE>
 __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bias_off, int ring_off) {
   constexpr int NT = 512 / QB;      // threads per workgroup
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
                                         v[u].w * inv_scale};
     }
   }
-  if (MODE == 2) {
+  if (MODE == 2 && ESTAGE) {
     uint16_t* e2 = reinterpret_cast<uint16_t*>(smem + bias_off);
     const int R = a.R;
     const float* Eg = a.E + static_cast<size_t>(hg) * 4 * R * Rb;
@@ -297,6 +300,7 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
     const bool edge = !on || (c - 31 < 0) || (W && c + 31 >= W);
     const bool inband = on && (MODE != 0) && (c - 31 < Rb);
     if (MODE == 1 && inband) {
+      asm volatile("; in-band step: table bias" ::: "memory");
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int m = 8 * (i >> 2) + 4 * lh + (i & 3);
@@ -311,7 +315,17 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
       auto curve_block = [&](int beta) {
         const int dl = 32 * beta + 1 + ln;
         u32x4 ev = {0u, 0u, 0u, 0u};
-        if ((EF == 16 || lh == 0) && dl >= 0 && dl < Rb) ev = ld16(e2w + dl * EF + 8 * lh);
+        if (ESTAGE) {
+          if ((EF == 16 || lh == 0) && dl >= 0 && dl < Rb) ev = ld16(e2w + dl * EF + 8 * lh);
+        } else if ((EF == 16 || lh == 0) && dl >= 0 && dl < Rb) {
+          // E[h, f, dl] for f = 8 lh .. 8 lh + 7 (coalesced over the lanes' distances)
+          const float* ep = a.E + (static_cast<size_t>(h) * a.R + 8 * lh) * Rb + dl;
+          float e[8];
+#pragma unroll
+          for (int f = 0; f < 8; ++f) e[f] = (8 * lh + f < a.R) ? ep[static_cast<size_t>(f) * Rb] * inv_scale : 0.f;
+          ev = u32x4{pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
+                     pack_bf16x2(e[6], e[7])};
+        }
         f32x16 cacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) cacc[i] = 0.f;
@@ -340,6 +354,7 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
       wave_sync_lds();
     }
     if (edge) {
+      asm volatile("; edge step: mask" ::: "memory");          // keep this a branch, not selects
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int m = 8 * (i >> 2) + 4 * lh + (i & 3);
@@ -420,7 +435,9 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
     for (int qb = 0; qb < QB; ++qb) {
       const bool need = mx[qb] > m_run[qb] + kRescale;
       if (__any(need)) {
-        const float alpha = need ? fast_exp2(m_run[qb] - mx[qb]) : 1.f;
+        // rare path; the factor passes through an asm so the O multiply stays inside the branch
+        float alpha = need ? fast_exp2(m_run[qb] - mx[qb]) : 1.f;
+        asm volatile("; rare path: rescale O" : "+v"(alpha));
         if (need) m_run[qb] = mx[qb];
         l_run[qb] *= alpha;
 #pragma unroll
@@ -467,12 +484,22 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
     bf16x8 pf[QB][2];
     step_scores(js + 1, snext);
     step_probs(sacc, m_use, pf);
+#if RBA_SCHED == 1
 #pragma unroll
     for (int g = 0; g < NC; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x402, 12, 0);  // VALU / transcendental
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);         // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 6 * QB, 0);     // VALU / transcendental
     }
+#elif RBA_SCHED == 2
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int g = 0; g < NC; ++g) {
+      if (g + 2 < NC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 6 * QB, 0);
+    }
+#endif
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) asm volatile("" : "+v"(snext[qb]));
 
@@ -480,12 +507,22 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
     float mx[QB];
     step_pv(js, pf);
     step_rowmax(snext, mx);
+#if RBA_SCHED == 1
 #pragma unroll
     for (int g = 0; g < 2 * NDB; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 3 * QB, 0);
     }
+#elif RBA_SCHED == 2
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int g = 0; g < 2 * NDB; ++g) {
+      if (g + 2 < 2 * NDB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 3 * QB, 0);
+    }
+#endif
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -541,11 +578,11 @@ int ring_bytes(int mode, bool ring, int QB) {
 
 constexpr int kMaxLds = 160 * 1024;
 
-int lds_total(int mode, int Rb, int R, bool ring, int QB) {
-  return 2 * BUF_BYTES + bias_bytes(mode, Rb, R) + ring_bytes(mode, ring, QB);
+int lds_total(int mode, int Rb, int R, bool ring, int QB, bool estage = true) {
+  return 2 * BUF_BYTES + (estage || mode != 2 ? bias_bytes(mode, Rb, R) : 0) + ring_bytes(mode, ring, QB);
 }
 
-template <int MODE, int EF, bool RING, int QB>
+template <int MODE, int EF, bool RING, int QB, bool ESTAGE = true>
 hipError_t launch_fast(FwdArgs a, hipStream_t s) {
   a.hpw = 4;
   a.rows_wg = ROWS_WG;
@@ -553,18 +590,18 @@ hipError_t launch_fast(FwdArgs a, hipStream_t s) {
   a.n_hgroups = a.Hq / 4;
   a.longest_first = (a.window == 0 || a.window > ROWS_WG) ? 1 : 0;
   const int bias_off = 2 * BUF_BYTES;
-  const int ring_off = bias_off + bias_bytes(MODE, a.bias_range, a.R);
+  const int ring_off = bias_off + ((MODE != 2 || ESTAGE) ? bias_bytes(MODE, a.bias_range, a.R) : 0);
   const int total = ring_off + ring_bytes(MODE, RING, QB);
   const long long nblk = static_cast<long long>(a.n_qtiles) * a.n_hgroups * a.B;
   if (nblk <= 0) return hipSuccess;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_fast_kernel<MODE, EF, RING, QB>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_fast_kernel<MODE, EF, RING, QB, ESTAGE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((fwd_fast_kernel<MODE, EF, RING, QB>), dim3(static_cast<unsigned>(nblk)), dim3(512 / QB), total, s,
+  hipLaunchKernelGGL((fwd_fast_kernel<MODE, EF, RING, QB, ESTAGE>), dim3(static_cast<unsigned>(nblk)), dim3(512 / QB), total, s,
                      a, bias_off, ring_off);
   return hipGetLastError();
 }
@@ -575,32 +612,24 @@ hipError_t launch_fast(FwdArgs a, hipStream_t s) {
 int fwd_fast_lds_bytes(int D_, int G, int mode, int Rb, int R, float scale) {
   if (D_ != D || G % 4 != 0 || !(scale > 0.f)) return -1;
   if (mode != 0 && Rb % 4 != 0) return -1;
-  const int need = lds_total(mode, Rb, R, false, 2);
-  return need <= kMaxLds ? need : -1;
+  if (mode == 1 && lds_total(1, Rb, R, false, 1) > kMaxLds) return -1;
+  return lds_total(mode, Rb, R, false, 1, false);
 }
-
-namespace {
-template <int QB>
-hipError_t launch_fast_qb(const FwdArgs& a, int mode, hipStream_t s) {
-  switch (mode) {
-    case 0: return launch_fast<0, 8, false, QB>(a, s);
-    case 1: return launch_fast<1, 8, false, QB>(a, s);
-    default:
-      if (a.R > 8) return launch_fast<2, 16, false, QB>(a, s);
-      if (lds_total(2, a.bias_range, a.R, true, QB) <= kMaxLds) return launch_fast<2, 8, true, QB>(a, s);
-      return launch_fast<2, 8, false, QB>(a, s);
-  }
-}
-}  // namespace
 
 hipError_t launch_fwd_bf16_fast(const FwdArgs& a, int mode, hipStream_t s) {
-  static const int rows_per_wave = [] {
-    const char* e = getenv("RBA_FAST_ROWS_PER_WAVE");
-    return (e && atoi(e) == 64) ? 64 : 32;
-  }();
-  // 8 waves of 32 rows unless their per-wave curve buffers do not fit next to the staged E
-  const bool fits8 = lds_total(mode, a.bias_range, a.R, false, 1) <= kMaxLds;
-  return (rows_per_wave == 64 || !fits8) ? launch_fast_qb<2>(a, mode, s) : launch_fast_qb<1>(a, mode, s);
+  // 8 waves x 32 query rows; E staged in LDS when it fits next to the K/V tiles and the
+  // per-wave curve buffers, else read from global memory by the curve MFMA.
+  switch (mode) {
+    case 0: return launch_fast<0, 8, false, 1>(a, s);
+    case 1: return launch_fast<1, 8, false, 1>(a, s);
+    default: {
+      const bool stage = lds_total(2, a.bias_range, a.R, false, 1, true) <= kMaxLds;
+      // with one 32-row block per wave the ring costs no extra LDS: consecutive key blocks
+      // share a curve block
+      if (a.R > 8) return stage ? launch_fast<2, 16, true, 1, true>(a, s) : launch_fast<2, 16, true, 1, false>(a, s);
+      return stage ? launch_fast<2, 8, true, 1, true>(a, s) : launch_fast<2, 8, true, 1, false>(a, s);
+    }
+  }
 }
 
 }  // namespace rba
