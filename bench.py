@@ -32,7 +32,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 KERNEL_SOURCES = {
-    "prefill": ["fwd_bf16.hip"],
+    "prefill": ["fwd_bf16.hip", "fwd_bf16_fast.hip"],
     "decode": ["decode_bf16.hip"],
     "f32": ["attn_f32.hip"],
 }
@@ -132,6 +132,8 @@ def main():
     ap.add_argument("--workload", default="local_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -140,6 +142,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read_per_copy": n, "bytes_written_per_copy": n}))
+        return
 
     import transformer_attention_learned_amd as rba
     from transformer_attention_learned_amd.workloads import WORKLOADS, make_inputs

@@ -37,6 +37,9 @@
 //   * steps outside the window are skipped by the mask; steps beyond the bias
 //     range are content-only (the NoPE tail of global layers).
 
+#ifndef RBA_FORCE_GLOBAL_E
+#define RBA_FORCE_GLOBAL_E 0
+#endif
 #ifndef RBA_SCHED
 #define RBA_SCHED 0   // MFMA / VALU interleave pattern of the pipelined steps (0: compiler default)
 #endif
@@ -174,59 +177,6 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
   // first tile in flight while the bias parameters are staged
   load_tile(t_begin * BN);
 
-  // ---- stage the group's bias parameters in LDS, in accumulator units (bias / scale) ------
-  if (MODE == 1) {
-    // the 4 table rows of the group are contiguous in memory and in LDS: [hw][delta]
-    float4* tab4 = reinterpret_cast<float4*>(smem + bias_off);
-    const float4* src4 = reinterpret_cast<const float4*>(a.table + static_cast<size_t>(hg) * 4 * Rb);
-    for (int base = tid; base < Rb; base += 4 * NT) {
-      float4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (base + NT * u < Rb) v[u] = src4[base + NT * u];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (base + NT * u < Rb)
-          tab4[base + NT * u] = float4{v[u].x * inv_scale, v[u].y * inv_scale, v[u].z * inv_scale,
-                                        v[u].w * inv_scale};
-    }
-  }
-  if (MODE == 2 && ESTAGE) {
-    uint16_t* e2 = reinterpret_cast<uint16_t*>(smem + bias_off);
-    const int R = a.R;
-    const float* Eg = a.E + static_cast<size_t>(hg) * 4 * R * Rb;
-    // element (hw, f, d) of E -> e2[(hw * Rb + d) * EF + f]; 4 consecutive d per float4
-    const int per_hw = EF * Rb / 4;
-    const int nvec = 4 * per_hw;
-    for (int base = tid; base < nvec; base += NT * 4) {
-      float4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int vi = base + NT * u;
-        const int hw = vi / per_hw;
-        const int rr = vi - hw * per_hw;
-        const int f = rr / (Rb / 4);
-        v[u] = float4{0.f, 0.f, 0.f, 0.f};
-        if (vi < nvec && f < R)
-          v[u] = reinterpret_cast<const float4*>(Eg + (static_cast<size_t>(hw) * R + f) * Rb)[rr - f * (Rb / 4)];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int vi = base + NT * u;
-        if (vi >= nvec) continue;
-        const int hw = vi / per_hw;
-        const int rr = vi - hw * per_hw;
-        const int f = rr / (Rb / 4);
-        const int d = 4 * (rr - f * (Rb / 4));
-        uint16_t* dst = e2 + (hw * Rb + d) * EF + f;
-        dst[0] = f32_to_bf16(v[u].x * inv_scale);
-        dst[EF] = f32_to_bf16(v[u].y * inv_scale);
-        dst[2 * EF] = f32_to_bf16(v[u].z * inv_scale);
-        dst[3 * EF] = f32_to_bf16(v[u].w * inv_scale);
-      }
-    }
-  }
-
   // ---- per-wave constants -------------------------------------------------------------------
   bf16x8 qf[QB][NC];
 #pragma unroll
@@ -265,6 +215,61 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
         w[jj] = lo | (hi << 16);
       }
       rf[qb] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+    }
+  }
+
+  // ---- stage the group's bias parameters in LDS, in accumulator units (bias / scale) ------
+  if (MODE == 1) {
+    // the 4 table rows of the group are contiguous in memory and in LDS: [hw][delta]
+    float4* tab4 = reinterpret_cast<float4*>(smem + bias_off);
+    const float4* src4 = reinterpret_cast<const float4*>(a.table + static_cast<size_t>(hg) * 4 * Rb);
+    for (int base = tid; base < Rb; base += 4 * NT) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (base + NT * u < Rb) v[u] = src4[base + NT * u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (base + NT * u < Rb)
+          tab4[base + NT * u] = float4{v[u].x * inv_scale, v[u].y * inv_scale, v[u].z * inv_scale,
+                                        v[u].w * inv_scale};
+    }
+  }
+  if (MODE == 2 && ESTAGE) {
+    // float4 loads of E[h, f, 4q .. 4q+3]; the feature index varies fastest over the lanes so
+    // that 8 neighbouring lanes fill one 16-byte row e2[(hw, d)][0..7] (2-way bank conflicts)
+    uint16_t* e2 = reinterpret_cast<uint16_t*>(smem + bias_off);
+    const int R = a.R;
+    const float* Eg = a.E + static_cast<size_t>(hg) * 4 * R * Rb;
+    const int per_hw = EF * Rb / 4;          // float4 items per head
+    const int nvec = 4 * per_hw;
+    for (int base = tid; base < nvec; base += 4 * NT) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int vi = base + NT * u;
+        const int hw = vi / per_hw;
+        const int rr = vi - hw * per_hw;
+        const int f = rr % EF;
+        const int dq = rr / EF;
+        v[u] = float4{0.f, 0.f, 0.f, 0.f};
+        if (vi < nvec && f < R)
+          v[u] = reinterpret_cast<const float4*>(Eg + (static_cast<size_t>(hw) * R + f) * Rb)[dq];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int vi = base + NT * u;
+        if (vi >= nvec) continue;
+        const int hw = vi / per_hw;
+        const int rr = vi - hw * per_hw;
+        const int f = rr % EF;
+        const int dq = rr / EF;
+        uint16_t* dst = e2 + (hw * Rb + 4 * dq) * EF + f;
+        dst[0] = f32_to_bf16(v[u].x * inv_scale);
+        dst[EF] = f32_to_bf16(v[u].y * inv_scale);
+        dst[2 * EF] = f32_to_bf16(v[u].z * inv_scale);
+        dst[3 * EF] = f32_to_bf16(v[u].w * inv_scale);
+      }
     }
   }
 
@@ -623,7 +628,7 @@ hipError_t launch_fwd_bf16_fast(const FwdArgs& a, int mode, hipStream_t s) {
     case 0: return launch_fast<0, 8, false, 1>(a, s);
     case 1: return launch_fast<1, 8, false, 1>(a, s);
     default: {
-      const bool stage = lds_total(2, a.bias_range, a.R, false, 1, true) <= kMaxLds;
+      const bool stage = !RBA_FORCE_GLOBAL_E && lds_total(2, a.bias_range, a.R, false, 1, true) <= kMaxLds;
       // with one 32-row block per wave the ring costs no extra LDS: consecutive key blocks
       // share a curve block
       if (a.R > 8) return stage ? launch_fast<2, 16, true, 1, true>(a, s) : launch_fast<2, 16, true, 1, false>(a, s);
