@@ -179,8 +179,16 @@ def main():
         need = rba.decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.S, w.window)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
+        # A windowed step touches only window rows per sequence (134 MB for the local decode),
+        # which would stay in the 256 MB Infinity Cache across steps; rotating over 4 cache
+        # lengths makes consecutive steps read 4 disjoint windows, so the bytes come from HBM.
+        kv_lens = [w.S - j * w.window for j in range(4)] if (w.window and 4 * w.window <= w.S) else [w.S]
+        it = [0]
+
         def step():
-            rba.decode(inp["q"], inp["k"], inp["v"], w.S, window=w.window,
+            kv_len = kv_lens[it[0] % len(kv_lens)]
+            it[0] += 1
+            rba.decode(inp["q"], inp["k"], inp["v"], kv_len, window=w.window,
                        bias_range=w.bias_range, mode=w.mode, table=inp["table"], r=inp["r"],
                        E=inp["E"], scale=w.scale, out=out, workspace=ws)
 

@@ -8,12 +8,14 @@
 //
 // The step is bound by streaming K and V from HBM.  Grid = (split, kv head,
 // batch); each of the 4 waves of a workgroup streams its own contiguous run of
-// cache rows, 64 at a time:
+// cache rows, 32 at a time, with the next tile's loads in flight during the current one:
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16, the K rows loaded straight from
 //     global memory into the A operand (16 bytes per lane, no LDS), the G query
 //     heads of the kv head as B-operand columns;
 //   * V is staged in a wave-private LDS tile, transposed, and O^T = V^T P^T
 //     runs on the same MFMA with P kept in registers;
+//   * the bias curve of the workgroup's in-band distances (table row or r.E) is
+//     computed once into LDS; the key loop reads one value per in-band logit;
 //   * the 4 waves merge (max / sum-exp) through LDS; with several splits the
 //     workgroup writes an unnormalised partial that a second kernel combines.
 
@@ -24,19 +26,21 @@ namespace rba {
 
 namespace {
 
-constexpr int TK = 64;
+constexpr int TK = 32;          // cache rows per tile (one 32x32 MFMA block)
 
 __device__ __forceinline__ int vt_pos(int x) {
   return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
 template <int D, int MODE>
-__global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
-  constexpr int VST = TK + 8;
-  constexpr int NC = D / 16;
-  constexpr int NDB = D / 32;
-  constexpr int VT_ELEMS = D * VST;  // per wave (bf16)
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * VT_ELEMS];
+__global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int curve_off) {
+  constexpr int VST = TK + 8;          // V^T row stride (bf16): 80-byte rows, 16-byte aligned
+  constexpr int NC = D / 16;           // K = 16 chunks of the head dim
+  constexpr int NDB = D / 32;          // 32-wide head-dim blocks of O^T
+  constexpr int NVI = (TK / 4) * (D / 8) / 64;   // V items (4 rows x 8 dims) per lane
+  constexpr int VT_BYTES = D * VST * 2;          // per wave
+  // dynamic LDS: [4 x V^T tile | merge buffer, when larger] then the bias curve [G][n_curve]
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -58,6 +62,31 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
   // This wave's rows.
   const int w_beg = a.key_begin + (split * 4 + wave) * a.keys_per_wave;
   const int w_end = min(a.kv_len, w_beg + a.keys_per_wave);
+  const int ntiles = w_end > w_beg ? (w_end - w_beg + TK - 1) / TK : 0;
+
+  // ---- registers of the tile in flight: K as MFMA A-operand fragments, V as row pieces ---
+  u32x4 kreg[NC], vreg[NVI][4];
+  auto load_tile = [&](int tk0) {
+    const int key = tk0 + ln;
+    const uint16_t* kp = kbase + static_cast<size_t>(key) * kv_row + 8 * lh;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kreg[c] = u32x4{0u, 0u, 0u, 0u};
+      if (key < w_end) kreg[c] = ld16(kp + 16 * c);
+    }
+#pragma unroll
+    for (int it = 0; it < NVI; ++it) {
+      const int item = lane + 64 * it;
+      const int kg = item & 7;
+      const int dg = item >> 3;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int kk = tk0 + 4 * kg + s;
+        vreg[it][s] = u32x4{0u, 0u, 0u, 0u};
+        if (kk < w_end) vreg[it][s] = ld16(vbase + static_cast<size_t>(kk) * kv_row + 8 * dg);
+      }
+    }
+  };
 
   bf16x8 qf[NC];
   {
@@ -69,12 +98,34 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
       qf[c] = as_bf16x8(v);
     }
   }
-  float rv[16];
-  if (MODE == 2) {
-    const uint16_t* rp = a.r + (static_cast<size_t>(b) * a.Hq + (col_live ? h : 0)) * a.R;
-#pragma unroll
-    for (int f = 0; f < 16; ++f) rv[f] = (col_live && f < a.R) ? bf16_to_f32(rp[f]) * kLog2e : 0.f;
+  if (ntiles > 0) load_tile(w_beg);
+  // ---- bias curve of this workgroup's in-band distances, once, into LDS -------------------
+  // Rows [wg_beg, wg_end) carry a bias iff delta = qpos - key < bias_range; the curve of query
+  // head n at distance delta is table[h, delta] or sum_f r[b, h, f] E[h, f, delta] (log2 units).
+  float* curve = reinterpret_cast<float*>(smem + curve_off);
+  const int wg_beg = a.key_begin + split * 4 * a.keys_per_wave;
+  const int wg_end = min(a.kv_len, wg_beg + 4 * a.keys_per_wave);
+  const int d_lo = max(0, qpos - (wg_end - 1));                // smallest distance in the group
+  const int d_hi = min(a.bias_range, qpos - wg_beg + 1);       // one past the largest in band
+  const int n_curve = d_hi - d_lo;                             // <= 0: no bias in this group
+  if (MODE != 0 && n_curve > 0) {
+    for (int idx = tid; idx < G * n_curve; idx += 256) {
+      const int n = idx / n_curve;
+      const int dd = d_lo + (idx - n * n_curve);
+      const int hh = hkv * G + n;
+      float v;
+      if (MODE == 1) {
+        v = a.table[static_cast<size_t>(hh) * a.bias_range + dd];
+      } else {
+        const uint16_t* rp = a.r + (static_cast<size_t>(b) * a.Hq + hh) * a.R;
+        const float* ep = a.E + static_cast<size_t>(hh) * a.R * a.bias_range + dd;
+        v = 0.f;
+        for (int f = 0; f < a.R; ++f) v = fmaf(bf16_to_f32(rp[f]), ep[static_cast<size_t>(f) * a.bias_range], v);
+      }
+      curve[idx] = v * kLog2e;
+    }
   }
+  __syncthreads();
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 oacc[NDB];
@@ -83,95 +134,72 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
 
-  uint16_t* vt = smem + wave * VT_ELEMS;
+  uint16_t* vt = reinterpret_cast<uint16_t*>(smem) + wave * (VT_BYTES / 2);
   const float NEG_INF = -INFINITY;
 
-  for (int tk0 = w_beg; tk0 < w_end; tk0 += TK) {
-    // V tile -> LDS (transposed), 4 keys x 8 dims per item.
-    __builtin_amdgcn_wave_barrier();
-    for (int item = lane; item < (TK / 4) * (D / 8); item += 64) {
-      const int kg = item & 15;
-      const int dg = item >> 4;
-      u32x4 rows[4];
+  for (int t = 0; t < ntiles; ++t) {
+    const int tk0 = w_beg + t * TK;
+    // S^T = K Q^T from the registers of this tile
+    f32x16 sacc;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int key = tk0 + 4 * kg + s;
-        rows[s] = u32x4{0u, 0u, 0u, 0u};
-        if (key < w_end) rows[s] = ld16(vbase + static_cast<size_t>(key) * kv_row + 8 * dg);
-      }
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) sacc = mfma32(as_bf16x8(kreg[c]), qf[c], sacc);
+    // V of this tile -> LDS, transposed (the previous tile's reads of this buffer are done)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int it = 0; it < NVI; ++it) {
+      const int item = lane + 64 * it;
+      const int kg = item & 7;
+      const int dg = item >> 3;
       const int pos = vt_pos(4 * kg);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int w = e >> 1;
-        const int sh = (e & 1) * 16;
-        const uint32_t k0 = (rows[0][w] >> sh) & 0xffffu;
-        const uint32_t k1 = (rows[1][w] >> sh) & 0xffffu;
-        const uint32_t k2 = (rows[2][w] >> sh) & 0xffffu;
-        const uint32_t k3 = (rows[3][w] >> sh) & 0xffffu;
-        st8(vt + (8 * dg + e) * VST + pos, u32x2{k0 | (k1 << 16), k2 | (k3 << 16)});
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t p01 = __builtin_amdgcn_perm(vreg[it][1][w], vreg[it][0][w], sel);
+        const uint32_t p23 = __builtin_amdgcn_perm(vreg[it][3][w], vreg[it][2][w], sel);
+        st8(vt + (8 * dg + e) * VST + pos, u32x2{p01, p23});
       }
     }
-    // S^T = K Q^T, K straight from global memory.
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-      const int key = tk0 + 32 * kb + ln;
-      const uint16_t* kp = kbase + static_cast<size_t>(key) * kv_row + 8 * lh;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (key < w_end) v = ld16(kp + 16 * c);
-        sacc[kb] = mfma32(as_bf16x8(v), qf[c], sacc[kb]);
-      }
-    }
+    // registers are free: the next tile's loads are now in flight during this tile's work
+    if (t + 1 < ntiles) load_tile(tk0 + TK);
+
+    // logits (log2 units), bias for the last bias_range rows, mask beyond this wave's rows
     float mx = NEG_INF;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = tk0 + 32 * kb + 8 * (i >> 2) + 4 * lh + (i & 3);
+    for (int i = 0; i < 16; ++i) {
+      const int key = tk0 + 8 * (i >> 2) + 4 * lh + (i & 3);
+      float sv = sacc[i] * a.c_qk;
+      if (MODE != 0) {
         const int d = qpos - key;
-        float s = sacc[kb][i] * a.c_qk;
-        if (MODE != 0 && d < a.bias_range && key < w_end && col_live) {
-          if (MODE == 1) {
-            s += a.table[static_cast<size_t>(h) * a.bias_range + d] * kLog2e;
-          } else {
-            const float* Eh = a.E + static_cast<size_t>(h) * a.R * a.bias_range + d;
-            float bsum = 0.f;
-#pragma unroll
-            for (int f = 0; f < 16; ++f)
-              if (f < a.R) bsum = fmaf(rv[f], Eh[static_cast<size_t>(f) * a.bias_range], bsum);
-            s += bsum;
-          }
-        }
-        if (key >= w_end) s = NEG_INF;
-        sacc[kb][i] = s;
-        mx = fmaxf(mx, s);
+        if (d < a.bias_range && key < w_end && col_live) sv += curve[ln * n_curve + (d - d_lo)];
       }
+      if (key >= w_end) sv = NEG_INF;
+      sacc[i] = sv;
+      mx = fmaxf(mx, sv);
     }
-    mx = fmaxf(mx, xor32(mx));
+    mx = pair_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
-    float psum = 0.f;
-    bf16x8 pf[2][2];
+    float psum = l_run * alpha;
+    bf16x8 pf[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kk = 0; kk < 2; ++kk) {
+      uint32_t w[4];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        uint32_t w[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float p0 = fast_exp2(sacc[kb][8 * kk + 2 * jj] - m_use);
-          const float p1 = fast_exp2(sacc[kb][8 * kk + 2 * jj + 1] - m_use);
-          psum += p0 + p1;
-          w[jj] = pack_bf16x2(p0, p1);
-        }
-        pf[kb][kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+      for (int jj = 0; jj < 4; ++jj) {
+        const float p0 = fast_exp2(sacc[8 * kk + 2 * jj] - m_use);
+        const float p1 = fast_exp2(sacc[8 * kk + 2 * jj + 1] - m_use);
+        w[jj] = pack_bf16x2(p0, p1);
+        psum = sum_bf16x2(w[jj], psum);
       }
-    l_run = l_run * alpha + psum;
+      pf[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+    }
+    l_run = psum;
     m_run = m_new;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -184,19 +212,14 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 vf = as_bf16x8(ld16(vt + (32 * db + ln) * VST + 32 * kb + 16 * kk + 8 * lh));
-          oacc[db] = mfma32(vf, pf[kb][kk], oacc[db]);
-        }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 vf = as_bf16x8(ld16(vt + (32 * db + ln) * VST + 16 * kk + 8 * lh));
+        oacc[db] = mfma32(vf, pf[kk], oacc[db]);
+      }
   }
 
   // ---- merge the 4 waves through LDS (reusing the V^T area) ---------------------------
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = pair_sum(l_run);
   __syncthreads();
   float* mb = reinterpret_cast<float*>(smem);           // [4][G][D] partial acc
   float* ml = mb + 4 * G * D;                           // [4][G][2] (m, l)
@@ -265,7 +288,24 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
 template <int D, int MODE>
 hipError_t launch_d(DecodeArgs a, hipStream_t s) {
   const dim3 grid(a.n_split, a.Hkv, a.B);
-  hipLaunchKernelGGL((decode_bf16_kernel<D, MODE>), grid, dim3(256), 0, s, a);
+  constexpr int VT_ALL = 4 * D * (TK + 8) * 2;
+  const int merge = 4 * a.G * (D + 2) * 4;
+  const int curve_off = ((VT_ALL > merge ? VT_ALL : merge) + 15) / 16 * 16;
+  int n_curve_max = 0;
+  if (MODE != 0) {
+    const long long span = 4LL * a.keys_per_wave;   // rows of one workgroup
+    n_curve_max = static_cast<int>(span < a.bias_range ? span : a.bias_range);
+  }
+  const int total = curve_off + a.G * n_curve_max * 4;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_bf16_kernel<D, MODE>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  if (total > 160 * 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_bf16_kernel<D, MODE>), grid, dim3(256), total, s, a, curve_off);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, s, a);
@@ -275,17 +315,16 @@ hipError_t launch_d(DecodeArgs a, hipStream_t s) {
 }  // namespace
 
 void decode_split(int B, int Hkv, int kv_len, int window, int* n_split, int* keys_per_wave) {
+  // Enough workgroups to keep every CU streaming (2 resident per CU, 4 waves each); a wave
+  // takes a contiguous run of cache rows, a multiple of the 32-row tile.
   const int key_begin = window ? (kv_len > window ? kv_len - window : 0) : 0;
   const long long n_vis = static_cast<long long>(kv_len) - key_begin;
   const long long pairs = static_cast<long long>(B) * Hkv;
-  long long ns = 1;
-  if (n_vis > 1024) {
-    const long long target_wg = 1024;
-    ns = (target_wg + pairs - 1) / pairs;
-    const long long max_ns = (n_vis + 4 * TK - 1) / (4 * TK);
-    if (ns > max_ns) ns = max_ns;
-    if (ns < 1) ns = 1;
-  }
+  const long long target_wg = 2048;
+  long long ns = (target_wg + pairs - 1) / pairs;
+  const long long max_ns = (n_vis + 4 * 128 - 1) / (4 * 128);   // at least 128 rows per wave
+  if (ns > max_ns) ns = max_ns;
+  if (ns < 1) ns = 1;
   long long kpw = (n_vis + 4 * ns - 1) / (4 * ns);
   kpw = (kpw + TK - 1) / TK * TK;
   if (kpw < TK) kpw = TK;
