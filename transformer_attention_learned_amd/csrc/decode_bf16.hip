@@ -109,20 +109,47 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
   const int d_hi = min(a.bias_range, qpos - wg_beg + 1);       // one past the largest in band
   const int n_curve = d_hi - d_lo;                             // <= 0: no bias in this group
   if (MODE != 0 && n_curve > 0) {
-    for (int idx = tid; idx < G * n_curve; idx += 256) {
-      const int n = idx / n_curve;
-      const int dd = d_lo + (idx - n * n_curve);
-      const int hh = hkv * G + n;
-      float v;
+    // items (n, delta), 4 per thread per round with every load of a round issued together
+    const int n_items = G * n_curve;
+    for (int base = tid; base < n_items; base += 4 * 256) {
+      float v[4];
       if (MODE == 1) {
-        v = a.table[static_cast<size_t>(hh) * a.bias_range + dd];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int idx = base + 256 * u;
+          const int n = idx / n_curve;
+          const int dd = d_lo + (idx - n * n_curve);
+          v[u] = (idx < n_items) ? a.table[static_cast<size_t>(hkv * G + n) * a.bias_range + dd] : 0.f;
+        }
       } else {
-        const uint16_t* rp = a.r + (static_cast<size_t>(b) * a.Hq + hh) * a.R;
-        const float* ep = a.E + static_cast<size_t>(hh) * a.R * a.bias_range + dd;
-        v = 0.f;
-        for (int f = 0; f < a.R; ++f) v = fmaf(bf16_to_f32(rp[f]), ep[static_cast<size_t>(f) * a.bias_range], v);
+        float e[4][16], rr[4][16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int idx = base + 256 * u;
+          const int n = idx / n_curve;
+          const int dd = d_lo + (idx - n * n_curve);
+          const int hh = hkv * G + n;
+          const bool live = idx < n_items;
+          const uint16_t* rp = a.r + (static_cast<size_t>(b) * a.Hq + hh) * a.R;
+          const float* ep = a.E + static_cast<size_t>(hh) * a.R * a.bias_range + dd;
+#pragma unroll
+          for (int f = 0; f < 16; ++f) {
+            const bool ok = live && f < a.R;
+            e[u][f] = ok ? ep[static_cast<size_t>(f) * a.bias_range] : 0.f;
+            rr[u][f] = ok ? bf16_to_f32(rp[f]) : 0.f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float acc = 0.f;
+#pragma unroll
+          for (int f = 0; f < 16; ++f) acc = fmaf(rr[u][f], e[u][f], acc);
+          v[u] = acc;
+        }
       }
-      curve[idx] = v * kLog2e;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (base + 256 * u < n_items) curve[base + 256 * u] = v[u] * kLog2e;
     }
   }
   __syncthreads();
