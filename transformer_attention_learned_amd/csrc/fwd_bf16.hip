@@ -392,7 +392,9 @@ hipError_t launch_mode(const FwdArgs& a, int mode, hipStream_t s) {
 hipError_t launch_fwd_bf16(const FwdArgs& a0, int D, int mode, hipStream_t s) {
   const bool vec_ok = (reinterpret_cast<uintptr_t>(a0.table) & 15u) == 0 &&
                       (reinterpret_cast<uintptr_t>(a0.E) & 15u) == 0;
-  if (vec_ok && fwd_fast_lds_bytes(D, a0.G, mode, a0.bias_range, a0.R, a0.c_qk) >= 0)
+  // the fast path addresses K and V through 32-bit buffer offsets within one sequence
+  const bool off32 = static_cast<long long>(a0.S) * a0.Hkv * D * 2 < (1LL << 31);
+  if (vec_ok && off32 && fwd_fast_lds_bytes(D, a0.G, mode, a0.bias_range, a0.R, a0.c_qk) >= 0)
     return launch_fwd_bf16_fast(a0, mode, s);
   FwdArgs a = a0;
   a.hpw = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0 ? 2 : 1);

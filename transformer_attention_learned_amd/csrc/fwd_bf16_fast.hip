@@ -40,9 +40,8 @@
 #ifndef RBA_FORCE_GLOBAL_E
 #define RBA_FORCE_GLOBAL_E 0
 #endif
-#ifndef RBA_SCHED
-#define RBA_SCHED 0   // MFMA / VALU interleave pattern of the pipelined steps (0: compiler default)
-#endif
+
+#include <type_traits>
 
 #include "rba_device.h"
 #include "rba_internal.h"
@@ -88,7 +87,7 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: geometry stays scalar
   const int ln = lane & 31;
   const int lh = lane >> 5;
 
@@ -124,27 +123,29 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
   // row-major; V: 256 items of 4 keys x 8 dims, transposed.  With 256 threads each thread
   // takes 4 K chunks and one V item; with 512 threads half take K, half take V.
   u32x4 kreg[4], vreg[4];
-  const bool v_thread = (NT == 256) || (tid >= 256);
-  const bool k_thread = (NT == 256) || (tid < 256);
+  const bool v_thread = (NT == 256) || (wave >= 4);
+  const bool k_thread = (NT == 256) || (wave < 4);
   const int vt_id = tid & 255;
   const int v_kg = vt_id & 15;
   const int v_dg = vt_id >> 4;
+  // Byte offsets inside a tile; rows at or past S read as zeros through the buffer range
+  // (rows - r0) * row bytes - head offset, which every in-range 16-byte chunk fits below.
+  const int kv_row_b = a.Hkv * D * 2;
+  const int head_b = hkv * D * 2;
+  const int k_voff = (vt_id >> 4) * kv_row_b + 16 * (vt_id & 15);
+  const int v_voff = 4 * v_kg * kv_row_b + 16 * v_dg;
+  auto rows_rsrc = [&](const uint16_t* base, int r0) {
+    const int left = S - r0;
+    return make_rsrc(base + static_cast<size_t>(r0) * kv_row, left > 0 ? left * kv_row_b - head_b : 0);
+  };
   auto load_tile = [&](int tk0) {
     if (k_thread) {
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int key = tk0 + it * 16 + (vt_id >> 4);
-        kreg[it] = u32x4{0u, 0u, 0u, 0u};
-        if (key < S) kreg[it] = ld16(kbase + static_cast<size_t>(key) * kv_row + 8 * (vt_id & 15));
-      }
+      for (int it = 0; it < 4; ++it) kreg[it] = buf_ld16(rows_rsrc(kbase, tk0 + 16 * it), k_voff);
     }
     if (v_thread) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int key = tk0 + 4 * v_kg + s;
-        vreg[s] = u32x4{0u, 0u, 0u, 0u};
-        if (key < S) vreg[s] = ld16(vbase + static_cast<size_t>(key) * kv_row + 8 * v_dg);
-      }
+      for (int s = 0; s < 4; ++s) vreg[s] = buf_ld16(rows_rsrc(vbase, tk0 + s), v_voff);
     }
     if (QB == 2) {   // 1 wave per SIMD: park the staged tile in the accumulation registers
 #pragma unroll
@@ -292,8 +293,19 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
   const uint16_t* e2w = (MODE == 2) ? reinterpret_cast<const uint16_t*>(smem + bias_off) + (wave & 3) * Rb * EF : nullptr;
   uint16_t* ring = (MODE == 2) ? reinterpret_cast<uint16_t*>(smem + ring_off) + wave * (RING ? QB : 1) * 32 * RST : nullptr;
 
-  // Accumulator start values of step js for query block qb: bias / scale where the
-  // key is visible and in band, 0 where visible and beyond the band, -inf elsewhere.
+  // Whether step js of query block qb starts from something other than zero (bias in band,
+  // or a mask at the window / causal edges); uniform across the wave.
+  auto step_special = [&](int js, int qb) -> bool {
+    const int j0 = (t_begin + (js >> 1)) * BN + 32 * (js & 1);
+    const int c = (i0w + 32 * qb) - j0;
+    bool on = (c + 31 >= 0) && (j0 < S) && (i0w + 32 * qb < S);
+    if (W) on = on && (c - 31 < W);
+    const bool edge = !on || (c - 31 < 0) || (W && c + 31 >= W);
+    const bool inband = on && (MODE != 0) && (c - 31 < Rb);
+    return edge || inband;
+  };
+  // Accumulator start values of a special step: bias / scale where the key is visible and
+  // in band, 0 where visible and beyond the band, -inf elsewhere.
   auto step_init = [&](int js, int qb) -> f32x16 {
     f32x16 init;
 #pragma unroll
@@ -380,14 +392,23 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
   };
   // S^T of step js accumulated onto `acc`; the K fragment of chunk c+1 is read before
   // the MFMAs of chunk c.
-  auto step_scores = [&](int js, f32x16 (&acc)[QB]) {
+  // SPEC false: the step starts from the MFMA's zero operand (no start values in registers).
+  auto step_scores = [&](int js, f32x16 (&acc)[QB], auto spec_c) {
+    constexpr bool SPEC = decltype(spec_c)::value;
     bf16x8 kf = k_frag(js, 0);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       bf16x8 kn = kf;
       if (c + 1 < NC) kn = k_frag(js, c + 1);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) acc[qb] = mfma32(kf, qf[qb][c], acc[qb]);
+      for (int qb = 0; qb < QB; ++qb) {
+        if (c == 0 && !SPEC) {
+          const f32x16 zero = {};
+          acc[qb] = mfma32(kf, qf[qb][0], zero);
+        } else {
+          acc[qb] = mfma32(kf, qf[qb][c], acc[qb]);
+        }
+      }
       kf = kn;
     }
   };
@@ -458,93 +479,96 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
   if (ntiles > 1) load_tile((t_begin + 1) * BN);
   __syncthreads();
 
-  f32x16 sacc[QB];
-  {
+  using false_t = std::integral_constant<bool, false>;
+  using true_t = std::integral_constant<bool, true>;
+  // whether any query block of step js needs start values (the two stage-1 variants)
+  auto any_special = [&](int js) {
+    bool sp = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) sacc[qb] = step_init(0, qb);
-    step_scores(0, sacc);
+    for (int qb = 0; qb < QB; ++qb) sp = sp || step_special(js, qb);
+    return sp;
+  };
+
+  f32x16 sa[QB], sb[QB];
+  {
+    if (any_special(0)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sa[qb] = step_init(0, qb);
+      step_scores(0, sa, true_t{});
+    } else {
+      step_scores(0, sa, false_t{});
+    }
     float mx[QB];
-    step_rowmax(sacc, mx);
+    step_rowmax(sa, mx);
     rescale(mx);
   }
 
   // ---- steady state: two straight-line stages per 32-key step ----------------------------------
-  for (int js = 0; js + 1 < nsteps; ++js) {
+  // One iteration consumes the scores of step js (scur) and produces those of step js+1 (snxt);
+  // the loop is unrolled by two so that the two score sets swap roles without copies.
+  auto iteration = [&](int js, auto odd_c, f32x16 (&scur)[QB], f32x16 (&snxt)[QB]) {
+    constexpr bool ODD = decltype(odd_c)::value;
     const int tl = js >> 1;
-    if ((js & 1) == 0 && tl + 1 < ntiles) {
+    if (!ODD && tl + 1 < ntiles) {
       __syncthreads();                      // everyone is done with the buffer of tile tl-1
       store_tile((tl + 1) & 1);
       if (tl + 2 < ntiles) load_tile((t_begin + tl + 2) * BN);
     }
-    if ((js & 1) == 1 && tl + 1 < ntiles) __syncthreads();   // tile tl+1 is in LDS
+    if (ODD && tl + 1 < ntiles) __syncthreads();   // tile tl+1 is in LDS
 
-    f32x16 snext[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) snext[qb] = step_init(js + 1, qb);
     float m_use[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) m_use[qb] = (m_run[qb] == NEG_INF) ? 0.f : m_run[qb];
 
-    // stage 1: S MFMAs of step js+1 interleaved with the exp / pack of step js
+    // stage 1: S MFMAs of step js+1 interleaved with the exp / pack of step js, in a variant
+    // with start values (bias, masks) and one that starts from zero
     bf16x8 pf[QB][2];
-    step_scores(js + 1, snext);
-    step_probs(sacc, m_use, pf);
-#if RBA_SCHED == 1
+    // (the empty asm at the end of each variant keeps the compiler from merging their tails,
+    // which would pull the exp work out of the MFMA stream)
+    auto fence_stage1 = [&]() {
 #pragma unroll
-    for (int g = 0; g < NC; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);         // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x402, 6 * QB, 0);     // VALU / transcendental
+      for (int qb = 0; qb < QB; ++qb) {
+        asm volatile("" : "+v"(snxt[qb]));
+        asm volatile("" : "+v"(pf[qb][0]), "+v"(pf[qb][1]));
+      }
+    };
+    if (any_special(js + 1)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) snxt[qb] = step_init(js + 1, qb);
+      step_scores(js + 1, snxt, true_t{});
+      step_probs(scur, m_use, pf);
+      fence_stage1();
+    } else {
+      step_scores(js + 1, snxt, false_t{});
+      step_probs(scur, m_use, pf);
+      fence_stage1();
     }
-#elif RBA_SCHED == 2
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int g = 0; g < NC; ++g) {
-      if (g + 2 < NC) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 6 * QB, 0);
-    }
-#endif
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) asm volatile("" : "+v"(snext[qb]));
 
     // stage 2: P.V MFMAs of step js interleaved with the row max of step js+1
     float mx[QB];
     step_pv(js, pf);
-    step_rowmax(snext, mx);
-#if RBA_SCHED == 1
-#pragma unroll
-    for (int g = 0; g < 2 * NDB; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 3 * QB, 0);
-    }
-#elif RBA_SCHED == 2
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int g = 0; g < 2 * NDB; ++g) {
-      if (g + 2 < 2 * NDB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 3 * QB, 0);
-    }
-#endif
+    step_rowmax(snxt, mx);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(oacc[qb][db]));
 
     rescale(mx);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) sacc[qb] = snext[qb];
+  };
+  int js = 0;
+  for (; js + 2 < nsteps; js += 2) {        // nsteps is even: pairs, then one even step
+    iteration(js, false_t{}, sa, sb);
+    iteration(js + 1, true_t{}, sb, sa);
   }
+  iteration(js, false_t{}, sa, sb);
 
-  // ---- last step --------------------------------------------------------------------------------
+  // ---- last step (scores in sb) -------------------------------------------------------------------
   {
     float m_use[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) m_use[qb] = (m_run[qb] == NEG_INF) ? 0.f : m_run[qb];
     bf16x8 pf[QB][2];
-    step_probs(sacc, m_use, pf);
+    step_probs(sb, m_use, pf);
     step_pv(nsteps - 1, pf);
   }
 

@@ -44,6 +44,16 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 
+// Buffer resource over `bytes` bytes from `base` (raw, unswizzled): loads whose 16 bytes
+// lie past the end return zeros, so row guards need no branches.  The base must be uniform
+// across the wave.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
 // D = A * B + C on a 32x32 output tile, K = 16 bf16 (fp32 accumulate).
 // Lane l holds A row (l % 32) and B column (l % 32), 8 K-elements each; the
 // K-elements of the two operands are paired by (l / 32, element index), so any
