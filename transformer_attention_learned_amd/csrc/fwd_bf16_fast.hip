@@ -56,7 +56,9 @@ constexpr int NC = D / 16;        // K = 16 chunks of the head dim
 constexpr int NDB = D / 32;       // 32-wide head-dim blocks of O^T
 constexpr int KST = D + 8;        // K tile row stride (bf16)
 constexpr int VST = BN + 8;       // V^T tile row stride (bf16)
-constexpr int RST = 68;           // curve buffer row stride (bf16)
+constexpr int RST = 68;           // ring curve buffer row stride (bf16), E read from global memory
+constexpr int CBW = 72;           // curve buffer row stride (bf16), staged E: 64 slots + pad
+constexpr int PAD = 64;           // zero distances staged on each side of the bias range
 constexpr int ROWS_WG = 64;       // query rows per workgroup
 constexpr float kRescale = 8.f;   // lazy rescale threshold (log2 units)
 
@@ -64,6 +66,7 @@ constexpr int KS_BYTES = BN * KST * 2;
 constexpr int VT_BYTES = D * VST * 2;
 constexpr int BUF_BYTES = KS_BYTES + VT_BYTES;
 constexpr int RING_BYTES_PER_QB = 32 * RST * 2;
+constexpr int CURVE_BYTES_PER_QB = 32 * CBW * 2;
 
 // QB 32-row query blocks per wave; 8 / QB waves = 4 heads x (2 / QB) row halves.
 
@@ -220,20 +223,34 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
   }
 
   // ---- stage the group's bias parameters in LDS, in accumulator units (bias / scale) ------
+  // Rows in LDS are padded with PAD zero distances on both sides, so that every in-band step
+  // reads its distances c - 62 .. c + 63 without guards: zero below 0 (those keys are masked
+  // anyway) and at and beyond the range.
+  const int Rp = Rb + 2 * PAD;             // padded row length (distances -PAD .. Rb + PAD - 1)
   if (MODE == 1) {
-    // the 4 table rows of the group are contiguous in memory and in LDS: [hw][delta]
-    float4* tab4 = reinterpret_cast<float4*>(smem + bias_off);
+    float* tab = reinterpret_cast<float*>(smem + bias_off);
     const float4* src4 = reinterpret_cast<const float4*>(a.table + static_cast<size_t>(hg) * 4 * Rb);
-    for (int base = tid; base < Rb; base += 4 * NT) {
+    const int per_hw = Rb / 4;
+    for (int base = tid; base < 4 * per_hw; base += 4 * NT) {
       float4 v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (base + NT * u < Rb) v[u] = src4[base + NT * u];
+        if (base + NT * u < 4 * per_hw) v[u] = src4[base + NT * u];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (base + NT * u < Rb)
-          tab4[base + NT * u] = float4{v[u].x * inv_scale, v[u].y * inv_scale, v[u].z * inv_scale,
-                                        v[u].w * inv_scale};
+      for (int u = 0; u < 4; ++u) {
+        const int vi = base + NT * u;
+        if (vi < 4 * per_hw) {
+          const int hw = vi / per_hw;
+          const int q4 = vi - hw * per_hw;
+          *reinterpret_cast<float4*>(tab + hw * Rp + PAD + 4 * q4) =
+              float4{v[u].x * inv_scale, v[u].y * inv_scale, v[u].z * inv_scale, v[u].w * inv_scale};
+        }
+      }
+    }
+    for (int i = tid; i < 4 * 2 * PAD; i += NT) {
+      const int hw = i / (2 * PAD);
+      const int k = i - hw * 2 * PAD;
+      tab[hw * Rp + (k < PAD ? k : Rb + k)] = 0.f;
     }
   }
   if (MODE == 2 && ESTAGE) {
@@ -265,12 +282,21 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
         const int rr = vi - hw * per_hw;
         const int f = rr % EF;
         const int dq = rr / EF;
-        uint16_t* dst = e2 + (hw * Rb + 4 * dq) * EF + f;
+        uint16_t* dst = e2 + (hw * (Rp + 1) + PAD + 4 * dq) * EF + f;
         dst[0] = f32_to_bf16(v[u].x * inv_scale);
         dst[EF] = f32_to_bf16(v[u].y * inv_scale);
         dst[2 * EF] = f32_to_bf16(v[u].z * inv_scale);
         dst[3 * EF] = f32_to_bf16(v[u].w * inv_scale);
       }
+    }
+    // zero pads (one extra distance row at the end for the upper-half lanes' over-read)
+    uint32_t* e2u = reinterpret_cast<uint32_t*>(e2);
+    const int pad_words = (2 * PAD + 1) * EF / 2;
+    for (int i = tid; i < 4 * pad_words; i += NT) {
+      const int hw = i / pad_words;
+      const int k = i - hw * pad_words;
+      const int lo_words = PAD * EF / 2;
+      e2u[(hw * (Rp + 1)) * EF / 2 + (k < lo_words ? k : Rb * EF / 2 + k)] = 0u;
     }
   }
 
@@ -289,9 +315,18 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
   }
 
   const float NEG_INF = -INFINITY;
-  const float* tabw = (MODE == 1) ? reinterpret_cast<const float*>(smem + bias_off) + (wave & 3) * Rb : nullptr;
-  const uint16_t* e2w = (MODE == 2) ? reinterpret_cast<const uint16_t*>(smem + bias_off) + (wave & 3) * Rb * EF : nullptr;
-  uint16_t* ring = (MODE == 2) ? reinterpret_cast<uint16_t*>(smem + ring_off) + wave * (RING ? QB : 1) * 32 * RST : nullptr;
+  // v_perm selectors for the curve reads: bf16 number r (0..2) of a dword pair into the top
+  // half, zero bytes (selector 12) below; r = parity of the lane's row (+1 for sel_b)
+  auto perm_sel = [](int r) -> uint32_t {
+    return 0x0c0cu | (static_cast<uint32_t>(2 * r) << 16) | (static_cast<uint32_t>(2 * r + 1) << 24);
+  };
+  const uint32_t sel_a = perm_sel(ln & 1);
+  const uint32_t sel_b = perm_sel((ln & 1) + 1);
+  // the wave's head row at distance 0
+  const float* tabw = (MODE == 1) ? reinterpret_cast<const float*>(smem + bias_off) + (wave & 3) * Rp + PAD : nullptr;
+  const uint16_t* e2w = (MODE == 2) ? reinterpret_cast<const uint16_t*>(smem + bias_off) + ((wave & 3) * (Rp + 1) + PAD) * EF : nullptr;
+  uint16_t* ring = (MODE == 2) ? reinterpret_cast<uint16_t*>(smem + ring_off) +
+                                     wave * QB * 32 * (ESTAGE ? CBW : RST) : nullptr;
 
   // Whether step js of query block qb starts from something other than zero (bias in band,
   // or a mask at the window / causal edges); uniform across the wave.
@@ -318,23 +353,51 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
     const bool inband = on && (MODE != 0) && (c - 31 < Rb);
     if (MODE == 1 && inband) {
       asm volatile("; in-band step: table bias" ::: "memory");
+      // d = c + n - m with m = 8 g + 4 lh + j: one base per lane, immediate offsets 27 - 8 g - j
+      const float* tb = tabw + (c + ln - 4 * lh - 27);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = 8 * (i >> 2) + 4 * lh + (i & 3);
-        const int d = c + ln - m;
-        const float tv = tabw[min(max(d, 0), Rb - 1)];
-        init[i] = (d >= 0 && d < Rb) ? tv : 0.f;
-      }
+      for (int i = 0; i < 16; ++i) init[i] = tb[27 - 8 * (i >> 2) - (i & 3)];
     }
-    if (MODE == 2 && inband) {
+    if (MODE == 2 && ESTAGE && inband) {
+      asm volatile("; in-band step: r.E bias" ::: "memory");
+      // curves of the 64 distances c - 31 .. c + 32 for every query row of the block (two
+      // MFMAs over the R features), written unskewed: row n, column = distance - (c - 31)
+      uint16_t* cb = ring + (QB > 1 ? qb : 0) * 32 * CBW;
+      const uint16_t* ep = e2w + (c - 31 + ln) * EF + 8 * lh;
+      const f32x16 zero = {};
+      const f32x16 lo = mfma32(as_bf16x8(ld16(ep)), rf[qb], zero);
+      const f32x16 hi = mfma32(as_bf16x8(ld16(ep + 32 * EF)), rf[qb], zero);
+      uint16_t* wp = cb + ln * CBW + 4 * lh;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        st8(wp + 8 * k, u32x2{pack_bf16x2(lo[4 * k], lo[4 * k + 1]), pack_bf16x2(lo[4 * k + 2], lo[4 * k + 3])});
+        st8(wp + 32 + 8 * k, u32x2{pack_bf16x2(hi[4 * k], hi[4 * k + 1]), pack_bf16x2(hi[4 * k + 2], hi[4 * k + 3])});
+      }
+      wave_sync_lds();
+      // key m of lane n sits at column 31 + n - m: keys m0 .. m0 + 3 (m0 = 8 g + 4 lh) are the
+      // four columns from 28 + n - m0, which start on a 2-byte boundary for odd n.  Read the
+      // three dwords around them (dword accesses are always aligned) and let v_perm move each
+      // bf16 into the top half of an fp32 with zeros below: column 28 + n - m0 + k holds key
+      // m0 + 3 - k.
+      const uint32_t* rd = reinterpret_cast<const uint32_t*>(cb) + ln * (CBW / 2) + (ln >> 1) + 2 - 2 * lh;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const uint32_t d0 = rd[12 - 4 * g4], d1 = rd[13 - 4 * g4], d2 = rd[14 - 4 * g4];
+        init[4 * g4 + 3] = __uint_as_float(__builtin_amdgcn_perm(d1, d0, sel_a));
+        init[4 * g4 + 2] = __uint_as_float(__builtin_amdgcn_perm(d1, d0, sel_b));
+        init[4 * g4 + 1] = __uint_as_float(__builtin_amdgcn_perm(d2, d1, sel_a));
+        init[4 * g4 + 0] = __uint_as_float(__builtin_amdgcn_perm(d2, d1, sel_b));
+      }
+      wave_sync_lds();
+    }
+    if (MODE == 2 && !ESTAGE && inband) {
+      // E from global memory: ring of curve blocks, consecutive key blocks share one
       uint16_t* rg = ring + (RING ? qb : 0) * 32 * RST;
       const int gam = c >> 5;
       auto curve_block = [&](int beta) {
         const int dl = 32 * beta + 1 + ln;
         u32x4 ev = {0u, 0u, 0u, 0u};
-        if (ESTAGE) {
-          if ((EF == 16 || lh == 0) && dl >= 0 && dl < Rb) ev = ld16(e2w + dl * EF + 8 * lh);
-        } else if ((EF == 16 || lh == 0) && dl >= 0 && dl < Rb) {
+        if ((EF == 16 || lh == 0) && dl >= 0 && dl < Rb) {
           // E[h, f, dl] for f = 8 lh .. 8 lh + 7 (coalesced over the lanes' distances)
           const float* ep = a.E + (static_cast<size_t>(h) * a.R + 8 * lh) * Rb + dl;
           float e[8];
@@ -595,20 +658,20 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
 }
 
 int bias_bytes(int mode, int Rb, int R) {
-  if (mode == 1) return 4 * Rb * 4;
-  if (mode == 2) return 4 * Rb * (R > 8 ? 16 : 8) * 2;
+  if (mode == 1) return 4 * (Rb + 2 * PAD) * 4;
+  if (mode == 2) return 4 * (Rb + 2 * PAD + 1) * (R > 8 ? 16 : 8) * 2;
   return 0;
 }
 
-// one curve buffer per wave, or per (wave, query block) with the ring; 8 / QB waves
-int ring_bytes(int mode, bool ring, int QB) {
-  return mode == 2 ? (8 / QB) * (ring ? QB : 1) * RING_BYTES_PER_QB : 0;
+// curve buffers, one per (wave, query block): 8 in all
+int ring_bytes(int mode, bool estage) {
+  return mode == 2 ? 8 * (estage ? CURVE_BYTES_PER_QB : RING_BYTES_PER_QB) : 0;
 }
 
 constexpr int kMaxLds = 160 * 1024;
 
-int lds_total(int mode, int Rb, int R, bool ring, int QB, bool estage = true) {
-  return 2 * BUF_BYTES + (estage || mode != 2 ? bias_bytes(mode, Rb, R) : 0) + ring_bytes(mode, ring, QB);
+int lds_total(int mode, int Rb, int R, bool estage) {
+  return 2 * BUF_BYTES + (estage || mode != 2 ? bias_bytes(mode, Rb, R) : 0) + ring_bytes(mode, estage);
 }
 
 template <int MODE, int EF, bool RING, int QB, bool ESTAGE = true>
@@ -620,7 +683,7 @@ hipError_t launch_fast(FwdArgs a, hipStream_t s) {
   a.longest_first = (a.window == 0 || a.window > ROWS_WG) ? 1 : 0;
   const int bias_off = 2 * BUF_BYTES;
   const int ring_off = bias_off + ((MODE != 2 || ESTAGE) ? bias_bytes(MODE, a.bias_range, a.R) : 0);
-  const int total = ring_off + ring_bytes(MODE, RING, QB);
+  const int total = ring_off + ring_bytes(MODE, ESTAGE);
   const long long nblk = static_cast<long long>(a.n_qtiles) * a.n_hgroups * a.B;
   if (nblk <= 0) return hipSuccess;
   static bool attr_set = false;
@@ -641,8 +704,8 @@ hipError_t launch_fast(FwdArgs a, hipStream_t s) {
 int fwd_fast_lds_bytes(int D_, int G, int mode, int Rb, int R, float scale) {
   if (D_ != D || G % 4 != 0 || !(scale > 0.f)) return -1;
   if (mode != 0 && Rb % 4 != 0) return -1;
-  if (mode == 1 && lds_total(1, Rb, R, false, 1) > kMaxLds) return -1;
-  return lds_total(mode, Rb, R, false, 1, false);
+  if (mode == 1 && lds_total(1, Rb, R, true) > kMaxLds) return -1;
+  return lds_total(mode, Rb, R, mode != 2);
 }
 
 hipError_t launch_fwd_bf16_fast(const FwdArgs& a, int mode, hipStream_t s) {
@@ -652,9 +715,7 @@ hipError_t launch_fwd_bf16_fast(const FwdArgs& a, int mode, hipStream_t s) {
     case 0: return launch_fast<0, 8, false, 1>(a, s);
     case 1: return launch_fast<1, 8, false, 1>(a, s);
     default: {
-      const bool stage = !RBA_FORCE_GLOBAL_E && lds_total(2, a.bias_range, a.R, false, 1, true) <= kMaxLds;
-      // with one 32-row block per wave the ring costs no extra LDS: consecutive key blocks
-      // share a curve block
+      const bool stage = !RBA_FORCE_GLOBAL_E && lds_total(2, a.bias_range, a.R, true) <= kMaxLds;
       if (a.R > 8) return stage ? launch_fast<2, 16, true, 1, true>(a, s) : launch_fast<2, 16, true, 1, false>(a, s);
       return stage ? launch_fast<2, 8, true, 1, true>(a, s) : launch_fast<2, 8, true, 1, false>(a, s);
     }
