@@ -50,10 +50,15 @@ def visible_keys_decode(kv_len: int, window: int) -> int:
 
 
 def kernel_hash(kind: str) -> str:
+    """sha256 of the kernel sources with comments and blank lines removed (first 16 hex digits)."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kind] + ["rba_device.h", "rba_internal.h"]:
-        with open(os.path.join(ROOT, "transformer_attention_learned_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "transformer_attention_learned_amd", "csrc", name)) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        for line in text.splitlines():
+            code = re.sub(r"//.*", "", line).strip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -25,15 +25,14 @@
 //     mask start at zero;
 //   * online softmax with lazy rescaling: the running max only moves when a
 //     row's max grows by more than 2^8, so the O rescale is rare;
-//   * table bias: the group's table rows sit in LDS and are read at the
-//     distance in the steps that reach below the range;
-//   * input-dependent bias r_i . E[h, :, delta]: E (bf16) for the group's heads
-//     is staged in LDS once per workgroup; the curve of a 32x32 block over its
-//     63 distances is two 32-distance curve blocks (one MFMA each, K = the R
-//     features) written to a per-wave LDS buffer whose rows are skewed by the
-//     query index, so that the diagonal read delta = c + n - m is four
-//     contiguous values per 8-byte read; with the ring variant consecutive key
-//     blocks share one curve block;
+//   * table bias: the group's table rows sit in LDS, padded with zero distances on both sides,
+//     and each lane reads its 16 distances from one base with immediate offsets;
+//   * input-dependent bias r_i . E[h, :, delta]: E (bf16, zero-padded the same way) for the
+//     group's heads is staged in LDS once per workgroup; the curves of a 32x32 block over its
+//     64 distances are two MFMAs (K = the R features) stored unskewed to a per-wave buffer
+//     (row = query, column = distance), and each lane reads its diagonal delta = c + n - m with
+//     aligned dword reads and v_perm; when E does not fit in LDS the curve MFMA reads it from
+//     global memory and consecutive key blocks share curve blocks through a skewed ring;
 //   * steps outside the window are skipped by the mask; steps beyond the bias
 //     range are content-only (the NoPE tail of global layers).
 
