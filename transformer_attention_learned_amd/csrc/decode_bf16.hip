@@ -14,8 +14,8 @@
 //     heads of the kv head as B-operand columns;
 //   * V is staged in a wave-private LDS tile, transposed, and O^T = V^T P^T
 //     runs on the same MFMA with P kept in registers;
-//   * the bias curve of the workgroup's in-band distances (table row or r.E) is
-//     computed once into LDS; the key loop reads one value per in-band logit;
+//   * the bias curve of a tile's 32 distances (table row or r.E) is evaluated by its wave
+//     during the previous tile, into a wave-private LDS buffer read once per logit;
 //   * the 4 waves merge (max / sum-exp) through LDS; with several splits the
 //     workgroup writes an unnormalised partial that a second kernel combines.
 
@@ -28,11 +28,19 @@ namespace {
 
 constexpr int TK = 32;          // cache rows per tile (one 32x32 MFMA block)
 
+#ifndef RBA_DECODE_TARGET_WG
+#define RBA_DECODE_TARGET_WG 2048   // workgroups the split aims for
+#endif
+#ifndef RBA_DECODE_MIN_ROWS
+#define RBA_DECODE_MIN_ROWS 128     // fewest cache rows per wave
+#endif
+
 __device__ __forceinline__ int vt_pos(int x) {
   return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
-template <int D, int MODE>
+// RMAX: r.E features held per curve item (8 or 16; 1 for the table)
+template <int D, int MODE, int RMAX>
 __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int curve_off) {
   constexpr int VST = TK + 8;          // V^T row stride (bf16): 80-byte rows, 16-byte aligned
   constexpr int NC = D / 16;           // K = 16 chunks of the head dim
@@ -99,60 +107,77 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
     }
   }
   if (ntiles > 0) load_tile(w_beg);
-  // ---- bias curve of this workgroup's in-band distances, once, into LDS -------------------
-  // Rows [wg_beg, wg_end) carry a bias iff delta = qpos - key < bias_range; the curve of query
-  // head n at distance delta is table[h, delta] or sum_f r[b, h, f] E[h, f, delta] (log2 units).
-  float* curve = reinterpret_cast<float*>(smem + curve_off);
-  const int wg_beg = a.key_begin + split * 4 * a.keys_per_wave;
-  const int wg_end = min(a.kv_len, wg_beg + 4 * a.keys_per_wave);
-  const int d_lo = max(0, qpos - (wg_end - 1));                // smallest distance in the group
-  const int d_hi = min(a.bias_range, qpos - wg_beg + 1);       // one past the largest in band
-  const int n_curve = d_hi - d_lo;                             // <= 0: no bias in this group
-  if (MODE != 0 && n_curve > 0) {
-    // items (n, delta), 4 per thread per round with every load of a round issued together
-    const int n_items = G * n_curve;
-    for (int base = tid; base < n_items; base += 4 * 256) {
-      float v[4];
-      if (MODE == 1) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int idx = base + 256 * u;
-          const int n = idx / n_curve;
-          const int dd = d_lo + (idx - n * n_curve);
-          v[u] = (idx < n_items) ? a.table[static_cast<size_t>(hkv * G + n) * a.bias_range + dd] : 0.f;
-        }
-      } else {
-        float e[4][16], rr[4][16];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int idx = base + 256 * u;
-          const int n = idx / n_curve;
-          const int dd = d_lo + (idx - n * n_curve);
-          const int hh = hkv * G + n;
-          const bool live = idx < n_items;
-          const uint16_t* rp = a.r + (static_cast<size_t>(b) * a.Hq + hh) * a.R;
-          const float* ep = a.E + static_cast<size_t>(hh) * a.R * a.bias_range + dd;
-#pragma unroll
-          for (int f = 0; f < 16; ++f) {
-            const bool ok = live && f < a.R;
-            e[u][f] = ok ? ep[static_cast<size_t>(f) * a.bias_range] : 0.f;
-            rr[u][f] = ok ? bf16_to_f32(rp[f]) : 0.f;
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          float acc = 0.f;
-#pragma unroll
-          for (int f = 0; f < 16; ++f) acc = fmaf(rr[u][f], e[u][f], acc);
-          v[u] = acc;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (base + 256 * u < n_items) curve[base + 256 * u] = v[u] * kLog2e;
-    }
+
+  // ---- bias: each wave evaluates the curve of the next tile's 32 distances while the current
+  // tile is processed, into a wave-private pair of buffers [G][TK] (log2 units).  The curve of
+  // query head n at distance delta is table[h, delta] or sum_f r[b, h, f] E[h, f, delta]; it is
+  // zero at and beyond bias_range.  r is staged once per workgroup.
+  float* rs = reinterpret_cast<float*>(smem + curve_off);                  // [G][R] (r.E)
+  float* cbuf = rs + (MODE == 2 ? G * a.R : 0) + wave * 2 * G * TK;         // [2][G][TK]
+  if (MODE == 2) {
+    for (int i = tid; i < G * a.R; i += 256)
+      rs[i] = bf16_to_f32(a.r[(static_cast<size_t>(b) * a.Hq + hkv * G) * a.R + i]);
+    __syncthreads();
   }
-  __syncthreads();
+  // items (n, j) of a tile curve: head n < G, row j < TK; lane l takes items l, l + 64, ...
+  const int n_items = G * TK;
+  auto tile_in_band = [&](int tk0) { return MODE != 0 && qpos - (tk0 + TK - 1) < a.bias_range; };
+  // The first 128 items of a tile curve are fetched early (next to the tile's K/V loads) into
+  // registers and finished after the current tile; larger groups do the rest in place.
+  float epre[2][RMAX];
+  auto item_geo = [&](int tk0, int item, int& n, int& d, bool& live) {
+    n = item / TK;
+    const int j = item - n * TK;
+    d = qpos - (tk0 + j);
+    live = item < n_items && d >= 0 && d < a.bias_range && tk0 + j < w_end;
+    if (item >= n_items) n = 0;
+  };
+  auto fetch_items = [&](int tk0, int base, float (&e)[2][RMAX]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      int n, d;
+      bool live;
+      item_geo(tk0, base + lane + 64 * u, n, d, live);
+      const int hh = hkv * G + n;
+      if (MODE == 1) {
+        e[u][0] = live ? a.table[static_cast<size_t>(hh) * a.bias_range + d] : 0.f;
+      } else {
+        const float* ep = a.E + static_cast<size_t>(hh) * a.R * a.bias_range + (live ? d : 0);
+#pragma unroll
+        for (int f = 0; f < RMAX; ++f) e[u][f] = (live && f < a.R) ? ep[static_cast<size_t>(f) * a.bias_range] : 0.f;
+      }
+    }
+  };
+  auto finish_items = [&](int tk0, int base, const float (&e)[2][RMAX], float* dst) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int item = base + lane + 64 * u;
+      int n, d;
+      bool live;
+      item_geo(tk0, item, n, d, live);
+      float acc = 0.f;
+      if (MODE == 1) {
+        acc = e[u][0];
+      } else {
+#pragma unroll
+        for (int f = 0; f < RMAX; ++f)
+          if (f < a.R) acc = fmaf(rs[n * a.R + f], e[u][f], acc);
+      }
+      if (item < n_items) dst[item] = acc * kLog2e;
+    }
+  };
+  auto curve_finish = [&](int tk0, float* dst) {
+    finish_items(tk0, 0, epre, dst);
+    for (int base = 128; base < n_items; base += 128) {
+      float e[2][RMAX];
+      fetch_items(tk0, base, e);
+      finish_items(tk0, base, e, dst);
+    }
+  };
+  if (ntiles > 0 && tile_in_band(w_beg)) {
+    fetch_items(w_beg, 0, epre);
+    curve_finish(w_beg, cbuf);
+  }
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 oacc[NDB];
@@ -193,17 +218,18 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
     }
     // registers are free: the next tile's loads are now in flight during this tile's work
     if (t + 1 < ntiles) load_tile(tk0 + TK);
+    const bool next_band = t + 1 < ntiles && tile_in_band(tk0 + TK);
+    if (next_band) fetch_items(tk0 + TK, 0, epre);
 
-    // logits (log2 units), bias for the last bias_range rows, mask beyond this wave's rows
+    // logits (log2 units), bias of in-band rows, mask beyond this wave's rows
+    const bool in_band = tile_in_band(tk0);
+    const float* cv = cbuf + (t & 1) * G * TK + (col_live ? ln : 0) * TK + 4 * lh;
     float mx = NEG_INF;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = tk0 + 8 * (i >> 2) + 4 * lh + (i & 3);
       float sv = sacc[i] * a.c_qk;
-      if (MODE != 0) {
-        const int d = qpos - key;
-        if (d < a.bias_range && key < w_end && col_live) sv += curve[ln * n_curve + (d - d_lo)];
-      }
+      if (in_band) sv += cv[8 * (i >> 2) + (i & 3)];   // zero past the range and past the rows
       if (key >= w_end) sv = NEG_INF;
       sacc[i] = sv;
       mx = fmaxf(mx, sv);
@@ -243,6 +269,8 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
         const bf16x8 vf = as_bf16x8(ld16(vt + (32 * db + ln) * VST + 16 * kk + 8 * lh));
         oacc[db] = mfma32(vf, pf[kk], oacc[db]);
       }
+    // curve of the next tile into the other buffer (this tile's logits are done with theirs)
+    if (next_band) curve_finish(tk0 + TK, cbuf + ((t + 1) & 1) * G * TK);
   }
 
   // ---- merge the 4 waves through LDS (reusing the V^T area) ---------------------------
@@ -312,27 +340,23 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   if (d == 0 && a.lse) a.lse[bh] = (M + fast_log2(l)) * kLn2;
 }
 
-template <int D, int MODE>
+template <int D, int MODE, int RMAX>
 hipError_t launch_d(DecodeArgs a, hipStream_t s) {
   const dim3 grid(a.n_split, a.Hkv, a.B);
   constexpr int VT_ALL = 4 * D * (TK + 8) * 2;
   const int merge = 4 * a.G * (D + 2) * 4;
   const int curve_off = ((VT_ALL > merge ? VT_ALL : merge) + 15) / 16 * 16;
-  int n_curve_max = 0;
-  if (MODE != 0) {
-    const long long span = 4LL * a.keys_per_wave;   // rows of one workgroup
-    n_curve_max = static_cast<int>(span < a.bias_range ? span : a.bias_range);
-  }
-  const int total = curve_off + a.G * n_curve_max * 4;
+  // after the V^T tiles / merge buffer: r [G][R] (r.E), then per wave two tile curves [G][TK]
+  const int total = curve_off + (MODE == 2 ? a.G * a.R * 4 : 0) + (MODE != 0 ? 4 * 2 * a.G * TK * 4 : 0);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_bf16_kernel<D, MODE>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_bf16_kernel<D, MODE, RMAX>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   if (total > 160 * 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_bf16_kernel<D, MODE>), grid, dim3(256), total, s, a, curve_off);
+  hipLaunchKernelGGL((decode_bf16_kernel<D, MODE, RMAX>), grid, dim3(256), total, s, a, curve_off);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, s, a);
@@ -347,9 +371,9 @@ void decode_split(int B, int Hkv, int kv_len, int window, int* n_split, int* key
   const int key_begin = window ? (kv_len > window ? kv_len - window : 0) : 0;
   const long long n_vis = static_cast<long long>(kv_len) - key_begin;
   const long long pairs = static_cast<long long>(B) * Hkv;
-  const long long target_wg = 2048;
+  const long long target_wg = RBA_DECODE_TARGET_WG;
   long long ns = (target_wg + pairs - 1) / pairs;
-  const long long max_ns = (n_vis + 4 * 128 - 1) / (4 * 128);   // at least 128 rows per wave
+  const long long max_ns = (n_vis + 4 * RBA_DECODE_MIN_ROWS - 1) / (4 * RBA_DECODE_MIN_ROWS);   // rows per wave
   if (ns > max_ns) ns = max_ns;
   if (ns < 1) ns = 1;
   long long kpw = (n_vis + 4 * ns - 1) / (4 * ns);
@@ -364,15 +388,15 @@ void decode_split(int B, int Hkv, int kv_len, int window, int* n_split, int* key
 hipError_t launch_decode_bf16(DecodeArgs a, int D, int mode, hipStream_t s) {
   if (D == 128) {
     switch (mode) {
-      case 0: return launch_d<128, 0>(a, s);
-      case 1: return launch_d<128, 1>(a, s);
-      default: return launch_d<128, 2>(a, s);
+      case 0: return launch_d<128, 0, 1>(a, s);
+      case 1: return launch_d<128, 1, 1>(a, s);
+      default: return a.R > 8 ? launch_d<128, 2, 16>(a, s) : launch_d<128, 2, 8>(a, s);
     }
   }
   switch (mode) {
-    case 0: return launch_d<64, 0>(a, s);
-    case 1: return launch_d<64, 1>(a, s);
-    default: return launch_d<64, 2>(a, s);
+    case 0: return launch_d<64, 0, 1>(a, s);
+    case 1: return launch_d<64, 1, 1>(a, s);
+    default: return a.R > 8 ? launch_d<64, 2, 16>(a, s) : launch_d<64, 2, 8>(a, s);
   }
 }
 
