@@ -206,14 +206,17 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
+    # one event before every step and one after the last: the whole span gives ms_per_step, the
+    # gaps give the median and minimum step
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record()
+    for i in range(args.steps):
         step()
-    stop.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    timing = {"median_ms": round(per_step[len(per_step) // 2], 5), "min_ms": round(per_step[0], 5)}
 
     tflops = flops / (ms * 1e-3) / 1e12
     if w.kind == "prefill":
@@ -241,7 +244,7 @@ def main():
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": w.dtype, "data": "synthetic (seeded, drawn on the GPU)", "config": cfg,
-            "roofline": roof}
+            "timing": timing, "roofline": roof}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)

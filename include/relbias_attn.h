@@ -22,8 +22,12 @@
  *                   token's coefficients (output of the fourth projection,
  *                   "Inkling 975B MoE architecture deep dive", section "No RoPE?
  *                   No Problem?") weighting a bank of R learned distance curves
- *                   ("Thinking Machines dropped RoPE", steps 1-3).  A bank shared
- *                   by all heads is the case E[h] == E for every h.
+ *                   ("Thinking Machines dropped RoPE", steps 1-3).
+ *   RBA_BIAS_RPROJ_SHARED
+ *                   beta = sum_{f<R} r[token, h, f] * E[f, delta]: as RBA_BIAS_RPROJ
+ *                   with one bank of R curves used by every head of the layer, the
+ *                   form that essay's step 2 describes (one set of learned distance
+ *                   functions for all heads and tokens); E is [R, bias_range].
  *
  * Conventions shared by every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
@@ -56,7 +60,12 @@ extern "C" {
 
 typedef enum { RBA_OK = 0, RBA_EINVAL = 1, RBA_ENOTSUP = 2, RBA_EHIP = 3 } rba_status_t;
 typedef enum { RBA_F32 = 0, RBA_BF16 = 1 } rba_dtype_t;
-typedef enum { RBA_BIAS_NONE = 0, RBA_BIAS_TABLE = 1, RBA_BIAS_RPROJ = 2 } rba_bias_mode_t;
+typedef enum {
+  RBA_BIAS_NONE = 0,
+  RBA_BIAS_TABLE = 1,
+  RBA_BIAS_RPROJ = 2,
+  RBA_BIAS_RPROJ_SHARED = 3
+} rba_bias_mode_t;
 
 /*
  * Prefill: every token of B sequences of length S attends to its own
@@ -71,9 +80,10 @@ typedef enum { RBA_BIAS_NONE = 0, RBA_BIAS_TABLE = 1, RBA_BIAS_RPROJ = 2 } rba_b
  *   bias_range  bias applied iff 0 <= i-j < bias_range (ignored for RBA_BIAS_NONE).
  *   mode        rba_bias_mode_t.
  *   table       RBA_BIAS_TABLE: [Hq, bias_range] fp32; else ignored (may be NULL).
- *   r           RBA_BIAS_RPROJ: [B, S, Hq, R] of dtype; else ignored.
- *   E           RBA_BIAS_RPROJ: [Hq, R, bias_range] fp32; else ignored.
- *   R           RBA_BIAS_RPROJ: number of curves, 1..16.
+ *   r           RBA_BIAS_RPROJ(_SHARED): [B, S, Hq, R] of dtype; else ignored.
+ *   E           RBA_BIAS_RPROJ: [Hq, R, bias_range] fp32; RBA_BIAS_RPROJ_SHARED:
+ *               [R, bias_range] fp32; else ignored.
+ *   R           RBA_BIAS_RPROJ(_SHARED): number of curves, 1..16.
  *   scale       multiplier of q.k (typically 1/sqrt(D)); the bias is not scaled.
  *   stream      hipStream_t.
  */
@@ -97,7 +107,7 @@ size_t relbias_attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int kv_
  *   q           [B, Hq, D]
  *   k_cache     [B, L_max, Hkv, D]; v_cache the same.  1 <= kv_len <= L_max.
  *   o           [B, Hq, D] (written); lse [B, Hq] fp32 or NULL.
- *   r           RBA_BIAS_RPROJ: [B, Hq, R] of dtype (coefficients of the new token).
+ *   r           RBA_BIAS_RPROJ(_SHARED): [B, Hq, R] of dtype (coefficients of the new token).
  *   table, E, R, scale: as in relbias_attn_fwd.
  *   workspace   device scratch of at least relbias_attn_decode_workspace_size(...)
  *               bytes (may be NULL when that size is 0); contents on entry are

@@ -13,6 +13,7 @@ What it computes (plain definition, float64, no tiling, no online softmax):
     beta(h, i, delta) = 0                          if mode == NONE or delta >= bias_range
                       = table[h, delta]            if mode == TABLE
                       = sum_f r[b,i,h,f] E[h,f,delta]   if mode == RPROJ
+                      = sum_f r[b,i,h,f] E[f,delta]     if mode == RPROJ_SHARED
     s_ij = scale * <q[b,i,h,:], k[b,j,g,:]> + beta(h, i, delta_ij)
     o[b,i,h,:] = sum_{visible j} softmax_j(s_ij) v[b,j,g,:]
     lse[b,h,i] = log sum_{visible j} exp(s_ij)
@@ -41,8 +42,10 @@ Readings where the pages are silent or garbled (each is pinned by a test):
   * the bias applies for 0 <= delta < bias_range and is exactly 0 at
     delta == bias_range;
   * the table is causal only (no negative-offset half, no buckets);
-  * the bank E is per head ([Hq, R, bias_range]); the page's head-shared bank
-    is the special case E[h] == E for every h;
+  * the bank E is per head ([Hq, R, bias_range]) in mode RPROJ; mode
+    RPROJ_SHARED takes the essay's form, one bank [R, bias_range] that every
+    head reads (step 2 of the same essay: the learned distance functions are
+    common to all heads and tokens of the layer);
   * GQA: query head h reads kv head floor(h / G), G = Hq / Hkv.
 
 Inputs are taken as stored (bf16 / fp32 values upcast to float64).
@@ -55,9 +58,12 @@ import numpy as np
 MODE_NONE = 0
 MODE_TABLE = 1
 MODE_RPROJ = 2
+MODE_RPROJ_SHARED = 3
 
 _MODES = {"none": MODE_NONE, "table": MODE_TABLE, "rproj": MODE_RPROJ,
-          MODE_NONE: MODE_NONE, MODE_TABLE: MODE_TABLE, MODE_RPROJ: MODE_RPROJ}
+          "rproj_shared": MODE_RPROJ_SHARED,
+          MODE_NONE: MODE_NONE, MODE_TABLE: MODE_TABLE, MODE_RPROJ: MODE_RPROJ,
+          MODE_RPROJ_SHARED: MODE_RPROJ_SHARED}
 
 
 def _f64(x):
@@ -95,7 +101,9 @@ def bias_matrix(mode, qpos, kpos, bias_range, h, *, table=None, r_rows=None, E=N
     mode RPROJ: sum_f r_rows[i, f] * E[h, f, delta], i.e. the query token's
     curve read at the distance ("Thinking Machines dropped RoPE", steps 2-3 and
     the code listing).  r_rows is r[b, :, h, :] for the query rows, [Sq, R].
-    Both: zero for delta < 0 and delta >= bias_range (same essay, step 4).
+    mode RPROJ_SHARED: the same with one bank E [R, bias_range] for every head
+    (same essay, step 2).
+    All: zero for delta < 0 and delta >= bias_range (same essay, step 4).
     """
     mode = _MODES[mode]
     qpos = np.asarray(qpos, dtype=np.int64)
@@ -110,7 +118,8 @@ def bias_matrix(mode, qpos, kpos, bias_range, h, *, table=None, r_rows=None, E=N
         row = _f64(table)[h]                       # [bias_range]
         vals = row[idx]
     else:
-        curves = _f64(r_rows) @ _f64(E)[h]         # [Sq, R] @ [R, bias_range] -> [Sq, bias_range]
+        bank = _f64(E) if mode == MODE_RPROJ_SHARED else _f64(E)[h]   # [R, bias_range]
+        curves = _f64(r_rows) @ bank               # [Sq, R] @ [R, bias_range] -> [Sq, bias_range]
         vals = np.take_along_axis(curves, idx, axis=1)
     out[inband] = vals[inband]
     return out
@@ -120,8 +129,9 @@ def attention(q, k, v, *, qpos, kpos, scale, window=0, bias_range=0, mode="none"
               table=None, r=None, E=None, rows=None, row_block=512):
     """Plain definition of relative-position-bias attention, float64.
 
-    q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D]; r [B, Sq, Hq, R] (RPROJ);
-    table [Hq, bias_range] (TABLE); E [Hq, R, bias_range] (RPROJ).
+    q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D]; r [B, Sq, Hq, R] (RPROJ, RPROJ_SHARED);
+    table [Hq, bias_range] (TABLE); E [Hq, R, bias_range] (RPROJ) or
+    [R, bias_range] (RPROJ_SHARED).
     qpos [Sq], kpos [Sk]: integer token positions.
     rows: optional 1-D array of query-row indices to evaluate (others skipped).
     Returns (o [B, len(rows), Hq, D], lse [B, Hq, len(rows)]) in float64.
@@ -141,9 +151,10 @@ def attention(q, k, v, *, qpos, kpos, scale, window=0, bias_range=0, mode="none"
     qpos = np.asarray(qpos, dtype=np.int64)
     kpos = np.asarray(kpos, dtype=np.int64)
     rows = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
-    r64 = _f64(r) if mode == MODE_RPROJ else None
+    rproj = mode in (MODE_RPROJ, MODE_RPROJ_SHARED)
+    r64 = _f64(r) if rproj else None
     tab64 = _f64(table) if mode == MODE_TABLE else None
-    E64 = _f64(E) if mode == MODE_RPROJ else None
+    E64 = _f64(E) if rproj else None
     n = len(rows)
     o = np.zeros((B, n, Hq, D), dtype=np.float64)
     lse = np.zeros((B, Hq, n), dtype=np.float64)

@@ -62,6 +62,15 @@ def _dec(lib, **kw):
                                    a["scale"], a["ws"], a["wsb"], a["stream"])
 
 
+def test_mode_constants_match_header():
+    """The binding's mode numbers are the header's enum values."""
+    text = open(HEADER).read()
+    for name, value in (("RBA_BIAS_NONE", 0), ("RBA_BIAS_TABLE", 1), ("RBA_BIAS_RPROJ", 2),
+                        ("RBA_BIAS_RPROJ_SHARED", 3)):
+        assert re.search(rf"\b{name}\s*=\s*{value}\b", text), name
+    assert rba.MODES == {"none": 0, "table": 1, "rproj": 2, "rproj_shared": 3}
+
+
 @pytest.mark.parametrize("kw,code,needle", [
     (dict(dtype=7), EINVAL, "dtype"),
     (dict(Hq=6, Hkv=4), EINVAL, "multiple"),
@@ -76,6 +85,9 @@ def _dec(lib, **kw):
     (dict(mode=2, r=P, E=P, R=0), ENOTSUP, "R="),
     (dict(mode=2, r=None, E=P, R=8), EINVAL, "r and E"),
     (dict(mode=2, r=P, E=P + 2, R=8), EINVAL, "E is not"),
+    (dict(mode=3, r=P, E=P, R=17), ENOTSUP, "R="),
+    (dict(mode=3, r=P, E=None, R=8), EINVAL, "r and E"),
+    (dict(mode=4), EINVAL, "mode"),
     (dict(q=None), EINVAL, "non-NULL"),
     (dict(o=P + 8), EINVAL, "aligned"),
     (dict(B=-1), EINVAL, "B="),

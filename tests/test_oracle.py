@@ -114,6 +114,18 @@ def test_listing_worked_example():
             np.testing.assert_array_equal(beta, expected[h])
 
 
+def test_listing_worked_example_shared_bank():
+    """Mode rproj_shared takes the listing's single bank as it stands ([R, range], no head axis)."""
+    fx = json.load(open(os.path.join(GOLDEN, "listing_bias_4tok.json")))
+    rs = np.array(fx["relative_states"], dtype=np.float64)        # (T, H, C)
+    proj = np.array(fx["proj"], dtype=np.float64)                  # (C, R_dist)
+    expected = np.array(fx["expected_bias"], dtype=np.float64)     # (H, T, T)
+    pos = np.array(fx["positions"])
+    for h in range(rs.shape[1]):
+        beta = oracle.bias_matrix("rproj_shared", pos, pos, proj.shape[1], h, r_rows=rs[:, h, :], E=proj)
+        np.testing.assert_array_equal(beta, expected[h])
+
+
 def test_rproj_bias_through_sdpa_mask():
     """r.E bias + causal window, fed to torch SDPA as an additive mask, equals the oracle."""
     rng = _rng(7)
@@ -264,6 +276,8 @@ def _brute(q, k, v, qpos, kpos, scale, window, Rb, mode, table, r, E):
                     if mode != "none" and d < Rb:
                         if mode == "table":
                             s += table[h, d]
+                        elif mode == "rproj_shared":        # one bank E[f, d] for every head
+                            s += sum(r[b, i, h, f] * E[f, d] for f in range(E.shape[0]))
                         else:
                             s += sum(r[b, i, h, f] * E[h, f, d] for f in range(E.shape[1]))
                     scores.append(s)
@@ -278,7 +292,7 @@ def _brute(q, k, v, qpos, kpos, scale, window, Rb, mode, table, r, E):
 
 @pytest.mark.parametrize("seed,mode,W,Rb,G", [
     (s, m, W, Rb, G) for s, (m, W, Rb, G) in enumerate(itertools.product(
-        ["none", "table", "rproj"], [0, 1, 5], [1, 4, 40], [1, 3]))])
+        ["none", "table", "rproj", "rproj_shared"], [0, 1, 5], [1, 4, 40], [1, 3]))])
 def test_bruteforce_small(seed, mode, W, Rb, G):
     rng = _rng(100 + seed)
     B, S, Hkv, D, R = 2, 13, 1, 3, 2
@@ -288,7 +302,7 @@ def test_bruteforce_small(seed, mode, W, Rb, G):
     v = rng.standard_normal((B, S, Hkv, D))
     table = rng.standard_normal((Hq, Rb))
     r = rng.standard_normal((B, S, Hq, R))
-    E = rng.standard_normal((Hq, R, Rb))
+    E = rng.standard_normal((Hq, R, Rb) if mode != "rproj_shared" else (R, Rb))
     pos = np.arange(S) + 5
     o, lse = oracle.attention(q, k, v, qpos=pos, kpos=pos, scale=0.7, window=W, bias_range=Rb,
                               mode=mode, table=table, r=r, E=E)
@@ -297,7 +311,8 @@ def test_bruteforce_small(seed, mode, W, Rb, G):
     np.testing.assert_allclose(lse, lb, atol=1e-12)
 
 
-@pytest.mark.parametrize("mode,W,Rb", [("rproj", 0, 6), ("table", 7, 7), ("none", 4, 1)])
+@pytest.mark.parametrize("mode,W,Rb", [("rproj", 0, 6), ("table", 7, 7), ("none", 4, 1),
+                                       ("rproj_shared", 9, 5)])
 def test_decode_matches_bruteforce(mode, W, Rb):
     """Decode: one query at position kv_len-1 against cache rows [0, kv_len)."""
     rng = _rng(5)
@@ -306,7 +321,7 @@ def test_decode_matches_bruteforce(mode, W, Rb):
     kc = rng.standard_normal((B, Lmax, Hkv, D))
     vc = rng.standard_normal((B, Lmax, Hkv, D))
     r = rng.standard_normal((B, Hq, R))
-    E = rng.standard_normal((Hq, R, Rb))
+    E = rng.standard_normal((Hq, R, Rb) if mode != "rproj_shared" else (R, Rb))
     table = rng.standard_normal((Hq, Rb))
     o, lse = oracle.decode(q, kc, vc, L, scale=0.45, window=W, bias_range=Rb, mode=mode,
                            table=table, r=r, E=E)

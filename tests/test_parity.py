@@ -123,6 +123,11 @@ SWEEP = [
     dict(S=260, D=64), dict(S=260, D=64, mode="table", window=100),
     dict(S=129, R=3), dict(S=129, R=16), dict(S=129, R=11, window=50),
     dict(S=500, mode="rproj", window=96, bias_range=40, Hq=4, Hkv=4),
+    # one bank shared by every head, the essay's form: R = 16 curves, logits scaled by 1/d
+    dict(S=700, mode="rproj_shared", R=16, window=512, bias_range=512, Hq=8, Hkv=2,
+         logit_scale="inv_d"),
+    dict(S=1100, mode="rproj_shared", R=16, bias_range=1024, logit_scale="inv_d"),
+    dict(S=333, mode="rproj_shared", R=5, window=130, bias_range=77, D=64),
 ]
 
 
@@ -134,8 +139,10 @@ def test_prefill_small(kw):
 @pytest.mark.parametrize("kw", [dict(S=200, mode="table", bias_range=40, window=50),
                                 dict(S=130, mode="rproj", R=5, bias_range=30),
                                 dict(S=70, mode="none", Hq=4, Hkv=2, D=64),
-                                dict(S=3, mode="table", bias_range=2, D=128)],
-                         ids=["table", "rproj", "none_gqa", "tiny"])
+                                dict(S=3, mode="table", bias_range=2, D=128),
+                                dict(S=90, mode="rproj_shared", R=16, bias_range=33, window=60,
+                                     logit_scale="inv_d")],
+                         ids=["table", "rproj", "none_gqa", "tiny", "rproj_shared"])
 def test_prefill_f32_small(kw):
     check_prefill(small(dtype="f32", rmsnorm_qk=False, **kw))
 
@@ -225,6 +232,9 @@ DEC_SWEEP = [
     dict(S=6000, kv_len=4100, bias_range=1024), dict(S=600, kv_len=600, mode="table", bias_range=70),
     dict(S=9000, kv_len=8191, mode="none", Hq=8, Hkv=8), dict(S=300, kv_len=260, Hq=16, Hkv=2, D=64),
     dict(S=3000, kv_len=2500, R=13, Hq=4, Hkv=4, window=700, bias_range=300),
+    dict(S=3000, kv_len=2600, mode="rproj_shared", R=16, window=512, bias_range=512,
+         logit_scale="inv_d"),
+    dict(S=5000, kv_len=4500, mode="rproj_shared", R=8, bias_range=1024, Hq=32, Hkv=8),
 ]
 
 
@@ -238,8 +248,9 @@ def test_decode_small(kw):
     check_decode(w, kv_len)
 
 
-@pytest.mark.parametrize("kw", [dict(mode="rproj", window=0), dict(mode="table", window=20)],
-                         ids=["rproj", "table_window"])
+@pytest.mark.parametrize("kw", [dict(mode="rproj", window=0), dict(mode="table", window=20),
+                                dict(mode="rproj_shared", window=40, logit_scale="inv_d")],
+                         ids=["rproj", "table_window", "rproj_shared"])
 def test_decode_f32_small(kw):
     w = Workload(name="dec_f32", kind="decode", dtype="f32", B=2, Hq=4, Hkv=2, D=64, S=300,
                  bias_range=50, R=4, seed=3, **kw)

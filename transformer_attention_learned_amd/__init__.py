@@ -9,8 +9,9 @@ device memory and streams.  If the library is not built, every call raises.
   decode(q, k_cache, v_cache, kv_len, ...)  one new token per sequence
   decode_workspace_size(...)             scratch bytes decode needs
 
-Bias modes: "none", "table" (table [Hq, bias_range] fp32) and "rproj"
-(r [.., Hq, R] in the activation dtype, E [Hq, R, bias_range] fp32).
+Bias modes: "none", "table" (table [Hq, bias_range] fp32), "rproj"
+(r [.., Hq, R] in the activation dtype, E [Hq, R, bias_range] fp32) and
+"rproj_shared" (the same r, one bank E [R, bias_range] for every head).
 """
 
 from __future__ import annotations
@@ -25,7 +26,7 @@ __all__ = ["fwd", "decode", "decode_workspace_size", "last_error", "version", "l
 
 RBA_OK, RBA_EINVAL, RBA_ENOTSUP, RBA_EHIP = 0, 1, 2, 3
 RBA_F32, RBA_BF16 = 0, 1
-MODES = {"none": 0, "table": 1, "rproj": 2}
+MODES = {"none": 0, "table": 1, "rproj": 2, "rproj_shared": 3}
 
 _LIB = None
 
@@ -118,12 +119,12 @@ def _bias_args(mode, table, r, E, Hq, act_dtype, dev):
         if table is None:
             raise ValueError("mode 'table' needs table [Hq, bias_range]")
         _check(table, "table", dtype=torch.float32, ndim=2, device=dev)
-    elif m == 2:
+    elif m in (2, 3):
         if r is None or E is None:
-            raise ValueError("mode 'rproj' needs r and E")
-        _check(E, "E", dtype=torch.float32, ndim=3, device=dev)
+            raise ValueError("rproj modes need r and E")
+        _check(E, "E", dtype=torch.float32, ndim=3 if m == 2 else 2, device=dev)
         _check(r, "r", dtype=act_dtype, device=dev)
-        R = int(E.shape[1])
+        R = int(E.shape[1] if m == 2 else E.shape[0])
         if r.shape[-1] != R or r.shape[-2] != Hq:
             raise ValueError(f"r must end in [Hq={Hq}, R={R}], got {tuple(r.shape)}")
     return m, R
@@ -147,7 +148,7 @@ def fwd(q, k, v, *, window=0, bias_range=0, mode="none", table=None, r=None, E=N
     if tuple(k.shape) != (B, S, Hkv, D) or tuple(v.shape) != (B, S, Hkv, D):
         raise ValueError(f"k/v must be [B,S,Hkv,D] = {(B, S, Hkv, D)}")
     m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev)
-    if m == 2 and tuple(r.shape) != (B, S, Hq, R):
+    if m in (2, 3) and tuple(r.shape) != (B, S, Hq, R):
         raise ValueError(f"r must be [B,S,Hq,R] = {(B, S, Hq, R)}")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -159,8 +160,8 @@ def fwd(q, k, v, *, window=0, bias_range=0, mode="none", table=None, r=None, E=N
     _check(lse, "lse", dtype=torch.float32, device=dev)
     st = lib.relbias_attn_fwd(_dtype_id(q), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                               B, S, Hq, Hkv, D, int(window), int(bias_range), m,
-                              _ptr(table if m == 1 else None), _ptr(r if m == 2 else None),
-                              _ptr(E if m == 2 else None), R, float(scale),
+                              _ptr(table if m == 1 else None), _ptr(r if m in (2, 3) else None),
+                              _ptr(E if m in (2, 3) else None), R, float(scale),
                               _stream_handle(dev, stream))
     if st != RBA_OK:
         raise LibraryError(st, last_error())
@@ -191,7 +192,7 @@ def decode(q, k_cache, v_cache, kv_len, *, window=0, bias_range=0, mode="none", 
     if tuple(k_cache.shape) != (B, L_max, Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("k_cache/v_cache must be [B,L_max,Hkv,D] matching q")
     m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev)
-    if m == 2 and tuple(r.shape) != (B, Hq, R):
+    if m in (2, 3) and tuple(r.shape) != (B, Hq, R):
         raise ValueError(f"r must be [B,Hq,R] = {(B, Hq, R)}")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -206,7 +207,7 @@ def decode(q, k_cache, v_cache, kv_len, *, window=0, bias_range=0, mode="none", 
     st = lib.relbias_attn_decode(_dtype_id(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
                                  _ptr(lse), B, L_max, int(kv_len), Hq, Hkv, D, int(window),
                                  int(bias_range), m, _ptr(table if m == 1 else None),
-                                 _ptr(r if m == 2 else None), _ptr(E if m == 2 else None), R,
+                                 _ptr(r if m in (2, 3) else None), _ptr(E if m in (2, 3) else None), R,
                                  float(scale), _ptr(workspace), wbytes,
                                  _stream_handle(dev, stream))
     if st != RBA_OK:

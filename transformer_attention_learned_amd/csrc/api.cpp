@@ -44,7 +44,8 @@ int check_common(const char* fn, int dtype, int Hq, int Hkv, int D, int window, 
   if (Hq < 1 || Hkv < 1) return fail(RBA_EINVAL, "%s: Hq=%d and Hkv=%d must be >= 1", fn, Hq, Hkv);
   if (Hq % Hkv) return fail(RBA_EINVAL, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
   if (window < 0) return fail(RBA_EINVAL, "%s: window=%d must be >= 0 (0 = full causal)", fn, window);
-  if (mode != RBA_BIAS_NONE && mode != RBA_BIAS_TABLE && mode != RBA_BIAS_RPROJ)
+  if (mode != RBA_BIAS_NONE && mode != RBA_BIAS_TABLE && mode != RBA_BIAS_RPROJ &&
+      mode != RBA_BIAS_RPROJ_SHARED)
     return fail(RBA_EINVAL, "%s: unknown bias mode %d", fn, mode);
   if (!std::isfinite(scale)) return fail(RBA_EINVAL, "%s: scale is not finite", fn);
   if (dtype == RBA_BF16 && D != 64 && D != 128)
@@ -60,7 +61,7 @@ int check_common(const char* fn, int dtype, int Hq, int Hkv, int D, int window, 
     if (!table) return fail(RBA_EINVAL, "%s: table mode needs a table pointer", fn);
     if (!aligned_to(table, 4)) return fail(RBA_EINVAL, "%s: table is not 4-byte aligned", fn);
   }
-  if (mode == RBA_BIAS_RPROJ) {
+  if (mode == RBA_BIAS_RPROJ || mode == RBA_BIAS_RPROJ_SHARED) {
     if (R < 1 || R > 16) return fail(RBA_ENOTSUP, "%s: R=%d outside 1..16", fn, R);
     if (!r || !E) return fail(RBA_EINVAL, "%s: rproj mode needs r and E pointers", fn);
     if (!aligned_to(E, 4)) return fail(RBA_EINVAL, "%s: E is not 4-byte aligned", fn);
@@ -68,6 +69,13 @@ int check_common(const char* fn, int dtype, int Hq, int Hkv, int D, int window, 
   }
   return RBA_OK;
 }
+
+// The kernels know three bias modes; the shared bank is r.E with a head stride of 0 for E.
+int kernel_mode(int mode) { return mode == RBA_BIAS_RPROJ_SHARED ? RBA_BIAS_RPROJ : mode; }
+long long e_head_stride(int mode, int R, int bias_range) {
+  return mode == RBA_BIAS_RPROJ ? static_cast<long long>(R) * bias_range : 0;
+}
+bool is_rproj(int mode) { return mode == RBA_BIAS_RPROJ || mode == RBA_BIAS_RPROJ_SHARED; }
 
 }  // namespace
 
@@ -118,9 +126,10 @@ int relbias_attn_fwd(int dtype, const void* q, const void* k, const void* v, voi
     a.G = G;
     a.window = window;
     a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
-    a.R = mode == RBA_BIAS_RPROJ ? R : 0;
+    a.R = is_rproj(mode) ? R : 0;
+    a.e_hs = e_head_stride(mode, R, bias_range);
     a.c_qk = scale * rba::kLog2e;
-    e = rba::launch_fwd_bf16(a, D, mode, hs);
+    e = rba::launch_fwd_bf16(a, D, kernel_mode(mode), hs);
   } else {
     rba::F32Args a{};
     a.q = static_cast<const float*>(q);
@@ -142,8 +151,9 @@ int relbias_attn_fwd(int dtype, const void* q, const void* k, const void* v, voi
     a.q_pos0 = 0;
     a.window = window;
     a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
-    a.mode = mode;
-    a.R = mode == RBA_BIAS_RPROJ ? R : 0;
+    a.mode = kernel_mode(mode);
+    a.R = is_rproj(mode) ? R : 0;
+    a.e_hs = e_head_stride(mode, R, bias_range);
     a.scale = scale;
     e = rba::launch_attn_f32(a, hs);
   }
@@ -209,12 +219,13 @@ int relbias_attn_decode(int dtype, const void* q, const void* k_cache, const voi
     a.G = G;
     a.window = window;
     a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
-    a.R = mode == RBA_BIAS_RPROJ ? R : 0;
+    a.R = is_rproj(mode) ? R : 0;
+    a.e_hs = e_head_stride(mode, R, bias_range);
     a.key_begin = window ? (kv_len > window ? kv_len - window : 0) : 0;
     a.n_split = ns;
     a.keys_per_wave = kpw;
     a.c_qk = scale * rba::kLog2e;
-    e = rba::launch_decode_bf16(a, D, mode, hs);
+    e = rba::launch_decode_bf16(a, D, kernel_mode(mode), hs);
   } else {
     rba::F32Args a{};
     a.q = static_cast<const float*>(q);
@@ -236,8 +247,9 @@ int relbias_attn_decode(int dtype, const void* q, const void* k_cache, const voi
     a.q_pos0 = kv_len - 1;
     a.window = window;
     a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
-    a.mode = mode;
-    a.R = mode == RBA_BIAS_RPROJ ? R : 0;
+    a.mode = kernel_mode(mode);
+    a.R = is_rproj(mode) ? R : 0;
+    a.e_hs = e_head_stride(mode, R, bias_range);
     a.scale = scale;
     e = rba::launch_attn_f32(a, hs);
   }

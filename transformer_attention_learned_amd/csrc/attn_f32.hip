@@ -80,7 +80,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Args a) {
         if (a.mode == 1) {
           s += a.table[static_cast<size_t>(h) * a.bias_range + delta];
         } else {
-          const float* Eh = a.E + static_cast<size_t>(h) * a.R * a.bias_range + delta;
+          const float* Eh = a.E + static_cast<size_t>(h) * a.e_hs + delta;
           float bsum = 0.f;
 #pragma unroll
           for (int f = 0; f < 16; ++f)

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
       if (MODE == 1) {
         e[u][0] = live ? a.table[static_cast<size_t>(hh) * a.bias_range + d] : 0.f;
       } else {
-        const float* ep = a.E + static_cast<size_t>(hh) * a.R * a.bias_range + (live ? d : 0);
+        const float* ep = a.E + static_cast<size_t>(hh) * a.e_hs + (live ? d : 0);
 #pragma unroll
         for (int f = 0; f < RMAX; ++f) e[u][f] = (live && f < a.R) ? ep[static_cast<size_t>(f) * a.bias_range] : 0.f;
       }

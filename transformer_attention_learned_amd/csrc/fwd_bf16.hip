@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(FwdArgs 
   const float NEG_INF = -INFINITY;
   float* cs = Cs + (MODE == 2 ? wave * 32 * CST : 0);
   const float* tab = (MODE == 1) ? a.table + static_cast<size_t>(h) * a.bias_range : nullptr;
-  const float* Eh = (MODE == 2) ? a.E + static_cast<size_t>(h) * a.R * a.bias_range : nullptr;
+  const float* Eh = (MODE == 2) ? a.E + static_cast<size_t>(h) * a.e_hs : nullptr;
 
   for (int t = t_begin; t <= t_end; ++t) {
     const int tk0 = t * BN;

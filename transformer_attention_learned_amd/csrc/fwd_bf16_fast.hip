@@ -257,7 +257,7 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
     // that 8 neighbouring lanes fill one 16-byte row e2[(hw, d)][0..7] (2-way bank conflicts)
     uint16_t* e2 = reinterpret_cast<uint16_t*>(smem + bias_off);
     const int R = a.R;
-    const float* Eg = a.E + static_cast<size_t>(hg) * 4 * R * Rb;
+    const float* Eg = a.E + static_cast<size_t>(hg) * 4 * a.e_hs;
     const int per_hw = EF * Rb / 4;          // float4 items per head
     const int nvec = 4 * per_hw;
     for (int base = tid; base < nvec; base += 4 * NT) {
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
         const int dq = rr / EF;
         v[u] = float4{0.f, 0.f, 0.f, 0.f};
         if (vi < nvec && f < R)
-          v[u] = reinterpret_cast<const float4*>(Eg + (static_cast<size_t>(hw) * R + f) * Rb)[dq];
+          v[u] = reinterpret_cast<const float4*>(Eg + static_cast<size_t>(hw) * a.e_hs + static_cast<size_t>(f) * Rb)[dq];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
         u32x4 ev = {0u, 0u, 0u, 0u};
         if ((EF == 16 || lh == 0) && dl >= 0 && dl < Rb) {
           // E[h, f, dl] for f = 8 lh .. 8 lh + 7 (coalesced over the lanes' distances)
-          const float* ep = a.E + (static_cast<size_t>(h) * a.R + 8 * lh) * Rb + dl;
+          const float* ep = a.E + static_cast<size_t>(h) * a.e_hs + static_cast<size_t>(8 * lh) * Rb + dl;
           float e[8];
 #pragma unroll
           for (int f = 0; f < 8; ++f) e[f] = (8 * lh + f < a.R) ? ep[static_cast<size_t>(f) * Rb] * inv_scale : 0.f;

@@ -20,7 +20,8 @@ struct FwdArgs {
   float* lse;
   const float* table;   // [Hq, bias_range]
   const uint16_t* r;    // [B, S, Hq, R]
-  const float* E;       // [Hq, R, bias_range]
+  const float* E;       // [Hq, R, bias_range], head h at E + h * e_hs
+  long long e_hs;       // head stride of E in floats (R * bias_range, or 0 for one shared bank)
   int B, S, Hq, Hkv, G;
   int window;           // 0 = full causal
   int bias_range;
@@ -44,6 +45,7 @@ struct F32Args {
   const float* table;
   const float* r;       // [B, Sq, Hq, R]
   const float* E;
+  long long e_hs;       // head stride of E in floats (0: one bank for all heads)
   int B, Sq, Hq, Hkv, G, D;
   int kv_rows;          // row count of the k/v buffers per batch entry (L_max or S)
   int Lk;               // keys 0..Lk-1 exist
@@ -62,6 +64,7 @@ struct DecodeArgs {
   const float* table;
   const uint16_t* r;    // [B, Hq, R]
   const float* E;
+  long long e_hs;       // head stride of E in floats (0: one bank for all heads)
   float* ws;            // partials [B, Hq, n_part, D + 2] (unnormalised acc, m, l) or null
   int B, L_max, kv_len, Hq, Hkv, G;
   int window, bias_range, R;

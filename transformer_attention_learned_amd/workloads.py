@@ -28,7 +28,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-MODE_IDS = {"none": 0, "table": 1, "rproj": 2}
+MODE_IDS = {"none": 0, "table": 1, "rproj": 2, "rproj_shared": 3}
 
 
 @dataclass(frozen=True)
@@ -43,18 +43,19 @@ class Workload:
     S: int                    # prefill sequence length, or decode cache length (kv_len)
     window: int               # 0 = full causal
     bias_range: int
-    mode: str                 # "none" | "table" | "rproj"
+    mode: str                 # "none" | "table" | "rproj" | "rproj_shared"
     R: int = 8
     seed: int = 0
     rmsnorm_qk: bool = False
     table_std: float = 0.5
     table_trend: float = 0.0  # added to table[h, delta]: trend * delta
     e_std: float = 0.1
+    logit_scale: str = "rsqrt_d"   # "rsqrt_d": 1/sqrt(D); "inv_d": 1/D (the essay's Inkling form)
     extra: dict = field(default_factory=dict)
 
     @property
     def scale(self) -> float:
-        return 1.0 / math.sqrt(self.D)
+        return 1.0 / self.D if self.logit_scale == "inv_d" else 1.0 / math.sqrt(self.D)
 
     @property
     def torch_dtype(self):
@@ -117,7 +118,8 @@ def make_inputs(w: Workload, device="cpu", seed=None):
 
     Prefill returns q [B,S,Hq,D], k/v [B,S,Hkv,D], r [B,S,Hq,R] (rproj);
     decode returns q [B,Hq,D], k/v caches [B,S,Hkv,D], r [B,Hq,R].
-    table [Hq, bias_range] fp32 (table mode), E [Hq, R, bias_range] fp32 (rproj).
+    table [Hq, bias_range] fp32 (table mode), E [Hq, R, bias_range] fp32 (rproj) or
+    [R, bias_range] (rproj_shared: one bank for every head).
     """
     gen = torch.Generator(device=device)
     gen.manual_seed(w.seed if seed is None else seed)
@@ -148,9 +150,9 @@ def make_inputs(w: Workload, device="cpu", seed=None):
             t = t + w.table_trend * torch.arange(w.bias_range, device=device,
                                                  dtype=torch.float32)[None, :]
         table = t.contiguous()
-    elif w.mode == "rproj":
-        E = (torch.randn((w.Hq, w.R, w.bias_range), generator=gen, device=device,
-                         dtype=torch.float32) * w.e_std).contiguous()
+    elif w.mode in ("rproj", "rproj_shared"):
+        eshape = (w.Hq, w.R, w.bias_range) if w.mode == "rproj" else (w.R, w.bias_range)
+        E = (torch.randn(eshape, generator=gen, device=device, dtype=torch.float32) * w.e_std).contiguous()
         r = torch.randn(rshape, generator=gen, device=device, dtype=torch.float32).to(dt)
     return dict(q=q, k=k, v=v, table=table, E=E, r=r)
 
