@@ -177,6 +177,54 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
     }
   };
 
+  // ---- bias parameters: the first round of their loads (L2-resident) goes out before the
+  // HBM loads of the first tile and the query rows, so that converting them into LDS does not
+  // wait for those (loads complete in issue order)
+  const int Rp = Rb + 2 * PAD;             // padded row length (distances -PAD .. Rb + PAD - 1)
+  constexpr int PRE = 8;                   // float4 loads per thread in the first round
+  const int n_pvec = (MODE == 1) ? Rb : (MODE == 2 && ESTAGE) ? EF * Rb : 0;   // float4 per group
+  const int per_hw = (MODE == 1) ? Rb / 4 : EF * Rb / 4;                        // float4 per head
+  const float* Eg = (MODE == 2) ? a.E + static_cast<size_t>(hg) * 4 * a.e_hs : nullptr;
+  auto pfetch = [&](int vi) -> float4 {    // float4 number vi of the group's bias parameters
+    if (MODE == 1)
+      return reinterpret_cast<const float4*>(a.table + static_cast<size_t>(hg) * 4 * Rb)[vi];
+    // E[h, f, 4q .. 4q+3]; the feature index varies fastest over the lanes so that 8
+    // neighbouring lanes fill one 16-byte row e2[(hw, d)][0..7] (2-way bank conflicts)
+    const int hw = vi / per_hw;
+    const int rr = vi - hw * per_hw;
+    const int f = rr % EF;
+    const int dq = rr / EF;
+    if (f >= a.R) return float4{0.f, 0.f, 0.f, 0.f};
+    return reinterpret_cast<const float4*>(Eg + static_cast<size_t>(hw) * a.e_hs + static_cast<size_t>(f) * Rb)[dq];
+  };
+  auto pstore = [&](int vi, float4 v) {    // scaled to accumulator units, into LDS
+    const int hw = vi / per_hw;
+    const int rr = vi - hw * per_hw;
+    if (MODE == 1) {
+      float* tab = reinterpret_cast<float*>(smem + bias_off);
+      *reinterpret_cast<float4*>(tab + hw * Rp + PAD + 4 * rr) =
+          float4{v.x * inv_scale, v.y * inv_scale, v.z * inv_scale, v.w * inv_scale};
+    } else {
+      uint16_t* e2 = reinterpret_cast<uint16_t*>(smem + bias_off);
+      const int f = rr % EF;
+      const int dq = rr / EF;
+      uint16_t* dst = e2 + (hw * (Rp + 1) + PAD + 4 * dq) * EF + f;
+      dst[0] = f32_to_bf16(v.x * inv_scale);
+      dst[EF] = f32_to_bf16(v.y * inv_scale);
+      dst[2 * EF] = f32_to_bf16(v.z * inv_scale);
+      dst[3 * EF] = f32_to_bf16(v.w * inv_scale);
+    }
+  };
+  float4 pre[PRE];
+  if (n_pvec > 0) {
+#pragma unroll
+    for (int u = 0; u < PRE; ++u) {
+      const int vi = tid + NT * u;
+      pre[u] = float4{0.f, 0.f, 0.f, 0.f};
+      if (vi < n_pvec) pre[u] = pfetch(vi);
+    }
+  }
+
   // first tile in flight while the bias parameters are staged
   load_tile(t_begin * BN);
 
@@ -225,27 +273,22 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
   // Rows in LDS are padded with PAD zero distances on both sides, so that every in-band step
   // reads its distances c - 62 .. c + 63 without guards: zero below 0 (those keys are masked
   // anyway) and at and beyond the range.
-  const int Rp = Rb + 2 * PAD;             // padded row length (distances -PAD .. Rb + PAD - 1)
+  if (n_pvec > 0) {
+#pragma unroll
+    for (int u = 0; u < PRE; ++u)
+      if (tid + NT * u < n_pvec) pstore(tid + NT * u, pre[u]);
+    for (int base = tid + NT * PRE; base < n_pvec; base += NT * PRE) {   // larger ranges
+      float4 v[PRE];
+#pragma unroll
+      for (int u = 0; u < PRE; ++u)
+        if (base + NT * u < n_pvec) v[u] = pfetch(base + NT * u);
+#pragma unroll
+      for (int u = 0; u < PRE; ++u)
+        if (base + NT * u < n_pvec) pstore(base + NT * u, v[u]);
+    }
+  }
   if (MODE == 1) {
     float* tab = reinterpret_cast<float*>(smem + bias_off);
-    const float4* src4 = reinterpret_cast<const float4*>(a.table + static_cast<size_t>(hg) * 4 * Rb);
-    const int per_hw = Rb / 4;
-    for (int base = tid; base < 4 * per_hw; base += 4 * NT) {
-      float4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (base + NT * u < 4 * per_hw) v[u] = src4[base + NT * u];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int vi = base + NT * u;
-        if (vi < 4 * per_hw) {
-          const int hw = vi / per_hw;
-          const int q4 = vi - hw * per_hw;
-          *reinterpret_cast<float4*>(tab + hw * Rp + PAD + 4 * q4) =
-              float4{v[u].x * inv_scale, v[u].y * inv_scale, v[u].z * inv_scale, v[u].w * inv_scale};
-        }
-      }
-    }
     for (int i = tid; i < 4 * 2 * PAD; i += NT) {
       const int hw = i / (2 * PAD);
       const int k = i - hw * 2 * PAD;
@@ -253,43 +296,8 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
     }
   }
   if (MODE == 2 && ESTAGE) {
-    // float4 loads of E[h, f, 4q .. 4q+3]; the feature index varies fastest over the lanes so
-    // that 8 neighbouring lanes fill one 16-byte row e2[(hw, d)][0..7] (2-way bank conflicts)
-    uint16_t* e2 = reinterpret_cast<uint16_t*>(smem + bias_off);
-    const int R = a.R;
-    const float* Eg = a.E + static_cast<size_t>(hg) * 4 * a.e_hs;
-    const int per_hw = EF * Rb / 4;          // float4 items per head
-    const int nvec = 4 * per_hw;
-    for (int base = tid; base < nvec; base += 4 * NT) {
-      float4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int vi = base + NT * u;
-        const int hw = vi / per_hw;
-        const int rr = vi - hw * per_hw;
-        const int f = rr % EF;
-        const int dq = rr / EF;
-        v[u] = float4{0.f, 0.f, 0.f, 0.f};
-        if (vi < nvec && f < R)
-          v[u] = reinterpret_cast<const float4*>(Eg + static_cast<size_t>(hw) * a.e_hs + static_cast<size_t>(f) * Rb)[dq];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int vi = base + NT * u;
-        if (vi >= nvec) continue;
-        const int hw = vi / per_hw;
-        const int rr = vi - hw * per_hw;
-        const int f = rr % EF;
-        const int dq = rr / EF;
-        uint16_t* dst = e2 + (hw * (Rp + 1) + PAD + 4 * dq) * EF + f;
-        dst[0] = f32_to_bf16(v[u].x * inv_scale);
-        dst[EF] = f32_to_bf16(v[u].y * inv_scale);
-        dst[2 * EF] = f32_to_bf16(v[u].z * inv_scale);
-        dst[3 * EF] = f32_to_bf16(v[u].w * inv_scale);
-      }
-    }
     // zero pads (one extra distance row at the end for the upper-half lanes' over-read)
-    uint32_t* e2u = reinterpret_cast<uint32_t*>(e2);
+    uint32_t* e2u = reinterpret_cast<uint32_t*>(smem + bias_off);
     const int pad_words = (2 * PAD + 1) * EF / 2;
     for (int i = tid; i < 4 * pad_words; i += NT) {
       const int hw = i / pad_words;
