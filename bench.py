@@ -10,7 +10,8 @@ prefill kernel and the float64 oracle timed on this host as a CPU baseline.
                   [--no-cpu-baseline] [--cpu-seconds T]
 
 Other workloads (--workload): global_prefill, long_global_prefill,
-decode_global, decode_local, tiny_local_f32.
+decode_global, decode_local, tiny_local_f32, and decode_global_paged /
+decode_local_paged (the decode steps over a paged cache, 64-row pages).
 """
 
 from __future__ import annotations
@@ -190,12 +191,26 @@ def main():
         kv_lens = [w.S - j * w.window for j in range(4)] if (w.window and 4 * w.window <= w.S) else [w.S]
         it = [0]
 
-        def step():
-            kv_len = kv_lens[it[0] % len(kv_lens)]
-            it[0] += 1
-            rba.decode(inp["q"], inp["k"], inp["v"], kv_len, window=w.window,
-                       bias_range=w.bias_range, mode=w.mode, table=inp["table"], r=inp["r"],
-                       E=inp["E"], scale=w.scale, out=out, workspace=ws)
+        if w.extra.get("page_size"):
+            # paged cache: the table scatters each sequence over a page pool; every sequence
+            # has the step's cache length
+            from transformer_attention_learned_amd.workloads import paged_view
+            kp, vp, bt = paged_view(w, inp["k"], inp["v"])
+            lens_t = [torch.full((w.B,), L, dtype=torch.int32, device=dev) for L in kv_lens]
+
+            def step():
+                j = it[0] % len(kv_lens)
+                it[0] += 1
+                rba.decode_paged(inp["q"], kp, vp, bt, lens_t[j], kv_lens[j], window=w.window,
+                                 bias_range=w.bias_range, mode=w.mode, table=inp["table"],
+                                 r=inp["r"], E=inp["E"], scale=w.scale, out=out, workspace=ws)
+        else:
+            def step():
+                kv_len = kv_lens[it[0] % len(kv_lens)]
+                it[0] += 1
+                rba.decode(inp["q"], inp["k"], inp["v"], kv_len, window=w.window,
+                           bias_range=w.bias_range, mode=w.mode, table=inp["table"], r=inp["r"],
+                           E=inp["E"], scale=w.scale, out=out, workspace=ws)
 
         nvis = visible_keys_decode(w.S, w.window)
         flops = 4.0 * w.D * w.Hq * w.B * nvis
@@ -240,6 +255,8 @@ def main():
            "useful_gflop_per_step": round(flops / 1e9, 4), "tokens_per_step": tokens,
            "tokens_per_s": round(tokens / (ms * 1e-3), 1), "tflops": round(tflops, 3),
            "parallelism": "single-gpu"}
+    if w.extra.get("page_size"):
+        cfg["page_size"] = w.extra["page_size"]
     line = {"metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

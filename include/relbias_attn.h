@@ -120,6 +120,46 @@ int relbias_attn_decode(int dtype, const void* q, const void* k_cache, const voi
                         const float* E, int R, float scale, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/*
+ * Bytes of device workspace relbias_attn_decode_paged needs (0 when none): the
+ * launch is sized for max_kv_len, so this is the contiguous size at that length.
+ */
+size_t relbias_attn_decode_paged_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len,
+                                                int window);
+
+/*
+ * Single-token decode against a paged KV cache with a cache length per sequence,
+ * two of the shapes a fused-bias attention kernel has to cover ("Thinking Machines
+ * dropped RoPE", the paragraphs on the kernel cost of the bias, which list paged
+ * KV and variable sequence lengths among them).  Per sequence b it computes exactly
+ * what relbias_attn_decode computes with kv_len = kv_lens[b] over the logical
+ * cache whose row j is row (j % page_size) of page block_table[b][j / page_size].
+ *
+ *   q           [B, Hq, D]; o [B, Hq, D] (written); lse [B, Hq] fp32 or NULL.
+ *   k_pages     [num_pages, page_size, Hkv, D] of dtype: the pool of key pages;
+ *               v_pages the same for values.  Pages may be shared or in any order.
+ *   block_table DEVICE int32 [B, max_pages]: page of each sequence's logical page.
+ *   kv_lens     DEVICE int32 [B]: cache length of each sequence, 1..max_kv_len;
+ *               the query sits at position kv_lens[b] - 1.
+ *   max_kv_len  host upper bound of every kv_lens[b] (sizes the launch);
+ *               1 <= max_kv_len <= max_pages * page_size.
+ *   page_size   rows per page, a multiple of 16.
+ *   window, bias_range, mode, table, r ([B, Hq, R]), E, R, scale: as in
+ *               relbias_attn_decode.
+ *   workspace   at least relbias_attn_decode_paged_workspace_size(...) bytes
+ *               (may be NULL when that size is 0).
+ * The device values are not validated: lengths are clamped to [0, max_kv_len] and
+ * page indices to [0, num_pages), so wrong values give wrong results but no
+ * access outside the given buffers; kv_lens[b] = 0 leaves o[b] undefined.
+ * Supported: dtype RBA_BF16 with D in {64, 128} (RBA_ENOTSUP otherwise).
+ */
+int relbias_attn_decode_paged(int dtype, const void* q, const void* k_pages, const void* v_pages,
+                              const int* block_table, const int* kv_lens, void* o, float* lse,
+                              int B, int num_pages, int page_size, int max_pages, int max_kv_len,
+                              int Hq, int Hkv, int D, int window, int bias_range, int mode,
+                              const float* table, const void* r, const float* E, int R,
+                              float scale, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message for the calling thread's last non-OK status ("" if none).  The pointer
  * stays valid until the next call on the same thread. */
 const char* relbias_attn_last_error(void);

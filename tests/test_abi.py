@@ -34,7 +34,8 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == {"relbias_attn_fwd", "relbias_attn_decode",
-                          "relbias_attn_decode_workspace_size", "relbias_attn_last_error",
+                          "relbias_attn_decode_workspace_size", "relbias_attn_decode_paged",
+                          "relbias_attn_decode_paged_workspace_size", "relbias_attn_last_error",
                           "relbias_attn_version"}
     for n in names:
         assert hasattr(lib, n), n
@@ -138,3 +139,44 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(rba, "library_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         rba.load_library()
+
+
+def _paged(lib, **kw):
+    a = dict(dtype=BF16, q=P, kp=P, vp=P, bt=P, lens=P, o=P, lse=None, B=2, num_pages=8,
+             page_size=32, max_pages=4, max_kv_len=100, Hq=8, Hkv=2, D=128, window=0,
+             bias_range=8, mode=0, table=None, r=None, E=None, R=0, scale=0.1, ws=None, wsb=0,
+             stream=None)
+    a.update(kw)
+    return lib.relbias_attn_decode_paged(
+        a["dtype"], a["q"], a["kp"], a["vp"], a["bt"], a["lens"], a["o"], a["lse"], a["B"],
+        a["num_pages"], a["page_size"], a["max_pages"], a["max_kv_len"], a["Hq"], a["Hkv"], a["D"],
+        a["window"], a["bias_range"], a["mode"], a["table"], a["r"], a["E"], a["R"], a["scale"],
+        a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(dtype=F32, D=64), ENOTSUP, "bf16 only"),
+    (dict(page_size=24), ENOTSUP, "page_size"),
+    (dict(page_size=0), ENOTSUP, "page_size"),
+    (dict(max_kv_len=129), EINVAL, "max_kv_len"),
+    (dict(max_kv_len=0), EINVAL, "max_kv_len"),
+    (dict(num_pages=0), EINVAL, "num_pages"),
+    (dict(bt=None), EINVAL, "non-NULL"),
+    (dict(lens=None), EINVAL, "non-NULL"),
+    (dict(bt=P + 2), EINVAL, "4-byte"),
+    (dict(kp=P + 8), EINVAL, "aligned"),
+    (dict(Hq=66, Hkv=1), ENOTSUP, "Hq/Hkv"),
+    (dict(mode=2, r=P, E=P, R=0), ENOTSUP, "R="),
+    (dict(B=-1), EINVAL, "B="),
+])
+def test_decode_paged_rejects(lib, kw, code, needle):
+    assert _paged(lib, **kw) == code
+    assert needle in rba.last_error()
+
+
+def test_decode_paged_empty_and_workspace(lib):
+    assert _paged(lib, B=0) == 0
+    # the paged launch is sized for max_kv_len: same scratch as a contiguous cache of that length
+    for args in [(64, 32, 8, 128, 65536, 0), (64, 32, 8, 128, 65536, 512), (1, 4, 1, 64, 100, 0)]:
+        assert (lib.relbias_attn_decode_paged_workspace_size(*args)
+                == lib.relbias_attn_decode_workspace_size(*args))

@@ -8,6 +8,8 @@ device memory and streams.  If the library is not built, every call raises.
   fwd(q, k, v, ...)                      prefill, q [B,S,Hq,D], k/v [B,S,Hkv,D]
   decode(q, k_cache, v_cache, kv_len, ...)  one new token per sequence
   decode_workspace_size(...)             scratch bytes decode needs
+  decode_paged(q, k_pages, v_pages, block_table, kv_lens, max_kv_len, ...)
+                                         decode over a paged cache, one length per sequence
 
 Bias modes: "none", "table" (table [Hq, bias_range] fp32), "rproj"
 (r [.., Hq, R] in the activation dtype, E [Hq, R, bias_range] fp32) and
@@ -20,7 +22,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "decode", "decode_workspace_size", "last_error", "version", "library_path",
+__all__ = ["fwd", "decode", "decode_paged", "decode_workspace_size", "last_error", "version", "library_path",
            "load_library", "RBA_OK", "RBA_EINVAL", "RBA_ENOTSUP", "RBA_EHIP", "MODES",
            "LibraryError"]
 
@@ -63,6 +65,11 @@ def load_library():
     lib.relbias_attn_decode.restype = i
     lib.relbias_attn_decode_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.relbias_attn_decode_workspace_size.restype = sz
+    lib.relbias_attn_decode_paged.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
+                                              i, i, i, vp, vp, vp, i, f, vp, sz, vp]
+    lib.relbias_attn_decode_paged.restype = i
+    lib.relbias_attn_decode_paged_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.relbias_attn_decode_paged_workspace_size.restype = sz
     lib.relbias_attn_last_error.argtypes = []
     lib.relbias_attn_last_error.restype = ctypes.c_char_p
     lib.relbias_attn_version.argtypes = []
@@ -210,6 +217,53 @@ def decode(q, k_cache, v_cache, kv_len, *, window=0, bias_range=0, mode="none", 
                                  _ptr(r if m in (2, 3) else None), _ptr(E if m in (2, 3) else None), R,
                                  float(scale), _ptr(workspace), wbytes,
                                  _stream_handle(dev, stream))
+    if st != RBA_OK:
+        raise LibraryError(st, last_error())
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, kv_lens, max_kv_len, *, window=0,
+                 bias_range=0, mode="none", table=None, r=None, E=None, scale=None, out=None,
+                 lse=None, workspace=None, return_lse=False, stream=None):
+    """One decode step over a paged cache (relbias_attn_decode_paged).
+
+    q [B,Hq,D] bf16; k_pages/v_pages [num_pages, page_size, Hkv, D]; block_table int32
+    [B, max_pages] and kv_lens int32 [B] on the device; max_kv_len: host bound of kv_lens.
+    Sequence b's row j is row j % page_size of page block_table[b, j // page_size].
+    """
+    import torch
+    lib = load_library()
+    dev = q.device
+    _check(q, "q", ndim=3)
+    _check(k_pages, "k_pages", dtype=q.dtype, ndim=4, device=dev)
+    _check(v_pages, "v_pages", dtype=q.dtype, ndim=4, device=dev)
+    _check(block_table, "block_table", dtype=torch.int32, ndim=2, device=dev)
+    _check(kv_lens, "kv_lens", dtype=torch.int32, ndim=1, device=dev)
+    B, Hq, D = q.shape
+    num_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if tuple(k_pages.shape) != (num_pages, page_size, Hkv, D) or v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages/v_pages must be [num_pages, page_size, Hkv, D] matching q")
+    if block_table.shape[0] != B or kv_lens.shape[0] != B:
+        raise ValueError("block_table [B, max_pages] and kv_lens [B] must match q's batch")
+    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev)
+    if m in (2, 3) and tuple(r.shape) != (B, Hq, R):
+        raise ValueError(f"r must be [B,Hq,R] = {(B, Hq, R)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = lib.relbias_attn_decode_paged_workspace_size(B, Hq, Hkv, D, int(max_kv_len), int(window))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.relbias_attn_decode_paged(
+        _dtype_id(q), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(kv_lens),
+        _ptr(out), _ptr(lse), B, num_pages, page_size, int(block_table.shape[1]), int(max_kv_len),
+        Hq, Hkv, D, int(window), int(bias_range), m, _ptr(table if m == 1 else None),
+        _ptr(r if m in (2, 3) else None), _ptr(E if m in (2, 3) else None), R, float(scale),
+        _ptr(workspace), wbytes, _stream_handle(dev, stream))
     if st != RBA_OK:
         raise LibraryError(st, last_error())
     return (out, lse) if (return_lse or lse is not None) else out

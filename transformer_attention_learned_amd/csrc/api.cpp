@@ -257,4 +257,83 @@ int relbias_attn_decode(int dtype, const void* q, const void* k_cache, const voi
   return ok();
 }
 
+size_t relbias_attn_decode_paged_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len,
+                                                int window) {
+  return relbias_attn_decode_workspace_size(B, Hq, Hkv, D, max_kv_len, window);
+}
+
+int relbias_attn_decode_paged(int dtype, const void* q, const void* k_pages, const void* v_pages,
+                              const int* block_table, const int* kv_lens, void* o, float* lse,
+                              int B, int num_pages, int page_size, int max_pages, int max_kv_len,
+                              int Hq, int Hkv, int D, int window, int bias_range, int mode,
+                              const float* table, const void* r, const float* E, int R,
+                              float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "relbias_attn_decode_paged";
+  if (B < 0) return fail(RBA_EINVAL, "%s: B=%d must be >= 0", fn, B);
+  int st = check_common(fn, dtype, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale);
+  if (st != RBA_OK) return st;
+  if (B == 0) return ok();
+  if (dtype != RBA_BF16) return fail(RBA_ENOTSUP, "%s: paged caches are supported for bf16 only", fn);
+  if (page_size < 16 || page_size % 16)
+    return fail(RBA_ENOTSUP, "%s: page_size=%d must be a positive multiple of 16", fn, page_size);
+  if (num_pages < 1 || max_pages < 1)
+    return fail(RBA_EINVAL, "%s: num_pages=%d and max_pages=%d must be >= 1", fn, num_pages, max_pages);
+  if (max_kv_len < 1 || static_cast<long long>(max_kv_len) > static_cast<long long>(max_pages) * page_size)
+    return fail(RBA_EINVAL, "%s: need 1 <= max_kv_len (%d) <= max_pages * page_size (%lld)", fn,
+                max_kv_len, static_cast<long long>(max_pages) * page_size);
+  if (static_cast<long long>(num_pages) * page_size >= (1LL << 31))
+    return fail(RBA_ENOTSUP, "%s: page pool too large (rows must fit in int32)", fn);
+  if (!q || !k_pages || !v_pages || !o || !block_table || !kv_lens)
+    return fail(RBA_EINVAL, "%s: q, k_pages, v_pages, block_table, kv_lens and o must be non-NULL", fn);
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o))
+    return fail(RBA_EINVAL, "%s: q, page pools and o must be 16-byte aligned", fn);
+  if (!aligned_to(block_table, 4) || !aligned_to(kv_lens, 4))
+    return fail(RBA_EINVAL, "%s: block_table and kv_lens must be 4-byte aligned", fn);
+  if (lse && !aligned_to(lse, 4)) return fail(RBA_EINVAL, "%s: lse is not 4-byte aligned", fn);
+  const int G = Hq / Hkv;
+  if (G > 32) return fail(RBA_ENOTSUP, "%s: bf16 decode supports Hq/Hkv <= 32, got %d", fn, G);
+  int ns = 1, kpw = 64;
+  rba::decode_split(B, Hkv, max_kv_len, window, &ns, &kpw);
+  const size_t need = relbias_attn_decode_paged_workspace_size(B, Hq, Hkv, D, max_kv_len, window);
+  if (need > 0) {
+    if (!workspace) return fail(RBA_EINVAL, "%s: workspace of %zu bytes required, got NULL", fn, need);
+    if (workspace_bytes < need)
+      return fail(RBA_EINVAL, "%s: workspace too small (%zu < %zu bytes)", fn, workspace_bytes, need);
+    if (!aligned_to(workspace, 4)) return fail(RBA_EINVAL, "%s: workspace is not 4-byte aligned", fn);
+  }
+  if (Hkv > 65535 || B > 65535) return fail(RBA_ENOTSUP, "%s: grid too large", fn);
+  rba::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_pages);
+  a.v = static_cast<const uint16_t*>(v_pages);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.table = table;
+  a.r = static_cast<const uint16_t*>(r);
+  a.E = E;
+  a.ws = static_cast<float*>(workspace);
+  a.B = B;
+  a.L_max = 0;
+  a.kv_len = max_kv_len;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.window = window;
+  a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
+  a.R = is_rproj(mode) ? R : 0;
+  a.e_hs = e_head_stride(mode, R, bias_range);
+  a.key_begin = 0;              // per sequence, from kv_lens
+  a.n_split = ns;
+  a.keys_per_wave = kpw;
+  a.c_qk = scale * rba::kLog2e;
+  a.block_table = block_table;
+  a.kv_lens = kv_lens;
+  a.page_size = page_size;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  hipError_t e = rba::launch_decode_bf16(a, D, kernel_mode(mode), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

@@ -63,20 +63,33 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
   const bool col_live = ln < G;
 
   const size_t kv_row = static_cast<size_t>(a.Hkv) * D;
-  const uint16_t* kbase = a.k + static_cast<size_t>(b) * a.L_max * kv_row + static_cast<size_t>(hkv) * D;
-  const uint16_t* vbase = a.v + static_cast<size_t>(b) * a.L_max * kv_row + static_cast<size_t>(hkv) * D;
-  const int qpos = a.kv_len - 1;
+  const bool paged = a.block_table != nullptr;
+  // this sequence's cache length (paged: per sequence, clamped to the bound the launch was
+  // sized for) and first visible row
+  const int kv_len = paged ? min(max(a.kv_lens[b], 0), a.kv_len) : a.kv_len;
+  const int key_begin = paged ? (a.window ? max(0, kv_len - a.window) : 0) : a.key_begin;
+  const uint16_t* kbase = a.k + static_cast<size_t>(hkv) * D + (paged ? 0 : static_cast<size_t>(b) * a.L_max * kv_row);
+  const uint16_t* vbase = a.v + static_cast<size_t>(hkv) * D + (paged ? 0 : static_cast<size_t>(b) * a.L_max * kv_row);
+  const int* bt = paged ? a.block_table + static_cast<size_t>(b) * a.max_pages : nullptr;
+  // pool row of cache row `key` of this sequence (paged), page index clamped into the pool
+  auto pool_row = [&](int key) -> int {
+    const int pg = min(max(bt[key / a.page_size], 0), a.num_pages - 1);
+    return pg * a.page_size + key % a.page_size;
+  };
+  const int qpos = kv_len - 1;
 
   // This wave's rows.
-  const int w_beg = a.key_begin + (split * 4 + wave) * a.keys_per_wave;
-  const int w_end = min(a.kv_len, w_beg + a.keys_per_wave);
+  const int w_beg = key_begin + (split * 4 + wave) * a.keys_per_wave;
+  const int w_end = min(kv_len, w_beg + a.keys_per_wave);
   const int ntiles = w_end > w_beg ? (w_end - w_beg + TK - 1) / TK : 0;
 
   // ---- registers of the tile in flight: K as MFMA A-operand fragments, V as row pieces ---
   u32x4 kreg[NC], vreg[NVI][4];
   auto load_tile = [&](int tk0) {
     const int key = tk0 + ln;
-    const uint16_t* kp = kbase + static_cast<size_t>(key) * kv_row + 8 * lh;
+    // paged: one table read per lane (its K row); the V rows take theirs from the K lanes
+    const int prow = paged ? (key < w_end ? pool_row(key) : 0) : key;
+    const uint16_t* kp = kbase + static_cast<size_t>(prow) * kv_row + 8 * lh;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       kreg[c] = u32x4{0u, 0u, 0u, 0u};
@@ -90,8 +103,9 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int kk = tk0 + 4 * kg + s;
+        const int vrow = paged ? __shfl(prow, 4 * kg + s, 64) : kk;
         vreg[it][s] = u32x4{0u, 0u, 0u, 0u};
-        if (kk < w_end) vreg[it][s] = ld16(vbase + static_cast<size_t>(kk) * kv_row + 8 * dg);
+        if (kk < w_end) vreg[it][s] = ld16(vbase + static_cast<size_t>(vrow) * kv_row + 8 * dg);
       }
     }
   };

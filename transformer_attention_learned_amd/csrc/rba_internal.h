@@ -68,7 +68,13 @@ struct DecodeArgs {
   float* ws;            // partials [B, Hq, n_part, D + 2] (unnormalised acc, m, l) or null
   int B, L_max, kv_len, Hq, Hkv, G;
   int window, bias_range, R;
-  int key_begin;        // first visible key (kv_len - window, clamped at 0)
+  int key_begin;        // first visible key (kv_len - window, clamped at 0); per sequence when paged
+  // paged cache: k/v are page pools [num_pages, page_size, Hkv, D]; row j of sequence b lives
+  // in page block_table[b * max_pages + j / page_size] at slot j % page_size; the cache length
+  // of sequence b is kv_lens[b] (kv_len is then the upper bound the split was sized for)
+  const int* block_table;   // null: contiguous caches [B, L_max, Hkv, D]
+  const int* kv_lens;
+  int page_size, max_pages, num_pages;
   int n_split;          // workgroups per (b, kv head); each has 4 waves
   int keys_per_wave;    // multiple of 64
   float c_qk;

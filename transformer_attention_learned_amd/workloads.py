@@ -83,7 +83,31 @@ WORKLOADS = {
                               S=65536, window=0, bias_range=1024, mode="rproj", seed=5),
     "decode_local": Workload("decode_local", "decode", "bf16", B=64, Hq=32, Hkv=8, D=128,
                              S=65536, window=512, bias_range=512, mode="rproj", seed=5),
+    # the same decode steps over a paged cache: 64-row pages in a pool, each sequence's pages
+    # scattered by a seeded permutation (the page-table layout of a serving engine)
+    "decode_global_paged": Workload("decode_global_paged", "decode", "bf16", B=64, Hq=32, Hkv=8,
+                                    D=128, S=65536, window=0, bias_range=1024, mode="rproj", seed=5,
+                                    extra={"page_size": 64}),
+    "decode_local_paged": Workload("decode_local_paged", "decode", "bf16", B=64, Hq=32, Hkv=8,
+                                   D=128, S=65536, window=512, bias_range=512, mode="rproj", seed=5,
+                                   extra={"page_size": 64}),
 }
+
+
+def paged_view(w: Workload, k, v, seed=None):
+    """Page pools and block table over the contiguous caches of a decode workload.
+
+    The caches [B, L, Hkv, D] are viewed as B * L / page_size pages (no copy); sequence b's
+    logical page p is pool page perm[b * max_pages + p] for a seeded permutation, so the
+    table scatters every sequence over the pool.  Returns (k_pages, v_pages, block_table).
+    """
+    ps = w.extra["page_size"]
+    B, L, Hkv, D = k.shape
+    mp = L // ps
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed((w.seed if seed is None else seed) + 1000)
+    perm = torch.randperm(B * mp, generator=gen).to(torch.int32).to(k.device)
+    return (k.view(B * mp, ps, Hkv, D), v.view(B * mp, ps, Hkv, D), perm.view(B, mp))
 
 
 def _randn(shape, gen, device, dtype, chunk_elems=1 << 28):
