@@ -335,6 +335,298 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
   }
 }
 
+// Decode for groups of at most 16 query heads on v_mfma_f32_16x16x32_bf16: the heads are the
+// 16 MFMA columns, which halves the O accumulators and the query fragments against the 32x32
+// form and leaves registers for two cache tiles in flight per wave (the step is bound by how
+// many bytes each wave keeps in flight).  Same work split, bias, merge and partials as above.
+//   * S^T (16 rows x 16 heads) per 16-row block: A = K rows straight from global memory,
+//     B = q; a lane holds rows 16 kb + 4 (l / 16) + i of head l % 16.
+//   * O^T += V^T P^T with the 32 rows of a tile as K: the rows are paired with the MFMA's K
+//     elements in the order the scores already sit in (element j of lane group g is row
+//     16 (j / 4) + 4 g + j % 4), so P is packed in place; V^T is stored in LDS with the rows
+//     permuted to that order, one 16-byte read per lane.
+template <int D, int MODE, int RMAX>
+__global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curve_off) {
+  constexpr int VST = TK + 8;          // V^T row stride (bf16)
+  constexpr int NC = D / 32;           // K = 32 chunks of the head dim
+  constexpr int NDB = D / 16;          // 16-wide head-dim blocks of O^T
+  constexpr int NVI = (TK / 4) * (D / 8) / 64;   // V items (4 rows x 8 dims) per lane
+  constexpr int VT_BYTES = D * VST * 2;          // per wave
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n16 = lane & 15;           // head column
+  const int g = lane >> 4;             // row group
+  const int split = blockIdx.x;
+  const int hkv = blockIdx.y;
+  const int b = blockIdx.z;
+  const int G = a.G;
+  const bool col_live = n16 < G;
+
+  const size_t kv_row = static_cast<size_t>(a.Hkv) * D;
+  const bool paged = a.block_table != nullptr;
+  const int kv_len = paged ? min(max(a.kv_lens[b], 0), a.kv_len) : a.kv_len;
+  const int key_begin = paged ? (a.window ? max(0, kv_len - a.window) : 0) : a.key_begin;
+  const uint16_t* kbase = a.k + static_cast<size_t>(hkv) * D + (paged ? 0 : static_cast<size_t>(b) * a.L_max * kv_row);
+  const uint16_t* vbase = a.v + static_cast<size_t>(hkv) * D + (paged ? 0 : static_cast<size_t>(b) * a.L_max * kv_row);
+  const int* bt = paged ? a.block_table + static_cast<size_t>(b) * a.max_pages : nullptr;
+  auto pool_row = [&](int key) -> int {
+    const int pg = min(max(bt[key / a.page_size], 0), a.num_pages - 1);
+    return pg * a.page_size + key % a.page_size;
+  };
+  const int qpos = kv_len - 1;
+
+  const int w_beg = key_begin + (split * 4 + wave) * a.keys_per_wave;
+  const int w_end = min(kv_len, w_beg + a.keys_per_wave);
+  const int ntiles = w_end > w_beg ? (w_end - w_beg + TK - 1) / TK : 0;
+
+  // ---- two register sets of tiles in flight: K as A-operand fragments, V as row pieces ----
+  u32x4 kreg[2][2][NC], vreg[2][NVI][4];
+  auto load_tile = [&](int set, int tk0) {
+    // K rows tk0 + 16 kb + (l % 16); paged: one table read per lane and row block
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = tk0 + 16 * kb + n16;
+      const int prow = paged ? (key < w_end ? pool_row(key) : 0) : key;
+      const uint16_t* kp = kbase + static_cast<size_t>(prow) * kv_row + 8 * g;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        kreg[set][kb][c] = u32x4{0u, 0u, 0u, 0u};
+        if (key < w_end) kreg[set][kb][c] = ld16(kp + 32 * c);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NVI; ++it) {
+      const int item = lane + 64 * it;
+      const int kg = item & 7;
+      const int dg = item >> 3;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int kk = tk0 + 4 * kg + s4;
+        int vrow = kk;
+        if (paged) vrow = kk < w_end ? pool_row(kk) : 0;
+        vreg[set][it][s4] = u32x4{0u, 0u, 0u, 0u};
+        if (kk < w_end) vreg[set][it][s4] = ld16(vbase + static_cast<size_t>(vrow) * kv_row + 8 * dg);
+      }
+    }
+  };
+
+  bf16x8 qf[NC];
+  {
+    const uint16_t* qp = a.q + (static_cast<size_t>(b) * a.Hq + hkv * G + (col_live ? n16 : 0)) * D + 8 * g;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (col_live) v = ld16(qp + 32 * c);
+      qf[c] = as_bf16x8(v);
+    }
+  }
+  if (ntiles > 0) load_tile(0, w_beg);
+  if (ntiles > 1) load_tile(1, w_beg + TK);
+
+  // ---- bias curves per tile, as in the 32x32 kernel ---------------------------------------
+  float* rs = reinterpret_cast<float*>(smem + curve_off);                  // [G][R] (r.E)
+  float* cbuf = rs + (MODE == 2 ? G * a.R : 0) + wave * 2 * G * TK;         // [2][G][TK]
+  if (MODE == 2) {
+    for (int i = tid; i < G * a.R; i += 256)
+      rs[i] = bf16_to_f32(a.r[(static_cast<size_t>(b) * a.Hq + hkv * G) * a.R + i]);
+    __syncthreads();
+  }
+  const int n_items = G * TK;
+  auto tile_in_band = [&](int tk0) { return MODE != 0 && qpos - (tk0 + TK - 1) < a.bias_range; };
+  auto item_geo = [&](int tk0, int item, int& n, int& d, bool& live) {
+    n = item / TK;
+    const int j = item - n * TK;
+    d = qpos - (tk0 + j);
+    live = item < n_items && d >= 0 && d < a.bias_range && tk0 + j < w_end;
+    if (item >= n_items) n = 0;
+  };
+  auto fetch_items = [&](int tk0, int base, float (&e)[2][RMAX]) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      int n, d;
+      bool live;
+      item_geo(tk0, base + lane + 64 * u, n, d, live);
+      const int hh = hkv * G + n;
+      if (MODE == 1) {
+        e[u][0] = live ? a.table[static_cast<size_t>(hh) * a.bias_range + d] : 0.f;
+      } else {
+        const float* ep = a.E + static_cast<size_t>(hh) * a.e_hs + (live ? d : 0);
+#pragma unroll
+        for (int f = 0; f < RMAX; ++f) e[u][f] = (live && f < a.R) ? ep[static_cast<size_t>(f) * a.bias_range] : 0.f;
+      }
+    }
+  };
+  auto finish_items = [&](int tk0, int base, const float (&e)[2][RMAX], float* dst) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int item = base + lane + 64 * u;
+      int n, d;
+      bool live;
+      item_geo(tk0, item, n, d, live);
+      float acc = 0.f;
+      if (MODE == 1) {
+        acc = e[u][0];
+      } else {
+#pragma unroll
+        for (int f = 0; f < RMAX; ++f)
+          if (f < a.R) acc = fmaf(rs[n * a.R + f], e[u][f], acc);
+      }
+      if (item < n_items) dst[item] = acc * kLog2e;
+    }
+  };
+  // (the inputs are fetched where they are used: registers go to the tiles in flight)
+  auto curve_tile = [&](int tk0, float* dst) {
+    for (int base = 0; base < n_items; base += 128) {
+      float e[2][RMAX];
+      fetch_items(tk0, base, e);
+      finish_items(tk0, base, e, dst);
+    }
+  };
+  if (ntiles > 0 && tile_in_band(w_beg)) curve_tile(w_beg, cbuf);
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint16_t* vt = reinterpret_cast<uint16_t*>(smem) + wave * (VT_BYTES / 2);
+  const float NEG_INF = -INFINITY;
+  // V^T position of tile row k: 8 (k % 16 / 4) + 4 (k / 16) + k % 4
+  auto vt_pos16 = [](int k) { return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3); };
+
+  auto process = [&](int t, int set) {
+    const int tk0 = w_beg + t * TK;
+    // S^T of the two 16-row blocks
+    f32x4 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sacc[kb] = mfma16(as_bf16x8(kreg[set][kb][c]), qf[c], sacc[kb]);
+    }
+    // V of this tile -> LDS, transposed and row-permuted (the previous tile's reads are done)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int it = 0; it < NVI; ++it) {
+      const int item = lane + 64 * it;
+      const int kg = item & 7;
+      const int dg = item >> 3;
+      const int pos = vt_pos16(4 * kg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t p01 = __builtin_amdgcn_perm(vreg[set][it][1][w], vreg[set][it][0][w], sel);
+        const uint32_t p23 = __builtin_amdgcn_perm(vreg[set][it][3][w], vreg[set][it][2][w], sel);
+        st8(vt + (8 * dg + e) * VST + pos, u32x2{p01, p23});
+      }
+    }
+    // this set's registers are free: the tile two ahead goes in flight
+    if (t + 2 < ntiles) load_tile(set, tk0 + 2 * TK);
+
+    // logits (log2 units), bias of in-band rows, mask beyond this wave's rows
+    const bool in_band = tile_in_band(tk0);
+    const float* cv = cbuf + (t & 1) * G * TK + (col_live ? n16 : 0) * TK + 4 * g;
+    float mx = NEG_INF;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = tk0 + 16 * kb + 4 * g + i;
+        float sv = sacc[kb][i] * a.c_qk;
+        if (in_band) sv += cv[16 * kb + i];
+        if (key >= w_end) sv = NEG_INF;
+        sacc[kb][i] = sv;
+        mx = fmaxf(mx, sv);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float psum = l_run * alpha;
+    uint32_t w4[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const float p0 = fast_exp2(sacc[kb][i] - m_use);
+        const float p1 = fast_exp2(sacc[kb][i + 1] - m_use);
+        w4[2 * kb + i / 2] = pack_bf16x2(p0, p1);
+        psum = sum_bf16x2(w4[2 * kb + i / 2], psum);
+      }
+    const bf16x8 pf = as_bf16x8(u32x4{w4[0], w4[1], w4[2], w4[3]});
+    l_run = psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const bf16x8 vf = as_bf16x8(ld16(vt + (16 * db + n16) * VST + 8 * g));
+      oacc[db] = mfma16(vf, pf, oacc[db]);
+    }
+    if (t + 1 < ntiles && tile_in_band(tk0 + TK)) curve_tile(tk0 + TK, cbuf + ((t + 1) & 1) * G * TK);
+  };
+  for (int t = 0; t < ntiles; t += 2) {   // two register sets: the unroll keeps their indices static
+    process(t, 0);
+    if (t + 1 < ntiles) process(t + 1, 1);
+  }
+
+  // ---- merge the 4 waves through LDS (reusing the V^T area) ---------------------------
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  __syncthreads();
+  float* mb = reinterpret_cast<float*>(smem);           // [4][G][D] partial acc
+  float* ml = mb + 4 * G * D;                           // [4][G][2] (m, l)
+  if (col_live) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mb[(wave * G + n16) * D + 16 * db + 4 * g + i] = oacc[db][i];
+    if (g == 0) {
+      ml[(wave * G + n16) * 2 + 0] = m_run;
+      ml[(wave * G + n16) * 2 + 1] = l_tot;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int n = idx / D;
+    const int d = idx % D;
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[(w * G + n) * 2]);
+    const float Mu = (M == NEG_INF) ? 0.f : M;
+    float acc = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float sc = fast_exp2(ml[(w * G + n) * 2] - Mu);
+      acc += sc * mb[(w * G + n) * D + d];
+      l += sc * ml[(w * G + n) * 2 + 1];
+    }
+    const int hh = hkv * G + n;
+    if (a.n_split == 1) {
+      a.o[(static_cast<size_t>(b) * a.Hq + hh) * D + d] = f32_to_bf16(acc / l);
+      if (d == 0 && a.lse) a.lse[static_cast<size_t>(b) * a.Hq + hh] = (M + fast_log2(l)) * kLn2;
+    } else {
+      float* wp = a.ws + ((static_cast<size_t>(b) * a.Hq + hh) * a.n_split + split) * (D + 2);
+      wp[d] = acc;
+      if (d == 0) {
+        wp[D] = M;
+        wp[D + 1] = l;
+      }
+    }
+  }
+}
+
 // Combine the split partials of one (batch, head): o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
@@ -362,15 +654,21 @@ hipError_t launch_d(DecodeArgs a, hipStream_t s) {
   const int curve_off = ((VT_ALL > merge ? VT_ALL : merge) + 15) / 16 * 16;
   // after the V^T tiles / merge buffer: r [G][R] (r.E), then per wave two tile curves [G][TK]
   const int total = curve_off + (MODE == 2 ? a.G * a.R * 4 : 0) + (MODE != 0 ? 4 * 2 * a.G * TK * 4 : 0);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_bf16_kernel<D, MODE, RMAX>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   if (total > 160 * 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_bf16_kernel<D, MODE, RMAX>), grid, dim3(256), total, s, a, curve_off);
+  // groups of up to 16 query heads: the 16x16 MFMA kernel (two tiles in flight per wave)
+  static bool attr_set[2] = {false, false};
+  const bool narrow = a.G <= 16;
+  const void* fn = narrow ? reinterpret_cast<const void*>(&decode16_kernel<D, MODE, RMAX>)
+                          : reinterpret_cast<const void*>(&decode_bf16_kernel<D, MODE, RMAX>);
+  if (!attr_set[narrow]) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set[narrow] = true;
+  }
+  if (narrow)
+    hipLaunchKernelGGL((decode16_kernel<D, MODE, RMAX>), grid, dim3(256), total, s, a, curve_off);
+  else
+    hipLaunchKernelGGL((decode_bf16_kernel<D, MODE, RMAX>), grid, dim3(256), total, s, a, curve_off);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, s, a);

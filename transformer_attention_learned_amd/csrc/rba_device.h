@@ -64,6 +64,13 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// D = A * B + C on a 16x16 output tile, K = 32 bf16 (fp32 accumulate).  Lane l holds A row
+// (l % 16) and B column (l % 16), 8 K-elements each, paired by (l / 16, element index) as in
+// the 32x32 form; output: lane l holds column l % 16, rows 4 * (l / 16) + i for i = 0..3.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
