@@ -235,6 +235,10 @@ DEC_SWEEP = [
     dict(S=3000, kv_len=2600, mode="rproj_shared", R=16, window=512, bias_range=512,
          logit_scale="inv_d"),
     dict(S=5000, kv_len=4500, mode="rproj_shared", R=8, bias_range=1024, Hq=32, Hkv=8),
+    # groups of more than 16 query heads take the 32x32-MFMA kernel
+    dict(S=3000, kv_len=2900, Hq=32, Hkv=1, window=700, bias_range=512),
+    dict(S=2000, kv_len=1999, Hq=24, Hkv=1, mode="table", bias_range=300),
+    dict(S=700, kv_len=650, Hq=32, Hkv=1, D=64, mode="none"),
 ]
 
 
