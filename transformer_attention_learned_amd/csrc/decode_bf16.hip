@@ -385,11 +385,14 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
   // ---- two register sets of tiles in flight: K as A-operand fragments, V as row pieces ----
   u32x4 kreg[2][2][NC], vreg[2][NVI][4];
   auto load_tile = [&](int set, int tk0) {
-    // K rows tk0 + 16 kb + (l % 16); paged: one table read per lane and row block
+    // K rows tk0 + 16 kb + (l % 16); paged: one table read per lane and row block, and lane
+    // l < 32 keeps the pool row of cache row tk0 + l for the V loads below
+    int prow32 = 0;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key = tk0 + 16 * kb + n16;
       const int prow = paged ? (key < w_end ? pool_row(key) : 0) : key;
+      if (kb == (g & 1)) prow32 = prow;
       const uint16_t* kp = kbase + static_cast<size_t>(prow) * kv_row + 8 * g;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
       for (int s4 = 0; s4 < 4; ++s4) {
         const int kk = tk0 + 4 * kg + s4;
         int vrow = kk;
-        if (paged) vrow = kk < w_end ? pool_row(kk) : 0;
+        if (paged) vrow = __shfl(prow32, 4 * kg + s4, 64);
         vreg[set][it][s4] = u32x4{0u, 0u, 0u, 0u};
         if (kk < w_end) vreg[set][it][s4] = ld16(vbase + static_cast<size_t>(vrow) * kv_row + 8 * dg);
       }
