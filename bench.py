@@ -101,8 +101,8 @@ def cpu_baseline(w, inp, seconds: float):
                 tab = None if inp["table"] is None else inp["table"][hs].cpu()
                 E = None if inp["E"] is None else inp["E"][hs].cpu()
                 t0 = time.perf_counter()
-                oracle.prefill(q, k, v, scale=w.scale, window=w.window, bias_range=w.bias_range,
-                               mode=w.mode, table=tab, r=r, E=E)
+                oracle.prefill(q, k, v, scale=w.scale, temp_len=w.temp_len, window=w.window,
+                               bias_range=w.bias_range, mode=w.mode, table=tab, r=r, E=E)
                 t_total += time.perf_counter() - t0
                 done_flops += 4.0 * w.D * G * pairs
                 n_slices += 1
@@ -117,7 +117,8 @@ def cpu_baseline(w, inp, seconds: float):
         for b in range(w.B):
             t0 = time.perf_counter()
             oracle.decode(inp["q"][b:b + 1], inp["k"][b:b + 1], inp["v"][b:b + 1], w.S,
-                          scale=w.scale, window=w.window, bias_range=w.bias_range, mode=w.mode,
+                          scale=w.scale, temp_len=w.temp_len, window=w.window,
+                          bias_range=w.bias_range, mode=w.mode,
                           table=inp["table"], r=None if inp["r"] is None else inp["r"][b:b + 1],
                           E=inp["E"])
             t_total += time.perf_counter() - t0
@@ -174,7 +175,7 @@ def main():
         def step():
             rba.fwd(inp["q"], inp["k"], inp["v"], window=w.window, bias_range=w.bias_range,
                     mode=w.mode, table=inp["table"], r=inp["r"], E=inp["E"], scale=w.scale,
-                    out=out)
+                    temp_len=w.temp_len, out=out)
 
         flops = 4.0 * w.D * w.Hq * w.B * visible_pairs_prefill(w.S, w.window)
         tokens = w.B * w.S
@@ -203,14 +204,15 @@ def main():
                 it[0] += 1
                 rba.decode_paged(inp["q"], kp, vp, bt, lens_t[j], kv_lens[j], window=w.window,
                                  bias_range=w.bias_range, mode=w.mode, table=inp["table"],
-                                 r=inp["r"], E=inp["E"], scale=w.scale, out=out, workspace=ws)
+                                 r=inp["r"], E=inp["E"], scale=w.scale, temp_len=w.temp_len,
+                                 out=out, workspace=ws)
         else:
             def step():
                 kv_len = kv_lens[it[0] % len(kv_lens)]
                 it[0] += 1
                 rba.decode(inp["q"], inp["k"], inp["v"], kv_len, window=w.window,
                            bias_range=w.bias_range, mode=w.mode, table=inp["table"], r=inp["r"],
-                           E=inp["E"], scale=w.scale, out=out, workspace=ws)
+                           E=inp["E"], scale=w.scale, temp_len=w.temp_len, out=out, workspace=ws)
 
         nvis = visible_keys_decode(w.S, w.window)
         flops = 4.0 * w.D * w.Hq * w.B * nvis
@@ -257,6 +259,8 @@ def main():
            "parallelism": "single-gpu"}
     if w.extra.get("page_size"):
         cfg["page_size"] = w.extra["page_size"]
+    if w.temp_len:
+        cfg["temp_len"] = w.temp_len
     line = {"metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

@@ -13,6 +13,17 @@
  * dropped RoPE", steps 1-5, for the input-dependent bias and the hard zero
  * outside the range).  The bias is added after `scale`, it is not scaled.
  *
+ * Optional context-length temperature (temp_len > 0): the logit of a query that
+ * sees n keys becomes tau(n) * s with
+ *     tau(n) = 1 for n <= temp_len,   tau(n) = ln(n) / ln(temp_len) beyond,
+ * a factor on the q.k term and the bias alike ("Thinking Machines dropped RoPE",
+ * section "The temperature scale is dependent on context length": global layers
+ * scale the queries and the position bias by a factor that is flat up to 128k
+ * visible keys and grows logarithmically after; that page prints no formula, the
+ * log-ratio above is the plain log-n form it names).  n counts the visible keys:
+ * pos + 1, capped at window when window > 0.  temp_len = 131072 gives the 128k
+ * threshold; temp_len = 0 turns the temperature off.
+ *
  * Bias modes:
  *   RBA_BIAS_NONE   beta = 0 (content only).
  *   RBA_BIAS_TABLE  beta = table[h, delta]: a learned per-head table indexed by
@@ -85,12 +96,14 @@ typedef enum {
  *               [R, bias_range] fp32; else ignored.
  *   R           RBA_BIAS_RPROJ(_SHARED): number of curves, 1..16.
  *   scale       multiplier of q.k (typically 1/sqrt(D)); the bias is not scaled.
+ *   temp_len    0 (no temperature) or >= 2: the visible-key count beyond which the
+ *               context-length temperature grows (see above); 1 or negative: RBA_EINVAL.
  *   stream      hipStream_t.
  */
 int relbias_attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int S, int Hq, int Hkv, int D, int window, int bias_range, int mode,
                      const float* table, const void* r, const float* E, int R, float scale,
-                     void* stream);
+                     int temp_len, void* stream);
 
 /*
  * Bytes of device workspace relbias_attn_decode needs for these sizes
@@ -108,7 +121,8 @@ size_t relbias_attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int kv_
  *   k_cache     [B, L_max, Hkv, D]; v_cache the same.  1 <= kv_len <= L_max.
  *   o           [B, Hq, D] (written); lse [B, Hq] fp32 or NULL.
  *   r           RBA_BIAS_RPROJ(_SHARED): [B, Hq, R] of dtype (coefficients of the new token).
- *   table, E, R, scale: as in relbias_attn_fwd.
+ *   table, E, R, scale, temp_len: as in relbias_attn_fwd (the query sees
+ *               min(kv_len, window) keys with a window, kv_len without).
  *   workspace   device scratch of at least relbias_attn_decode_workspace_size(...)
  *               bytes (may be NULL when that size is 0); contents on entry are
  *               ignored.  Calls that share one workspace must be ordered on one stream.
@@ -117,7 +131,7 @@ size_t relbias_attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int kv_
 int relbias_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
                         void* o, float* lse, int B, int L_max, int kv_len, int Hq, int Hkv, int D,
                         int window, int bias_range, int mode, const float* table, const void* r,
-                        const float* E, int R, float scale, void* workspace,
+                        const float* E, int R, float scale, int temp_len, void* workspace,
                         size_t workspace_bytes, void* stream);
 
 /*
@@ -144,8 +158,8 @@ size_t relbias_attn_decode_paged_workspace_size(int B, int Hq, int Hkv, int D, i
  *   max_kv_len  host upper bound of every kv_lens[b] (sizes the launch);
  *               1 <= max_kv_len <= max_pages * page_size.
  *   page_size   rows per page, a multiple of 16.
- *   window, bias_range, mode, table, r ([B, Hq, R]), E, R, scale: as in
- *               relbias_attn_decode.
+ *   window, bias_range, mode, table, r ([B, Hq, R]), E, R, scale, temp_len: as in
+ *               relbias_attn_decode (the temperature follows each kv_lens[b]).
  *   workspace   at least relbias_attn_decode_paged_workspace_size(...) bytes
  *               (may be NULL when that size is 0).
  * The device values are not validated: lengths are clamped to [0, max_kv_len] and
@@ -158,7 +172,8 @@ int relbias_attn_decode_paged(int dtype, const void* q, const void* k_pages, con
                               int B, int num_pages, int page_size, int max_pages, int max_kv_len,
                               int Hq, int Hkv, int D, int window, int bias_range, int mode,
                               const float* table, const void* r, const float* E, int R,
-                              float scale, void* workspace, size_t workspace_bytes, void* stream);
+                              float scale, int temp_len, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /* Message for the calling thread's last non-OK status ("" if none).  The pointer
  * stays valid until the next call on the same thread. */

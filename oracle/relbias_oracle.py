@@ -15,6 +15,8 @@ What it computes (plain definition, float64, no tiling, no online softmax):
                       = sum_f r[b,i,h,f] E[h,f,delta]   if mode == RPROJ
                       = sum_f r[b,i,h,f] E[f,delta]     if mode == RPROJ_SHARED
     s_ij = scale * <q[b,i,h,:], k[b,j,g,:]> + beta(h, i, delta_ij)
+    optional temperature (temp_len > 0): s_ij <- tau(n_i) * s_ij, with n_i the
+      number of keys query i sees and tau(n) = max(1, ln n / ln temp_len)
     o[b,i,h,:] = sum_{visible j} softmax_j(s_ij) v[b,j,g,:]
     lse[b,h,i] = log sum_{visible j} exp(s_ij)
 
@@ -47,6 +49,14 @@ Readings where the pages are silent or garbled (each is pinned by a test):
     head reads (step 2 of the same essay: the learned distance functions are
     common to all heads and tokens of the layer);
   * GQA: query head h reads kv head floor(h / G), G = Hq / Hkv.
+  * context-length temperature ("Thinking Machines dropped RoPE", section "The
+    temperature scale is dependent on context length"): global layers multiply
+    the queries and the position bias by a factor of the number n of keys the
+    query sees, flat up to 128k and growing logarithmically after; the page's
+    formula is missing, and the plain log-n reading taken here is
+    tau(n) = max(1, ln n / ln temp_len) with temp_len = 131072 for that page
+    (an argument, so that small cases reach tau > 1).  It scales the whole
+    logit, content term and bias alike.
 
 Inputs are taken as stored (bf16 / fp32 values upcast to float64).
 """
@@ -125,8 +135,22 @@ def bias_matrix(mode, qpos, kpos, bias_range, h, *, table=None, r_rows=None, E=N
     return out
 
 
+def temperature(n_visible, temp_len):
+    """Context-length temperature tau(n) = max(1, ln n / ln temp_len); 1 when temp_len == 0.
+
+    "Thinking Machines dropped RoPE", section "The temperature scale is dependent
+    on context length": flat until the threshold, logarithmic growth beyond.
+    """
+    n = np.asarray(n_visible, dtype=np.float64)
+    if not temp_len:
+        return np.ones_like(n)
+    if temp_len < 2:
+        raise ValueError("temp_len must be 0 or >= 2")
+    return np.maximum(1.0, np.log(np.maximum(n, 1.0)) / np.log(float(temp_len)))
+
+
 def attention(q, k, v, *, qpos, kpos, scale, window=0, bias_range=0, mode="none",
-              table=None, r=None, E=None, rows=None, row_block=512):
+              table=None, r=None, E=None, rows=None, row_block=512, temp_len=0):
     """Plain definition of relative-position-bias attention, float64.
 
     q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D]; r [B, Sq, Hq, R] (RPROJ, RPROJ_SHARED);
@@ -134,6 +158,8 @@ def attention(q, k, v, *, qpos, kpos, scale, window=0, bias_range=0, mode="none"
     [R, bias_range] (RPROJ_SHARED).
     qpos [Sq], kpos [Sk]: integer token positions.
     rows: optional 1-D array of query-row indices to evaluate (others skipped).
+    temp_len: context-length temperature threshold (0: none); the logit of a row
+    that sees n keys is multiplied by temperature(n, temp_len).
     Returns (o [B, len(rows), Hq, D], lse [B, Hq, len(rows)]) in float64.
 
     Formula: "Learned Relative-Position Bias", section "Standard Relative Bias
@@ -173,6 +199,7 @@ def attention(q, k, v, *, qpos, kpos, scale, window=0, bias_range=0, mode="none"
                                    r_rows=None if r64 is None else r64[b, rr, h, :], E=E64)
                 logits = logits + beta
                 vis = visible_mask(qpos[rr], kpos, window)
+                logits = logits * temperature(vis.sum(axis=1), temp_len)[:, None]
                 logits = np.where(vis, logits, -np.inf)
                 m = logits.max(axis=1, keepdims=True)
                 if not np.all(np.isfinite(m)):
@@ -185,17 +212,17 @@ def attention(q, k, v, *, qpos, kpos, scale, window=0, bias_range=0, mode="none"
 
 
 def prefill(q, k, v, *, scale, window=0, bias_range=0, mode="none", table=None, r=None,
-            E=None, rows=None, row_block=512):
+            E=None, rows=None, row_block=512, temp_len=0):
     """Prefill: query i and key j sit at positions i and j (one sequence per batch row)."""
     S = q.shape[1]
     pos = np.arange(S, dtype=np.int64)
     return attention(q, k, v, qpos=pos, kpos=pos, scale=scale, window=window,
                      bias_range=bias_range, mode=mode, table=table, r=r, E=E, rows=rows,
-                     row_block=row_block)
+                     row_block=row_block, temp_len=temp_len)
 
 
 def decode(q, k_cache, v_cache, kv_len, *, scale, window=0, bias_range=0, mode="none",
-           table=None, r=None, E=None, batch=None):
+           table=None, r=None, E=None, batch=None, temp_len=0):
     """Single-token decode against a KV cache.
 
     q [B, Hq, D] is the newest token, at position kv_len - 1; the cache already
@@ -213,7 +240,8 @@ def decode(q, k_cache, v_cache, kv_len, *, scale, window=0, bias_range=0, mode="
         vb = v_cache[b:b + 1, :kv_len]
         rb = None if r is None else r[b:b + 1][:, None]
         o, l = attention(qb, kb, vb, qpos=qpos, kpos=kpos, scale=scale, window=window,
-                         bias_range=bias_range, mode=mode, table=table, r=rb, E=E)
+                         bias_range=bias_range, mode=mode, table=table, r=rb, E=E,
+                         temp_len=temp_len)
         outs.append(o[0, 0])
         lses.append(l[0, :, 0])
     return np.stack(outs), np.stack(lses)

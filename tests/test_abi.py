@@ -44,23 +44,24 @@ def test_exports_every_declared_symbol(lib):
 
 def _fwd(lib, **kw):
     a = dict(dtype=BF16, q=P, k=P, v=P, o=P, lse=None, B=1, S=16, Hq=4, Hkv=2, D=128, window=0,
-             bias_range=8, mode=0, table=None, r=None, E=None, R=0, scale=0.1, stream=None)
+             bias_range=8, mode=0, table=None, r=None, E=None, R=0, scale=0.1, temp_len=0,
+             stream=None)
     a.update(kw)
     return lib.relbias_attn_fwd(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
                                 a["S"], a["Hq"], a["Hkv"], a["D"], a["window"], a["bias_range"],
                                 a["mode"], a["table"], a["r"], a["E"], a["R"], a["scale"],
-                                a["stream"])
+                                a["temp_len"], a["stream"])
 
 
 def _dec(lib, **kw):
     a = dict(dtype=BF16, q=P, k=P, v=P, o=P, lse=None, B=2, L=100, kv_len=50, Hq=8, Hkv=2, D=128,
-             window=0, bias_range=8, mode=0, table=None, r=None, E=None, R=0, scale=0.1, ws=None,
-             wsb=0, stream=None)
+             window=0, bias_range=8, mode=0, table=None, r=None, E=None, R=0, scale=0.1,
+             temp_len=0, ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib.relbias_attn_decode(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
                                    a["L"], a["kv_len"], a["Hq"], a["Hkv"], a["D"], a["window"],
                                    a["bias_range"], a["mode"], a["table"], a["r"], a["E"], a["R"],
-                                   a["scale"], a["ws"], a["wsb"], a["stream"])
+                                   a["scale"], a["temp_len"], a["ws"], a["wsb"], a["stream"])
 
 
 def test_mode_constants_match_header():
@@ -94,6 +95,8 @@ def test_mode_constants_match_header():
     (dict(B=-1), EINVAL, "B="),
     (dict(scale=float("nan")), EINVAL, "scale"),
     (dict(mode=1, table=P, bias_range=(1 << 20) + 1), ENOTSUP, "bias_range"),
+    (dict(temp_len=1), EINVAL, "temp_len"),
+    (dict(temp_len=-5), EINVAL, "temp_len"),
 ])
 def test_fwd_rejects(lib, kw, code, needle):
     assert _fwd(lib, **kw) == code
@@ -114,6 +117,7 @@ def test_fwd_empty_is_a_noop(lib):
     (dict(v=P + 4), EINVAL, "aligned"),
     (dict(D=32), ENOTSUP, "head_dim"),
     (dict(mode=2, r=P, E=P, R=0), ENOTSUP, "R="),
+    (dict(temp_len=1), EINVAL, "temp_len"),
 ])
 def test_decode_rejects(lib, kw, code, needle):
     assert _dec(lib, **kw) == code
@@ -144,14 +148,14 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
 def _paged(lib, **kw):
     a = dict(dtype=BF16, q=P, kp=P, vp=P, bt=P, lens=P, o=P, lse=None, B=2, num_pages=8,
              page_size=32, max_pages=4, max_kv_len=100, Hq=8, Hkv=2, D=128, window=0,
-             bias_range=8, mode=0, table=None, r=None, E=None, R=0, scale=0.1, ws=None, wsb=0,
-             stream=None)
+             bias_range=8, mode=0, table=None, r=None, E=None, R=0, scale=0.1, temp_len=0, ws=None,
+             wsb=0, stream=None)
     a.update(kw)
     return lib.relbias_attn_decode_paged(
         a["dtype"], a["q"], a["kp"], a["vp"], a["bt"], a["lens"], a["o"], a["lse"], a["B"],
         a["num_pages"], a["page_size"], a["max_pages"], a["max_kv_len"], a["Hq"], a["Hkv"], a["D"],
         a["window"], a["bias_range"], a["mode"], a["table"], a["r"], a["E"], a["R"], a["scale"],
-        a["ws"], a["wsb"], a["stream"])
+        a["temp_len"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code,needle", [
@@ -168,6 +172,7 @@ def _paged(lib, **kw):
     (dict(Hq=66, Hkv=1), ENOTSUP, "Hq/Hkv"),
     (dict(mode=2, r=P, E=P, R=0), ENOTSUP, "R="),
     (dict(B=-1), EINVAL, "B="),
+    (dict(temp_len=-1), EINVAL, "temp_len"),
 ])
 def test_decode_paged_rejects(lib, kw, code, needle):
     assert _paged(lib, **kw) == code

@@ -341,3 +341,106 @@ def test_bias_zero_at_range_boundary():
         for j in range(10):
             d = i - j
             assert beta[i, j] == (d + 1 if 0 <= d < Rb else 0.0)
+
+
+# --- P9: context-length temperature ---------------------------------------------------------
+# "Thinking Machines dropped RoPE", section "The temperature scale is dependent on context
+# length": global layers multiply the queries and the position bias by a factor of the number
+# of keys the query sees, flat up to a threshold and logarithmic beyond (log-n scaling).
+
+def test_temperature_values():
+    """tau = 1 up to the threshold T, then log base T of n: tau(T^k) = k, tau(T^(k/2)) = k/2."""
+    T = 4
+    n = np.array([1, 2, 3, 4, 8, 16, 32, 64, 256])
+    np.testing.assert_allclose(oracle.temperature(n, T), [1, 1, 1, 1, 1.5, 2, 2.5, 3, 4],
+                               rtol=1e-15)
+    np.testing.assert_array_equal(oracle.temperature(n, 0), np.ones(len(n)))
+    big = oracle.temperature([131072, 131073, 131072 ** 2], 131072)
+    assert big[0] == 1.0 and 1.0 < big[1] < 1.0 + 1e-5
+    assert big[2] == pytest.approx(2.0, rel=1e-14)
+
+
+@pytest.mark.parametrize("window", [0, 16])
+def test_temperature_equal_logits_closed_form(window):
+    """Equal visible logits L give lse = tau(n) * L + ln n; tau multiplies content and bias."""
+    S, T = 64, 4
+    q = np.ones((1, S, 1, 1))
+    k = np.ones((1, S, 1, 1))
+    v = _rng(31).standard_normal((1, S, 1, 1))
+    table = np.full((1, S), 0.25)                      # bias 0.25 at every distance
+    _, lse = oracle.prefill(q, k, v, scale=0.5, bias_range=S, mode="table", table=table,
+                            window=window, temp_len=T)
+    L = 0.5 * 1.0 + 0.25
+    tau_of = {1: 1.0, 2: 1.0, 4: 1.0, 8: 1.5, 16: 2.0, 32: 2.5, 64: 3.0}
+    checked = 0
+    for i in range(S):
+        n = min(i + 1, window) if window else i + 1
+        if n in tau_of:
+            assert abs(lse[0, 0, i] - (tau_of[n] * L + math.log(n))) < 1e-12, (i, n)
+            checked += 1
+    assert checked >= 5
+    # content only (no bias): the factor reaches the q.k term alone
+    _, lse0 = oracle.prefill(q, k, v, scale=0.5, window=window, temp_len=T)
+    i = 63
+    n = min(i + 1, window) if window else i + 1
+    assert abs(lse0[0, 0, i] - (tau_of[n] * 0.5 + math.log(n))) < 1e-12
+
+
+@pytest.mark.parametrize("mode,window", [("table", 20), ("rproj", 0), ("rproj_shared", 9)])
+def test_temperature_is_query_and_bias_scaling(mode, window):
+    """torch SDPA with each query row and its bias row multiplied by tau(n_i) gives the oracle's
+    tempered attention (the page's description: queries and position bias scaled by tau)."""
+    rng = _rng(41)
+    B, S, Hq, Hkv, D, R, Rb, T = 1, 48, 2, 1, 8, 3, 12, 5
+    q = rng.standard_normal((B, S, Hq, D))
+    k = rng.standard_normal((B, S, Hkv, D))
+    v = rng.standard_normal((B, S, Hkv, D))
+    table = rng.standard_normal((Hq, Rb))
+    r = rng.standard_normal((B, S, Hq, R))
+    E = rng.standard_normal((R, Rb) if mode == "rproj_shared" else (Hq, R, Rb))
+    o, lse = oracle.prefill(q, k, v, scale=0.4, window=window, bias_range=Rb, mode=mode,
+                            table=table, r=r, E=E, temp_len=T)
+    # bias built here by direct indexing, independent of the oracle's bias_matrix
+    bias = np.zeros((Hq, S, S))
+    for h in range(Hq):
+        for i in range(S):
+            for j in range(max(0, i - Rb + 1), i + 1):
+                d = i - j
+                if mode == "table":
+                    bias[h, i, j] = table[h, d]
+                else:
+                    bank = E if mode == "rproj_shared" else E[h]
+                    bias[h, i, j] = float(r[0, i, h] @ bank[:, d])
+    n = np.arange(1, S + 1)
+    if window:
+        n = np.minimum(n, window)
+    tau = np.array([max(1.0, math.log(x) / math.log(T)) for x in n])
+    ref = _sdpa_f64(q * tau[None, :, None, None], k, v, scale=0.4, window=window,
+                    bias=bias * tau[None, :, None])
+    np.testing.assert_allclose(o, ref, atol=1e-12)
+    assert np.abs(tau - 1).max() > 0.3          # the case reaches well past the threshold
+    # negative control: without the temperature the result differs
+    o_flat, _ = oracle.prefill(q, k, v, scale=0.4, window=window, bias_range=Rb, mode=mode,
+                               table=table, r=r, E=E)
+    assert np.abs(o_flat - o).max() > 1e-3
+
+
+def test_temperature_flat_below_threshold_and_decode():
+    """A threshold at or above every visible count changes nothing; decode tempers like the
+    last prefill row (the query sees kv_len keys, or the window)."""
+    rng = _rng(43)
+    B, S, Hq, Hkv, D, Rb = 2, 30, 4, 2, 6, 9
+    q = rng.standard_normal((B, S, Hq, D))
+    k = rng.standard_normal((B, S, Hkv, D))
+    v = rng.standard_normal((B, S, Hkv, D))
+    table = rng.standard_normal((Hq, Rb))
+    kw = dict(scale=0.5, bias_range=Rb, mode="table", table=table)
+    o0, l0 = oracle.prefill(q, k, v, **kw)
+    o1, l1 = oracle.prefill(q, k, v, temp_len=S, **kw)
+    np.testing.assert_array_equal(o0, o1)
+    np.testing.assert_array_equal(l0, l1)
+    for W in (0, 11):
+        op, lp = oracle.prefill(q, k, v, window=W, temp_len=3, **kw)
+        od, ld = oracle.decode(q[:, -1], k, v, S, window=W, temp_len=3, **kw)
+        np.testing.assert_allclose(od, op[:, -1], atol=1e-13)
+        np.testing.assert_allclose(ld, lp[:, :, -1], atol=1e-13)

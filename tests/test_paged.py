@@ -67,14 +67,16 @@ def _check(w, lens, page_size, n_extra=3):
     kv_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
     o, lse = rba.decode_paged(inp["q"], kp, vp, bt, kv_lens, max(lens), window=w.window,
                               bias_range=w.bias_range, mode=w.mode, table=inp["table"],
-                              r=inp["r"], E=inp["E"], scale=w.scale, return_lse=True)
+                              r=inp["r"], E=inp["E"], scale=w.scale, temp_len=w.temp_len,
+                              return_lse=True)
     torch.cuda.synchronize()
     got_o, got_l = _t2np(o), _t2np(lse)
     assert np.all(np.isfinite(got_o)) and np.all(np.isfinite(got_l))
     ref_o = np.zeros_like(got_o)
     ref_l = np.zeros_like(got_l)
     for b, L in enumerate(lens):
-        ro, rl = oracle.decode(inp["q"], inp["k"], inp["v"], L, scale=w.scale, window=w.window,
+        ro, rl = oracle.decode(inp["q"], inp["k"], inp["v"], L, scale=w.scale,
+                               temp_len=w.temp_len, window=w.window,
                                bias_range=w.bias_range, mode=w.mode, table=inp["table"],
                                r=inp["r"], E=inp["E"], batch=[b])
         ref_o[b], ref_l[b] = ro[0], rl[0]
@@ -102,6 +104,8 @@ CASES = [
      [1300, 1000, 513, 17], 64),
     (dict(D=64, Hq=16, Hkv=2, S=300), [300, 299, 150, 48], 16),
     (dict(B=3, S=5000, bias_range=1024, Hq=32, Hkv=8), [5000, 4097, 1025], 128),
+    # context-length temperature follows each sequence's own length
+    (dict(S=3000, temp_len=256), [3000, 2000, 257, 100], 64),
 ]
 
 

@@ -79,7 +79,7 @@ def _t2np(t):
 def run_prefill(w: Workload, inp):
     return rba.fwd(inp["q"], inp["k"], inp["v"], window=w.window, bias_range=w.bias_range,
                    mode=w.mode, table=inp["table"], r=inp["r"], E=inp["E"], scale=w.scale,
-                   return_lse=True)
+                   temp_len=w.temp_len, return_lse=True)
 
 
 def check_prefill(w: Workload, rows=None, dev="cuda:0"):
@@ -88,7 +88,8 @@ def check_prefill(w: Workload, rows=None, dev="cuda:0"):
     inp = make_inputs(w, device=dev)
     o, lse = run_prefill(w, inp)
     torch.cuda.synchronize()
-    ref_o, ref_lse = oracle.prefill(inp["q"], inp["k"], inp["v"], scale=w.scale, window=w.window,
+    ref_o, ref_lse = oracle.prefill(inp["q"], inp["k"], inp["v"], scale=w.scale,
+                                    temp_len=w.temp_len, window=w.window,
                                     bias_range=w.bias_range, mode=w.mode, table=inp["table"],
                                     r=inp["r"], E=inp["E"], rows=rows)
     if rows is None:
@@ -128,6 +129,12 @@ SWEEP = [
          logit_scale="inv_d"),
     dict(S=1100, mode="rproj_shared", R=16, bias_range=1024, logit_scale="inv_d"),
     dict(S=333, mode="rproj_shared", R=5, window=130, bias_range=77, D=64),
+    # context-length temperature past a small threshold: rows that see more than temp_len
+    # keys have their logits (content and bias) sharpened by ln n / ln temp_len
+    dict(S=1000, temp_len=100), dict(S=700, window=512, bias_range=512, temp_len=64),
+    dict(S=333, mode="table", bias_range=100, temp_len=2),
+    dict(S=1100, mode="rproj_shared", R=16, bias_range=1024, logit_scale="inv_d", temp_len=256),
+    dict(S=260, D=64, temp_len=50), dict(S=190, Hq=6, Hkv=2, temp_len=20, mode="table"),
 ]
 
 
@@ -141,8 +148,9 @@ def test_prefill_small(kw):
                                 dict(S=70, mode="none", Hq=4, Hkv=2, D=64),
                                 dict(S=3, mode="table", bias_range=2, D=128),
                                 dict(S=90, mode="rproj_shared", R=16, bias_range=33, window=60,
-                                     logit_scale="inv_d")],
-                         ids=["table", "rproj", "none_gqa", "tiny", "rproj_shared"])
+                                     logit_scale="inv_d"),
+                                dict(S=150, mode="table", bias_range=40, window=70, temp_len=9)],
+                         ids=["table", "rproj", "none_gqa", "tiny", "rproj_shared", "temp"])
 def test_prefill_f32_small(kw):
     check_prefill(small(dtype="f32", rmsnorm_qk=False, **kw))
 
@@ -197,7 +205,7 @@ def test_long_global_prefill_workload():
 def run_decode(w: Workload, inp, kv_len):
     return rba.decode(inp["q"], inp["k"], inp["v"], kv_len, window=w.window,
                       bias_range=w.bias_range, mode=w.mode, table=inp["table"], r=inp["r"],
-                      E=inp["E"], scale=w.scale, return_lse=True)
+                      E=inp["E"], scale=w.scale, temp_len=w.temp_len, return_lse=True)
 
 
 def check_decode(w: Workload, kv_len, batches=None, key_margin=None):
@@ -219,6 +227,7 @@ def check_decode(w: Workload, kv_len, batches=None, key_margin=None):
         vb = inp["v"][b:b + 1, k0:kv_len]
         rb = None if inp["r"] is None else inp["r"][b:b + 1][:, None]
         ro, rl = oracle.attention(qb, kb, vb, qpos=[kv_len - 1], kpos=kpos, scale=w.scale,
+                                  temp_len=w.temp_len,
                                   window=w.window, bias_range=w.bias_range, mode=w.mode,
                                   table=inp["table"], r=rb, E=inp["E"])
         assert_parity(_t2np(o[b]), ro[0, 0], w.dtype, f"{w.name} b={b}")
@@ -239,6 +248,10 @@ DEC_SWEEP = [
     dict(S=3000, kv_len=2900, Hq=32, Hkv=1, window=700, bias_range=512),
     dict(S=2000, kv_len=1999, Hq=24, Hkv=1, mode="table", bias_range=300),
     dict(S=700, kv_len=650, Hq=32, Hkv=1, D=64, mode="none"),
+    # context-length temperature (the query sees kv_len keys, or the window)
+    dict(S=6000, kv_len=5000, temp_len=1024), dict(S=3000, kv_len=2900, window=700, temp_len=100),
+    dict(S=3000, kv_len=2900, Hq=32, Hkv=1, bias_range=512, temp_len=300),
+    dict(S=2000, kv_len=900, mode="table", bias_range=300, temp_len=1000),
 ]
 
 
@@ -253,8 +266,9 @@ def test_decode_small(kw):
 
 
 @pytest.mark.parametrize("kw", [dict(mode="rproj", window=0), dict(mode="table", window=20),
-                                dict(mode="rproj_shared", window=40, logit_scale="inv_d")],
-                         ids=["rproj", "table_window", "rproj_shared"])
+                                dict(mode="rproj_shared", window=40, logit_scale="inv_d"),
+                                dict(mode="rproj", window=0, temp_len=16)],
+                         ids=["rproj", "table_window", "rproj_shared", "temp"])
 def test_decode_f32_small(kw):
     w = Workload(name="dec_f32", kind="decode", dtype="f32", B=2, Hq=4, Hkv=2, D=64, S=300,
                  bias_range=50, R=4, seed=3, **kw)

@@ -58,15 +58,15 @@ def load_library():
     lib = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.relbias_attn_fwd.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp, i,
-                                     f, vp]
+                                     f, i, vp]
     lib.relbias_attn_fwd.restype = i
     lib.relbias_attn_decode.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp, vp,
-                                        vp, i, f, vp, sz, vp]
+                                        vp, i, f, i, vp, sz, vp]
     lib.relbias_attn_decode.restype = i
     lib.relbias_attn_decode_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.relbias_attn_decode_workspace_size.restype = sz
     lib.relbias_attn_decode_paged.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
-                                              i, i, i, vp, vp, vp, i, f, vp, sz, vp]
+                                              i, i, i, vp, vp, vp, i, f, i, vp, sz, vp]
     lib.relbias_attn_decode_paged.restype = i
     lib.relbias_attn_decode_paged_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.relbias_attn_decode_paged_workspace_size.restype = sz
@@ -138,10 +138,11 @@ def _bias_args(mode, table, r, E, Hq, act_dtype, dev):
 
 
 def fwd(q, k, v, *, window=0, bias_range=0, mode="none", table=None, r=None, E=None,
-        scale=None, out=None, lse=None, return_lse=False, stream=None):
+        scale=None, temp_len=0, out=None, lse=None, return_lse=False, stream=None):
     """Prefill attention with a relative-position bias (relbias_attn_fwd).
 
     q [B,S,Hq,D], k/v [B,S,Hkv,D] (bf16 or fp32, contiguous, on one GPU).
+    temp_len: context-length temperature threshold (0: none; 131072 for the 128k form).
     Returns o [B,S,Hq,D] (and lse [B,Hq,S] fp32 when return_lse or lse is given).
     """
     import torch
@@ -168,7 +169,7 @@ def fwd(q, k, v, *, window=0, bias_range=0, mode="none", table=None, r=None, E=N
     st = lib.relbias_attn_fwd(_dtype_id(q), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                               B, S, Hq, Hkv, D, int(window), int(bias_range), m,
                               _ptr(table if m == 1 else None), _ptr(r if m in (2, 3) else None),
-                              _ptr(E if m in (2, 3) else None), R, float(scale),
+                              _ptr(E if m in (2, 3) else None), R, float(scale), int(temp_len),
                               _stream_handle(dev, stream))
     if st != RBA_OK:
         raise LibraryError(st, last_error())
@@ -180,8 +181,8 @@ def decode_workspace_size(B, Hq, Hkv, D, kv_len, window=0) -> int:
 
 
 def decode(q, k_cache, v_cache, kv_len, *, window=0, bias_range=0, mode="none", table=None,
-           r=None, E=None, scale=None, out=None, lse=None, workspace=None, return_lse=False,
-           stream=None):
+           r=None, E=None, scale=None, temp_len=0, out=None, lse=None, workspace=None,
+           return_lse=False, stream=None):
     """One decode step (relbias_attn_decode): q [B,Hq,D] at position kv_len-1.
 
     k_cache/v_cache [B,L_max,Hkv,D]; rows [0, kv_len) are valid and row kv_len-1
@@ -215,7 +216,7 @@ def decode(q, k_cache, v_cache, kv_len, *, window=0, bias_range=0, mode="none", 
                                  _ptr(lse), B, L_max, int(kv_len), Hq, Hkv, D, int(window),
                                  int(bias_range), m, _ptr(table if m == 1 else None),
                                  _ptr(r if m in (2, 3) else None), _ptr(E if m in (2, 3) else None), R,
-                                 float(scale), _ptr(workspace), wbytes,
+                                 float(scale), int(temp_len), _ptr(workspace), wbytes,
                                  _stream_handle(dev, stream))
     if st != RBA_OK:
         raise LibraryError(st, last_error())
@@ -223,8 +224,8 @@ def decode(q, k_cache, v_cache, kv_len, *, window=0, bias_range=0, mode="none", 
 
 
 def decode_paged(q, k_pages, v_pages, block_table, kv_lens, max_kv_len, *, window=0,
-                 bias_range=0, mode="none", table=None, r=None, E=None, scale=None, out=None,
-                 lse=None, workspace=None, return_lse=False, stream=None):
+                 bias_range=0, mode="none", table=None, r=None, E=None, scale=None, temp_len=0,
+                 out=None, lse=None, workspace=None, return_lse=False, stream=None):
     """One decode step over a paged cache (relbias_attn_decode_paged).
 
     q [B,Hq,D] bf16; k_pages/v_pages [num_pages, page_size, Hkv, D]; block_table int32
@@ -263,7 +264,7 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens, max_kv_len, *, windo
         _ptr(out), _ptr(lse), B, num_pages, page_size, int(block_table.shape[1]), int(max_kv_len),
         Hq, Hkv, D, int(window), int(bias_range), m, _ptr(table if m == 1 else None),
         _ptr(r if m in (2, 3) else None), _ptr(E if m in (2, 3) else None), R, float(scale),
-        _ptr(workspace), wbytes, _stream_handle(dev, stream))
+        int(temp_len), _ptr(workspace), wbytes, _stream_handle(dev, stream))
     if st != RBA_OK:
         raise LibraryError(st, last_error())
     return (out, lse) if (return_lse or lse is not None) else out

@@ -70,6 +70,16 @@ int check_common(const char* fn, int dtype, int Hq, int Hkv, int D, int window, 
   return RBA_OK;
 }
 
+// temp_len: 0 (no context-length temperature) or the visible-key count beyond which it grows.
+int check_temp(const char* fn, int temp_len) {
+  if (temp_len < 0 || temp_len == 1)
+    return fail(RBA_EINVAL, "%s: temp_len=%d must be 0 (no temperature) or >= 2", fn, temp_len);
+  return RBA_OK;
+}
+float temp_inv_log2(int temp_len) {
+  return temp_len > 0 ? static_cast<float>(1.0 / std::log2(static_cast<double>(temp_len))) : 0.f;
+}
+
 // The kernels know three bias modes; the shared bank is r.E with a head stride of 0 for E.
 int kernel_mode(int mode) { return mode == RBA_BIAS_RPROJ_SHARED ? RBA_BIAS_RPROJ : mode; }
 long long e_head_stride(int mode, int R, int bias_range) {
@@ -88,10 +98,11 @@ const char* relbias_attn_version(void) { return "relbias_attn 0.1 gfx950"; }
 int relbias_attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int S, int Hq, int Hkv, int D, int window, int bias_range, int mode,
                      const float* table, const void* r, const float* E, int R, float scale,
-                     void* stream) {
+                     int temp_len, void* stream) {
   const char* fn = "relbias_attn_fwd";
   if (B < 0 || S < 0) return fail(RBA_EINVAL, "%s: B=%d and S=%d must be >= 0", fn, B, S);
   int st = check_common(fn, dtype, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale);
+  if (st == RBA_OK) st = check_temp(fn, temp_len);
   if (st != RBA_OK) return st;
   if (B == 0 || S == 0) return ok();
   if (!q || !k || !v || !o) return fail(RBA_EINVAL, "%s: q, k, v and o must be non-NULL", fn);
@@ -129,6 +140,8 @@ int relbias_attn_fwd(int dtype, const void* q, const void* k, const void* v, voi
     a.R = is_rproj(mode) ? R : 0;
     a.e_hs = e_head_stride(mode, R, bias_range);
     a.c_qk = scale * rba::kLog2e;
+    a.temp_len = temp_len;
+    a.temp_inv_log2 = temp_inv_log2(temp_len);
     e = rba::launch_fwd_bf16(a, D, kernel_mode(mode), hs);
   } else {
     rba::F32Args a{};
@@ -155,6 +168,8 @@ int relbias_attn_fwd(int dtype, const void* q, const void* k, const void* v, voi
     a.R = is_rproj(mode) ? R : 0;
     a.e_hs = e_head_stride(mode, R, bias_range);
     a.scale = scale;
+    a.temp_len = temp_len;
+    a.temp_inv_log2 = temp_inv_log2(temp_len);
     e = rba::launch_attn_f32(a, hs);
   }
   if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
@@ -172,11 +187,12 @@ size_t relbias_attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int kv_
 int relbias_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
                         void* o, float* lse, int B, int L_max, int kv_len, int Hq, int Hkv, int D,
                         int window, int bias_range, int mode, const float* table, const void* r,
-                        const float* E, int R, float scale, void* workspace,
+                        const float* E, int R, float scale, int temp_len, void* workspace,
                         size_t workspace_bytes, void* stream) {
   const char* fn = "relbias_attn_decode";
   if (B < 0) return fail(RBA_EINVAL, "%s: B=%d must be >= 0", fn, B);
   int st = check_common(fn, dtype, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale);
+  if (st == RBA_OK) st = check_temp(fn, temp_len);
   if (st != RBA_OK) return st;
   if (B == 0) return ok();
   if (L_max < 1 || kv_len < 1 || kv_len > L_max)
@@ -225,6 +241,8 @@ int relbias_attn_decode(int dtype, const void* q, const void* k_cache, const voi
     a.n_split = ns;
     a.keys_per_wave = kpw;
     a.c_qk = scale * rba::kLog2e;
+    a.temp_len = temp_len;
+    a.temp_inv_log2 = temp_inv_log2(temp_len);
     e = rba::launch_decode_bf16(a, D, kernel_mode(mode), hs);
   } else {
     rba::F32Args a{};
@@ -251,6 +269,8 @@ int relbias_attn_decode(int dtype, const void* q, const void* k_cache, const voi
     a.R = is_rproj(mode) ? R : 0;
     a.e_hs = e_head_stride(mode, R, bias_range);
     a.scale = scale;
+    a.temp_len = temp_len;
+    a.temp_inv_log2 = temp_inv_log2(temp_len);
     e = rba::launch_attn_f32(a, hs);
   }
   if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
@@ -267,10 +287,12 @@ int relbias_attn_decode_paged(int dtype, const void* q, const void* k_pages, con
                               int B, int num_pages, int page_size, int max_pages, int max_kv_len,
                               int Hq, int Hkv, int D, int window, int bias_range, int mode,
                               const float* table, const void* r, const float* E, int R,
-                              float scale, void* workspace, size_t workspace_bytes, void* stream) {
+                              float scale, int temp_len, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   const char* fn = "relbias_attn_decode_paged";
   if (B < 0) return fail(RBA_EINVAL, "%s: B=%d must be >= 0", fn, B);
   int st = check_common(fn, dtype, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale);
+  if (st == RBA_OK) st = check_temp(fn, temp_len);
   if (st != RBA_OK) return st;
   if (B == 0) return ok();
   if (dtype != RBA_BF16) return fail(RBA_ENOTSUP, "%s: paged caches are supported for bf16 only", fn);
@@ -326,6 +348,8 @@ int relbias_attn_decode_paged(int dtype, const void* q, const void* k_pages, con
   a.n_split = ns;
   a.keys_per_wave = kpw;
   a.c_qk = scale * rba::kLog2e;
+  a.temp_len = temp_len;
+  a.temp_inv_log2 = temp_inv_log2(temp_len);
   a.block_table = block_table;
   a.kv_lens = kv_lens;
   a.page_size = page_size;

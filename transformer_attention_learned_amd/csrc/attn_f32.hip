@@ -46,6 +46,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Args a) {
     for (int f = 0; f < 16; ++f) rv[f] = (f < a.R && live) ? rp[f] : 0.f;
   }
   float m = -INFINITY, l = 0.f;
+  // context-length temperature of this query (keys 0..pos exist), on q.k and bias alike
+  const float tq = temp_factor(visible_keys(pos, a.window), a.temp_len, a.temp_inv_log2);
 
   // keys any row of this tile can see
   const int pos_lo = a.q_pos0 + qt * 64;
@@ -88,6 +90,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Args a) {
           s += bsum;
         }
       }
+      s *= tq;
       const float m_new = fmaxf(m, s);
       const float alpha = expf(m - m_new);
       const float p = expf(s - m_new);

@@ -68,6 +68,10 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
   // sized for) and first visible row
   const int kv_len = paged ? min(max(a.kv_lens[b], 0), a.kv_len) : a.kv_len;
   const int key_begin = paged ? (a.window ? max(0, kv_len - a.window) : 0) : a.key_begin;
+  // context-length temperature of this sequence's query, on q.k and bias alike
+  const float tq = temp_factor(visible_keys(kv_len - 1, a.window), a.temp_len, a.temp_inv_log2);
+  const float c_qk = a.c_qk * tq;
+  const float c_bias = kLog2e * tq;
   const uint16_t* kbase = a.k + static_cast<size_t>(hkv) * D + (paged ? 0 : static_cast<size_t>(b) * a.L_max * kv_row);
   const uint16_t* vbase = a.v + static_cast<size_t>(hkv) * D + (paged ? 0 : static_cast<size_t>(b) * a.L_max * kv_row);
   const int* bt = paged ? a.block_table + static_cast<size_t>(b) * a.max_pages : nullptr;
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
         for (int f = 0; f < RMAX; ++f)
           if (f < a.R) acc = fmaf(rs[n * a.R + f], e[u][f], acc);
       }
-      if (item < n_items) dst[item] = acc * kLog2e;
+      if (item < n_items) dst[item] = acc * c_bias;
     }
   };
   auto curve_finish = [&](int tk0, float* dst) {
@@ -242,7 +246,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = tk0 + 8 * (i >> 2) + 4 * lh + (i & 3);
-      float sv = sacc[i] * a.c_qk;
+      float sv = sacc[i] * c_qk;
       if (in_band) sv += cv[8 * (i >> 2) + (i & 3)];   // zero past the range and past the rows
       if (key >= w_end) sv = NEG_INF;
       sacc[i] = sv;
@@ -369,6 +373,10 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
   const bool paged = a.block_table != nullptr;
   const int kv_len = paged ? min(max(a.kv_lens[b], 0), a.kv_len) : a.kv_len;
   const int key_begin = paged ? (a.window ? max(0, kv_len - a.window) : 0) : a.key_begin;
+  // context-length temperature of this sequence's query, on q.k and bias alike
+  const float tq = temp_factor(visible_keys(kv_len - 1, a.window), a.temp_len, a.temp_inv_log2);
+  const float c_qk = a.c_qk * tq;
+  const float c_bias = kLog2e * tq;
   const uint16_t* kbase = a.k + static_cast<size_t>(hkv) * D + (paged ? 0 : static_cast<size_t>(b) * a.L_max * kv_row);
   const uint16_t* vbase = a.v + static_cast<size_t>(hkv) * D + (paged ? 0 : static_cast<size_t>(b) * a.L_max * kv_row);
   const int* bt = paged ? a.block_table + static_cast<size_t>(b) * a.max_pages : nullptr;
@@ -477,7 +485,7 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
         for (int f = 0; f < RMAX; ++f)
           if (f < a.R) acc = fmaf(rs[n * a.R + f], e[u][f], acc);
       }
-      if (item < n_items) dst[item] = acc * kLog2e;
+      if (item < n_items) dst[item] = acc * c_bias;
     }
   };
   // (the inputs are fetched where they are used: registers go to the tiles in flight)
@@ -541,7 +549,7 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = tk0 + 16 * kb + 4 * g + i;
-        float sv = sacc[kb][i] * a.c_qk;
+        float sv = sacc[kb][i] * c_qk;
         if (in_band) sv += cv[16 * kb + i];
         if (key >= w_end) sv = NEG_INF;
         sacc[kb][i] = sv;

@@ -288,6 +288,11 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(FwdArgs 
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
+        if (a.temp_len) {   // context-length temperature of the lane's query row, on q.k and bias
+          const float tq = temp_factor(visible_keys(i0 + 32 * qb + ln, a.window), a.temp_len, a.temp_inv_log2);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[qb][kb][i] *= tq;
+        }
         const bool edge = (c - 31 < 0) || (a.window && c + 31 >= a.window);
         if (edge) {
 #pragma unroll

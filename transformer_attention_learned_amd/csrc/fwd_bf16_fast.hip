@@ -115,6 +115,12 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
 
   const float cqk = a.c_qk;              // scale * log2(e)
   const float inv_scale = kLog2e / cqk;  // bias -> accumulator units (bias / scale)
+  // per query row: scale * log2(e) times the row's context-length temperature, which
+  // multiplies the q.k term and the bias alike (both sit in the accumulator)
+  float cqk_r[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+    cqk_r[qb] = cqk * temp_factor(visible_keys(i0w + 32 * qb + ln, W), a.temp_len, a.temp_inv_log2);
 
   const size_t q_row = static_cast<size_t>(a.Hq) * D;
   const size_t kv_row = static_cast<size_t>(a.Hkv) * D;
@@ -504,8 +510,8 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
         uint32_t w[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const float p0 = fast_exp2(fmaf(acc[qb][8 * kk + 2 * jj], cqk, -m_use[qb]));
-          const float p1 = fast_exp2(fmaf(acc[qb][8 * kk + 2 * jj + 1], cqk, -m_use[qb]));
+          const float p0 = fast_exp2(fmaf(acc[qb][8 * kk + 2 * jj], cqk_r[qb], -m_use[qb]));
+          const float p1 = fast_exp2(fmaf(acc[qb][8 * kk + 2 * jj + 1], cqk_r[qb], -m_use[qb]));
           w[jj] = pack_bf16x2(p0, p1);
           psum = sum_bf16x2(w[jj], psum);
         }
@@ -522,7 +528,7 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
 #pragma unroll
       for (int i = 3; i < 15; i += 2) v = fmaxf(fmaxf(v, acc[qb][i]), acc[qb][i + 1]);
       v = fmaxf(v, acc[qb][15]);
-      mx[qb] = pair_max(v) * cqk;
+      mx[qb] = pair_max(v) * cqk_r[qb];
     }
   };
   // Lazy rescale: move the running max only when a row grew by more than 2^kRescale.

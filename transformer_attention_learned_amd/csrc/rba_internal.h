@@ -5,10 +5,30 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 namespace rba {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// Context-length temperature of a query that sees n keys: 1 while n <= temp_len, then
+// log(n) / log(temp_len), a factor on both the q.k term and the bias ("Thinking Machines
+// dropped RoPE", section "The temperature scale is dependent on context length": flat up to
+// 128k visible keys, logarithmic growth beyond).  temp_len == 0: no temperature.
+// inv_log2_len = 1 / log2(temp_len).
+__host__ __device__ inline float temp_factor(int n, int temp_len, float inv_log2_len) {
+#ifdef __HIP_DEVICE_COMPILE__
+  return (temp_len > 0 && n > temp_len) ? __builtin_amdgcn_logf(static_cast<float>(n)) * inv_log2_len : 1.f;
+#else
+  return (temp_len > 0 && n > temp_len) ? static_cast<float>(std::log2(static_cast<double>(n))) * inv_log2_len : 1.f;
+#endif
+}
+
+// Keys a query at position `pos` sees when keys 0..pos exist (window 0: all of them).
+__host__ __device__ inline int visible_keys(int pos, int window) {
+  return window ? (pos + 1 < window ? pos + 1 : window) : pos + 1;
+}
 
 // Prefill arguments (bf16 MFMA path).  Strides are implied by the dense shapes
 // q/o [B,S,Hq,D], k/v [B,S,Hkv,D], r [B,S,Hq,R], lse [B,Hq,S].
@@ -32,6 +52,8 @@ struct FwdArgs {
   int n_hgroups;        // Hq / hpw
   int longest_first;    // schedule query tiles with the most keys first
   float c_qk;           // scale * log2(e)
+  int temp_len;         // context-length temperature threshold (0: none)
+  float temp_inv_log2;  // 1 / log2(temp_len)
 };
 
 // Generic fp32 attention (VALU): queries at positions q_pos0 + i, keys at
@@ -52,6 +74,8 @@ struct F32Args {
   int q_pos0;           // position of query 0
   int window, bias_range, mode, R;
   float scale;
+  int temp_len;         // context-length temperature threshold (0: none)
+  float temp_inv_log2;  // 1 / log2(temp_len)
 };
 
 // Decode arguments (bf16 MFMA path).
@@ -78,6 +102,8 @@ struct DecodeArgs {
   int n_split;          // workgroups per (b, kv head); each has 4 waves
   int keys_per_wave;    // multiple of 64
   float c_qk;
+  int temp_len;         // context-length temperature threshold (0: none)
+  float temp_inv_log2;  // 1 / log2(temp_len)
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int D, int mode, hipStream_t s);

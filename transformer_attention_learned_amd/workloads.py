@@ -51,6 +51,7 @@ class Workload:
     table_trend: float = 0.0  # added to table[h, delta]: trend * delta
     e_std: float = 0.1
     logit_scale: str = "rsqrt_d"   # "rsqrt_d": 1/sqrt(D); "inv_d": 1/D (the essay's Inkling form)
+    temp_len: int = 0         # context-length temperature threshold (0: none)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -67,6 +68,10 @@ class Workload:
         return Workload(**d)
 
 
+# Global layers carry the context-length temperature, flat up to 128k visible keys (at these
+# lengths it is exactly 1, but the kernels take the tempered path).
+GLOBAL_TEMP_LEN = 131072
+
 WORKLOADS = {
     "tiny_local_f32": Workload("tiny_local_f32", "prefill", "f32", B=1, Hq=1, Hkv=1, D=32, S=256,
                                window=64, bias_range=64, mode="table", seed=1, table_std=0.5),
@@ -75,19 +80,21 @@ WORKLOADS = {
                               rmsnorm_qk=True),
     "global_prefill": Workload("global_prefill", "prefill", "bf16", B=1, Hq=32, Hkv=8, D=128,
                                S=32768, window=0, bias_range=1024, mode="rproj", seed=3,
-                               rmsnorm_qk=True),
+                               rmsnorm_qk=True, temp_len=GLOBAL_TEMP_LEN),
     "long_global_prefill": Workload("long_global_prefill", "prefill", "bf16", B=1, Hq=16, Hkv=4,
                                     D=128, S=131072, window=0, bias_range=1024, mode="table",
-                                    seed=4, rmsnorm_qk=True, table_std=0.5, table_trend=-0.01),
+                                    seed=4, rmsnorm_qk=True, table_std=0.5, table_trend=-0.01,
+                                    temp_len=GLOBAL_TEMP_LEN),
     "decode_global": Workload("decode_global", "decode", "bf16", B=64, Hq=32, Hkv=8, D=128,
-                              S=65536, window=0, bias_range=1024, mode="rproj", seed=5),
+                              S=65536, window=0, bias_range=1024, mode="rproj", seed=5,
+                              temp_len=GLOBAL_TEMP_LEN),
     "decode_local": Workload("decode_local", "decode", "bf16", B=64, Hq=32, Hkv=8, D=128,
                              S=65536, window=512, bias_range=512, mode="rproj", seed=5),
     # the same decode steps over a paged cache: 64-row pages in a pool, each sequence's pages
     # scattered by a seeded permutation (the page-table layout of a serving engine)
     "decode_global_paged": Workload("decode_global_paged", "decode", "bf16", B=64, Hq=32, Hkv=8,
                                     D=128, S=65536, window=0, bias_range=1024, mode="rproj", seed=5,
-                                    extra={"page_size": 64}),
+                                    temp_len=GLOBAL_TEMP_LEN, extra={"page_size": 64}),
     "decode_local_paged": Workload("decode_local_paged", "decode", "bf16", B=64, Hq=32, Hkv=8,
                                    D=128, S=65536, window=512, bias_range=512, mode="rproj", seed=5,
                                    extra={"page_size": 64}),
