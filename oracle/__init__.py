@@ -3,8 +3,9 @@
 Only tests, the smoke check and the benchmark's CPU-baseline leg use this
 package; the product path never imports it.
 """
-from .relbias_oracle import (MODE_NONE, MODE_TABLE, MODE_RPROJ, attention, bias_matrix,
-                             decode, prefill, temperature, visible_mask)
+from .relbias_oracle import (MODE_NONE, MODE_TABLE, MODE_RPROJ, attention,
+                             attention_backward, bias_matrix, decode, prefill, prefill_backward,
+                             temperature, visible_mask)
 
-__all__ = ["MODE_NONE", "MODE_TABLE", "MODE_RPROJ", "attention", "bias_matrix", "decode",
-           "prefill", "temperature", "visible_mask"]
+__all__ = ["MODE_NONE", "MODE_TABLE", "MODE_RPROJ", "attention", "attention_backward",
+           "bias_matrix", "decode", "prefill", "prefill_backward", "temperature", "visible_mask"]

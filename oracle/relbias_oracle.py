@@ -59,6 +59,10 @@ Readings where the pages are silent or garbled (each is pinned by a test):
     logit, content term and bias alike.
 
 Inputs are taken as stored (bf16 / fp32 values upcast to float64).
+
+attention_backward / prefill_backward give the gradients of the same definition (chain rule
+written out per batch and head); they are pinned against torch autograd through SDPA, central
+finite differences and exact identities of the softmax gradient.
 """
 
 from __future__ import annotations
@@ -246,3 +250,96 @@ def decode(q, k_cache, v_cache, kv_len, *, scale, window=0, bias_range=0, mode="
         lses.append(l[0, :, 0])
     return np.stack(outs), np.stack(lses)
 
+
+
+def attention_backward(q, k, v, dout, *, qpos, kpos, scale, window=0, bias_range=0,
+                       mode="none", table=None, r=None, E=None, temp_len=0):
+    """Gradients of attention() for an upstream gradient dout on o, float64.
+
+    The bias is learned ("Thinking Machines dropped RoPE": the bank of distance functions
+    and the coefficient projection are trained with the model; "Learned Relative-Position
+    Bias", section "Standard Relative Bias (T5-style)": the table is a learned parameter),
+    so the parameters that shape it get gradients too.  Plain chain rule of the definition,
+    per (batch, head), no tiling:
+      P = softmax of the masked logits s, o = P v
+      dP = dout v^T,  dS = P * (dP - rowsum(dout * o))      (gradient on s)
+      dZ = tau * dS      (gradient on scale * q.k + beta; tau = temperature, 1 if none)
+      dq = scale * dZ k,  dk = scale * dZ^T q,  dv = P^T dout   (GQA: kv heads sum their
+      query heads)
+      beta's gradient is dZ at the in-band pairs (0 <= delta < bias_range):
+        TABLE:  dtable[h, d] = sum of dZ over the pairs at distance d
+        RPROJ:  with dC[i, d] = sum of dZ[i, j] over keys at distance d from query i,
+                dr[b, i, h, :] = dC[i] @ E[h]^T  and  dE[h] += r[b, :, h, :]^T @ dC
+        RPROJ_SHARED: the same with E [R, bias_range], dE summed over heads.
+
+    q [B, Sq, Hq, D], k/v [B, Sk, Hkv, D], dout like q.  Returns a dict with dq, dk, dv and
+    dtable (TABLE) or dr and dE (RPROJ, RPROJ_SHARED).
+    """
+    mode = _MODES[mode]
+    q64, k64, v64, do64 = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Sq, Hq, D = q64.shape
+    Hkv = k64.shape[2]
+    G = Hq // Hkv
+    qpos = np.asarray(qpos, dtype=np.int64)
+    kpos = np.asarray(kpos, dtype=np.int64)
+    rproj = mode in (MODE_RPROJ, MODE_RPROJ_SHARED)
+    r64 = _f64(r) if rproj else None
+    E64 = _f64(E) if rproj else None
+    tab64 = _f64(table) if mode == MODE_TABLE else None
+    dq = np.zeros_like(q64)
+    dk = np.zeros_like(k64)
+    dv = np.zeros_like(v64)
+    out = {"dq": dq, "dk": dk, "dv": dv}
+    if mode == MODE_TABLE:
+        out["dtable"] = np.zeros_like(tab64)
+    if rproj:
+        out["dr"] = np.zeros_like(r64)
+        out["dE"] = np.zeros_like(E64)
+    delta = qpos[:, None] - kpos[None, :]
+    vis = visible_mask(qpos, kpos, window)
+    tau = temperature(vis.sum(axis=1), temp_len)[:, None]
+    inband = vis & (delta >= 0) & (delta < bias_range) if mode != MODE_NONE else None
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            qq, kk, vv, dd = q64[b, :, h, :], k64[b, :, g, :], v64[b, :, g, :], do64[b, :, h, :]
+            beta = bias_matrix(mode, qpos, kpos, bias_range, h, table=tab64,
+                               r_rows=None if r64 is None else r64[b, :, h, :], E=E64)
+            s = np.where(vis, tau * (scale * (qq @ kk.T) + beta), -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            p /= p.sum(axis=1, keepdims=True)
+            o = p @ vv
+            dp = dd @ vv.T
+            ds = p * (dp - (dd * o).sum(axis=1, keepdims=True))
+            dz = tau * ds
+            dq[b, :, h, :] = scale * (dz @ kk)
+            dk[b, :, g, :] += scale * (dz.T @ qq)
+            dv[b, :, g, :] += p.T @ dd
+            if mode == MODE_NONE:
+                continue
+            ii, jj = np.nonzero(inband)
+            dist = delta[ii, jj]
+            if mode == MODE_TABLE:
+                np.add.at(out["dtable"][h], dist, dz[ii, jj])
+            else:
+                dC = np.zeros((Sq, bias_range))
+                np.add.at(dC, (ii, dist), dz[ii, jj])
+                bank = E64 if mode == MODE_RPROJ_SHARED else E64[h]    # [R, bias_range]
+                out["dr"][b, :, h, :] = dC @ bank.T
+                gE = r64[b, :, h, :].T @ dC                            # [R, bias_range]
+                if mode == MODE_RPROJ_SHARED:
+                    out["dE"] += gE
+                else:
+                    out["dE"][h] += gE
+    return out
+
+
+def prefill_backward(q, k, v, dout, *, scale, window=0, bias_range=0, mode="none", table=None,
+                     r=None, E=None, temp_len=0):
+    """attention_backward for a prefill (query i and key j at positions i and j)."""
+    S = q.shape[1]
+    pos = np.arange(S, dtype=np.int64)
+    return attention_backward(q, k, v, dout, qpos=pos, kpos=pos, scale=scale, window=window,
+                              bias_range=bias_range, mode=mode, table=table, r=r, E=E,
+                              temp_len=temp_len)
