@@ -175,6 +175,50 @@ int relbias_attn_decode_paged(int dtype, const void* q, const void* k_pages, con
                               float scale, int temp_len, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/*
+ * Bytes of device workspace relbias_attn_bwd needs: one fp32 per (batch, row, query head).
+ * Pure host function.
+ */
+size_t relbias_attn_bwd_workspace_size(int B, int S, int Hq);
+
+/*
+ * Backward of relbias_attn_fwd: gradients of a scalar loss given its gradient dout on o.
+ * The bias is a learned part of the layer ("Thinking Machines dropped RoPE": the bank of
+ * distance curves and the coefficient projection are trained with the model; "Learned
+ * Relative-Position Bias", section "Standard Relative Bias (T5-style)": the table is a
+ * learned parameter), so the call also returns the gradient of the bias parameters.
+ * With P the forward's softmax and tau the temperature (1 when temp_len = 0):
+ *   dP = dout v^T,  dS = P * (dP - rowsum(dout * o)),  dZ = tau * dS,
+ *   dq = scale dZ k,  dk = scale dZ^T q,  dv = P^T dout  (kv heads sum their query heads),
+ *   at in-band pairs the bias gradient is dZ, reduced to dtable[h, d] (sum along the
+ *   diagonal at distance d), or to dr[token, h, f] = sum_j dZ E[h, f, delta] and
+ *   dE[h, f, d] = sum over tokens of r[token, h, f] dZ at distance d (summed over heads
+ *   for RBA_BIAS_RPROJ_SHARED).
+ *
+ *   dtype       RBA_BF16 only (RBA_ENOTSUP otherwise); D in {64, 128}.
+ *   q, k, v, window, bias_range, mode, table, r, E, R, scale, temp_len, shapes:
+ *               exactly as passed to relbias_attn_fwd.
+ *   o           [B, S, Hq, D]: the forward's output.
+ *   lse         [B, Hq, S] fp32: the forward's log-sum-exp (required).
+ *   dout        [B, S, Hq, D]: gradient of the loss on o.
+ *   dq          [B, S, Hq, D] (written); dk, dv [B, S, Hkv, D] (written).
+ *   dtable      RBA_BIAS_TABLE: [Hq, bias_range] fp32 (written); else ignored.
+ *   dr          RBA_BIAS_RPROJ(_SHARED): [B, S, Hq, R] of dtype (written); else ignored.
+ *   dE          RBA_BIAS_RPROJ: [Hq, R, bias_range] fp32; RBA_BIAS_RPROJ_SHARED:
+ *               [R, bias_range] fp32 (written); else ignored.
+ *   workspace   device scratch of at least relbias_attn_bwd_workspace_size(B, S, Hq)
+ *               bytes; contents on entry are ignored.  Calls that share one workspace,
+ *               dtable or dE must be ordered on one stream.
+ * dtable and dE are summed with fp32 atomics, so their last bits may differ between runs;
+ * dq, dk, dv and dr are deterministic.
+ */
+int relbias_attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     float* dtable, void* dr, float* dE, int B, int S, int Hq, int Hkv, int D,
+                     int window, int bias_range, int mode, const float* table, const void* r,
+                     const float* E, int R, float scale, int temp_len, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
 /* Message for the calling thread's last non-OK status ("" if none).  The pointer
  * stays valid until the next call on the same thread. */
 const char* relbias_attn_last_error(void);

@@ -36,7 +36,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"relbias_attn_fwd", "relbias_attn_decode",
                           "relbias_attn_decode_workspace_size", "relbias_attn_decode_paged",
                           "relbias_attn_decode_paged_workspace_size", "relbias_attn_last_error",
-                          "relbias_attn_version"}
+                          "relbias_attn_version", "relbias_attn_bwd",
+                          "relbias_attn_bwd_workspace_size"}
     for n in names:
         assert hasattr(lib, n), n
     assert "gfx950" in rba.version()
@@ -185,3 +186,43 @@ def test_decode_paged_empty_and_workspace(lib):
     for args in [(64, 32, 8, 128, 65536, 0), (64, 32, 8, 128, 65536, 512), (1, 4, 1, 64, 100, 0)]:
         assert (lib.relbias_attn_decode_paged_workspace_size(*args)
                 == lib.relbias_attn_decode_workspace_size(*args))
+
+
+def _bwd(lib, **kw):
+    a = dict(dtype=BF16, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, dtable=None, dr=None,
+             dE=None, B=1, S=16, Hq=4, Hkv=2, D=128, window=0, bias_range=8, mode=0, table=None,
+             r=None, E=None, R=0, scale=0.1, temp_len=0, ws=P, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.relbias_attn_bwd(
+        a["dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+        a["dtable"], a["dr"], a["dE"], a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["window"],
+        a["bias_range"], a["mode"], a["table"], a["r"], a["E"], a["R"], a["scale"],
+        a["temp_len"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(dtype=F32), ENOTSUP, "bf16 only"),
+    (dict(dtype=7), EINVAL, "dtype"),
+    (dict(Hq=6, Hkv=4), EINVAL, "multiple"),
+    (dict(D=96), ENOTSUP, "head_dim"),
+    (dict(lse=None), EINVAL, "non-NULL"),
+    (dict(do=None), EINVAL, "non-NULL"),
+    (dict(dk=P + 8), EINVAL, "aligned"),
+    (dict(mode=1, table=P, dtable=None), EINVAL, "dtable"),
+    (dict(mode=2, r=P, E=P, R=8, dr=P, dE=None), EINVAL, "dr and dE"),
+    (dict(mode=3, r=P, E=P, R=8, dr=None, dE=P), EINVAL, "dr and dE"),
+    (dict(ws=None), EINVAL, "workspace"),
+    (dict(wsb=4), EINVAL, "too small"),
+    (dict(temp_len=1), EINVAL, "temp_len"),
+    (dict(B=-1), EINVAL, "B="),
+])
+def test_bwd_rejects(lib, kw, code, needle):
+    assert _bwd(lib, **kw) == code
+    assert needle in rba.last_error()
+
+
+def test_bwd_empty_and_workspace(lib):
+    assert _bwd(lib, B=0) == 0
+    assert _bwd(lib, S=0, q=None) == 0
+    assert lib.relbias_attn_bwd_workspace_size(2, 100, 8) == 2 * 100 * 8 * 4
+    assert lib.relbias_attn_bwd_workspace_size(0, 100, 8) == 0

@@ -22,7 +22,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "decode", "decode_paged", "decode_workspace_size", "last_error", "version", "library_path",
+__all__ = ["fwd", "bwd", "decode", "decode_paged", "decode_workspace_size", "last_error", "version",
+           "library_path",
            "load_library", "RBA_OK", "RBA_EINVAL", "RBA_ENOTSUP", "RBA_EHIP", "MODES",
            "LibraryError"]
 
@@ -70,6 +71,11 @@ def load_library():
     lib.relbias_attn_decode_paged.restype = i
     lib.relbias_attn_decode_paged_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.relbias_attn_decode_paged_workspace_size.restype = sz
+    lib.relbias_attn_bwd.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i,
+                                     i, i, i, i, vp, vp, vp, i, f, i, vp, sz, vp]
+    lib.relbias_attn_bwd.restype = i
+    lib.relbias_attn_bwd_workspace_size.argtypes = [i, i, i]
+    lib.relbias_attn_bwd_workspace_size.restype = sz
     lib.relbias_attn_last_error.argtypes = []
     lib.relbias_attn_last_error.restype = ctypes.c_char_p
     lib.relbias_attn_version.argtypes = []
@@ -174,6 +180,56 @@ def fwd(q, k, v, *, window=0, bias_range=0, mode="none", table=None, r=None, E=N
     if st != RBA_OK:
         raise LibraryError(st, last_error())
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def bwd(q, k, v, o, lse, dout, *, window=0, bias_range=0, mode="none", table=None, r=None,
+        E=None, scale=None, temp_len=0, workspace=None, stream=None):
+    """Backward of fwd (relbias_attn_bwd): gradients for an upstream gradient dout on o.
+
+    q, k, v, window, bias_range, mode, table, r, E, scale, temp_len: as passed to fwd;
+    o and lse [B,Hq,S] fp32: fwd's outputs.  bf16 only.  Returns a dict with dq, dk, dv and
+    dtable (mode "table") or dr and dE (modes "rproj", "rproj_shared").
+    """
+    import torch
+    lib = load_library()
+    dev = q.device
+    _check(q, "q", ndim=4)
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check(t, n, dtype=q.dtype, ndim=4, device=dev)
+    _check(lse, "lse", dtype=torch.float32, ndim=3, device=dev)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, S, Hkv, D) or tuple(v.shape) != (B, S, Hkv, D):
+        raise ValueError(f"k/v must be [B,S,Hkv,D] = {(B, S, Hkv, D)}")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must have q's shape")
+    if tuple(lse.shape) != (B, Hq, S):
+        raise ValueError(f"lse must be [B,Hq,S] = {(B, Hq, S)}")
+    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev)
+    if m in (2, 3) and tuple(r.shape) != (B, S, Hq, R):
+        raise ValueError(f"r must be [B,S,Hq,R] = {(B, S, Hq, R)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v)}
+    if m == 1:
+        out["dtable"] = torch.empty_like(table)
+    if m in (2, 3):
+        out["dr"] = torch.empty_like(r)
+        out["dE"] = torch.empty_like(E)
+    need = lib.relbias_attn_bwd_workspace_size(B, S, Hq)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.relbias_attn_bwd(
+        _dtype_id(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(out["dq"]),
+        _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out.get("dtable")), _ptr(out.get("dr")),
+        _ptr(out.get("dE")), B, S, Hq, Hkv, D, int(window), int(bias_range), m,
+        _ptr(table if m == 1 else None), _ptr(r if m in (2, 3) else None),
+        _ptr(E if m in (2, 3) else None), R, float(scale), int(temp_len), _ptr(workspace), wbytes,
+        _stream_handle(dev, stream))
+    if st != RBA_OK:
+        raise LibraryError(st, last_error())
+    return out
 
 
 def decode_workspace_size(B, Hq, Hkv, D, kv_len, window=0) -> int:

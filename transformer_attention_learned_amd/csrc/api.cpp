@@ -360,4 +360,79 @@ int relbias_attn_decode_paged(int dtype, const void* q, const void* k_pages, con
   return ok();
 }
 
+size_t relbias_attn_bwd_workspace_size(int B, int S, int Hq) {
+  if (B <= 0 || S <= 0 || Hq <= 0) return 0;
+  return static_cast<size_t>(B) * S * Hq * sizeof(float);
+}
+
+int relbias_attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     float* dtable, void* dr, float* dE, int B, int S, int Hq, int Hkv, int D,
+                     int window, int bias_range, int mode, const float* table, const void* r,
+                     const float* E, int R, float scale, int temp_len, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  const char* fn = "relbias_attn_bwd";
+  if (B < 0 || S < 0) return fail(RBA_EINVAL, "%s: B=%d and S=%d must be >= 0", fn, B, S);
+  int st = check_common(fn, dtype, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale);
+  if (st == RBA_OK) st = check_temp(fn, temp_len);
+  if (st != RBA_OK) return st;
+  if (dtype != RBA_BF16) return fail(RBA_ENOTSUP, "%s: the backward pass is supported for bf16 only", fn);
+  if (B == 0 || S == 0) return ok();
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return fail(RBA_EINVAL, "%s: q, k, v, o, lse, dout, dq, dk and dv must be non-NULL", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(RBA_EINVAL, "%s: q, k, v, o, dout, dq, dk and dv must be 16-byte aligned", fn);
+  if (!aligned_to(lse, 4)) return fail(RBA_EINVAL, "%s: lse is not 4-byte aligned", fn);
+  if (mode == RBA_BIAS_TABLE && (!dtable || !aligned_to(dtable, 4)))
+    return fail(RBA_EINVAL, "%s: table mode needs a 4-byte aligned dtable", fn);
+  if (is_rproj(mode) && (!dr || !dE || !aligned_to(dr, 2) || !aligned_to(dE, 4)))
+    return fail(RBA_EINVAL, "%s: rproj modes need aligned dr and dE", fn);
+  const long long rows = static_cast<long long>(B) * S;
+  if (rows * Hq * D >= (1LL << 40)) return fail(RBA_ENOTSUP, "%s: problem too large", fn);
+  if (rba::bwd_lds_bytes(D, kernel_mode(mode), bias_range) < 0)
+    return fail(RBA_ENOTSUP, "%s: bias_range=%d needs more LDS than the kernels have", fn, bias_range);
+  const size_t need = relbias_attn_bwd_workspace_size(B, S, Hq);
+  if (!workspace) return fail(RBA_EINVAL, "%s: workspace of %zu bytes required, got NULL", fn, need);
+  if (workspace_bytes < need)
+    return fail(RBA_EINVAL, "%s: workspace too small (%zu < %zu bytes)", fn, workspace_bytes, need);
+  if (!aligned_to(workspace, 4)) return fail(RBA_EINVAL, "%s: workspace is not 4-byte aligned", fn);
+  const int G = Hq / Hkv;
+  const long long nq = ((S + 127) / 128) * static_cast<long long>(Hq) * B;
+  if (nq > 0x7fffffffLL) return fail(RBA_ENOTSUP, "%s: grid too large", fn);
+  rba::BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.dr = static_cast<uint16_t*>(dr);
+  a.dE = dE;
+  a.dtable = dtable;
+  a.table = table;
+  a.r = static_cast<const uint16_t*>(r);
+  a.E = E;
+  a.e_hs = e_head_stride(mode, R, bias_range);
+  a.dsum = static_cast<float*>(workspace);
+  a.B = B;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.window = window;
+  a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
+  a.R = is_rproj(mode) ? R : 0;
+  a.c_qk = scale * rba::kLog2e;
+  a.scale = scale;
+  a.temp_len = temp_len;
+  a.temp_inv_log2 = temp_inv_log2(temp_len);
+  hipError_t e = rba::launch_bwd_bf16(a, D, kernel_mode(mode), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

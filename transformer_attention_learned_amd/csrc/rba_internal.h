@@ -106,7 +106,38 @@ struct DecodeArgs {
   float temp_inv_log2;  // 1 / log2(temp_len)
 };
 
+// Backward arguments (bf16 MFMA path).  Shapes as in FwdArgs; dq like q, dk / dv like k / v,
+// dr like r (bf16), dE like E and dtable like table (fp32, accumulated; zeroed by the pre pass).
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;     // [B, Hq, S] natural-log sum-exp of the forward
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  uint16_t* dr;         // [B, S, Hq, R]
+  float* dE;            // head h at dE + h * e_hs
+  float* dtable;        // [Hq, bias_range]
+  const float* table;
+  const uint16_t* r;
+  const float* E;
+  long long e_hs;       // head stride of E and dE in floats (0: one shared bank)
+  float* dsum;          // workspace [B, Hq, S]: rowsum(dout * o)
+  int B, S, Hq, Hkv, G;
+  int window, bias_range, R;
+  float c_qk;           // scale * log2(e)
+  float scale;
+  int temp_len;
+  float temp_inv_log2;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, int D, int mode, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int D, int mode, hipStream_t s);
+// LDS bytes of the larger backward kernel for this shape, or -1 when it does not fit.
+int bwd_lds_bytes(int D, int mode, int bias_range);
 // Fast prefill path (head_dim 128, Hq/Hkv a multiple of 4): LDS bytes it needs, or -1
 // when the shape is outside its domain; and its launcher.
 int fwd_fast_lds_bytes(int D, int G, int mode, int bias_range, int R, float scale);
