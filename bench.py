@@ -10,8 +10,11 @@ prefill kernel and the float64 oracle timed on this host as a CPU baseline.
                   [--no-cpu-baseline] [--cpu-seconds T]
 
 Other workloads (--workload): global_prefill, long_global_prefill,
-decode_global, decode_local, tiny_local_f32, and decode_global_paged /
-decode_local_paged (the decode steps over a paged cache, 64-row pages).
+decode_global, decode_local, tiny_local_f32, decode_global_paged /
+decode_local_paged (the decode steps over a paged cache, 64-row pages), and
+local_prefill_bwd / global_prefill_bwd / long_global_prefill_bwd (one
+relbias_attn_bwd call per step, the forward's o and lse computed before timing;
+10*D algorithmic flops per visible pair: the five products of the backward).
 """
 
 from __future__ import annotations
@@ -36,6 +39,7 @@ KERNEL_SOURCES = {
     "prefill": ["fwd_bf16.hip", "fwd_bf16_fast.hip"],
     "decode": ["decode_bf16.hip"],
     "f32": ["attn_f32.hip"],
+    "backward": ["bwd_bf16.hip"],
 }
 
 
@@ -89,7 +93,30 @@ def cpu_baseline(w, inp, seconds: float):
         cores = 1
     G = w.Hq // w.Hkv
     done_flops, t_total, n_slices = 0.0, 0.0, 0
-    if w.kind == "prefill":
+    if w.kind == "backward":
+        # one (batch, kv-group) slice over a causal prefix of the sequence (a prefix is an
+        # exact sub-problem): the float64 score matrices of the whole sequence do not fit
+        Sp = min(w.S, 4096)
+        pairs = visible_pairs_prefill(Sp, w.window)
+        for g in range(w.Hkv):
+            hs = slice(g * G, (g + 1) * G)
+            cut = lambda t: None if t is None else t[:1, :Sp, hs].contiguous().cpu()
+            k = inp["k"][:1, :Sp, g:g + 1].contiguous().cpu()
+            v = inp["v"][:1, :Sp, g:g + 1].contiguous().cpu()
+            tab = None if inp["table"] is None else inp["table"][hs].cpu()
+            E = None if inp["E"] is None else inp["E"][hs].cpu()
+            t0 = time.perf_counter()
+            oracle.prefill_backward(cut(inp["q"]), k, v, cut(inp["dout"]), scale=w.scale,
+                                    window=w.window, bias_range=w.bias_range, mode=w.mode,
+                                    table=tab, r=cut(inp["r"]), E=E, temp_len=w.temp_len)
+            t_total += time.perf_counter() - t0
+            done_flops += 10.0 * w.D * G * pairs
+            n_slices += 1
+            if t_total >= seconds:
+                break
+        sample = (f"{n_slices} of {w.Hkv} kv-group slices of batch 0, first {Sp} rows, "
+                  f"{G} query heads each")
+    elif w.kind == "prefill":
         pairs = visible_pairs_prefill(w.S, w.window)
         for b in range(w.B):
             for g in range(w.Hkv):
@@ -169,7 +196,23 @@ def main():
     inp = make_inputs(w, device=dev)
     torch.cuda.synchronize()
 
-    if w.kind == "prefill":
+    if w.kind == "backward":
+        o, lse = rba.fwd(inp["q"], inp["k"], inp["v"], window=w.window, bias_range=w.bias_range,
+                         mode=w.mode, table=inp["table"], r=inp["r"], E=inp["E"], scale=w.scale,
+                         temp_len=w.temp_len, return_lse=True)
+        ws = torch.empty(max(rba.load_library().relbias_attn_bwd_workspace_size(w.B, w.S, w.Hq), 1),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            rba.bwd(inp["q"], inp["k"], inp["v"], o, lse, inp["dout"], window=w.window,
+                    bias_range=w.bias_range, mode=w.mode, table=inp["table"], r=inp["r"],
+                    E=inp["E"], scale=w.scale, temp_len=w.temp_len, workspace=ws)
+
+        flops = 10.0 * w.D * w.Hq * w.B * visible_pairs_prefill(w.S, w.window)
+        tokens = w.B * w.S
+        hbm_bytes = None
+        kind = "backward"
+    elif w.kind == "prefill":
         out = torch.empty_like(inp["q"])
 
         def step():
@@ -236,7 +279,7 @@ def main():
     timing = {"median_ms": round(per_step[len(per_step) // 2], 5), "min_ms": round(per_step[0], 5)}
 
     tflops = flops / (ms * 1e-3) / 1e12
-    if w.kind == "prefill":
+    if w.kind in ("prefill", "backward"):
         value, unit = tflops, "TFLOP/s"
         if w.dtype == "bf16":
             roof = {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS,
@@ -251,7 +294,7 @@ def main():
                 "frac": round(gbs / PEAK_HBM_GBS, 5)}
     roof["traffic"] = profiled_traffic(w.name, kind)
 
-    cfg = {"workload": w.name, "B": w.B, "S" if w.kind == "prefill" else "kv_len": w.S,
+    cfg = {"workload": w.name, "B": w.B, "kv_len" if w.kind == "decode" else "S": w.S,
            "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "window": w.window, "bias_range": w.bias_range,
            "bias": w.mode, "R": w.R if w.mode == "rproj" else None,
            "useful_gflop_per_step": round(flops / 1e9, 4), "tokens_per_step": tokens,

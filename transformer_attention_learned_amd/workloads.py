@@ -34,7 +34,7 @@ MODE_IDS = {"none": 0, "table": 1, "rproj": 2, "rproj_shared": 3}
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "prefill" | "decode"
+    kind: str                 # "prefill" | "decode" | "backward" (gradients of a prefill)
     dtype: str                # "f32" | "bf16"
     B: int
     Hq: int
@@ -101,6 +101,11 @@ WORKLOADS = {
 }
 
 
+# Backward passes of the three prefill layers (same inputs, plus the output gradient).
+for _name in ("local_prefill", "global_prefill", "long_global_prefill"):
+    WORKLOADS[_name + "_bwd"] = WORKLOADS[_name].with_(name=_name + "_bwd", kind="backward")
+
+
 def paged_view(w: Workload, k, v, seed=None):
     """Page pools and block table over the contiguous caches of a decode workload.
 
@@ -147,7 +152,8 @@ def _rmsnorm_randn(shape, gen, device, dtype, chunk_elems=1 << 28):
 def make_inputs(w: Workload, device="cpu", seed=None):
     """Draw every input of workload `w` on `device` (seeded, deterministic per device).
 
-    Prefill returns q [B,S,Hq,D], k/v [B,S,Hkv,D], r [B,S,Hq,R] (rproj);
+    Prefill returns q [B,S,Hq,D], k/v [B,S,Hkv,D], r [B,S,Hq,R] (rproj); backward the same
+    plus dout [B,S,Hq,D] (N(0,1), drawn after every other input);
     decode returns q [B,Hq,D], k/v caches [B,S,Hkv,D], r [B,Hq,R].
     table [Hq, bias_range] fp32 (table mode), E [Hq, R, bias_range] fp32 (rproj) or
     [R, bias_range] (rproj_shared: one bank for every head).
@@ -155,7 +161,7 @@ def make_inputs(w: Workload, device="cpu", seed=None):
     gen = torch.Generator(device=device)
     gen.manual_seed(w.seed if seed is None else seed)
     dt = w.torch_dtype
-    if w.kind == "prefill":
+    if w.kind in ("prefill", "backward"):
         B, S = w.B, w.S
         qshape, kshape = (B, S, w.Hq, w.D), (B, S, w.Hkv, w.D)
         rshape = (B, S, w.Hq, w.R)
@@ -185,7 +191,10 @@ def make_inputs(w: Workload, device="cpu", seed=None):
         eshape = (w.Hq, w.R, w.bias_range) if w.mode == "rproj" else (w.R, w.bias_range)
         E = (torch.randn(eshape, generator=gen, device=device, dtype=torch.float32) * w.e_std).contiguous()
         r = torch.randn(rshape, generator=gen, device=device, dtype=torch.float32).to(dt)
-    return dict(q=q, k=k, v=v, table=table, E=E, r=r)
+    dout = None
+    if w.kind == "backward":   # gradient on the output, drawn last
+        dout = _randn((w.B * w.S, w.Hq, w.D), gen, device, dt).view(q.shape)
+    return dict(q=q, k=k, v=v, table=table, E=E, r=r, dout=dout)
 
 
 def small_case(dtype="bf16", B=1, S=200, Hq=4, Hkv=2, D=128, window=0, bias_range=64,
