@@ -43,8 +43,10 @@ namespace rba {
 namespace {
 
 constexpr int BN = 64;        // keys per tile (dq kernel), query rows per tile (dk/dv kernel)
-constexpr int CST = 65;       // row stride (floats) of the curve scratch
+constexpr int CST = 68;       // row stride (floats) of the curve scratch: 16-byte rows, and the
+                              // diagonal reads (stride CST + 1 = 5 mod 64 banks) do not collide
 constexpr int PADT = 64;      // zero distances staged on each side of a table row
+constexpr int PADE = 64;      // zero distances staged on each side of E
 constexpr int GST = 64 + 8;   // G row stride (bf16): row = query, 64 distances
 constexpr int GTS = 32 + 8;   // G^T row stride (bf16): row = distance, 32 queries
 constexpr int DQ_WAVES = 4;
@@ -72,38 +74,64 @@ __device__ __forceinline__ f32x16 zero16() {
 // Row of element i of a 32x32 MFMA output in lane half lh.
 __device__ __forceinline__ int out_row(int i, int lh) { return 8 * (i >> 2) + 4 * lh + (i & 3); }
 
-// Stage rows [r0, r0 + 64) of a [.., ld]-strided bf16 tensor (D columns) into LDS twice:
-// row-major (stride D + 8) and, if tr != nullptr, transposed with the row permutation vt_pos
-// (stride 64 + 8).  Rows >= nrows read as zero.  Items of 4 rows x 8 columns.
+// Rows [r0, r0 + 64) of a [.., ld]-strided bf16 tensor (D columns), in items of 4 rows x 8
+// columns: load_rows fetches a thread's items into registers (rows >= nrows read as zero),
+// store_rows writes them to LDS twice: row-major (stride D + 8) and, if tr != nullptr,
+// transposed with the row permutation vt_pos (stride 64 + 8).  Split so that the loads of
+// the next tile are in flight while the current one is used.
 template <int D>
-__device__ __forceinline__ void stage_rows(const uint16_t* base, size_t ld, int r0, int nrows,
-                                           uint16_t* rm, uint16_t* tr, int t, int nt) {
-  constexpr int NI = (BN / 4) * (D / 8);
-  for (int it = t; it < NI; it += nt) {
+constexpr int row_items() { return (BN / 4) * (D / 8); }
+
+template <int D, int NIT>
+__device__ __forceinline__ void load_rows(const uint16_t* base, size_t ld, int r0, int nrows,
+                                          u32x4 (&pre)[NIT][4], int t, int nt) {
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int it = t + k * nt;
     const int rg = it % (BN / 4);
     const int dg = it / (BN / 4);
-    u32x4 rows[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int row = r0 + 4 * rg + s;
-      rows[s] = u32x4{0u, 0u, 0u, 0u};
-      if (row < nrows) rows[s] = ld16(base + static_cast<size_t>(row) * ld + 8 * dg);
-      st16(rm + (4 * rg + s) * (D + 8) + 8 * dg, rows[s]);
+      pre[k][s] = u32x4{0u, 0u, 0u, 0u};
+      if (it < row_items<D>() && row < nrows) pre[k][s] = ld16(base + static_cast<size_t>(row) * ld + 8 * dg);
     }
+  }
+}
+
+template <int D, int NIT>
+__device__ __forceinline__ void store_rows(const u32x4 (&pre)[NIT][4], uint16_t* rm, uint16_t* tr,
+                                           int t, int nt) {
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int it = t + k * nt;
+    if (it >= row_items<D>()) continue;
+    const int rg = it % (BN / 4);
+    const int dg = it / (BN / 4);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) st16(rm + (4 * rg + s) * (D + 8) + 8 * dg, pre[k][s]);
     if (tr) {
       const int pos = vt_pos(4 * rg);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int w = e >> 1;
         const int sh = (e & 1) * 16;
-        const uint32_t x0 = (rows[0][w] >> sh) & 0xffffu;
-        const uint32_t x1 = (rows[1][w] >> sh) & 0xffffu;
-        const uint32_t x2 = (rows[2][w] >> sh) & 0xffffu;
-        const uint32_t x3 = (rows[3][w] >> sh) & 0xffffu;
+        const uint32_t x0 = (pre[k][0][w] >> sh) & 0xffffu;
+        const uint32_t x1 = (pre[k][1][w] >> sh) & 0xffffu;
+        const uint32_t x2 = (pre[k][2][w] >> sh) & 0xffffu;
+        const uint32_t x3 = (pre[k][3][w] >> sh) & 0xffffu;
         st8(tr + (8 * dg + e) * (BN + 8) + pos, u32x2{x0 | (x1 << 16), x2 | (x3 << 16)});
       }
     }
   }
+}
+
+// A 32x32 MFMA output column into a curve-scratch row: rows 8 g + 4 lh + 0..3 are
+// consecutive, one 16-byte store each (dst = row start + 4 lh).
+__device__ __forceinline__ void store_curve(const f32x16& v, float* dst) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *reinterpret_cast<f32x4*>(dst + 8 * g) = f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
 }
 
 // The r.E curve block of 32 query rows q0.. over the 64 distances base .. base + 63, written
@@ -135,8 +163,7 @@ __device__ __forceinline__ void curve_block(const BwdArgs& a, const float* Eh, c
       }
       cacc = mfma32(as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}), rf[fc], cacc);
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) cs[ln * CST + 32 * half + out_row(i, lh)] = cacc[i];
+    store_curve(cacc, cs + ln * CST + 32 * half + 4 * lh);
   }
 }
 
@@ -157,6 +184,48 @@ __device__ __forceinline__ void load_rf(const BwdArgs& a, int b, int row, int h,
     rf[fc] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
   }
 }
+
+// E staged in LDS for the curve MFMA: row PADE + distance holds, per chunk of 8 curves, the
+// bf16 high parts and then the low parts of E * log2(e) (the A operands of the two lane
+// halves), zero outside [0, bias_range) and for curves >= R.  Consecutive threads read
+// consecutive distances of one curve.
+__device__ __forceinline__ void stage_et(const BwdArgs& a, const float* Eh, uint16_t* et, int nfc,
+                                         int t, int nt) {
+  const int rows = a.bias_range + 2 * PADE;
+  const int n = rows * 8 * nfc;
+  for (int x = t; x < n; x += nt) {
+    const int row = x % rows;
+    const int f = x / rows;                 // 8 fc + j
+    const int d = row - PADE;
+    float e = 0.f;
+    if (f < a.R && d >= 0 && d < a.bias_range) e = Eh[static_cast<size_t>(f) * a.bias_range + d] * kLog2e;
+    const uint16_t hi = f32_to_bf16(e);
+    const uint16_t lo = f32_to_bf16(e - bf16_to_f32(hi));
+    uint16_t* dst = et + row * 16 * nfc + 16 * (f >> 3) + (f & 7);
+    dst[0] = hi;
+    dst[8] = lo;
+  }
+}
+
+// The curve block of the forward from the staged E: cs[query][distance - base], log2 units.
+__device__ __forceinline__ void curve_block_lds(const uint16_t* et, int nfc, const bf16x8 (&rf)[2],
+                                                int base, float* cs, int ln, int lh) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const uint16_t* er = et + (PADE + base + 32 * half + ln) * 16 * nfc + 8 * lh;
+    f32x16 cacc = zero16();
+    for (int fc = 0; fc < nfc; ++fc) cacc = mfma32(as_bf16x8(ld16(er + 16 * fc)), rf[fc], cacc);
+    store_curve(cacc, cs + ln * CST + 32 * half + 4 * lh);
+  }
+}
+
+// Bytes of the staged E for the curve MFMA.
+__host__ __device__ inline int et_bytes(int bias_range, int R) {
+  return (bias_range + 2 * PADE) * 16 * ((R + 7) / 8) * 2;
+}
+// Row stride (bf16) of E staged curve-major for the dr MFMA, and its bytes.
+__host__ __device__ inline int ef_stride(int bias_range) { return (bias_range + 2 * PADE + 7) & ~7; }
+__host__ __device__ inline int ef_bytes(int bias_range, int R) { return R * ef_stride(bias_range) * 2; }
 
 // ---- pre pass: rowsum(dO * O) and zeroed parameter gradients ----------------------------------
 template <int D>
@@ -189,17 +258,33 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, float* zero_ptr
 }
 
 // ---- dq (+ dr, dE, dtable): query-parallel -----------------------------------------------------
+// LDS: K, V, K^T tiles; per wave the curve scratch (r.E) and the skewed dZ buffers; the table
+// row (table mode); E staged for the curve and dr MFMAs when ESTAGE.
 template <int D, int MODE>
+struct DqLayout {
+  static constexpr int KST = D + 8;
+  static constexpr int TST = BN + 8;
+  static constexpr int TILE_BYTES = (2 * BN * KST + D * TST) * 2;
+  static constexpr int CS_BYTES = (MODE == 2) ? 32 * CST * 4 : 0;
+  static constexpr int G_BYTES = (MODE == 2) ? 32 * GST * 2 : 0;
+  static constexpr int GT_BYTES = (MODE != 0) ? 64 * GTS * 2 : 0;
+  static constexpr int WAVE_BYTES = CS_BYTES + G_BYTES + GT_BYTES;
+  static constexpr int FIXED = TILE_BYTES + DQ_WAVES * WAVE_BYTES;
+  static int bytes(int Rb, int R, bool estage) {
+    int n = FIXED;
+    if (MODE == 1) n += (Rb + 2 * PADT) * 4;
+    if (MODE == 2 && estage) n += et_bytes(Rb, R) + ef_bytes(Rb, R);
+    return n;
+  }
+};
+
+template <int D, int MODE, bool ESTAGE>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles, int longest_first) {
-  constexpr int KST = D + 8;
-  constexpr int TST = BN + 8;
+  using L = DqLayout<D, MODE>;
+  constexpr int KST = L::KST;
+  constexpr int TST = L::TST;
   constexpr int NC = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int TILE_BYTES = (2 * BN * KST + D * TST) * 2;
-  constexpr int CS_BYTES = (MODE == 2) ? 32 * CST * 4 : 0;
-  constexpr int G_BYTES = (MODE == 2) ? 32 * GST * 2 : 0;
-  constexpr int GT_BYTES = (MODE != 0) ? 64 * GTS * 2 : 0;
-  constexpr int WAVE_BYTES = CS_BYTES + G_BYTES + GT_BYTES;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Vs = Ks + BN * KST;
@@ -211,10 +296,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
   const int ln = lane & 31;
   const int lh = lane >> 5;
 
-  unsigned char* wsp = smem + TILE_BYTES + wave * WAVE_BYTES;
+  unsigned char* wsp = smem + L::TILE_BYTES + wave * L::WAVE_BYTES;
   float* cs = reinterpret_cast<float*>(wsp);
-  uint16_t* Gs = reinterpret_cast<uint16_t*>(wsp + CS_BYTES);
-  uint16_t* GTs = reinterpret_cast<uint16_t*>(wsp + CS_BYTES + G_BYTES);
+  uint16_t* Gs = reinterpret_cast<uint16_t*>(wsp + L::CS_BYTES);
+  uint16_t* GTs = reinterpret_cast<uint16_t*>(wsp + L::CS_BYTES + L::G_BYTES);
+  float* tabs = reinterpret_cast<float*>(smem + L::FIXED);                 // table mode
+  uint16_t* et = reinterpret_cast<uint16_t*>(smem + L::FIXED);             // r.E, ESTAGE
+  uint16_t* ef = et + et_bytes(a.bias_range, a.R) / 2;
 
   const int per_q = a.Hq * a.B;
   int qt = blockIdx.x / per_q;
@@ -232,6 +320,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
   const int hkv = h / a.G;
   const int row = i0 + ln;
   const bool row_ok = row < S;
+  const int nfc = (a.R + 7) / 8;
 
   const int wg_last = min(S, wg_i0 + 32 * DQ_WAVES) - 1;
   const int kmin = W ? max(0, wg_i0 - W + 1) : 0;
@@ -243,6 +332,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
   const uint16_t* kbase = a.k + static_cast<size_t>(b) * S * kv_row + static_cast<size_t>(hkv) * D;
   const uint16_t* vbase = a.v + static_cast<size_t>(b) * S * kv_row + static_cast<size_t>(hkv) * D;
   const size_t qoff = (static_cast<size_t>(b) * S + (row_ok ? row : 0)) * q_row + static_cast<size_t>(h) * D;
+  const float* Eh = (MODE == 2) ? a.E + static_cast<size_t>(h) * a.e_hs : nullptr;
+
+  // bias parameters of the head in LDS (made visible by the first barrier of the tile loop)
+  if (MODE == 1) {
+    const float* tp = a.table + static_cast<size_t>(h) * Rb;
+    for (int x = tid; x < Rb + 2 * PADT; x += 256) {
+      const int d = x - PADT;
+      tabs[x] = (d >= 0 && d < Rb) ? tp[d] * kLog2e : 0.f;
+    }
+  }
+  if (MODE == 2 && ESTAGE) {
+    stage_et(a, Eh, et, nfc, tid, 256);
+    const int efs = ef_stride(Rb);
+    for (int x = tid; x < a.R * efs; x += 256) {
+      const int f = x / efs;
+      const int d = x - f * efs - PADE;
+      ef[x] = (d >= 0 && d < Rb) ? f32_to_bf16(Eh[static_cast<size_t>(f) * Rb + d]) : static_cast<uint16_t>(0);
+    }
+  }
 
   // Q^T and dO^T fragments (B operands): lane (n = ln, lh) holds x[row][16c + 8lh .. +7]
   bf16x8 qf[NC], dof[NC];
@@ -261,10 +369,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
   const float lse2 = row_ok ? a.lse[lrow] * kLog2e : INFINITY;
   const float dsum = row_ok ? a.dsum[lrow] : 0.f;
   const float tq = temp_factor(visible_keys(row, W), a.temp_len, a.temp_inv_log2);
+  const float cq = a.c_qk * tq;
 
   bf16x8 rf[2];        // r of this row (curve MFMA, B operand)
   bf16x8 rA[2];        // r^T of the wave's rows (dE MFMA, A operand): row f = ln, rows 16kk + 8lh + e
-  const float* Eh = (MODE == 2) ? a.E + static_cast<size_t>(h) * a.e_hs : nullptr;
   if (MODE == 2) load_rf(a, b, row, h, rf);
   if (MODE != 0) {
 #pragma unroll
@@ -288,7 +396,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
       rA[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
     }
     // zero the skewed buffers once: every in-band block writes the same set of positions
-    for (int x = lane; x < (G_BYTES + GT_BYTES) / 16; x += 64)
+    for (int x = lane; x < (L::G_BYTES + L::GT_BYTES) / 16; x += 64)
       st16(reinterpret_cast<unsigned char*>(Gs) + 16 * x, u32x4{0u, 0u, 0u, 0u});
   }
 
@@ -296,25 +404,41 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqacc[db] = zero16();
   f32x16 dracc = zero16();
-  const float* tab = (MODE == 1) ? a.table + static_cast<size_t>(h) * Rb : nullptr;
   float* dEh = (MODE == 2) ? a.dE + static_cast<size_t>(h) * a.e_hs : nullptr;
   float* dtab = (MODE == 1) ? a.dtable + static_cast<size_t>(h) * Rb : nullptr;
+
+  // K / V tiles: the next tile's rows are loaded into registers while the current one is used
+  constexpr int KIT = (row_items<D>() + 255) / 256;
+  constexpr int NCH = BN * (D / 8);
+  constexpr int VIT = (NCH + 255) / 256;
+  u32x4 kpre[KIT][4], vpre[VIT];
+  auto load_kv = [&](int tk0) {
+    load_rows<D, KIT>(kbase, kv_row, tk0, S, kpre, tid, 256);
+#pragma unroll
+    for (int q = 0; q < VIT; ++q) {
+      const int x = tid + 256 * q;
+      const int rr = x / (D / 8);
+      const int ch = x % (D / 8);
+      vpre[q] = u32x4{0u, 0u, 0u, 0u};
+      if (x < NCH && tk0 + rr < S) vpre[q] = ld16(vbase + static_cast<size_t>(tk0 + rr) * kv_row + 8 * ch);
+    }
+  };
+  auto store_kv = [&]() {
+    store_rows<D, KIT>(kpre, Ks, Kt, tid, 256);
+#pragma unroll
+    for (int q = 0; q < VIT; ++q) {
+      const int x = tid + 256 * q;
+      if (x < NCH) st16(Vs + (x / (D / 8)) * KST + 8 * (x % (D / 8)), vpre[q]);
+    }
+  };
+  if (t_begin <= t_end) load_kv(t_begin * BN);
 
   for (int t = t_begin; t <= t_end; ++t) {
     const int tk0 = t * BN;
     __syncthreads();   // the previous tile's LDS reads are complete
-    stage_rows<D>(kbase, kv_row, tk0, S, Ks, Kt, tid, 256);
-    {
-      constexpr int NCH = BN * (D / 8);
-      for (int x = tid; x < NCH; x += 256) {
-        const int rr = x / (D / 8);
-        const int ch = x % (D / 8);
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (tk0 + rr < S) v = ld16(vbase + static_cast<size_t>(tk0 + rr) * kv_row + 8 * ch);
-        st16(Vs + rr * KST + 8 * ch, v);
-      }
-    }
+    store_kv();
     __syncthreads();
+    if (t < t_end) load_kv(tk0 + BN);
     if (!wave_live) continue;
 
 #pragma unroll 1
@@ -333,33 +457,39 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
         sacc = mfma32(kf, qf[cc], sacc);
         pacc = mfma32(vf, dof[cc], pacc);
       }
+      // log2-domain logits tau * (scale log2(e) q.k + log2(e) beta)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] *= a.c_qk;
+      for (int i = 0; i < 16; ++i) sacc[i] *= cq;
       const bool inband = (MODE != 0) && (c - 31 < Rb);
       if (MODE == 1 && inband) {
+        // distances c + ln - m lie in [-31, Rb + 62]: inside the zero-padded row
+        const float* tb = tabs + PADT + c + ln;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = fmaf(tb[-out_row(i, lh)], tq, sacc[i]);
+      }
+      if (MODE == 2 && inband) {
+        if (ESTAGE) curve_block_lds(et, nfc, rf, c - 31, cs, ln, lh);
+        else curve_block<D>(a, Eh, rf, c - 31, cs, ln, lh);
+        wave_sync_lds();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = fmaf(cs[ln * CST + (ln - out_row(i, lh) + 31)], tq, sacc[i]);
+        wave_sync_lds();
+      }
+      // P and dS = P * (dP - rowsum); the temperature factor of dZ = tau dS is applied to the
+      // accumulated dq and to the bias-gradient inputs
+      float dz[16];
+      const bool edge = (c - 31 < 0) || (W && c + 31 >= W);
+      if (edge) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int d = c + ln - out_row(i, lh);
-          const int dc = min(max(d, 0), Rb - 1);
-          const float tv = tab[dc];
-          sacc[i] += (d >= 0 && d < Rb) ? tv * kLog2e : 0.f;
+          const bool vis = d >= 0 && (W == 0 || d < W);
+          const float p = vis ? fast_exp2(sacc[i] - lse2) : 0.f;
+          dz[i] = p * (pacc[i] - dsum);
         }
-      }
-      if (MODE == 2 && inband) {
-        curve_block<D>(a, Eh, rf, c - 31, cs, ln, lh);
-        wave_sync_lds();
+      } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] += cs[ln * CST + (ln - out_row(i, lh) + 31)];
-        wave_sync_lds();
-      }
-      // P, dZ = tau * P * (dP - rowsum)
-      float dz[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int d = c + ln - out_row(i, lh);
-        const bool vis = d >= 0 && (W == 0 || d < W);
-        const float p = vis ? fast_exp2(sacc[i] * tq - lse2) : 0.f;
-        dz[i] = p * (pacc[i] - dsum) * tq;
+        for (int i = 0; i < 16; ++i) dz[i] = fast_exp2(sacc[i] - lse2) * (pacc[i] - dsum);
       }
       bf16x8 dzf[2];
 #pragma unroll
@@ -369,7 +499,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
         for (int jj = 0; jj < 4; ++jj) w[jj] = pack_bf16x2(dz[8 * kk + 2 * jj], dz[8 * kk + 2 * jj + 1]);
         dzf[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
       }
-      // dQ^T += K^T dZ^T
+      // dQ^T += K^T dS^T
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -384,7 +514,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int dp = ln - out_row(i, lh) + 32;
-          const uint16_t v16 = f32_to_bf16(dz[i]);
+          const uint16_t v16 = f32_to_bf16(dz[i] * tq);
           GTs[dp * GTS + ln] = v16;
           if (MODE == 2) Gs[ln * GST + dp] = v16;
         }
@@ -413,22 +543,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
         }
         if (MODE == 2) {
           // dr^T[f][query] += sum_dist E[f][dist] G^T[dist][query], 16 distances per MFMA
+          const int efs = ef_stride(Rb);
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
             const int d0 = c - 32 + 16 * kk + 8 * lh;
-            uint32_t w[4];
+            bf16x8 ea;
+            if (ESTAGE) {
+              u32x4 x = {0u, 0u, 0u, 0u};
+              if (ln < a.R) x = ld16(ef + ln * efs + PADE + d0);
+              ea = as_bf16x8(x);
+            } else {
+              uint32_t w[4];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              float e2[2];
+              for (int jj = 0; jj < 4; ++jj) {
+                float e2[2];
 #pragma unroll
-              for (int u = 0; u < 2; ++u) {
-                const int dd = d0 + 2 * jj + u;
-                e2[u] = (ln < a.R && dd >= 0 && dd < Rb) ? Eh[static_cast<size_t>(ln) * Rb + dd] : 0.f;
+                for (int u = 0; u < 2; ++u) {
+                  const int dd = d0 + 2 * jj + u;
+                  e2[u] = (ln < a.R && dd >= 0 && dd < Rb) ? Eh[static_cast<size_t>(ln) * Rb + dd] : 0.f;
+                }
+                w[jj] = pack_bf16x2(e2[0], e2[1]);
               }
-              w[jj] = pack_bf16x2(e2[0], e2[1]);
+              ea = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
             }
             const bf16x8 gf = as_bf16x8(ld16(Gs + ln * GST + 16 * kk + 8 * lh));
-            dracc = mfma32(as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}), gf, dracc);
+            dracc = mfma32(ea, gf, dracc);
           }
         }
         wave_sync_lds();
@@ -438,14 +577,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
 
   if (!wave_live || !row_ok) return;
   uint16_t* dqp = a.dq + qoff;
+  const float sq = a.scale * tq;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d = 32 * db + 8 * g4 + 4 * lh;
       const f32x16& acc = dqacc[db];
-      st8(dqp + d, u32x2{pack_bf16x2(acc[4 * g4] * a.scale, acc[4 * g4 + 1] * a.scale),
-                         pack_bf16x2(acc[4 * g4 + 2] * a.scale, acc[4 * g4 + 3] * a.scale)});
+      st8(dqp + d, u32x2{pack_bf16x2(acc[4 * g4] * sq, acc[4 * g4 + 1] * sq),
+                         pack_bf16x2(acc[4 * g4 + 2] * sq, acc[4 * g4 + 3] * sq)});
     }
   if (MODE == 2) {
     uint16_t* drp = a.dr + ((static_cast<size_t>(b) * S + row) * a.Hq + h) * a.R;
@@ -458,8 +598,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
 }
 
 // ---- dk, dv: key-parallel ------------------------------------------------------------------------
-template <int D, int MODE>
-__global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a, int tab_off, int cs_off) {
+template <int D>
+struct DkvLayout {
+  static constexpr int TILES = (2 * BN * (D + 8) + 2 * D * (BN + 8)) * 2 + 4 * BN * 4 + BN * 16 * 2;
+  static constexpr int CS_BYTES = DKV_WAVES * 32 * CST * 4;
+  // bias parameters after the tiles: table row, or curve scratch (+ staged E)
+  static int bytes(int mode, int Rb, int R, bool estage) {
+    int n = TILES;
+    if (mode == 1) n += (Rb + 2 * PADT) * 4;
+    if (mode == 2) n += CS_BYTES + (estage ? et_bytes(Rb, R) : 0);
+    return n;
+  }
+};
+
+template <int D, int MODE, bool ESTAGE>
+__global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  using L = DkvLayout<D>;
   constexpr int QST = D + 8;
   constexpr int TST = BN + 8;
   constexpr int NC = D / 16;
@@ -470,15 +624,18 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a, 
   uint16_t* dOs = Qs + BN * QST;
   uint16_t* Qt = dOs + BN * QST;
   uint16_t* dOt = Qt + D * TST;
-  float* rowp = reinterpret_cast<float*>(dOt + D * TST);   // [3][BN]: lse2, rowsum, temperature
-  float* tabs = reinterpret_cast<float*>(smem + tab_off);  // [PADT + Rb + PADT]
+  float* rowp = reinterpret_cast<float*>(dOt + D * TST);   // [4][BN]: lse2, rowsum, c_qk*tau, tau
+  uint16_t* rrow = reinterpret_cast<uint16_t*>(rowp + 4 * BN);   // [BN][16]: r of the tile's rows
+  float* tabs = reinterpret_cast<float*>(smem + L::TILES);  // table mode: [PADT + Rb + PADT]
+  float* cs_all = reinterpret_cast<float*>(smem + L::TILES);
+  uint16_t* et = reinterpret_cast<uint16_t*>(smem + L::TILES + L::CS_BYTES);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31;
   const int lh = lane >> 5;
-  float* cs = reinterpret_cast<float*>(smem + cs_off) + wave * 32 * CST;
+  float* cs = cs_all + wave * 32 * CST;
 
   const int per_k = a.Hkv * a.B;
   const int kt = blockIdx.x / per_k;
@@ -494,6 +651,8 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a, 
   const bool wave_live = j0w < S;
   const int key = j0w + ln;
   const bool key_ok = key < S;
+  const int nfc = (a.R + 7) / 8;
+  const bool temp = a.temp_len > 0;
 
   const size_t q_row = static_cast<size_t>(a.Hq) * D;
   const size_t kv_row = static_cast<size_t>(a.Hkv) * D;
@@ -523,111 +682,166 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a, 
   const int t_begin = j_lo / BN;
   const int t_end = i_last / BN;
 
-  for (int hh = 0; hh < a.G; ++hh) {
-    const int h = hkv * a.G + hh;
-    const float* Eh = (MODE == 2) ? a.E + static_cast<size_t>(h) * a.e_hs : nullptr;
-    if (MODE == 1) {
-      __syncthreads();   // the previous head's table reads are complete
-      const float* tp = a.table + static_cast<size_t>(h) * Rb;
-      for (int x = tid; x < Rb + 2 * PADT; x += NT) {
-        const int d = x - PADT;
-        tabs[x] = (d >= 0 && d < Rb) ? tp[d] * kLog2e : 0.f;
+  // (head, query tile) steps in one sequence, so the next step's Q / dO rows and per-row
+  // values are loaded into registers while the current step is used
+  const int ntiles = t_end - t_begin + 1;
+  const int nsteps = ntiles > 0 ? a.G * ntiles : 0;
+  constexpr int QIT = (row_items<D>() + NT - 1) / NT;
+  u32x4 qpre[QIT][4], dpre[QIT][4];
+  float lpre = 0.f, spre = 0.f, tpre = 1.f;
+  u32x4 rpre[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+  auto load_step = [&](int st) {
+    const int h = hkv * a.G + st / ntiles;
+    const int qt0 = (t_begin + st % ntiles) * BN;
+    load_rows<D, QIT>(a.q + static_cast<size_t>(b) * S * q_row + static_cast<size_t>(h) * D, q_row, qt0, S,
+                      qpre, tid, NT);
+    load_rows<D, QIT>(a.dout + static_cast<size_t>(b) * S * q_row + static_cast<size_t>(h) * D, q_row, qt0, S,
+                      dpre, tid, NT);
+    if (tid < BN) {
+      const int rr = qt0 + tid;
+      const bool ok = rr < S;
+      const size_t lrow = (static_cast<size_t>(b) * a.Hq + h) * S + (ok ? rr : 0);
+      lpre = ok ? a.lse[lrow] * kLog2e : INFINITY;
+      spre = ok ? a.dsum[lrow] : 0.f;
+      tpre = temp_factor(visible_keys(rr, W), a.temp_len, a.temp_inv_log2);
+      if (MODE == 2) {   // r of the row, zero past R (16 curves at most)
+        const uint16_t* rp = a.r + ((static_cast<size_t>(b) * S + (ok ? rr : 0)) * a.Hq + h) * a.R;
+        uint32_t w[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const uint32_t lo = (ok && 2 * jj < a.R) ? rp[2 * jj] : 0u;
+          const uint32_t hi = (ok && 2 * jj + 1 < a.R) ? rp[2 * jj + 1] : 0u;
+          w[jj] = lo | (hi << 16);
+        }
+        rpre[0] = u32x4{w[0], w[1], w[2], w[3]};
+        rpre[1] = u32x4{w[4], w[5], w[6], w[7]};
       }
     }
-    const uint16_t* qbase = a.q + static_cast<size_t>(b) * S * q_row + static_cast<size_t>(h) * D;
-    const uint16_t* dobase = a.dout + static_cast<size_t>(b) * S * q_row + static_cast<size_t>(h) * D;
-    for (int t = t_begin; t <= t_end; ++t) {
-      const int qt0 = t * BN;
-      __syncthreads();   // the previous tile's LDS reads are complete
-      if (tid < NT / 2) stage_rows<D>(qbase, q_row, qt0, S, Qs, Qt, tid, NT / 2);
-      else stage_rows<D>(dobase, q_row, qt0, S, dOs, dOt, tid - NT / 2, NT / 2);
-      if (tid < BN) {
-        const int rr = qt0 + tid;
-        const bool ok = rr < S;
-        const size_t lrow = (static_cast<size_t>(b) * a.Hq + h) * S + (ok ? rr : 0);
-        rowp[tid] = ok ? a.lse[lrow] * kLog2e : INFINITY;
-        rowp[BN + tid] = ok ? a.dsum[lrow] : 0.f;
-        rowp[2 * BN + tid] = temp_factor(visible_keys(rr, W), a.temp_len, a.temp_inv_log2);
+  };
+  if (nsteps > 0) load_step(0);
+
+  for (int st = 0; st < nsteps; ++st) {
+    const int hh = st / ntiles;
+    const int h = hkv * a.G + hh;
+    const int qt0 = (t_begin + st % ntiles) * BN;
+    const float* Eh = (MODE == 2) ? a.E + static_cast<size_t>(h) * a.e_hs : nullptr;
+    __syncthreads();   // the previous step's LDS reads are complete
+    store_rows<D, QIT>(qpre, Qs, Qt, tid, NT);
+    store_rows<D, QIT>(dpre, dOs, dOt, tid, NT);
+    if (tid < BN) {
+      rowp[tid] = lpre;
+      rowp[BN + tid] = spre;
+      rowp[2 * BN + tid] = a.c_qk * tpre;
+      rowp[3 * BN + tid] = tpre;
+      if (MODE == 2) {
+        st16(rrow + 16 * tid, rpre[0]);
+        st16(rrow + 16 * tid + 8, rpre[1]);
       }
-      __syncthreads();
-      if (!wave_live) continue;
+    }
+    if (st % ntiles == 0) {   // a new head: its bias parameters
+      if (MODE == 1) {
+        const float* tp = a.table + static_cast<size_t>(h) * Rb;
+        for (int x = tid; x < Rb + 2 * PADT; x += NT) {
+          const int d = x - PADT;
+          tabs[x] = (d >= 0 && d < Rb) ? tp[d] * kLog2e : 0.f;
+        }
+      }
+      if (MODE == 2 && ESTAGE && (hh == 0 || a.e_hs != 0)) stage_et(a, Eh, et, nfc, tid, NT);
+    }
+    __syncthreads();
+    if (st + 1 < nsteps) load_step(st + 1);
+    if (!wave_live) continue;
 
 #pragma unroll 1
-      for (int qb = 0; qb < 2; ++qb) {
-        const int i0b = qt0 + 32 * qb;
-        const int c = i0b - j0w;                  // delta = c + m - n
-        bool on = (c + 31 >= 0) && (i0b < S);
-        if (W) on = on && (c - 31 < W);
-        if (!on) continue;
+    for (int qb = 0; qb < 2; ++qb) {
+      const int i0b = qt0 + 32 * qb;
+      const int c = i0b - j0w;                  // delta = c + m - n
+      bool on = (c + 31 >= 0) && (i0b < S);
+      if (W) on = on && (c - 31 < W);
+      if (!on) continue;
 
-        f32x16 sacc = zero16(), pacc = zero16();
+      f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-          const bf16x8 qa = as_bf16x8(ld16(Qs + (32 * qb + ln) * QST + 16 * cc + 8 * lh));
-          const bf16x8 da = as_bf16x8(ld16(dOs + (32 * qb + ln) * QST + 16 * cc + 8 * lh));
-          sacc = mfma32(qa, kf[cc], sacc);
-          pacc = mfma32(da, vf[cc], pacc);
+      for (int cc = 0; cc < NC; ++cc) {
+        const bf16x8 qa = as_bf16x8(ld16(Qs + (32 * qb + ln) * QST + 16 * cc + 8 * lh));
+        const bf16x8 da = as_bf16x8(ld16(dOs + (32 * qb + ln) * QST + 16 * cc + 8 * lh));
+        sacc = mfma32(qa, kf[cc], sacc);
+        pacc = mfma32(da, vf[cc], pacc);
+      }
+      // bias (log2 units) per element, before the temperature
+      const bool inband = (MODE != 0) && (c - 31 < Rb);
+      float bias[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bias[i] = 0.f;
+      if (MODE == 1 && inband) {
+        // distances c + m - ln lie in [-31, Rb + 62]: inside the zero-padded row
+        const float* tb = tabs + PADT + c - ln;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bias[i] = tb[out_row(i, lh)];
+      }
+      if (MODE == 2 && inband) {
+        const bf16x8 rf[2] = {as_bf16x8(ld16(rrow + 16 * (32 * qb + ln))),
+                              as_bf16x8(ld16(rrow + 16 * (32 * qb + ln) + 8))};
+        if (ESTAGE) curve_block_lds(et, nfc, rf, c - 31, cs, ln, lh);
+        else curve_block<D>(a, Eh, rf, c - 31, cs, ln, lh);
+        wave_sync_lds();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = out_row(i, lh);
+          bias[i] = cs[m * CST + (m - ln + 31)];
+        }
+        wave_sync_lds();
+      }
+      // P into sacc, dZ = tau * P * (dP - rowsum) into pacc (in place)
+      const bool edge = (c - 31 < 0) || (W && c + 31 >= W);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int m0 = 32 * qb + 8 * g4 + 4 * lh;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(rowp + m0);
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(rowp + BN + m0);
+        f32x4 c4, t4;
+        if (temp) {
+          c4 = *reinterpret_cast<const f32x4*>(rowp + 2 * BN + m0);
+          t4 = *reinterpret_cast<const f32x4*>(rowp + 3 * BN + m0);
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] *= a.c_qk;
-        const bool inband = (MODE != 0) && (c - 31 < Rb);
-        if (MODE == 1 && inband) {
-          // distances c + m - ln lie in [-31, Rb + 62]: inside the zero-padded row
-          const float* tb = tabs + PADT + c - ln;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[i] += tb[out_row(i, lh)];
-        }
-        if (MODE == 2 && inband) {
-          bf16x8 rf[2];
-          load_rf(a, b, i0b + ln, h, rf);
-          curve_block<D>(a, Eh, rf, c - 31, cs, ln, lh);
-          wave_sync_lds();
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int m = out_row(i, lh);
-            sacc[i] += cs[m * CST + (m - ln + 31)];
-          }
-          wave_sync_lds();
-        }
-        // P into sacc, dZ into pacc (in place)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int m0 = 32 * qb + 8 * g4 + 4 * lh;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(rowp + m0);
-          const f32x4 s4 = *reinterpret_cast<const f32x4*>(rowp + BN + m0);
-          const f32x4 t4 = *reinterpret_cast<const f32x4*>(rowp + 2 * BN + m0);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int i = 4 * g4 + u;
+        for (int u = 0; u < 4; ++u) {
+          const int i = 4 * g4 + u;
+          float x;
+          if (temp) x = fmaf(bias[i], t4[u], fmaf(sacc[i], c4[u], -l4[u]));
+          else x = fmaf(sacc[i], a.c_qk, bias[i] - l4[u]);
+          float p = fast_exp2(x);
+          if (edge) {
             const int d = c + out_row(i, lh) - ln;
-            const bool vis = d >= 0 && (W == 0 || d < W);
-            const float p = vis ? fast_exp2(sacc[i] * t4[u] - l4[u]) : 0.f;
-            pacc[i] = p * (pacc[i] - s4[u]) * t4[u];
-            sacc[i] = p;
+            if (!(d >= 0 && (W == 0 || d < W))) p = 0.f;
           }
+          float dzv = p * (pacc[i] - s4[u]);
+          if (temp) dzv *= t4[u];
+          pacc[i] = dzv;
+          sacc[i] = p;
         }
-        bf16x8 pf[2], dzf[2];
+      }
+      bf16x8 pf[2], dzf[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        uint32_t w[4], x[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          w[jj] = pack_bf16x2(sacc[8 * kk + 2 * jj], sacc[8 * kk + 2 * jj + 1]);
+          x[jj] = pack_bf16x2(pacc[8 * kk + 2 * jj], pacc[8 * kk + 2 * jj + 1]);
+        }
+        pf[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+        dzf[kk] = as_bf16x8(u32x4{x[0], x[1], x[2], x[3]});
+      }
+      // dV^T += dO^T P,  dK^T += Q^T dZ
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          uint32_t w[4], x[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            w[jj] = pack_bf16x2(sacc[8 * kk + 2 * jj], sacc[8 * kk + 2 * jj + 1]);
-            x[jj] = pack_bf16x2(pacc[8 * kk + 2 * jj], pacc[8 * kk + 2 * jj + 1]);
-          }
-          pf[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
-          dzf[kk] = as_bf16x8(u32x4{x[0], x[1], x[2], x[3]});
+          const int off = (32 * db + ln) * TST + 32 * qb + 16 * kk + 8 * lh;
+          dvacc[db] = mfma32(as_bf16x8(ld16(dOt + off)), pf[kk], dvacc[db]);
+          dkacc[db] = mfma32(as_bf16x8(ld16(Qt + off)), dzf[kk], dkacc[db]);
         }
-        // dV^T += dO^T P,  dK^T += Q^T dZ
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const int off = (32 * db + ln) * TST + 32 * qb + 16 * kk + 8 * lh;
-            dvacc[db] = mfma32(as_bf16x8(ld16(dOt + off)), pf[kk], dvacc[db]);
-            dkacc[db] = mfma32(as_bf16x8(ld16(Qt + off)), dzf[kk], dkacc[db]);
-          }
-      }
     }
   }
 
@@ -650,29 +864,36 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a, 
 
 constexpr int kMaxLds = 160 * 1024;
 
-template <int D, int MODE>
-int dq_lds_bytes() {
-  constexpr int KST = D + 8;
-  constexpr int TST = BN + 8;
-  constexpr int tile = (2 * BN * KST + D * TST) * 2;
-  constexpr int wave = ((MODE == 2) ? 32 * CST * 4 + 32 * GST * 2 : 0) + ((MODE != 0) ? 64 * GTS * 2 : 0);
-  return tile + DQ_WAVES * wave;
-}
-
-template <int D>
-void dkdv_lds_layout(int mode, int Rb, int* tab_off, int* cs_off, int* total) {
-  const int tiles = (2 * BN * (D + 8) + 2 * D * (BN + 8)) * 2 + 3 * BN * 4;
-  *tab_off = tiles;
-  const int tab_bytes = (mode == 1) ? (Rb + 2 * PADT) * 4 : 0;
-  *cs_off = tiles + ((tab_bytes + 15) & ~15);
-  *total = *cs_off + ((mode == 2) ? DKV_WAVES * 32 * CST * 4 : 0);
-}
-
 template <typename K>
 hipError_t allow_lds(K* kernel, int bytes) {
   if (bytes <= 64 * 1024) return hipSuccess;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <int D, int MODE, bool ESTAGE>
+hipError_t launch_dq(const BwdArgs& a, hipStream_t s) {
+  const int n_qtiles = (a.S + 32 * DQ_WAVES - 1) / (32 * DQ_WAVES);
+  const int longest_first = (a.window == 0 || a.window > 32 * DQ_WAVES) ? 1 : 0;
+  const int lds = DqLayout<D, MODE>::bytes(a.bias_range, a.R, ESTAGE);
+  hipError_t e = allow_lds(&bwd_dq_kernel<D, MODE, ESTAGE>, lds);
+  if (e != hipSuccess) return e;
+  const long long nq = static_cast<long long>(n_qtiles) * a.Hq * a.B;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, MODE, ESTAGE>), dim3(static_cast<unsigned>(nq)), dim3(64 * DQ_WAVES), lds, s,
+                     a, n_qtiles, longest_first);
+  return hipGetLastError();
+}
+
+template <int D, int MODE, bool ESTAGE>
+hipError_t launch_dkdv(const BwdArgs& a, hipStream_t s) {
+  const int lds = DkvLayout<D>::bytes(MODE, a.bias_range, a.R, ESTAGE);
+  hipError_t e = allow_lds(&bwd_dkdv_kernel<D, MODE, ESTAGE>, lds);
+  if (e != hipSuccess) return e;
+  const int n_ktiles = (a.S + 32 * DKV_WAVES - 1) / (32 * DKV_WAVES);
+  const long long nk = static_cast<long long>(n_ktiles) * a.Hkv * a.B;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, MODE, ESTAGE>), dim3(static_cast<unsigned>(nk)), dim3(64 * DKV_WAVES), lds, s,
+                     a);
+  return hipGetLastError();
 }
 
 template <int D, int MODE>
@@ -693,29 +914,12 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(pre_grid), dim3(256), 0, s, a, zero_ptr, n_zero);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-
-  // dq (+ bias-parameter gradients)
-  const int n_qtiles = (a.S + 32 * DQ_WAVES - 1) / (32 * DQ_WAVES);
-  const int longest_first = (a.window == 0 || a.window > 32 * DQ_WAVES) ? 1 : 0;
-  const int dq_lds = dq_lds_bytes<D, MODE>();
-  e = allow_lds(&bwd_dq_kernel<D, MODE>, dq_lds);
+  // r.E: E staged in LDS where it fits beside the tiles
+  const bool dq_stage = MODE == 2 && DqLayout<D, MODE>::bytes(a.bias_range, a.R, true) <= kMaxLds;
+  const bool kv_stage = MODE == 2 && DkvLayout<D>::bytes(MODE, a.bias_range, a.R, true) <= kMaxLds;
+  e = dq_stage ? launch_dq<D, MODE, true>(a, s) : launch_dq<D, MODE, false>(a, s);
   if (e != hipSuccess) return e;
-  const long long nq = static_cast<long long>(n_qtiles) * a.Hq * a.B;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, MODE>), dim3(static_cast<unsigned>(nq)), dim3(64 * DQ_WAVES), dq_lds, s,
-                     a, n_qtiles, longest_first);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  // dk, dv
-  int tab_off = 0, cs_off = 0, total = 0;
-  dkdv_lds_layout<D>(MODE, a.bias_range, &tab_off, &cs_off, &total);
-  e = allow_lds(&bwd_dkdv_kernel<D, MODE>, total);
-  if (e != hipSuccess) return e;
-  const int n_ktiles = (a.S + 32 * DKV_WAVES - 1) / (32 * DKV_WAVES);
-  const long long nk = static_cast<long long>(n_ktiles) * a.Hkv * a.B;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, MODE>), dim3(static_cast<unsigned>(nk)), dim3(64 * DKV_WAVES), total, s,
-                     a, tab_off, cs_off);
-  return hipGetLastError();
+  return kv_stage ? launch_dkdv<D, MODE, true>(a, s) : launch_dkdv<D, MODE, false>(a, s);
 }
 
 template <int D>
@@ -729,18 +933,20 @@ hipError_t launch_bwd_mode(const BwdArgs& a, int mode, hipStream_t s) {
 
 }  // namespace
 
-// LDS the backward kernels need for this shape (the larger of the two), or -1 past 160 KB.
+// LDS the backward kernels need for this shape (the larger of the two, E read from global
+// memory), or -1 past 160 KB.
 int bwd_lds_bytes(int D, int mode, int bias_range) {
-  int t = 0, c = 0, total = 0;
-  int dq = 0;
+  int dq = 0, kv = 0;
   if (D == 128) {
-    dq = mode == 0 ? dq_lds_bytes<128, 0>() : (mode == 1 ? dq_lds_bytes<128, 1>() : dq_lds_bytes<128, 2>());
-    dkdv_lds_layout<128>(mode, bias_range, &t, &c, &total);
+    dq = mode == 0 ? DqLayout<128, 0>::bytes(bias_range, 1, false)
+                   : (mode == 1 ? DqLayout<128, 1>::bytes(bias_range, 1, false) : DqLayout<128, 2>::bytes(bias_range, 1, false));
+    kv = DkvLayout<128>::bytes(mode, bias_range, 1, false);
   } else {
-    dq = mode == 0 ? dq_lds_bytes<64, 0>() : (mode == 1 ? dq_lds_bytes<64, 1>() : dq_lds_bytes<64, 2>());
-    dkdv_lds_layout<64>(mode, bias_range, &t, &c, &total);
+    dq = mode == 0 ? DqLayout<64, 0>::bytes(bias_range, 1, false)
+                   : (mode == 1 ? DqLayout<64, 1>::bytes(bias_range, 1, false) : DqLayout<64, 2>::bytes(bias_range, 1, false));
+    kv = DkvLayout<64>::bytes(mode, bias_range, 1, false);
   }
-  const int m = std::max(dq, total);
+  const int m = std::max(dq, kv);
   return m > kMaxLds ? -1 : m;
 }
 
