@@ -449,13 +449,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
       if (W) on = on && (c - 31 < W);
       if (!on) continue;
 
+      // operands read one step ahead of the MFMAs that use them
       f32x16 sacc = zero16(), pacc = zero16();
+      const uint16_t* kr = Ks + (32 * kb + ln) * KST + 8 * lh;
+      const uint16_t* vr = Vs + (32 * kb + ln) * KST + 8 * lh;
+      bf16x8 kf = as_bf16x8(ld16(kr)), vf = as_bf16x8(ld16(vr));
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) {
-        const bf16x8 kf = as_bf16x8(ld16(Ks + (32 * kb + ln) * KST + 16 * cc + 8 * lh));
-        const bf16x8 vf = as_bf16x8(ld16(Vs + (32 * kb + ln) * KST + 16 * cc + 8 * lh));
+        bf16x8 kn = kf, vn = vf;
+        if (cc + 1 < NC) {
+          kn = as_bf16x8(ld16(kr + 16 * (cc + 1)));
+          vn = as_bf16x8(ld16(vr + 16 * (cc + 1)));
+        }
         sacc = mfma32(kf, qf[cc], sacc);
         pacc = mfma32(vf, dof[cc], pacc);
+        kf = kn;
+        vf = vn;
       }
       // log2-domain logits tau * (scale log2(e) q.k + log2(e) beta)
 #pragma unroll
@@ -483,9 +492,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int d = c + ln - out_row(i, lh);
-          const bool vis = d >= 0 && (W == 0 || d < W);
-          const float p = vis ? fast_exp2(sacc[i] - lse2) : 0.f;
-          dz[i] = p * (pacc[i] - dsum);
+          const bool vis = (d >= 0) & ((W == 0) | (d < W));
+          const float p = fast_exp2(sacc[i] - lse2);
+          dz[i] = (vis ? p : 0.f) * (pacc[i] - dsum);
         }
       } else {
 #pragma unroll
@@ -500,13 +509,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
         dzf[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
       }
       // dQ^T += K^T dS^T
+      {
+        const uint16_t* ktr = Kt + ln * TST + 32 * kb + 8 * lh;
+        bf16x8 kt = as_bf16x8(ld16(ktr));
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 kt = as_bf16x8(ld16(Kt + (32 * db + ln) * TST + 32 * kb + 16 * kk + 8 * lh));
-          dqacc[db] = mfma32(kt, dzf[kk], dqacc[db]);
+        for (int x = 0; x < 2 * NDB; ++x) {
+          bf16x8 kn = kt;
+          if (x + 1 < 2 * NDB) kn = as_bf16x8(ld16(ktr + 32 * ((x + 1) >> 1) * TST + 16 * ((x + 1) & 1)));
+          dqacc[x >> 1] = mfma32(kt, dzf[x & 1], dqacc[x >> 1]);
+          kt = kn;
         }
+      }
 
       if (MODE != 0 && inband) {
         // skewed dZ: G^T[dist][query] (and G[query][dist]) with dist = n - m + 32 over the
@@ -652,7 +665,6 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   const int key = j0w + ln;
   const bool key_ok = key < S;
   const int nfc = (a.R + 7) / 8;
-  const bool temp = a.temp_len > 0;
 
   const size_t q_row = static_cast<size_t>(a.Hq) * D;
   const size_t kv_row = static_cast<size_t>(a.Hkv) * D;
@@ -760,13 +772,22 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
       if (W) on = on && (c - 31 < W);
       if (!on) continue;
 
+      // operands read one step ahead of the MFMAs that use them
       f32x16 sacc = zero16(), pacc = zero16();
+      const uint16_t* qr = Qs + (32 * qb + ln) * QST + 8 * lh;
+      const uint16_t* dr_ = dOs + (32 * qb + ln) * QST + 8 * lh;
+      bf16x8 qa = as_bf16x8(ld16(qr)), da = as_bf16x8(ld16(dr_));
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) {
-        const bf16x8 qa = as_bf16x8(ld16(Qs + (32 * qb + ln) * QST + 16 * cc + 8 * lh));
-        const bf16x8 da = as_bf16x8(ld16(dOs + (32 * qb + ln) * QST + 16 * cc + 8 * lh));
+        bf16x8 qn = qa, dn = da;
+        if (cc + 1 < NC) {
+          qn = as_bf16x8(ld16(qr + 16 * (cc + 1)));
+          dn = as_bf16x8(ld16(dr_ + 16 * (cc + 1)));
+        }
         sacc = mfma32(qa, kf[cc], sacc);
         pacc = mfma32(da, vf[cc], pacc);
+        qa = qn;
+        da = dn;
       }
       // bias (log2 units) per element, before the temperature
       const bool inband = (MODE != 0) && (c - 31 < Rb);
@@ -792,33 +813,44 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
         }
         wave_sync_lds();
       }
-      // P into sacc, dZ = tau * P * (dP - rowsum) into pacc (in place)
+      // P into sacc, dZ = tau * P * (dP - rowsum) into pacc (in place); per row: lse (log2
+      // units), rowsum, c_qk * tau and tau (tau = 1 without a temperature).  Interior and
+      // edge blocks get separate loops so that no branch sits inside the element loop.
       const bool edge = (c - 31 < 0) || (W && c + 31 >= W);
+      const int wlim = W ? W : 0x7fffffff;
+      if (edge) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int m0 = 32 * qb + 8 * g4 + 4 * lh;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(rowp + m0);
-        const f32x4 s4 = *reinterpret_cast<const f32x4*>(rowp + BN + m0);
-        f32x4 c4, t4;
-        if (temp) {
-          c4 = *reinterpret_cast<const f32x4*>(rowp + 2 * BN + m0);
-          t4 = *reinterpret_cast<const f32x4*>(rowp + 3 * BN + m0);
-        }
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int m0 = 32 * qb + 8 * g4 + 4 * lh;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(rowp + m0);
+          const f32x4 s4 = *reinterpret_cast<const f32x4*>(rowp + BN + m0);
+          const f32x4 c4 = *reinterpret_cast<const f32x4*>(rowp + 2 * BN + m0);
+          const f32x4 t4 = *reinterpret_cast<const f32x4*>(rowp + 3 * BN + m0);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = 4 * g4 + u;
-          float x;
-          if (temp) x = fmaf(bias[i], t4[u], fmaf(sacc[i], c4[u], -l4[u]));
-          else x = fmaf(sacc[i], a.c_qk, bias[i] - l4[u]);
-          float p = fast_exp2(x);
-          if (edge) {
+          for (int u = 0; u < 4; ++u) {
+            const int i = 4 * g4 + u;
             const int d = c + out_row(i, lh) - ln;
-            if (!(d >= 0 && (W == 0 || d < W))) p = 0.f;
+            const float p = fast_exp2(fmaf(bias[i], t4[u], fmaf(sacc[i], c4[u], -l4[u])));
+            const float pm = ((d >= 0) & (d < wlim)) ? p : 0.f;
+            pacc[i] = pm * (pacc[i] - s4[u]) * t4[u];
+            sacc[i] = pm;
           }
-          float dzv = p * (pacc[i] - s4[u]);
-          if (temp) dzv *= t4[u];
-          pacc[i] = dzv;
-          sacc[i] = p;
+        }
+      } else {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int m0 = 32 * qb + 8 * g4 + 4 * lh;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(rowp + m0);
+          const f32x4 s4 = *reinterpret_cast<const f32x4*>(rowp + BN + m0);
+          const f32x4 c4 = *reinterpret_cast<const f32x4*>(rowp + 2 * BN + m0);
+          const f32x4 t4 = *reinterpret_cast<const f32x4*>(rowp + 3 * BN + m0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = 4 * g4 + u;
+            const float p = fast_exp2(fmaf(bias[i], t4[u], fmaf(sacc[i], c4[u], -l4[u])));
+            pacc[i] = p * (pacc[i] - s4[u]) * t4[u];
+            sacc[i] = p;
+          }
         }
       }
       bf16x8 pf[2], dzf[2];
@@ -834,14 +866,23 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
         dzf[kk] = as_bf16x8(u32x4{x[0], x[1], x[2], x[3]});
       }
       // dV^T += dO^T P,  dK^T += Q^T dZ
+      {
+        const int off0 = ln * TST + 32 * qb + 8 * lh;
+        bf16x8 oa = as_bf16x8(ld16(dOt + off0)), qt = as_bf16x8(ld16(Qt + off0));
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int off = (32 * db + ln) * TST + 32 * qb + 16 * kk + 8 * lh;
-          dvacc[db] = mfma32(as_bf16x8(ld16(dOt + off)), pf[kk], dvacc[db]);
-          dkacc[db] = mfma32(as_bf16x8(ld16(Qt + off)), dzf[kk], dkacc[db]);
+        for (int x = 0; x < 2 * NDB; ++x) {
+          bf16x8 on = oa, qn = qt;
+          if (x + 1 < 2 * NDB) {
+            const int off = off0 + 32 * ((x + 1) >> 1) * TST + 16 * ((x + 1) & 1);
+            on = as_bf16x8(ld16(dOt + off));
+            qn = as_bf16x8(ld16(Qt + off));
+          }
+          dvacc[x >> 1] = mfma32(oa, pf[x & 1], dvacc[x >> 1]);
+          dkacc[x >> 1] = mfma32(qt, dzf[x & 1], dkacc[x >> 1]);
+          oa = on;
+          qt = qn;
         }
+      }
     }
   }
 
