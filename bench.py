@@ -11,7 +11,9 @@ prefill kernel and the float64 oracle timed on this host as a CPU baseline.
 
 Other workloads (--workload): global_prefill, long_global_prefill,
 decode_global, decode_local, tiny_local_f32, decode_global_paged /
-decode_local_paged (the decode steps over a paged cache, 64-row pages), and
+decode_local_paged (the decode steps over a paged cache, 64-row pages),
+decode_global_fp4 / decode_local_fp4 (over MXFP4 caches: 68 bytes per row and kv
+head for each of K and V; GB/s counts those bytes), and
 local_prefill_bwd / global_prefill_bwd / long_global_prefill_bwd (one
 relbias_attn_bwd call per step, the forward's o and lse computed before timing;
 10*D algorithmic flops per visible pair: the five products of the backward).
@@ -235,7 +237,20 @@ def main():
         kv_lens = [w.S - j * w.window for j in range(4)] if (w.window and 4 * w.window <= w.S) else [w.S]
         it = [0]
 
-        if w.extra.get("page_size"):
+        if w.extra.get("kv") == "fp4":
+            # MXFP4 caches: 64 code bytes + 4 scale bytes per row and kv head, quantised once
+            kc, ks = rba.kv_quantize_fp4(inp["k"])
+            vc, vs = rba.kv_quantize_fp4(inp["v"])
+            torch.cuda.synchronize()
+
+            def step():
+                kv_len = kv_lens[it[0] % len(kv_lens)]
+                it[0] += 1
+                rba.decode_fp4(inp["q"], kc, ks, vc, vs, kv_len, window=w.window,
+                               bias_range=w.bias_range, mode=w.mode, table=inp["table"],
+                               r=inp["r"], E=inp["E"], scale=w.scale, temp_len=w.temp_len,
+                               out=out, workspace=ws)
+        elif w.extra.get("page_size"):
             # paged cache: the table scatters each sequence over a page pool; every sequence
             # has the step's cache length
             from transformer_attention_learned_amd.workloads import paged_view
@@ -261,6 +276,8 @@ def main():
         flops = 4.0 * w.D * w.Hq * w.B * nvis
         tokens = w.B
         hbm_bytes = 2.0 * w.B * nvis * w.Hkv * w.D * 2   # K + V over visible rows
+        if w.extra.get("kv") == "fp4":
+            hbm_bytes = 2.0 * w.B * nvis * w.Hkv * (w.D // 2 + w.D // 32)
         kind = "decode"
 
     for _ in range(args.warmup):
@@ -304,6 +321,8 @@ def main():
         cfg["page_size"] = w.extra["page_size"]
     if w.temp_len:
         cfg["temp_len"] = w.temp_len
+    if w.extra.get("kv"):
+        cfg["kv_cache"] = "mxfp4"
     line = {"metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

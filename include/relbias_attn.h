@@ -176,6 +176,41 @@ int relbias_attn_decode_paged(int dtype, const void* q, const void* k_pages, con
                               void* stream);
 
 /*
+ * MXFP4 quantisation of bf16 rows, the FP4 KV cache format of relbias_attn_decode_fp4.  The
+ * pages list an FP4 KV cache among Inkling's KV-cache compression methods and MXFP4 among its
+ * FP4 formats ("models/inkling" (archdiff), the component diagram: KV-cache compression and
+ * FP8-to-FP4 training); the format is the OCP Microscaling one: each block of 32 consecutive
+ * elements of a row shares the scale 2^(s - 127) stored as one byte s (E8M0), each element is
+ * a 4-bit E2M1 code (bit 3 the sign; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).  Rounding: the
+ * block exponent is floor(log2(max |x|)) - 2, clamped to [-126, 127]; x / 2^exponent goes to
+ * the nearest magnitude, ties to the even code, saturating at 6; the sign bit is set iff
+ * x < 0; an all-zero block gets scale byte 0 and zero codes.  NaN inputs are not supported.
+ *
+ *   x       [rows, D] bf16, 16-byte aligned; D a multiple of 32.
+ *   codes   [rows, D / 2] bytes (written): element 2j in the low nibble of byte j, element
+ *           2j + 1 in the high nibble; 16-byte aligned.
+ *   scales  [rows, D / 32] bytes (written).
+ * A KV cache [B, L, Hkv, D] is rows = B * L * Hkv rows of D.
+ */
+int relbias_attn_kv_quantize_fp4(const void* x, void* codes, void* scales, long long rows, int D,
+                                 void* stream);
+
+/*
+ * relbias_attn_decode over MXFP4 caches: the same computation, with K and V read from
+ * k_codes [B, L_max, Hkv, D / 2] + k_scales [B, L_max, Hkv, D / 32] (and the same for V) in
+ * the layout relbias_attn_kv_quantize_fp4 writes; each element is code value * 2^(s - 127)
+ * (scale byte 0 reads as 0).  q is bf16 [B, Hq, D]; every other argument (workspace size
+ * included) as in relbias_attn_decode with dtype RBA_BF16.  Supported: D = 128 and
+ * Hq / Hkv <= 16 (RBA_ENOTSUP otherwise).
+ */
+int relbias_attn_decode_fp4(const void* q, const void* k_codes, const void* k_scales,
+                            const void* v_codes, const void* v_scales, void* o, float* lse, int B,
+                            int L_max, int kv_len, int Hq, int Hkv, int D, int window,
+                            int bias_range, int mode, const float* table, const void* r,
+                            const float* E, int R, float scale, int temp_len, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace relbias_attn_bwd needs: one fp32 per (batch, row, query head).
  * Pure host function.
  */

@@ -37,7 +37,8 @@ def test_exports_every_declared_symbol(lib):
                           "relbias_attn_decode_workspace_size", "relbias_attn_decode_paged",
                           "relbias_attn_decode_paged_workspace_size", "relbias_attn_last_error",
                           "relbias_attn_version", "relbias_attn_bwd",
-                          "relbias_attn_bwd_workspace_size"}
+                          "relbias_attn_bwd_workspace_size", "relbias_attn_kv_quantize_fp4",
+                          "relbias_attn_decode_fp4"}
     for n in names:
         assert hasattr(lib, n), n
     assert "gfx950" in rba.version()
@@ -226,3 +227,29 @@ def test_bwd_empty_and_workspace(lib):
     assert _bwd(lib, S=0, q=None) == 0
     assert lib.relbias_attn_bwd_workspace_size(2, 100, 8) == 2 * 100 * 8 * 4
     assert lib.relbias_attn_bwd_workspace_size(0, 100, 8) == 0
+
+
+def test_fp4_rejects(lib):
+    q = lib.relbias_attn_kv_quantize_fp4
+    assert q(P, P, P, 10, 48, None) == EINVAL and "multiple of 32" in rba.last_error()
+    assert q(P, P, P, -1, 64, None) == EINVAL
+    assert q(None, P, P, 4, 64, None) == EINVAL and "non-NULL" in rba.last_error()
+    assert q(P + 8, P, P, 4, 64, None) == EINVAL and "aligned" in rba.last_error()
+    assert q(P, P, P, 0, 64, None) == 0
+
+    def dec(**kw):
+        a = dict(q=P, kc=P, ks=P, vc=P, vs=P, o=P, lse=None, B=2, L=100, kv_len=50, Hq=8, Hkv=2,
+                 D=128, window=0, bias_range=8, mode=0, table=None, r=None, E=None, R=0,
+                 scale=0.1, temp_len=0, ws=None, wsb=0)
+        a.update(kw)
+        return lib.relbias_attn_decode_fp4(
+            a["q"], a["kc"], a["ks"], a["vc"], a["vs"], a["o"], a["lse"], a["B"], a["L"],
+            a["kv_len"], a["Hq"], a["Hkv"], a["D"], a["window"], a["bias_range"], a["mode"],
+            a["table"], a["r"], a["E"], a["R"], a["scale"], a["temp_len"], a["ws"], a["wsb"], None)
+    assert dec(D=64) == ENOTSUP and "head_dim 128" in rba.last_error()
+    assert dec(Hq=32, Hkv=1) == ENOTSUP and "<= 16" in rba.last_error()
+    assert dec(kv_len=0) == EINVAL and "kv_len" in rba.last_error()
+    assert dec(ks=None) == EINVAL and "non-NULL" in rba.last_error()
+    assert dec(vc=P + 4) == EINVAL and "aligned" in rba.last_error()
+    assert dec(temp_len=1) == EINVAL and "temp_len" in rba.last_error()
+    assert dec(B=0) == 0

@@ -1,0 +1,146 @@
+"""GPU checks of the MXFP4 KV cache: the quantiser against the oracle's encoding bit for bit,
+and decode over MXFP4 caches against the float64 oracle on the dequantised caches.
+
+In the decode cases the oracle encodes the evaluated sequences itself (oracle/mxfp4.py), the
+GPU's bytes must equal its bytes, and the expected outputs come from the oracle's own
+dequantised caches.  Decode bar: the bf16 bar of the other decode tests (max |err| <= 2e-2,
+relative L2 <= 5e-3) on o and lse.
+"""
+
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import mxfp4
+import transformer_attention_learned_amd as rba
+from transformer_attention_learned_amd.workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX_ABS, BF16_REL_L2 = 2e-2, 5e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rba.load_library()
+
+
+def _host_quant(x):
+    """Oracle MXFP4 encoding of a bf16 tensor [..., D] -> (packed codes, scales) as uint8 tensors."""
+    codes, sb = mxfp4.quantize(x)
+    return torch.from_numpy(mxfp4.pack(codes)), torch.from_numpy(sb)
+
+
+def test_quantize_bit_exact():
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    rows, D = 3000, 128
+    x = torch.randn((rows, D), generator=gen, device="cuda", dtype=torch.float32)
+    # block magnitudes over a wide exponent range, exact midpoints, zero and tiny blocks
+    k = torch.randint(-30, 30, (rows, D // 32), generator=gen, device="cuda").to(torch.float32)
+    x = x * torch.exp2(k).repeat_interleave(32, dim=1)
+    mids = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 4.0], device="cuda")
+    x[0, :8] = mids
+    x[0, 8:16] = -mids
+    x[1, :32] = 0.0
+    x[2, :32] = 1e-30
+    x[3, 32:64] = -0.0
+    xb = x.to(torch.bfloat16).contiguous()
+    codes, scales = rba.kv_quantize_fp4(xb)
+    torch.cuda.synchronize()
+    ref_codes, ref_sb = mxfp4.quantize(xb)
+    np.testing.assert_array_equal(scales.cpu().numpy(), ref_sb)
+    np.testing.assert_array_equal(codes.cpu().numpy(), mxfp4.pack(ref_codes))
+    # the midpoints row: the scale is 2^0 and each midpoint went to its even neighbour
+    deq = mxfp4.dequantize(mxfp4.unpack(codes[0].cpu().numpy()), scales[0].cpu().numpy())
+    np.testing.assert_array_equal(deq[:8], [0, 1, 1, 2, 2, 4, 4, 4])
+
+
+def _check_decode(w: Workload, kv_len, batches=None):
+    """Quantise the caches on the GPU, decode, and compare with the oracle: the oracle encodes the
+    evaluated sequences itself (its bytes must equal the GPU's) and decodes the dequantised rows."""
+    _say(f"  fp4 decode case {w.name}: B={w.B} L={w.S} kv_len={kv_len} Hq={w.Hq} Hkv={w.Hkv} "
+         f"W={w.window} Rb={w.bias_range} mode={w.mode} temp_len={w.temp_len} seed={w.seed}")
+    inp = make_inputs(w, device="cuda")
+    batches = list(range(w.B)) if batches is None else batches
+    kc, ks = rba.kv_quantize_fp4(inp["k"])
+    vc, vs = rba.kv_quantize_fp4(inp["v"])
+    o, lse = rba.decode_fp4(inp["q"], kc, ks, vc, vs, kv_len, window=w.window,
+                            bias_range=w.bias_range, mode=w.mode, table=inp["table"], r=inp["r"],
+                            E=inp["E"], scale=w.scale, temp_len=w.temp_len, return_lse=True)
+    torch.cuda.synchronize()
+    idx = torch.tensor(batches)
+    hk, hks = _host_quant(inp["k"][idx, :kv_len].cpu())
+    hv, hvs = _host_quant(inp["v"][idx, :kv_len].cpu())
+    assert torch.equal(kc[idx, :kv_len].cpu(), hk) and torch.equal(ks[idx, :kv_len].cpu(), hks)
+    assert torch.equal(vc[idx, :kv_len].cpu(), hv) and torch.equal(vs[idx, :kv_len].cpu(), hvs)
+    kd = mxfp4.dequantize(mxfp4.unpack(hk.numpy()), hks.numpy())
+    vd = mxfp4.dequantize(mxfp4.unpack(hv.numpy()), hvs.numpy())
+    sub = lambda t: None if t is None else t[idx.to(t.device)]
+    ro, rl = oracle.decode(sub(inp["q"]), kd, vd, kv_len, scale=w.scale, window=w.window,
+                           bias_range=w.bias_range, mode=w.mode, table=inp["table"],
+                           r=sub(inp["r"]), E=inp["E"], temp_len=w.temp_len)
+    got_o = o[idx.cuda()].to("cpu", torch.float64).numpy()
+    got_l = lse[idx.cuda()].to("cpu", torch.float64).numpy()
+    for name, g, r in (("o", got_o, ro), ("lse", got_l, rl)):
+        assert np.all(np.isfinite(g))
+        max_abs = float(np.abs(g - r).max())
+        rel = float(np.linalg.norm(g - r) / np.linalg.norm(r))
+        _say(f"    parity fp4 {name}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+        assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, (name, max_abs, rel)
+
+
+CASES = [
+    dict(S=100, kv_len=1), dict(S=100, kv_len=65), dict(S=3000, kv_len=2999),
+    dict(S=6000, kv_len=5000, bias_range=1024), dict(S=6000, kv_len=5000, window=512, bias_range=512),
+    dict(S=2000, kv_len=1999, mode="table", bias_range=300), dict(S=1500, kv_len=1400, mode="none"),
+    dict(S=3000, kv_len=2600, mode="rproj_shared", R=16, window=512, bias_range=512,
+         logit_scale="inv_d"),
+    dict(S=3000, kv_len=2900, Hq=16, Hkv=1, window=700), dict(S=4000, kv_len=3000, temp_len=1024),
+]
+
+
+@pytest.mark.parametrize("kw", CASES, ids=lambda kw: "-".join(f"{k}{v}" for k, v in kw.items()))
+def test_decode_fp4_matches_oracle(kw):
+    kv_len = kw.pop("kv_len")
+    base = dict(kind="decode", dtype="bf16", B=3, Hq=8, Hkv=2, D=128, S=100, window=0,
+                bias_range=64, mode="rproj", R=8, seed=zlib.crc32(repr(sorted(kw.items())).encode()) % 1000)
+    base.update(kw)
+    w = Workload(name="fp4_" + "_".join(f"{k}{v}" for k, v in kw.items()), **base)
+    _check_decode(w, kv_len)
+
+
+def test_decode_fp4_local_layer_workload():
+    """The local-layer decode shape (B64, window 512, 2048-row caches), three sequences checked."""
+    w = WORKLOADS["decode_local"].with_(S=2048, name="fp4_decode_local")
+    _check_decode(w, 2048, batches=[0, 17, 63])
+
+
+def test_quantize_then_decode_equals_host_quantised_decode():
+    """Caches quantised on the GPU give the same bytes, hence the same decode, as the oracle's."""
+    w = Workload(name="fp4_ident", kind="decode", dtype="bf16", B=2, Hq=8, Hkv=2, D=128, S=1024,
+                 window=0, bias_range=256, mode="rproj", R=8, seed=77)
+    inp = make_inputs(w, device="cuda")
+    kc, ks = rba.kv_quantize_fp4(inp["k"])
+    vc, vs = rba.kv_quantize_fp4(inp["v"])
+    hkc, hks = _host_quant(inp["k"].cpu())
+    torch.cuda.synchronize()
+    assert torch.equal(kc.cpu(), hkc) and torch.equal(ks.cpu(), hks)
+    o1 = rba.decode_fp4(inp["q"], kc, ks, vc, vs, 1000, bias_range=256, mode="rproj", r=inp["r"],
+                        E=inp["E"])
+    hvc, hvs = _host_quant(inp["v"].cpu())
+    o2 = rba.decode_fp4(inp["q"], hkc.cuda(), hks.cuda(), hvc.cuda(), hvs.cuda(), 1000,
+                        bias_range=256, mode="rproj", r=inp["r"], E=inp["E"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)

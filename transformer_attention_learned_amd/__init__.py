@@ -22,7 +22,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "bwd", "decode", "decode_paged", "decode_workspace_size", "last_error", "version",
+__all__ = ["fwd", "bwd", "decode", "decode_paged", "decode_fp4", "kv_quantize_fp4",
+           "decode_workspace_size", "last_error", "version",
            "library_path",
            "load_library", "RBA_OK", "RBA_EINVAL", "RBA_ENOTSUP", "RBA_EHIP", "MODES",
            "LibraryError"]
@@ -76,6 +77,11 @@ def load_library():
     lib.relbias_attn_bwd.restype = i
     lib.relbias_attn_bwd_workspace_size.argtypes = [i, i, i]
     lib.relbias_attn_bwd_workspace_size.restype = sz
+    lib.relbias_attn_kv_quantize_fp4.argtypes = [vp, vp, vp, ctypes.c_longlong, i, vp]
+    lib.relbias_attn_kv_quantize_fp4.restype = i
+    lib.relbias_attn_decode_fp4.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i,
+                                            vp, vp, vp, i, f, i, vp, sz, vp]
+    lib.relbias_attn_decode_fp4.restype = i
     lib.relbias_attn_last_error.argtypes = []
     lib.relbias_attn_last_error.restype = ctypes.c_char_p
     lib.relbias_attn_version.argtypes = []
@@ -230,6 +236,69 @@ def bwd(q, k, v, o, lse, dout, *, window=0, bias_range=0, mode="none", table=Non
     if st != RBA_OK:
         raise LibraryError(st, last_error())
     return out
+
+
+def kv_quantize_fp4(x, stream=None):
+    """MXFP4 quantisation (relbias_attn_kv_quantize_fp4) of bf16 x [..., D] (D % 32 == 0).
+
+    Returns (codes uint8 [..., D / 2], scales uint8 [..., D / 32]) on x's device.
+    """
+    import torch
+    lib = load_library()
+    _check(x, "x", dtype=torch.bfloat16)
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    codes = torch.empty(x.shape[:-1] + (D // 2,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1] + (D // 32,), dtype=torch.uint8, device=x.device)
+    st = lib.relbias_attn_kv_quantize_fp4(_ptr(x), _ptr(codes), _ptr(scales), rows, D,
+                                          _stream_handle(x.device, stream))
+    if st != RBA_OK:
+        raise LibraryError(st, last_error())
+    return codes, scales
+
+
+def decode_fp4(q, k_codes, k_scales, v_codes, v_scales, kv_len, *, window=0, bias_range=0,
+               mode="none", table=None, r=None, E=None, scale=None, temp_len=0, out=None,
+               lse=None, workspace=None, return_lse=False, stream=None):
+    """One decode step over MXFP4 caches (relbias_attn_decode_fp4).
+
+    q [B,Hq,D] bf16; k_codes / v_codes uint8 [B,L_max,Hkv,D/2]; k_scales / v_scales uint8
+    [B,L_max,Hkv,D/32] (as kv_quantize_fp4 writes them).  Other arguments as in decode.
+    """
+    import torch
+    lib = load_library()
+    dev = q.device
+    _check(q, "q", dtype=torch.bfloat16, ndim=3)
+    for t, n in ((k_codes, "k_codes"), (k_scales, "k_scales"), (v_codes, "v_codes"),
+                 (v_scales, "v_scales")):
+        _check(t, n, dtype=torch.uint8, ndim=4, device=dev)
+    B, Hq, D = q.shape
+    L_max, Hkv = k_codes.shape[1], k_codes.shape[2]
+    if (tuple(k_codes.shape) != (B, L_max, Hkv, D // 2) or v_codes.shape != k_codes.shape or
+            tuple(k_scales.shape) != (B, L_max, Hkv, D // 32) or v_scales.shape != k_scales.shape):
+        raise ValueError("codes must be [B,L_max,Hkv,D/2] and scales [B,L_max,Hkv,D/32]")
+    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev)
+    if m in (2, 3) and tuple(r.shape) != (B, Hq, R):
+        raise ValueError(f"r must be [B,Hq,R] = {(B, Hq, R)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = lib.relbias_attn_decode_workspace_size(B, Hq, Hkv, D, int(kv_len), int(window))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.relbias_attn_decode_fp4(
+        _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales), _ptr(out),
+        _ptr(lse), B, L_max, int(kv_len), Hq, Hkv, D, int(window), int(bias_range), m,
+        _ptr(table if m == 1 else None), _ptr(r if m in (2, 3) else None),
+        _ptr(E if m in (2, 3) else None), R, float(scale), int(temp_len), _ptr(workspace), wbytes,
+        _stream_handle(dev, stream))
+    if st != RBA_OK:
+        raise LibraryError(st, last_error())
+    return (out, lse) if (return_lse or lse is not None) else out
 
 
 def decode_workspace_size(B, Hq, Hkv, D, kv_len, window=0) -> int:

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librelbias_attn.so")
 
 SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_bf16_fast.hip", "attn_f32.hip", "decode_bf16.hip",
-           "bwd_bf16.hip"]
+           "bwd_bf16.hip", "kv_fp4.hip"]
 ARCH = "gfx950"
 
 

@@ -360,6 +360,88 @@ int relbias_attn_decode_paged(int dtype, const void* q, const void* k_pages, con
   return ok();
 }
 
+int relbias_attn_kv_quantize_fp4(const void* x, void* codes, void* scales, long long rows, int D,
+                                 void* stream) {
+  const char* fn = "relbias_attn_kv_quantize_fp4";
+  if (rows < 0) return fail(RBA_EINVAL, "%s: rows=%lld must be >= 0", fn, rows);
+  if (D < 32 || D % 32) return fail(RBA_EINVAL, "%s: D=%d must be a positive multiple of 32", fn, D);
+  if (rows == 0) return ok();
+  if (!x || !codes || !scales) return fail(RBA_EINVAL, "%s: x, codes and scales must be non-NULL", fn);
+  if (!aligned16(x) || !aligned16(codes))
+    return fail(RBA_EINVAL, "%s: x and codes must be 16-byte aligned", fn);
+  if (rows > (1LL << 40) / D) return fail(RBA_ENOTSUP, "%s: problem too large", fn);
+  hipError_t e = rba::launch_quantize_fp4(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(codes),
+                                          static_cast<uint8_t*>(scales), rows * (D / 32),
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+int relbias_attn_decode_fp4(const void* q, const void* k_codes, const void* k_scales,
+                            const void* v_codes, const void* v_scales, void* o, float* lse, int B,
+                            int L_max, int kv_len, int Hq, int Hkv, int D, int window,
+                            int bias_range, int mode, const float* table, const void* r,
+                            const float* E, int R, float scale, int temp_len, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  const char* fn = "relbias_attn_decode_fp4";
+  if (B < 0) return fail(RBA_EINVAL, "%s: B=%d must be >= 0", fn, B);
+  int st = check_common(fn, RBA_BF16, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale);
+  if (st == RBA_OK) st = check_temp(fn, temp_len);
+  if (st != RBA_OK) return st;
+  if (D != 128) return fail(RBA_ENOTSUP, "%s: MXFP4 caches are supported for head_dim 128, got %d", fn, D);
+  const int G = Hq / Hkv;
+  if (G > 16) return fail(RBA_ENOTSUP, "%s: MXFP4 caches support Hq/Hkv <= 16, got %d", fn, G);
+  if (B == 0) return ok();
+  if (L_max < 1 || kv_len < 1 || kv_len > L_max)
+    return fail(RBA_EINVAL, "%s: need 1 <= kv_len (%d) <= L_max (%d)", fn, kv_len, L_max);
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !o)
+    return fail(RBA_EINVAL, "%s: q, codes, scales and o must be non-NULL", fn);
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(o))
+    return fail(RBA_EINVAL, "%s: q, codes and o must be 16-byte aligned", fn);
+  if (lse && !aligned_to(lse, 4)) return fail(RBA_EINVAL, "%s: lse is not 4-byte aligned", fn);
+  int ns = 1, kpw = 64;
+  rba::decode_split(B, Hkv, kv_len, window, &ns, &kpw);
+  const size_t need = relbias_attn_decode_workspace_size(B, Hq, Hkv, D, kv_len, window);
+  if (need > 0) {
+    if (!workspace) return fail(RBA_EINVAL, "%s: workspace of %zu bytes required, got NULL", fn, need);
+    if (workspace_bytes < need)
+      return fail(RBA_EINVAL, "%s: workspace too small (%zu < %zu bytes)", fn, workspace_bytes, need);
+    if (!aligned_to(workspace, 4)) return fail(RBA_EINVAL, "%s: workspace is not 4-byte aligned", fn);
+  }
+  if (Hkv > 65535 || B > 65535) return fail(RBA_ENOTSUP, "%s: grid too large", fn);
+  rba::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_codes);
+  a.v = static_cast<const uint16_t*>(v_codes);
+  a.k_scale = static_cast<const uint8_t*>(k_scales);
+  a.v_scale = static_cast<const uint8_t*>(v_scales);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.table = table;
+  a.r = static_cast<const uint16_t*>(r);
+  a.E = E;
+  a.ws = static_cast<float*>(workspace);
+  a.B = B;
+  a.L_max = L_max;
+  a.kv_len = kv_len;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.window = window;
+  a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
+  a.R = is_rproj(mode) ? R : 0;
+  a.e_hs = e_head_stride(mode, R, bias_range);
+  a.key_begin = window ? (kv_len > window ? kv_len - window : 0) : 0;
+  a.n_split = ns;
+  a.keys_per_wave = kpw;
+  a.c_qk = scale * rba::kLog2e;
+  a.temp_len = temp_len;
+  a.temp_inv_log2 = temp_inv_log2(temp_len);
+  hipError_t e = rba::launch_decode_fp4(a, kernel_mode(mode), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 size_t relbias_attn_bwd_workspace_size(int B, int S, int Hq) {
   if (B <= 0 || S <= 0 || Hq <= 0) return 0;
   return static_cast<size_t>(B) * S * Hq * sizeof(float);

@@ -349,7 +349,23 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
 //     elements in the order the scores already sit in (element j of lane group g is row
 //     16 (j / 4) + 4 g + j % 4), so P is packed in place; V^T is stored in LDS with the rows
 //     permuted to that order, one 16-byte read per lane.
-template <int D, int MODE, int RMAX>
+// 8 MXFP4 codes (element 2j in the low nibble of byte j) times the block scale -> 8 bf16,
+// with the hardware FP4 conversion (v_cvt_scalef32_pk_bf16_fp4, one byte per instruction).
+__device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t codes, float sc) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3))};
+}
+// E8M0 scale byte -> 2^(byte - 127) as fp32 (byte 0, an all-zero block, reads as 0).
+__device__ __forceinline__ float e8m0(uint32_t byte) { return __uint_as_float(byte << 23); }
+
+// FP4: the caches hold MXFP4 codes (a.k / a.v: D / 2 bytes per row and kv head) and E8M0
+// block scales (a.k_scale / a.v_scale: D / 32 bytes); the tiles in flight are the packed bytes
+// (a quarter of the registers of bf16 rows) and are widened to bf16 where the MFMAs use them.
+// A lane's K fragment then covers head dims 32 g + 8 c .. + 7 (one 16-byte load per row and a
+// single scale), so the query fragments use the same dims.
+template <int D, int MODE, int RMAX, bool FP4>
 __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curve_off) {
   constexpr int VST = TK + 8;          // V^T row stride (bf16)
   constexpr int NC = D / 32;           // K = 32 chunks of the head dim
@@ -391,7 +407,17 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
   const int ntiles = w_end > w_beg ? (w_end - w_beg + TK - 1) / TK : 0;
 
   // ---- two register sets of tiles in flight: K as A-operand fragments, V as row pieces ----
-  u32x4 kreg[2][2][NC], vreg[2][NVI][4];
+  u32x4 kreg[2][2][FP4 ? 1 : NC], vreg[2][NVI][FP4 ? 1 : 4];
+  // FP4: 16 code bytes and the scale byte per K row, 4 code bytes and a scale byte per V row
+  u32x4 kc[2][2];
+  uint32_t ksb[2][2], vc[2][NVI][4], vsb[2][NVI][4];
+  constexpr int CB = D / 2, SB = D / 32;
+  const size_t crow = static_cast<size_t>(a.Hkv) * CB, srow = static_cast<size_t>(a.Hkv) * SB;
+  const size_t cbatch = paged ? 0 : static_cast<size_t>(b) * a.L_max;
+  const uint8_t* kcb = reinterpret_cast<const uint8_t*>(a.k) + (cbatch * a.Hkv + hkv) * CB;
+  const uint8_t* vcb = reinterpret_cast<const uint8_t*>(a.v) + (cbatch * a.Hkv + hkv) * CB;
+  const uint8_t* ksp = FP4 ? a.k_scale + (cbatch * a.Hkv + hkv) * SB : nullptr;
+  const uint8_t* vsp = FP4 ? a.v_scale + (cbatch * a.Hkv + hkv) * SB : nullptr;
   auto load_tile = [&](int set, int tk0) {
     // K rows tk0 + 16 kb + (l % 16); paged: one table read per lane and row block, and lane
     // l < 32 keeps the pool row of cache row tk0 + l for the V loads below
@@ -401,11 +427,20 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
       const int key = tk0 + 16 * kb + n16;
       const int prow = paged ? (key < w_end ? pool_row(key) : 0) : key;
       if (kb == (g & 1)) prow32 = prow;
-      const uint16_t* kp = kbase + static_cast<size_t>(prow) * kv_row + 8 * g;
+      if constexpr (FP4) {
+        kc[set][kb] = u32x4{0u, 0u, 0u, 0u};
+        ksb[set][kb] = 0u;
+        if (key < w_end) {
+          kc[set][kb] = ld16(kcb + static_cast<size_t>(prow) * crow + 16 * g);
+          ksb[set][kb] = ksp[static_cast<size_t>(prow) * srow + g];
+        }
+      } else {
+        const uint16_t* kp = kbase + static_cast<size_t>(prow) * kv_row + 8 * g;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        kreg[set][kb][c] = u32x4{0u, 0u, 0u, 0u};
-        if (key < w_end) kreg[set][kb][c] = ld16(kp + 32 * c);
+        for (int c = 0; c < NC; ++c) {
+          kreg[set][kb][c] = u32x4{0u, 0u, 0u, 0u};
+          if (key < w_end) kreg[set][kb][c] = ld16(kp + 32 * c);
+        }
       }
     }
 #pragma unroll
@@ -418,19 +453,28 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
         const int kk = tk0 + 4 * kg + s4;
         int vrow = kk;
         if (paged) vrow = __shfl(prow32, 4 * kg + s4, 64);
-        vreg[set][it][s4] = u32x4{0u, 0u, 0u, 0u};
-        if (kk < w_end) vreg[set][it][s4] = ld16(vbase + static_cast<size_t>(vrow) * kv_row + 8 * dg);
+        if constexpr (FP4) {
+          vc[set][it][s4] = 0u;
+          vsb[set][it][s4] = 0u;
+          if (kk < w_end) {
+            vc[set][it][s4] = *reinterpret_cast<const uint32_t*>(vcb + static_cast<size_t>(vrow) * crow + 4 * dg);
+            vsb[set][it][s4] = vsp[static_cast<size_t>(vrow) * srow + (dg >> 2)];
+          }
+        } else {
+          vreg[set][it][s4] = u32x4{0u, 0u, 0u, 0u};
+          if (kk < w_end) vreg[set][it][s4] = ld16(vbase + static_cast<size_t>(vrow) * kv_row + 8 * dg);
+        }
       }
     }
   };
 
   bf16x8 qf[NC];
   {
-    const uint16_t* qp = a.q + (static_cast<size_t>(b) * a.Hq + hkv * G + (col_live ? n16 : 0)) * D + 8 * g;
+    const uint16_t* qp = a.q + (static_cast<size_t>(b) * a.Hq + hkv * G + (col_live ? n16 : 0)) * D + (FP4 ? 32 * g : 8 * g);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (col_live) v = ld16(qp + 32 * c);
+      if (col_live) v = ld16(qp + (FP4 ? 8 * c : 32 * c));
       qf[c] = as_bf16x8(v);
     }
   }
@@ -515,8 +559,15 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (FP4) {
+        const float ks = e8m0(ksb[set][kb]);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) sacc[kb] = mfma16(as_bf16x8(kreg[set][kb][c]), qf[c], sacc[kb]);
+        for (int c = 0; c < NC; ++c)
+          sacc[kb] = mfma16(as_bf16x8(fp4x8_to_bf16(kc[set][kb][c], ks)), qf[c], sacc[kb]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) sacc[kb] = mfma16(as_bf16x8(kreg[set][kb][c]), qf[c], sacc[kb]);
+      }
     }
     // V of this tile -> LDS, transposed and row-permuted (the previous tile's reads are done)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -528,13 +579,27 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
       const int kg = item & 7;
       const int dg = item >> 3;
       const int pos = vt_pos16(4 * kg);
+      if constexpr (FP4) {
+        u32x4 rows[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t p01 = __builtin_amdgcn_perm(vreg[set][it][1][w], vreg[set][it][0][w], sel);
-        const uint32_t p23 = __builtin_amdgcn_perm(vreg[set][it][3][w], vreg[set][it][2][w], sel);
-        st8(vt + (8 * dg + e) * VST + pos, u32x2{p01, p23});
+        for (int s4 = 0; s4 < 4; ++s4) rows[s4] = fp4x8_to_bf16(vc[set][it][s4], e8m0(vsb[set][it][s4]));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int w = e >> 1;
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t p01 = __builtin_amdgcn_perm(rows[1][w], rows[0][w], sel);
+          const uint32_t p23 = __builtin_amdgcn_perm(rows[3][w], rows[2][w], sel);
+          st8(vt + (8 * dg + e) * VST + pos, u32x2{p01, p23});
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int w = e >> 1;
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t p01 = __builtin_amdgcn_perm(vreg[set][it][1][w], vreg[set][it][0][w], sel);
+          const uint32_t p23 = __builtin_amdgcn_perm(vreg[set][it][3][w], vreg[set][it][2][w], sel);
+          st8(vt + (8 * dg + e) * VST + pos, u32x2{p01, p23});
+        }
       }
     }
     // this set's registers are free: the tile two ahead goes in flight
@@ -657,7 +722,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   if (d == 0 && a.lse) a.lse[bh] = (M + fast_log2(l)) * kLn2;
 }
 
-template <int D, int MODE, int RMAX>
+template <int D, int MODE, int RMAX, bool FP4 = false>
 hipError_t launch_d(DecodeArgs a, hipStream_t s) {
   const dim3 grid(a.n_split, a.Hkv, a.B);
   constexpr int VT_ALL = 4 * D * (TK + 8) * 2;
@@ -667,9 +732,10 @@ hipError_t launch_d(DecodeArgs a, hipStream_t s) {
   const int total = curve_off + (MODE == 2 ? a.G * a.R * 4 : 0) + (MODE != 0 ? 4 * 2 * a.G * TK * 4 : 0);
   if (total > 160 * 1024) return hipErrorInvalidValue;
   // groups of up to 16 query heads: the 16x16 MFMA kernel (two tiles in flight per wave)
+  // (FP4 caches: the 16x16 kernel only; the C ABI rejects larger groups)
   static bool attr_set[2] = {false, false};
-  const bool narrow = a.G <= 16;
-  const void* fn = narrow ? reinterpret_cast<const void*>(&decode16_kernel<D, MODE, RMAX>)
+  const bool narrow = FP4 || a.G <= 16;
+  const void* fn = narrow ? reinterpret_cast<const void*>(&decode16_kernel<D, MODE, RMAX, FP4>)
                           : reinterpret_cast<const void*>(&decode_bf16_kernel<D, MODE, RMAX>);
   if (!attr_set[narrow]) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
@@ -677,7 +743,7 @@ hipError_t launch_d(DecodeArgs a, hipStream_t s) {
     attr_set[narrow] = true;
   }
   if (narrow)
-    hipLaunchKernelGGL((decode16_kernel<D, MODE, RMAX>), grid, dim3(256), total, s, a, curve_off);
+    hipLaunchKernelGGL((decode16_kernel<D, MODE, RMAX, FP4>), grid, dim3(256), total, s, a, curve_off);
   else
     hipLaunchKernelGGL((decode_bf16_kernel<D, MODE, RMAX>), grid, dim3(256), total, s, a, curve_off);
   hipError_t e = hipGetLastError();
@@ -706,6 +772,14 @@ void decode_split(int B, int Hkv, int kv_len, int window, int* n_split, int* key
   if (ns < 1) ns = 1;
   *n_split = static_cast<int>(ns);
   *keys_per_wave = static_cast<int>(kpw);
+}
+
+hipError_t launch_decode_fp4(DecodeArgs a, int mode, hipStream_t s) {
+  switch (mode) {
+    case 0: return launch_d<128, 0, 1, true>(a, s);
+    case 1: return launch_d<128, 1, 1, true>(a, s);
+    default: return a.R > 8 ? launch_d<128, 2, 16, true>(a, s) : launch_d<128, 2, 8, true>(a, s);
+  }
 }
 
 hipError_t launch_decode_bf16(DecodeArgs a, int D, int mode, hipStream_t s) {

@@ -96,6 +96,8 @@ struct DecodeArgs {
   // paged cache: k/v are page pools [num_pages, page_size, Hkv, D]; row j of sequence b lives
   // in page block_table[b * max_pages + j / page_size] at slot j % page_size; the cache length
   // of sequence b is kv_lens[b] (kv_len is then the upper bound the split was sized for)
+  const uint8_t* k_scale;   // MXFP4 caches: E8M0 scales [B, L_max, Hkv, D / 32] (k / v then
+  const uint8_t* v_scale;   // hold the packed codes [B, L_max, Hkv, D / 2]); null for bf16
   const int* block_table;   // null: contiguous caches [B, L_max, Hkv, D]
   const int* kv_lens;
   int page_size, max_pages, num_pages;
@@ -144,6 +146,10 @@ int fwd_fast_lds_bytes(int D, int G, int mode, int bias_range, int R, float scal
 hipError_t launch_fwd_bf16_fast(const FwdArgs& a, int mode, hipStream_t s);
 hipError_t launch_attn_f32(const F32Args& a, hipStream_t s);
 hipError_t launch_decode_bf16(DecodeArgs a, int D, int mode, hipStream_t s);
+// Decode over MXFP4 caches (D = 128, G <= 16) and the MXFP4 quantiser of bf16 rows
+// (nblk blocks of 32 elements: 16 code bytes and one scale byte each).
+hipError_t launch_decode_fp4(DecodeArgs a, int mode, hipStream_t s);
+hipError_t launch_quantize_fp4(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long nblk, hipStream_t s);
 
 // Decode split policy, shared by the workspace-size query and the launcher.
 void decode_split(int B, int Hkv, int kv_len, int window, int* n_split, int* keys_per_wave);

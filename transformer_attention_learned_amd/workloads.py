@@ -101,6 +101,10 @@ WORKLOADS = {
 }
 
 
+# The decode steps over MXFP4 caches (the caches quantised once before timing).
+for _name in ("decode_global", "decode_local"):
+    WORKLOADS[_name + "_fp4"] = WORKLOADS[_name].with_(name=_name + "_fp4", extra={"kv": "fp4"})
+
 # Backward passes of the three prefill layers (same inputs, plus the output gradient).
 for _name in ("local_prefill", "global_prefill", "long_global_prefill"):
     WORKLOADS[_name + "_bwd"] = WORKLOADS[_name].with_(name=_name + "_bwd", kind="backward")
