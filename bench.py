@@ -202,8 +202,9 @@ def main():
         o, lse = rba.fwd(inp["q"], inp["k"], inp["v"], window=w.window, bias_range=w.bias_range,
                          mode=w.mode, table=inp["table"], r=inp["r"], E=inp["E"], scale=w.scale,
                          temp_len=w.temp_len, return_lse=True)
-        ws = torch.empty(max(rba.load_library().relbias_attn_bwd_workspace_size(w.B, w.S, w.Hq), 1),
-                         dtype=torch.uint8, device=dev)
+        need = rba.load_library().relbias_attn_bwd_workspace_size(w.B, w.S, w.Hq, rba.MODES[w.mode],
+                                                                  w.bias_range)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
         def step():
             rba.bwd(inp["q"], inp["k"], inp["v"], o, lse, inp["dout"], window=w.window,

@@ -211,10 +211,11 @@ int relbias_attn_decode_fp4(const void* q, const void* k_codes, const void* k_sc
                             size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of device workspace relbias_attn_bwd needs: one fp32 per (batch, row, query head).
- * Pure host function.
+ * Bytes of device workspace relbias_attn_bwd needs: one fp32 per (batch, row, query head),
+ * and for the input-dependent modes the curve table r_i . E[h, :, d] of every row (bf16,
+ * bias_range + 96 distances per row, rounded up to 8).  Pure host function.
  */
-size_t relbias_attn_bwd_workspace_size(int B, int S, int Hq);
+size_t relbias_attn_bwd_workspace_size(int B, int S, int Hq, int mode, int bias_range);
 
 /*
  * Backward of relbias_attn_fwd: gradients of a scalar loss given its gradient dout on o.
@@ -241,8 +242,8 @@ size_t relbias_attn_bwd_workspace_size(int B, int S, int Hq);
  *   dr          RBA_BIAS_RPROJ(_SHARED): [B, S, Hq, R] of dtype (written); else ignored.
  *   dE          RBA_BIAS_RPROJ: [Hq, R, bias_range] fp32; RBA_BIAS_RPROJ_SHARED:
  *               [R, bias_range] fp32 (written); else ignored.
- *   workspace   device scratch of at least relbias_attn_bwd_workspace_size(B, S, Hq)
- *               bytes; contents on entry are ignored.  Calls that share one workspace,
+ *   workspace   device scratch of at least relbias_attn_bwd_workspace_size(B, S, Hq, mode,
+ *               bias_range) bytes, 16-byte aligned; contents on entry are ignored.  Calls that share one workspace,
  *               dtable or dE must be ordered on one stream.
  * dtable and dE are summed with fp32 atomics, so their last bits may differ between runs;
  * dq, dk, dv and dr are deterministic.

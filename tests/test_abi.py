@@ -214,6 +214,7 @@ def _bwd(lib, **kw):
     (dict(mode=3, r=P, E=P, R=8, dr=None, dE=P), EINVAL, "dr and dE"),
     (dict(ws=None), EINVAL, "workspace"),
     (dict(wsb=4), EINVAL, "too small"),
+    (dict(ws=P + 4), EINVAL, "16-byte"),
     (dict(temp_len=1), EINVAL, "temp_len"),
     (dict(B=-1), EINVAL, "B="),
 ])
@@ -225,8 +226,12 @@ def test_bwd_rejects(lib, kw, code, needle):
 def test_bwd_empty_and_workspace(lib):
     assert _bwd(lib, B=0) == 0
     assert _bwd(lib, S=0, q=None) == 0
-    assert lib.relbias_attn_bwd_workspace_size(2, 100, 8) == 2 * 100 * 8 * 4
-    assert lib.relbias_attn_bwd_workspace_size(0, 100, 8) == 0
+    assert lib.relbias_attn_bwd_workspace_size(2, 100, 8, 0, 64) == 6400       # rowsum only
+    assert lib.relbias_attn_bwd_workspace_size(2, 100, 8, 1, 64) == 6400
+    # r.E: plus the bf16 curve table, rows of 32 + 512 + 64 distances
+    assert lib.relbias_attn_bwd_workspace_size(2, 100, 8, 2, 512) == 6400 + 1600 * 608 * 2
+    assert lib.relbias_attn_bwd_workspace_size(2, 100, 8, 3, 77) == 6400 + 1600 * 176 * 2
+    assert lib.relbias_attn_bwd_workspace_size(0, 100, 8, 2, 64) == 0
 
 
 def test_fp4_rejects(lib):

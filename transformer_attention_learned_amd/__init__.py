@@ -75,7 +75,7 @@ def load_library():
     lib.relbias_attn_bwd.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i,
                                      i, i, i, i, vp, vp, vp, i, f, i, vp, sz, vp]
     lib.relbias_attn_bwd.restype = i
-    lib.relbias_attn_bwd_workspace_size.argtypes = [i, i, i]
+    lib.relbias_attn_bwd_workspace_size.argtypes = [i, i, i, i, i]
     lib.relbias_attn_bwd_workspace_size.restype = sz
     lib.relbias_attn_kv_quantize_fp4.argtypes = [vp, vp, vp, ctypes.c_longlong, i, vp]
     lib.relbias_attn_kv_quantize_fp4.restype = i
@@ -222,7 +222,7 @@ def bwd(q, k, v, o, lse, dout, *, window=0, bias_range=0, mode="none", table=Non
     if m in (2, 3):
         out["dr"] = torch.empty_like(r)
         out["dE"] = torch.empty_like(E)
-    need = lib.relbias_attn_bwd_workspace_size(B, S, Hq)
+    need = lib.relbias_attn_bwd_workspace_size(B, S, Hq, m, int(bias_range))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

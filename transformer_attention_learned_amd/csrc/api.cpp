@@ -442,9 +442,13 @@ int relbias_attn_decode_fp4(const void* q, const void* k_codes, const void* k_sc
   return ok();
 }
 
-size_t relbias_attn_bwd_workspace_size(int B, int S, int Hq) {
+size_t relbias_attn_bwd_workspace_size(int B, int S, int Hq, int mode, int bias_range) {
   if (B <= 0 || S <= 0 || Hq <= 0) return 0;
-  return static_cast<size_t>(B) * S * Hq * sizeof(float);
+  const size_t rows = static_cast<size_t>(B) * S * Hq;
+  size_t n = (rows * sizeof(float) + 255) / 256 * 256;       // rowsum(dout * o)
+  if (is_rproj(mode) && bias_range > 0)                      // curve table, bf16
+    n += rows * static_cast<size_t>(rba::bwd_curve_pitch(bias_range)) * 2;
+  return n;
 }
 
 int relbias_attn_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
@@ -472,13 +476,13 @@ int relbias_attn_bwd(int dtype, const void* q, const void* k, const void* v, con
     return fail(RBA_EINVAL, "%s: rproj modes need aligned dr and dE", fn);
   const long long rows = static_cast<long long>(B) * S;
   if (rows * Hq * D >= (1LL << 40)) return fail(RBA_ENOTSUP, "%s: problem too large", fn);
-  if (rba::bwd_lds_bytes(D, kernel_mode(mode), bias_range) < 0)
+  if (rba::bwd_lds_bytes(D, kernel_mode(mode), bias_range, is_rproj(mode) ? R : 0) < 0)
     return fail(RBA_ENOTSUP, "%s: bias_range=%d needs more LDS than the kernels have", fn, bias_range);
-  const size_t need = relbias_attn_bwd_workspace_size(B, S, Hq);
+  const size_t need = relbias_attn_bwd_workspace_size(B, S, Hq, mode, bias_range);
   if (!workspace) return fail(RBA_EINVAL, "%s: workspace of %zu bytes required, got NULL", fn, need);
   if (workspace_bytes < need)
     return fail(RBA_EINVAL, "%s: workspace too small (%zu < %zu bytes)", fn, workspace_bytes, need);
-  if (!aligned_to(workspace, 4)) return fail(RBA_EINVAL, "%s: workspace is not 4-byte aligned", fn);
+  if (!aligned_to(workspace, 16)) return fail(RBA_EINVAL, "%s: workspace is not 16-byte aligned", fn);
   const int G = Hq / Hkv;
   const long long nq = ((S + 127) / 128) * static_cast<long long>(Hq) * B;
   if (nq > 0x7fffffffLL) return fail(RBA_ENOTSUP, "%s: grid too large", fn);
@@ -500,6 +504,10 @@ int relbias_attn_bwd(int dtype, const void* q, const void* k, const void* v, con
   a.E = E;
   a.e_hs = e_head_stride(mode, R, bias_range);
   a.dsum = static_cast<float*>(workspace);
+  a.ctab = is_rproj(mode)
+      ? reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(workspace) +
+                                    (static_cast<size_t>(B) * S * Hq * sizeof(float) + 255) / 256 * 256)
+      : nullptr;
   a.B = B;
   a.S = S;
   a.Hq = Hq;

@@ -12,15 +12,21 @@
 //     d beta = dZ at in-band pairs; dtable[h, d] = sum of d beta along the diagonal at
 //     distance d; dr[i, f] = sum_j d beta_ij E[f, i - j]; dE[f, d] = sum_i r[i, f] d beta_(i, i-d).
 //
-// Three kernels on one stream:
+// Kernels on one stream:
 //   * bwd_pre: rowsum(dO * O) per (batch, head, row) into the workspace, and zero dE / dtable.
+//   * bwd_curves (input-dependent bias only): the curve table C[b, h, i, d] = r_i . E[h, :, d]
+//     for every row and distance d < bias_range, bf16, with zero distances on both sides of a
+//     row, in the workspace.  The two main kernels read the bias from it instead of forming
+//     the curves again block by block (the forward forms them once, the backward would form
+//     them twice); for the local layer it is 2 * 32 * 4096 rows of 608 bf16, about 320 MB.
 //   * bwd_dq: one workgroup = 4 waves x 32 query rows of one head (the forward's transposed
 //     layout: S^T = K Q^T, so each lane owns one query row and its lse, rowsum and temperature
 //     are scalars).  Per 32 x 32 block it recomputes S^T and dP^T = V dO^T, forms dZ^T and
 //     accumulates dQ^T += K^T dZ^T (K^T in LDS with the key permutation of the forward's V^T).
-//     In-band blocks also write dZ into two wave-private skewed buffers, G[query][distance]
-//     and its transpose, over the block's 64-distance window; then
-//       dr^T += E G^T            (one MFMA per 16 distances; E rows read from global memory)
+//     A lane's 16 bias values sit at 4 runs of 4 consecutive distances of its own curve row:
+//     four 8-byte loads.  In-band blocks also write dZ into two wave-private skewed buffers,
+//     G[query][distance] and its transpose, over the block's 64-distance window; then
+//       dr^T += E G^T            (one MFMA per 16 distances; E staged in LDS, curve-major)
 //       dE   += r^T G  per 32 distances (A = r^T, held in registers for the wave's rows),
 //     and the dE / dtable block goes to global memory with fp32 atomics: each instruction
 //     adds 32 consecutive distances of one curve, two cache lines.  dtable uses the same MFMA
@@ -29,9 +35,9 @@
 //     query heads and the query tiles that see its keys.  Untransposed layout S = Q K^T (each
 //     lane owns one key), K and V held in registers as B operands; Q, dO and their transposes
 //     in LDS; per-row lse, rowsum and temperature from LDS.  dV^T += dO^T P and dK^T += Q^T dZ
-//     take P and dZ straight from the registers the score MFMAs left them in.  The bias is
-//     recomputed per block: table rows staged in LDS with zero padding, or the r.E curve block
-//     by MFMA (as in the forward) shared across the wave through LDS.
+//     take P and dZ straight from the registers the score MFMAs left them in.  The bias comes
+//     from the table row staged in LDS, or from the curve table (one 2-byte load per element,
+//     issued before the score MFMAs).
 
 #include <algorithm>
 
@@ -43,8 +49,6 @@ namespace rba {
 namespace {
 
 constexpr int BN = 64;        // keys per tile (dq kernel), query rows per tile (dk/dv kernel)
-constexpr int CST = 68;       // row stride (floats) of the curve scratch: 16-byte rows, and the
-                              // diagonal reads (stride CST + 1 = 5 mod 64 banks) do not collide
 constexpr int PADT = 64;      // zero distances staged on each side of a table row
 constexpr int PADE = 64;      // zero distances staged on each side of E
 constexpr int GST = 64 + 8;   // G row stride (bf16): row = query, 64 distances
@@ -126,106 +130,57 @@ __device__ __forceinline__ void store_rows(const u32x4 (&pre)[NIT][4], uint16_t*
   }
 }
 
-// A 32x32 MFMA output column into a curve-scratch row: rows 8 g + 4 lh + 0..3 are
-// consecutive, one 16-byte store each (dst = row start + 4 lh).
-__device__ __forceinline__ void store_curve(const f32x16& v, float* dst) {
-#pragma unroll
-  for (int g = 0; g < 4; ++g)
-    *reinterpret_cast<f32x4*>(dst + 8 * g) = f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
-}
+// Row of the curve table: CPAD_L zero distances, the bias_range curve values, CPAD_R zeros.
+constexpr int CPAD_L = 32;
+constexpr int CPAD_R = 64;
 
-// The r.E curve block of 32 query rows q0.. over the 64 distances base .. base + 63, written
-// to a wave-private scratch cs[query][distance - base] in log2 units: two MFMAs (32 distances
-// each) with A = E^T (row = distance, E split into bf16 high and low parts carried by the two
-// lane halves) and B = r of the rows (both halves), as in the forward.
-template <int D>
-__device__ __forceinline__ void curve_block(const BwdArgs& a, const float* Eh, const bf16x8 (&rf)[2],
-                                            int base, float* cs, int ln, int lh) {
-  const int nfc = (a.R + 7) / 8;
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int dl = base + 32 * half + ln;
-    f32x16 cacc = zero16();
-    for (int fc = 0; fc < nfc; ++fc) {
-      uint32_t w[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        float e2[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int f = 8 * fc + 2 * jj + u;
-          float e = 0.f;
-          if (f < a.R && dl >= 0 && dl < a.bias_range) e = Eh[static_cast<size_t>(f) * a.bias_range + dl] * kLog2e;
-          const float hi = bf16_to_f32(f32_to_bf16(e));
-          e2[u] = lh ? (e - hi) : e;
-        }
-        w[jj] = pack_bf16x2(e2[0], e2[1]);
-      }
-      cacc = mfma32(as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}), rf[fc], cacc);
+// ---- curve table: C[b, h, i, d] = sum_f r[b, i, h, f] E[h, f, d] ---------------------------------
+// One workgroup per (batch, head, 64 rows): E[h] staged in LDS (fp32) in the table's own column
+// layout (zero outside [0, bias_range)), and the rows' r; each item is 8 consecutive columns of
+// one row: two 16-byte LDS reads per curve, one 16-byte store.
+__global__ __launch_bounds__(256) void bwd_curves_kernel(BwdArgs a, int pitch) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  float* es = reinterpret_cast<float*>(smem);                  // [R][pitch]
+  float* rsh = es + a.R * pitch;                               // [64][R]
+  const int Rb = a.bias_range;
+  const int ntile = (a.S + 63) / 64;
+  const int tile = blockIdx.x % ntile;
+  const int bh = blockIdx.x / ntile;                           // b * Hq + h
+  const int h = bh % a.Hq;
+  const int b = bh / a.Hq;
+  const int i0 = tile * 64;
+  const float* Eh = a.E + static_cast<size_t>(h) * a.e_hs;
+  for (int x = threadIdx.x; x < a.R * pitch; x += 256) {
+    const int f = x / pitch;
+    const int d = x - f * pitch - CPAD_L;
+    es[x] = (d >= 0 && d < Rb) ? Eh[static_cast<size_t>(f) * Rb + d] : 0.f;
+  }
+  for (int x = threadIdx.x; x < 64 * a.R; x += 256) {
+    const int rr = x / a.R;
+    const int f = x - rr * a.R;
+    const int i = i0 + rr;
+    rsh[x] = i < a.S ? bf16_to_f32(a.r[((static_cast<size_t>(b) * a.S + i) * a.Hq + h) * a.R + f]) : 0.f;
+  }
+  __syncthreads();
+  const int chunks = pitch / 8;
+  const int rows = min(64, a.S - i0);
+  uint16_t* out = a.ctab + (static_cast<size_t>(bh) * a.S + i0) * pitch;
+  for (int it = threadIdx.x; it < rows * chunks; it += 256) {
+    const int rr = it / chunks;
+    const int t0 = 8 * (it - rr * chunks);
+    f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < a.R; ++f) {
+      const float rv = rsh[rr * a.R + f];
+      const f32x4 e0 = *reinterpret_cast<const f32x4*>(es + f * pitch + t0);
+      const f32x4 e1 = *reinterpret_cast<const f32x4*>(es + f * pitch + t0 + 4);
+      v0 += rv * e0;
+      v1 += rv * e1;
     }
-    store_curve(cacc, cs + ln * CST + 32 * half + 4 * lh);
+    st16(out + static_cast<size_t>(rr) * pitch + t0,
+         u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v1[0], v1[1]),
+               pack_bf16x2(v1[2], v1[3])});
   }
 }
-
-// r of one query row (lane column) as the B operand of the curve MFMA: both halves carry
-// r[row][8 fc + j].
-__device__ __forceinline__ void load_rf(const BwdArgs& a, int b, int row, int h, bf16x8 (&rf)[2]) {
-  const uint16_t* rp = a.r + ((static_cast<size_t>(b) * a.S + row) * a.Hq + h) * a.R;
-#pragma unroll
-  for (int fc = 0; fc < 2; ++fc) {
-    uint32_t w[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int f0 = 8 * fc + 2 * jj;
-      const uint32_t lo = (row < a.S && f0 < a.R) ? rp[f0] : 0u;
-      const uint32_t hi = (row < a.S && f0 + 1 < a.R) ? rp[f0 + 1] : 0u;
-      w[jj] = lo | (hi << 16);
-    }
-    rf[fc] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
-  }
-}
-
-// E staged in LDS for the curve MFMA: row PADE + distance holds, per chunk of 8 curves, the
-// bf16 high parts and then the low parts of E * log2(e) (the A operands of the two lane
-// halves), zero outside [0, bias_range) and for curves >= R.  Consecutive threads read
-// consecutive distances of one curve.
-__device__ __forceinline__ void stage_et(const BwdArgs& a, const float* Eh, uint16_t* et, int nfc,
-                                         int t, int nt) {
-  const int rows = a.bias_range + 2 * PADE;
-  const int n = rows * 8 * nfc;
-  for (int x = t; x < n; x += nt) {
-    const int row = x % rows;
-    const int f = x / rows;                 // 8 fc + j
-    const int d = row - PADE;
-    float e = 0.f;
-    if (f < a.R && d >= 0 && d < a.bias_range) e = Eh[static_cast<size_t>(f) * a.bias_range + d] * kLog2e;
-    const uint16_t hi = f32_to_bf16(e);
-    const uint16_t lo = f32_to_bf16(e - bf16_to_f32(hi));
-    uint16_t* dst = et + row * 16 * nfc + 16 * (f >> 3) + (f & 7);
-    dst[0] = hi;
-    dst[8] = lo;
-  }
-}
-
-// The curve block of the forward from the staged E: cs[query][distance - base], log2 units.
-__device__ __forceinline__ void curve_block_lds(const uint16_t* et, int nfc, const bf16x8 (&rf)[2],
-                                                int base, float* cs, int ln, int lh) {
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const uint16_t* er = et + (PADE + base + 32 * half + ln) * 16 * nfc + 8 * lh;
-    f32x16 cacc = zero16();
-    for (int fc = 0; fc < nfc; ++fc) cacc = mfma32(as_bf16x8(ld16(er + 16 * fc)), rf[fc], cacc);
-    store_curve(cacc, cs + ln * CST + 32 * half + 4 * lh);
-  }
-}
-
-// Bytes of the staged E for the curve MFMA.
-__host__ __device__ inline int et_bytes(int bias_range, int R) {
-  return (bias_range + 2 * PADE) * 16 * ((R + 7) / 8) * 2;
-}
-// Row stride (bf16) of E staged curve-major for the dr MFMA, and its bytes.
-__host__ __device__ inline int ef_stride(int bias_range) { return (bias_range + 2 * PADE + 7) & ~7; }
-__host__ __device__ inline int ef_bytes(int bias_range, int R) { return R * ef_stride(bias_range) * 2; }
 
 // ---- pre pass: rowsum(dO * O) and zeroed parameter gradients ----------------------------------
 template <int D>
@@ -258,28 +213,29 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, float* zero_ptr
 }
 
 // ---- dq (+ dr, dE, dtable): query-parallel -----------------------------------------------------
-// LDS: K, V, K^T tiles; per wave the curve scratch (r.E) and the skewed dZ buffers; the table
-// row (table mode); E staged for the curve and dr MFMAs when ESTAGE.
+// LDS: K, V, K^T tiles; per wave the skewed dZ buffers; the table row (table mode) or E staged
+// curve-major for the dr MFMA (r.E).
 template <int D, int MODE>
 struct DqLayout {
   static constexpr int KST = D + 8;
   static constexpr int TST = BN + 8;
   static constexpr int TILE_BYTES = (2 * BN * KST + D * TST) * 2;
-  static constexpr int CS_BYTES = (MODE == 2) ? 32 * CST * 4 : 0;
   static constexpr int G_BYTES = (MODE == 2) ? 32 * GST * 2 : 0;
   static constexpr int GT_BYTES = (MODE != 0) ? 64 * GTS * 2 : 0;
-  static constexpr int WAVE_BYTES = CS_BYTES + G_BYTES + GT_BYTES;
+  static constexpr int WAVE_BYTES = G_BYTES + GT_BYTES;
   static constexpr int FIXED = TILE_BYTES + DQ_WAVES * WAVE_BYTES;
-  static int bytes(int Rb, int R, bool estage) {
+  static int bytes(int Rb, int R) {
     int n = FIXED;
     if (MODE == 1) n += (Rb + 2 * PADT) * 4;
-    if (MODE == 2 && estage) n += et_bytes(Rb, R) + ef_bytes(Rb, R);
+    if (MODE == 2) n += R * ef_stride(Rb) * 2;
     return n;
   }
+  // Row stride (bf16) of E staged curve-major for the dr MFMA.
+  __host__ __device__ static int ef_stride(int Rb) { return (Rb + 2 * PADE + 7) & ~7; }
 };
 
-template <int D, int MODE, bool ESTAGE>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles, int longest_first) {
+template <int D, int MODE>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles, int longest_first, int pitch) {
   using L = DqLayout<D, MODE>;
   constexpr int KST = L::KST;
   constexpr int TST = L::TST;
@@ -297,12 +253,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
   const int lh = lane >> 5;
 
   unsigned char* wsp = smem + L::TILE_BYTES + wave * L::WAVE_BYTES;
-  float* cs = reinterpret_cast<float*>(wsp);
-  uint16_t* Gs = reinterpret_cast<uint16_t*>(wsp + L::CS_BYTES);
-  uint16_t* GTs = reinterpret_cast<uint16_t*>(wsp + L::CS_BYTES + L::G_BYTES);
+  uint16_t* Gs = reinterpret_cast<uint16_t*>(wsp);
+  uint16_t* GTs = reinterpret_cast<uint16_t*>(wsp + L::G_BYTES);
   float* tabs = reinterpret_cast<float*>(smem + L::FIXED);                 // table mode
-  uint16_t* et = reinterpret_cast<uint16_t*>(smem + L::FIXED);             // r.E, ESTAGE
-  uint16_t* ef = et + et_bytes(a.bias_range, a.R) / 2;
+  uint16_t* ef = reinterpret_cast<uint16_t*>(smem + L::FIXED);             // r.E
 
   const int per_q = a.Hq * a.B;
   int qt = blockIdx.x / per_q;
@@ -320,7 +274,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
   const int hkv = h / a.G;
   const int row = i0 + ln;
   const bool row_ok = row < S;
-  const int nfc = (a.R + 7) / 8;
 
   const int wg_last = min(S, wg_i0 + 32 * DQ_WAVES) - 1;
   const int kmin = W ? max(0, wg_i0 - W + 1) : 0;
@@ -333,6 +286,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
   const uint16_t* vbase = a.v + static_cast<size_t>(b) * S * kv_row + static_cast<size_t>(hkv) * D;
   const size_t qoff = (static_cast<size_t>(b) * S + (row_ok ? row : 0)) * q_row + static_cast<size_t>(h) * D;
   const float* Eh = (MODE == 2) ? a.E + static_cast<size_t>(h) * a.e_hs : nullptr;
+  // this lane's curve row (rows past the end read the last row; their P is zero)
+  const uint16_t* crow = (MODE == 2)
+      ? a.ctab + ((static_cast<size_t>(b) * a.Hq + h) * S + (row_ok ? row : S - 1)) * pitch + CPAD_L
+      : nullptr;
 
   // bias parameters of the head in LDS (made visible by the first barrier of the tile loop)
   if (MODE == 1) {
@@ -342,9 +299,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
       tabs[x] = (d >= 0 && d < Rb) ? tp[d] * kLog2e : 0.f;
     }
   }
-  if (MODE == 2 && ESTAGE) {
-    stage_et(a, Eh, et, nfc, tid, 256);
-    const int efs = ef_stride(Rb);
+  const int efs = L::ef_stride(Rb);
+  if (MODE == 2) {
     for (int x = tid; x < a.R * efs; x += 256) {
       const int f = x / efs;
       const int d = x - f * efs - PADE;
@@ -370,10 +326,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
   const float dsum = row_ok ? a.dsum[lrow] : 0.f;
   const float tq = temp_factor(visible_keys(row, W), a.temp_len, a.temp_inv_log2);
   const float cq = a.c_qk * tq;
+  const float cb = kLog2e * tq;
 
-  bf16x8 rf[2];        // r of this row (curve MFMA, B operand)
   bf16x8 rA[2];        // r^T of the wave's rows (dE MFMA, A operand): row f = ln, rows 16kk + 8lh + e
-  if (MODE == 2) load_rf(a, b, row, h, rf);
   if (MODE != 0) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -448,6 +403,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
       bool on = (c + 31 >= 0) && (kb0 < S);
       if (W) on = on && (c - 31 < W);
       if (!on) continue;
+      const bool inband = (MODE != 0) && (c - 31 < Rb);
+
+      // r.E bias: distances c + ln - (8 g + 4 lh + u) of the lane's curve row, four runs of 4
+      // (8-byte loads; the distances lie in [-31, Rb + 61], inside the padded row)
+      u32x2 braw[4];
+      if (MODE == 2 && inband) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          u32x2 x;
+          __builtin_memcpy(&x, crow + c + ln - 8 * g4 - 4 * lh - 3, 8);
+          braw[g4] = x;
+        }
+      }
 
       // operands read one step ahead of the MFMAs that use them
       f32x16 sacc = zero16(), pacc = zero16();
@@ -469,7 +437,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
       // log2-domain logits tau * (scale log2(e) q.k + log2(e) beta)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] *= cq;
-      const bool inband = (MODE != 0) && (c - 31 < Rb);
       if (MODE == 1 && inband) {
         // distances c + ln - m lie in [-31, Rb + 62]: inside the zero-padded row
         const float* tb = tabs + PADT + c + ln;
@@ -477,12 +444,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
         for (int i = 0; i < 16; ++i) sacc[i] = fmaf(tb[-out_row(i, lh)], tq, sacc[i]);
       }
       if (MODE == 2 && inband) {
-        if (ESTAGE) curve_block_lds(et, nfc, rf, c - 31, cs, ln, lh);
-        else curve_block<D>(a, Eh, rf, c - 31, cs, ln, lh);
-        wave_sync_lds();
+        // element u of run g4 is distance (start + 3 - u): the high half of word 1 for u = 0
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = fmaf(cs[ln * CST + (ln - out_row(i, lh) + 31)], tq, sacc[i]);
-        wave_sync_lds();
+        for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint32_t w = braw[g4][(3 - u) >> 1];
+            const float beta = __uint_as_float(((3 - u) & 1) ? (w & 0xffff0000u) : (w << 16));
+            sacc[4 * g4 + u] = fmaf(beta, cb, sacc[4 * g4 + u]);
+          }
       }
       // P and dS = P * (dP - rowsum); the temperature factor of dZ = tau dS is applied to the
       // accumulated dq and to the bias-gradient inputs
@@ -556,31 +526,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
         }
         if (MODE == 2) {
           // dr^T[f][query] += sum_dist E[f][dist] G^T[dist][query], 16 distances per MFMA
-          const int efs = ef_stride(Rb);
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
             const int d0 = c - 32 + 16 * kk + 8 * lh;
-            bf16x8 ea;
-            if (ESTAGE) {
-              u32x4 x = {0u, 0u, 0u, 0u};
-              if (ln < a.R) x = ld16(ef + ln * efs + PADE + d0);
-              ea = as_bf16x8(x);
-            } else {
-              uint32_t w[4];
-#pragma unroll
-              for (int jj = 0; jj < 4; ++jj) {
-                float e2[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                  const int dd = d0 + 2 * jj + u;
-                  e2[u] = (ln < a.R && dd >= 0 && dd < Rb) ? Eh[static_cast<size_t>(ln) * Rb + dd] : 0.f;
-                }
-                w[jj] = pack_bf16x2(e2[0], e2[1]);
-              }
-              ea = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
-            }
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (ln < a.R) x = ld16(ef + ln * efs + PADE + d0);
             const bf16x8 gf = as_bf16x8(ld16(Gs + ln * GST + 16 * kk + 8 * lh));
-            dracc = mfma32(ea, gf, dracc);
+            dracc = mfma32(as_bf16x8(x), gf, dracc);
           }
         }
         wave_sync_lds();
@@ -613,19 +565,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
 // ---- dk, dv: key-parallel ------------------------------------------------------------------------
 template <int D>
 struct DkvLayout {
-  static constexpr int TILES = (2 * BN * (D + 8) + 2 * D * (BN + 8)) * 2 + 4 * BN * 4 + BN * 16 * 2;
-  static constexpr int CS_BYTES = DKV_WAVES * 32 * CST * 4;
-  // bias parameters after the tiles: table row, or curve scratch (+ staged E)
-  static int bytes(int mode, int Rb, int R, bool estage) {
-    int n = TILES;
-    if (mode == 1) n += (Rb + 2 * PADT) * 4;
-    if (mode == 2) n += CS_BYTES + (estage ? et_bytes(Rb, R) : 0);
-    return n;
-  }
+  static constexpr int TILES = (2 * BN * (D + 8) + 2 * D * (BN + 8)) * 2 + 4 * BN * 4;
+  static int bytes(int mode, int Rb) { return TILES + (mode == 1 ? (Rb + 2 * PADT) * 4 : 0); }
 };
 
-template <int D, int MODE, bool ESTAGE>
-__global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) {
+template <int D, int MODE>
+__global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a, int pitch) {
   using L = DkvLayout<D>;
   constexpr int QST = D + 8;
   constexpr int TST = BN + 8;
@@ -638,17 +583,13 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   uint16_t* Qt = dOs + BN * QST;
   uint16_t* dOt = Qt + D * TST;
   float* rowp = reinterpret_cast<float*>(dOt + D * TST);   // [4][BN]: lse2, rowsum, c_qk*tau, tau
-  uint16_t* rrow = reinterpret_cast<uint16_t*>(rowp + 4 * BN);   // [BN][16]: r of the tile's rows
   float* tabs = reinterpret_cast<float*>(smem + L::TILES);  // table mode: [PADT + Rb + PADT]
-  float* cs_all = reinterpret_cast<float*>(smem + L::TILES);
-  uint16_t* et = reinterpret_cast<uint16_t*>(smem + L::TILES + L::CS_BYTES);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31;
   const int lh = lane >> 5;
-  float* cs = cs_all + wave * 32 * CST;
 
   const int per_k = a.Hkv * a.B;
   const int kt = blockIdx.x / per_k;
@@ -664,7 +605,6 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   const bool wave_live = j0w < S;
   const int key = j0w + ln;
   const bool key_ok = key < S;
-  const int nfc = (a.R + 7) / 8;
 
   const size_t q_row = static_cast<size_t>(a.Hq) * D;
   const size_t kv_row = static_cast<size_t>(a.Hkv) * D;
@@ -701,7 +641,6 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   constexpr int QIT = (row_items<D>() + NT - 1) / NT;
   u32x4 qpre[QIT][4], dpre[QIT][4];
   float lpre = 0.f, spre = 0.f, tpre = 1.f;
-  u32x4 rpre[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
   auto load_step = [&](int st) {
     const int h = hkv * a.G + st / ntiles;
     const int qt0 = (t_begin + st % ntiles) * BN;
@@ -716,18 +655,6 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
       lpre = ok ? a.lse[lrow] * kLog2e : INFINITY;
       spre = ok ? a.dsum[lrow] : 0.f;
       tpre = temp_factor(visible_keys(rr, W), a.temp_len, a.temp_inv_log2);
-      if (MODE == 2) {   // r of the row, zero past R (16 curves at most)
-        const uint16_t* rp = a.r + ((static_cast<size_t>(b) * S + (ok ? rr : 0)) * a.Hq + h) * a.R;
-        uint32_t w[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const uint32_t lo = (ok && 2 * jj < a.R) ? rp[2 * jj] : 0u;
-          const uint32_t hi = (ok && 2 * jj + 1 < a.R) ? rp[2 * jj + 1] : 0u;
-          w[jj] = lo | (hi << 16);
-        }
-        rpre[0] = u32x4{w[0], w[1], w[2], w[3]};
-        rpre[1] = u32x4{w[4], w[5], w[6], w[7]};
-      }
     }
   };
   if (nsteps > 0) load_step(0);
@@ -736,7 +663,6 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
     const int hh = st / ntiles;
     const int h = hkv * a.G + hh;
     const int qt0 = (t_begin + st % ntiles) * BN;
-    const float* Eh = (MODE == 2) ? a.E + static_cast<size_t>(h) * a.e_hs : nullptr;
     __syncthreads();   // the previous step's LDS reads are complete
     store_rows<D, QIT>(qpre, Qs, Qt, tid, NT);
     store_rows<D, QIT>(dpre, dOs, dOt, tid, NT);
@@ -745,24 +671,19 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
       rowp[BN + tid] = spre;
       rowp[2 * BN + tid] = a.c_qk * tpre;
       rowp[3 * BN + tid] = tpre;
-      if (MODE == 2) {
-        st16(rrow + 16 * tid, rpre[0]);
-        st16(rrow + 16 * tid + 8, rpre[1]);
-      }
     }
-    if (st % ntiles == 0) {   // a new head: its bias parameters
-      if (MODE == 1) {
-        const float* tp = a.table + static_cast<size_t>(h) * Rb;
-        for (int x = tid; x < Rb + 2 * PADT; x += NT) {
-          const int d = x - PADT;
-          tabs[x] = (d >= 0 && d < Rb) ? tp[d] * kLog2e : 0.f;
-        }
+    if (MODE == 1 && st % ntiles == 0) {   // a new head: its table row, zero-padded
+      const float* tp = a.table + static_cast<size_t>(h) * Rb;
+      for (int x = tid; x < Rb + 2 * PADT; x += NT) {
+        const int d = x - PADT;
+        tabs[x] = (d >= 0 && d < Rb) ? tp[d] * kLog2e : 0.f;
       }
-      if (MODE == 2 && ESTAGE && (hh == 0 || a.e_hs != 0)) stage_et(a, Eh, et, nfc, tid, NT);
     }
     __syncthreads();
     if (st + 1 < nsteps) load_step(st + 1);
     if (!wave_live) continue;
+    // curve rows of this step's queries (rows past the end read the last row; P is zero there)
+    const uint16_t* cplane = (MODE == 2) ? a.ctab + (static_cast<size_t>(b) * a.Hq + h) * S * pitch + CPAD_L : nullptr;
 
 #pragma unroll 1
     for (int qb = 0; qb < 2; ++qb) {
@@ -771,6 +692,19 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
       bool on = (c + 31 >= 0) && (i0b < S);
       if (W) on = on && (c - 31 < W);
       if (!on) continue;
+      const bool inband = (MODE != 0) && (c - 31 < Rb);
+
+      // r.E bias of element (query m, key ln): curve row i0b + m at distance c + m - ln, in
+      // [-31, Rb + 61]; issued before the score MFMAs
+      uint16_t braw[16];
+      if (MODE == 2 && inband) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = out_row(i, lh);
+          const int rr = min(i0b + m, S - 1);
+          braw[i] = cplane[static_cast<size_t>(rr) * pitch + c + m - ln];
+        }
+      }
 
       // operands read one step ahead of the MFMAs that use them
       f32x16 sacc = zero16(), pacc = zero16();
@@ -790,7 +724,6 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
         da = dn;
       }
       // bias (log2 units) per element, before the temperature
-      const bool inband = (MODE != 0) && (c - 31 < Rb);
       float bias[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) bias[i] = 0.f;
@@ -801,17 +734,8 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
         for (int i = 0; i < 16; ++i) bias[i] = tb[out_row(i, lh)];
       }
       if (MODE == 2 && inband) {
-        const bf16x8 rf[2] = {as_bf16x8(ld16(rrow + 16 * (32 * qb + ln))),
-                              as_bf16x8(ld16(rrow + 16 * (32 * qb + ln) + 8))};
-        if (ESTAGE) curve_block_lds(et, nfc, rf, c - 31, cs, ln, lh);
-        else curve_block<D>(a, Eh, rf, c - 31, cs, ln, lh);
-        wave_sync_lds();
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = out_row(i, lh);
-          bias[i] = cs[m * CST + (m - ln + 31)];
-        }
-        wave_sync_lds();
+        for (int i = 0; i < 16; ++i) bias[i] = bf16_to_f32(braw[i]) * kLog2e;
       }
       // P into sacc, dZ = tau * P * (dP - rowsum) into pacc (in place); per row: lse (log2
       // units), rowsum, c_qk * tau and tau (tau = 1 without a temperature).  Interior and
@@ -912,31 +836,6 @@ hipError_t allow_lds(K* kernel, int bytes) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-template <int D, int MODE, bool ESTAGE>
-hipError_t launch_dq(const BwdArgs& a, hipStream_t s) {
-  const int n_qtiles = (a.S + 32 * DQ_WAVES - 1) / (32 * DQ_WAVES);
-  const int longest_first = (a.window == 0 || a.window > 32 * DQ_WAVES) ? 1 : 0;
-  const int lds = DqLayout<D, MODE>::bytes(a.bias_range, a.R, ESTAGE);
-  hipError_t e = allow_lds(&bwd_dq_kernel<D, MODE, ESTAGE>, lds);
-  if (e != hipSuccess) return e;
-  const long long nq = static_cast<long long>(n_qtiles) * a.Hq * a.B;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, MODE, ESTAGE>), dim3(static_cast<unsigned>(nq)), dim3(64 * DQ_WAVES), lds, s,
-                     a, n_qtiles, longest_first);
-  return hipGetLastError();
-}
-
-template <int D, int MODE, bool ESTAGE>
-hipError_t launch_dkdv(const BwdArgs& a, hipStream_t s) {
-  const int lds = DkvLayout<D>::bytes(MODE, a.bias_range, a.R, ESTAGE);
-  hipError_t e = allow_lds(&bwd_dkdv_kernel<D, MODE, ESTAGE>, lds);
-  if (e != hipSuccess) return e;
-  const int n_ktiles = (a.S + 32 * DKV_WAVES - 1) / (32 * DKV_WAVES);
-  const long long nk = static_cast<long long>(n_ktiles) * a.Hkv * a.B;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, MODE, ESTAGE>), dim3(static_cast<unsigned>(nk)), dim3(64 * DKV_WAVES), lds, s,
-                     a);
-  return hipGetLastError();
-}
-
 template <int D, int MODE>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   // pre pass
@@ -955,12 +854,36 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(pre_grid), dim3(256), 0, s, a, zero_ptr, n_zero);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // r.E: E staged in LDS where it fits beside the tiles
-  const bool dq_stage = MODE == 2 && DqLayout<D, MODE>::bytes(a.bias_range, a.R, true) <= kMaxLds;
-  const bool kv_stage = MODE == 2 && DkvLayout<D>::bytes(MODE, a.bias_range, a.R, true) <= kMaxLds;
-  e = dq_stage ? launch_dq<D, MODE, true>(a, s) : launch_dq<D, MODE, false>(a, s);
+  const int pitch = bwd_curve_pitch(a.bias_range);
+  if (MODE == 2) {
+    const int lds = (a.R * pitch + 64 * a.R) * 4;
+    e = allow_lds(&bwd_curves_kernel, lds);
+    if (e != hipSuccess) return e;
+    const long long ng = static_cast<long long>(a.B) * a.Hq * ((a.S + 63) / 64);
+    hipLaunchKernelGGL(bwd_curves_kernel, dim3(static_cast<unsigned>(ng)), dim3(256), lds, s, a, pitch);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // dq (+ bias-parameter gradients)
+  const int n_qtiles = (a.S + 32 * DQ_WAVES - 1) / (32 * DQ_WAVES);
+  const int longest_first = (a.window == 0 || a.window > 32 * DQ_WAVES) ? 1 : 0;
+  const long long nq = static_cast<long long>(n_qtiles) * a.Hq * a.B;
+  const int dq_lds = DqLayout<D, MODE>::bytes(a.bias_range, a.R);
+  e = allow_lds(&bwd_dq_kernel<D, MODE>, dq_lds);
   if (e != hipSuccess) return e;
-  return kv_stage ? launch_dkdv<D, MODE, true>(a, s) : launch_dkdv<D, MODE, false>(a, s);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, MODE>), dim3(static_cast<unsigned>(nq)), dim3(64 * DQ_WAVES), dq_lds, s,
+                     a, n_qtiles, longest_first, pitch);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // dk, dv
+  const int kv_lds = DkvLayout<D>::bytes(MODE, a.bias_range);
+  e = allow_lds(&bwd_dkdv_kernel<D, MODE>, kv_lds);
+  if (e != hipSuccess) return e;
+  const int n_ktiles = (a.S + 32 * DKV_WAVES - 1) / (32 * DKV_WAVES);
+  const long long nk = static_cast<long long>(n_ktiles) * a.Hkv * a.B;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, MODE>), dim3(static_cast<unsigned>(nk)), dim3(64 * DKV_WAVES), kv_lds, s,
+                     a, pitch);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -974,20 +897,22 @@ hipError_t launch_bwd_mode(const BwdArgs& a, int mode, hipStream_t s) {
 
 }  // namespace
 
-// LDS the backward kernels need for this shape (the larger of the two, E read from global
-// memory), or -1 past 160 KB.
-int bwd_lds_bytes(int D, int mode, int bias_range) {
+int bwd_curve_pitch(int bias_range) { return (CPAD_L + bias_range + CPAD_R + 7) & ~7; }
+
+// LDS the backward kernels need for this shape (the largest of the three), or -1 past 160 KB.
+int bwd_lds_bytes(int D, int mode, int bias_range, int R) {
   int dq = 0, kv = 0;
   if (D == 128) {
-    dq = mode == 0 ? DqLayout<128, 0>::bytes(bias_range, 1, false)
-                   : (mode == 1 ? DqLayout<128, 1>::bytes(bias_range, 1, false) : DqLayout<128, 2>::bytes(bias_range, 1, false));
-    kv = DkvLayout<128>::bytes(mode, bias_range, 1, false);
+    dq = mode == 0 ? DqLayout<128, 0>::bytes(bias_range, R)
+                   : (mode == 1 ? DqLayout<128, 1>::bytes(bias_range, R) : DqLayout<128, 2>::bytes(bias_range, R));
+    kv = DkvLayout<128>::bytes(mode, bias_range);
   } else {
-    dq = mode == 0 ? DqLayout<64, 0>::bytes(bias_range, 1, false)
-                   : (mode == 1 ? DqLayout<64, 1>::bytes(bias_range, 1, false) : DqLayout<64, 2>::bytes(bias_range, 1, false));
-    kv = DkvLayout<64>::bytes(mode, bias_range, 1, false);
+    dq = mode == 0 ? DqLayout<64, 0>::bytes(bias_range, R)
+                   : (mode == 1 ? DqLayout<64, 1>::bytes(bias_range, R) : DqLayout<64, 2>::bytes(bias_range, R));
+    kv = DkvLayout<64>::bytes(mode, bias_range);
   }
-  const int m = std::max(dq, kv);
+  const int cv = mode == 2 ? (R * bwd_curve_pitch(bias_range) + 64 * R) * 4 : 0;
+  const int m = std::max(std::max(dq, kv), cv);
   return m > kMaxLds ? -1 : m;
 }
 

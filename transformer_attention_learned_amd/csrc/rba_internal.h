@@ -128,6 +128,7 @@ struct BwdArgs {
   const float* E;
   long long e_hs;       // head stride of E and dE in floats (0: one shared bank)
   float* dsum;          // workspace [B, Hq, S]: rowsum(dout * o)
+  uint16_t* ctab;       // workspace (r.E): curve table [B, Hq, S, bwd_curve_pitch(bias_range)]
   int B, S, Hq, Hkv, G;
   int window, bias_range, R;
   float c_qk;           // scale * log2(e)
@@ -138,8 +139,10 @@ struct BwdArgs {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int D, int mode, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int D, int mode, hipStream_t s);
-// LDS bytes of the larger backward kernel for this shape, or -1 when it does not fit.
-int bwd_lds_bytes(int D, int mode, int bias_range);
+// LDS bytes of the largest backward kernel for this shape, or -1 when it does not fit; the
+// row pitch (bf16) of the backward's curve table.
+int bwd_lds_bytes(int D, int mode, int bias_range, int R);
+int bwd_curve_pitch(int bias_range);
 // Fast prefill path (head_dim 128, Hq/Hkv a multiple of 4): LDS bytes it needs, or -1
 // when the shape is outside its domain; and its launcher.
 int fwd_fast_lds_bytes(int D, int G, int mode, int bias_range, int R, float scale);
