@@ -135,6 +135,11 @@ SWEEP = [
     dict(S=333, mode="table", bias_range=100, temp_len=2),
     dict(S=1100, mode="rproj_shared", R=16, bias_range=1024, logit_scale="inv_d", temp_len=256),
     dict(S=260, D=64, temp_len=50), dict(S=190, Hq=6, Hkv=2, temp_len=20, mode="table"),
+    # windows inside the bias range with more work items (batch x head group x 64-row tile)
+    # than CUs: the kernel walks runs of items per workgroup, runs cross head groups and batch
+    # entries, tails are ragged
+    dict(S=1000, B=3, Hq=32, Hkv=8, window=300, bias_range=512),
+    dict(S=700, B=4, Hq=32, Hkv=8, R=16, window=512, bias_range=512, temp_len=300),
 ]
 
 

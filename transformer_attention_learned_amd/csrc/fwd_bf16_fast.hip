@@ -82,9 +82,13 @@ __device__ __forceinline__ void wave_sync_lds() {
 // MODE 0 none, 1 table, 2 r.E; EF = features per distance in the staged E (8 or 16);
 // RING: one curve buffer per query block, shared by consecutive key blocks.
 // ESTAGE: E is staged in LDS (bf16); otherwise the curve MFMA reads fp32 E from global memory.
-template <int MODE, int EF, bool RING, int QB, bool ESTAGE>
+// ALLBAND: every visible key is inside the bias range (window <= range, local layers), so every
+// step carries the bias; with staged E its curves are then formed a step ahead, without branches.
+template <int MODE, int EF, bool RING, int QB, bool ESTAGE, bool ALLBAND>
 __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bias_off, int ring_off) {
   constexpr int NT = 512 / QB;      // threads per workgroup
+  // staged-E curves formed one step ahead of their use
+  constexpr bool PIPE = MODE == 2 && ESTAGE && ALLBAND;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int tid = threadIdx.x;
@@ -130,7 +134,9 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
   // ---- K/V staging: 64 keys x 128 dims of K and of V per tile.  K: 1024 chunks of 16 B,
   // row-major; V: 256 items of 4 keys x 8 dims, transposed.  With 256 threads each thread
   // takes 4 K chunks and one V item; with 512 threads half take K, half take V.
-  u32x4 kreg[4], vreg[4];
+  // staging registers: with 512 threads a thread stages either K or V, so both share one set
+  constexpr int VR0 = (NT == 512) ? 0 : 4;
+  u32x4 sreg[VR0 + 4];
   const bool v_thread = (NT == 256) || (wave >= 4);
   const bool k_thread = (NT == 256) || (wave < 4);
   const int vt_id = tid & 255;
@@ -149,18 +155,15 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
   auto load_tile = [&](int tk0) {
     if (k_thread) {
 #pragma unroll
-      for (int it = 0; it < 4; ++it) kreg[it] = buf_ld16(rows_rsrc(kbase, tk0 + 16 * it), k_voff);
+      for (int it = 0; it < 4; ++it) sreg[it] = buf_ld16(rows_rsrc(kbase, tk0 + 16 * it), k_voff);
     }
     if (v_thread) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) vreg[s] = buf_ld16(rows_rsrc(vbase, tk0 + s), v_voff);
+      for (int s = 0; s < 4; ++s) sreg[VR0 + s] = buf_ld16(rows_rsrc(vbase, tk0 + s), v_voff);
     }
     if (QB == 2) {   // 1 wave per SIMD: park the staged tile in the accumulation registers
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        asm volatile("" : "+a"(kreg[it]));
-        asm volatile("" : "+a"(vreg[it]));
-      }
+      for (int it = 0; it < VR0 + 4; ++it) asm volatile("" : "+a"(sreg[it]));
     }
   };
   auto store_tile = [&](int buf) {
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
     uint16_t* Vt = reinterpret_cast<uint16_t*>(smem + buf * BUF_BYTES + KS_BYTES);
     if (k_thread) {
 #pragma unroll
-      for (int it = 0; it < 4; ++it) st16(Ks + (it * 16 + (vt_id >> 4)) * KST + 8 * (vt_id & 15), kreg[it]);
+      for (int it = 0; it < 4; ++it) st16(Ks + (it * 16 + (vt_id >> 4)) * KST + 8 * (vt_id & 15), sreg[it]);
     }
     if (v_thread) {
       const int pos = vt_pos(4 * v_kg);
@@ -176,8 +179,8 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
       for (int e = 0; e < 8; ++e) {
         const int w = e >> 1;
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
-        const uint32_t p01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
-        const uint32_t p23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);
+        const uint32_t p01 = __builtin_amdgcn_perm(sreg[VR0 + 1][w], sreg[VR0 + 0][w], sel);
+        const uint32_t p23 = __builtin_amdgcn_perm(sreg[VR0 + 3][w], sreg[VR0 + 2][w], sel);
         st8(Vt + (8 * v_dg + e) * VST + pos, u32x2{p01, p23});
       }
     }
@@ -191,12 +194,16 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
   const int n_pvec = (MODE == 1) ? Rb : (MODE == 2 && ESTAGE) ? EF * Rb : 0;   // float4 per group
   const int per_hw = (MODE == 1) ? Rb / 4 : EF * Rb / 4;                        // float4 per head
   const float* Eg = (MODE == 2) ? a.E + static_cast<size_t>(hg) * 4 * a.e_hs : nullptr;
+  // head (0..3 within the group) of float4 number vi, without an integer division
+  auto item_head = [&](int vi) -> int {
+    return static_cast<int>(vi >= per_hw) + static_cast<int>(vi >= 2 * per_hw) + static_cast<int>(vi >= 3 * per_hw);
+  };
   auto pfetch = [&](int vi) -> float4 {    // float4 number vi of the group's bias parameters
     if (MODE == 1)
       return reinterpret_cast<const float4*>(a.table + static_cast<size_t>(hg) * 4 * Rb)[vi];
     // E[h, f, 4q .. 4q+3]; the feature index varies fastest over the lanes so that 8
     // neighbouring lanes fill one 16-byte row e2[(hw, d)][0..7] (2-way bank conflicts)
-    const int hw = vi / per_hw;
+    const int hw = item_head(vi);
     const int rr = vi - hw * per_hw;
     const int f = rr % EF;
     const int dq = rr / EF;
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
     return reinterpret_cast<const float4*>(Eg + static_cast<size_t>(hw) * a.e_hs + static_cast<size_t>(f) * Rb)[dq];
   };
   auto pstore = [&](int vi, float4 v) {    // scaled to accumulator units, into LDS
-    const int hw = vi / per_hw;
+    const int hw = item_head(vi);
     const int rr = vi - hw * per_hw;
     if (MODE == 1) {
       float* tab = reinterpret_cast<float*>(smem + bias_off);
@@ -256,6 +263,7 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
       for (int c = 0; c < NC; ++c) asm volatile("" : "+a"(qf[qb][c]));
   }
   bf16x8 rf[QB];
+  const bool r_vec = a.R == EF && (reinterpret_cast<uintptr_t>(a.r) & 15) == 0;
   if (MODE == 2) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -263,15 +271,23 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
       const uint16_t* rp = a.r + ((static_cast<size_t>(b) * S + row) * a.Hq + h) * a.R;
       const int f0 = (EF == 16) ? 8 * lh : 0;
       const bool live = row < S && (EF == 16 || lh == 0);
-      uint32_t w[4];
+      if (r_vec) {
+        // rows of exactly EF features, 16-byte aligned: one load, no arithmetic on the value
+        // (its first use, the curve MFMA of the first step, waits for it there)
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (live) v = ld16(rp + f0);
+        rf[qb] = as_bf16x8(v);
+      } else {
+        uint32_t w[4];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int f = f0 + 2 * jj;
-        const uint32_t lo = (live && f < a.R) ? rp[f] : 0u;
-        const uint32_t hi = (live && f + 1 < a.R) ? rp[f + 1] : 0u;
-        w[jj] = lo | (hi << 16);
+        for (int jj = 0; jj < 4; ++jj) {
+          const int f = f0 + 2 * jj;
+          const uint32_t lo = (live && f < a.R) ? rp[f] : 0u;
+          const uint32_t hi = (live && f + 1 < a.R) ? rp[f + 1] : 0u;
+          w[jj] = lo | (hi << 16);
+        }
+        rf[qb] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
       }
-      rf[qb] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
     }
   }
 
@@ -341,6 +357,42 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
   uint16_t* ring = (MODE == 2) ? reinterpret_cast<uint16_t*>(smem + ring_off) +
                                      wave * QB * 32 * (ESTAGE ? CBW : RST) : nullptr;
 
+  // All-in-band layers, staged E: curves of step js, two MFMAs over the R features give the curves of the 64
+  // distances c - 31 .. c + 32 for every query row of the block; they are written unskewed to the
+  // wave's curve buffer (row = query, column = distance - (c - 31)) and each lane's diagonal is
+  // read back into cr.  Issued one step ahead, so that neither the MFMA nor the LDS round trip
+  // sits in front of the step's score MFMAs.
+  uint32_t cr[QB][12];
+  auto curve_issue = [&](int js) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int j0 = (t_begin + (js >> 1)) * BN + 32 * (js & 1);
+      // every visible key is in band, so a step outside the band is fully masked: clamp its
+      // offset to keep the reads inside the staged rows (distances -PAD .. Rb + PAD)
+      const int c = min(max((i0w + 32 * qb) - j0, -33), Rb + 31);
+      uint16_t* cb = ring + (QB > 1 ? qb : 0) * 32 * CBW;
+      const uint16_t* ep = e2w + (c - 31 + ln) * EF + 8 * lh;
+      const f32x16 zero = {};
+      const f32x16 lo = mfma32(as_bf16x8(ld16(ep)), rf[qb], zero);
+      const f32x16 hi = mfma32(as_bf16x8(ld16(ep + 32 * EF)), rf[qb], zero);
+      uint16_t* wp = cb + ln * CBW + 4 * lh;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        st8(wp + 8 * k, u32x2{pack_bf16x2(lo[4 * k], lo[4 * k + 1]), pack_bf16x2(lo[4 * k + 2], lo[4 * k + 3])});
+        st8(wp + 32 + 8 * k, u32x2{pack_bf16x2(hi[4 * k], hi[4 * k + 1]), pack_bf16x2(hi[4 * k + 2], hi[4 * k + 3])});
+      }
+      wave_sync_lds();
+      // dword reads are always aligned; the lane's run of key m0 .. m0 + 3 spans three of them
+      const uint32_t* rd = reinterpret_cast<const uint32_t*>(cb) + ln * (CBW / 2) + (ln >> 1) + 2 - 2 * lh;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        cr[qb][3 * g4] = rd[12 - 4 * g4];
+        cr[qb][3 * g4 + 1] = rd[13 - 4 * g4];
+        cr[qb][3 * g4 + 2] = rd[14 - 4 * g4];
+      }
+    }
+  };
+
   // Whether step js of query block qb starts from something other than zero (bias in band,
   // or a mask at the window / causal edges); uniform across the wave.
   auto step_special = [&](int js, int qb) -> bool {
@@ -371,7 +423,7 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
 #pragma unroll
       for (int i = 0; i < 16; ++i) init[i] = tb[27 - 8 * (i >> 2) - (i & 3)];
     }
-    if (MODE == 2 && ESTAGE && inband) {
+    if (MODE == 2 && ESTAGE && !PIPE && inband) {
       asm volatile("; in-band step: r.E bias" ::: "memory");
       // curves of the 64 distances c - 31 .. c + 32 for every query row of the block (two
       // MFMAs over the R features), written unskewed: row n, column = distance - (c - 31)
@@ -402,6 +454,22 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
         init[4 * g4 + 0] = __uint_as_float(__builtin_amdgcn_perm(d2, d1, sel_b));
       }
       wave_sync_lds();
+    }
+    if (PIPE) {
+      asm volatile("; in-band step: r.E bias, curves read a step ahead" ::: "memory");
+      // key m of lane n sits at column 31 + n - m of the curve buffer: keys m0 .. m0 + 3
+      // (m0 = 8 g + 4 lh) are the four columns from 28 + n - m0, which start on a 2-byte boundary
+      // for odd n.  The three dwords around them were read a step ahead (curve_issue); v_perm
+      // moves each bf16 into the top half of an fp32 with zeros below: column 28 + n - m0 + k
+      // holds key m0 + 3 - k.
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const uint32_t d0 = cr[qb][3 * g4], d1 = cr[qb][3 * g4 + 1], d2 = cr[qb][3 * g4 + 2];
+        init[4 * g4 + 3] = __uint_as_float(__builtin_amdgcn_perm(d1, d0, sel_a));
+        init[4 * g4 + 2] = __uint_as_float(__builtin_amdgcn_perm(d1, d0, sel_b));
+        init[4 * g4 + 1] = __uint_as_float(__builtin_amdgcn_perm(d2, d1, sel_a));
+        init[4 * g4 + 0] = __uint_as_float(__builtin_amdgcn_perm(d2, d1, sel_b));
+      }
     }
     if (MODE == 2 && !ESTAGE && inband) {
       // E from global memory: ring of curve blocks, consecutive key blocks share one
@@ -559,6 +627,7 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
   using true_t = std::integral_constant<bool, true>;
   // whether any query block of step js needs start values (the two stage-1 variants)
   auto any_special = [&](int js) {
+    if (ALLBAND) return true;
     bool sp = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) sp = sp || step_special(js, qb);
@@ -566,6 +635,7 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
   };
 
   f32x16 sa[QB], sb[QB];
+  if (PIPE) curve_issue(0);
   {
     if (any_special(0)) {
 #pragma unroll
@@ -576,6 +646,7 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
     }
     float mx[QB];
     step_rowmax(sa, mx);
+    if (PIPE) curve_issue(1);   // (past the last step: offsets clamped, results unused)
     rescale(mx);
   }
 
@@ -624,6 +695,7 @@ __global__ __launch_bounds__(512 / QB, 1) void fwd_fast_kernel(FwdArgs a, int bi
     float mx[QB];
     step_pv(js, pf);
     step_rowmax(snxt, mx);
+    if (PIPE) curve_issue(js + 2);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -687,7 +759,7 @@ int lds_total(int mode, int Rb, int R, bool estage) {
   return 2 * BUF_BYTES + (estage || mode != 2 ? bias_bytes(mode, Rb, R) : 0) + ring_bytes(mode, estage);
 }
 
-template <int MODE, int EF, bool RING, int QB, bool ESTAGE = true>
+template <int MODE, int EF, bool RING, int QB, bool ESTAGE = true, bool ALLBAND = false>
 hipError_t launch_fast(FwdArgs a, hipStream_t s) {
   a.hpw = 4;
   a.rows_wg = ROWS_WG;
@@ -701,12 +773,12 @@ hipError_t launch_fast(FwdArgs a, hipStream_t s) {
   if (nblk <= 0) return hipSuccess;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_fast_kernel<MODE, EF, RING, QB, ESTAGE>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_fast_kernel<MODE, EF, RING, QB, ESTAGE, ALLBAND>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((fwd_fast_kernel<MODE, EF, RING, QB, ESTAGE>), dim3(static_cast<unsigned>(nblk)), dim3(512 / QB), total, s,
+  hipLaunchKernelGGL((fwd_fast_kernel<MODE, EF, RING, QB, ESTAGE, ALLBAND>), dim3(static_cast<unsigned>(nblk)), dim3(512 / QB), total, s,
                      a, bias_off, ring_off);
   return hipGetLastError();
 }
@@ -729,8 +801,14 @@ hipError_t launch_fwd_bf16_fast(const FwdArgs& a, int mode, hipStream_t s) {
     case 1: return launch_fast<1, 8, false, 1>(a, s);
     default: {
       const bool stage = !RBA_FORCE_GLOBAL_E && lds_total(2, a.bias_range, a.R, true) <= kMaxLds;
-      if (a.R > 8) return stage ? launch_fast<2, 16, true, 1, true>(a, s) : launch_fast<2, 16, true, 1, false>(a, s);
-      return stage ? launch_fast<2, 8, true, 1, true>(a, s) : launch_fast<2, 8, true, 1, false>(a, s);
+      // every visible key in band (window <= range): branch-free curve steps
+      const bool allband = a.window != 0 && a.window <= a.bias_range;
+      if (a.R > 8) {
+        if (!stage) return launch_fast<2, 16, true, 1, false>(a, s);
+        return allband ? launch_fast<2, 16, true, 1, true, true>(a, s) : launch_fast<2, 16, true, 1, true>(a, s);
+      }
+      if (!stage) return launch_fast<2, 8, true, 1, false>(a, s);
+      return allband ? launch_fast<2, 8, true, 1, true, true>(a, s) : launch_fast<2, 8, true, 1, true>(a, s);
     }
   }
 }
