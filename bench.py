@@ -38,7 +38,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 KERNEL_SOURCES = {
-    "prefill": ["fwd_bf16.hip", "fwd_bf16_fast.hip"],
+    "prefill": ["fwd_bf16.hip", "fwd_bf16_fast.hip", "fwd_bf16_split.hip"],
     "decode": ["decode_bf16.hip"],
     "f32": ["attn_f32.hip"],
     "backward": ["bwd_bf16.hip"],
@@ -217,11 +217,14 @@ def main():
         kind = "backward"
     elif w.kind == "prefill":
         out = torch.empty_like(inp["q"])
+        need = rba.fwd_workspace_size(w.B, w.S, w.Hq, w.Hkv, w.D, dtype=w.dtype, window=w.window,
+                                      bias_range=w.bias_range, mode=w.mode, R=w.R, scale=w.scale)
+        fws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
 
         def step():
             rba.fwd(inp["q"], inp["k"], inp["v"], window=w.window, bias_range=w.bias_range,
                     mode=w.mode, table=inp["table"], r=inp["r"], E=inp["E"], scale=w.scale,
-                    temp_len=w.temp_len, out=out)
+                    temp_len=w.temp_len, out=out, workspace=fws)
 
         flops = 4.0 * w.D * w.Hq * w.B * visible_pairs_prefill(w.S, w.window)
         tokens = w.B * w.S

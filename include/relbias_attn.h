@@ -98,12 +98,30 @@ typedef enum {
  *   scale       multiplier of q.k (typically 1/sqrt(D)); the bias is not scaled.
  *   temp_len    0 (no temperature) or >= 2: the visible-key count beyond which the
  *               context-length temperature grows (see above); 1 or negative: RBA_EINVAL.
+ *   workspace   device scratch of at least relbias_attn_fwd_workspace_size(...) bytes,
+ *               16-byte aligned, owned by the caller; contents on entry are ignored and
+ *               are undefined on return.  NULL is allowed when that size is 0.  A call
+ *               reads and writes it on `stream` only: calls that overlap in time need
+ *               distinct workspaces.  Too small or misaligned: RBA_EINVAL.
+ *   workspace_bytes  its size in bytes.
  *   stream      hipStream_t.
  */
 int relbias_attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int S, int Hq, int Hkv, int D, int window, int bias_range, int mode,
                      const float* table, const void* r, const float* E, int R, float scale,
-                     int temp_len, void* stream);
+                     int temp_len, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace relbias_attn_fwd needs for these arguments (0: none).
+ * With the input-dependent bias (head_dim 128, Hq/Hkv a multiple of 4, bias_range a
+ * multiple of 4) the bf16 prefill converts E once per call into a bf16, distance-major
+ * copy there: heads * (bias_range + 129) * EF * 2 bytes rounded up to 256, with EF = 8
+ * for R <= 8 and 16 above, heads = Hq (RBA_BIAS_RPROJ) or 1 (RBA_BIAS_RPROJ_SHARED).
+ * Pure host function; arguments that relbias_attn_fwd would reject give 0.
+ */
+size_t relbias_attn_fwd_workspace_size(int dtype, int B, int S, int Hq, int Hkv, int D,
+                                       int window, int bias_range, int mode, int R,
+                                       float scale);
 
 /*
  * Bytes of device workspace relbias_attn_decode needs for these sizes

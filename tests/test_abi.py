@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) == {"relbias_attn_fwd", "relbias_attn_decode",
+    assert set(names) == {"relbias_attn_fwd", "relbias_attn_fwd_workspace_size", "relbias_attn_decode",
                           "relbias_attn_decode_workspace_size", "relbias_attn_decode_paged",
                           "relbias_attn_decode_paged_workspace_size", "relbias_attn_last_error",
                           "relbias_attn_version", "relbias_attn_bwd",
@@ -47,12 +47,12 @@ def test_exports_every_declared_symbol(lib):
 def _fwd(lib, **kw):
     a = dict(dtype=BF16, q=P, k=P, v=P, o=P, lse=None, B=1, S=16, Hq=4, Hkv=2, D=128, window=0,
              bias_range=8, mode=0, table=None, r=None, E=None, R=0, scale=0.1, temp_len=0,
-             stream=None)
+             ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib.relbias_attn_fwd(a["dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
                                 a["S"], a["Hq"], a["Hkv"], a["D"], a["window"], a["bias_range"],
                                 a["mode"], a["table"], a["r"], a["E"], a["R"], a["scale"],
-                                a["temp_len"], a["stream"])
+                                a["temp_len"], a["ws"], a["wsb"], a["stream"])
 
 
 def _dec(lib, **kw):
@@ -102,6 +102,37 @@ def test_mode_constants_match_header():
 ])
 def test_fwd_rejects(lib, kw, code, needle):
     assert _fwd(lib, **kw) == code
+    assert needle in rba.last_error()
+
+
+def test_fwd_workspace_policy(lib):
+    # the input-dependent bias takes a converted copy of E:
+    # heads x (bias_range + 2 * 64 + 1) rows x 8 (R <= 8) or 16 features x 2 bytes, 256-aligned
+    ws = lib.relbias_attn_fwd_workspace_size
+    assert ws(BF16, 2, 4096, 32, 8, 128, 512, 512, 2, 8, 0.088) == 32 * 641 * 8 * 2
+    assert ws(BF16, 2, 4096, 32, 8, 128, 512, 512, 3, 16, 0.088) == (641 * 16 * 2 + 255) // 256 * 256
+    assert ws(BF16, 1, 300, 4, 1, 128, 64, 100, 2, 11, 0.088) == (4 * 229 * 16 * 2 + 255) // 256 * 256
+    assert ws(BF16, 1, 32768, 32, 8, 128, 0, 1024, 2, 8, 0.088) == 32 * 1153 * 8 * 2
+    # no converted copy: other bias modes, fp32, shapes outside the kernel
+    assert ws(BF16, 2, 4096, 32, 8, 128, 512, 512, 0, 0, 0.088) == 0
+    assert ws(BF16, 2, 4096, 32, 8, 128, 512, 512, 1, 0, 0.088) == 0
+    assert ws(F32, 2, 4096, 32, 8, 128, 512, 512, 2, 8, 0.088) == 0
+    assert ws(BF16, 2, 4096, 32, 8, 64, 512, 512, 2, 8, 0.088) == 0
+    assert ws(BF16, 2, 4096, 6, 2, 128, 512, 512, 2, 8, 0.088) == 0
+    assert ws(BF16, 2, 4096, 32, 8, 128, 512, 77, 2, 8, 0.088) == 0
+    # arguments the forward would reject
+    assert ws(BF16, 2, 4096, 32, 8, 128, 512, 512, 2, 17, 0.088) == 0
+    assert ws(BF16, 2, 4096, 32, 7, 128, 512, 512, 2, 8, 0.088) == 0
+
+
+@pytest.mark.parametrize("kw,needle", [
+    (dict(ws=None, wsb=0), "required"),
+    (dict(ws=P, wsb=1024), "too small"),
+    (dict(ws=P + 8, wsb=1 << 20), "16-byte"),
+])
+def test_fwd_workspace_rejects(lib, kw, needle):
+    local = dict(mode=2, r=P, E=P, R=8, window=64, bias_range=64, Hq=4, Hkv=1, S=100)
+    assert _fwd(lib, **local, **kw) == EINVAL
     assert needle in rba.last_error()
 
 

@@ -60,8 +60,10 @@ def load_library():
     lib = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.relbias_attn_fwd.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, vp, i,
-                                     f, i, vp]
+                                     f, i, vp, sz, vp]
     lib.relbias_attn_fwd.restype = i
+    lib.relbias_attn_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i, i, i, f]
+    lib.relbias_attn_fwd_workspace_size.restype = sz
     lib.relbias_attn_decode.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp, vp,
                                         vp, i, f, i, vp, sz, vp]
     lib.relbias_attn_decode.restype = i
@@ -149,12 +151,26 @@ def _bias_args(mode, table, r, E, Hq, act_dtype, dev):
     return m, R
 
 
+def fwd_workspace_size(B, S, Hq, Hkv, D, *, dtype="bf16", window=0, bias_range=0, mode="none",
+                       R=0, scale=None):
+    """Workspace bytes fwd needs for these sizes (relbias_attn_fwd_workspace_size)."""
+    lib = load_library()
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dt = RBA_BF16 if dtype in ("bf16", "bfloat16") else RBA_F32
+    return int(lib.relbias_attn_fwd_workspace_size(dt, B, S, Hq, Hkv, D, int(window), int(bias_range),
+                                                   m, int(R), float(scale)))
+
+
 def fwd(q, k, v, *, window=0, bias_range=0, mode="none", table=None, r=None, E=None,
-        scale=None, temp_len=0, out=None, lse=None, return_lse=False, stream=None):
+        scale=None, temp_len=0, out=None, lse=None, return_lse=False, workspace=None, stream=None):
     """Prefill attention with a relative-position bias (relbias_attn_fwd).
 
     q [B,S,Hq,D], k/v [B,S,Hkv,D] (bf16 or fp32, contiguous, on one GPU).
     temp_len: context-length temperature threshold (0: none; 131072 for the 128k form).
+    workspace: optional uint8 device tensor of at least fwd_workspace_size(...) bytes; allocated
+    here when needed and not given.
     Returns o [B,S,Hq,D] (and lse [B,Hq,S] fp32 when return_lse or lse is given).
     """
     import torch
@@ -178,10 +194,16 @@ def fwd(q, k, v, *, window=0, bias_range=0, mode="none", table=None, r=None, E=N
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
     _check(lse, "lse", dtype=torch.float32, device=dev)
+    need = int(lib.relbias_attn_fwd_workspace_size(_dtype_id(q), B, S, Hq, Hkv, D, int(window),
+                                                   int(bias_range), m, R, float(scale)))
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", dtype=torch.uint8, device=dev)
     st = lib.relbias_attn_fwd(_dtype_id(q), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                               B, S, Hq, Hkv, D, int(window), int(bias_range), m,
                               _ptr(table if m == 1 else None), _ptr(r if m in (2, 3) else None),
                               _ptr(E if m in (2, 3) else None), R, float(scale), int(temp_len),
+                              _ptr(workspace), workspace.numel() if workspace is not None else 0,
                               _stream_handle(dev, stream))
     if st != RBA_OK:
         raise LibraryError(st, last_error())

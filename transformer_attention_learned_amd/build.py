@@ -20,8 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librelbias_attn.so")
 
-SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_bf16_fast.hip", "attn_f32.hip", "decode_bf16.hip",
-           "bwd_bf16.hip", "kv_fp4.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_bf16_fast.hip", "fwd_bf16_split.hip", "attn_f32.hip",
+           "decode_bf16.hip", "bwd_bf16.hip", "kv_fp4.hip"]
 ARCH = "gfx950"
 
 

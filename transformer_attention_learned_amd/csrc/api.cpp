@@ -87,6 +87,35 @@ long long e_head_stride(int mode, int R, int bias_range) {
 }
 bool is_rproj(int mode) { return mode == RBA_BIAS_RPROJ || mode == RBA_BIAS_RPROJ_SHARED; }
 
+// Kernel arguments of a bf16 prefill (the launch geometry is the launcher's).
+rba::FwdArgs bf16_fwd_args(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                           int S, int Hq, int Hkv, int window, int bias_range, int mode,
+                           const float* table, const void* r, const float* E, int R, float scale,
+                           int temp_len) {
+  rba::FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.table = table;
+  a.r = static_cast<const uint16_t*>(r);
+  a.E = E;
+  a.B = B;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.window = window;
+  a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
+  a.R = is_rproj(mode) ? R : 0;
+  a.e_hs = e_head_stride(mode, R, bias_range);
+  a.c_qk = scale * rba::kLog2e;
+  a.temp_len = temp_len;
+  a.temp_inv_log2 = temp_inv_log2(temp_len);
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -95,10 +124,22 @@ const char* relbias_attn_last_error(void) { return g_err.c_str(); }
 
 const char* relbias_attn_version(void) { return "relbias_attn 0.1 gfx950"; }
 
+size_t relbias_attn_fwd_workspace_size(int dtype, int B, int S, int Hq, int Hkv, int D,
+                                       int window, int bias_range, int mode, int R, float scale) {
+  if (dtype != RBA_BF16 || B <= 0 || S <= 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || window < 0) return 0;
+  if (!(D == 64 || D == 128) || !std::isfinite(scale)) return 0;
+  if (mode != RBA_BIAS_NONE && (bias_range < 1 || bias_range > kMaxBiasRange)) return 0;
+  if (is_rproj(mode) && (R < 1 || R > 16)) return 0;
+  if (mode < RBA_BIAS_NONE || mode > RBA_BIAS_RPROJ_SHARED) return 0;
+  const rba::FwdArgs a = bf16_fwd_args(nullptr, nullptr, nullptr, nullptr, nullptr, B, S, Hq, Hkv,
+                                       window, bias_range, mode, nullptr, nullptr, nullptr, R, scale, 0);
+  return static_cast<size_t>(rba::fwd_bf16_workspace(a, D, kernel_mode(mode)));
+}
+
 int relbias_attn_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int S, int Hq, int Hkv, int D, int window, int bias_range, int mode,
                      const float* table, const void* r, const float* E, int R, float scale,
-                     int temp_len, void* stream) {
+                     int temp_len, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "relbias_attn_fwd";
   if (B < 0 || S < 0) return fail(RBA_EINVAL, "%s: B=%d and S=%d must be >= 0", fn, B, S);
   int st = check_common(fn, dtype, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale);
@@ -121,28 +162,17 @@ int relbias_attn_fwd(int dtype, const void* q, const void* k, const void* v, voi
     const long long rows_wg = 32LL * (4 / hpw);
     const long long nblk = ((S + rows_wg - 1) / rows_wg) * (Hq / hpw) * static_cast<long long>(B);
     if (nblk > 0x7fffffffLL) return fail(RBA_ENOTSUP, "%s: grid too large", fn);
-    rba::FwdArgs a{};
-    a.q = static_cast<const uint16_t*>(q);
-    a.k = static_cast<const uint16_t*>(k);
-    a.v = static_cast<const uint16_t*>(v);
-    a.o = static_cast<uint16_t*>(o);
-    a.lse = lse;
-    a.table = table;
-    a.r = static_cast<const uint16_t*>(r);
-    a.E = E;
-    a.B = B;
-    a.S = S;
-    a.Hq = Hq;
-    a.Hkv = Hkv;
-    a.G = G;
-    a.window = window;
-    a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
-    a.R = is_rproj(mode) ? R : 0;
-    a.e_hs = e_head_stride(mode, R, bias_range);
-    a.c_qk = scale * rba::kLog2e;
-    a.temp_len = temp_len;
-    a.temp_inv_log2 = temp_inv_log2(temp_len);
-    e = rba::launch_fwd_bf16(a, D, kernel_mode(mode), hs);
+    (void)G;
+    const rba::FwdArgs a = bf16_fwd_args(q, k, v, o, lse, B, S, Hq, Hkv, window, bias_range, mode,
+                                         table, r, E, R, scale, temp_len);
+    const long long need = rba::fwd_bf16_workspace(a, D, kernel_mode(mode));
+    if (need > 0) {
+      if (!workspace) return fail(RBA_EINVAL, "%s: workspace of %lld bytes required, got NULL", fn, need);
+      if (workspace_bytes < static_cast<size_t>(need))
+        return fail(RBA_EINVAL, "%s: workspace too small (%zu < %lld bytes)", fn, workspace_bytes, need);
+      if (!aligned16(workspace)) return fail(RBA_EINVAL, "%s: workspace is not 16-byte aligned", fn);
+    }
+    e = rba::launch_fwd_bf16(a, D, kernel_mode(mode), workspace, hs);
   } else {
     rba::F32Args a{};
     a.q = static_cast<const float*>(q);

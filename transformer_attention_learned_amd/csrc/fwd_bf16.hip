@@ -394,12 +394,30 @@ hipError_t launch_mode(const FwdArgs& a, int mode, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a0, int D, int mode, hipStream_t s) {
+namespace {
+// The two MFMA kernels address K and V through 32-bit buffer offsets within one sequence.
+bool kv_off32(const FwdArgs& a, int D) { return static_cast<long long>(a.S) * a.Hkv * D * 2 < (1LL << 31); }
+// Sliding-window (local) layers and the input-dependent bias take the split kernel, whose
+// 32-row workgroups pair up on a CU (and which reads E rows converted once per call); full
+// causal layers without it keep one workgroup of 64 rows per CU, whose long key loops amortise
+// its start-up (measured faster there).
+bool use_split(const FwdArgs& a, int D, int mode) {
+  return (a.window != 0 || mode == 2) && kv_off32(a, D) &&
+         fwd_split_workspace(D, a.G, mode, a.bias_range, a.R, a.e_hs == 0, a.Hq, a.c_qk) >= 0;
+}
+}  // namespace
+
+long long fwd_bf16_workspace(const FwdArgs& a, int D, int mode) {
+  if (!use_split(a, D, mode)) return 0;
+  const long long n = fwd_split_workspace(D, a.G, mode, a.bias_range, a.R, a.e_hs == 0, a.Hq, a.c_qk);
+  return (n + 255) / 256 * 256;
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a0, int D, int mode, void* workspace, hipStream_t s) {
+  if (use_split(a0, D, mode)) return launch_fwd_bf16_split(a0, mode, workspace, s);
   const bool vec_ok = (reinterpret_cast<uintptr_t>(a0.table) & 15u) == 0 &&
                       (reinterpret_cast<uintptr_t>(a0.E) & 15u) == 0;
-  // the fast path addresses K and V through 32-bit buffer offsets within one sequence
-  const bool off32 = static_cast<long long>(a0.S) * a0.Hkv * D * 2 < (1LL << 31);
-  if (vec_ok && off32 && fwd_fast_lds_bytes(D, a0.G, mode, a0.bias_range, a0.R, a0.c_qk) >= 0)
+  if (vec_ok && kv_off32(a0, D) && fwd_fast_lds_bytes(D, a0.G, mode, a0.bias_range, a0.R, a0.c_qk) >= 0)
     return launch_fwd_bf16_fast(a0, mode, s);
   FwdArgs a = a0;
   a.hpw = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0 ? 2 : 1);

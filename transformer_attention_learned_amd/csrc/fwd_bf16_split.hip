@@ -1,0 +1,587 @@
+// Prefill for head_dim 128 and GQA groups of 4k query heads, two workgroups per CU (gfx950).
+//
+// Same operation as the other prefill kernels (scaled q.k plus a bias read at the distance
+// i - j, zero at and beyond the range, causal / sliding window; "Thinking Machines dropped
+// RoPE", steps 3-5 and the kernel-cost section), organised so that two workgroups share a CU:
+//
+//   * workgroup = 4 waves = the 4 query heads of one GQA group over the same 32 query rows,
+//     one wave per SIMD; a second workgroup on the CU supplies the other wave of each SIMD, so
+//     one workgroup's barriers and start-up overlap the other's key loop;
+//   * K/V tiles of 32 keys (one key step) in a ring of three LDS buffers: the tile of step j + 2
+//     is written while steps j (P.V) and j + 1 (scores) read theirs, so one barrier per step
+//     covers both hazards; its rows were fetched into registers two steps before (two register
+//     sets; V transposed on its way to LDS);
+//   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: each lane owns one query row,
+//     P stays in registers; the key loop is a two-stage software pipeline (S MFMAs of step j + 1
+//     beside the exp of step j, P.V MFMAs of step j beside the row max of step j + 1);
+//   * bias and masks enter through the S accumulator's start values; lazy rescaling of O;
+//   * table bias: the group's table rows in LDS, zero-padded, read with immediate offsets;
+//   * input-dependent bias r_i . E[h, :, delta]: E in bf16, distance-major rows of EF features
+//     in accumulator units (converted once per call into the caller's workspace), so that a
+//     curve block's operand is one 16-byte load per lane; the curves of a step (two MFMAs over
+//     the R features for its 64 distances) go through the wave's LDS curve buffer and are formed
+//     one step ahead of their use, their E rows one step before that; with the window inside the
+//     range every step is in band and this path has no branches.
+
+#include <algorithm>
+#include <type_traits>
+
+#include "rba_device.h"
+#include "rba_internal.h"
+
+namespace rba {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int BN = 32;            // keys per tile (= per step)
+constexpr int NC = D / 16;        // K = 16 chunks of the head dim
+constexpr int NDB = D / 32;       // 32-wide head-dim blocks of O^T
+constexpr int KST = D + 8;        // K tile row stride (bf16)
+constexpr int VST = BN + 8;       // V^T tile row stride (bf16)
+constexpr int NBUF = 3;           // tile ring
+constexpr int CBW = 72;           // curve buffer row stride (bf16)
+constexpr int PAD = 64;           // zero distances on each side of the bias range (table rows, E rows)
+constexpr int ROWS_WG = 32;       // query rows per workgroup
+constexpr int NT = 256;           // threads per workgroup
+constexpr float kRescale = 8.f;   // lazy rescale threshold (log2 units)
+
+constexpr int KS_BYTES = BN * KST * 2;
+constexpr int VT_BYTES = D * VST * 2;
+constexpr int BUF_BYTES = KS_BYTES + VT_BYTES;
+constexpr int CURVE_BYTES = 32 * CBW * 2;   // per wave
+constexpr int TILE_BYTES = NBUF * BUF_BYTES;
+
+__device__ __forceinline__ int vt_pos(int x) {
+  return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// E (fp32 [heads, R, Rb], head h at E + h * e_hs) -> bf16 rows [heads][Rb + 2 PAD + 1][EF]:
+// entry (h, PAD + d, f) = E[h, f, d] / scale for 0 <= d < Rb and f < R, zero elsewhere (the pads
+// and the features past R), so that every read of the kernels below is in range and unguarded.
+__global__ void e2_convert_kernel(const float* __restrict__ E, long long e_hs, int heads, int R, int Rb,
+                                  float inv_scale, int EF, uint16_t* __restrict__ e2) {
+  const int rows = Rb + 2 * PAD + 1;
+  const long long n = static_cast<long long>(heads) * rows * EF;
+  for (long long i = blockIdx.x * static_cast<long long>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<long long>(gridDim.x) * blockDim.x) {
+    const int f = static_cast<int>(i % EF);
+    const long long hp = i / EF;
+    const int p = static_cast<int>(hp % rows);
+    const int h = static_cast<int>(hp / rows);
+    const int d = p - PAD;
+    float v = 0.f;
+    if (d >= 0 && d < Rb && f < R) v = E[h * e_hs + static_cast<long long>(f) * Rb + d] * inv_scale;
+    e2[i] = f32_to_bf16(v);
+  }
+}
+
+// MODE 0 none, 1 table, 2 r.E (EF = 8 or 16 features per E row); ALLBAND: every visible key is
+// inside the bias range (window <= range), so every step of MODE 2 is in band.
+template <int MODE, int EF, bool ALLBAND>
+__global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint16_t* __restrict__ e2g) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: geometry stays scalar
+  const int ln = lane & 31;
+  const int lh = lane >> 5;
+
+  const int per_q = a.n_hgroups * a.B;
+  int qt = blockIdx.x / per_q;
+  const int rem = blockIdx.x - qt * per_q;
+  const int hg = rem % a.n_hgroups;
+  const int b = rem / a.n_hgroups;
+  if (a.longest_first) qt = a.n_qtiles - 1 - qt;
+
+  const int S = a.S;
+  const int W = a.window;
+  const int Rb = a.bias_range;
+  const int i0 = qt * ROWS_WG;                 // first query row (all four waves)
+  const int h = hg * 4 + wave;
+  const int hkv = h / a.G;
+  const int row_last = min(S, i0 + ROWS_WG) - 1;
+  const int kmin = W ? max(0, i0 - W + 1) : 0;
+  const int t_begin = kmin / BN;
+  const int nsteps = row_last / BN - t_begin + 1;
+
+  const float cqk = a.c_qk;              // scale * log2(e)
+  const float inv_scale = kLog2e / cqk;  // bias -> accumulator units (bias / scale)
+  // scale * log2(e) times the row's context-length temperature, which multiplies the q.k term
+  // and the bias alike (both sit in the accumulator)
+  const float cqk_r = cqk * temp_factor(visible_keys(i0 + ln, W), a.temp_len, a.temp_inv_log2);
+
+  const size_t q_row = static_cast<size_t>(a.Hq) * D;
+  const size_t kv_row = static_cast<size_t>(a.Hkv) * D;
+  const uint16_t* kbase = a.k + static_cast<size_t>(b) * S * kv_row + static_cast<size_t>(hkv) * D;
+  const uint16_t* vbase = a.v + static_cast<size_t>(b) * S * kv_row + static_cast<size_t>(hkv) * D;
+
+  // ---- K/V staging, 32 keys x 128 dims each: waves 0-1 take K (512 chunks of 16 B, 4 per
+  // thread, row-major), waves 2-3 take V (128 items of 4 keys x 8 dims, transposed on the way
+  // to LDS); each thread stages one of them, so both share one set of registers.
+  u32x4 sreg[2][4];   // tiles of even / odd steps
+  const bool k_thread = wave < 2;
+  const int vt = tid & 127;
+  const int v_kg = vt & 7;
+  const int v_dg = vt >> 3;
+  // Rows at or past S read as zeros through the buffer range (rows - r0) * row bytes - head
+  // offset, which every in-range 16-byte chunk fits below.
+  const int kv_row_b = a.Hkv * D * 2;
+  const int head_b = hkv * D * 2;
+  // byte offsets of the thread's four 16-byte chunks from the tile's first row: K rows
+  // it * 8 + vt / 16, V rows 4 * v_kg + s
+  const int k_voff = (vt >> 4) * kv_row_b + 16 * (vt & 15);
+  const int v_voff = 4 * v_kg * kv_row_b + 16 * v_dg;
+  const int step_off = k_thread ? 8 * kv_row_b : kv_row_b;
+  const int voff0 = k_thread ? k_voff : v_voff;
+  const uint16_t* kvbase = k_thread ? kbase : vbase;
+  auto load_tile = [&](int t, u32x4 (&reg)[4]) {   // tile t of the step sequence
+    // one buffer resource per tile: its range ends at row S, so rows past the sequence read as
+    // zeros (the head offset keeps every in-range chunk of the last row below the bound)
+    const int tk0 = (t_begin + t) * BN;
+    const int left = S - tk0;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(kvbase + static_cast<size_t>(tk0) * kv_row,
+                                                left > 0 ? left * kv_row_b - head_b : 0);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) reg[it] = buf_ld16(rs, voff0 + it * step_off);
+  };
+  auto store_tile = [&](int t, const u32x4 (&reg)[4]) {
+    const int buf = t % NBUF;
+    uint16_t* Ks = reinterpret_cast<uint16_t*>(smem + buf * BUF_BYTES);
+    uint16_t* Vt = reinterpret_cast<uint16_t*>(smem + buf * BUF_BYTES + KS_BYTES);
+    if (k_thread) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) st16(Ks + (it * 8 + (vt >> 4)) * KST + 8 * (vt & 15), reg[it]);
+    } else {
+      const int pos = vt_pos(4 * v_kg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+        const uint32_t p01 = __builtin_amdgcn_perm(reg[1][w], reg[0][w], sel);
+        const uint32_t p23 = __builtin_amdgcn_perm(reg[3][w], reg[2][w], sel);
+        st8(Vt + (8 * v_dg + e) * VST + pos, u32x2{p01, p23});
+      }
+    }
+  };
+
+  // ---- table rows of the group (MODE 1), in accumulator units, PAD zero distances each side
+  const int Rp = Rb + 2 * PAD;
+  if (MODE == 1) {
+    float* tab = reinterpret_cast<float*>(smem + TILE_BYTES);
+    const float* tg = a.table + static_cast<size_t>(hg) * 4 * Rb;
+    for (int i = tid; i < 4 * Rp; i += NT) {
+      const int hw = static_cast<int>(i >= Rp) + static_cast<int>(i >= 2 * Rp) + static_cast<int>(i >= 3 * Rp);
+      const int d = i - hw * Rp - PAD;
+      tab[i] = (d >= 0 && d < Rb) ? tg[hw * Rb + d] * inv_scale : 0.f;
+    }
+  }
+
+  // tiles 0 and 1 in flight first (HBM), then the query rows
+  load_tile(0, sreg[0]);
+  if (nsteps > 1) load_tile(1, sreg[1]);
+
+  bf16x8 qf[NC];
+  {
+    const int row = i0 + ln;
+    const uint16_t* qp = a.q + (static_cast<size_t>(b) * S + row) * q_row + static_cast<size_t>(h) * D + 8 * lh;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row < S) v = ld16(qp + 16 * c);
+      qf[c] = as_bf16x8(v);
+    }
+  }
+  bf16x8 rf;
+  const uint16_t* e2h = nullptr;   // this head's E rows at distance 0
+  if (MODE == 2) {
+    const int row = i0 + ln;
+    const uint16_t* rp = a.r + ((static_cast<size_t>(b) * S + row) * a.Hq + h) * a.R;
+    const int f0 = (EF == 16) ? 8 * lh : 0;
+    const bool live = row < S && (EF == 16 || lh == 0);
+    if (a.R == EF && (reinterpret_cast<uintptr_t>(a.r) & 15) == 0) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (live) v = ld16(rp + f0);
+      rf = as_bf16x8(v);
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int f = f0 + 2 * jj;
+        const uint32_t lo = (live && f < a.R) ? rp[f] : 0u;
+        const uint32_t hi = (live && f + 1 < a.R) ? rp[f + 1] : 0u;
+        w[jj] = lo | (hi << 16);
+      }
+      rf = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+    }
+    e2h = e2g + (static_cast<size_t>(a.e_hs ? h : 0) * (Rp + 1) + PAD) * EF;
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+
+  const float NEG_INF = -INFINITY;
+  auto perm_sel = [](int r) -> uint32_t {
+    return 0x0c0cu | (static_cast<uint32_t>(2 * r) << 16) | (static_cast<uint32_t>(2 * r + 1) << 24);
+  };
+  const uint32_t sel_a = perm_sel(ln & 1);
+  const uint32_t sel_b = perm_sel((ln & 1) + 1);
+  const float* tabw = (MODE == 1) ? reinterpret_cast<const float*>(smem + TILE_BYTES) + wave * Rp + PAD : nullptr;
+  uint16_t* cbuf = (MODE == 2) ? reinterpret_cast<uint16_t*>(smem + TILE_BYTES) + wave * (CURVE_BYTES / 2) : nullptr;
+
+  // Step js covers keys j0 .. j0 + 31 with j0 = (t_begin + js) * BN; delta = c + n - m with
+  // c = i0 - j0, n the lane's row, m the key within the step.
+  auto step_c = [&](int js) { return i0 - (t_begin + js) * BN; };
+  auto step_on = [&](int js) {
+    const int j0 = (t_begin + js) * BN;
+    const int c = i0 - j0;
+    bool on = (c + 31 >= 0) && (j0 < S) && (i0 < S);
+    if (W) on = on && (c - 31 < W);
+    return on;
+  };
+  auto step_inband = [&](int js) { return MODE != 0 && step_on(js) && step_c(js) - 31 < Rb; };
+  auto step_edge = [&](int js) {
+    const int c = step_c(js);
+    return !step_on(js) || (c - 31 < 0) || (W && c + 31 >= W);
+  };
+
+  // ---- r.E curves: E rows of step js are loaded one step before its curves are formed
+  u32x4 ef_lo = {0u, 0u, 0u, 0u}, ef_hi = {0u, 0u, 0u, 0u};
+  uint32_t cr[12];
+#pragma unroll
+  for (int i = 0; i < 12; ++i) cr[i] = 0u;
+  auto curve_c = [&](int js) {
+    // a step outside the band is fully masked (ALLBAND) or skipped: clamp its offset so that
+    // the E rows read stay inside the padded rows (distances -PAD .. Rb + PAD)
+    return min(max(step_c(js), -33), Rb + 31);
+  };
+  auto e_fetch = [&](int js) {
+    const uint16_t* ep = e2h + (curve_c(js) - 31 + ln) * EF + 8 * lh;
+    ef_lo = ld16(ep);
+    ef_hi = ld16(ep + 32 * EF);
+  };
+  // curves of step js from the fetched E rows: two MFMAs over the R features give the 64
+  // distances c - 31 .. c + 32 for every query row; written unskewed to the wave's buffer
+  // (row = query, column = distance - (c - 31)), then each lane's diagonal read back into cr
+  auto curve_issue = [&](int js) {
+    const f32x16 zero = {};
+    const f32x16 lo = mfma32(as_bf16x8(ef_lo), rf, zero);
+    const f32x16 hi = mfma32(as_bf16x8(ef_hi), rf, zero);
+    uint16_t* wp = cbuf + ln * CBW + 4 * lh;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      st8(wp + 8 * k, u32x2{pack_bf16x2(lo[4 * k], lo[4 * k + 1]), pack_bf16x2(lo[4 * k + 2], lo[4 * k + 3])});
+      st8(wp + 32 + 8 * k, u32x2{pack_bf16x2(hi[4 * k], hi[4 * k + 1]), pack_bf16x2(hi[4 * k + 2], hi[4 * k + 3])});
+    }
+    wave_sync_lds();
+    // key m of lane n sits at column 31 + n - m; keys m0 .. m0 + 3 (m0 = 8 g + 4 lh) span
+    // the three aligned dwords read here
+    const uint32_t* rd = reinterpret_cast<const uint32_t*>(cbuf) + ln * (CBW / 2) + (ln >> 1) + 2 - 2 * lh;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      cr[3 * g4] = rd[12 - 4 * g4];
+      cr[3 * g4 + 1] = rd[13 - 4 * g4];
+      cr[3 * g4 + 2] = rd[14 - 4 * g4];
+    }
+  };
+  // the curve work of step js (when it has any), and the E rows of step js + 1
+  auto curve_step = [&](int js) {
+    if (MODE != 2) return;
+    if (ALLBAND) {
+      curve_issue(js);
+      e_fetch(js + 1);
+    } else {
+      if (step_inband(js)) curve_issue(js);
+      if (step_inband(js + 1)) e_fetch(js + 1);
+    }
+  };
+
+  // Whether step js starts from something other than zero; uniform across the wave.
+  auto step_special = [&](int js) -> bool {
+    if (MODE == 2 && ALLBAND) return true;
+    return step_edge(js) || step_inband(js);
+  };
+  // Accumulator start values: bias / scale where the key is visible and in band, 0 where
+  // visible and beyond the band, -inf elsewhere.
+  auto step_init = [&](int js) -> f32x16 {
+    f32x16 init;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) init[i] = 0.f;
+    const int c = step_c(js);
+    const bool on = step_on(js);
+    const bool inband = step_inband(js);
+    if (MODE == 1 && inband) {
+      asm volatile("; in-band step: table bias" ::: "memory");
+      const float* tb = tabw + (c + ln - 4 * lh - 27);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) init[i] = tb[27 - 8 * (i >> 2) - (i & 3)];
+    }
+    if (MODE == 2 && (ALLBAND || inband)) {
+      asm volatile("; in-band step: r.E bias" ::: "memory");
+      // column 28 + n - m0 + k holds key m0 + 3 - k; v_perm moves each bf16 into the top half
+      // of an fp32 with zeros below
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const uint32_t d0 = cr[3 * g4], d1 = cr[3 * g4 + 1], d2 = cr[3 * g4 + 2];
+        init[4 * g4 + 3] = __uint_as_float(__builtin_amdgcn_perm(d1, d0, sel_a));
+        init[4 * g4 + 2] = __uint_as_float(__builtin_amdgcn_perm(d1, d0, sel_b));
+        init[4 * g4 + 1] = __uint_as_float(__builtin_amdgcn_perm(d2, d1, sel_a));
+        init[4 * g4 + 0] = __uint_as_float(__builtin_amdgcn_perm(d2, d1, sel_b));
+      }
+    }
+    if (step_edge(js)) {
+      asm volatile("; edge step: mask" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = 8 * (i >> 2) + 4 * lh + (i & 3);
+        const int d = c + ln - m;
+        if (!on || d < 0 || (W && d >= W)) init[i] = NEG_INF;
+      }
+    }
+    return init;
+  };
+
+  auto k_frag = [&](int js, int c) -> bf16x8 {
+    const uint16_t* Ks = reinterpret_cast<const uint16_t*>(smem + (js % NBUF) * BUF_BYTES);
+    return as_bf16x8(ld16(Ks + ln * KST + 16 * c + 8 * lh));
+  };
+  auto v_frag = [&](int js, int idx) -> bf16x8 {   // idx = 2 * db + kk
+    const uint16_t* Vt = reinterpret_cast<const uint16_t*>(smem + (js % NBUF) * BUF_BYTES + KS_BYTES);
+    return as_bf16x8(ld16(Vt + (32 * (idx >> 1) + ln) * VST + 16 * (idx & 1) + 8 * lh));
+  };
+  auto step_scores = [&](int js, f32x16& acc, auto spec_c) {
+    constexpr bool SPEC = decltype(spec_c)::value;
+    bf16x8 kf = k_frag(js, 0);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      bf16x8 kn = kf;
+      if (c + 1 < NC) kn = k_frag(js, c + 1);
+      if (c == 0 && !SPEC) {
+        const f32x16 zero = {};
+        acc = mfma32(kf, qf[0], zero);
+      } else {
+        acc = mfma32(kf, qf[c], acc);
+      }
+      kf = kn;
+    }
+  };
+  auto step_pv = [&](int js, const bf16x8 (&pf)[2]) {
+    bf16x8 vf = v_frag(js, 0);
+#pragma unroll
+    for (int idx = 0; idx < 2 * NDB; ++idx) {
+      bf16x8 vn = vf;
+      if (idx + 1 < 2 * NDB) vn = v_frag(js, idx + 1);
+      oacc[idx >> 1] = mfma32(vf, pf[idx & 1], oacc[idx >> 1]);
+      vf = vn;
+    }
+  };
+  auto step_probs = [&](const f32x16& acc, float m_use, bf16x8 (&pf)[2]) {
+    float psum = l_run;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      uint32_t w[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float p0 = fast_exp2(fmaf(acc[8 * kk + 2 * jj], cqk_r, -m_use));
+        const float p1 = fast_exp2(fmaf(acc[8 * kk + 2 * jj + 1], cqk_r, -m_use));
+        w[jj] = pack_bf16x2(p0, p1);
+        psum = sum_bf16x2(w[jj], psum);
+      }
+      pf[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+    }
+    l_run = psum;
+  };
+  auto step_rowmax = [&](const f32x16& acc) -> float {
+    float v = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) v = fmaxf(fmaxf(v, acc[i]), acc[i + 1]);
+    v = fmaxf(v, acc[15]);
+    return pair_max(v) * cqk_r;
+  };
+  auto rescale = [&](float mx) {
+    const bool need = mx > m_run + kRescale;
+    if (__any(need)) {
+      float alpha = need ? fast_exp2(m_run - mx) : 1.f;
+      asm volatile("; rare path: rescale O" : "+v"(alpha));
+      if (need) m_run = mx;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
+  };
+
+  using false_t = std::integral_constant<bool, false>;
+  using true_t = std::integral_constant<bool, true>;
+
+  // ---- prologue: tiles 0 and 1 in LDS, tile 2 in flight, curves and scores of step 0 ---------
+  if (MODE == 2 && (ALLBAND || step_inband(0))) e_fetch(0);
+  store_tile(0, sreg[0]);
+  if (nsteps > 1) store_tile(1, sreg[1]);
+  if (nsteps > 2) load_tile(2, sreg[0]);
+  if (nsteps > 3) load_tile(3, sreg[1]);
+  __syncthreads();
+
+  f32x16 sa, sb;
+  {
+    if (MODE == 2 && (ALLBAND || step_inband(0))) curve_issue(0);
+    if (MODE == 2 && (ALLBAND || step_inband(1))) e_fetch(1);
+    if (step_special(0)) {
+      sa = step_init(0);
+      step_scores(0, sa, true_t{});
+    } else {
+      step_scores(0, sa, false_t{});
+    }
+    const float mx = step_rowmax(sa);
+    curve_step(1);
+    rescale(mx);
+  }
+
+  // ---- key loop: iteration js consumes the scores of step js and produces those of js + 1 ----
+  // (ODD: js odd, so that the register set of tile js + 2 is a compile-time index)
+  auto iteration = [&](int js, auto odd_c, f32x16& scur, f32x16& snxt) {
+    constexpr int RS = decltype(odd_c)::value ? 1 : 0;   // register set of tiles js + 2 and js + 4
+    // tile js + 1 is in LDS (written a step ago); every wave is done with tile js - 1, whose
+    // buffer now takes tile js + 2 (its rows were fetched two steps ago); the freed registers
+    // take tile js + 4
+    __syncthreads();
+    if (js + 2 < nsteps) store_tile(js + 2, sreg[RS]);
+    if (js + 4 < nsteps) load_tile(js + 4, sreg[RS]);
+
+    const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
+    bf16x8 pf[2];
+    auto fence_stage1 = [&]() {
+      asm volatile("" : "+v"(snxt));
+      asm volatile("" : "+v"(pf[0]), "+v"(pf[1]));
+    };
+    // stage 1: S MFMAs of step js + 1 beside the exp / pack of step js
+    if (step_special(js + 1)) {
+      snxt = step_init(js + 1);
+      step_scores(js + 1, snxt, true_t{});
+      step_probs(scur, m_use, pf);
+      fence_stage1();
+    } else {
+      step_scores(js + 1, snxt, false_t{});
+      step_probs(scur, m_use, pf);
+      fence_stage1();
+    }
+    // stage 2: P.V MFMAs of step js beside the row max of step js + 1, then the curves of
+    // step js + 2
+    step_pv(js, pf);
+    const float mx = step_rowmax(snxt);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(oacc[db]));
+    if (js + 2 < nsteps) curve_step(js + 2);
+    rescale(mx);
+  };
+  int js = 0;
+  for (; js + 2 < nsteps; js += 2) {
+    iteration(js, false_t{}, sa, sb);
+    iteration(js + 1, true_t{}, sb, sa);
+  }
+  f32x16* slast = &sa;
+  if (js + 1 < nsteps) {
+    iteration(js, false_t{}, sa, sb);
+    slast = &sb;
+    ++js;
+  }
+
+  // ---- last step ------------------------------------------------------------------------------
+  {
+    const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
+    bf16x8 pf[2];
+    step_probs(*slast, m_use, pf);
+    step_pv(js, pf);
+  }
+
+  // ---- epilogue -------------------------------------------------------------------------------
+  const int row = i0 + ln;
+  const float lt = pair_sum(l_run);
+  if (row < S) {
+    const float inv = 1.f / lt;
+    uint16_t* op = a.o + (static_cast<size_t>(b) * S + row) * q_row + static_cast<size_t>(h) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * db + 8 * g4 + 4 * lh;
+        const f32x16& acc = oacc[db];
+        st8(op + d, u32x2{pack_bf16x2(acc[4 * g4] * inv, acc[4 * g4 + 1] * inv),
+                          pack_bf16x2(acc[4 * g4 + 2] * inv, acc[4 * g4 + 3] * inv)});
+      }
+    if (a.lse && lh == 0) a.lse[(static_cast<size_t>(b) * a.Hq + h) * S + row] = (m_run + fast_log2(lt)) * kLn2;
+  }
+}
+
+constexpr int kMaxLdsPerWg = 80 * 1024;   // two workgroups per CU
+
+int split_lds(int mode, int Rb) {
+  if (mode == 1) return TILE_BYTES + 4 * (Rb + 2 * PAD) * 4;
+  if (mode == 2) return TILE_BYTES + 4 * CURVE_BYTES;
+  return TILE_BYTES;
+}
+
+template <int MODE, int EF, bool ALLBAND>
+hipError_t launch_split(FwdArgs a, const uint16_t* e2, hipStream_t s) {
+  a.hpw = 4;
+  a.rows_wg = ROWS_WG;
+  a.n_qtiles = (a.S + ROWS_WG - 1) / ROWS_WG;
+  a.n_hgroups = a.Hq / 4;
+  a.longest_first = (a.window == 0 || a.window > ROWS_WG) ? 1 : 0;
+  const long long nblk = static_cast<long long>(a.n_qtiles) * a.n_hgroups * a.B;
+  if (nblk <= 0) return hipSuccess;
+  const int lds = split_lds(MODE, a.bias_range);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_split_kernel<MODE, EF, ALLBAND>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsPerWg);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((fwd_split_kernel<MODE, EF, ALLBAND>), dim3(static_cast<unsigned>(nblk)), dim3(NT), lds, s, a, e2);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Workspace bytes the split prefill needs (the converted E of r.E bias), or -1 when the shape
+// is outside its domain (head_dim 128, GQA groups of 4k heads, positive scale, LDS per
+// workgroup within half the CU).
+long long fwd_split_workspace(int D_, int G, int mode, int Rb, int R, int e_shared, int Hq, float scale) {
+  if (D_ != D || G % 4 != 0 || !(scale > 0.f)) return -1;
+  if (mode != 0 && Rb % 4 != 0) return -1;
+  if (split_lds(mode, Rb) > kMaxLdsPerWg) return -1;
+  if (mode != 2) return 0;
+  const int EF = R > 8 ? 16 : 8;
+  return static_cast<long long>(e_shared ? 1 : Hq) * (Rb + 2 * PAD + 1) * EF * 2;
+}
+
+hipError_t launch_fwd_bf16_split(const FwdArgs& a, int mode, void* workspace, hipStream_t s) {
+  if (mode != 2) return mode == 1 ? launch_split<1, 8, false>(a, nullptr, s) : launch_split<0, 8, false>(a, nullptr, s);
+  const int EF = a.R > 8 ? 16 : 8;
+  const int heads = a.e_hs ? a.Hq : 1;
+  uint16_t* e2 = static_cast<uint16_t*>(workspace);
+  const long long n = static_cast<long long>(heads) * (a.bias_range + 2 * PAD + 1) * EF;
+  const int blocks = static_cast<int>(std::min<long long>((n + 255) / 256, 4096));
+  hipLaunchKernelGGL(e2_convert_kernel, dim3(blocks), dim3(256), 0, s, a.E, a.e_hs, heads, a.R, a.bias_range,
+                     kLog2e / a.c_qk, EF, e2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool allband = a.window != 0 && a.window <= a.bias_range;
+  if (EF == 16) return allband ? launch_split<2, 16, true>(a, e2, s) : launch_split<2, 16, false>(a, e2, s);
+  return allband ? launch_split<2, 8, true>(a, e2, s) : launch_split<2, 8, false>(a, e2, s);
+}
+
+}  // namespace rba

@@ -137,7 +137,14 @@ struct BwdArgs {
   float temp_inv_log2;
 };
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, int D, int mode, hipStream_t s);
+hipError_t launch_fwd_bf16(const FwdArgs& a, int D, int mode, void* workspace, hipStream_t s);
+// Workspace bytes the bf16 prefill of this shape takes (0: none); the size query and the launch
+// share it, so both pick the same kernel.
+long long fwd_bf16_workspace(const FwdArgs& a, int D, int mode);
+// Split prefill (two workgroups per CU, sliding-window layers): workspace bytes it needs (the
+// converted E of r.E bias), or -1 outside its domain; and its launcher.
+long long fwd_split_workspace(int D, int G, int mode, int bias_range, int R, int e_shared, int Hq, float scale);
+hipError_t launch_fwd_bf16_split(const FwdArgs& a, int mode, void* workspace, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int D, int mode, hipStream_t s);
 // LDS bytes of the largest backward kernel for this shape, or -1 when it does not fit; the
 // row pitch (bf16) of the backward's curve table.
