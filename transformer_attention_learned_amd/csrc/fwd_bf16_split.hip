@@ -40,7 +40,7 @@ constexpr int NDB = D / 32;       // 32-wide head-dim blocks of O^T
 constexpr int KST = D + 8;        // K tile row stride (bf16)
 constexpr int VST = BN + 8;       // V^T tile row stride (bf16)
 constexpr int NBUF = 3;           // tile ring
-constexpr int CBW = 72;           // curve buffer row stride (bf16)
+constexpr int CBW = 68;           // curve buffer row stride (bf16): conflict-free 8-byte writes, 2-way dword reads
 constexpr int PAD = 64;           // zero distances on each side of the bias range (table rows, E rows)
 constexpr int ROWS_WG = 32;       // query rows per workgroup
 constexpr int NT = 256;           // threads per workgroup
