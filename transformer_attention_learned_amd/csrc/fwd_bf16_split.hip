@@ -8,9 +8,11 @@
 //     one wave per SIMD; a second workgroup on the CU supplies the other wave of each SIMD, so
 //     one workgroup's barriers and start-up overlap the other's key loop;
 //   * K/V tiles of 32 keys (one key step) in a ring of three LDS buffers: the tile of step j + 2
-//     is written while steps j (P.V) and j + 1 (scores) read theirs, so one barrier per step
-//     covers both hazards; its rows were fetched into registers two steps before (two register
-//     sets; V transposed on its way to LDS);
+//     is loaded while steps j (P.V) and j + 1 (scores) read theirs, so one barrier per step
+//     covers both hazards; the loads go straight from memory into LDS (16 bytes per lane, no
+//     registers, no stores), K and V row-major with the 16-byte chunks of a row XOR-swizzled so
+//     that the fragment reads are conflict-free; V^T fragments come from row-major V with the
+//     LDS transpose read (ds_read_b64_tr_b16);
 //   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: each lane owns one query row,
 //     P stays in registers; the key loop is a two-stage software pipeline (S MFMAs of step j + 1
 //     beside the exp of step j, P.V MFMAs of step j beside the row max of step j + 1);
@@ -37,8 +39,6 @@ constexpr int D = 128;
 constexpr int BN = 32;            // keys per tile (= per step)
 constexpr int NC = D / 16;        // K = 16 chunks of the head dim
 constexpr int NDB = D / 32;       // 32-wide head-dim blocks of O^T
-constexpr int KST = D + 8;        // K tile row stride (bf16)
-constexpr int VST = BN + 8;       // V^T tile row stride (bf16)
 constexpr int NBUF = 3;           // tile ring
 constexpr int CBW = 68;           // curve buffer row stride (bf16): conflict-free 8-byte writes, 2-way dword reads
 constexpr int PAD = 64;           // zero distances on each side of the bias range (table rows, E rows)
@@ -46,14 +46,24 @@ constexpr int ROWS_WG = 32;       // query rows per workgroup
 constexpr int NT = 256;           // threads per workgroup
 constexpr float kRescale = 8.f;   // lazy rescale threshold (log2 units)
 
-constexpr int KS_BYTES = BN * KST * 2;
-constexpr int VT_BYTES = D * VST * 2;
-constexpr int BUF_BYTES = KS_BYTES + VT_BYTES;
+constexpr int KT_BYTES = BN * D * 2;   // K tile: 32 rows of 256 bytes
+constexpr int VT_BYTES = BN * D * 2;   // V tile: 32 rows of 256 bytes
+constexpr int BUF_BYTES = KT_BYTES + VT_BYTES;
 constexpr int CURVE_BYTES = 32 * CBW * 2;   // per wave
 constexpr int TILE_BYTES = NBUF * BUF_BYTES;
 
-__device__ __forceinline__ int vt_pos(int x) {
-  return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at dst + 16 l
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
+}
+// LDS transpose read: within each group of 16 lanes, lane i receives 16-bit element i % 4 of the
+// 8-byte pieces addressed by lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4
+__device__ __forceinline__ u32x2 tr_read(const void* p) {
+  const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+  return __builtin_bit_cast(u32x2, x);
 }
 
 __device__ __forceinline__ void wave_sync_lds() {
@@ -123,54 +133,38 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
   const uint16_t* kbase = a.k + static_cast<size_t>(b) * S * kv_row + static_cast<size_t>(hkv) * D;
   const uint16_t* vbase = a.v + static_cast<size_t>(b) * S * kv_row + static_cast<size_t>(hkv) * D;
 
-  // ---- K/V staging, 32 keys x 128 dims each: waves 0-1 take K (512 chunks of 16 B, 4 per
-  // thread, row-major), waves 2-3 take V (128 items of 4 keys x 8 dims, transposed on the way
-  // to LDS); each thread stages one of them, so both share one set of registers.
-  u32x4 sreg[2][4];   // tiles of even / odd steps
-  const bool k_thread = wave < 2;
-  const int vt = tid & 127;
-  const int v_kg = vt & 7;
-  const int v_dg = vt >> 3;
-  // Rows at or past S read as zeros through the buffer range (rows - r0) * row bytes - head
-  // offset, which every in-range 16-byte chunk fits below.
+  // ---- K/V tiles, 32 keys x 128 dims each, loaded straight into LDS: one load moves 1 KB (4 rows
+  // of 256 bytes); wave w loads the K and the V row blocks 2w and 2w + 1.  The 16-byte chunk c of
+  // row r sits at slot c ^ (r % 16) of the row in the K tile and at slot c ^ 4 (r % 4) in the V
+  // tile, so that the fragment reads below hit distinct banks.  Rows at or past S read as zeros
+  // through the buffer range (rows - r0) * row bytes - head offset, which every in-range chunk
+  // fits below.
   const int kv_row_b = a.Hkv * D * 2;
   const int head_b = hkv * D * 2;
-  // byte offsets of the thread's four 16-byte chunks from the tile's first row: K rows
-  // it * 8 + vt / 16, V rows 4 * v_kg + s
-  const int k_voff = (vt >> 4) * kv_row_b + 16 * (vt & 15);
-  const int v_voff = 4 * v_kg * kv_row_b + 16 * v_dg;
-  const int step_off = k_thread ? 8 * kv_row_b : kv_row_b;
-  const int voff0 = k_thread ? k_voff : v_voff;
-  const uint16_t* kvbase = k_thread ? kbase : vbase;
-  auto load_tile = [&](int t, u32x4 (&reg)[4]) {   // tile t of the step sequence
-    // one buffer resource per tile: its range ends at row S, so rows past the sequence read as
-    // zeros (the head offset keeps every in-range chunk of the last row below the bound)
+  int kvo[2], vvo[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 4 * (2 * wave + q) + (lane >> 4);
+    const int sl = lane & 15;
+    kvo[q] = r * kv_row_b + 16 * (sl ^ (r & 15));
+    vvo[q] = r * kv_row_b + 16 * (sl ^ (4 * (r & 3)));
+  }
+  auto dma_tile = [&](int t, unsigned char* buf) {   // tile t of the step sequence
     const int tk0 = (t_begin + t) * BN;
     const int left = S - tk0;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(kvbase + static_cast<size_t>(tk0) * kv_row,
-                                                left > 0 ? left * kv_row_b - head_b : 0);
+    const int nrec = left > 0 ? left * kv_row_b - head_b : 0;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + static_cast<size_t>(tk0) * kv_row, nrec);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + static_cast<size_t>(tk0) * kv_row, nrec);
+    unsigned char* kdst = buf + 2 * wave * 1024;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) reg[it] = buf_ld16(rs, voff0 + it * step_off);
-  };
-  auto store_tile = [&](int t, const u32x4 (&reg)[4]) {
-    const int buf = t % NBUF;
-    uint16_t* Ks = reinterpret_cast<uint16_t*>(smem + buf * BUF_BYTES);
-    uint16_t* Vt = reinterpret_cast<uint16_t*>(smem + buf * BUF_BYTES + KS_BYTES);
-    if (k_thread) {
-#pragma unroll
-      for (int it = 0; it < 4; ++it) st16(Ks + (it * 8 + (vt >> 4)) * KST + 8 * (vt & 15), reg[it]);
-    } else {
-      const int pos = vt_pos(4 * v_kg);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
-        const uint32_t p01 = __builtin_amdgcn_perm(reg[1][w], reg[0][w], sel);
-        const uint32_t p23 = __builtin_amdgcn_perm(reg[3][w], reg[2][w], sel);
-        st8(Vt + (8 * v_dg + e) * VST + pos, u32x2{p01, p23});
-      }
+    for (int q = 0; q < 2; ++q) {
+      dma16(rk, kdst + q * 1024, kvo[q]);
+      dma16(rv, kdst + KT_BYTES + q * 1024, vvo[q]);
     }
   };
+  // this wave's loads into LDS have landed (they are its only vector-memory writes to LDS; the
+  // barrier that follows publishes them)
+  auto dma_wait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
 
   // ---- table rows of the group (MODE 1), in accumulator units, PAD zero distances each side
   const int Rp = Rb + 2 * PAD;
@@ -185,8 +179,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
   }
 
   // tiles 0 and 1 in flight first (HBM), then the query rows
-  load_tile(0, sreg[0]);
-  if (nsteps > 1) load_tile(1, sreg[1]);
+  dma_tile(0, smem);
+  if (nsteps > 1) dma_tile(1, smem + BUF_BYTES);
 
   bf16x8 qf[NC];
   {
@@ -352,21 +346,35 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
     return init;
   };
 
-  auto k_frag = [&](int js, int c) -> bf16x8 {
-    const uint16_t* Ks = reinterpret_cast<const uint16_t*>(smem + (js % NBUF) * BUF_BYTES);
-    return as_bf16x8(ld16(Ks + ln * KST + 16 * c + 8 * lh));
+  // K fragment of chunk c (dims 16 c + 8 lh .. + 7 of key ln): slot (2 c + lh) ^ (ln % 16)
+  int kaddr[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) kaddr[c] = ln * 256 + 16 * ((2 * c + lh) ^ (ln & 15));
+  // V^T fragment (dims 32 db + ln, keys of slot e = 16 kk + 4 lh + e % 4 + 8 (e / 4), the P
+  // layout): two transpose reads of 4 keys each; lane t = 4 j + q of a 16-lane group addresses
+  // key row 16 kk + 4 lh + j (+ 8), dims 32 db + 16 gq + 4 q .. + 3, i.e. half q % 2 of chunk
+  // 4 db + 2 gq + q / 2, whose slot is that chunk ^ 4 j (row % 4 = j)
+  int vaddr[NDB];
+  {
+    const int t16 = lane & 15, j = t16 >> 2, q = t16 & 3, gq = (lane >> 4) & 1;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      vaddr[db] = (4 * lh + j) * 256 + 16 * ((4 * db + 2 * gq + (q >> 1)) ^ (4 * j)) + 8 * (q & 1);
+  }
+  // (buf: the tile's LDS buffer)
+  auto k_frag = [&](const unsigned char* buf, int c) -> bf16x8 { return as_bf16x8(ld16(buf + kaddr[c])); };
+  auto v_frag = [&](const unsigned char* buf, int idx) -> bf16x8 {   // idx = 2 * db + kk
+    const unsigned char* vb = buf + KT_BYTES + vaddr[idx >> 1] + 16 * (idx & 1) * 256;
+    const u32x2 lo = tr_read(vb), hi = tr_read(vb + 8 * 256);
+    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
   };
-  auto v_frag = [&](int js, int idx) -> bf16x8 {   // idx = 2 * db + kk
-    const uint16_t* Vt = reinterpret_cast<const uint16_t*>(smem + (js % NBUF) * BUF_BYTES + KS_BYTES);
-    return as_bf16x8(ld16(Vt + (32 * (idx >> 1) + ln) * VST + 16 * (idx & 1) + 8 * lh));
-  };
-  auto step_scores = [&](int js, f32x16& acc, auto spec_c) {
+  auto step_scores = [&](const unsigned char* buf, f32x16& acc, auto spec_c) {
     constexpr bool SPEC = decltype(spec_c)::value;
-    bf16x8 kf = k_frag(js, 0);
+    bf16x8 kf = k_frag(buf, 0);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       bf16x8 kn = kf;
-      if (c + 1 < NC) kn = k_frag(js, c + 1);
+      if (c + 1 < NC) kn = k_frag(buf, c + 1);
       if (c == 0 && !SPEC) {
         const f32x16 zero = {};
         acc = mfma32(kf, qf[0], zero);
@@ -376,12 +384,12 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
       kf = kn;
     }
   };
-  auto step_pv = [&](int js, const bf16x8 (&pf)[2]) {
-    bf16x8 vf = v_frag(js, 0);
+  auto step_pv = [&](const unsigned char* buf, const bf16x8 (&pf)[2]) {
+    bf16x8 vf = v_frag(buf, 0);
 #pragma unroll
     for (int idx = 0; idx < 2 * NDB; ++idx) {
       bf16x8 vn = vf;
-      if (idx + 1 < 2 * NDB) vn = v_frag(js, idx + 1);
+      if (idx + 1 < 2 * NDB) vn = v_frag(buf, idx + 1);
       oacc[idx >> 1] = mfma32(vf, pf[idx & 1], oacc[idx >> 1]);
       vf = vn;
     }
@@ -428,10 +436,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
 
   // ---- prologue: tiles 0 and 1 in LDS, tile 2 in flight, curves and scores of step 0 ---------
   if (MODE == 2 && (ALLBAND || step_inband(0))) e_fetch(0);
-  store_tile(0, sreg[0]);
-  if (nsteps > 1) store_tile(1, sreg[1]);
-  if (nsteps > 2) load_tile(2, sreg[0]);
-  if (nsteps > 3) load_tile(3, sreg[1]);
+  dma_wait();
   __syncthreads();
 
   f32x16 sa, sb;
@@ -440,9 +445,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
     if (MODE == 2 && (ALLBAND || step_inband(1))) e_fetch(1);
     if (step_special(0)) {
       sa = step_init(0);
-      step_scores(0, sa, true_t{});
+      step_scores(smem, sa, true_t{});
     } else {
-      step_scores(0, sa, false_t{});
+      step_scores(smem, sa, false_t{});
     }
     const float mx = step_rowmax(sa);
     curve_step(1);
@@ -450,15 +455,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
   }
 
   // ---- key loop: iteration js consumes the scores of step js and produces those of js + 1 ----
-  // (ODD: js odd, so that the register set of tile js + 2 is a compile-time index)
-  auto iteration = [&](int js, auto odd_c, f32x16& scur, f32x16& snxt) {
-    constexpr int RS = decltype(odd_c)::value ? 1 : 0;   // register set of tiles js + 2 and js + 4
-    // tile js + 1 is in LDS (written a step ago); every wave is done with tile js - 1, whose
-    // buffer now takes tile js + 2 (its rows were fetched two steps ago); the freed registers
-    // take tile js + 4
-    __syncthreads();
-    if (js + 2 < nsteps) store_tile(js + 2, sreg[RS]);
-    if (js + 4 < nsteps) load_tile(js + 4, sreg[RS]);
+  // One iteration on three distinct buffers (restrict: the compiler then knows that the loads
+  // into dbuf do not feed the reads of tiles js and js + 1, and does not wait for them there).
+  auto iteration_body = [&](int js, f32x16& scur, f32x16& snxt, unsigned char* __restrict__ dbuf,
+                            const unsigned char* __restrict__ cbuf_t, const unsigned char* __restrict__ nbuf_t) {
+    if (js + 2 < nsteps) dma_tile(js + 2, dbuf);
 
     const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
     bf16x8 pf[2];
@@ -469,31 +470,39 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
     // stage 1: S MFMAs of step js + 1 beside the exp / pack of step js
     if (step_special(js + 1)) {
       snxt = step_init(js + 1);
-      step_scores(js + 1, snxt, true_t{});
+      step_scores(nbuf_t, snxt, true_t{});
       step_probs(scur, m_use, pf);
       fence_stage1();
     } else {
-      step_scores(js + 1, snxt, false_t{});
+      step_scores(nbuf_t, snxt, false_t{});
       step_probs(scur, m_use, pf);
       fence_stage1();
     }
     // stage 2: P.V MFMAs of step js beside the row max of step js + 1, then the curves of
     // step js + 2
-    step_pv(js, pf);
+    step_pv(cbuf_t, pf);
     const float mx = step_rowmax(snxt);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(oacc[db]));
     if (js + 2 < nsteps) curve_step(js + 2);
     rescale(mx);
   };
+  auto iteration = [&](int js, f32x16& scur, f32x16& snxt) {
+    // tile js + 1 (loaded a step ago) is in LDS once every wave's loads have landed; every wave
+    // is then also done with tile js - 1, whose buffer takes tile js + 2
+    dma_wait();
+    __syncthreads();
+    iteration_body(js, scur, snxt, smem + ((js + 2) % NBUF) * BUF_BYTES, smem + (js % NBUF) * BUF_BYTES,
+                   smem + ((js + 1) % NBUF) * BUF_BYTES);
+  };
   int js = 0;
   for (; js + 2 < nsteps; js += 2) {
-    iteration(js, false_t{}, sa, sb);
-    iteration(js + 1, true_t{}, sb, sa);
+    iteration(js, sa, sb);
+    iteration(js + 1, sb, sa);
   }
   f32x16* slast = &sa;
   if (js + 1 < nsteps) {
-    iteration(js, false_t{}, sa, sb);
+    iteration(js, sa, sb);
     slast = &sb;
     ++js;
   }
@@ -503,7 +512,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
     const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
     bf16x8 pf[2];
     step_probs(*slast, m_use, pf);
-    step_pv(js, pf);
+    step_pv(smem + (js % NBUF) * BUF_BYTES, pf);
   }
 
   // ---- epilogue -------------------------------------------------------------------------------
