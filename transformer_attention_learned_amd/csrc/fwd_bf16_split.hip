@@ -75,21 +75,25 @@ __device__ __forceinline__ void wave_sync_lds() {
 // E (fp32 [heads, R, Rb], head h at E + h * e_hs) -> bf16 rows [heads][Rb + 2 PAD + 1][EF]:
 // entry (h, PAD + d, f) = E[h, f, d] / scale for 0 <= d < Rb and f < R, zero elsewhere (the pads
 // and the features past R), so that every read of the kernels below is in range and unguarded.
-__global__ void e2_convert_kernel(const float* __restrict__ E, long long e_hs, int heads, int R, int Rb,
+// One thread per (head, row) and 8 features: one 16-byte store; grid.y = head, grid.z = feature half.
+__global__ void e2_convert_kernel(const float* __restrict__ E, long long e_hs, int R, int Rb,
                                   float inv_scale, int EF, uint16_t* __restrict__ e2) {
   const int rows = Rb + 2 * PAD + 1;
-  const long long n = static_cast<long long>(heads) * rows * EF;
-  for (long long i = blockIdx.x * static_cast<long long>(blockDim.x) + threadIdx.x; i < n;
-       i += static_cast<long long>(gridDim.x) * blockDim.x) {
-    const int f = static_cast<int>(i % EF);
-    const long long hp = i / EF;
-    const int p = static_cast<int>(hp % rows);
-    const int h = static_cast<int>(hp / rows);
-    const int d = p - PAD;
-    float v = 0.f;
-    if (d >= 0 && d < Rb && f < R) v = E[h * e_hs + static_cast<long long>(f) * Rb + d] * inv_scale;
-    e2[i] = f32_to_bf16(v);
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= rows) return;
+  const int h = blockIdx.y;
+  const int f0 = 8 * blockIdx.z;
+  const int d = p - PAD;
+  const bool live = d >= 0 && d < Rb;
+  const float* eh = E + h * e_hs + static_cast<long long>(f0) * Rb + d;
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float x0 = (live && f0 + 2 * k < R) ? eh[static_cast<long long>(2 * k) * Rb] * inv_scale : 0.f;
+    const float x1 = (live && f0 + 2 * k + 1 < R) ? eh[static_cast<long long>(2 * k + 1) * Rb] * inv_scale : 0.f;
+    w[k] = static_cast<uint32_t>(f32_to_bf16(x0)) | (static_cast<uint32_t>(f32_to_bf16(x1)) << 16);
   }
+  st16(e2 + (static_cast<size_t>(h) * rows + p) * EF + f0, u32x4{w[0], w[1], w[2], w[3]});
 }
 
 // MODE 0 none, 1 table, 2 r.E (EF = 8 or 16 features per E row); ALLBAND: every visible key is
@@ -569,7 +573,7 @@ hipError_t launch_split(FwdArgs a, const uint16_t* e2, hipStream_t s) {
 // is outside its domain (head_dim 128, GQA groups of 4k heads, positive scale, LDS per
 // workgroup within half the CU).
 long long fwd_split_workspace(int D_, int G, int mode, int Rb, int R, int e_shared, int Hq, float scale) {
-  if (D_ != D || G % 4 != 0 || !(scale > 0.f)) return -1;
+  if (D_ != D || G % 4 != 0 || !(scale > 0.f) || Hq > 65535) return -1;
   if (mode != 0 && Rb % 4 != 0) return -1;
   if (split_lds(mode, Rb) > kMaxLdsPerWg) return -1;
   if (mode != 2) return 0;
@@ -582,10 +586,9 @@ hipError_t launch_fwd_bf16_split(const FwdArgs& a, int mode, void* workspace, hi
   const int EF = a.R > 8 ? 16 : 8;
   const int heads = a.e_hs ? a.Hq : 1;
   uint16_t* e2 = static_cast<uint16_t*>(workspace);
-  const long long n = static_cast<long long>(heads) * (a.bias_range + 2 * PAD + 1) * EF;
-  const int blocks = static_cast<int>(std::min<long long>((n + 255) / 256, 4096));
-  hipLaunchKernelGGL(e2_convert_kernel, dim3(blocks), dim3(256), 0, s, a.E, a.e_hs, heads, a.R, a.bias_range,
-                     kLog2e / a.c_qk, EF, e2);
+  const int rows = a.bias_range + 2 * PAD + 1;
+  hipLaunchKernelGGL(e2_convert_kernel, dim3((rows + 255) / 256, heads, EF / 8), dim3(256), 0, s, a.E, a.e_hs,
+                     a.R, a.bias_range, kLog2e / a.c_qk, EF, e2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool allband = a.window != 0 && a.window <= a.bias_range;
