@@ -169,6 +169,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
   // this wave's loads into LDS have landed (they are its only vector-memory writes to LDS; the
   // barrier that follows publishes them)
   auto dma_wait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
+  // the same inside the key loop when the only loads issued after the awaited tile are the two
+  // E-row loads of a later step: vector-memory loads complete in issue order, so vmcnt(2)
+  // leaves those in flight instead of waiting out their latency before the barrier
+  auto dma_wait_but2 = [&]() { __builtin_amdgcn_s_waitcnt(0x0F72); };   // vmcnt(2)
 
   // ---- table rows of the group (MODE 1), in accumulator units, PAD zero distances each side
   const int Rp = Rb + 2 * PAD;
@@ -461,9 +465,15 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
   // ---- key loop: iteration js consumes the scores of step js and produces those of js + 1 ----
   // One iteration on three distinct buffers (restrict: the compiler then knows that the loads
   // into dbuf do not feed the reads of tiles js and js + 1, and does not wait for them there).
+  // INNER: step js + 2 is known to exist (inside the unrolled loop), so the tile load and the
+  // curve step are unconditional and the compiler counts the loads in flight exactly (a
+  // conditional load makes it wait for all of them before the next use of the E rows).
   auto iteration_body = [&](int js, f32x16& scur, f32x16& snxt, unsigned char* __restrict__ dbuf,
-                            const unsigned char* __restrict__ cbuf_t, const unsigned char* __restrict__ nbuf_t) {
-    if (js + 2 < nsteps) dma_tile(js + 2, dbuf);
+                            const unsigned char* __restrict__ cbuf_t, const unsigned char* __restrict__ nbuf_t,
+                            auto inner_c) {
+    constexpr bool INNER = decltype(inner_c)::value;
+    const bool more = INNER || js + 2 < nsteps;
+    if (more) dma_tile(js + 2, dbuf);
 
     const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
     bf16x8 pf[2];
@@ -488,27 +498,38 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
     const float mx = step_rowmax(snxt);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(oacc[db]));
-    if (js + 2 < nsteps) curve_step(js + 2);
+    if (more) curve_step(js + 2);
     rescale(mx);
   };
-  auto iteration = [&](int js, f32x16& scur, f32x16& snxt) {
+  auto iteration = [&](int js, f32x16& scur, f32x16& snxt, auto inner_c) {
     // tile js + 1 (loaded a step ago) is in LDS once every wave's loads have landed; every wave
-    // is then also done with tile js - 1, whose buffer takes tile js + 2
-    dma_wait();
+    // is then also done with tile js - 1, whose buffer takes tile js + 2.  The loads issued
+    // after tile js + 1 are the E rows of step js + 2 when that step is in band (the curve step
+    // of js + 1 fetched them), nothing else.
+    if (MODE == 2 && (ALLBAND || step_inband(js + 2)))
+      dma_wait_but2();
+    else
+      dma_wait();
     __syncthreads();
     iteration_body(js, scur, snxt, smem + ((js + 2) % NBUF) * BUF_BYTES, smem + (js % NBUF) * BUF_BYTES,
-                   smem + ((js + 1) % NBUF) * BUF_BYTES);
+                   smem + ((js + 1) % NBUF) * BUF_BYTES, inner_c);
   };
   int js = 0;
-  for (; js + 2 < nsteps; js += 2) {
-    iteration(js, sa, sb);
-    iteration(js + 1, sb, sa);
+  for (; js + 3 < nsteps; js += 2) {
+    iteration(js, sa, sb, true_t{});
+    iteration(js + 1, sb, sa, true_t{});
   }
+  // one or two iterations left (nsteps - js = 2 or 3), or none
   f32x16* slast = &sa;
   if (js + 1 < nsteps) {
-    iteration(js, sa, sb);
+    iteration(js, sa, sb, false_t{});
     slast = &sb;
     ++js;
+    if (js + 1 < nsteps) {
+      iteration(js, sb, sa, false_t{});
+      slast = &sa;
+      ++js;
+    }
   }
 
   // ---- last step ------------------------------------------------------------------------------
