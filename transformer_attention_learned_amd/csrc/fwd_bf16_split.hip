@@ -268,11 +268,12 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
     // the E rows read stay inside the padded rows (distances -PAD .. Rb + PAD)
     return min(max(step_c(js), -33), Rb + 31);
   };
-  auto e_fetch = [&](int js) {
+  auto e_fetch_to = [&](int js, u32x4& lo, u32x4& hi) {
     const uint16_t* ep = e2h + (curve_c(js) - 31 + ln) * EF + 8 * lh;
-    ef_lo = ld16(ep);
-    ef_hi = ld16(ep + 32 * EF);
+    lo = ld16(ep);
+    hi = ld16(ep + 32 * EF);
   };
+  auto e_fetch = [&](int js) { e_fetch_to(js, ef_lo, ef_hi); };
   // curves of step js from the fetched E rows: two MFMAs over the R features give the 64
   // distances c - 31 .. c + 32 for every query row; written unskewed to the wave's buffer
   // (row = query, column = distance - (c - 31)), then each lane's diagonal read back into cr
@@ -442,15 +443,19 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
   using false_t = std::integral_constant<bool, false>;
   using true_t = std::integral_constant<bool, true>;
 
-  // ---- prologue: tiles 0 and 1 in LDS, tile 2 in flight, curves and scores of step 0 ---------
+  // ---- prologue: tiles 0 and 1, the query rows and the E rows of steps 0 and 1 requested
+  // together (one memory round trip), then the curves and scores of step 0 ---------------------
+  u32x4 ef1_lo = {0u, 0u, 0u, 0u}, ef1_hi = {0u, 0u, 0u, 0u};
   if (MODE == 2 && (ALLBAND || step_inband(0))) e_fetch(0);
+  if (MODE == 2 && (ALLBAND || step_inband(1))) e_fetch_to(1, ef1_lo, ef1_hi);
   dma_wait();
   __syncthreads();
 
   f32x16 sa, sb;
   {
     if (MODE == 2 && (ALLBAND || step_inband(0))) curve_issue(0);
-    if (MODE == 2 && (ALLBAND || step_inband(1))) e_fetch(1);
+    ef_lo = ef1_lo;
+    ef_hi = ef1_hi;
     if (step_special(0)) {
       sa = step_init(0);
       step_scores(smem, sa, true_t{});
@@ -501,42 +506,49 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
     if (more) curve_step(js + 2);
     rescale(mx);
   };
-  auto iteration = [&](int js, f32x16& scur, f32x16& snxt, auto inner_c) {
-    // tile js + 1 (loaded a step ago) is in LDS once every wave's loads have landed; every wave
-    // is then also done with tile js - 1, whose buffer takes tile js + 2.  The loads issued
-    // after tile js + 1 are the E rows of step js + 2 when that step is in band (the curve step
-    // of js + 1 fetched them), nothing else.
+  // tile js + 1 (loaded a step ago) is in LDS once every wave's loads have landed; every wave
+  // is then also done with tile js - 1, whose buffer takes tile js + 2.  The loads issued after
+  // tile js + 1 are the E rows of step js + 2 when that step is in band (the curve step of
+  // js + 1 fetched them), nothing else.
+  auto iteration_wait = [&](int js) {
     if (MODE == 2 && (ALLBAND || step_inband(js + 2)))
       dma_wait_but2();
     else
       dma_wait();
     __syncthreads();
-    iteration_body(js, scur, snxt, smem + ((js + 2) % NBUF) * BUF_BYTES, smem + (js % NBUF) * BUF_BYTES,
-                   smem + ((js + 1) % NBUF) * BUF_BYTES, inner_c);
+  };
+  // Tile t sits in ring buffer t % 3.  In the unrolled loop the buffer of each iteration is a
+  // compile-time constant (SL = js % 3), so every fragment read addresses LDS as a per-lane
+  // offset plus an immediate, with no address arithmetic per step.
+  auto iteration_at = [&](int js, f32x16& scur, f32x16& snxt, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
+    iteration_wait(js);
+    iteration_body(js, scur, snxt, smem + ((SL + 2) % NBUF) * BUF_BYTES, smem + SL * BUF_BYTES,
+                   smem + ((SL + 1) % NBUF) * BUF_BYTES, true_t{});
+  };
+  auto iteration = [&](int js, f32x16& scur, f32x16& snxt) {
+    iteration_wait(js);
+    const int sl = js % NBUF;
+    iteration_body(js, scur, snxt, smem + ((sl + 2) % NBUF) * BUF_BYTES, smem + sl * BUF_BYTES,
+                   smem + ((sl + 1) % NBUF) * BUF_BYTES, false_t{});
   };
   int js = 0;
-  for (; js + 3 < nsteps; js += 2) {
-    iteration(js, sa, sb, true_t{});
-    iteration(js + 1, sb, sa, true_t{});
+  for (; js + 4 < nsteps; js += 3) {
+    iteration_at(js, sa, sb, std::integral_constant<int, 0>{});
+    iteration_at(js + 1, sb, sa, std::integral_constant<int, 1>{});
+    iteration_at(js + 2, sa, sb, std::integral_constant<int, 2>{});
+    sa = sb;   // the scores of step js + 3 back in the first set
   }
-  // one or two iterations left (nsteps - js = 2 or 3), or none
-  f32x16* slast = &sa;
-  if (js + 1 < nsteps) {
-    iteration(js, sa, sb, false_t{});
-    slast = &sb;
-    ++js;
-    if (js + 1 < nsteps) {
-      iteration(js, sb, sa, false_t{});
-      slast = &sa;
-      ++js;
-    }
+  for (; js + 1 < nsteps; ++js) {
+    iteration(js, sa, sb);
+    sa = sb;
   }
 
   // ---- last step ------------------------------------------------------------------------------
   {
     const float m_use = (m_run == NEG_INF) ? 0.f : m_run;
     bf16x8 pf[2];
-    step_probs(*slast, m_use, pf);
+    step_probs(sa, m_use, pf);
     step_pv(smem + (js % NBUF) * BUF_BYTES, pf);
   }
 
