@@ -275,12 +275,15 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
   };
   auto e_fetch = [&](int js) { e_fetch_to(js, ef_lo, ef_hi); };
   // curves of step js from the fetched E rows: two MFMAs over the R features give the 64
-  // distances c - 31 .. c + 32 for every query row; written unskewed to the wave's buffer
-  // (row = query, column = distance - (c - 31)), then each lane's diagonal read back into cr
-  auto curve_issue = [&](int js) {
+  // distances c - 31 .. c + 32 for every query row (curve_mfma); written unskewed to the wave's
+  // buffer (row = query, column = distance - (c - 31)), then each lane's diagonal read back
+  // into cr (curve_store)
+  auto curve_mfma = [&](f32x16& lo, f32x16& hi) {
     const f32x16 zero = {};
-    const f32x16 lo = mfma32(as_bf16x8(ef_lo), rf, zero);
-    const f32x16 hi = mfma32(as_bf16x8(ef_hi), rf, zero);
+    lo = mfma32(as_bf16x8(ef_lo), rf, zero);
+    hi = mfma32(as_bf16x8(ef_hi), rf, zero);
+  };
+  auto curve_store = [&](const f32x16& lo, const f32x16& hi) {
     uint16_t* wp = cbuf + ln * CBW + 4 * lh;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -297,6 +300,11 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
       cr[3 * g4 + 1] = rd[13 - 4 * g4];
       cr[3 * g4 + 2] = rd[14 - 4 * g4];
     }
+  };
+  auto curve_issue = [&](int js) {
+    f32x16 lo, hi;
+    curve_mfma(lo, hi);
+    curve_store(lo, hi);
   };
   // the curve work of step js (when it has any), and the E rows of step js + 1
   auto curve_step = [&](int js) {
@@ -394,14 +402,19 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
     }
   };
   auto step_pv = [&](const unsigned char* buf, const bf16x8 (&pf)[2]) {
-    bf16x8 vf = v_frag(buf, 0);
+    bf16x8 vf[2 * NDB];
 #pragma unroll
-    for (int idx = 0; idx < 2 * NDB; ++idx) {
-      bf16x8 vn = vf;
-      if (idx + 1 < 2 * NDB) vn = v_frag(buf, idx + 1);
-      oacc[idx >> 1] = mfma32(vf, pf[idx & 1], oacc[idx >> 1]);
-      vf = vn;
-    }
+    for (int idx = 0; idx < 2 * NDB; ++idx) vf[idx] = v_frag(buf, idx);
+#pragma unroll
+    for (int idx = 0; idx < 2 * NDB; ++idx) oacc[idx >> 1] = mfma32(vf[idx], pf[idx & 1], oacc[idx >> 1]);
+    // V fragments read one head-dim block ahead of the MFMAs that consume them (left alone,
+    // the scheduler reuses one set of registers and waits out each read)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
   auto step_probs = [&](const f32x16& acc, float m_use, bf16x8 (&pf)[2]) {
     float psum = l_run;
@@ -498,13 +511,29 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
       fence_stage1();
     }
     // stage 2: P.V MFMAs of step js beside the row max of step js + 1, then the curves of
-    // step js + 2
-    step_pv(cbuf_t, pf);
-    const float mx = step_rowmax(snxt);
+    // step js + 2.  In the branch-free loop the two curve MFMAs go in ahead of the P.V MFMAs
+    // (pinned there: the compiler would otherwise sink them to their use), so that their
+    // results are ready when the conversions and LDS writes that follow the P.V MFMAs need them.
+    if (MODE == 2 && ALLBAND && INNER) {
+      f32x16 clo, chi;
+      curve_mfma(clo, chi);
+      asm volatile("" : "+v"(clo), "+v"(chi), "+v"(pf[0]), "+v"(pf[1]));
+      __builtin_amdgcn_sched_barrier(0);
+      step_pv(cbuf_t, pf);
+      const float mx = step_rowmax(snxt);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(oacc[db]));
-    if (more) curve_step(js + 2);
-    rescale(mx);
+      for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(oacc[db]));
+      curve_store(clo, chi);
+      e_fetch(js + 3);
+      rescale(mx);
+    } else {
+      step_pv(cbuf_t, pf);
+      const float mx = step_rowmax(snxt);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) asm volatile("" : "+v"(oacc[db]));
+      if (more) curve_step(js + 2);
+      rescale(mx);
+    }
   };
   // tile js + 1 (loaded a step ago) is in LDS once every wave's loads have landed; every wave
   // is then also done with tile js - 1, whose buffer takes tile js + 2.  The loads issued after
