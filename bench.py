@@ -7,6 +7,7 @@ TFLOP/s (4*D flops per visible (query head, key) pair), the roofline of the
 prefill kernel and the float64 oracle timed on this host as a CPU baseline.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+  (default warmup: as many steps as fill 0.3 s, so that the clocks have settled)
                   [--no-cpu-baseline] [--cpu-seconds T]
 
 Other workloads (--workload): global_prefill, long_global_prefill,
@@ -164,7 +165,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps; default: as many as fill 0.3 s (at least 10), "
+                         "long enough for the GPU clocks to settle at their sustained level")
     ap.add_argument("--workload", default="local_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -284,8 +287,21 @@ def main():
             hbm_bytes = 2.0 * w.B * nvis * w.Hkv * (w.D // 2 + w.D // 32)
         kind = "decode"
 
-    for _ in range(args.warmup):
-        step()
+    if args.warmup is None:
+        # The GPU raises its clocks only under sustained load: a few milliseconds of warmup
+        # times the kernels well below their steady-state speed (about 15 % slower for the
+        # local prefill).  Warm up for 0.3 s, synchronising every 10 steps so that wall time
+        # tracks GPU time.
+        t0, n = time.perf_counter(), 0
+        while n < 10 or time.perf_counter() - t0 < 0.3:
+            step()
+            n += 1
+            if n % 10 == 0:
+                torch.cuda.synchronize()
+        args.warmup = n
+    else:
+        for _ in range(args.warmup):
+            step()
     torch.cuda.synchronize()
     # one event before every step and one after the last: the whole span gives ms_per_step, the
     # gaps give the median and minimum step
