@@ -135,6 +135,9 @@ SWEEP = [
     dict(S=333, mode="table", bias_range=100, temp_len=2),
     dict(S=1100, mode="rproj_shared", R=16, bias_range=1024, logit_scale="inv_d", temp_len=256),
     dict(S=260, D=64, temp_len=50), dict(S=190, Hq=6, Hkv=2, temp_len=20, mode="table"),
+    # table ranges too long for the 32-row kernel's LDS take the 64-row kernel
+    dict(S=2200, mode="table", bias_range=2048, Hq=8, Hkv=2),
+    dict(S=2200, mode="table", window=600, bias_range=2048, Hq=8, Hkv=2),
     # windows inside the bias range with more work items (batch x head group x 64-row tile)
     # than CUs: the kernel walks runs of items per workgroup, runs cross head groups and batch
     # entries, tails are ragged

@@ -397,13 +397,13 @@ hipError_t launch_mode(const FwdArgs& a, int mode, hipStream_t s) {
 namespace {
 // The two MFMA kernels address K and V through 32-bit buffer offsets within one sequence.
 bool kv_off32(const FwdArgs& a, int D) { return static_cast<long long>(a.S) * a.Hkv * D * 2 < (1LL << 31); }
-// Sliding-window (local) layers, the input-dependent bias and layers without bias take the
-// split kernel, whose 32-row workgroups pair up on a CU (and which reads E rows converted once
-// per call); full causal layers with the bias table keep one workgroup of 64 rows per CU, whose
-// long key loops amortise its start-up (measured faster there: 986 against 950 TF/s at
-// S = 32768, while without bias the split kernel wins, 954 against 911 TF/s at S = 16384).
+// Every layer the split kernel's domain covers takes it: its 32-row workgroups pair up on a CU
+// (and it reads E rows converted once per call); measured faster than the 64-row kernel for
+// sliding-window and full causal layers alike (full causal with the bias table at S = 32768:
+// 4.08 against 4.43 ms).  The 64-row kernel remains for shapes outside that domain (a table
+// range too long for the split kernel's LDS).
 bool use_split(const FwdArgs& a, int D, int mode) {
-  return (a.window != 0 || mode != 1) && kv_off32(a, D) &&
+  return kv_off32(a, D) &&
          fwd_split_workspace(D, a.G, mode, a.bias_range, a.R, a.e_hs == 0, a.Hq, a.c_qk) >= 0;
 }
 }  // namespace
