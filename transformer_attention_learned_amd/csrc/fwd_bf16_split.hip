@@ -243,20 +243,18 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
   uint16_t* cbuf = (MODE == 2) ? reinterpret_cast<uint16_t*>(smem + TILE_BYTES) + wave * (CURVE_BYTES / 2) : nullptr;
 
   // Step js covers keys j0 .. j0 + 31 with j0 = (t_begin + js) * BN; delta = c + n - m with
-  // c = i0 - j0, n the lane's row, m the key within the step.
+  // c = i0 - j0, n the lane's row, m the key within the step.  For js >= 0 the step has visible
+  // keys exactly when js < nsteps; it crosses the diagonal only as the last step (c = 0), the
+  // window's far edge only among the first js_w steps (c + 31 >= W), and it is in band from
+  // step js_band on (c - 31 < Rb).  The thresholds are computed once, so that the per-step
+  // flags are single compares.
   auto step_c = [&](int js) { return i0 - (t_begin + js) * BN; };
-  auto step_on = [&](int js) {
-    const int j0 = (t_begin + js) * BN;
-    const int c = i0 - j0;
-    bool on = (c + 31 >= 0) && (j0 < S) && (i0 < S);
-    if (W) on = on && (c - 31 < W);
-    return on;
-  };
-  auto step_inband = [&](int js) { return MODE != 0 && step_on(js) && step_c(js) - 31 < Rb; };
-  auto step_edge = [&](int js) {
-    const int c = step_c(js);
-    return !step_on(js) || (c - 31 < 0) || (W && c + 31 >= W);
-  };
+  const int c_first = i0 - t_begin * BN;
+  const int js_w = (W && c_first + 31 >= W) ? (c_first + 31 - W) / BN + 1 : 0;
+  const int js_band = (c_first - 31 < Rb) ? 0 : (c_first - 31 - Rb) / BN + 1;
+  auto step_on = [&](int js) { return js < nsteps; };
+  auto step_inband = [&](int js) { return MODE != 0 && js < nsteps && js >= js_band; };
+  auto step_edge = [&](int js) { return js >= nsteps - 1 || js < js_w; };
 
   // ---- r.E curves: E rows of step js are loaded one step before its curves are formed
   u32x4 ef_lo = {0u, 0u, 0u, 0u}, ef_hi = {0u, 0u, 0u, 0u};
