@@ -351,11 +351,13 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
     }
     if (step_edge(js)) {
       asm volatile("; edge step: mask" ::: "memory");
+      // visible iff 0 <= d < W (d >= 0 without a window): one unsigned compare per element
+      const int dbase = c + ln - 4 * lh;
+      const unsigned lim = !on ? 0u : (W ? static_cast<unsigned>(W) : 0x80000000u);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int m = 8 * (i >> 2) + 4 * lh + (i & 3);
-        const int d = c + ln - m;
-        if (!on || d < 0 || (W && d >= W)) init[i] = NEG_INF;
+        const int d = dbase - (8 * (i >> 2) + (i & 3));
+        if (static_cast<unsigned>(d) >= lim) init[i] = NEG_INF;
       }
     }
     return init;
