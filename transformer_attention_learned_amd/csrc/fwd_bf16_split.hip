@@ -15,7 +15,10 @@
 //     LDS transpose read (ds_read_b64_tr_b16);
 //   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: each lane owns one query row,
 //     P stays in registers; the key loop is a two-stage software pipeline (S MFMAs of step j + 1
-//     beside the exp of step j, P.V MFMAs of step j beside the row max of step j + 1);
+//     beside the exp of step j, P.V MFMAs of step j beside the row max of step j + 1), unrolled
+//     by three so that every iteration's ring buffer is a compile-time constant (fragment reads
+//     are a per-lane register offset plus an immediate); per-step flags (edge, band) are
+//     compares against thresholds computed once per workgroup;
 //   * bias and masks enter through the S accumulator's start values; lazy rescaling of O;
 //   * table bias: the group's table rows in LDS, zero-padded, read with immediate offsets;
 //   * input-dependent bias r_i . E[h, :, delta]: E in bf16, distance-major rows of EF features
