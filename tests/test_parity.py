@@ -135,6 +135,11 @@ SWEEP = [
     dict(S=333, mode="table", bias_range=100, temp_len=2),
     dict(S=1100, mode="rproj_shared", R=16, bias_range=1024, logit_scale="inv_d", temp_len=256),
     dict(S=260, D=64, temp_len=50), dict(S=190, Hq=6, Hkv=2, temp_len=20, mode="table"),
+    # windows and ranges off the 32-key step grid, larger than the sequence, or equal (every
+    # visible key in band: the branch-free r.E path with its first steps cut by the window)
+    dict(S=300, window=1000, bias_range=2000), dict(S=333, window=100, bias_range=100),
+    dict(S=333, window=33, bias_range=40, mode="table"), dict(S=290, window=95, bias_range=95, R=16),
+    dict(S=450, window=200, bias_range=31), dict(S=450, window=200, bias_range=33, mode="none"),
     # table ranges too long for the 32-row kernel's LDS take the 64-row kernel
     dict(S=2200, mode="table", bias_range=2048, Hq=8, Hkv=2),
     dict(S=2200, mode="table", window=600, bias_range=2048, Hq=8, Hkv=2),
