@@ -101,7 +101,8 @@ def version() -> str:
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: the c_void_p argtypes convert it (and None to NULL) without a wrapper object
+    return None if t is None else t.data_ptr()
 
 
 def _dtype_id(t):
@@ -122,14 +123,19 @@ def _check(t, name, *, dtype=None, ndim=None, device=None):
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if device is not None and t.device != device:
+    # device check by index (get_device: -1 on the host), cheaper than comparing device objects
+    if device is not None and t.get_device() != (-1 if device.index is None else device.index):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
 def _stream_handle(device, stream):
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return stream.cuda_stream
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None and device.index is not None:
+        return raw(device.index)   # the current stream's handle, without a Stream object
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _bias_args(mode, table, r, E, Hq, act_dtype, dev):
