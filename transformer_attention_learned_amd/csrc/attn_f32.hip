@@ -1,12 +1,16 @@
 // fp32 attention with a relative-position bias on the vector ALUs (no bf16
-// anywhere): used for fp32 prefill and fp32 decode.  One wave handles 64
-// consecutive query rows of one head; key tiles of 64 rows are staged in LDS
-// and each lane runs an online softmax over the keys its row can see.
+// anywhere): used for fp32 prefill and fp32 decode.  A workgroup of 4 waves handles 64
+// consecutive query rows of one head (lane = row); key tiles of 64 rows are staged in LDS, and
+// wave w runs an online softmax over the keys 4 i + w of each tile that its rows can see, so a
+// short problem still spreads its per-row key loop over four waves.  The four partial results
+// (running max, sum and accumulator, in the log2 domain) are merged through LDS at the end.
 //
 // Same operation as the bf16 kernels: logit = scale * q.k + bias(delta), bias
 // zero at and beyond the range, causal / sliding-window visibility
 // ("Learned Relative-Position Bias", section "Standard Relative Bias
 // (T5-style)"; "Thinking Machines dropped RoPE", steps 3-5).
+
+#include <algorithm>
 
 #include "rba_device.h"
 #include "rba_internal.h"
@@ -16,13 +20,23 @@ namespace rba {
 namespace {
 
 constexpr int TK = 64;
+constexpr int NW = 4;   // waves per workgroup, splitting each tile's keys
 
 template <int D>
-__global__ __launch_bounds__(64) void attn_f32_kernel(F32Args a) {
-  __shared__ float Kt[TK][D + 1];
-  __shared__ float Vt[TK][D + 1];
+constexpr int f32_lds_floats() {
+  // K and V tiles during the key loop; the merge buffers after it
+  return std::max(2 * TK * (D + 1), 2 * NW * 64 + (NW - 1) * 64 * 33);
+}
 
-  const int lane = threadIdx.x;
+template <int D>
+__global__ __launch_bounds__(64 * NW) void attn_f32_kernel(F32Args a) {
+  __shared__ float sm[f32_lds_floats<D>()];
+  float (*Kt)[D + 1] = reinterpret_cast<float (*)[D + 1]>(sm);
+  float (*Vt)[D + 1] = reinterpret_cast<float (*)[D + 1]>(sm + TK * (D + 1));
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qtiles = (a.Sq + 63) / 64;
   const int qt = blockIdx.x % qtiles;
   const int h = (blockIdx.x / qtiles) % a.Hq;
@@ -45,9 +59,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Args a) {
 #pragma unroll
     for (int f = 0; f < 16; ++f) rv[f] = (f < a.R && live) ? rp[f] : 0.f;
   }
+  // running max and sum in the log2 domain (logit x log2(e))
   float m = -INFINITY, l = 0.f;
   // context-length temperature of this query (keys 0..pos exist), on q.k and bias alike
   const float tq = temp_factor(visible_keys(pos, a.window), a.temp_len, a.temp_inv_log2);
+  const float c2 = tq * kLog2e;
 
   // keys any row of this tile can see
   const int pos_lo = a.q_pos0 + qt * 64;
@@ -60,7 +76,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Args a) {
 
   for (int t0 = kbeg; t0 <= kend; t0 += TK) {
     __syncthreads();
-    for (int idx = lane; idx < TK * D; idx += 64) {
+    for (int idx = tid; idx < TK * D; idx += 64 * NW) {
       const int row = idx / D, d = idx % D;
       const int key = t0 + row;
       const bool ok = key <= kend;
@@ -70,14 +86,14 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Args a) {
     __syncthreads();
     if (!live) continue;
     const int n = min(TK, kend - t0 + 1);
-    for (int jj = 0; jj < n; ++jj) {
+    for (int jj = wave; jj < n; jj += NW) {
       const int key = t0 + jj;
       const int delta = pos - key;
       if (delta < 0 || (a.window && delta >= a.window)) continue;
-      float s = 0.f;
+      float sp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int d = 0; d < D; ++d) s = fmaf(qv[d], Kt[jj][d], s);
-      s *= a.scale;
+      for (int d = 0; d < D; ++d) sp[d & 3] = fmaf(qv[d], Kt[jj][d], sp[d & 3]);
+      float s = ((sp[0] + sp[1]) + (sp[2] + sp[3])) * a.scale;
       if (a.mode != 0 && delta < a.bias_range) {
         if (a.mode == 1) {
           s += a.table[static_cast<size_t>(h) * a.bias_range + delta];
@@ -90,22 +106,61 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(F32Args a) {
           s += bsum;
         }
       }
-      s *= tq;
+      s *= c2;
       const float m_new = fmaxf(m, s);
-      const float alpha = expf(m - m_new);
-      const float p = expf(s - m_new);
+      const float alpha = fast_exp2(m - m_new);
+      const float p = fast_exp2(s - m_new);
       l = l * alpha + p;
 #pragma unroll
       for (int d = 0; d < D; ++d) acc[d] = fmaf(p, Vt[jj][d], acc[d] * alpha);
       m = m_new;
     }
   }
-  if (!live) return;
-  const float inv = 1.f / l;
+
+  // ---- merge the four waves' partials of each row: max, then sums rescaled to it ----------
+  float* cm = sm;                    // [NW][64] running maxima
+  float* cl = sm + NW * 64;          // [NW][64] running sums
+  float* cacc = sm + 2 * NW * 64;    // [NW - 1][64][33] accumulator chunks of waves 1..3
+  __syncthreads();                   // the tiles are dead
+  cm[wave * 64 + lane] = m;
+  cl[wave * 64 + lane] = l;
+  __syncthreads();
+  float M = cm[lane];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, cm[w * 64 + lane]);
+  // every row sees its own key, so M is finite for live rows; a wave that saw none of the
+  // row's keys has m = -inf and contributes zero
+  float ltot = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float mw = cm[w * 64 + lane];
+    ltot += (mw == -INFINITY) ? 0.f : cl[w * 64 + lane] * fast_exp2(mw - M);
+  }
+  const float own = (m == -INFINITY || !live) ? 0.f : fast_exp2(m - M);
+#pragma unroll
+  for (int dc = 0; dc < D / 32; ++dc) {
+    __syncthreads();   // the previous chunk has been read
+    if (wave > 0) {
+#pragma unroll
+      for (int k = 0; k < 32; ++k) cacc[((wave - 1) * 64 + lane) * 33 + k] = acc[32 * dc + k] * own;
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        float x = acc[32 * dc + k] * own;
+#pragma unroll
+        for (int w = 1; w < NW; ++w) x += cacc[((w - 1) * 64 + lane) * 33 + k];
+        acc[32 * dc + k] = x;
+      }
+    }
+  }
+  if (wave != 0 || !live) return;
+  const float inv = 1.f / ltot;
   float* op = a.o + ((static_cast<size_t>(b) * a.Sq + qi) * a.Hq + h) * D;
 #pragma unroll
   for (int d = 0; d < D; ++d) op[d] = acc[d] * inv;
-  if (a.lse) a.lse[(static_cast<size_t>(b) * a.Hq + h) * a.Sq + qi] = m + logf(l);
+  if (a.lse) a.lse[(static_cast<size_t>(b) * a.Hq + h) * a.Sq + qi] = (M + fast_log2(ltot)) * kLn2;
 }
 
 }  // namespace
@@ -115,9 +170,9 @@ hipError_t launch_attn_f32(const F32Args& a, hipStream_t s) {
   if (nblk <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(nblk));
   switch (a.D) {
-    case 32: hipLaunchKernelGGL(attn_f32_kernel<32>, grid, dim3(64), 0, s, a); break;
-    case 64: hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, s, a); break;
-    default: hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, s, a); break;
+    case 32: hipLaunchKernelGGL(attn_f32_kernel<32>, grid, dim3(64 * NW), 0, s, a); break;
+    case 64: hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64 * NW), 0, s, a); break;
+    default: hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64 * NW), 0, s, a); break;
   }
   return hipGetLastError();
 }
