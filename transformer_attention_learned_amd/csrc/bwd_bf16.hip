@@ -183,30 +183,47 @@ __global__ __launch_bounds__(256) void bwd_curves_kernel(BwdArgs a, int pitch) {
 }
 
 // ---- pre pass: rowsum(dO * O) and zeroed parameter gradients ----------------------------------
+// 16 lanes per row (each lane 16 bytes of O and of dO for D = 128, 8 bytes for D = 64), so a
+// wave reads 4 whole rows per load: coalesced 256-byte runs; a 16-lane sum finishes the row.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, float* zero_ptr, long long n_zero) {
+  constexpr int LPR = 16;          // lanes per row
+  constexpr int EPL = D / LPR;     // elements per lane: 8 (D = 128) or 4 (D = 64)
   const long long nrows = static_cast<long long>(a.B) * a.S * a.Hq;
   const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
-  for (long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; idx < nrows; idx += stride) {
-    // idx = (b * S + i) * Hq + h: consecutive threads read consecutive rows
-    const uint16_t* op = a.o + idx * D;
-    const uint16_t* dp = a.dout + idx * D;
+  const int sub = threadIdx.x % LPR;
+  const long long rstride = stride / LPR;
+  // every lane of a 16-lane group walks the same rows, so the group's shuffles see live lanes
+  for (long long idx = (static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x) / LPR; idx < nrows;
+       idx += rstride) {
+    // idx = (b * Hq + h) * S + i, the layout of the row sums: consecutive groups write
+    // consecutive floats (and read rows Hq * D apart)
+    const long long i = idx % a.S;
+    const long long bh = idx / a.S;
+    const long long h = bh % a.Hq;
+    const long long b = bh / a.Hq;
+    const long long row = (b * a.S + i) * a.Hq + h;
+    const uint16_t* op = a.o + row * D + EPL * sub;
+    const uint16_t* dp = a.dout + row * D + EPL * sub;
     float acc = 0.f;
+    uint32_t x[EPL / 2], y[EPL / 2];
+    if constexpr (EPL == 8) {
+      const u32x4 xv = ld16(op), yv = ld16(dp);
 #pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-      const u32x4 x = ld16(op + 8 * c);
-      const u32x4 y = ld16(dp + 8 * c);
+      for (int w = 0; w < 4; ++w) { x[w] = xv[w]; y[w] = yv[w]; }
+    } else {
+      const u32x2 xv = ld8(op), yv = ld8(dp);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        acc = fmaf(__uint_as_float(x[w] << 16), __uint_as_float(y[w] << 16), acc);
-        acc = fmaf(__uint_as_float(x[w] & 0xffff0000u), __uint_as_float(y[w] & 0xffff0000u), acc);
-      }
+      for (int w = 0; w < 2; ++w) { x[w] = xv[w]; y[w] = yv[w]; }
     }
-    const long long h = idx % a.Hq;
-    const long long bi = idx / a.Hq;
-    const long long b = bi / a.S;
-    const long long i = bi - b * a.S;
-    a.dsum[(b * a.Hq + h) * a.S + i] = acc;
+#pragma unroll
+    for (int w = 0; w < EPL / 2; ++w) {
+      acc = fmaf(__uint_as_float(x[w] << 16), __uint_as_float(y[w] << 16), acc);
+      acc = fmaf(__uint_as_float(x[w] & 0xffff0000u), __uint_as_float(y[w] & 0xffff0000u), acc);
+    }
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, LPR);
+    if (sub == 0) a.dsum[idx] = acc;
   }
   for (long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; idx < n_zero; idx += stride)
     zero_ptr[idx] = 0.f;
@@ -849,7 +866,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
     n_zero = static_cast<long long>(a.e_hs ? a.Hq : 1) * a.R * a.bias_range;
   }
   const long long nrows = static_cast<long long>(a.B) * a.S * a.Hq;
-  const long long want = (std::max(nrows, n_zero) + 255) / 256;
+  const long long want = (std::max(16 * nrows, n_zero) + 255) / 256;   // 16 lanes per row
   const unsigned pre_grid = static_cast<unsigned>(std::min<long long>(std::max<long long>(want, 1), 8192));
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(pre_grid), dim3(256), 0, s, a, zero_ptr, n_zero);
   hipError_t e = hipGetLastError();
