@@ -136,8 +136,10 @@ constexpr int CPAD_R = 64;
 
 // ---- curve table: C[b, h, i, d] = sum_f r[b, i, h, f] E[h, f, d] ---------------------------------
 // One workgroup per (batch, head, 64 rows): E[h] staged in LDS (fp32) in the table's own column
-// layout (zero outside [0, bias_range)), and the rows' r; each item is 8 consecutive columns of
-// one row: two 16-byte LDS reads per curve, one 16-byte store.
+// layout (zero outside [0, bias_range)), and the rows' r; a thread holds the E values of 8
+// consecutive columns (RM curves, RM >= R) in registers and writes those columns for every
+// (256 / chunks)-th row: one 16-byte store per row, the row's r read from LDS.
+template <int RM>
 __global__ __launch_bounds__(256) void bwd_curves_kernel(BwdArgs a, int pitch) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   float* es = reinterpret_cast<float*>(smem);                  // [R][pitch]
@@ -162,23 +164,37 @@ __global__ __launch_bounds__(256) void bwd_curves_kernel(BwdArgs a, int pitch) {
     rsh[x] = i < a.S ? bf16_to_f32(a.r[((static_cast<size_t>(b) * a.S + i) * a.Hq + h) * a.R + f]) : 0.f;
   }
   __syncthreads();
+  // thread -> (column chunk, row phase): the chunk's E values (R x 8) stay in registers and the
+  // rows are walked with a stride of the phase count, so each 16-byte store costs two LDS reads
+  // (the row's r) instead of two per curve
   const int chunks = pitch / 8;
   const int rows = min(64, a.S - i0);
+  const int cpt = min(chunks, 256);         // chunks side by side
+  const int phases = 256 / cpt;             // rows side by side
+  const int ph = threadIdx.x / cpt;
+  if (ph >= phases) return;
   uint16_t* out = a.ctab + (static_cast<size_t>(bh) * a.S + i0) * pitch;
-  for (int it = threadIdx.x; it < rows * chunks; it += 256) {
-    const int rr = it / chunks;
-    const int t0 = 8 * (it - rr * chunks);
-    f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
-    for (int f = 0; f < a.R; ++f) {
-      const float rv = rsh[rr * a.R + f];
-      const f32x4 e0 = *reinterpret_cast<const f32x4*>(es + f * pitch + t0);
-      const f32x4 e1 = *reinterpret_cast<const f32x4*>(es + f * pitch + t0 + 4);
-      v0 += rv * e0;
-      v1 += rv * e1;
+  for (int ch = threadIdx.x % cpt; ch < chunks; ch += cpt) {
+    const int t0 = 8 * ch;
+    f32x4 e0[RM], e1[RM];
+#pragma unroll
+    for (int f = 0; f < RM; ++f) {
+      const bool fl = f < a.R;
+      e0[f] = fl ? *reinterpret_cast<const f32x4*>(es + f * pitch + t0) : f32x4{0.f, 0.f, 0.f, 0.f};
+      e1[f] = fl ? *reinterpret_cast<const f32x4*>(es + f * pitch + t0 + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    st16(out + static_cast<size_t>(rr) * pitch + t0,
-         u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v1[0], v1[1]),
-               pack_bf16x2(v1[2], v1[3])});
+    for (int rr = ph; rr < rows; rr += phases) {
+      f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int f = 0; f < RM; ++f) {
+        const float rv = f < a.R ? rsh[rr * a.R + f] : 0.f;
+        v0 += rv * e0[f];
+        v1 += rv * e1[f];
+      }
+      st16(out + static_cast<size_t>(rr) * pitch + t0,
+           u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v1[0], v1[1]),
+                 pack_bf16x2(v1[2], v1[3])});
+    }
   }
 }
 
@@ -874,10 +890,16 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   const int pitch = bwd_curve_pitch(a.bias_range);
   if (MODE == 2) {
     const int lds = (a.R * pitch + 64 * a.R) * 4;
-    e = allow_lds(&bwd_curves_kernel, lds);
-    if (e != hipSuccess) return e;
     const long long ng = static_cast<long long>(a.B) * a.Hq * ((a.S + 63) / 64);
-    hipLaunchKernelGGL(bwd_curves_kernel, dim3(static_cast<unsigned>(ng)), dim3(256), lds, s, a, pitch);
+    if (a.R > 8) {
+      e = allow_lds(&bwd_curves_kernel<16>, lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(bwd_curves_kernel<16>, dim3(static_cast<unsigned>(ng)), dim3(256), lds, s, a, pitch);
+    } else {
+      e = allow_lds(&bwd_curves_kernel<8>, lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(bwd_curves_kernel<8>, dim3(static_cast<unsigned>(ng)), dim3(256), lds, s, a, pitch);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
