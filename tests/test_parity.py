@@ -288,6 +288,18 @@ def test_decode_f32_small(kw):
     check_decode(w, 250)
 
 
+# the fp32 kernel splits each key tile over four waves: caches shorter than the split, one key,
+# a window of one, ragged tiles, head_dim 128 and 32
+@pytest.mark.parametrize("kv_len,kw", [(1, dict()), (3, dict(window=2)), (65, dict(window=1)),
+                                       (130, dict(D=128, mode="table")), (70, dict(D=32, window=64))],
+                         ids=["one_key", "three_keys", "window_1", "d128_table", "d32_window"])
+def test_decode_f32_short(kv_len, kw):
+    base = dict(B=2, Hq=4, Hkv=2, D=64, S=200, window=0, bias_range=50, R=4, seed=5, mode="rproj")
+    base.update(kw)
+    w = Workload(name="dec_f32_short", kind="decode", dtype="f32", **base)
+    check_decode(w, kv_len)
+
+
 def test_decode_global_workload():
     w = WORKLOADS["decode_global"]
     check_decode(w, w.S, batches=[0, 9, 31, 63])
