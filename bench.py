@@ -39,7 +39,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 KERNEL_SOURCES = {
-    "prefill": ["fwd_bf16.hip", "fwd_bf16_fast.hip", "fwd_bf16_split.hip"],
+    "prefill": ["fwd_bf16.hip", "fwd_bf16_split.hip"],
     "decode": ["decode_bf16.hip"],
     "f32": ["attn_f32.hip"],
     "backward": ["bwd_bf16.hip"],

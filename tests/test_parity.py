@@ -61,8 +61,8 @@ def assert_lse(got, ref, dtype, what=""):
     """The log-sum-exp is held to the same bar as the output.
 
     On the bf16 path the row sum adds the bf16-rounded probabilities (the same
-    ones the P.V product uses) and the r.E bias uses a bf16 copy of E, so lse
-    carries errors of order 2^-9 (about 2e-3 in natural log units per source).
+    ones the P.V product uses), so lse carries errors of order 2^-9 (about 2e-3
+    in natural log units).
     """
     max_abs, rel = _errs(got, ref)
     _say(f"    lse {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
@@ -140,9 +140,12 @@ SWEEP = [
     dict(S=300, window=1000, bias_range=2000), dict(S=333, window=100, bias_range=100),
     dict(S=333, window=33, bias_range=40, mode="table"), dict(S=290, window=95, bias_range=95, R=16),
     dict(S=450, window=200, bias_range=31), dict(S=450, window=200, bias_range=33, mode="none"),
-    # table ranges too long for the 32-row kernel's LDS take the 64-row kernel
+    # table ranges too long for the split kernel's LDS take the generic kernel (table rows read
+    # from global memory)
     dict(S=2200, mode="table", bias_range=2048, Hq=8, Hkv=2),
     dict(S=2200, mode="table", window=600, bias_range=2048, Hq=8, Hkv=2),
+    # the generic kernel without bias: head_dim 128 with a GQA ratio of 2, head_dim 64
+    dict(S=200, mode="none", Hq=2, Hkv=1), dict(S=260, D=64, mode="none", window=90),
     # windows inside the bias range with more work items (batch x head group x 64-row tile)
     # than CUs: the kernel walks runs of items per workgroup, runs cross head groups and batch
     # entries, tails are ragged
@@ -153,6 +156,31 @@ SWEEP = [
 
 @pytest.mark.parametrize("kw", SWEEP, ids=lambda kw: "-".join(f"{k}{v}" for k, v in kw.items()))
 def test_prefill_small(kw):
+    check_prefill(small(seed=zlib.crc32(repr(sorted(kw.items())).encode()) % 10007, **kw))
+
+
+# Sharp input-dependent biases: E drawn at std 0.5 and 1.0 (a bias RMS of about 1.4 and 2.8 at
+# R = 8), the per-token sharp locality the input-dependent form is for ("Thinking Machines
+# dropped RoPE", the paragraph after the code listing: one token can demand sharp locality while
+# the next reaches back through the whole window).  The kernels carry E as a bf16 high and low
+# part and keep the formed curve in fp32, so these stay inside the bf16 bar; a table at std 3 is
+# the control (the table path always reads fp32).
+SHARP = [
+    dict(S=1100, Hq=8, Hkv=2, window=512, bias_range=512, e_std=0.5),
+    dict(S=1100, Hq=8, Hkv=2, window=512, bias_range=512, e_std=1.0),
+    dict(S=1100, Hq=8, Hkv=2, window=512, bias_range=512, e_std=1.0, R=16),
+    dict(S=1500, Hq=8, Hkv=2, bias_range=1024, e_std=0.5),
+    dict(S=1500, Hq=8, Hkv=2, bias_range=1024, e_std=1.0),
+    dict(S=1500, Hq=8, Hkv=2, bias_range=1024, e_std=1.0, R=16),
+    dict(S=1300, mode="rproj_shared", R=16, bias_range=1024, e_std=1.0, logit_scale="inv_d"),
+    dict(S=900, window=512, bias_range=512, e_std=1.0, D=64),
+    dict(S=700, window=300, bias_range=200, e_std=1.0, R=11, Hq=6, Hkv=2),
+    dict(S=1100, Hq=8, Hkv=2, mode="table", bias_range=1024, table_std=3.0),
+]
+
+
+@pytest.mark.parametrize("kw", SHARP, ids=lambda kw: "-".join(f"{k}{v}" for k, v in kw.items()))
+def test_prefill_sharp_bias(kw):
     check_prefill(small(seed=zlib.crc32(repr(sorted(kw.items())).encode()) % 10007, **kw))
 
 
@@ -199,8 +227,20 @@ def _sample_rows(S, Rb, seed, n_edge=64, n_rand=64):
 
 
 def test_local_prefill_workload():
-    w = WORKLOADS["local_prefill"]
+    """Every output element of the local-layer workload against the full oracle."""
+    check_prefill(WORKLOADS["local_prefill"])
+
+
+def test_local_prefill_workload_sharp_bias():
+    """The local-layer workload with E at std 1.0 (bias RMS about 2.8), row sample."""
+    w = WORKLOADS["local_prefill"].with_(name="local_prefill_e1", e_std=1.0)
     check_prefill(w, rows=_sample_rows(w.S, w.bias_range, 2, n_edge=128, n_rand=256))
+
+
+def test_global_prefill_workload_sharp_bias():
+    """The global-layer workload with E at std 1.0, row sample."""
+    w = WORKLOADS["global_prefill"].with_(name="global_prefill_e1", e_std=1.0)
+    check_prefill(w, rows=_sample_rows(w.S, w.bias_range, 3, n_edge=32, n_rand=32))
 
 
 def test_global_prefill_workload():
@@ -265,6 +305,10 @@ DEC_SWEEP = [
     dict(S=6000, kv_len=5000, temp_len=1024), dict(S=3000, kv_len=2900, window=700, temp_len=100),
     dict(S=3000, kv_len=2900, Hq=32, Hkv=1, bias_range=512, temp_len=300),
     dict(S=2000, kv_len=900, mode="table", bias_range=300, temp_len=1000),
+    # sharp input-dependent biases (E at std 1.0)
+    dict(S=3000, kv_len=2900, window=512, bias_range=512, e_std=1.0),
+    dict(S=3000, kv_len=2900, bias_range=1024, e_std=1.0),
+    dict(S=3000, kv_len=2900, Hq=32, Hkv=1, bias_range=1024, e_std=1.0, R=16),
 ]
 
 

@@ -395,13 +395,12 @@ hipError_t launch_mode(const FwdArgs& a, int mode, hipStream_t s) {
 }  // namespace
 
 namespace {
-// The two MFMA kernels address K and V through 32-bit buffer offsets within one sequence.
+// The MFMA kernels address K and V through 32-bit buffer offsets within one sequence.
 bool kv_off32(const FwdArgs& a, int D) { return static_cast<long long>(a.S) * a.Hkv * D * 2 < (1LL << 31); }
-// Every layer the split kernel's domain covers takes it: its 32-row workgroups pair up on a CU
-// (and it reads E rows converted once per call); measured faster than the 64-row kernel for
-// sliding-window and full causal layers alike (full causal with the bias table at S = 32768:
-// 4.08 against 4.43 ms).  The 64-row kernel remains for shapes outside that domain (a table
-// range too long for the split kernel's LDS).
+// Every layer the split kernel's domain covers takes it (head_dim 128, GQA groups of 4k heads,
+// positive scale, LDS within half a CU: its 32-row workgroups pair up on a CU and it reads E rows
+// converted once per call).  The kernel above takes the other shapes: head_dim 64, other group
+// sizes, ranges off the 4-distance grid, a table range too long for the split kernel's LDS.
 bool use_split(const FwdArgs& a, int D, int mode) {
   return kv_off32(a, D) &&
          fwd_split_workspace(D, a.G, mode, a.bias_range, a.R, a.e_hs == 0, a.Hq, a.c_qk) >= 0;
@@ -416,10 +415,6 @@ long long fwd_bf16_workspace(const FwdArgs& a, int D, int mode) {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a0, int D, int mode, void* workspace, hipStream_t s) {
   if (use_split(a0, D, mode)) return launch_fwd_bf16_split(a0, mode, workspace, s);
-  const bool vec_ok = (reinterpret_cast<uintptr_t>(a0.table) & 15u) == 0 &&
-                      (reinterpret_cast<uintptr_t>(a0.E) & 15u) == 0;
-  if (vec_ok && kv_off32(a0, D) && fwd_fast_lds_bytes(D, a0.G, mode, a0.bias_range, a0.R, a0.c_qk) >= 0)
-    return launch_fwd_bf16_fast(a0, mode, s);
   FwdArgs a = a0;
   a.hpw = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0 ? 2 : 1);
   if (D == 128) return launch_mode<128, 1>(a, mode, s);

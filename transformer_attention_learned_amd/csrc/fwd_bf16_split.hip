@@ -21,12 +21,14 @@
 //     compares against thresholds computed once per workgroup;
 //   * bias and masks enter through the S accumulator's start values; lazy rescaling of O;
 //   * table bias: the group's table rows in LDS, zero-padded, read with immediate offsets;
-//   * input-dependent bias r_i . E[h, :, delta]: E in bf16, distance-major rows of EF features
-//     in accumulator units (converted once per call into the caller's workspace), so that a
-//     curve block's operand is one 16-byte load per lane; the curves of a step (two MFMAs over
-//     the R features for its 64 distances) go through the wave's LDS curve buffer and are formed
-//     one step ahead of their use, their E rows one step before that; with the window inside the
-//     range every step is in band and this path has no branches.
+//   * input-dependent bias r_i . E[h, :, delta]: E in accumulator units split into a bf16 high
+//     and low part (about 16 mantissa bits), distance-major rows of EW = 16 or 32 entries
+//     (converted once per call into the caller's workspace), so that a curve block's operand is
+//     one 16-byte load per lane and MFMA; the high and low parts of R <= 8 features share one
+//     MFMA (they fill its two K halves).  The curves of a step (MFMAs over the features for its
+//     64 distances, fp32) go through the wave's LDS curve buffer in fp32 and are formed one step
+//     ahead of their use, their E rows one step before that; with the window inside the range
+//     every step is in band and this path has no branches.
 
 #include <algorithm>
 #include <type_traits>
@@ -43,7 +45,6 @@ constexpr int BN = 32;            // keys per tile (= per step)
 constexpr int NC = D / 16;        // K = 16 chunks of the head dim
 constexpr int NDB = D / 32;       // 32-wide head-dim blocks of O^T
 constexpr int NBUF = 3;           // tile ring
-constexpr int CBW = 68;           // curve buffer row stride (bf16): conflict-free 8-byte writes, 2-way dword reads
 constexpr int PAD = 64;           // zero distances on each side of the bias range (table rows, E rows)
 constexpr int ROWS_WG = 32;       // query rows per workgroup
 constexpr int NT = 256;           // threads per workgroup
@@ -52,11 +53,13 @@ constexpr float kRescale = 8.f;   // lazy rescale threshold (log2 units)
 constexpr int KT_BYTES = BN * D * 2;   // K tile: 32 rows of 256 bytes
 constexpr int VT_BYTES = BN * D * 2;   // V tile: 32 rows of 256 bytes
 constexpr int BUF_BYTES = KT_BYTES + VT_BYTES;
-constexpr int CURVE_BYTES = 32 * CBW * 2;   // per wave
+constexpr int CURVE_FLOATS = 32 * 40;   // per wave: 32 skewed fp32 rows of 36 live entries, 40 apart
+constexpr int CURVE_BYTES = CURVE_FLOATS * 4;
 constexpr int TILE_BYTES = NBUF * BUF_BYTES;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) float lds_float;
 
 // 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at dst + 16 l
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, int voff) {
@@ -75,12 +78,14 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// E (fp32 [heads, R, Rb], head h at E + h * e_hs) -> bf16 rows [heads][Rb + 2 PAD + 1][EF]:
-// entry (h, PAD + d, f) = E[h, f, d] / scale for 0 <= d < Rb and f < R, zero elsewhere (the pads
-// and the features past R), so that every read of the kernels below is in range and unguarded.
-// One thread per (head, row) and 8 features: one 16-byte store; grid.y = head, grid.z = feature half.
+// E (fp32 [heads, R, Rb], head h at E + h * e_hs) -> bf16 rows [heads][Rb + 2 PAD + 1][EW] of a
+// high and a low part: with x = E[h, f, d] / scale in fp32, entry (h, PAD + d, f) = bf16(x) and
+// entry (h, PAD + d, EW / 2 + f) = bf16(x - bf16(x)) for 0 <= d < Rb and f < R, zero elsewhere
+// (the pads and the features past R), so that every read of the kernels below is in range and
+// unguarded and the pair carries about 16 mantissa bits of x.  One thread per (head, row) and 8
+// features: two 16-byte stores; grid.y = head, grid.z = feature octet (EW / 16 of them).
 __global__ void e2_convert_kernel(const float* __restrict__ E, long long e_hs, int R, int Rb,
-                                  float inv_scale, int EF, uint16_t* __restrict__ e2) {
+                                  float inv_scale, int EW, uint16_t* __restrict__ e2) {
   const int rows = Rb + 2 * PAD + 1;
   const int p = blockIdx.x * blockDim.x + threadIdx.x;
   if (p >= rows) return;
@@ -89,19 +94,29 @@ __global__ void e2_convert_kernel(const float* __restrict__ E, long long e_hs, i
   const int d = p - PAD;
   const bool live = d >= 0 && d < Rb;
   const float* eh = E + h * e_hs + static_cast<long long>(f0) * Rb + d;
-  uint32_t w[4];
+  uint32_t whi[4], wlo[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float x0 = (live && f0 + 2 * k < R) ? eh[static_cast<long long>(2 * k) * Rb] * inv_scale : 0.f;
-    const float x1 = (live && f0 + 2 * k + 1 < R) ? eh[static_cast<long long>(2 * k + 1) * Rb] * inv_scale : 0.f;
-    w[k] = static_cast<uint32_t>(f32_to_bf16(x0)) | (static_cast<uint32_t>(f32_to_bf16(x1)) << 16);
+    uint16_t hb[2], lb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int f = f0 + 2 * k + u;
+      const float x = (live && f < R) ? eh[static_cast<long long>(2 * k + u) * Rb] * inv_scale : 0.f;
+      hb[u] = f32_to_bf16(x);
+      lb[u] = f32_to_bf16(x - bf16_to_f32(hb[u]));
+    }
+    whi[k] = static_cast<uint32_t>(hb[0]) | (static_cast<uint32_t>(hb[1]) << 16);
+    wlo[k] = static_cast<uint32_t>(lb[0]) | (static_cast<uint32_t>(lb[1]) << 16);
   }
-  st16(e2 + (static_cast<size_t>(h) * rows + p) * EF + f0, u32x4{w[0], w[1], w[2], w[3]});
+  uint16_t* row = e2 + (static_cast<size_t>(h) * rows + p) * EW;
+  st16(row + f0, u32x4{whi[0], whi[1], whi[2], whi[3]});
+  st16(row + EW / 2 + f0, u32x4{wlo[0], wlo[1], wlo[2], wlo[3]});
 }
 
-// MODE 0 none, 1 table, 2 r.E (EF = 8 or 16 features per E row); ALLBAND: every visible key is
-// inside the bias range (window <= range), so every step of MODE 2 is in band.
-template <int MODE, int EF, bool ALLBAND>
+// MODE 0 none, 1 table, 2 r.E (EW = 16 or 32 entries per E row: the high and low parts of up
+// to 8 or 16 features); ALLBAND: every visible key is inside the bias range (window <= range),
+// so every step of MODE 2 is in band.
+template <int MODE, int EW, bool ALLBAND>
 __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint16_t* __restrict__ e2g) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
@@ -172,10 +187,13 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
   // this wave's loads into LDS have landed (they are its only vector-memory writes to LDS; the
   // barrier that follows publishes them)
   auto dma_wait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
-  // the same inside the key loop when the only loads issued after the awaited tile are the two
-  // E-row loads of a later step: vector-memory loads complete in issue order, so vmcnt(2)
-  // leaves those in flight instead of waiting out their latency before the barrier
-  auto dma_wait_but2 = [&]() { __builtin_amdgcn_s_waitcnt(0x0F72); };   // vmcnt(2)
+  // the same inside the key loop when the only loads issued after the awaited tile are the
+  // 2 NEF E-row loads of a later step: vector-memory loads complete in issue order, so
+  // vmcnt(2 NEF) leaves those in flight instead of waiting out their latency before the barrier
+  auto dma_wait_but_e = [&]() {
+    if (EW == 32) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
+    else __builtin_amdgcn_s_waitcnt(0x0F72);            // vmcnt(2)
+  };
 
   // ---- table rows of the group (MODE 1), in accumulator units, PAD zero distances each side
   const int Rp = Rb + 2 * PAD;
@@ -204,14 +222,17 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
       qf[c] = as_bf16x8(v);
     }
   }
+  // r fragment (B operand of the curve MFMAs): with EW = 16 both lane halves hold features 0..7
+  // (they meet the high and the low part of E), with EW = 32 lane half lh holds features 8 lh ..
+  // 8 lh + 7 (the high and the low part take one MFMA each)
   bf16x8 rf;
   const uint16_t* e2h = nullptr;   // this head's E rows at distance 0
   if (MODE == 2) {
     const int row = i0 + ln;
     const uint16_t* rp = a.r + ((static_cast<size_t>(b) * S + row) * a.Hq + h) * a.R;
-    const int f0 = (EF == 16) ? 8 * lh : 0;
-    const bool live = row < S && (EF == 16 || lh == 0);
-    if (a.R == EF && (reinterpret_cast<uintptr_t>(a.r) & 15) == 0) {
+    const int f0 = (EW == 32) ? 8 * lh : 0;
+    const bool live = row < S;
+    if (a.R == EW / 2 && (reinterpret_cast<uintptr_t>(a.r) & 15) == 0) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (live) v = ld16(rp + f0);
       rf = as_bf16x8(v);
@@ -226,7 +247,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
       }
       rf = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
     }
-    e2h = e2g + (static_cast<size_t>(a.e_hs ? h : 0) * (Rp + 1) + PAD) * EF;
+    e2h = e2g + (static_cast<size_t>(a.e_hs ? h : 0) * (Rp + 1) + PAD) * EW;
   }
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -237,13 +258,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
 
   const float NEG_INF = -INFINITY;
-  auto perm_sel = [](int r) -> uint32_t {
-    return 0x0c0cu | (static_cast<uint32_t>(2 * r) << 16) | (static_cast<uint32_t>(2 * r + 1) << 24);
-  };
-  const uint32_t sel_a = perm_sel(ln & 1);
-  const uint32_t sel_b = perm_sel((ln & 1) + 1);
   const float* tabw = (MODE == 1) ? reinterpret_cast<const float*>(smem + TILE_BYTES) + wave * Rp + PAD : nullptr;
-  uint16_t* cbuf = (MODE == 2) ? reinterpret_cast<uint16_t*>(smem + TILE_BYTES) + wave * (CURVE_BYTES / 2) : nullptr;
+  float* cbuf = (MODE == 2) ? reinterpret_cast<float*>(smem + TILE_BYTES) + wave * CURVE_FLOATS : nullptr;
 
   // Step js covers keys j0 .. j0 + 31 with j0 = (t_begin + js) * BN; delta = c + n - m with
   // c = i0 - j0, n the lane's row, m the key within the step.  For js >= 0 the step has visible
@@ -260,47 +276,76 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
   auto step_edge = [&](int js) { return js >= nsteps - 1 || js < js_w; };
 
   // ---- r.E curves: E rows of step js are loaded one step before its curves are formed
-  u32x4 ef_lo = {0u, 0u, 0u, 0u}, ef_hi = {0u, 0u, 0u, 0u};
-  uint32_t cr[12];
+  constexpr int NEF = EW / 16;   // curve MFMAs per 32 distances (high and low part of E)
+  u32x4 ef[2][NEF];              // [distance block][MFMA]
 #pragma unroll
-  for (int i = 0; i < 12; ++i) cr[i] = 0u;
+  for (int u = 0; u < 2 * NEF; ++u) ef[u / NEF][u % NEF] = u32x4{0u, 0u, 0u, 0u};
+  float cr[16];                  // the bias of this lane's 16 keys of the step, accumulator units
+#pragma unroll
+  for (int i = 0; i < 16; ++i) cr[i] = 0.f;
   auto curve_c = [&](int js) {
     // a step outside the band is fully masked (ALLBAND) or skipped: clamp its offset so that
     // the E rows read stay inside the padded rows (distances -PAD .. Rb + PAD)
     return min(max(step_c(js), -33), Rb + 31);
   };
-  auto e_fetch_to = [&](int js, u32x4& lo, u32x4& hi) {
-    const uint16_t* ep = e2h + (curve_c(js) - 31 + ln) * EF + 8 * lh;
-    lo = ld16(ep);
-    hi = ld16(ep + 32 * EF);
+  auto e_fetch_to = [&](int js, u32x4 (&e)[2][NEF]) {
+    // A operand: E row of distance c - 31 + ln (block 0) or c + 1 + ln (block 1); MFMA u takes
+    // entries 16 u + 8 lh .. + 7 of the row
+    const uint16_t* ep = e2h + (curve_c(js) - 31 + ln) * EW + 8 * lh;
+#pragma unroll
+    for (int u = 0; u < NEF; ++u) {
+      e[0][u] = ld16(ep + 16 * u);
+      e[1][u] = ld16(ep + 32 * EW + 16 * u);
+    }
   };
-  auto e_fetch = [&](int js) { e_fetch_to(js, ef_lo, ef_hi); };
-  // curves of step js from the fetched E rows: two MFMAs over the R features give the 64
-  // distances c - 31 .. c + 32 for every query row (curve_mfma); written unskewed to the wave's
-  // buffer (row = query, column = distance - (c - 31)), then each lane's diagonal read back
-  // into cr (curve_store)
+  auto e_fetch = [&](int js) { e_fetch_to(js, ef); };
+  // curves of step js from the fetched E rows: MFMAs over the features give the 64 distances
+  // c - 31 .. c + 32 for every query row, in fp32 (curve_mfma): lane (n, lh) holds row n at
+  // t = 8 g + 4 lh + k (block 0) and 32 + the same (block 1), t = distance - (c - 31).
+  // curve_store writes them to the wave's buffer and reads back the lane's diagonal
+  // t = 31 + n - m for its keys m = 8 g + 4 lh + k.  Row n keeps only the t it reads,
+  // n .. n + 31, as entries t - 4 (n / 4) in 0..35 of a 36-entry row; the rows sit 40 entries
+  // apart in an order that makes both the 16-byte writes and the dword reads conflict-free
+  // (row slot ((5 (n / 4 + 2 (n % 4))) % 8) + 8 (n % 4)).  Chunks a row does not read are
+  // not written (a per-lane constant predicate).
+  const int cslot = ((5 * ((ln >> 2) + 2 * (ln & 3))) & 7) + 8 * (ln & 3);
+  const int cbase = 40 * cslot - 4 * (ln >> 2);
+  bool cwrite[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int ts = 32 * (u >> 2) + 8 * (u & 3) + 4 * lh;
+    cwrite[u] = ts + 3 >= ln && ts <= ln + 31;
+  }
+  const lds_float* crd = nullptr;
+  if (MODE == 2) {
+    crd = (const lds_float*)(cbuf + cbase + 4 + ln - 4 * lh);
+    // an opaque register: the reads below then use it as their base with immediate offsets,
+    // instead of one address computation each (the LDS offset of the buffer is too large for
+    // the pair-read offset field)
+    asm volatile("" : "+v"(crd));
+  }
   auto curve_mfma = [&](f32x16& lo, f32x16& hi) {
     const f32x16 zero = {};
-    lo = mfma32(as_bf16x8(ef_lo), rf, zero);
-    hi = mfma32(as_bf16x8(ef_hi), rf, zero);
+    lo = mfma32(as_bf16x8(ef[0][0]), rf, zero);
+    hi = mfma32(as_bf16x8(ef[1][0]), rf, zero);
+#pragma unroll
+    for (int u = 1; u < NEF; ++u) {
+      lo = mfma32(as_bf16x8(ef[0][u]), rf, lo);
+      hi = mfma32(as_bf16x8(ef[1][u]), rf, hi);
+    }
   };
   auto curve_store = [&](const f32x16& lo, const f32x16& hi) {
-    uint16_t* wp = cbuf + ln * CBW + 4 * lh;
+    float* wp = cbuf + cbase + 4 * lh;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      st8(wp + 8 * k, u32x2{pack_bf16x2(lo[4 * k], lo[4 * k + 1]), pack_bf16x2(lo[4 * k + 2], lo[4 * k + 3])});
-      st8(wp + 32 + 8 * k, u32x2{pack_bf16x2(hi[4 * k], hi[4 * k + 1]), pack_bf16x2(hi[4 * k + 2], hi[4 * k + 3])});
+    for (int g = 0; g < 4; ++g) {
+      if (__builtin_expect(cwrite[g], 1)) st16(wp + 8 * g, __builtin_bit_cast(u32x4, f32x4{lo[4 * g], lo[4 * g + 1], lo[4 * g + 2], lo[4 * g + 3]}));
+      if (__builtin_expect(cwrite[4 + g], 1)) st16(wp + 32 + 8 * g, __builtin_bit_cast(u32x4, f32x4{hi[4 * g], hi[4 * g + 1], hi[4 * g + 2], hi[4 * g + 3]}));
     }
     wave_sync_lds();
-    // key m of lane n sits at column 31 + n - m; keys m0 .. m0 + 3 (m0 = 8 g + 4 lh) span
-    // the three aligned dwords read here
-    const uint32_t* rd = reinterpret_cast<const uint32_t*>(cbuf) + ln * (CBW / 2) + (ln >> 1) + 2 - 2 * lh;
+    // key m = 8 g + 4 lh + k at entry cbase + 31 + n - m (crd: entry cbase + 4 + n - 4 lh, so
+    // that the 16 reads are one base register and dword offsets 0..27, paired into ds_read2_b32)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      cr[3 * g4] = rd[12 - 4 * g4];
-      cr[3 * g4 + 1] = rd[13 - 4 * g4];
-      cr[3 * g4 + 2] = rd[14 - 4 * g4];
-    }
+    for (int i = 0; i < 16; ++i) cr[i] = crd[27 - 8 * (i >> 2) - (i & 3)];
   };
   auto curve_issue = [&](int js) {
     f32x16 lo, hi;
@@ -341,16 +386,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
     }
     if (MODE == 2 && (ALLBAND || inband)) {
       asm volatile("; in-band step: r.E bias" ::: "memory");
-      // column 28 + n - m0 + k holds key m0 + 3 - k; v_perm moves each bf16 into the top half
-      // of an fp32 with zeros below
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const uint32_t d0 = cr[3 * g4], d1 = cr[3 * g4 + 1], d2 = cr[3 * g4 + 2];
-        init[4 * g4 + 3] = __uint_as_float(__builtin_amdgcn_perm(d1, d0, sel_a));
-        init[4 * g4 + 2] = __uint_as_float(__builtin_amdgcn_perm(d1, d0, sel_b));
-        init[4 * g4 + 1] = __uint_as_float(__builtin_amdgcn_perm(d2, d1, sel_a));
-        init[4 * g4 + 0] = __uint_as_float(__builtin_amdgcn_perm(d2, d1, sel_b));
-      }
+      for (int i = 0; i < 16; ++i) init[i] = cr[i];
     }
     if (step_edge(js)) {
       asm volatile("; edge step: mask" ::: "memory");
@@ -461,17 +498,19 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
 
   // ---- prologue: tiles 0 and 1, the query rows and the E rows of steps 0 and 1 requested
   // together (one memory round trip), then the curves and scores of step 0 ---------------------
-  u32x4 ef1_lo = {0u, 0u, 0u, 0u}, ef1_hi = {0u, 0u, 0u, 0u};
+  u32x4 ef1[2][NEF];
+#pragma unroll
+  for (int u = 0; u < 2 * NEF; ++u) ef1[u / NEF][u % NEF] = u32x4{0u, 0u, 0u, 0u};
   if (MODE == 2 && (ALLBAND || step_inband(0))) e_fetch(0);
-  if (MODE == 2 && (ALLBAND || step_inband(1))) e_fetch_to(1, ef1_lo, ef1_hi);
+  if (MODE == 2 && (ALLBAND || step_inband(1))) e_fetch_to(1, ef1);
   dma_wait();
   __syncthreads();
 
   f32x16 sa, sb;
   {
     if (MODE == 2 && (ALLBAND || step_inband(0))) curve_issue(0);
-    ef_lo = ef1_lo;
-    ef_hi = ef1_hi;
+#pragma unroll
+    for (int u = 0; u < 2 * NEF; ++u) ef[u / NEF][u % NEF] = ef1[u / NEF][u % NEF];
     if (step_special(0)) {
       sa = step_init(0);
       step_scores(smem, sa, true_t{});
@@ -544,7 +583,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
   // js + 1 fetched them), nothing else.
   auto iteration_wait = [&](int js) {
     if (MODE == 2 && (ALLBAND || step_inband(js + 2)))
-      dma_wait_but2();
+      dma_wait_but_e();
     else
       dma_wait();
     __syncthreads();
@@ -611,7 +650,7 @@ int split_lds(int mode, int Rb) {
   return TILE_BYTES;
 }
 
-template <int MODE, int EF, bool ALLBAND>
+template <int MODE, int EW, bool ALLBAND>
 hipError_t launch_split(FwdArgs a, const uint16_t* e2, hipStream_t s) {
   a.hpw = 4;
   a.rows_wg = ROWS_WG;
@@ -623,12 +662,12 @@ hipError_t launch_split(FwdArgs a, const uint16_t* e2, hipStream_t s) {
   const int lds = split_lds(MODE, a.bias_range);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_split_kernel<MODE, EF, ALLBAND>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_split_kernel<MODE, EW, ALLBAND>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsPerWg);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((fwd_split_kernel<MODE, EF, ALLBAND>), dim3(static_cast<unsigned>(nblk)), dim3(NT), lds, s, a, e2);
+  hipLaunchKernelGGL((fwd_split_kernel<MODE, EW, ALLBAND>), dim3(static_cast<unsigned>(nblk)), dim3(NT), lds, s, a, e2);
   return hipGetLastError();
 }
 
@@ -642,23 +681,23 @@ long long fwd_split_workspace(int D_, int G, int mode, int Rb, int R, int e_shar
   if (mode != 0 && Rb % 4 != 0) return -1;
   if (split_lds(mode, Rb) > kMaxLdsPerWg) return -1;
   if (mode != 2) return 0;
-  const int EF = R > 8 ? 16 : 8;
-  return static_cast<long long>(e_shared ? 1 : Hq) * (Rb + 2 * PAD + 1) * EF * 2;
+  const int EW = R > 8 ? 32 : 16;
+  return static_cast<long long>(e_shared ? 1 : Hq) * (Rb + 2 * PAD + 1) * EW * 2;
 }
 
 hipError_t launch_fwd_bf16_split(const FwdArgs& a, int mode, void* workspace, hipStream_t s) {
-  if (mode != 2) return mode == 1 ? launch_split<1, 8, false>(a, nullptr, s) : launch_split<0, 8, false>(a, nullptr, s);
-  const int EF = a.R > 8 ? 16 : 8;
+  if (mode != 2) return mode == 1 ? launch_split<1, 16, false>(a, nullptr, s) : launch_split<0, 16, false>(a, nullptr, s);
+  const int EW = a.R > 8 ? 32 : 16;
   const int heads = a.e_hs ? a.Hq : 1;
   uint16_t* e2 = static_cast<uint16_t*>(workspace);
   const int rows = a.bias_range + 2 * PAD + 1;
-  hipLaunchKernelGGL(e2_convert_kernel, dim3((rows + 255) / 256, heads, EF / 8), dim3(256), 0, s, a.E, a.e_hs,
-                     a.R, a.bias_range, kLog2e / a.c_qk, EF, e2);
+  hipLaunchKernelGGL(e2_convert_kernel, dim3((rows + 255) / 256, heads, EW / 16), dim3(256), 0, s, a.E, a.e_hs,
+                     a.R, a.bias_range, kLog2e / a.c_qk, EW, e2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool allband = a.window != 0 && a.window <= a.bias_range;
-  if (EF == 16) return allband ? launch_split<2, 16, true>(a, e2, s) : launch_split<2, 16, false>(a, e2, s);
-  return allband ? launch_split<2, 8, true>(a, e2, s) : launch_split<2, 8, false>(a, e2, s);
+  if (EW == 32) return allband ? launch_split<2, 32, true>(a, e2, s) : launch_split<2, 32, false>(a, e2, s);
+  return allband ? launch_split<2, 16, true>(a, e2, s) : launch_split<2, 16, false>(a, e2, s);
 }
 
 }  // namespace rba

@@ -141,8 +141,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int D, int mode, void* workspace, h
 // Workspace bytes the bf16 prefill of this shape takes (0: none); the size query and the launch
 // share it, so both pick the same kernel.
 long long fwd_bf16_workspace(const FwdArgs& a, int D, int mode);
-// Split prefill (two workgroups per CU, sliding-window layers): workspace bytes it needs (the
-// converted E of r.E bias), or -1 outside its domain; and its launcher.
+// Split prefill (two workgroups per CU): workspace bytes it needs (the converted E of r.E bias),
+// or -1 outside its domain; and its launcher.
 long long fwd_split_workspace(int D, int G, int mode, int bias_range, int R, int e_shared, int Hq, float scale);
 hipError_t launch_fwd_bf16_split(const FwdArgs& a, int mode, void* workspace, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int D, int mode, hipStream_t s);
@@ -150,10 +150,6 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int D, int mode, hipStream_t s);
 // row pitch (bf16) of the backward's curve table.
 int bwd_lds_bytes(int D, int mode, int bias_range, int R);
 int bwd_curve_pitch(int bias_range);
-// Fast prefill path (head_dim 128, Hq/Hkv a multiple of 4): LDS bytes it needs, or -1
-// when the shape is outside its domain; and its launcher.
-int fwd_fast_lds_bytes(int D, int G, int mode, int bias_range, int R, float scale);
-hipError_t launch_fwd_bf16_fast(const FwdArgs& a, int mode, hipStream_t s);
 hipError_t launch_attn_f32(const F32Args& a, hipStream_t s);
 hipError_t launch_decode_bf16(DecodeArgs a, int D, int mode, hipStream_t s);
 // Decode over MXFP4 caches (D = 128, G <= 16) and the MXFP4 quantiser of bf16 rows
