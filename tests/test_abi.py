@@ -106,13 +106,14 @@ def test_fwd_rejects(lib, kw, code, needle):
 
 
 def test_fwd_workspace_policy(lib):
-    # the input-dependent bias takes a converted copy of E:
-    # heads x (bias_range + 2 * 64 + 1) rows x 8 (R <= 8) or 16 features x 2 bytes, 256-aligned
+    # the input-dependent bias takes a converted copy of E, a bf16 high and low part per feature:
+    # heads x (bias_range + 2 * 64 + 1) rows x 16 (R <= 8) or 32 (R <= 16) entries x 2 bytes,
+    # 256-aligned
     ws = lib.relbias_attn_fwd_workspace_size
-    assert ws(BF16, 2, 4096, 32, 8, 128, 512, 512, 2, 8, 0.088) == 32 * 641 * 8 * 2
-    assert ws(BF16, 2, 4096, 32, 8, 128, 512, 512, 3, 16, 0.088) == (641 * 16 * 2 + 255) // 256 * 256
-    assert ws(BF16, 1, 300, 4, 1, 128, 64, 100, 2, 11, 0.088) == (4 * 229 * 16 * 2 + 255) // 256 * 256
-    assert ws(BF16, 1, 32768, 32, 8, 128, 0, 1024, 2, 8, 0.088) == 32 * 1153 * 8 * 2
+    assert ws(BF16, 2, 4096, 32, 8, 128, 512, 512, 2, 8, 0.088) == 32 * 641 * 16 * 2
+    assert ws(BF16, 2, 4096, 32, 8, 128, 512, 512, 3, 16, 0.088) == (641 * 32 * 2 + 255) // 256 * 256
+    assert ws(BF16, 1, 300, 4, 1, 128, 64, 100, 2, 11, 0.088) == (4 * 229 * 32 * 2 + 255) // 256 * 256
+    assert ws(BF16, 1, 32768, 32, 8, 128, 0, 1024, 2, 8, 0.088) == 32 * 1153 * 16 * 2
     # no converted copy: other bias modes, fp32, shapes outside the kernel
     assert ws(BF16, 2, 4096, 32, 8, 128, 512, 512, 0, 0, 0.088) == 0
     assert ws(BF16, 2, 4096, 32, 8, 128, 512, 512, 1, 0, 0.088) == 0
@@ -289,3 +290,43 @@ def test_fp4_rejects(lib):
     assert dec(vc=P + 4) == EINVAL and "aligned" in rba.last_error()
     assert dec(temp_len=1) == EINVAL and "temp_len" in rba.last_error()
     assert dec(B=0) == 0
+
+
+# --- the binding checks the exact shapes of the bias parameters before any library call -----
+
+def _cpu_inputs(S=16, Hq=4, Hkv=2, D=128, B=1):
+    import torch
+    q = torch.zeros((B, S, Hq, D), dtype=torch.bfloat16)
+    k = torch.zeros((B, S, Hkv, D), dtype=torch.bfloat16)
+    return q, k, k.clone()
+
+
+@pytest.mark.parametrize("mode,shapes,needle", [
+    ("table", dict(table=(4, 7)), "table must be"),         # shorter than bias_range
+    ("table", dict(table=(2, 8)), "table must be"),         # fewer heads than Hq
+    ("rproj", dict(E=(4, 8, 7), r=(1, 16, 4, 8)), "E must be"),
+    ("rproj", dict(E=(3, 8, 8), r=(1, 16, 4, 8)), "E must be"),
+    ("rproj_shared", dict(E=(8, 5), r=(1, 16, 4, 8)), "E must be"),
+    ("rproj", dict(E=(4, 8, 8), r=(1, 16, 4, 6)), "r must end in"),
+])
+def test_binding_checks_bias_shapes(lib, mode, shapes, needle):
+    import torch
+    q, k, v = _cpu_inputs()
+    kw = {n: torch.zeros(s, dtype=torch.float32 if n != "r" else torch.bfloat16) for n, s in shapes.items()}
+    with pytest.raises(ValueError, match=needle):
+        rba.fwd(q, k, v, bias_range=8, mode=mode, **kw)
+    with pytest.raises(ValueError, match=needle):
+        rba.bwd(q, k, v, q, torch.zeros((1, 4, 16)), q, bias_range=8, mode=mode, **kw)
+    qd = torch.zeros((1, 4, 128), dtype=torch.bfloat16)
+    kc = torch.zeros((1, 32, 2, 128), dtype=torch.bfloat16)
+    kwd = dict(kw)
+    if "r" in kwd:
+        kwd["r"] = torch.zeros((1,) + tuple(shapes["r"][2:]), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match=needle):
+        rba.decode(qd, kc, kc, 20, bias_range=8, mode=mode, **kwd)
+
+
+def test_binding_rejects_unknown_mode(lib):
+    q, k, v = _cpu_inputs()
+    with pytest.raises(ValueError, match="unknown bias mode"):
+        rba.fwd(q, k, v, bias_range=8, mode=7)

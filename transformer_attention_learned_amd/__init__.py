@@ -138,20 +138,31 @@ def _stream_handle(device, stream):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _bias_args(mode, table, r, E, Hq, act_dtype, dev):
+def _bias_args(mode, table, r, E, Hq, act_dtype, dev, bias_range):
+    """Bias mode id and R; checks the exact shapes of the bias parameters (the C ABI can not:
+    a table or bank shorter than bias_range or with fewer heads would be read past its end)."""
     import torch
     m = MODES[mode] if isinstance(mode, str) else int(mode)
+    if m not in (0, 1, 2, 3):
+        raise ValueError(f"unknown bias mode {mode!r}")
     R = 0
+    Rb = int(bias_range)
     if m == 1:
         if table is None:
             raise ValueError("mode 'table' needs table [Hq, bias_range]")
         _check(table, "table", dtype=torch.float32, ndim=2, device=dev)
+        if tuple(table.shape) != (Hq, Rb):
+            raise ValueError(f"table must be [Hq, bias_range] = {(Hq, Rb)}, got {tuple(table.shape)}")
     elif m in (2, 3):
         if r is None or E is None:
             raise ValueError("rproj modes need r and E")
         _check(E, "E", dtype=torch.float32, ndim=3 if m == 2 else 2, device=dev)
         _check(r, "r", dtype=act_dtype, device=dev)
         R = int(E.shape[1] if m == 2 else E.shape[0])
+        want = (Hq, R, Rb) if m == 2 else (R, Rb)
+        if tuple(E.shape) != want:
+            raise ValueError(f"E must be {'[Hq, R, bias_range]' if m == 2 else '[R, bias_range]'} = "
+                             f"{want}, got {tuple(E.shape)}")
         if r.shape[-1] != R or r.shape[-2] != Hq:
             raise ValueError(f"r must end in [Hq={Hq}, R={R}], got {tuple(r.shape)}")
     return m, R
@@ -189,7 +200,7 @@ def fwd(q, k, v, *, window=0, bias_range=0, mode="none", table=None, r=None, E=N
     Hkv = k.shape[2]
     if tuple(k.shape) != (B, S, Hkv, D) or tuple(v.shape) != (B, S, Hkv, D):
         raise ValueError(f"k/v must be [B,S,Hkv,D] = {(B, S, Hkv, D)}")
-    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev)
+    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev, bias_range)
     if m in (2, 3) and tuple(r.shape) != (B, S, Hq, R):
         raise ValueError(f"r must be [B,S,Hq,R] = {(B, S, Hq, R)}")
     if scale is None:
@@ -239,7 +250,7 @@ def bwd(q, k, v, o, lse, dout, *, window=0, bias_range=0, mode="none", table=Non
         raise ValueError("o and dout must have q's shape")
     if tuple(lse.shape) != (B, Hq, S):
         raise ValueError(f"lse must be [B,Hq,S] = {(B, Hq, S)}")
-    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev)
+    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev, bias_range)
     if m in (2, 3) and tuple(r.shape) != (B, S, Hq, R):
         raise ValueError(f"r must be [B,S,Hq,R] = {(B, S, Hq, R)}")
     if scale is None:
@@ -305,7 +316,7 @@ def decode_fp4(q, k_codes, k_scales, v_codes, v_scales, kv_len, *, window=0, bia
     if (tuple(k_codes.shape) != (B, L_max, Hkv, D // 2) or v_codes.shape != k_codes.shape or
             tuple(k_scales.shape) != (B, L_max, Hkv, D // 32) or v_scales.shape != k_scales.shape):
         raise ValueError("codes must be [B,L_max,Hkv,D/2] and scales [B,L_max,Hkv,D/32]")
-    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev)
+    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev, bias_range)
     if m in (2, 3) and tuple(r.shape) != (B, Hq, R):
         raise ValueError(f"r must be [B,Hq,R] = {(B, Hq, R)}")
     if scale is None:
@@ -352,7 +363,7 @@ def decode(q, k_cache, v_cache, kv_len, *, window=0, bias_range=0, mode="none", 
     L_max, Hkv = k_cache.shape[1], k_cache.shape[2]
     if tuple(k_cache.shape) != (B, L_max, Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("k_cache/v_cache must be [B,L_max,Hkv,D] matching q")
-    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev)
+    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev, bias_range)
     if m in (2, 3) and tuple(r.shape) != (B, Hq, R):
         raise ValueError(f"r must be [B,Hq,R] = {(B, Hq, R)}")
     if scale is None:
@@ -399,7 +410,7 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens, max_kv_len, *, windo
         raise ValueError("k_pages/v_pages must be [num_pages, page_size, Hkv, D] matching q")
     if block_table.shape[0] != B or kv_lens.shape[0] != B:
         raise ValueError("block_table [B, max_pages] and kv_lens [B] must match q's batch")
-    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev)
+    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev, bias_range)
     if m in (2, 3) and tuple(r.shape) != (B, Hq, R):
         raise ValueError(f"r must be [B,Hq,R] = {(B, Hq, R)}")
     if scale is None:

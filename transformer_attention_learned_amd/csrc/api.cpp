@@ -116,6 +116,99 @@ rba::FwdArgs bf16_fwd_args(const void* q, const void* k, const void* v, void* o,
   return a;
 }
 
+// Decode against a contiguous cache.
+int decode_impl(const char* fn, int dtype, const void* q, const void* k_cache, const void* v_cache,
+                void* o, float* lse, int B, int L_max, int kv_len, int Hq, int Hkv, int D,
+                int window, int bias_range, int mode, const float* table, const void* r,
+                const float* E, int R, float scale, int temp_len, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (B < 0) return fail(RBA_EINVAL, "%s: B=%d must be >= 0", fn, B);
+  int st = check_common(fn, dtype, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale);
+  if (st == RBA_OK) st = check_temp(fn, temp_len);
+  if (st != RBA_OK) return st;
+  if (B == 0) return ok();
+  if (L_max < 1 || kv_len < 1 || kv_len > L_max)
+    return fail(RBA_EINVAL, "%s: need 1 <= kv_len (%d) <= L_max (%d)", fn, kv_len, L_max);
+  if (!q || !k_cache || !v_cache || !o)
+    return fail(RBA_EINVAL, "%s: q, k_cache, v_cache and o must be non-NULL", fn);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(RBA_EINVAL, "%s: q, caches and o must be 16-byte aligned", fn);
+  if (lse && !aligned_to(lse, 4)) return fail(RBA_EINVAL, "%s: lse is not 4-byte aligned", fn);
+  const int G = Hq / Hkv;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == RBA_BF16) {
+    if (G > 32) return fail(RBA_ENOTSUP, "%s: bf16 decode supports Hq/Hkv <= 32, got %d", fn, G);
+    if (Hkv > 65535 || B > 65535) return fail(RBA_ENOTSUP, "%s: grid too large", fn);
+    int ns = 1, kpw = 64;
+    rba::decode_split(B, Hkv, kv_len, window, &ns, &kpw);
+    const size_t need = relbias_attn_decode_workspace_size(B, Hq, Hkv, D, kv_len, window);
+    if (need > 0) {
+      if (!workspace) return fail(RBA_EINVAL, "%s: workspace of %zu bytes required, got NULL", fn, need);
+      if (workspace_bytes < need)
+        return fail(RBA_EINVAL, "%s: workspace too small (%zu < %zu bytes)", fn, workspace_bytes, need);
+      if (!aligned_to(workspace, 4)) return fail(RBA_EINVAL, "%s: workspace is not 4-byte aligned", fn);
+    }
+    rba::DecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k_cache);
+    a.v = static_cast<const uint16_t*>(v_cache);
+    a.o = static_cast<uint16_t*>(o);
+    a.lse = lse;
+    a.table = table;
+    a.r = static_cast<const uint16_t*>(r);
+    a.E = E;
+    a.ws = static_cast<float*>(workspace);
+    a.B = B;
+    a.L_max = L_max;
+    a.kv_len = kv_len;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = G;
+    a.window = window;
+    a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
+    a.R = is_rproj(mode) ? R : 0;
+    a.e_hs = e_head_stride(mode, R, bias_range);
+    a.key_begin = window ? (kv_len > window ? kv_len - window : 0) : 0;
+    a.n_split = ns;
+    a.keys_per_wave = kpw;
+    a.c_qk = scale * rba::kLog2e;
+    a.temp_len = temp_len;
+    a.temp_inv_log2 = temp_inv_log2(temp_len);
+    e = rba::launch_decode_bf16(a, D, kernel_mode(mode), hs);
+  } else {
+    rba::F32Args a{};
+    a.q = static_cast<const float*>(q);
+    a.k = static_cast<const float*>(k_cache);
+    a.v = static_cast<const float*>(v_cache);
+    a.o = static_cast<float*>(o);
+    a.lse = lse;
+    a.table = table;
+    a.r = static_cast<const float*>(r);
+    a.E = E;
+    a.B = B;
+    a.Sq = 1;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = G;
+    a.D = D;
+    a.kv_rows = L_max;
+    a.Lk = kv_len;
+    a.q_pos0 = kv_len - 1;
+    a.window = window;
+    a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
+    a.mode = kernel_mode(mode);
+    a.R = is_rproj(mode) ? R : 0;
+    a.e_hs = e_head_stride(mode, R, bias_range);
+    a.scale = scale;
+    a.temp_len = temp_len;
+    a.temp_inv_log2 = temp_inv_log2(temp_len);
+    e = rba::launch_attn_f32(a, hs);
+  }
+  if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -219,92 +312,9 @@ int relbias_attn_decode(int dtype, const void* q, const void* k_cache, const voi
                         int window, int bias_range, int mode, const float* table, const void* r,
                         const float* E, int R, float scale, int temp_len, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  const char* fn = "relbias_attn_decode";
-  if (B < 0) return fail(RBA_EINVAL, "%s: B=%d must be >= 0", fn, B);
-  int st = check_common(fn, dtype, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale);
-  if (st == RBA_OK) st = check_temp(fn, temp_len);
-  if (st != RBA_OK) return st;
-  if (B == 0) return ok();
-  if (L_max < 1 || kv_len < 1 || kv_len > L_max)
-    return fail(RBA_EINVAL, "%s: need 1 <= kv_len (%d) <= L_max (%d)", fn, kv_len, L_max);
-  if (!q || !k_cache || !v_cache || !o)
-    return fail(RBA_EINVAL, "%s: q, k_cache, v_cache and o must be non-NULL", fn);
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
-    return fail(RBA_EINVAL, "%s: q, caches and o must be 16-byte aligned", fn);
-  if (lse && !aligned_to(lse, 4)) return fail(RBA_EINVAL, "%s: lse is not 4-byte aligned", fn);
-  const int G = Hq / Hkv;
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (dtype == RBA_BF16) {
-    if (G > 32) return fail(RBA_ENOTSUP, "%s: bf16 decode supports Hq/Hkv <= 32, got %d", fn, G);
-    int ns = 1, kpw = 64;
-    rba::decode_split(B, Hkv, kv_len, window, &ns, &kpw);
-    const size_t need = relbias_attn_decode_workspace_size(B, Hq, Hkv, D, kv_len, window);
-    if (need > 0) {
-      if (!workspace) return fail(RBA_EINVAL, "%s: workspace of %zu bytes required, got NULL", fn, need);
-      if (workspace_bytes < need)
-        return fail(RBA_EINVAL, "%s: workspace too small (%zu < %zu bytes)", fn, workspace_bytes, need);
-      if (!aligned_to(workspace, 4)) return fail(RBA_EINVAL, "%s: workspace is not 4-byte aligned", fn);
-    }
-    if (Hkv > 65535 || B > 65535) return fail(RBA_ENOTSUP, "%s: grid too large", fn);
-    rba::DecodeArgs a{};
-    a.q = static_cast<const uint16_t*>(q);
-    a.k = static_cast<const uint16_t*>(k_cache);
-    a.v = static_cast<const uint16_t*>(v_cache);
-    a.o = static_cast<uint16_t*>(o);
-    a.lse = lse;
-    a.table = table;
-    a.r = static_cast<const uint16_t*>(r);
-    a.E = E;
-    a.ws = static_cast<float*>(workspace);
-    a.B = B;
-    a.L_max = L_max;
-    a.kv_len = kv_len;
-    a.Hq = Hq;
-    a.Hkv = Hkv;
-    a.G = G;
-    a.window = window;
-    a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
-    a.R = is_rproj(mode) ? R : 0;
-    a.e_hs = e_head_stride(mode, R, bias_range);
-    a.key_begin = window ? (kv_len > window ? kv_len - window : 0) : 0;
-    a.n_split = ns;
-    a.keys_per_wave = kpw;
-    a.c_qk = scale * rba::kLog2e;
-    a.temp_len = temp_len;
-    a.temp_inv_log2 = temp_inv_log2(temp_len);
-    e = rba::launch_decode_bf16(a, D, kernel_mode(mode), hs);
-  } else {
-    rba::F32Args a{};
-    a.q = static_cast<const float*>(q);
-    a.k = static_cast<const float*>(k_cache);
-    a.v = static_cast<const float*>(v_cache);
-    a.o = static_cast<float*>(o);
-    a.lse = lse;
-    a.table = table;
-    a.r = static_cast<const float*>(r);
-    a.E = E;
-    a.B = B;
-    a.Sq = 1;
-    a.Hq = Hq;
-    a.Hkv = Hkv;
-    a.G = G;
-    a.D = D;
-    a.kv_rows = L_max;
-    a.Lk = kv_len;
-    a.q_pos0 = kv_len - 1;
-    a.window = window;
-    a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
-    a.mode = kernel_mode(mode);
-    a.R = is_rproj(mode) ? R : 0;
-    a.e_hs = e_head_stride(mode, R, bias_range);
-    a.scale = scale;
-    a.temp_len = temp_len;
-    a.temp_inv_log2 = temp_inv_log2(temp_len);
-    e = rba::launch_attn_f32(a, hs);
-  }
-  if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
-  return ok();
+  return decode_impl("relbias_attn_decode", dtype, q, k_cache, v_cache, o, lse, B, L_max, kv_len, Hq,
+                     Hkv, D, window, bias_range, mode, table, r, E, R, scale, temp_len, workspace,
+                     workspace_bytes, stream);
 }
 
 size_t relbias_attn_decode_paged_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len,

@@ -863,10 +863,8 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a, 
 constexpr int kMaxLds = 160 * 1024;
 
 template <typename K>
-hipError_t allow_lds(K* kernel, int bytes) {
-  if (bytes <= 64 * 1024) return hipSuccess;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+hipError_t allow_lds(K* kernel, int bytes, hipStream_t s) {
+  return set_max_lds(reinterpret_cast<const void*>(kernel), bytes, s);
 }
 
 template <int D, int MODE>
@@ -892,11 +890,11 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
     const int lds = (a.R * pitch + 64 * a.R) * 4;
     const long long ng = static_cast<long long>(a.B) * a.Hq * ((a.S + 63) / 64);
     if (a.R > 8) {
-      e = allow_lds(&bwd_curves_kernel<16>, lds);
+      e = allow_lds(&bwd_curves_kernel<16>, lds, s);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(bwd_curves_kernel<16>, dim3(static_cast<unsigned>(ng)), dim3(256), lds, s, a, pitch);
     } else {
-      e = allow_lds(&bwd_curves_kernel<8>, lds);
+      e = allow_lds(&bwd_curves_kernel<8>, lds, s);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(bwd_curves_kernel<8>, dim3(static_cast<unsigned>(ng)), dim3(256), lds, s, a, pitch);
     }
@@ -908,7 +906,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   const int longest_first = (a.window == 0 || a.window > 32 * DQ_WAVES) ? 1 : 0;
   const long long nq = static_cast<long long>(n_qtiles) * a.Hq * a.B;
   const int dq_lds = DqLayout<D, MODE>::bytes(a.bias_range, a.R);
-  e = allow_lds(&bwd_dq_kernel<D, MODE>, dq_lds);
+  e = allow_lds(&bwd_dq_kernel<D, MODE>, dq_lds, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dq_kernel<D, MODE>), dim3(static_cast<unsigned>(nq)), dim3(64 * DQ_WAVES), dq_lds, s,
                      a, n_qtiles, longest_first, pitch);
@@ -916,7 +914,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   // dk, dv
   const int kv_lds = DkvLayout<D>::bytes(MODE, a.bias_range);
-  e = allow_lds(&bwd_dkdv_kernel<D, MODE>, kv_lds);
+  e = allow_lds(&bwd_dkdv_kernel<D, MODE>, kv_lds, s);
   if (e != hipSuccess) return e;
   const int n_ktiles = (a.S + 32 * DKV_WAVES - 1) / (32 * DKV_WAVES);
   const long long nk = static_cast<long long>(n_ktiles) * a.Hkv * a.B;

@@ -733,14 +733,12 @@ hipError_t launch_d(DecodeArgs a, hipStream_t s) {
   if (total > 160 * 1024) return hipErrorInvalidValue;
   // groups of up to 16 query heads: the 16x16 MFMA kernel (two tiles in flight per wave)
   // (FP4 caches: the 16x16 kernel only; the C ABI rejects larger groups)
-  static bool attr_set[2] = {false, false};
   const bool narrow = FP4 || a.G <= 16;
   const void* fn = narrow ? reinterpret_cast<const void*>(&decode16_kernel<D, MODE, RMAX, FP4>)
                           : reinterpret_cast<const void*>(&decode_bf16_kernel<D, MODE, RMAX>);
-  if (!attr_set[narrow]) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  {
+    const hipError_t e = set_max_lds(fn, total, s);
     if (e != hipSuccess) return e;
-    attr_set[narrow] = true;
   }
   if (narrow)
     hipLaunchKernelGGL((decode16_kernel<D, MODE, RMAX, FP4>), grid, dim3(256), total, s, a, curve_off);

@@ -651,7 +651,7 @@ int split_lds(int mode, int Rb) {
 }
 
 template <int MODE, int EW, bool ALLBAND>
-hipError_t launch_split(FwdArgs a, const uint16_t* e2, hipStream_t s) {
+hipError_t launch_split(FwdArgs a, const float* E, void* workspace, hipStream_t s) {
   a.hpw = 4;
   a.rows_wg = ROWS_WG;
   a.n_qtiles = (a.S + ROWS_WG - 1) / ROWS_WG;
@@ -660,12 +660,17 @@ hipError_t launch_split(FwdArgs a, const uint16_t* e2, hipStream_t s) {
   const long long nblk = static_cast<long long>(a.n_qtiles) * a.n_hgroups * a.B;
   if (nblk <= 0) return hipSuccess;
   const int lds = split_lds(MODE, a.bias_range);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_split_kernel<MODE, EW, ALLBAND>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsPerWg);
+  // every check that can fail comes before the first launch
+  hipError_t e = set_max_lds(reinterpret_cast<const void*>(&fwd_split_kernel<MODE, EW, ALLBAND>), lds, s);
+  if (e != hipSuccess) return e;
+  uint16_t* e2 = static_cast<uint16_t*>(workspace);
+  if (MODE == 2) {
+    const int heads = a.e_hs ? a.Hq : 1;
+    const int rows = a.bias_range + 2 * PAD + 1;
+    hipLaunchKernelGGL(e2_convert_kernel, dim3((rows + 255) / 256, heads, EW / 16), dim3(256), 0, s, E,
+                       a.e_hs, a.R, a.bias_range, kLog2e / a.c_qk, EW, e2);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   hipLaunchKernelGGL((fwd_split_kernel<MODE, EW, ALLBAND>), dim3(static_cast<unsigned>(nblk)), dim3(NT), lds, s, a, e2);
   return hipGetLastError();
@@ -686,18 +691,12 @@ long long fwd_split_workspace(int D_, int G, int mode, int Rb, int R, int e_shar
 }
 
 hipError_t launch_fwd_bf16_split(const FwdArgs& a, int mode, void* workspace, hipStream_t s) {
-  if (mode != 2) return mode == 1 ? launch_split<1, 16, false>(a, nullptr, s) : launch_split<0, 16, false>(a, nullptr, s);
-  const int EW = a.R > 8 ? 32 : 16;
-  const int heads = a.e_hs ? a.Hq : 1;
-  uint16_t* e2 = static_cast<uint16_t*>(workspace);
-  const int rows = a.bias_range + 2 * PAD + 1;
-  hipLaunchKernelGGL(e2_convert_kernel, dim3((rows + 255) / 256, heads, EW / 16), dim3(256), 0, s, a.E, a.e_hs,
-                     a.R, a.bias_range, kLog2e / a.c_qk, EW, e2);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (mode == 0) return launch_split<0, 16, false>(a, nullptr, nullptr, s);
+  if (mode == 1) return launch_split<1, 16, false>(a, nullptr, nullptr, s);
   const bool allband = a.window != 0 && a.window <= a.bias_range;
-  if (EW == 32) return allband ? launch_split<2, 32, true>(a, e2, s) : launch_split<2, 32, false>(a, e2, s);
-  return allband ? launch_split<2, 16, true>(a, e2, s) : launch_split<2, 16, false>(a, e2, s);
+  if (a.R > 8)
+    return allband ? launch_split<2, 32, true>(a, a.E, workspace, s) : launch_split<2, 32, false>(a, a.E, workspace, s);
+  return allband ? launch_split<2, 16, true>(a, a.E, workspace, s) : launch_split<2, 16, false>(a, a.E, workspace, s);
 }
 
 }  // namespace rba

@@ -137,6 +137,10 @@ struct BwdArgs {
   float temp_inv_log2;
 };
 
+// Raise a kernel's dynamic-LDS limit to `bytes` (no-op up to 64 KB) on the device of stream s,
+// once per (kernel, device); thread-safe.
+hipError_t set_max_lds(const void* fn, int bytes, hipStream_t s);
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, int D, int mode, void* workspace, hipStream_t s);
 // Workspace bytes the bf16 prefill of this shape takes (0: none); the size query and the launch
 // share it, so both pick the same kernel.
