@@ -153,6 +153,33 @@ int relbias_attn_decode(int dtype, const void* q, const void* k_cache, const voi
                         size_t workspace_bytes, void* stream);
 
 /*
+ * Size of the fixed per-GPU scratch of relbias_attn_decode_noalloc (16 MiB).
+ */
+#define RBA_DECODE_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+
+/*
+ * relbias_attn_decode without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments (minus workspace and workspace_bytes), same kernels and the same results as
+ * relbias_attn_decode; bf16 only (RBA_ENOTSUP for RBA_F32).
+ *
+ * The split partials live in a fixed device array inside the library, one copy per GPU of
+ * RBA_DECODE_NOALLOC_SCRATCH_BYTES, held until the process ends; this call allocates nothing
+ * (no hipMalloc, no allocating library routine).  Sizes whose
+ * relbias_attn_decode_workspace_size(...) exceeds RBA_DECODE_NOALLOC_SCRATCH_BYTES return
+ * RBA_ENOTSUP before anything is launched.  The stream must belong to the current device
+ * (RBA_EINVAL otherwise).  Every call on one GPU shares that GPU's array and the array keeps the
+ * last call's contents (nothing there needs to start at zero): calls that overlap on one GPU
+ * (on different streams, or from several host threads) race and give wrong results; order them
+ * on one stream.
+ */
+int relbias_attn_decode_noalloc(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                                void* o, float* lse, int B, int L_max, int kv_len, int Hq, int Hkv,
+                                int D, int window, int bias_range, int mode, const float* table,
+                                const void* r, const float* E, int R, float scale, int temp_len,
+                                void* stream);
+
+/*
  * Bytes of device workspace relbias_attn_decode_paged needs (0 when none): the
  * launch is sized for max_kv_len, so this is the contiguous size at that length.
  */

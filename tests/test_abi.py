@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
                           "relbias_attn_decode_paged_workspace_size", "relbias_attn_last_error",
                           "relbias_attn_version", "relbias_attn_bwd",
                           "relbias_attn_bwd_workspace_size", "relbias_attn_kv_quantize_fp4",
-                          "relbias_attn_decode_fp4"}
+                          "relbias_attn_decode_fp4", "relbias_attn_decode_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
     assert "gfx950" in rba.version()
@@ -330,3 +330,27 @@ def test_binding_rejects_unknown_mode(lib):
     q, k, v = _cpu_inputs()
     with pytest.raises(ValueError, match="unknown bias mode"):
         rba.fwd(q, k, v, bias_range=8, mode=7)
+
+
+def test_decode_noalloc_rejects(lib):
+    """The allocation-free decode: bf16 only; sizes whose split partials exceed the fixed scratch
+    are refused in host code before anything is launched; the usual argument checks apply."""
+    assert "RBA_DECODE_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)" in open(HEADER).read()
+
+    def dec(**kw):
+        a = dict(dtype=BF16, q=P, k=P, v=P, o=P, lse=None, B=2, L=100, kv_len=50, Hq=8, Hkv=2,
+                 D=128, window=0, bias_range=8, mode=0, table=None, r=None, E=None, R=0, scale=0.1,
+                 temp_len=0, stream=None)
+        a.update(kw)
+        return lib.relbias_attn_decode_noalloc(
+            a["dtype"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["L"], a["kv_len"],
+            a["Hq"], a["Hkv"], a["D"], a["window"], a["bias_range"], a["mode"], a["table"], a["r"],
+            a["E"], a["R"], a["scale"], a["temp_len"], a["stream"])
+    assert dec(dtype=F32, D=64) == ENOTSUP and "bf16 only" in rba.last_error()
+    big = dict(B=8, Hq=32, Hkv=1, L=65536, kv_len=65536)
+    assert lib.relbias_attn_decode_workspace_size(8, 32, 1, 128, 65536, 0) > rba.DECODE_NOALLOC_SCRATCH_BYTES
+    assert dec(**big) == ENOTSUP and "scratch" in rba.last_error()
+    assert dec(kv_len=0) == EINVAL and "kv_len" in rba.last_error()
+    assert dec(q=None) == EINVAL and "non-NULL" in rba.last_error()
+    assert dec(temp_len=1) == EINVAL
+    assert dec(B=0) == 0

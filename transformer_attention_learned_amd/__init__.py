@@ -8,6 +8,7 @@ device memory and streams.  If the library is not built, every call raises.
   fwd(q, k, v, ...)                      prefill, q [B,S,Hq,D], k/v [B,S,Hkv,D]
   decode(q, k_cache, v_cache, kv_len, ...)  one new token per sequence
   decode_workspace_size(...)             scratch bytes decode needs
+  decode_noalloc(q, k_cache, v_cache, kv_len, ...)  decode with the library's fixed scratch
   decode_paged(q, k_pages, v_pages, block_table, kv_lens, max_kv_len, ...)
                                          decode over a paged cache, one length per sequence
 
@@ -22,13 +23,15 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "bwd", "decode", "decode_paged", "decode_fp4", "kv_quantize_fp4",
+__all__ = ["fwd", "bwd", "decode", "decode_noalloc", "decode_paged", "decode_fp4",
+           "kv_quantize_fp4", "DECODE_NOALLOC_SCRATCH_BYTES",
            "decode_workspace_size", "last_error", "version",
            "library_path",
            "load_library", "RBA_OK", "RBA_EINVAL", "RBA_ENOTSUP", "RBA_EHIP", "MODES",
            "LibraryError"]
 
 RBA_OK, RBA_EINVAL, RBA_ENOTSUP, RBA_EHIP = 0, 1, 2, 3
+DECODE_NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024   # RBA_DECODE_NOALLOC_SCRATCH_BYTES
 RBA_F32, RBA_BF16 = 0, 1
 MODES = {"none": 0, "table": 1, "rproj": 2, "rproj_shared": 3}
 
@@ -67,6 +70,9 @@ def load_library():
     lib.relbias_attn_decode.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp, vp,
                                         vp, i, f, i, vp, sz, vp]
     lib.relbias_attn_decode.restype = i
+    lib.relbias_attn_decode_noalloc.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i,
+                                                vp, vp, vp, i, f, i, vp]
+    lib.relbias_attn_decode_noalloc.restype = i
     lib.relbias_attn_decode_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.relbias_attn_decode_workspace_size.restype = sz
     lib.relbias_attn_decode_paged.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i,
@@ -382,6 +388,44 @@ def decode(q, k_cache, v_cache, kv_len, *, window=0, bias_range=0, mode="none", 
                                  _ptr(r if m in (2, 3) else None), _ptr(E if m in (2, 3) else None), R,
                                  float(scale), int(temp_len), _ptr(workspace), wbytes,
                                  _stream_handle(dev, stream))
+    if st != RBA_OK:
+        raise LibraryError(st, last_error())
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_noalloc(q, k_cache, v_cache, kv_len, *, window=0, bias_range=0, mode="none",
+                   table=None, r=None, E=None, scale=None, temp_len=0, out=None, lse=None,
+                   return_lse=False, stream=None):
+    """decode through relbias_attn_decode_noalloc: no workspace, the split partials go to the
+    library's fixed per-GPU scratch (bf16).  Calls that overlap on one GPU race; out (and lse)
+    are allocated here when not given, so a caller that must not allocate passes them."""
+    import torch
+    lib = load_library()
+    dev = q.device
+    _check(q, "q", dtype=torch.bfloat16, ndim=3)
+    _check(k_cache, "k_cache", dtype=q.dtype, ndim=4, device=dev)
+    _check(v_cache, "v_cache", dtype=q.dtype, ndim=4, device=dev)
+    B, Hq, D = q.shape
+    L_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, L_max, Hkv, D) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache/v_cache must be [B,L_max,Hkv,D] matching q")
+    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev, bias_range)
+    if m in (2, 3) and tuple(r.shape) != (B, Hq, R):
+        raise ValueError(f"r must be [B,Hq,R] = {(B, Hq, R)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", dtype=q.dtype, ndim=3, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    _check(lse, "lse", dtype=torch.float32, device=dev)
+    st = lib.relbias_attn_decode_noalloc(RBA_BF16, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                         _ptr(lse), B, L_max, int(kv_len), Hq, Hkv, D, int(window),
+                                         int(bias_range), m, _ptr(table if m == 1 else None),
+                                         _ptr(r if m in (2, 3) else None),
+                                         _ptr(E if m in (2, 3) else None), R, float(scale),
+                                         int(temp_len), _stream_handle(dev, stream))
     if st != RBA_OK:
         raise LibraryError(st, last_error())
     return (out, lse) if (return_lse or lse is not None) else out

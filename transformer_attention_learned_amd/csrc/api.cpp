@@ -116,13 +116,15 @@ rba::FwdArgs bf16_fwd_args(const void* q, const void* k, const void* v, void* o,
   return a;
 }
 
-// Decode against a contiguous cache.
+// Decode against a contiguous cache.  noalloc: the split partials go to the library's fixed
+// per-GPU scratch (relbias_attn_decode_noalloc) instead of the caller's workspace.
 int decode_impl(const char* fn, int dtype, const void* q, const void* k_cache, const void* v_cache,
                 void* o, float* lse, int B, int L_max, int kv_len, int Hq, int Hkv, int D,
                 int window, int bias_range, int mode, const float* table, const void* r,
                 const float* E, int R, float scale, int temp_len, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream, bool noalloc) {
   if (B < 0) return fail(RBA_EINVAL, "%s: B=%d must be >= 0", fn, B);
+  if (noalloc && dtype != RBA_BF16) return fail(RBA_ENOTSUP, "%s: supported for bf16 only", fn);
   int st = check_common(fn, dtype, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale);
   if (st == RBA_OK) st = check_temp(fn, temp_len);
   if (st != RBA_OK) return st;
@@ -143,7 +145,27 @@ int decode_impl(const char* fn, int dtype, const void* q, const void* k_cache, c
     int ns = 1, kpw = 64;
     rba::decode_split(B, Hkv, kv_len, window, &ns, &kpw);
     const size_t need = relbias_attn_decode_workspace_size(B, Hq, Hkv, D, kv_len, window);
-    if (need > 0) {
+    if (noalloc) {
+      if (need > static_cast<size_t>(RBA_DECODE_NOALLOC_SCRATCH_BYTES))
+        return fail(RBA_ENOTSUP,
+                    "%s: these sizes need %zu bytes of split scratch, more than the %d bytes the "
+                    "library holds per GPU; use relbias_attn_decode with a caller workspace",
+                    fn, need, RBA_DECODE_NOALLOC_SCRATCH_BYTES);
+      workspace = nullptr;
+      if (need > 0) {
+        // the scratch copy of the device the stream runs on, which must be the current one
+        int cur = 0, sdev = 0;
+        e = hipGetDevice(&cur);
+        if (e == hipSuccess && hs != nullptr) e = hipStreamGetDevice(hs, &sdev);
+        else sdev = cur;
+        if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
+        if (sdev != cur)
+          return fail(RBA_EINVAL, "%s: the stream belongs to device %d but device %d is current", fn,
+                      sdev, cur);
+        e = rba::decode_noalloc_scratch(&workspace);
+        if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
+      }
+    } else if (need > 0) {
       if (!workspace) return fail(RBA_EINVAL, "%s: workspace of %zu bytes required, got NULL", fn, need);
       if (workspace_bytes < need)
         return fail(RBA_EINVAL, "%s: workspace too small (%zu < %zu bytes)", fn, workspace_bytes, need);
@@ -314,7 +336,17 @@ int relbias_attn_decode(int dtype, const void* q, const void* k_cache, const voi
                         size_t workspace_bytes, void* stream) {
   return decode_impl("relbias_attn_decode", dtype, q, k_cache, v_cache, o, lse, B, L_max, kv_len, Hq,
                      Hkv, D, window, bias_range, mode, table, r, E, R, scale, temp_len, workspace,
-                     workspace_bytes, stream);
+                     workspace_bytes, stream, false);
+}
+
+int relbias_attn_decode_noalloc(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                                void* o, float* lse, int B, int L_max, int kv_len, int Hq, int Hkv,
+                                int D, int window, int bias_range, int mode, const float* table,
+                                const void* r, const float* E, int R, float scale, int temp_len,
+                                void* stream) {
+  return decode_impl("relbias_attn_decode_noalloc", dtype, q, k_cache, v_cache, o, lse, B, L_max,
+                     kv_len, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale, temp_len,
+                     nullptr, 0, stream, true);
 }
 
 size_t relbias_attn_decode_paged_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len,

@@ -19,6 +19,9 @@
 //   * the 4 waves merge (max / sum-exp) through LDS; with several splits the
 //     workgroup writes an unnormalised partial that a second kernel combines.
 
+#include <mutex>
+
+#include "relbias_attn.h"
 #include "rba_device.h"
 #include "rba_internal.h"
 
@@ -751,6 +754,33 @@ hipError_t launch_d(DecodeArgs a, hipStream_t s) {
 }
 
 }  // namespace
+
+// ---- fixed scratch of the allocation-free decode entry point ------------------------------------
+// The split partials of relbias_attn_decode_noalloc live in this file-scope device array instead
+// of a caller workspace: one copy per GPU the library runs on, held until the process ends.  Host
+// code never uses the array's name as an address (in host code it is only a stand-in): the
+// device address comes from hipGetSymbolAddress, once per device with that device current, and
+// is kept per device.
+static __device__ __align__(256) unsigned char scratch[RBA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+hipError_t decode_noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 void decode_split(int B, int Hkv, int kv_len, int window, int* n_split, int* keys_per_wave) {
   // Enough workgroups to keep every CU streaming (2 resident per CU, 4 waves each); a wave

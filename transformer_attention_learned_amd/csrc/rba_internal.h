@@ -161,6 +161,10 @@ hipError_t launch_decode_bf16(DecodeArgs a, int D, int mode, hipStream_t s);
 hipError_t launch_decode_fp4(DecodeArgs a, int mode, hipStream_t s);
 hipError_t launch_quantize_fp4(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long nblk, hipStream_t s);
 
+// Device address of the allocation-free decode's fixed scratch (RBA_DECODE_NOALLOC_SCRATCH_BYTES)
+// on the current device.
+hipError_t decode_noalloc_scratch(void** ptr);
+
 // Decode split policy, shared by the workspace-size query and the launcher.
 void decode_split(int B, int Hkv, int kv_len, int window, int* n_split, int* keys_per_wave);
 
