@@ -53,7 +53,7 @@ constexpr float kRescale = 8.f;   // lazy rescale threshold (log2 units)
 constexpr int KT_BYTES = BN * D * 2;   // K tile: 32 rows of 256 bytes
 constexpr int VT_BYTES = BN * D * 2;   // V tile: 32 rows of 256 bytes
 constexpr int BUF_BYTES = KT_BYTES + VT_BYTES;
-constexpr int CURVE_FLOATS = 32 * 40;   // per wave: 32 skewed fp32 rows of 36 live entries, 40 apart
+constexpr int CURVE_FLOATS = 32 * 36;   // per wave: 32 skewed fp32 rows of 36 entries
 constexpr int CURVE_BYTES = CURVE_FLOATS * 4;
 constexpr int TILE_BYTES = NBUF * BUF_BYTES;
 
@@ -304,12 +304,14 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
   // t = 8 g + 4 lh + k (block 0) and 32 + the same (block 1), t = distance - (c - 31).
   // curve_store writes them to the wave's buffer and reads back the lane's diagonal
   // t = 31 + n - m for its keys m = 8 g + 4 lh + k.  Row n keeps only the t it reads,
-  // n .. n + 31, as entries t - 4 (n / 4) in 0..35 of a 36-entry row; the rows sit 40 entries
-  // apart in an order that makes both the 16-byte writes and the dword reads conflict-free
-  // (row slot ((5 (n / 4 + 2 (n % 4))) % 8) + 8 (n % 4)).  Chunks a row does not read are
-  // not written (a per-lane constant predicate).
-  const int cslot = ((5 * ((ln >> 2) + 2 * (ln & 3))) & 7) + 8 * (ln & 3);
-  const int cbase = 40 * cslot - 4 * (ln >> 2);
+  // n .. n + 31, as entries t - 4 (n / 4) in 0..35 of a 36-entry row.  With n = 4 j + e the row
+  // sits in slot ((3 j + sigma(e)) % 8) + 8 e, sigma = (0, 1, 4, 5): then the dword reads of
+  // each half-wave (32 lanes) hit 32 distinct banks and the 16-byte writes of each group of 8
+  // lanes 8 distinct 4-bank groups (the LDS serves dword reads as 32 banks, half a wave per
+  // clock).  Chunks a row does not read are not written (a per-lane constant predicate).
+  const int cj = ln >> 2, ce = ln & 3;
+  const int cslot = ((3 * cj + (ce & 1) + 4 * (ce >> 1)) & 7) + 8 * ce;
+  const int cbase = 36 * cslot - 4 * cj;
   bool cwrite[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
