@@ -110,32 +110,33 @@ def visible_mask(qpos, kpos, window):
 def bias_matrix(mode, qpos, kpos, bias_range, h, *, table=None, r_rows=None, E=None):
     """Bias beta[i, j] for query head h, float64 [Sq, Sk].
 
-    mode TABLE: table[h, delta] (T5 style; "Learned Relative-Position Bias",
-    section "Standard Relative Bias (T5-style)", causal half only).
-    mode RPROJ: sum_f r_rows[i, f] * E[h, f, delta], i.e. the query token's
-    curve read at the distance ("Thinking Machines dropped RoPE", steps 2-3 and
-    the code listing).  r_rows is r[b, :, h, :] for the query rows, [Sq, R].
-    mode RPROJ_SHARED: the same with one bank E [R, bias_range] for every head
-    (same essay, step 2).
-    All: zero for delta < 0 and delta >= bias_range (same essay, step 4).
+    Only pairs at a distance d = qpos[i] - kpos[j] with 0 <= d < bias_range carry a bias; every
+    other pair (keys ahead of the query, keys at or beyond the range) gets exactly 0 ("Thinking
+    Machines dropped RoPE", step 4).  For an in-band pair:
+      mode TABLE: table[h, d], the learned value of that distance ("Learned Relative-Position
+        Bias", section "Standard Relative Bias (T5-style)", causal half only);
+      mode RPROJ: sum_f r_rows[i, f] * E[h, f, d], the query token's coefficients weighting the
+        bank of distance functions, each read at d ("Thinking Machines dropped RoPE", steps 1-3);
+        r_rows is r[b, :, h, :] for the query rows, [Sq, R];
+      mode RPROJ_SHARED: the same with one bank E [R, bias_range] for every head (same essay,
+        step 2).
     """
     mode = _MODES[mode]
     qpos = np.asarray(qpos, dtype=np.int64)
     kpos = np.asarray(kpos, dtype=np.int64)
-    delta = qpos[:, None] - kpos[None, :]
-    out = np.zeros(delta.shape, dtype=np.float64)
+    out = np.zeros((len(qpos), len(kpos)), dtype=np.float64)
     if mode == MODE_NONE:
         return out
-    inband = (delta >= 0) & (delta < bias_range)
-    idx = np.clip(delta, 0, bias_range - 1)
+    dist = qpos[:, None] - kpos[None, :]
+    ii, jj = np.nonzero((dist >= 0) & (dist < bias_range))     # the in-band pairs
+    d = dist[ii, jj]
     if mode == MODE_TABLE:
-        row = _f64(table)[h]                       # [bias_range]
-        vals = row[idx]
+        out[ii, jj] = _f64(table)[h][d]
     else:
-        bank = _f64(E) if mode == MODE_RPROJ_SHARED else _f64(E)[h]   # [R, bias_range]
-        curves = _f64(r_rows) @ bank               # [Sq, R] @ [R, bias_range] -> [Sq, bias_range]
-        vals = np.take_along_axis(curves, idx, axis=1)
-    out[inband] = vals[inband]
+        bank = _f64(E) if mode == MODE_RPROJ_SHARED else _f64(E)[h]    # [R, bias_range]
+        coef = _f64(r_rows)                                            # [Sq, R]
+        # per pair: the query row's coefficients dotted with the bank column at the distance
+        out[ii, jj] = np.einsum("pf,fp->p", coef[ii], bank[:, d])
     return out
 
 
