@@ -47,7 +47,10 @@ class LibraryError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "librelbias_attn.so")
+    """The in-tree librelbias_attn.so, or the build named by RBA_LIBRARY (for instance the
+    sanitizer build the CPU tests load)."""
+    return os.environ.get("RBA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "librelbias_attn.so")
 
 
 def load_library():

@@ -74,5 +74,53 @@ def build_library(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-only translation units (argument validation, dispatch, per-device state): the sanitizer
+# build instruments these with AddressSanitizer and UndefinedBehaviorSanitizer.
+HOST_SOURCES = ["api.cpp", "launch_attr.cpp"]
+SAN_LIB = os.path.join(BUILD, "san", "librelbias_attn_san.so")
+
+
+def sanitizer_runtime() -> str:
+    """clang's shared AddressSanitizer runtime (it has to be preloaded into the host process)."""
+    import glob
+    cands = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(hipcc())), "llvm", "lib",
+                                          "clang", "*", "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    if not cands:
+        raise RuntimeError("clang's libclang_rt.asan-x86_64.so not found under the ROCm tree")
+    return cands[-1]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """A copy of the library whose host code (HOST_SOURCES) is built with -fsanitize=address and
+    -fsanitize=undefined (host pass only), linked with the ordinary kernel objects; for the
+    CPU-tier validation tests.  Builds the ordinary objects first if they are missing."""
+    os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
+    dev_objs = [os.path.join(BUILD, s + ".o") for s in SOURCES if s not in HOST_SOURCES]
+    if not all(os.path.exists(o) for o in dev_objs):
+        build_library(verbose)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+    objs = []
+    for src in HOST_SOURCES:
+        out = os.path.join(BUILD, "san", src + ".o")
+        cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", out] + _flags() + san
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitized compile of {src} failed:\n{r.stdout}{r.stderr}")
+        objs.append(out)
+    clangxx = os.path.join(os.path.dirname(os.path.dirname(hipcc())), "llvm", "bin", "clang++")
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(hipcc())), "lib")
+    cmd = [clangxx, "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libsan", "-o",
+           SAN_LIB + ".tmp"] + objs + dev_objs + ["-L", rocm_lib, "-lamdhip64",
+                                                  "-Wl,-rpath," + rocm_lib]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitized link failed:\n" + r.stdout + r.stderr)
+    os.replace(SAN_LIB + ".tmp", SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     print(build_library(verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
