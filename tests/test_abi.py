@@ -260,9 +260,12 @@ def test_bwd_empty_and_workspace(lib):
     assert _bwd(lib, S=0, q=None) == 0
     assert lib.relbias_attn_bwd_workspace_size(2, 100, 8, 0, 64) == 6400       # rowsum only
     assert lib.relbias_attn_bwd_workspace_size(2, 100, 8, 1, 64) == 6400
-    # r.E: plus the bf16 curve table, rows of 32 + 512 + 64 distances
-    assert lib.relbias_attn_bwd_workspace_size(2, 100, 8, 2, 512) == 6400 + 1600 * 608 * 2
-    assert lib.relbias_attn_bwd_workspace_size(2, 100, 8, 3, 77) == 6400 + 1600 * 176 * 2
+    # r.E: plus E as bf16 high and low parts, heads x (bias_range + 129) rows x 32 entries x 2
+    # bytes: independent of the sequence length (one bank for the shared form)
+    assert lib.relbias_attn_bwd_workspace_size(2, 100, 8, 2, 512) == 6400 + 8 * 641 * 32 * 2
+    assert lib.relbias_attn_bwd_workspace_size(2, 100, 8, 3, 77) == 6400 + 1 * 206 * 32 * 2
+    assert (lib.relbias_attn_bwd_workspace_size(1, 1 << 20, 32, 2, 1024) ==
+            (1 << 20) * 32 * 4 + 32 * 1153 * 32 * 2)
     assert lib.relbias_attn_bwd_workspace_size(0, 100, 8, 2, 64) == 0
 
 

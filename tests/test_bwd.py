@@ -2,10 +2,13 @@
 oracle's gradients (oracle.prefill_backward), on the same seeded inputs.
 
 The library's forward provides o and lse; the oracle recomputes everything in float64 from
-q, k, v, dout and the bias parameters.  Bar for every gradient tensor: relative L2 error
-<= 1e-2 and max |err| <= 2e-2 * max |reference| (bf16 rounding of P and dZ before the MFMAs,
-and of the stored o in rowsum(dout * o), each about 2^-9 relative), with floors (RMS 1e-3,
-maximum 1e-2) for references that vanish.
+q, k, v, dout and the bias parameters.  Bar per gradient tensor: relative L2 error <= 5e-3 (the
+forward's bar) and max |err| <= 2e-2 * max |reference|, with floors (RMS 1e-3, maximum 1e-2)
+for references that vanish.  The kernels round P and dZ to bf16 before the MFMAs, and the
+stored o enters rowsum(dout * o), each about 2^-9 relative; the bias reaches the recomputed
+logits in fp32 (E as a bf16 high and low part).  dr takes 7.5e-3: its product adds two more
+bf16 operands (E and the diagonal sums of dZ, each rounded once more), and with a sharp bias
+(E at std 1.0) it measures about 5e-3.
 """
 
 import sys
@@ -21,7 +24,7 @@ from transformer_attention_learned_amd.workloads import WORKLOADS, Workload, mak
 
 pytestmark = pytest.mark.gpu
 
-REL_L2, MAX_REL = 1e-2, 2e-2
+REL_L2, REL_L2_DR, MAX_REL = 5e-3, 7.5e-3, 2e-2
 
 
 def _say(msg):
@@ -70,7 +73,8 @@ def compare(name, got, ref):
     max_rel = float(np.abs(got - ref).max()) / scale
     rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-3 * np.sqrt(ref.size)))
     _say(f"    {name}: rel_l2={rel:.3e} max_err/max_ref={max_rel:.3e}")
-    assert rel <= REL_L2 and max_rel <= MAX_REL, (name, rel, max_rel)
+    bar = REL_L2_DR if name.startswith("dr") else REL_L2
+    assert rel <= bar and max_rel <= MAX_REL, (name, rel, max_rel)
 
 
 def check_bwd(w: Workload, heads=None):
@@ -132,6 +136,25 @@ SWEEP = [
     dict(S=1000, temp_len=100), dict(S=333, mode="table", bias_range=100, temp_len=2),
     dict(S=600, window=300, temp_len=64, mode="rproj_shared", R=8),
 ]
+
+
+# Sharp input-dependent biases (E drawn with std 0.5 and 1.0: a bias RMS of about 1.4 and 2.8 at
+# R = 8), the per-token sharp locality the input-dependent form is for ("Thinking Machines
+# dropped RoPE", the paragraph after the code listing); a table drawn with std 3 as the control.
+SHARP = [
+    dict(S=1100, Hq=8, Hkv=2, window=512, bias_range=512, e_std=0.5),
+    dict(S=1100, Hq=8, Hkv=2, window=512, bias_range=512, e_std=1.0),
+    dict(S=1300, bias_range=1024, e_std=1.0),
+    dict(S=700, mode="rproj_shared", R=16, window=512, bias_range=512, e_std=1.0, Hq=8, Hkv=2,
+         logit_scale="inv_d"),
+    dict(S=600, window=300, bias_range=200, e_std=1.0, R=11, Hq=6, Hkv=2),
+    dict(S=600, mode="table", bias_range=300, table_std=3.0),
+]
+
+
+@pytest.mark.parametrize("kw", SHARP, ids=lambda kw: "-".join(f"{k}{v}" for k, v in kw.items()))
+def test_bwd_sharp_bias(kw):
+    check_bwd(small(seed=zlib.crc32(repr(sorted(kw.items())).encode()) % 10007, **kw))
 
 
 @pytest.mark.parametrize("kw", SWEEP, ids=lambda kw: "-".join(f"{k}{v}" for k, v in kw.items()))

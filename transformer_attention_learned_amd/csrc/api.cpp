@@ -518,8 +518,8 @@ size_t relbias_attn_bwd_workspace_size(int B, int S, int Hq, int mode, int bias_
   if (B <= 0 || S <= 0 || Hq <= 0) return 0;
   const size_t rows = static_cast<size_t>(B) * S * Hq;
   size_t n = (rows * sizeof(float) + 255) / 256 * 256;       // rowsum(dout * o)
-  if (is_rproj(mode) && bias_range > 0)                      // curve table, bf16
-    n += rows * static_cast<size_t>(rba::bwd_curve_pitch(bias_range)) * 2;
+  if (is_rproj(mode) && bias_range > 0)                      // E as bf16 high and low parts (R <= 16)
+    n += static_cast<size_t>(rba::e2_bytes(mode == RBA_BIAS_RPROJ_SHARED ? 1 : Hq, bias_range, 32));
   return n;
 }
 
@@ -576,7 +576,7 @@ int relbias_attn_bwd(int dtype, const void* q, const void* k, const void* v, con
   a.E = E;
   a.e_hs = e_head_stride(mode, R, bias_range);
   a.dsum = static_cast<float*>(workspace);
-  a.ctab = is_rproj(mode)
+  a.e2 = is_rproj(mode)
       ? reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(workspace) +
                                     (static_cast<size_t>(B) * S * Hq * sizeof(float) + 255) / 256 * 256)
       : nullptr;

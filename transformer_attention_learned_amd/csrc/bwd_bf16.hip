@@ -14,17 +14,19 @@
 //
 // Kernels on one stream:
 //   * bwd_pre: rowsum(dO * O) per (batch, head, row) into the workspace, and zero dE / dtable.
-//   * bwd_curves (input-dependent bias only): the curve table C[b, h, i, d] = r_i . E[h, :, d]
-//     for every row and distance d < bias_range, bf16, with zero distances on both sides of a
-//     row, in the workspace.  The two main kernels read the bias from it instead of forming
-//     the curves again block by block (the forward forms them once, the backward would form
-//     them twice); for the local layer it is 2 * 32 * 4096 rows of 608 bf16, about 320 MB.
+//   * the input-dependent bias r_i . E[h, :, d] is formed inside both main kernels, block by
+//     block, the way the forward forms it: E is converted once per call into the workspace as a
+//     bf16 high and low part (the forward's conversion, at scale 1: about 16 mantissa bits,
+//     heads x (bias_range + 129) rows, independent of the sequence length), and an in-band
+//     32 x 32 block forms the curves of its 32 query rows over its 64 distances with MFMAs over
+//     the features (fp32 results), writes them to a wave-private LDS buffer and reads its
+//     diagonal back, so the bias reaches the recomputed logits with fp32 accuracy.
 //   * bwd_dq: one workgroup = 4 waves x 32 query rows of one head (the forward's transposed
 //     layout: S^T = K Q^T, so each lane owns one query row and its lse, rowsum and temperature
 //     are scalars).  Per 32 x 32 block it recomputes S^T and dP^T = V dO^T, forms dZ^T and
 //     accumulates dQ^T += K^T dZ^T (K^T in LDS with the key permutation of the forward's V^T).
-//     A lane's 16 bias values sit at 4 runs of 4 consecutive distances of its own curve row:
-//     four 8-byte loads.  In-band blocks also write dZ into two wave-private skewed buffers,
+//     A lane's 16 bias values lie on its own query row's curve (the forward's skewed curve
+//     buffer layout).  In-band blocks also write dZ into two wave-private skewed buffers,
 //     G[query][distance] and its transpose, over the block's 64-distance window; then
 //       dr^T += E G^T            (one MFMA per 16 distances; E staged in LDS, curve-major)
 //       dE   += r^T G  per 32 distances (A = r^T, held in registers for the wave's rows),
@@ -36,8 +38,9 @@
 //     lane owns one key), K and V held in registers as B operands; Q, dO and their transposes
 //     in LDS; per-row lse, rowsum and temperature from LDS.  dV^T += dO^T P and dK^T += Q^T dZ
 //     take P and dZ straight from the registers the score MFMAs left them in.  The bias comes
-//     from the table row staged in LDS, or from the curve table (one 2-byte load per element,
-//     issued before the score MFMAs).
+//     from the table row staged in LDS, or from the block's curves (the B operand of their MFMA
+//     is r of the block's 32 query rows; a lane reads its key's value from each of the 16 rows
+//     it holds, 32 consecutive dwords per row and half-wave).
 
 #include <algorithm>
 
@@ -130,71 +133,75 @@ __device__ __forceinline__ void store_rows(const u32x4 (&pre)[NIT][4], uint16_t*
   }
 }
 
-// Row of the curve table: CPAD_L zero distances, the bias_range curve values, CPAD_R zeros.
-constexpr int CPAD_L = 32;
-constexpr int CPAD_R = 64;
+// ---- input-dependent bias, formed per 32 x 32 block (shared by the dq and dk/dv kernels) -------
+// The E rows of a block come from the converted copy (kE2Pad zero distances on each side, EW =
+// e2_width(R) entries per row: the high part of the features, then the low part).  A curve MFMA
+// pairs lane half lh's 8 K-elements of A (E) with the same lane half of B (r), so with EW = 16
+// lane half 0 carries hi * r and lane half 1 lo * r (B holds r[0..7] in both halves); with
+// EW = 32 a first MFMA takes hi and a second lo, lane half lh carrying features 8 lh .. 8 lh + 7.
+constexpr int CURVE_ROWS_DQ = 36;    // floats per query row, dq kernel (the forward's packed layout)
+constexpr int CURVE_ROWS_KV = 40;    // floats per query row, dk/dv kernel
+constexpr int CURVE_BYTES_DQ = 32 * CURVE_ROWS_DQ * 4;
+constexpr int CURVE_BYTES_KV = 32 * CURVE_ROWS_KV * 4;
 
-// ---- curve table: C[b, h, i, d] = sum_f r[b, i, h, f] E[h, f, d] ---------------------------------
-// One workgroup per (batch, head, 64 rows): E[h] staged in LDS (fp32) in the table's own column
-// layout (zero outside [0, bias_range)), and the rows' r; a thread holds the E values of 8
-// consecutive columns (RM curves, RM >= R) in registers and writes those columns for every
-// (256 / chunks)-th row: one 16-byte store per row, the row's r read from LDS.
-template <int RM>
-__global__ __launch_bounds__(256) void bwd_curves_kernel(BwdArgs a, int pitch) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  float* es = reinterpret_cast<float*>(smem);                  // [R][pitch]
-  float* rsh = es + a.R * pitch;                               // [64][R]
-  const int Rb = a.bias_range;
-  const int ntile = (a.S + 63) / 64;
-  const int tile = blockIdx.x % ntile;
-  const int bh = blockIdx.x / ntile;                           // b * Hq + h
-  const int h = bh % a.Hq;
-  const int b = bh / a.Hq;
-  const int i0 = tile * 64;
-  const float* Eh = a.E + static_cast<size_t>(h) * a.e_hs;
-  for (int x = threadIdx.x; x < a.R * pitch; x += 256) {
-    const int f = x / pitch;
-    const int d = x - f * pitch - CPAD_L;
-    es[x] = (d >= 0 && d < Rb) ? Eh[static_cast<size_t>(f) * Rb + d] : 0.f;
-  }
-  for (int x = threadIdx.x; x < 64 * a.R; x += 256) {
-    const int rr = x / a.R;
-    const int f = x - rr * a.R;
-    const int i = i0 + rr;
-    rsh[x] = i < a.S ? bf16_to_f32(a.r[((static_cast<size_t>(b) * a.S + i) * a.Hq + h) * a.R + f]) : 0.f;
-  }
-  __syncthreads();
-  // thread -> (column chunk, row phase): the chunk's E values (R x 8) stay in registers and the
-  // rows are walked with a stride of the phase count, so each 16-byte store costs two LDS reads
-  // (the row's r) instead of two per curve
-  const int chunks = pitch / 8;
-  const int rows = min(64, a.S - i0);
-  const int cpt = min(chunks, 256);         // chunks side by side
-  const int phases = 256 / cpt;             // rows side by side
-  const int ph = threadIdx.x / cpt;
-  if (ph >= phases) return;
-  uint16_t* out = a.ctab + (static_cast<size_t>(bh) * a.S + i0) * pitch;
-  for (int ch = threadIdx.x % cpt; ch < chunks; ch += cpt) {
-    const int t0 = 8 * ch;
-    f32x4 e0[RM], e1[RM];
+typedef __attribute__((address_space(3))) float lds_float;
+
+// r fragment (B operand) of query row `row`: EW = 16: features 0..7 in both lane halves;
+// EW = 32: features 8 lh .. 8 lh + 7; zero past R and for rows at or past S.
+template <int EW>
+__device__ __forceinline__ bf16x8 r_frag(const BwdArgs& a, int b, int h, int row, int lh) {
+  const int f0 = (EW == 32) ? 8 * lh : 0;
+  uint32_t w[4];
+  const uint16_t* rp = a.r + ((static_cast<size_t>(b) * a.S + (row < a.S ? row : 0)) * a.Hq + h) * a.R;
 #pragma unroll
-    for (int f = 0; f < RM; ++f) {
-      const bool fl = f < a.R;
-      e0[f] = fl ? *reinterpret_cast<const f32x4*>(es + f * pitch + t0) : f32x4{0.f, 0.f, 0.f, 0.f};
-      e1[f] = fl ? *reinterpret_cast<const f32x4*>(es + f * pitch + t0 + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int rr = ph; rr < rows; rr += phases) {
-      f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
+  for (int jj = 0; jj < 4; ++jj) {
+    const int f = f0 + 2 * jj;
+    const uint32_t lo = (row < a.S && f < a.R) ? rp[f] : 0u;
+    const uint32_t hi = (row < a.S && f + 1 < a.R) ? rp[f + 1] : 0u;
+    w[jj] = lo | (hi << 16);
+  }
+  return as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+}
+
+// E rows of a block whose distances are c - 31 + l (block 0) and c + 1 + l (block 1) for the
+// 32 lanes l; c lies in [-31, bias_range + 30] for every in-band block, so the rows read lie
+// inside the padded rows.  e2h: the head's converted rows at distance 0.
+template <int EW>
+__device__ __forceinline__ void e_rows(const uint16_t* e2h, int c, int ln, int lh, u32x4 (&e)[2][EW / 16]) {
+  const uint16_t* ep = e2h + (c - 31 + ln) * EW + 8 * lh;
 #pragma unroll
-      for (int f = 0; f < RM; ++f) {
-        const float rv = f < a.R ? rsh[rr * a.R + f] : 0.f;
-        v0 += rv * e0[f];
-        v1 += rv * e1[f];
-      }
-      st16(out + static_cast<size_t>(rr) * pitch + t0,
-           u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v1[0], v1[1]),
-                 pack_bf16x2(v1[2], v1[3])});
-    }
+  for (int u = 0; u < EW / 16; ++u) {
+    e[0][u] = ld16(ep + 16 * u);
+    e[1][u] = ld16(ep + 32 * EW + 16 * u);
+  }
+}
+
+// The curves of the block's 32 query rows over its 64 distances, fp32: lane (n, lh) gets row n
+// (the B operand's column) at t = 8 g + 4 lh + k (lo) and 32 + the same (hi), t = distance -
+// (c - 31).
+template <int EW>
+__device__ __forceinline__ void curve_mfma(const u32x4 (&e)[2][EW / 16], const bf16x8& rf, f32x16& lo, f32x16& hi) {
+  lo = mfma32(as_bf16x8(e[0][0]), rf, zero16());
+  hi = mfma32(as_bf16x8(e[1][0]), rf, zero16());
+#pragma unroll
+  for (int u = 1; u < EW / 16; ++u) {
+    lo = mfma32(as_bf16x8(e[0][u]), rf, lo);
+    hi = mfma32(as_bf16x8(e[1][u]), rf, hi);
+  }
+}
+
+// Writes of the curve chunks row n reads back (t = n .. n + 31): chunk u (t from 32 (u / 4) +
+// 8 (u % 4) + 4 lh) is written iff it overlaps that range; row n's entry t goes to
+// row_base + t - 4 (n / 4).  Per-lane constant predicates (exec masks, no branches).
+__device__ __forceinline__ void curve_write(float* row_base, int n, int lh, const f32x16& lo, const f32x16& hi) {
+  float* wp = row_base - 4 * (n >> 2) + 4 * lh;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int t0 = 8 * g + 4 * lh;
+    if (__builtin_expect(t0 + 3 >= n, 1))
+      st16(wp + 8 * g, __builtin_bit_cast(u32x4, f32x4{lo[4 * g], lo[4 * g + 1], lo[4 * g + 2], lo[4 * g + 3]}));
+    if (__builtin_expect(t0 + 32 <= n + 31, 1))
+      st16(wp + 32 + 8 * g, __builtin_bit_cast(u32x4, f32x4{hi[4 * g], hi[4 * g + 1], hi[4 * g + 2], hi[4 * g + 3]}));
   }
 }
 
@@ -255,7 +262,8 @@ struct DqLayout {
   static constexpr int TILE_BYTES = (2 * BN * KST + D * TST) * 2;
   static constexpr int G_BYTES = (MODE == 2) ? 32 * GST * 2 : 0;
   static constexpr int GT_BYTES = (MODE != 0) ? 64 * GTS * 2 : 0;
-  static constexpr int WAVE_BYTES = G_BYTES + GT_BYTES;
+  static constexpr int C_BYTES = (MODE == 2) ? CURVE_BYTES_DQ : 0;   // the block's curves (fp32)
+  static constexpr int WAVE_BYTES = G_BYTES + GT_BYTES + C_BYTES;
   static constexpr int FIXED = TILE_BYTES + DQ_WAVES * WAVE_BYTES;
   static int bytes(int Rb, int R) {
     int n = FIXED;
@@ -267,8 +275,8 @@ struct DqLayout {
   __host__ __device__ static int ef_stride(int Rb) { return (Rb + 2 * PADE + 7) & ~7; }
 };
 
-template <int D, int MODE>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles, int longest_first, int pitch) {
+template <int D, int MODE, int EW>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles, int longest_first) {
   using L = DqLayout<D, MODE>;
   constexpr int KST = L::KST;
   constexpr int TST = L::TST;
@@ -288,6 +296,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
   unsigned char* wsp = smem + L::TILE_BYTES + wave * L::WAVE_BYTES;
   uint16_t* Gs = reinterpret_cast<uint16_t*>(wsp);
   uint16_t* GTs = reinterpret_cast<uint16_t*>(wsp + L::G_BYTES);
+  float* cbuf = reinterpret_cast<float*>(wsp + L::G_BYTES + L::GT_BYTES);   // r.E: the block's curves
   float* tabs = reinterpret_cast<float*>(smem + L::FIXED);                 // table mode
   uint16_t* ef = reinterpret_cast<uint16_t*>(smem + L::FIXED);             // r.E
 
@@ -319,10 +328,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
   const uint16_t* vbase = a.v + static_cast<size_t>(b) * S * kv_row + static_cast<size_t>(hkv) * D;
   const size_t qoff = (static_cast<size_t>(b) * S + (row_ok ? row : 0)) * q_row + static_cast<size_t>(h) * D;
   const float* Eh = (MODE == 2) ? a.E + static_cast<size_t>(h) * a.e_hs : nullptr;
-  // this lane's curve row (rows past the end read the last row; their P is zero)
-  const uint16_t* crow = (MODE == 2)
-      ? a.ctab + ((static_cast<size_t>(b) * a.Hq + h) * S + (row_ok ? row : S - 1)) * pitch + CPAD_L
+  // r.E: the head's converted E rows at distance 0, the lane's r fragment (its own query row),
+  // and the curve buffer geometry (the forward's packed rows: row n in slot
+  // ((3 (n / 4) + sigma(n % 4)) % 8) + 8 (n % 4), 36 entries, entry t - 4 (n / 4))
+  const uint16_t* e2h = (MODE == 2)
+      ? a.e2 + (static_cast<size_t>(a.e_hs ? h : 0) * (Rb + 2 * kE2Pad + 1) + kE2Pad) * EW
       : nullptr;
+  bf16x8 rf = {};
+  const lds_float* crd = nullptr;
+  float* crow_w = nullptr;
+  if (MODE == 2) {
+    rf = r_frag<EW>(a, b, h, row, lh);
+    const int cj = ln >> 2, ce = ln & 3;
+    const int cslot = ((3 * cj + (ce & 1) + 4 * (ce >> 1)) & 7) + 8 * ce;
+    crow_w = cbuf + CURVE_ROWS_DQ * cslot;
+    crd = (const lds_float*)(crow_w - 4 * cj + 4 + ln - 4 * lh);
+    asm volatile("" : "+v"(crd));   // one base register, immediate offsets for the reads
+  }
 
   // bias parameters of the head in LDS (made visible by the first barrier of the tile loop)
   if (MODE == 1) {
@@ -438,17 +460,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
       if (!on) continue;
       const bool inband = (MODE != 0) && (c - 31 < Rb);
 
-      // r.E bias: distances c + ln - (8 g + 4 lh + u) of the lane's curve row, four runs of 4
-      // (8-byte loads; the distances lie in [-31, Rb + 61], inside the padded row)
-      u32x2 braw[4];
-      if (MODE == 2 && inband) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          u32x2 x;
-          __builtin_memcpy(&x, crow + c + ln - 8 * g4 - 4 * lh - 3, 8);
-          braw[g4] = x;
-        }
-      }
+      // r.E bias: the block's E rows, requested before the score MFMAs
+      u32x4 eb[2][EW / 16];
+      if (MODE == 2 && inband) e_rows<EW>(e2h, c, ln, lh, eb);
 
       // operands read one step ahead of the MFMAs that use them
       f32x16 sacc = zero16(), pacc = zero16();
@@ -477,15 +491,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
         for (int i = 0; i < 16; ++i) sacc[i] = fmaf(tb[-out_row(i, lh)], tq, sacc[i]);
       }
       if (MODE == 2 && inband) {
-        // element u of run g4 is distance (start + 3 - u): the high half of word 1 for u = 0
+        // curves of the wave's 32 rows over the block's distances c - 31 .. c + 32, fp32; key
+        // m = 8 g + 4 lh + k of row n at distance c + n - m, entry t = 31 + n - m of row n
+        f32x16 clo, chi;
+        curve_mfma<EW>(eb, rf, clo, chi);
+        curve_write(crow_w, ln, lh, clo, chi);
+        wave_sync_lds();
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const uint32_t w = braw[g4][(3 - u) >> 1];
-            const float beta = __uint_as_float(((3 - u) & 1) ? (w & 0xffff0000u) : (w << 16));
-            sacc[4 * g4 + u] = fmaf(beta, cb, sacc[4 * g4 + u]);
-          }
+        for (int i = 0; i < 16; ++i) sacc[i] = fmaf(crd[27 - 8 * (i >> 2) - (i & 3)], cb, sacc[i]);
+        wave_sync_lds();   // the next block's writes follow these reads
       }
       // P and dS = P * (dP - rowsum); the temperature factor of dZ = tau dS is applied to the
       // accumulated dq and to the bias-gradient inputs
@@ -599,11 +613,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
 template <int D>
 struct DkvLayout {
   static constexpr int TILES = (2 * BN * (D + 8) + 2 * D * (BN + 8)) * 2 + 4 * BN * 4;
-  static int bytes(int mode, int Rb) { return TILES + (mode == 1 ? (Rb + 2 * PADT) * 4 : 0); }
+  // table mode: the head's table row; r.E: a curve buffer per wave
+  static int bytes(int mode, int Rb) {
+    return TILES + (mode == 1 ? (Rb + 2 * PADT) * 4 : 0) + (mode == 2 ? DKV_WAVES * CURVE_BYTES_KV : 0);
+  }
 };
 
-template <int D, int MODE>
-__global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a, int pitch) {
+template <int D, int MODE, int EW>
+__global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using L = DkvLayout<D>;
   constexpr int QST = D + 8;
   constexpr int TST = BN + 8;
@@ -642,6 +659,17 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a, 
   const size_t q_row = static_cast<size_t>(a.Hq) * D;
   const size_t kv_row = static_cast<size_t>(a.Hkv) * D;
   const size_t koff = (static_cast<size_t>(b) * S + (key_ok ? key : 0)) * kv_row + static_cast<size_t>(hkv) * D;
+
+  // r.E: the wave's curve buffer, query row m at 40 m + t - 4 (m / 4) (entries t = m .. m + 31
+  // of the row are written); key n reads row m at t = 31 + m - n, which for element i (query
+  // m = 8 g + 4 lh + k) is 320 g + 41 k + 160 lh + 31 - n: one base register per lane and
+  // immediate offsets, and each half-wave reads 32 consecutive dwords of one row
+  float* cbuf = (MODE == 2) ? reinterpret_cast<float*>(smem + L::TILES) + wave * (CURVE_BYTES_KV / 4) : nullptr;
+  const lds_float* crd = nullptr;
+  if (MODE == 2) {
+    crd = (const lds_float*)(cbuf + 160 * lh + 31 - ln);
+    asm volatile("" : "+v"(crd));
+  }
 
   // K^T and V^T fragments (B operands): lane (n = ln, lh) holds x[key][16c + 8lh .. +7]
   bf16x8 kf[NC], vf[NC];
@@ -715,8 +743,10 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a, 
     __syncthreads();
     if (st + 1 < nsteps) load_step(st + 1);
     if (!wave_live) continue;
-    // curve rows of this step's queries (rows past the end read the last row; P is zero there)
-    const uint16_t* cplane = (MODE == 2) ? a.ctab + (static_cast<size_t>(b) * a.Hq + h) * S * pitch + CPAD_L : nullptr;
+    // r.E: the head's converted E rows at distance 0
+    const uint16_t* e2h = (MODE == 2)
+        ? a.e2 + (static_cast<size_t>(a.e_hs ? h : 0) * (Rb + 2 * kE2Pad + 1) + kE2Pad) * EW
+        : nullptr;
 
 #pragma unroll 1
     for (int qb = 0; qb < 2; ++qb) {
@@ -727,16 +757,14 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a, 
       if (!on) continue;
       const bool inband = (MODE != 0) && (c - 31 < Rb);
 
-      // r.E bias of element (query m, key ln): curve row i0b + m at distance c + m - ln, in
-      // [-31, Rb + 61]; issued before the score MFMAs
-      uint16_t braw[16];
+      // r.E bias of element (query m, key ln) at distance c + m - ln: the block's E rows and r
+      // of its query rows (B operand column ln = query i0b + ln), requested before the score
+      // MFMAs
+      u32x4 eb[2][EW / 16];
+      bf16x8 rq = {};
       if (MODE == 2 && inband) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = out_row(i, lh);
-          const int rr = min(i0b + m, S - 1);
-          braw[i] = cplane[static_cast<size_t>(rr) * pitch + c + m - ln];
-        }
+        e_rows<EW>(e2h, c, ln, lh, eb);
+        rq = r_frag<EW>(a, b, h, i0b + ln, lh);
       }
 
       // operands read one step ahead of the MFMAs that use them
@@ -767,8 +795,13 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a, 
         for (int i = 0; i < 16; ++i) bias[i] = tb[out_row(i, lh)];
       }
       if (MODE == 2 && inband) {
+        f32x16 clo, chi;
+        curve_mfma<EW>(eb, rq, clo, chi);
+        curve_write(cbuf + CURVE_ROWS_KV * ln, ln, lh, clo, chi);
+        wave_sync_lds();
 #pragma unroll
-        for (int i = 0; i < 16; ++i) bias[i] = bf16_to_f32(braw[i]) * kLog2e;
+        for (int i = 0; i < 16; ++i) bias[i] = crd[320 * (i >> 2) + 41 * (i & 3)] * kLog2e;
+        wave_sync_lds();   // the next block's writes follow these reads
       }
       // P into sacc, dZ = tau * P * (dP - rowsum) into pacc (in place); per row: lse (log2
       // units), rowsum, c_qk * tau and tau (tau = 1 without a temperature).  Interior and
@@ -867,7 +900,7 @@ hipError_t allow_lds(K* kernel, int bytes, hipStream_t s) {
   return set_max_lds(reinterpret_cast<const void*>(kernel), bytes, s);
 }
 
-template <int D, int MODE>
+template <int D, int MODE, int EW>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   // pre pass
   float* zero_ptr = nullptr;
@@ -885,20 +918,8 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(pre_grid), dim3(256), 0, s, a, zero_ptr, n_zero);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int pitch = bwd_curve_pitch(a.bias_range);
-  if (MODE == 2) {
-    const int lds = (a.R * pitch + 64 * a.R) * 4;
-    const long long ng = static_cast<long long>(a.B) * a.Hq * ((a.S + 63) / 64);
-    if (a.R > 8) {
-      e = allow_lds(&bwd_curves_kernel<16>, lds, s);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(bwd_curves_kernel<16>, dim3(static_cast<unsigned>(ng)), dim3(256), lds, s, a, pitch);
-    } else {
-      e = allow_lds(&bwd_curves_kernel<8>, lds, s);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(bwd_curves_kernel<8>, dim3(static_cast<unsigned>(ng)), dim3(256), lds, s, a, pitch);
-    }
-    e = hipGetLastError();
+  if (MODE == 2) {   // E as bf16 high and low parts (scale 1: the kernels add the bias in its own units)
+    e = launch_e2_convert(a.E, a.e_hs, a.R, a.bias_range, 1.f, a.e_hs ? a.Hq : 1, a.e2, s);
     if (e != hipSuccess) return e;
   }
   // dq (+ bias-parameter gradients)
@@ -906,35 +927,33 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
   const int longest_first = (a.window == 0 || a.window > 32 * DQ_WAVES) ? 1 : 0;
   const long long nq = static_cast<long long>(n_qtiles) * a.Hq * a.B;
   const int dq_lds = DqLayout<D, MODE>::bytes(a.bias_range, a.R);
-  e = allow_lds(&bwd_dq_kernel<D, MODE>, dq_lds, s);
+  e = allow_lds(&bwd_dq_kernel<D, MODE, EW>, dq_lds, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, MODE>), dim3(static_cast<unsigned>(nq)), dim3(64 * DQ_WAVES), dq_lds, s,
-                     a, n_qtiles, longest_first, pitch);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, MODE, EW>), dim3(static_cast<unsigned>(nq)), dim3(64 * DQ_WAVES), dq_lds, s,
+                     a, n_qtiles, longest_first);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dk, dv
   const int kv_lds = DkvLayout<D>::bytes(MODE, a.bias_range);
-  e = allow_lds(&bwd_dkdv_kernel<D, MODE>, kv_lds, s);
+  e = allow_lds(&bwd_dkdv_kernel<D, MODE, EW>, kv_lds, s);
   if (e != hipSuccess) return e;
   const int n_ktiles = (a.S + 32 * DKV_WAVES - 1) / (32 * DKV_WAVES);
   const long long nk = static_cast<long long>(n_ktiles) * a.Hkv * a.B;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, MODE>), dim3(static_cast<unsigned>(nk)), dim3(64 * DKV_WAVES), kv_lds, s,
-                     a, pitch);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, MODE, EW>), dim3(static_cast<unsigned>(nk)), dim3(64 * DKV_WAVES), kv_lds, s,
+                     a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_bwd_mode(const BwdArgs& a, int mode, hipStream_t s) {
   switch (mode) {
-    case 0: return launch_bwd<D, 0>(a, s);
-    case 1: return launch_bwd<D, 1>(a, s);
-    default: return launch_bwd<D, 2>(a, s);
+    case 0: return launch_bwd<D, 0, 16>(a, s);
+    case 1: return launch_bwd<D, 1, 16>(a, s);
+    default: return e2_width(a.R) == 32 ? launch_bwd<D, 2, 32>(a, s) : launch_bwd<D, 2, 16>(a, s);
   }
 }
 
 }  // namespace
-
-int bwd_curve_pitch(int bias_range) { return (CPAD_L + bias_range + CPAD_R + 7) & ~7; }
 
 // LDS the backward kernels need for this shape (the largest of the three), or -1 past 160 KB.
 int bwd_lds_bytes(int D, int mode, int bias_range, int R) {
@@ -948,8 +967,7 @@ int bwd_lds_bytes(int D, int mode, int bias_range, int R) {
                    : (mode == 1 ? DqLayout<64, 1>::bytes(bias_range, R) : DqLayout<64, 2>::bytes(bias_range, R));
     kv = DkvLayout<64>::bytes(mode, bias_range);
   }
-  const int cv = mode == 2 ? (R * bwd_curve_pitch(bias_range) + 64 * R) * 4 : 0;
-  const int m = std::max(std::max(dq, kv), cv);
+  const int m = std::max(dq, kv);
   return m > kMaxLds ? -1 : m;
 }
 

@@ -45,7 +45,7 @@ constexpr int BN = 32;            // keys per tile (= per step)
 constexpr int NC = D / 16;        // K = 16 chunks of the head dim
 constexpr int NDB = D / 32;       // 32-wide head-dim blocks of O^T
 constexpr int NBUF = 3;           // tile ring
-constexpr int PAD = 64;           // zero distances on each side of the bias range (table rows, E rows)
+constexpr int PAD = kE2Pad;       // zero distances on each side of the bias range (table rows, E rows)
 constexpr int ROWS_WG = 32;       // query rows per workgroup
 constexpr int NT = 256;           // threads per workgroup
 constexpr float kRescale = 8.f;   // lazy rescale threshold (log2 units)
@@ -667,11 +667,7 @@ hipError_t launch_split(FwdArgs a, const float* E, void* workspace, hipStream_t 
   if (e != hipSuccess) return e;
   uint16_t* e2 = static_cast<uint16_t*>(workspace);
   if (MODE == 2) {
-    const int heads = a.e_hs ? a.Hq : 1;
-    const int rows = a.bias_range + 2 * PAD + 1;
-    hipLaunchKernelGGL(e2_convert_kernel, dim3((rows + 255) / 256, heads, EW / 16), dim3(256), 0, s, E,
-                       a.e_hs, a.R, a.bias_range, kLog2e / a.c_qk, EW, e2);
-    e = hipGetLastError();
+    e = launch_e2_convert(E, a.e_hs, a.R, a.bias_range, kLog2e / a.c_qk, a.e_hs ? a.Hq : 1, e2, s);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((fwd_split_kernel<MODE, EW, ALLBAND>), dim3(static_cast<unsigned>(nblk)), dim3(NT), lds, s, a, e2);
@@ -679,6 +675,15 @@ hipError_t launch_split(FwdArgs a, const float* E, void* workspace, hipStream_t 
 }
 
 }  // namespace
+
+hipError_t launch_e2_convert(const float* E, long long e_hs, int R, int Rb, float inv_scale, int heads,
+                             uint16_t* e2, hipStream_t s) {
+  const int EW = e2_width(R);
+  const int rows = Rb + 2 * PAD + 1;
+  hipLaunchKernelGGL(e2_convert_kernel, dim3((rows + 255) / 256, heads, EW / 16), dim3(256), 0, s, E, e_hs, R, Rb,
+                     inv_scale, EW, e2);
+  return hipGetLastError();
+}
 
 // Workspace bytes the split prefill needs (the converted E of r.E bias), or -1 when the shape
 // is outside its domain (head_dim 128, GQA groups of 4k heads, positive scale, LDS per
@@ -688,8 +693,7 @@ long long fwd_split_workspace(int D_, int G, int mode, int Rb, int R, int e_shar
   if (mode != 0 && Rb % 4 != 0) return -1;
   if (split_lds(mode, Rb) > kMaxLdsPerWg) return -1;
   if (mode != 2) return 0;
-  const int EW = R > 8 ? 32 : 16;
-  return static_cast<long long>(e_shared ? 1 : Hq) * (Rb + 2 * PAD + 1) * EW * 2;
+  return e2_bytes(e_shared ? 1 : Hq, Rb, e2_width(R));
 }
 
 hipError_t launch_fwd_bf16_split(const FwdArgs& a, int mode, void* workspace, hipStream_t s) {

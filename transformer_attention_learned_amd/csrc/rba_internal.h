@@ -12,6 +12,15 @@ namespace rba {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// E converted for the MFMA curve blocks (split prefill and backward): distance-major rows of a
+// bf16 high and low part of E * inv_scale, [heads][bias_range + 2 kE2Pad + 1][e2_width(R)],
+// zero at the kE2Pad padding distances on each side (and one more row), zero past feature R.
+constexpr int kE2Pad = 64;
+inline int e2_width(int R) { return R > 8 ? 32 : 16; }
+inline long long e2_bytes(int heads, int bias_range, int width) {
+  return static_cast<long long>(heads) * (bias_range + 2 * kE2Pad + 1) * width * 2;
+}
+
 // Context-length temperature of a query that sees n keys: 1 while n <= temp_len, then
 // log(n) / log(temp_len), a factor on both the q.k term and the bias ("Thinking Machines
 // dropped RoPE", section "The temperature scale is dependent on context length": flat up to
@@ -128,7 +137,7 @@ struct BwdArgs {
   const float* E;
   long long e_hs;       // head stride of E and dE in floats (0: one shared bank)
   float* dsum;          // workspace [B, Hq, S]: rowsum(dout * o)
-  uint16_t* ctab;       // workspace (r.E): curve table [B, Hq, S, bwd_curve_pitch(bias_range)]
+  uint16_t* e2;         // workspace (r.E): E in the curve-block format (kE2Pad, e2_width(R)), scale 1
   int B, S, Hq, Hkv, G;
   int window, bias_range, R;
   float c_qk;           // scale * log2(e)
@@ -149,11 +158,12 @@ long long fwd_bf16_workspace(const FwdArgs& a, int D, int mode);
 // or -1 outside its domain; and its launcher.
 long long fwd_split_workspace(int D, int G, int mode, int bias_range, int R, int e_shared, int Hq, float scale);
 hipError_t launch_fwd_bf16_split(const FwdArgs& a, int mode, void* workspace, hipStream_t s);
+// The conversion of E into that format (heads rows of E at head stride e_hs).
+hipError_t launch_e2_convert(const float* E, long long e_hs, int R, int bias_range, float inv_scale, int heads,
+                             uint16_t* e2, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int D, int mode, hipStream_t s);
-// LDS bytes of the largest backward kernel for this shape, or -1 when it does not fit; the
-// row pitch (bf16) of the backward's curve table.
+// LDS bytes of the largest backward kernel for this shape, or -1 when it does not fit.
 int bwd_lds_bytes(int D, int mode, int bias_range, int R);
-int bwd_curve_pitch(int bias_range);
 hipError_t launch_attn_f32(const F32Args& a, hipStream_t s);
 hipError_t launch_decode_bf16(DecodeArgs a, int D, int mode, hipStream_t s);
 // Decode over MXFP4 caches (D = 128, G <= 16) and the MXFP4 quantiser of bf16 rows
