@@ -23,7 +23,8 @@ Inputs are resident in HBM before the timed region; a step is one library call
 
 --workload NAME times one workload alone (the profiling runs use this), also
 the paged and MXFP4 decode variants (decode_global_paged, decode_local_paged,
-decode_global_fp4, decode_local_fp4; GB/s then counts the MXFP4 bytes) and the
+decode_global_fp4, decode_local_fp4, decode_global_paged_fp4, decode_local_paged_fp4;
+GB/s then counts the MXFP4 bytes) and the
 backward passes (local_prefill_bwd, global_prefill_bwd,
 long_global_prefill_bwd; 10*D algorithmic flops per visible pair).
 """
@@ -186,7 +187,25 @@ def setup(w, dev):
         # lengths makes consecutive steps read 4 disjoint windows, so the bytes come from HBM.
         kv_lens = [w.S - j * w.window for j in range(4)] if (w.window and 4 * w.window <= w.S) else [w.S]
         it = [0]
-        if w.extra.get("kv") == "fp4":
+        if w.extra.get("kv") == "fp4" and w.extra.get("page_size"):
+            # MXFP4 page pools: the quantised caches viewed as pages, scattered by the table
+            from transformer_attention_learned_amd.workloads import paged_view
+            kc, ks = rba.kv_quantize_fp4(inp["k"])
+            vc, vs = rba.kv_quantize_fp4(inp["v"])
+            kcp, vcp, bt = paged_view(w, kc, vc)
+            ksp, vsp, bt2 = paged_view(w, ks, vs)
+            torch.cuda.synchronize()
+            assert torch.equal(bt, bt2)
+            lens_t = [torch.full((w.B,), L, dtype=torch.int32, device=dev) for L in kv_lens]
+
+            def step():
+                j = it[0] % len(kv_lens)
+                it[0] += 1
+                rba.decode_fp4_paged(inp["q"], kcp, ksp, vcp, vsp, bt, lens_t[j], kv_lens[j],
+                                     window=w.window, bias_range=w.bias_range, mode=w.mode,
+                                     table=inp["table"], r=inp["r"], E=inp["E"], scale=w.scale,
+                                     temp_len=w.temp_len, out=out, workspace=ws)
+        elif w.extra.get("kv") == "fp4":
             # MXFP4 caches: 64 code bytes + 4 scale bytes per row and kv head, quantised once
             kc, ks = rba.kv_quantize_fp4(inp["k"])
             vc, vs = rba.kv_quantize_fp4(inp["v"])

@@ -256,9 +256,36 @@ int relbias_attn_decode_fp4(const void* q, const void* k_codes, const void* k_sc
                             size_t workspace_bytes, void* stream);
 
 /*
+ * relbias_attn_decode_paged over MXFP4 page pools: the paged cache shapes the pages list for a
+ * fused-bias kernel ("Thinking Machines dropped RoPE", the paragraphs on the kernel cost of the
+ * bias: paged KV, variable sequence lengths) with the FP4 KV-cache compression of
+ * relbias_attn_decode_fp4 ("models/inkling" (archdiff), the component diagram).  Per sequence b
+ * it computes exactly what relbias_attn_decode_fp4 computes with kv_len = kv_lens[b] over the
+ * logical cache whose row j is row (j % page_size) of page block_table[b][j / page_size].
+ *
+ *   k_codes     [num_pages, page_size, Hkv, D / 2] MXFP4 codes, k_scales [num_pages,
+ *               page_size, Hkv, D / 32] E8M0 scale bytes, in the layout
+ *               relbias_attn_kv_quantize_fp4 writes (and the same for V); codes 16-byte aligned.
+ *   q, o, lse, block_table, kv_lens, num_pages, page_size, max_pages, max_kv_len, window,
+ *               bias_range, mode, table, r, E, R, scale, temp_len, workspace: as in
+ *               relbias_attn_decode_paged (dtype RBA_BF16), with the same clamping of the
+ *               device values and the same workspace size.
+ * Supported: D = 128 and Hq / Hkv <= 16 (RBA_ENOTSUP otherwise).
+ */
+int relbias_attn_decode_fp4_paged(const void* q, const void* k_codes, const void* k_scales,
+                                  const void* v_codes, const void* v_scales,
+                                  const int* block_table, const int* kv_lens, void* o, float* lse,
+                                  int B, int num_pages, int page_size, int max_pages,
+                                  int max_kv_len, int Hq, int Hkv, int D, int window,
+                                  int bias_range, int mode, const float* table, const void* r,
+                                  const float* E, int R, float scale, int temp_len,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace relbias_attn_bwd needs: one fp32 per (batch, row, query head),
- * and for the input-dependent modes the curve table r_i . E[h, :, d] of every row (bf16,
- * bias_range + 96 distances per row, rounded up to 8).  Pure host function.
+ * rounded up to 256 bytes, and for the input-dependent modes the bank E converted to bf16 high
+ * and low parts (per bank head (Hq, or 1 when shared): bias_range + 129 distances of 32 bf16
+ * values each); independent of S beyond the first term.  Pure host function.
  */
 size_t relbias_attn_bwd_workspace_size(int B, int S, int Hq, int mode, int bias_range);
 

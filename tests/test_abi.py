@@ -38,7 +38,8 @@ def test_exports_every_declared_symbol(lib):
                           "relbias_attn_decode_paged_workspace_size", "relbias_attn_last_error",
                           "relbias_attn_version", "relbias_attn_bwd",
                           "relbias_attn_bwd_workspace_size", "relbias_attn_kv_quantize_fp4",
-                          "relbias_attn_decode_fp4", "relbias_attn_decode_noalloc"}
+                          "relbias_attn_decode_fp4", "relbias_attn_decode_noalloc",
+                          "relbias_attn_decode_fp4_paged"}
     for n in names:
         assert hasattr(lib, n), n
     assert "gfx950" in rba.version()
@@ -293,6 +294,46 @@ def test_fp4_rejects(lib):
     assert dec(vc=P + 4) == EINVAL and "aligned" in rba.last_error()
     assert dec(temp_len=1) == EINVAL and "temp_len" in rba.last_error()
     assert dec(B=0) == 0
+
+
+def _fp4_paged(lib, **kw):
+    a = dict(q=P, kc=P, ks=P, vc=P, vs=P, bt=P, lens=P, o=P, lse=None, B=2, num_pages=8,
+             page_size=32, max_pages=4, max_kv_len=100, Hq=8, Hkv=2, D=128, window=0,
+             bias_range=8, mode=0, table=None, r=None, E=None, R=0, scale=0.1, temp_len=0, ws=None,
+             wsb=0)
+    a.update(kw)
+    return lib.relbias_attn_decode_fp4_paged(
+        a["q"], a["kc"], a["ks"], a["vc"], a["vs"], a["bt"], a["lens"], a["o"], a["lse"], a["B"],
+        a["num_pages"], a["page_size"], a["max_pages"], a["max_kv_len"], a["Hq"], a["Hkv"], a["D"],
+        a["window"], a["bias_range"], a["mode"], a["table"], a["r"], a["E"], a["R"], a["scale"],
+        a["temp_len"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(D=64), ENOTSUP, "head_dim 128"),
+    (dict(Hq=32, Hkv=1), ENOTSUP, "<= 16"),
+    (dict(page_size=24), ENOTSUP, "page_size"),
+    (dict(max_kv_len=129), EINVAL, "max_kv_len"),
+    (dict(max_kv_len=0), EINVAL, "max_kv_len"),
+    (dict(num_pages=0), EINVAL, "num_pages"),
+    (dict(bt=None), EINVAL, "non-NULL"),
+    (dict(lens=P + 2), EINVAL, "4-byte"),
+    (dict(ks=None), EINVAL, "non-NULL"),
+    (dict(vc=P + 4), EINVAL, "aligned"),
+    (dict(mode=1, table=None), EINVAL, "table"),
+    (dict(temp_len=1), EINVAL, "temp_len"),
+    (dict(B=-1), EINVAL, "B="),
+    (dict(max_kv_len=5000, num_pages=200, max_pages=200, ws=None), EINVAL, "workspace"),
+    (dict(max_kv_len=5000, num_pages=200, max_pages=200, ws=P, wsb=4), EINVAL, "too small"),
+])
+def test_decode_fp4_paged_rejects(lib, kw, code, needle):
+    assert _fp4_paged(lib, **kw) == code
+    assert needle in rba.last_error()
+
+
+def test_decode_fp4_paged_empty(lib):
+    assert _fp4_paged(lib, B=0) == 0
+    assert _fp4_paged(lib, B=0, q=None, bt=None) == 0
 
 
 # --- the binding checks the exact shapes of the bias parameters before any library call -----

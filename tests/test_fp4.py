@@ -1,5 +1,6 @@
 """GPU checks of the MXFP4 KV cache: the quantiser against the oracle's encoding bit for bit,
-and decode over MXFP4 caches against the float64 oracle on the dequantised caches.
+and decode over MXFP4 caches (contiguous, and paged with a length per sequence) against the
+float64 oracle on the dequantised caches.
 
 In the decode cases the oracle encodes the evaluated sequences itself (oracle/mxfp4.py), the
 GPU's bytes must equal its bytes, and the expected outputs come from the oracle's own
@@ -18,6 +19,7 @@ import oracle
 from oracle import mxfp4
 import transformer_attention_learned_amd as rba
 from transformer_attention_learned_amd.workloads import WORKLOADS, Workload, make_inputs
+from paged_pool import logical_rows, paginate
 
 pytestmark = pytest.mark.gpu
 
@@ -144,3 +146,94 @@ def test_quantize_then_decode_equals_host_quantised_decode():
                         bias_range=256, mode="rproj", r=inp["r"], E=inp["E"])
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+# ---- paged MXFP4 pools ---------------------------------------------------------------------------
+
+def _check_paged(w: Workload, lens, page_size):
+    """Scatter the seeded caches into shuffled pools, quantise the pools on the GPU (their bytes
+    must equal the oracle's encoding), decode through the block table with a length per
+    sequence, and compare each sequence with the oracle on its own dequantised logical rows."""
+    _say(f"  fp4 paged case {w.name}: B={w.B} L={w.S} Hq={w.Hq} Hkv={w.Hkv} W={w.window} "
+         f"Rb={w.bias_range} mode={w.mode} R={w.R} page={page_size} lens={lens} seed={w.seed}")
+    inp = make_inputs(w, device="cuda")
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed + 29)
+    kp, bt = paginate(inp["k"], page_size, 3, gen)
+    gen.manual_seed(w.seed + 29)
+    vp, bt2 = paginate(inp["v"], page_size, 3, gen)
+    assert torch.equal(bt, bt2)
+    kc, ks = rba.kv_quantize_fp4(kp)
+    vc, vs = rba.kv_quantize_fp4(vp)
+    kv_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o, lse = rba.decode_fp4_paged(inp["q"], kc, ks, vc, vs, bt, kv_lens, max(lens),
+                                  window=w.window, bias_range=w.bias_range, mode=w.mode,
+                                  table=inp["table"], r=inp["r"], E=inp["E"], scale=w.scale,
+                                  temp_len=w.temp_len, return_lse=True)
+    torch.cuda.synchronize()
+    hk, hks = _host_quant(kp.cpu())
+    hv, hvs = _host_quant(vp.cpu())
+    assert torch.equal(kc.cpu(), hk) and torch.equal(ks.cpu(), hks)
+    assert torch.equal(vc.cpu(), hv) and torch.equal(vs.cpu(), hvs)
+    got_o = o.to("cpu", torch.float64).numpy()
+    got_l = lse.to("cpu", torch.float64).numpy()
+    assert np.all(np.isfinite(got_o)) and np.all(np.isfinite(got_l))
+    ref_o, ref_l = np.zeros_like(got_o), np.zeros_like(got_l)
+    btc = bt.cpu()
+    for b, L in enumerate(lens):
+        deq = lambda c, sc: mxfp4.dequantize(mxfp4.unpack(logical_rows(c, btc[b], L).numpy()),
+                                             logical_rows(sc, btc[b], L).numpy())[None]
+        ro, rl = oracle.decode(inp["q"][b:b + 1], deq(hk, hks), deq(hv, hvs), L, scale=w.scale,
+                               window=w.window, bias_range=w.bias_range, mode=w.mode,
+                               table=inp["table"], r=None if inp["r"] is None else inp["r"][b:b + 1],
+                               E=inp["E"], temp_len=w.temp_len)
+        ref_o[b], ref_l[b] = ro[0], rl[0]
+    for name, g, r in (("o", got_o, ref_o), ("lse", got_l, ref_l)):
+        max_abs = float(np.abs(g - r).max())
+        rel = float(np.linalg.norm(g - r) / np.linalg.norm(r))
+        _say(f"    parity fp4 paged {name}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+        assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, (name, max_abs, rel)
+
+
+PAGED_CASES = [
+    (dict(), [700, 1, 33, 640], 16),
+    (dict(window=96), [700, 97, 96, 95], 64),
+    (dict(mode="table", bias_range=100, window=300), [699, 250, 301, 1], 256),
+    (dict(mode="none", Hq=4, Hkv=4), [512, 511, 513, 2], 32),
+    (dict(mode="rproj_shared", R=16, window=512, bias_range=512, logit_scale="inv_d", S=1300),
+     [1300, 1000, 513, 17], 64),
+    (dict(B=3, S=5000, bias_range=1024, Hq=32, Hkv=2), [5000, 4097, 1025], 128),
+    (dict(S=3000, temp_len=256), [3000, 2000, 257, 100], 64),
+]
+
+
+@pytest.mark.parametrize("kw,lens,page", PAGED_CASES,
+                         ids=lambda x: "-".join(f"{k}{v}" for k, v in x.items()) if isinstance(x, dict) else str(x))
+def test_decode_fp4_paged_matches_oracle(kw, lens, page):
+    base = dict(kind="decode", dtype="bf16", B=4, Hq=8, Hkv=2, D=128, S=700, window=0,
+                bias_range=64, mode="rproj", R=8,
+                seed=zlib.crc32(repr((sorted(kw.items()), lens, page)).encode()) % 10007)
+    base.update(kw)
+    _check_paged(Workload(name="fp4_paged", **base), lens, page)
+
+
+@pytest.mark.parametrize("window,page", [(0, 32), (512, 16)])
+def test_fp4_paged_identity_equals_contiguous(window, page):
+    """Identity block table, equal lengths: bitwise the contiguous MXFP4 decode."""
+    w = Workload(name="fp4_ident_paged", kind="decode", dtype="bf16", B=3, Hq=8, Hkv=2, D=128,
+                 S=4096, window=window, bias_range=512, mode="rproj", R=8, seed=41)
+    inp = make_inputs(w, device="cuda")
+    kc, ks = rba.kv_quantize_fp4(inp["k"])
+    vc, vs = rba.kv_quantize_fp4(inp["v"])
+    kv_len = 4000
+    o1, l1 = rba.decode_fp4(inp["q"], kc, ks, vc, vs, kv_len, window=window, bias_range=512,
+                            mode="rproj", r=inp["r"], E=inp["E"], return_lse=True)
+    B, mp = w.B, w.S // page
+    pages = lambda t: t.reshape((B * mp, page) + tuple(t.shape[2:]))
+    bt = torch.arange(B * mp, dtype=torch.int32, device="cuda").view(B, mp)
+    lens = torch.full((B,), kv_len, dtype=torch.int32, device="cuda")
+    o2, l2 = rba.decode_fp4_paged(inp["q"], pages(kc), pages(ks), pages(vc), pages(vs), bt, lens,
+                                  kv_len, window=window, bias_range=512, mode="rproj", r=inp["r"],
+                                  E=inp["E"], return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

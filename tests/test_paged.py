@@ -16,6 +16,7 @@ import torch
 import oracle
 import transformer_attention_learned_amd as rba
 from transformer_attention_learned_amd.workloads import Workload, make_inputs
+from paged_pool import paginate
 
 pytestmark = pytest.mark.gpu
 
@@ -38,31 +39,15 @@ def _t2np(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def _paginate(cache, page_size, n_extra, gen):
-    """Scatter [B, L, Hkv, D] into a shuffled pool; returns (pool, block_table)."""
-    B, L, Hkv, D = cache.shape
-    max_pages = (L + page_size - 1) // page_size
-    n_pages = B * max_pages + n_extra
-    perm = torch.randperm(n_pages, generator=gen, device="cpu")[:B * max_pages].to(cache.device)
-    fill = torch.Generator(device=cache.device)
-    fill.manual_seed(int(torch.randint(0, 1 << 30, (1,), generator=gen)))
-    # pages no sequence references hold noise: reading one would show in the parity check
-    pool = torch.randn((n_pages, page_size, Hkv, D), generator=fill, device=cache.device).to(cache.dtype)
-    padded = torch.zeros((B, max_pages * page_size, Hkv, D), dtype=cache.dtype, device=cache.device)
-    padded[:, :L] = cache
-    pool[perm] = padded.view(B * max_pages, page_size, Hkv, D)
-    return pool, perm.view(B, max_pages).to(torch.int32)
-
-
 def _check(w, lens, page_size, n_extra=3):
     _say(f"  paged case: B={w.B} L={w.S} Hq={w.Hq} Hkv={w.Hkv} D={w.D} W={w.window} "
          f"Rb={w.bias_range} mode={w.mode} R={w.R} page={page_size} lens={lens}")
     inp = make_inputs(w, device="cuda")
     gen = torch.Generator(device="cpu")
     gen.manual_seed(w.seed + 17)
-    kp, bt = _paginate(inp["k"], page_size, n_extra, gen)
+    kp, bt = paginate(inp["k"], page_size, n_extra, gen)
     gen.manual_seed(w.seed + 17)
-    vp, bt2 = _paginate(inp["v"], page_size, n_extra, gen)
+    vp, bt2 = paginate(inp["v"], page_size, n_extra, gen)
     assert torch.equal(bt, bt2)
     kv_lens = torch.tensor(lens, dtype=torch.int32, device="cuda")
     o, lse = rba.decode_paged(inp["q"], kp, vp, bt, kv_lens, max(lens), window=w.window,

@@ -93,6 +93,9 @@ def load_library():
     lib.relbias_attn_decode_fp4.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i,
                                             vp, vp, vp, i, f, i, vp, sz, vp]
     lib.relbias_attn_decode_fp4.restype = i
+    lib.relbias_attn_decode_fp4_paged.argtypes = [vp] * 9 + [i] * 11 + [vp, vp, vp, i, f, i, vp,
+                                                                          sz, vp]
+    lib.relbias_attn_decode_fp4_paged.restype = i
     lib.relbias_attn_last_error.argtypes = []
     lib.relbias_attn_last_error.restype = ctypes.c_char_p
     lib.relbias_attn_version.argtypes = []
@@ -341,6 +344,58 @@ def decode_fp4(q, k_codes, k_scales, v_codes, v_scales, kv_len, *, window=0, bia
     st = lib.relbias_attn_decode_fp4(
         _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales), _ptr(out),
         _ptr(lse), B, L_max, int(kv_len), Hq, Hkv, D, int(window), int(bias_range), m,
+        _ptr(table if m == 1 else None), _ptr(r if m in (2, 3) else None),
+        _ptr(E if m in (2, 3) else None), R, float(scale), int(temp_len), _ptr(workspace), wbytes,
+        _stream_handle(dev, stream))
+    if st != RBA_OK:
+        raise LibraryError(st, last_error())
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_fp4_paged(q, k_codes, k_scales, v_codes, v_scales, block_table, kv_lens, max_kv_len,
+                     *, window=0, bias_range=0, mode="none", table=None, r=None, E=None,
+                     scale=None, temp_len=0, out=None, lse=None, workspace=None,
+                     return_lse=False, stream=None):
+    """One decode step over MXFP4 page pools (relbias_attn_decode_fp4_paged).
+
+    k_codes / v_codes uint8 [num_pages, page_size, Hkv, D/2]; k_scales / v_scales uint8
+    [num_pages, page_size, Hkv, D/32]; block_table, kv_lens and max_kv_len as in decode_paged.
+    """
+    import torch
+    lib = load_library()
+    dev = q.device
+    _check(q, "q", dtype=torch.bfloat16, ndim=3)
+    for t, n in ((k_codes, "k_codes"), (k_scales, "k_scales"), (v_codes, "v_codes"),
+                 (v_scales, "v_scales")):
+        _check(t, n, dtype=torch.uint8, ndim=4, device=dev)
+    _check(block_table, "block_table", dtype=torch.int32, ndim=2, device=dev)
+    _check(kv_lens, "kv_lens", dtype=torch.int32, ndim=1, device=dev)
+    B, Hq, D = q.shape
+    num_pages, page_size, Hkv = k_codes.shape[0], k_codes.shape[1], k_codes.shape[2]
+    if (tuple(k_codes.shape) != (num_pages, page_size, Hkv, D // 2) or v_codes.shape != k_codes.shape
+            or tuple(k_scales.shape) != (num_pages, page_size, Hkv, D // 32)
+            or v_scales.shape != k_scales.shape):
+        raise ValueError("codes must be [num_pages,page_size,Hkv,D/2] and scales "
+                         "[num_pages,page_size,Hkv,D/32]")
+    if block_table.shape[0] != B or kv_lens.shape[0] != B:
+        raise ValueError("block_table [B, max_pages] and kv_lens [B] must match q's batch")
+    m, R = _bias_args(mode, table, r, E, Hq, q.dtype, dev, bias_range)
+    if m in (2, 3) and tuple(r.shape) != (B, Hq, R):
+        raise ValueError(f"r must be [B,Hq,R] = {(B, Hq, R)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = lib.relbias_attn_decode_paged_workspace_size(B, Hq, Hkv, D, int(max_kv_len), int(window))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.relbias_attn_decode_fp4_paged(
+        _ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales), _ptr(block_table),
+        _ptr(kv_lens), _ptr(out), _ptr(lse), B, num_pages, page_size, int(block_table.shape[1]),
+        int(max_kv_len), Hq, Hkv, D, int(window), int(bias_range), m,
         _ptr(table if m == 1 else None), _ptr(r if m in (2, 3) else None),
         _ptr(E if m in (2, 3) else None), R, float(scale), int(temp_len), _ptr(workspace), wbytes,
         _stream_handle(dev, stream))

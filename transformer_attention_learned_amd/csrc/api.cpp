@@ -76,6 +76,35 @@ int check_temp(const char* fn, int temp_len) {
     return fail(RBA_EINVAL, "%s: temp_len=%d must be 0 (no temperature) or >= 2", fn, temp_len);
   return RBA_OK;
 }
+// Host-side geometry of a paged cache: pool and table sizes, the launch bound max_kv_len, and
+// the block table and length pointers (their device values are clamped by the kernel).
+int check_paged(const char* fn, int num_pages, int page_size, int max_pages, int max_kv_len,
+                const int* block_table, const int* kv_lens) {
+  if (page_size < 16 || page_size % 16)
+    return fail(RBA_ENOTSUP, "%s: page_size=%d must be a positive multiple of 16", fn, page_size);
+  if (num_pages < 1 || max_pages < 1)
+    return fail(RBA_EINVAL, "%s: num_pages=%d and max_pages=%d must be >= 1", fn, num_pages, max_pages);
+  if (max_kv_len < 1 || static_cast<long long>(max_kv_len) > static_cast<long long>(max_pages) * page_size)
+    return fail(RBA_EINVAL, "%s: need 1 <= max_kv_len (%d) <= max_pages * page_size (%lld)", fn,
+                max_kv_len, static_cast<long long>(max_pages) * page_size);
+  if (static_cast<long long>(num_pages) * page_size >= (1LL << 31))
+    return fail(RBA_ENOTSUP, "%s: page pool too large (rows must fit in int32)", fn);
+  if (!block_table || !kv_lens) return fail(RBA_EINVAL, "%s: block_table and kv_lens must be non-NULL", fn);
+  if (!aligned_to(block_table, 4) || !aligned_to(kv_lens, 4))
+    return fail(RBA_EINVAL, "%s: block_table and kv_lens must be 4-byte aligned", fn);
+  return RBA_OK;
+}
+
+// A caller workspace of `need` bytes (none needed when need is 0).
+int check_workspace(const char* fn, size_t need, const void* workspace, size_t workspace_bytes) {
+  if (need == 0) return RBA_OK;
+  if (!workspace) return fail(RBA_EINVAL, "%s: workspace of %zu bytes required, got NULL", fn, need);
+  if (workspace_bytes < need)
+    return fail(RBA_EINVAL, "%s: workspace too small (%zu < %zu bytes)", fn, workspace_bytes, need);
+  if (!aligned_to(workspace, 4)) return fail(RBA_EINVAL, "%s: workspace is not 4-byte aligned", fn);
+  return RBA_OK;
+}
+
 float temp_inv_log2(int temp_len) {
   return temp_len > 0 ? static_cast<float>(1.0 / std::log2(static_cast<double>(temp_len))) : 0.f;
 }
@@ -116,6 +145,74 @@ rba::FwdArgs bf16_fwd_args(const void* q, const void* k, const void* v, void* o,
   return a;
 }
 
+// Kernel arguments of a bf16 decode over a contiguous cache (L_max > 0) or a paged pool
+// (L_max = 0; the caller adds the page table); kv_len is the cache length or the launch bound.
+rba::DecodeArgs bf16_decode_args(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const float* table, const void* r, const float* E,
+                                 void* workspace, int B, int L_max, int kv_len, int Hq, int Hkv,
+                                 int window, int bias_range, int mode, int R, float scale,
+                                 int temp_len) {
+  rba::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.table = table;
+  a.r = static_cast<const uint16_t*>(r);
+  a.E = E;
+  a.ws = static_cast<float*>(workspace);
+  a.B = B;
+  a.L_max = L_max;
+  a.kv_len = kv_len;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.window = window;
+  a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
+  a.R = is_rproj(mode) ? R : 0;
+  a.e_hs = e_head_stride(mode, R, bias_range);
+  a.key_begin = window ? (kv_len > window ? kv_len - window : 0) : 0;
+  rba::decode_split(B, Hkv, kv_len, window, &a.n_split, &a.keys_per_wave);
+  a.c_qk = scale * rba::kLog2e;
+  a.temp_len = temp_len;
+  a.temp_inv_log2 = temp_inv_log2(temp_len);
+  return a;
+}
+
+// Reads of a paged pool: sequence b's row j is row j % page_size of page block_table[b][j /
+// page_size]; lengths and the first visible key come from kv_lens per sequence.
+void set_pages(rba::DecodeArgs& a, const int* block_table, const int* kv_lens, int num_pages,
+               int page_size, int max_pages) {
+  a.key_begin = 0;
+  a.block_table = block_table;
+  a.kv_lens = kv_lens;
+  a.page_size = page_size;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+}
+
+// Checks of a decode over MXFP4 caches (contiguous or paged) that do not depend on the layout.
+int check_fp4(const char* fn, const void* q, const void* k_codes, const void* k_scales,
+              const void* v_codes, const void* v_scales, const void* o, const float* lse, int B,
+              int Hq, int Hkv, int D, int window, int bias_range, int mode, const float* table,
+              const void* r, const float* E, int R, float scale, int temp_len) {
+  if (B < 0) return fail(RBA_EINVAL, "%s: B=%d must be >= 0", fn, B);
+  int st = check_common(fn, RBA_BF16, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale);
+  if (st == RBA_OK) st = check_temp(fn, temp_len);
+  if (st != RBA_OK) return st;
+  if (D != 128) return fail(RBA_ENOTSUP, "%s: MXFP4 caches are supported for head_dim 128, got %d", fn, D);
+  const int G = Hq / Hkv;
+  if (G > 16) return fail(RBA_ENOTSUP, "%s: MXFP4 caches support Hq/Hkv <= 16, got %d", fn, G);
+  if (B == 0) return RBA_OK;
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !o)
+    return fail(RBA_EINVAL, "%s: q, codes, scales and o must be non-NULL", fn);
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(o))
+    return fail(RBA_EINVAL, "%s: q, codes and o must be 16-byte aligned", fn);
+  if (lse && !aligned_to(lse, 4)) return fail(RBA_EINVAL, "%s: lse is not 4-byte aligned", fn);
+  return RBA_OK;
+}
+
 // Decode against a contiguous cache.  noalloc: the split partials go to the library's fixed
 // per-GPU scratch (relbias_attn_decode_noalloc) instead of the caller's workspace.
 int decode_impl(const char* fn, int dtype, const void* q, const void* k_cache, const void* v_cache,
@@ -142,8 +239,6 @@ int decode_impl(const char* fn, int dtype, const void* q, const void* k_cache, c
   if (dtype == RBA_BF16) {
     if (G > 32) return fail(RBA_ENOTSUP, "%s: bf16 decode supports Hq/Hkv <= 32, got %d", fn, G);
     if (Hkv > 65535 || B > 65535) return fail(RBA_ENOTSUP, "%s: grid too large", fn);
-    int ns = 1, kpw = 64;
-    rba::decode_split(B, Hkv, kv_len, window, &ns, &kpw);
     const size_t need = relbias_attn_decode_workspace_size(B, Hq, Hkv, D, kv_len, window);
     if (noalloc) {
       if (need > static_cast<size_t>(RBA_DECODE_NOALLOC_SCRATCH_BYTES))
@@ -165,38 +260,13 @@ int decode_impl(const char* fn, int dtype, const void* q, const void* k_cache, c
         e = rba::decode_noalloc_scratch(&workspace);
         if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
       }
-    } else if (need > 0) {
-      if (!workspace) return fail(RBA_EINVAL, "%s: workspace of %zu bytes required, got NULL", fn, need);
-      if (workspace_bytes < need)
-        return fail(RBA_EINVAL, "%s: workspace too small (%zu < %zu bytes)", fn, workspace_bytes, need);
-      if (!aligned_to(workspace, 4)) return fail(RBA_EINVAL, "%s: workspace is not 4-byte aligned", fn);
+    } else {
+      st = check_workspace(fn, need, workspace, workspace_bytes);
+      if (st != RBA_OK) return st;
     }
-    rba::DecodeArgs a{};
-    a.q = static_cast<const uint16_t*>(q);
-    a.k = static_cast<const uint16_t*>(k_cache);
-    a.v = static_cast<const uint16_t*>(v_cache);
-    a.o = static_cast<uint16_t*>(o);
-    a.lse = lse;
-    a.table = table;
-    a.r = static_cast<const uint16_t*>(r);
-    a.E = E;
-    a.ws = static_cast<float*>(workspace);
-    a.B = B;
-    a.L_max = L_max;
-    a.kv_len = kv_len;
-    a.Hq = Hq;
-    a.Hkv = Hkv;
-    a.G = G;
-    a.window = window;
-    a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
-    a.R = is_rproj(mode) ? R : 0;
-    a.e_hs = e_head_stride(mode, R, bias_range);
-    a.key_begin = window ? (kv_len > window ? kv_len - window : 0) : 0;
-    a.n_split = ns;
-    a.keys_per_wave = kpw;
-    a.c_qk = scale * rba::kLog2e;
-    a.temp_len = temp_len;
-    a.temp_inv_log2 = temp_inv_log2(temp_len);
+    const rba::DecodeArgs a = bf16_decode_args(q, k_cache, v_cache, o, lse, table, r, E, workspace,
+                                               B, L_max, kv_len, Hq, Hkv, window, bias_range, mode,
+                                               R, scale, temp_len);
     e = rba::launch_decode_bf16(a, D, kernel_mode(mode), hs);
   } else {
     rba::F32Args a{};
@@ -368,65 +438,23 @@ int relbias_attn_decode_paged(int dtype, const void* q, const void* k_pages, con
   if (st != RBA_OK) return st;
   if (B == 0) return ok();
   if (dtype != RBA_BF16) return fail(RBA_ENOTSUP, "%s: paged caches are supported for bf16 only", fn);
-  if (page_size < 16 || page_size % 16)
-    return fail(RBA_ENOTSUP, "%s: page_size=%d must be a positive multiple of 16", fn, page_size);
-  if (num_pages < 1 || max_pages < 1)
-    return fail(RBA_EINVAL, "%s: num_pages=%d and max_pages=%d must be >= 1", fn, num_pages, max_pages);
-  if (max_kv_len < 1 || static_cast<long long>(max_kv_len) > static_cast<long long>(max_pages) * page_size)
-    return fail(RBA_EINVAL, "%s: need 1 <= max_kv_len (%d) <= max_pages * page_size (%lld)", fn,
-                max_kv_len, static_cast<long long>(max_pages) * page_size);
-  if (static_cast<long long>(num_pages) * page_size >= (1LL << 31))
-    return fail(RBA_ENOTSUP, "%s: page pool too large (rows must fit in int32)", fn);
-  if (!q || !k_pages || !v_pages || !o || !block_table || !kv_lens)
-    return fail(RBA_EINVAL, "%s: q, k_pages, v_pages, block_table, kv_lens and o must be non-NULL", fn);
+  st = check_paged(fn, num_pages, page_size, max_pages, max_kv_len, block_table, kv_lens);
+  if (st != RBA_OK) return st;
+  if (!q || !k_pages || !v_pages || !o)
+    return fail(RBA_EINVAL, "%s: q, k_pages, v_pages and o must be non-NULL", fn);
   if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o))
     return fail(RBA_EINVAL, "%s: q, page pools and o must be 16-byte aligned", fn);
-  if (!aligned_to(block_table, 4) || !aligned_to(kv_lens, 4))
-    return fail(RBA_EINVAL, "%s: block_table and kv_lens must be 4-byte aligned", fn);
   if (lse && !aligned_to(lse, 4)) return fail(RBA_EINVAL, "%s: lse is not 4-byte aligned", fn);
   const int G = Hq / Hkv;
   if (G > 32) return fail(RBA_ENOTSUP, "%s: bf16 decode supports Hq/Hkv <= 32, got %d", fn, G);
-  int ns = 1, kpw = 64;
-  rba::decode_split(B, Hkv, max_kv_len, window, &ns, &kpw);
-  const size_t need = relbias_attn_decode_paged_workspace_size(B, Hq, Hkv, D, max_kv_len, window);
-  if (need > 0) {
-    if (!workspace) return fail(RBA_EINVAL, "%s: workspace of %zu bytes required, got NULL", fn, need);
-    if (workspace_bytes < need)
-      return fail(RBA_EINVAL, "%s: workspace too small (%zu < %zu bytes)", fn, workspace_bytes, need);
-    if (!aligned_to(workspace, 4)) return fail(RBA_EINVAL, "%s: workspace is not 4-byte aligned", fn);
-  }
+  st = check_workspace(fn, relbias_attn_decode_paged_workspace_size(B, Hq, Hkv, D, max_kv_len, window),
+                       workspace, workspace_bytes);
+  if (st != RBA_OK) return st;
   if (Hkv > 65535 || B > 65535) return fail(RBA_ENOTSUP, "%s: grid too large", fn);
-  rba::DecodeArgs a{};
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k_pages);
-  a.v = static_cast<const uint16_t*>(v_pages);
-  a.o = static_cast<uint16_t*>(o);
-  a.lse = lse;
-  a.table = table;
-  a.r = static_cast<const uint16_t*>(r);
-  a.E = E;
-  a.ws = static_cast<float*>(workspace);
-  a.B = B;
-  a.L_max = 0;
-  a.kv_len = max_kv_len;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.G = G;
-  a.window = window;
-  a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
-  a.R = is_rproj(mode) ? R : 0;
-  a.e_hs = e_head_stride(mode, R, bias_range);
-  a.key_begin = 0;              // per sequence, from kv_lens
-  a.n_split = ns;
-  a.keys_per_wave = kpw;
-  a.c_qk = scale * rba::kLog2e;
-  a.temp_len = temp_len;
-  a.temp_inv_log2 = temp_inv_log2(temp_len);
-  a.block_table = block_table;
-  a.kv_lens = kv_lens;
-  a.page_size = page_size;
-  a.max_pages = max_pages;
-  a.num_pages = num_pages;
+  rba::DecodeArgs a = bf16_decode_args(q, k_pages, v_pages, o, lse, table, r, E, workspace, B, 0,
+                                       max_kv_len, Hq, Hkv, window, bias_range, mode, R, scale,
+                                       temp_len);
+  set_pages(a, block_table, kv_lens, num_pages, page_size, max_pages);
   hipError_t e = rba::launch_decode_bf16(a, D, kernel_mode(mode), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
   return ok();
@@ -456,59 +484,48 @@ int relbias_attn_decode_fp4(const void* q, const void* k_codes, const void* k_sc
                             const float* E, int R, float scale, int temp_len, void* workspace,
                             size_t workspace_bytes, void* stream) {
   const char* fn = "relbias_attn_decode_fp4";
-  if (B < 0) return fail(RBA_EINVAL, "%s: B=%d must be >= 0", fn, B);
-  int st = check_common(fn, RBA_BF16, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale);
-  if (st == RBA_OK) st = check_temp(fn, temp_len);
-  if (st != RBA_OK) return st;
-  if (D != 128) return fail(RBA_ENOTSUP, "%s: MXFP4 caches are supported for head_dim 128, got %d", fn, D);
-  const int G = Hq / Hkv;
-  if (G > 16) return fail(RBA_ENOTSUP, "%s: MXFP4 caches support Hq/Hkv <= 16, got %d", fn, G);
-  if (B == 0) return ok();
+  int st = check_fp4(fn, q, k_codes, k_scales, v_codes, v_scales, o, lse, B, Hq, Hkv, D, window,
+                     bias_range, mode, table, r, E, R, scale, temp_len);
+  if (st != RBA_OK || B == 0) return st == RBA_OK ? ok() : st;
   if (L_max < 1 || kv_len < 1 || kv_len > L_max)
     return fail(RBA_EINVAL, "%s: need 1 <= kv_len (%d) <= L_max (%d)", fn, kv_len, L_max);
-  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !o)
-    return fail(RBA_EINVAL, "%s: q, codes, scales and o must be non-NULL", fn);
-  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(o))
-    return fail(RBA_EINVAL, "%s: q, codes and o must be 16-byte aligned", fn);
-  if (lse && !aligned_to(lse, 4)) return fail(RBA_EINVAL, "%s: lse is not 4-byte aligned", fn);
-  int ns = 1, kpw = 64;
-  rba::decode_split(B, Hkv, kv_len, window, &ns, &kpw);
-  const size_t need = relbias_attn_decode_workspace_size(B, Hq, Hkv, D, kv_len, window);
-  if (need > 0) {
-    if (!workspace) return fail(RBA_EINVAL, "%s: workspace of %zu bytes required, got NULL", fn, need);
-    if (workspace_bytes < need)
-      return fail(RBA_EINVAL, "%s: workspace too small (%zu < %zu bytes)", fn, workspace_bytes, need);
-    if (!aligned_to(workspace, 4)) return fail(RBA_EINVAL, "%s: workspace is not 4-byte aligned", fn);
-  }
+  st = check_workspace(fn, relbias_attn_decode_workspace_size(B, Hq, Hkv, D, kv_len, window),
+                       workspace, workspace_bytes);
+  if (st != RBA_OK) return st;
   if (Hkv > 65535 || B > 65535) return fail(RBA_ENOTSUP, "%s: grid too large", fn);
-  rba::DecodeArgs a{};
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k_codes);
-  a.v = static_cast<const uint16_t*>(v_codes);
+  rba::DecodeArgs a = bf16_decode_args(q, k_codes, v_codes, o, lse, table, r, E, workspace, B, L_max,
+                                       kv_len, Hq, Hkv, window, bias_range, mode, R, scale, temp_len);
   a.k_scale = static_cast<const uint8_t*>(k_scales);
   a.v_scale = static_cast<const uint8_t*>(v_scales);
-  a.o = static_cast<uint16_t*>(o);
-  a.lse = lse;
-  a.table = table;
-  a.r = static_cast<const uint16_t*>(r);
-  a.E = E;
-  a.ws = static_cast<float*>(workspace);
-  a.B = B;
-  a.L_max = L_max;
-  a.kv_len = kv_len;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.G = G;
-  a.window = window;
-  a.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
-  a.R = is_rproj(mode) ? R : 0;
-  a.e_hs = e_head_stride(mode, R, bias_range);
-  a.key_begin = window ? (kv_len > window ? kv_len - window : 0) : 0;
-  a.n_split = ns;
-  a.keys_per_wave = kpw;
-  a.c_qk = scale * rba::kLog2e;
-  a.temp_len = temp_len;
-  a.temp_inv_log2 = temp_inv_log2(temp_len);
+  hipError_t e = rba::launch_decode_fp4(a, kernel_mode(mode), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+int relbias_attn_decode_fp4_paged(const void* q, const void* k_codes, const void* k_scales,
+                                  const void* v_codes, const void* v_scales,
+                                  const int* block_table, const int* kv_lens, void* o, float* lse,
+                                  int B, int num_pages, int page_size, int max_pages,
+                                  int max_kv_len, int Hq, int Hkv, int D, int window,
+                                  int bias_range, int mode, const float* table, const void* r,
+                                  const float* E, int R, float scale, int temp_len,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "relbias_attn_decode_fp4_paged";
+  int st = check_fp4(fn, q, k_codes, k_scales, v_codes, v_scales, o, lse, B, Hq, Hkv, D, window,
+                     bias_range, mode, table, r, E, R, scale, temp_len);
+  if (st != RBA_OK || B == 0) return st == RBA_OK ? ok() : st;
+  st = check_paged(fn, num_pages, page_size, max_pages, max_kv_len, block_table, kv_lens);
+  if (st != RBA_OK) return st;
+  st = check_workspace(fn, relbias_attn_decode_paged_workspace_size(B, Hq, Hkv, D, max_kv_len, window),
+                       workspace, workspace_bytes);
+  if (st != RBA_OK) return st;
+  if (Hkv > 65535 || B > 65535) return fail(RBA_ENOTSUP, "%s: grid too large", fn);
+  rba::DecodeArgs a = bf16_decode_args(q, k_codes, v_codes, o, lse, table, r, E, workspace, B, 0,
+                                       max_kv_len, Hq, Hkv, window, bias_range, mode, R, scale,
+                                       temp_len);
+  a.k_scale = static_cast<const uint8_t*>(k_scales);
+  a.v_scale = static_cast<const uint8_t*>(v_scales);
+  set_pages(a, block_table, kv_lens, num_pages, page_size, max_pages);
   hipError_t e = rba::launch_decode_fp4(a, kernel_mode(mode), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
   return ok();
