@@ -56,6 +56,7 @@ constexpr int BUF_BYTES = KT_BYTES + VT_BYTES;
 constexpr int CURVE_FLOATS = 32 * 36;   // per wave: 32 skewed fp32 rows of 36 entries
 constexpr int CURVE_BYTES = CURVE_FLOATS * 4;
 constexpr int TILE_BYTES = NBUF * BUF_BYTES;
+static_assert(4 * ROWS_WG * D * 2 <= TILE_BYTES, "the epilogue stages the four waves' rows in the ring");
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -626,21 +627,35 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
   }
 
   // ---- epilogue -------------------------------------------------------------------------------
+  // O^T holds 4-dim pieces of each row in the two lanes of that row; the rows go through the
+  // ring's LDS (8 KB per wave, once every wave is done with the last tile) so that each store
+  // instruction writes four whole 256-byte rows instead of 16 bytes of 32 rows.  Chunk c (16
+  // bytes) of row r sits at slot c ^ (r % 16), which keeps both the writes and the reads
+  // spread over the banks.
   const int row = i0 + ln;
   const float lt = pair_sum(l_run);
-  if (row < S) {
-    const float inv = 1.f / lt;
-    uint16_t* op = a.o + (static_cast<size_t>(b) * S + row) * q_row + static_cast<size_t>(h) * D;
+  const float inv = 1.f / lt;
+  unsigned char* ot = smem + wave * (ROWS_WG * D * 2);
+  __syncthreads();
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * db + 8 * g4 + 4 * lh;
-        const f32x16& acc = oacc[db];
-        st8(op + d, u32x2{pack_bf16x2(acc[4 * g4] * inv, acc[4 * g4 + 1] * inv),
-                          pack_bf16x2(acc[4 * g4 + 2] * inv, acc[4 * g4 + 3] * inv)});
-      }
-    if (a.lse && lh == 0) a.lse[(static_cast<size_t>(b) * a.Hq + h) * S + row] = (m_run + fast_log2(lt)) * kLn2;
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int chunk = (4 * db + g4) ^ (ln & 15);
+      const f32x16& acc = oacc[db];
+      *reinterpret_cast<u32x2*>(ot + ln * (D * 2) + chunk * 16 + 8 * lh) =
+          u32x2{pack_bf16x2(acc[4 * g4] * inv, acc[4 * g4 + 1] * inv),
+                pack_bf16x2(acc[4 * g4 + 2] * inv, acc[4 * g4 + 3] * inv)};
+    }
+  if (a.lse && lh == 0 && row < S)
+    a.lse[(static_cast<size_t>(b) * a.Hq + h) * S + row] = (m_run + fast_log2(lt)) * kLn2;
+  wave_sync_lds();
+#pragma unroll
+  for (int it = 0; it < ROWS_WG / 4; ++it) {
+    const int r = 4 * it + (lane >> 4);
+    const int c = lane & 15;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ot + r * (D * 2) + ((c ^ (r & 15)) * 16));
+    if (i0 + r < S) st16(a.o + (static_cast<size_t>(b) * S + i0 + r) * q_row + static_cast<size_t>(h) * D + 8 * c, v);
   }
 }
 
