@@ -303,7 +303,9 @@ size_t relbias_attn_bwd_workspace_size(int B, int S, int Hq, int mode, int bias_
  *   dE[h, f, d] = sum over tokens of r[token, h, f] dZ at distance d (summed over heads
  *   for RBA_BIAS_RPROJ_SHARED).
  *
- *   dtype       RBA_BF16 only (RBA_ENOTSUP otherwise); D in {64, 128}.
+ *   dtype       RBA_BF16 (D in {64, 128}; MFMA kernels) or RBA_F32 (D in {32, 64, 128};
+ *               vector-ALU kernels, fp32 throughout); every tensor below of that dtype
+ *               unless stated.
  *   q, k, v, window, bias_range, mode, table, r, E, R, scale, temp_len, shapes:
  *               exactly as passed to relbias_attn_fwd.
  *   o           [B, S, Hq, D]: the forward's output.

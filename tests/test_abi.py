@@ -235,7 +235,8 @@ def _bwd(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,code,needle", [
-    (dict(dtype=F32), ENOTSUP, "bf16 only"),
+    (dict(dtype=F32, D=96), ENOTSUP, "head_dim"),
+    (dict(dtype=F32, mode=2, r=P, E=P, R=8, dr=P + 2, dE=P), EINVAL, "dr and dE"),
     (dict(dtype=7), EINVAL, "dtype"),
     (dict(Hq=6, Hkv=4), EINVAL, "multiple"),
     (dict(D=96), ENOTSUP, "head_dim"),

@@ -8,7 +8,8 @@ for references that vanish.  The kernels round P and dZ to bf16 before the MFMAs
 stored o enters rowsum(dout * o), each about 2^-9 relative; the bias reaches the recomputed
 logits in fp32 (E as a bf16 high and low part).  dr takes 7.5e-3: its product adds two more
 bf16 operands (E and the diagonal sums of dZ, each rounded once more), and with a sharp bias
-(E at std 1.0) it measures about 5e-3.
+(E at std 1.0) it measures about 5e-3.  The fp32 path (vector-ALU kernels, no bf16 rounding)
+takes the forward's fp32 bar: 1e-5 relative L2 and 1e-5 of the largest reference element.
 """
 
 import sys
@@ -25,6 +26,9 @@ from transformer_attention_learned_amd.workloads import WORKLOADS, Workload, mak
 pytestmark = pytest.mark.gpu
 
 REL_L2, REL_L2_DR, MAX_REL = 5e-3, 7.5e-3, 2e-2
+# fp32 path: the fp32 bar of the forward (1e-5), relative L2 and max |err| / max |ref| alike;
+# fp32 products and sums of a few hundred terms sit near 1e-7-1e-6
+F32_REL = 1e-5
 
 
 def _say(msg):
@@ -61,20 +65,28 @@ def run_bwd(w: Workload, inp, dout):
     return g
 
 
-def compare(name, got, ref):
+def compare(name, got, ref, f32=False):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     # floors for references that vanish (dq, dk and the bias gradients when every row sees a
-    # single key, where dS is zero up to fp32 rounding): an RMS of 1e-3 per element, a
-    # maximum of 1e-2
-    scale = max(float(np.abs(ref).max()), 1e-2)
+    # single key, where dS is zero up to rounding): an RMS of 1e-3 per element and a maximum of
+    # 1e-2 for bf16.  fp32: there dZ = P (dP - rowsum) cancels two fp32 sums of D products of
+    # size about 1 taken in different orders, a residue of about 2^-24 D (1-3e-6 at D = 32) per
+    # element, times scale * k in dq and dk and times r or E (up to about 3) in dE and dr; the
+    # floors (RMS 1e-1, maximum 1) allow 1e-6 RMS and 1e-5 at most against such a vanishing
+    # reference at the 1e-5 bar
+    floor_rms, floor_max = (1e-1, 1.0) if f32 else (1e-3, 1e-2)
+    scale = max(float(np.abs(ref).max()), floor_max)
     max_rel = float(np.abs(got - ref).max()) / scale
-    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-3 * np.sqrt(ref.size)))
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), floor_rms * np.sqrt(ref.size)))
     _say(f"    {name}: rel_l2={rel:.3e} max_err/max_ref={max_rel:.3e}")
-    bar = REL_L2_DR if name.startswith("dr") else REL_L2
-    assert rel <= bar and max_rel <= MAX_REL, (name, rel, max_rel)
+    if f32:
+        assert rel <= F32_REL and max_rel <= F32_REL, (name, rel, max_rel)
+    else:
+        bar = REL_L2_DR if name.startswith("dr") else REL_L2
+        assert rel <= bar and max_rel <= MAX_REL, (name, rel, max_rel)
 
 
 def check_bwd(w: Workload, heads=None):
@@ -99,19 +111,20 @@ def check_bwd(w: Workload, heads=None):
             r=sub(inp["r"]),
             E=None if inp["E"] is None else (inp["E"] if shared else inp["E"][hs]),
             temp_len=w.temp_len)
-        compare(f"dq[kv {hk}]", _t2np(g["dq"][:, :, hs]), ref["dq"])
-        compare(f"dk[kv {hk}]", _t2np(g["dk"][:, :, hk:hk + 1]), ref["dk"])
-        compare(f"dv[kv {hk}]", _t2np(g["dv"][:, :, hk:hk + 1]), ref["dv"])
+        f32 = w.dtype == "f32"
+        compare(f"dq[kv {hk}]", _t2np(g["dq"][:, :, hs]), ref["dq"], f32)
+        compare(f"dk[kv {hk}]", _t2np(g["dk"][:, :, hk:hk + 1]), ref["dk"], f32)
+        compare(f"dv[kv {hk}]", _t2np(g["dv"][:, :, hk:hk + 1]), ref["dv"], f32)
         if w.mode == "table":
-            compare(f"dtable[kv {hk}]", _t2np(g["dtable"][hs]), ref["dtable"])
+            compare(f"dtable[kv {hk}]", _t2np(g["dtable"][hs]), ref["dtable"], f32)
         if w.mode in ("rproj", "rproj_shared"):
-            compare(f"dr[kv {hk}]", _t2np(g["dr"][:, :, hs]), ref["dr"])
+            compare(f"dr[kv {hk}]", _t2np(g["dr"][:, :, hs]), ref["dr"], f32)
             if shared:
                 dE_ref = ref["dE"] if dE_ref is None else dE_ref + ref["dE"]
             else:
-                compare(f"dE[kv {hk}]", _t2np(g["dE"][hs]), ref["dE"])
+                compare(f"dE[kv {hk}]", _t2np(g["dE"][hs]), ref["dE"], f32)
     if shared and heads is None:
-        compare("dE (shared bank)", _t2np(g["dE"]), dE_ref)
+        compare("dE (shared bank)", _t2np(g["dE"]), dE_ref, w.dtype == "f32")
 
 
 def small(**kw):
@@ -183,3 +196,57 @@ def test_bwd_deterministic_dq_dk_dv():
     g2 = run_bwd(w, inp, dout)
     for n in ("dq", "dk", "dv", "dr"):
         assert torch.equal(g1[n], g2[n]), n
+
+
+# fp32 backward: the vector-ALU kernels against the same oracle at the fp32 bar
+F32_SWEEP = [
+    dict(S=1), dict(S=33), dict(S=200), dict(S=200, mode="none"),
+    dict(S=200, mode="table", bias_range=50), dict(S=300, mode="table", window=70, bias_range=40),
+    dict(S=200, D=64, Hq=4, Hkv=2), dict(S=130, D=128, R=16, Hq=2, Hkv=1),
+    dict(S=250, mode="rproj_shared", R=5, bias_range=77, window=100, Hq=4, Hkv=2,
+         logit_scale="inv_d"),
+    dict(S=300, temp_len=64, window=150, bias_range=100), dict(S=200, e_std=1.0),
+    dict(S=120, bias_range=1),
+]
+
+
+@pytest.mark.parametrize("kw", F32_SWEEP, ids=lambda kw: "-".join(f"{k}{v}" for k, v in kw.items()))
+def test_bwd_f32(kw):
+    base = dict(dtype="f32", D=32, Hq=2, Hkv=1)
+    base.update(kw)
+    check_bwd(small(seed=zlib.crc32(repr(sorted(base.items())).encode()) % 10007, **base))
+
+
+def test_bwd_f32_tiny_layer():
+    """The tiny fp32 local layer (window 64, table bias) end to end."""
+    check_bwd(WORKLOADS["tiny_local_f32"].with_(name="bwd_tiny_f32"))
+
+
+def test_bwd_f32_single_key_rows():
+    """Window 1: every row sees only its own key, so P = 1, o = v and dZ = P (dP - rowsum) is zero;
+    what the fp32 kernels return for dq, dk, dr and dE is the rounding of two fp32 dot products of
+    length D, at most 2 gamma_D sum_d |dout v| per row (gamma_D = D 2^-24, the classical bound of
+    a recursive fp32 sum), carried through each gradient's formula; dv is the group's summed dout."""
+    w = small(dtype="f32", D=32, Hq=3, Hkv=1, B=2, S=97, window=1, seed=6545)
+    inp = make_inputs(w, device="cuda")
+    dout = _dout(w, inp["q"])
+    g = run_bwd(w, inp, dout)
+    q, k, v, do, r, E = (_t2np(t) for t in (inp["q"], inp["k"], inp["v"], dout, inp["r"], inp["E"]))
+    G = w.Hq // w.Hkv
+    vh = np.repeat(v, G, axis=2)                                   # [B, S, Hq, D]
+    res = 2 * w.D * 2.0 ** -24 * np.abs(do * vh).sum(-1)           # |dZ| bound per (b, i, h)
+    bound = {
+        "dq": w.scale * res[..., None] * np.abs(np.repeat(k, G, axis=2)),
+        "dk": w.scale * (res[..., None] * np.abs(q)).reshape(w.B, w.S, w.Hkv, G, w.D).sum(3),
+        "dr": res[..., None] * np.abs(E[:, :, 0])[None, None],
+    }
+    dE_bound = np.zeros_like(E)
+    dE_bound[:, :, 0] = np.einsum("bih,bihf->hf", res, np.abs(r))
+    for name in ("dq", "dk", "dr"):
+        got = np.abs(_t2np(g[name]))
+        _say(f"    {name}: max |got| = {got.max():.3e}, max bound = {bound[name].max():.3e}")
+        assert np.all(got <= 1.01 * bound[name] + 1e-30), name
+    gE = np.abs(_t2np(g["dE"]))
+    _say(f"    dE: max |got| = {gE.max():.3e}, max bound = {dE_bound.max():.3e}")
+    assert np.all(gE <= 1.01 * dE_bound + 1e-30)
+    compare("dv", _t2np(g["dv"]), do.reshape(w.B, w.S, w.Hkv, G, w.D).sum(3), f32=True)

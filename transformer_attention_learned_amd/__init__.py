@@ -244,8 +244,9 @@ def bwd(q, k, v, o, lse, dout, *, window=0, bias_range=0, mode="none", table=Non
     """Backward of fwd (relbias_attn_bwd): gradients for an upstream gradient dout on o.
 
     q, k, v, window, bias_range, mode, table, r, E, scale, temp_len: as passed to fwd;
-    o and lse [B,Hq,S] fp32: fwd's outputs.  bf16 only.  Returns a dict with dq, dk, dv and
-    dtable (mode "table") or dr and dE (modes "rproj", "rproj_shared").
+    o and lse [B,Hq,S] fp32: fwd's outputs.  bf16 (D 64 / 128) or fp32 (D 32 / 64 / 128).
+    Returns a dict with dq, dk, dv and dtable (mode "table") or dr and dE (modes "rproj",
+    "rproj_shared").
     """
     import torch
     lib = load_library()

@@ -551,7 +551,6 @@ int relbias_attn_bwd(int dtype, const void* q, const void* k, const void* v, con
   int st = check_common(fn, dtype, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale);
   if (st == RBA_OK) st = check_temp(fn, temp_len);
   if (st != RBA_OK) return st;
-  if (dtype != RBA_BF16) return fail(RBA_ENOTSUP, "%s: the backward pass is supported for bf16 only", fn);
   if (B == 0 || S == 0) return ok();
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
     return fail(RBA_EINVAL, "%s: q, k, v, o, lse, dout, dq, dk and dv must be non-NULL", fn);
@@ -561,11 +560,11 @@ int relbias_attn_bwd(int dtype, const void* q, const void* k, const void* v, con
   if (!aligned_to(lse, 4)) return fail(RBA_EINVAL, "%s: lse is not 4-byte aligned", fn);
   if (mode == RBA_BIAS_TABLE && (!dtable || !aligned_to(dtable, 4)))
     return fail(RBA_EINVAL, "%s: table mode needs a 4-byte aligned dtable", fn);
-  if (is_rproj(mode) && (!dr || !dE || !aligned_to(dr, 2) || !aligned_to(dE, 4)))
+  if (is_rproj(mode) && (!dr || !dE || !aligned_to(dr, dtype == RBA_F32 ? 4 : 2) || !aligned_to(dE, 4)))
     return fail(RBA_EINVAL, "%s: rproj modes need aligned dr and dE", fn);
   const long long rows = static_cast<long long>(B) * S;
   if (rows * Hq * D >= (1LL << 40)) return fail(RBA_ENOTSUP, "%s: problem too large", fn);
-  if (rba::bwd_lds_bytes(D, kernel_mode(mode), bias_range, is_rproj(mode) ? R : 0) < 0)
+  if (dtype == RBA_BF16 && rba::bwd_lds_bytes(D, kernel_mode(mode), bias_range, is_rproj(mode) ? R : 0) < 0)
     return fail(RBA_ENOTSUP, "%s: bias_range=%d needs more LDS than the kernels have", fn, bias_range);
   const size_t need = relbias_attn_bwd_workspace_size(B, S, Hq, mode, bias_range);
   if (!workspace) return fail(RBA_EINVAL, "%s: workspace of %zu bytes required, got NULL", fn, need);
@@ -573,8 +572,44 @@ int relbias_attn_bwd(int dtype, const void* q, const void* k, const void* v, con
     return fail(RBA_EINVAL, "%s: workspace too small (%zu < %zu bytes)", fn, workspace_bytes, need);
   if (!aligned_to(workspace, 16)) return fail(RBA_EINVAL, "%s: workspace is not 16-byte aligned", fn);
   const int G = Hq / Hkv;
-  const long long nq = ((S + 127) / 128) * static_cast<long long>(Hq) * B;
+  const long long nq = ((S + 31) / 32) * static_cast<long long>(Hq) * B;
   if (nq > 0x7fffffffLL) return fail(RBA_ENOTSUP, "%s: grid too large", fn);
+  if (dtype == RBA_F32) {
+    rba::BwdF32Args f{};
+    f.q = static_cast<const float*>(q);
+    f.k = static_cast<const float*>(k);
+    f.v = static_cast<const float*>(v);
+    f.o = static_cast<const float*>(o);
+    f.dout = static_cast<const float*>(dout);
+    f.lse = lse;
+    f.dq = static_cast<float*>(dq);
+    f.dk = static_cast<float*>(dk);
+    f.dv = static_cast<float*>(dv);
+    f.dr = static_cast<float*>(dr);
+    f.dE = dE;
+    f.dtable = dtable;
+    f.table = table;
+    f.r = static_cast<const float*>(r);
+    f.E = E;
+    f.e_hs = e_head_stride(mode, R, bias_range);
+    f.dsum = static_cast<float*>(workspace);
+    f.B = B;
+    f.S = S;
+    f.Hq = Hq;
+    f.Hkv = Hkv;
+    f.G = G;
+    f.D = D;
+    f.window = window;
+    f.bias_range = mode == RBA_BIAS_NONE ? 0 : bias_range;
+    f.mode = kernel_mode(mode);
+    f.R = is_rproj(mode) ? R : 0;
+    f.scale = scale;
+    f.temp_len = temp_len;
+    f.temp_inv_log2 = temp_inv_log2(temp_len);
+    hipError_t e = rba::launch_bwd_f32(f, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
+    return ok();
+  }
   rba::BwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);

@@ -146,6 +146,32 @@ struct BwdArgs {
   float temp_inv_log2;
 };
 
+// Backward arguments (fp32 vector-ALU path): the tensors of BwdArgs in fp32 (dr like r).
+struct BwdF32Args {
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* o;
+  const float* dout;
+  const float* lse;     // [B, Hq, S] natural-log sum-exp of the forward
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dr;            // [B, S, Hq, R]
+  float* dE;            // head h at dE + h * e_hs
+  float* dtable;        // [Hq, bias_range]
+  const float* table;
+  const float* r;
+  const float* E;
+  long long e_hs;       // head stride of E and dE in floats (0: one shared bank)
+  float* dsum;          // workspace [B, Hq, S]: rowsum(dout * o)
+  int B, S, Hq, Hkv, G, D;
+  int window, bias_range, mode, R;
+  float scale;
+  int temp_len;
+  float temp_inv_log2;
+};
+
 // Raise a kernel's dynamic-LDS limit to `bytes` (no-op up to 64 KB) on the device of stream s,
 // once per (kernel, device); thread-safe.
 hipError_t set_max_lds(const void* fn, int bytes, hipStream_t s);
@@ -162,6 +188,8 @@ hipError_t launch_fwd_bf16_split(const FwdArgs& a, int mode, void* workspace, hi
 hipError_t launch_e2_convert(const float* E, long long e_hs, int R, int bias_range, float inv_scale, int heads,
                              uint16_t* e2, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int D, int mode, hipStream_t s);
+// fp32 backward (D = 32, 64 or 128; mode 0 none, 1 table, 2 r.E)
+hipError_t launch_bwd_f32(const BwdF32Args& a, hipStream_t s);
 // LDS bytes of the largest backward kernel for this shape, or -1 when it does not fit.
 int bwd_lds_bytes(int D, int mode, int bias_range, int R);
 hipError_t launch_attn_f32(const F32Args& a, hipStream_t s);
