@@ -245,7 +245,7 @@ int relbias_attn_kv_quantize_fp4(const void* x, void* codes, void* scales, long 
  * k_codes [B, L_max, Hkv, D / 2] + k_scales [B, L_max, Hkv, D / 32] (and the same for V) in
  * the layout relbias_attn_kv_quantize_fp4 writes; each element is code value * 2^(s - 127)
  * (scale byte 0 reads as 0).  q is bf16 [B, Hq, D]; every other argument (workspace size
- * included) as in relbias_attn_decode with dtype RBA_BF16.  Supported: D = 128 and
+ * included) as in relbias_attn_decode with dtype RBA_BF16.  Supported: D = 64 or 128 and
  * Hq / Hkv <= 16 (RBA_ENOTSUP otherwise).
  */
 int relbias_attn_decode_fp4(const void* q, const void* k_codes, const void* k_scales,
@@ -270,7 +270,7 @@ int relbias_attn_decode_fp4(const void* q, const void* k_codes, const void* k_sc
  *               bias_range, mode, table, r, E, R, scale, temp_len, workspace: as in
  *               relbias_attn_decode_paged (dtype RBA_BF16), with the same clamping of the
  *               device values and the same workspace size.
- * Supported: D = 128 and Hq / Hkv <= 16 (RBA_ENOTSUP otherwise).
+ * Supported: D = 64 or 128 and Hq / Hkv <= 16 (RBA_ENOTSUP otherwise).
  */
 int relbias_attn_decode_fp4_paged(const void* q, const void* k_codes, const void* k_scales,
                                   const void* v_codes, const void* v_scales,

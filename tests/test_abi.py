@@ -288,7 +288,7 @@ def test_fp4_rejects(lib):
             a["q"], a["kc"], a["ks"], a["vc"], a["vs"], a["o"], a["lse"], a["B"], a["L"],
             a["kv_len"], a["Hq"], a["Hkv"], a["D"], a["window"], a["bias_range"], a["mode"],
             a["table"], a["r"], a["E"], a["R"], a["scale"], a["temp_len"], a["ws"], a["wsb"], None)
-    assert dec(D=64) == ENOTSUP and "head_dim 128" in rba.last_error()
+    assert dec(D=96) == ENOTSUP and "head_dim" in rba.last_error()
     assert dec(Hq=32, Hkv=1) == ENOTSUP and "<= 16" in rba.last_error()
     assert dec(kv_len=0) == EINVAL and "kv_len" in rba.last_error()
     assert dec(ks=None) == EINVAL and "non-NULL" in rba.last_error()
@@ -311,7 +311,7 @@ def _fp4_paged(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,code,needle", [
-    (dict(D=64), ENOTSUP, "head_dim 128"),
+    (dict(D=96), ENOTSUP, "head_dim"),
     (dict(Hq=32, Hkv=1), ENOTSUP, "<= 16"),
     (dict(page_size=24), ENOTSUP, "page_size"),
     (dict(max_kv_len=129), EINVAL, "max_kv_len"),

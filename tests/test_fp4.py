@@ -44,10 +44,11 @@ def _host_quant(x):
     return torch.from_numpy(mxfp4.pack(codes)), torch.from_numpy(sb)
 
 
-def test_quantize_bit_exact():
+@pytest.mark.parametrize("D", [64, 128])
+def test_quantize_bit_exact(D):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(5)
-    rows, D = 3000, 128
+    rows = 3000
     x = torch.randn((rows, D), generator=gen, device="cuda", dtype=torch.float32)
     # block magnitudes over a wide exponent range, exact midpoints, zero and tiny blocks
     k = torch.randint(-30, 30, (rows, D // 32), generator=gen, device="cuda").to(torch.float32)
@@ -110,6 +111,11 @@ CASES = [
     dict(S=3000, kv_len=2600, mode="rproj_shared", R=16, window=512, bias_range=512,
          logit_scale="inv_d"),
     dict(S=3000, kv_len=2900, Hq=16, Hkv=1, window=700), dict(S=4000, kv_len=3000, temp_len=1024),
+    # head_dim 64: a lane's K fragment is 8 code bytes of one 32-element block
+    dict(S=3000, kv_len=2999, D=64), dict(S=2000, kv_len=1500, D=64, mode="table", bias_range=300,
+                                           window=700),
+    dict(S=1000, kv_len=999, D=64, Hq=16, Hkv=1, mode="rproj_shared", R=16, logit_scale="inv_d"),
+    dict(S=100, kv_len=1, D=64),
 ]
 
 
@@ -204,6 +210,8 @@ PAGED_CASES = [
      [1300, 1000, 513, 17], 64),
     (dict(B=3, S=5000, bias_range=1024, Hq=32, Hkv=2), [5000, 4097, 1025], 128),
     (dict(S=3000, temp_len=256), [3000, 2000, 257, 100], 64),
+    (dict(D=64), [700, 1, 33, 640], 16),
+    (dict(D=64, window=96, mode="table", bias_range=50, Hq=8, Hkv=1), [700, 97, 96, 2], 64),
 ]
 
 

@@ -201,7 +201,8 @@ int check_fp4(const char* fn, const void* q, const void* k_codes, const void* k_
   int st = check_common(fn, RBA_BF16, Hq, Hkv, D, window, bias_range, mode, table, r, E, R, scale);
   if (st == RBA_OK) st = check_temp(fn, temp_len);
   if (st != RBA_OK) return st;
-  if (D != 128) return fail(RBA_ENOTSUP, "%s: MXFP4 caches are supported for head_dim 128, got %d", fn, D);
+  if (D != 64 && D != 128)
+    return fail(RBA_ENOTSUP, "%s: MXFP4 caches are supported for head_dim 64 or 128, got %d", fn, D);
   const int G = Hq / Hkv;
   if (G > 16) return fail(RBA_ENOTSUP, "%s: MXFP4 caches support Hq/Hkv <= 16, got %d", fn, G);
   if (B == 0) return RBA_OK;
@@ -497,7 +498,7 @@ int relbias_attn_decode_fp4(const void* q, const void* k_codes, const void* k_sc
                                        kv_len, Hq, Hkv, window, bias_range, mode, R, scale, temp_len);
   a.k_scale = static_cast<const uint8_t*>(k_scales);
   a.v_scale = static_cast<const uint8_t*>(v_scales);
-  hipError_t e = rba::launch_decode_fp4(a, kernel_mode(mode), static_cast<hipStream_t>(stream));
+  hipError_t e = rba::launch_decode_fp4(a, D, kernel_mode(mode), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
   return ok();
 }
@@ -526,7 +527,7 @@ int relbias_attn_decode_fp4_paged(const void* q, const void* k_codes, const void
   a.k_scale = static_cast<const uint8_t*>(k_scales);
   a.v_scale = static_cast<const uint8_t*>(v_scales);
   set_pages(a, block_table, kv_lens, num_pages, page_size, max_pages);
-  hipError_t e = rba::launch_decode_fp4(a, kernel_mode(mode), static_cast<hipStream_t>(stream));
+  hipError_t e = rba::launch_decode_fp4(a, D, kernel_mode(mode), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(RBA_EHIP, "%s: HIP error %s", fn, hipGetErrorString(e));
   return ok();
 }

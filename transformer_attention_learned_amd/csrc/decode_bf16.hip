@@ -366,8 +366,8 @@ __device__ __forceinline__ float e8m0(uint32_t byte) { return __uint_as_float(by
 // FP4: the caches hold MXFP4 codes (a.k / a.v: D / 2 bytes per row and kv head) and E8M0
 // block scales (a.k_scale / a.v_scale: D / 32 bytes); the tiles in flight are the packed bytes
 // (a quarter of the registers of bf16 rows) and are widened to bf16 where the MFMAs use them.
-// A lane's K fragment then covers head dims 32 g + 8 c .. + 7 (one 16-byte load per row and a
-// single scale), so the query fragments use the same dims.
+// A lane's K fragment then covers head dims (D / 4) g + 8 c .. + 7 (one 16-byte load per row at
+// D = 128, 8 bytes at D = 64, and a single scale), so the query fragments use the same dims.
 template <int D, int MODE, int RMAX, bool FP4>
 __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curve_off) {
   constexpr int VST = TK + 8;          // V^T row stride (bf16)
@@ -415,6 +415,8 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
   u32x4 kc[2][2];
   uint32_t ksb[2][2], vc[2][NVI][4], vsb[2][NVI][4];
   constexpr int CB = D / 2, SB = D / 32;
+  constexpr int EPL = D / 4;   // FP4: head-dim elements of a lane's K fragment (D = 64 or 128)
+  static_assert(!FP4 || EPL == 16 || EPL == 32, "MXFP4 caches: head_dim 64 or 128");
   const size_t crow = static_cast<size_t>(a.Hkv) * CB, srow = static_cast<size_t>(a.Hkv) * SB;
   const size_t cbatch = paged ? 0 : static_cast<size_t>(b) * a.L_max;
   const uint8_t* kcb = reinterpret_cast<const uint8_t*>(a.k) + (cbatch * a.Hkv + hkv) * CB;
@@ -434,8 +436,14 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
         kc[set][kb] = u32x4{0u, 0u, 0u, 0u};
         ksb[set][kb] = 0u;
         if (key < w_end) {
-          kc[set][kb] = ld16(kcb + static_cast<size_t>(prow) * crow + 16 * g);
-          ksb[set][kb] = ksp[static_cast<size_t>(prow) * srow + g];
+          const uint8_t* kp = kcb + static_cast<size_t>(prow) * crow + (EPL / 2) * g;
+          if constexpr (EPL == 32) {
+            kc[set][kb] = ld16(kp);
+          } else {
+            const u32x2 w2 = ld8(kp);
+            kc[set][kb] = u32x4{w2[0], w2[1], 0u, 0u};
+          }
+          ksb[set][kb] = ksp[static_cast<size_t>(prow) * srow + (EPL * g) / 32];
         }
       } else {
         const uint16_t* kp = kbase + static_cast<size_t>(prow) * kv_row + 8 * g;
@@ -473,7 +481,7 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
 
   bf16x8 qf[NC];
   {
-    const uint16_t* qp = a.q + (static_cast<size_t>(b) * a.Hq + hkv * G + (col_live ? n16 : 0)) * D + (FP4 ? 32 * g : 8 * g);
+    const uint16_t* qp = a.q + (static_cast<size_t>(b) * a.Hq + hkv * G + (col_live ? n16 : 0)) * D + (FP4 ? EPL * g : 8 * g);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       u32x4 v = {0u, 0u, 0u, 0u};
@@ -802,11 +810,18 @@ void decode_split(int B, int Hkv, int kv_len, int window, int* n_split, int* key
   *keys_per_wave = static_cast<int>(kpw);
 }
 
-hipError_t launch_decode_fp4(DecodeArgs a, int mode, hipStream_t s) {
+hipError_t launch_decode_fp4(DecodeArgs a, int D, int mode, hipStream_t s) {
+  if (D == 128) {
+    switch (mode) {
+      case 0: return launch_d<128, 0, 1, true>(a, s);
+      case 1: return launch_d<128, 1, 1, true>(a, s);
+      default: return a.R > 8 ? launch_d<128, 2, 16, true>(a, s) : launch_d<128, 2, 8, true>(a, s);
+    }
+  }
   switch (mode) {
-    case 0: return launch_d<128, 0, 1, true>(a, s);
-    case 1: return launch_d<128, 1, 1, true>(a, s);
-    default: return a.R > 8 ? launch_d<128, 2, 16, true>(a, s) : launch_d<128, 2, 8, true>(a, s);
+    case 0: return launch_d<64, 0, 1, true>(a, s);
+    case 1: return launch_d<64, 1, 1, true>(a, s);
+    default: return a.R > 8 ? launch_d<64, 2, 16, true>(a, s) : launch_d<64, 2, 8, true>(a, s);
   }
 }
 
