@@ -246,7 +246,7 @@ int relbias_attn_kv_quantize_fp4(const void* x, void* codes, void* scales, long 
  * the layout relbias_attn_kv_quantize_fp4 writes; each element is code value * 2^(s - 127)
  * (scale byte 0 reads as 0).  q is bf16 [B, Hq, D]; every other argument (workspace size
  * included) as in relbias_attn_decode with dtype RBA_BF16.  Supported: D = 64 or 128 and
- * Hq / Hkv <= 16 (RBA_ENOTSUP otherwise).
+ * Hq / Hkv <= 32 (RBA_ENOTSUP otherwise).
  */
 int relbias_attn_decode_fp4(const void* q, const void* k_codes, const void* k_scales,
                             const void* v_codes, const void* v_scales, void* o, float* lse, int B,
@@ -270,7 +270,7 @@ int relbias_attn_decode_fp4(const void* q, const void* k_codes, const void* k_sc
  *               bias_range, mode, table, r, E, R, scale, temp_len, workspace: as in
  *               relbias_attn_decode_paged (dtype RBA_BF16), with the same clamping of the
  *               device values and the same workspace size.
- * Supported: D = 64 or 128 and Hq / Hkv <= 16 (RBA_ENOTSUP otherwise).
+ * Supported: D = 64 or 128 and Hq / Hkv <= 32 (RBA_ENOTSUP otherwise).
  */
 int relbias_attn_decode_fp4_paged(const void* q, const void* k_codes, const void* k_scales,
                                   const void* v_codes, const void* v_scales,

@@ -289,7 +289,7 @@ def test_fp4_rejects(lib):
             a["kv_len"], a["Hq"], a["Hkv"], a["D"], a["window"], a["bias_range"], a["mode"],
             a["table"], a["r"], a["E"], a["R"], a["scale"], a["temp_len"], a["ws"], a["wsb"], None)
     assert dec(D=96) == ENOTSUP and "head_dim" in rba.last_error()
-    assert dec(Hq=32, Hkv=1) == ENOTSUP and "<= 16" in rba.last_error()
+    assert dec(Hq=64, Hkv=1) == ENOTSUP and "<= 32" in rba.last_error()
     assert dec(kv_len=0) == EINVAL and "kv_len" in rba.last_error()
     assert dec(ks=None) == EINVAL and "non-NULL" in rba.last_error()
     assert dec(vc=P + 4) == EINVAL and "aligned" in rba.last_error()
@@ -312,7 +312,7 @@ def _fp4_paged(lib, **kw):
 
 @pytest.mark.parametrize("kw,code,needle", [
     (dict(D=96), ENOTSUP, "head_dim"),
-    (dict(Hq=32, Hkv=1), ENOTSUP, "<= 16"),
+    (dict(Hq=64, Hkv=1), ENOTSUP, "<= 32"),
     (dict(page_size=24), ENOTSUP, "page_size"),
     (dict(max_kv_len=129), EINVAL, "max_kv_len"),
     (dict(max_kv_len=0), EINVAL, "max_kv_len"),

@@ -116,6 +116,11 @@ CASES = [
                                            window=700),
     dict(S=1000, kv_len=999, D=64, Hq=16, Hkv=1, mode="rproj_shared", R=16, logit_scale="inv_d"),
     dict(S=100, kv_len=1, D=64),
+    # groups of 17..32 query heads: the 32x32 MFMA kernel with its MXFP4 path
+    dict(S=2000, kv_len=1999, Hq=32, Hkv=1), dict(S=100, kv_len=1, Hq=32, Hkv=1),
+    dict(S=3000, kv_len=2500, Hq=24, Hkv=1, window=700, mode="table", bias_range=300),
+    dict(S=1500, kv_len=1400, Hq=20, Hkv=1, D=64, mode="rproj_shared", R=16, logit_scale="inv_d"),
+    dict(S=2500, kv_len=2400, Hq=32, Hkv=1, R=16, temp_len=512),
 ]
 
 
@@ -212,6 +217,7 @@ PAGED_CASES = [
     (dict(S=3000, temp_len=256), [3000, 2000, 257, 100], 64),
     (dict(D=64), [700, 1, 33, 640], 16),
     (dict(D=64, window=96, mode="table", bias_range=50, Hq=8, Hkv=1), [700, 97, 96, 2], 64),
+    (dict(Hq=32, Hkv=1), [700, 1, 33, 640], 32),
 ]
 
 

@@ -204,7 +204,7 @@ int check_fp4(const char* fn, const void* q, const void* k_codes, const void* k_
   if (D != 64 && D != 128)
     return fail(RBA_ENOTSUP, "%s: MXFP4 caches are supported for head_dim 64 or 128, got %d", fn, D);
   const int G = Hq / Hkv;
-  if (G > 16) return fail(RBA_ENOTSUP, "%s: MXFP4 caches support Hq/Hkv <= 16, got %d", fn, G);
+  if (G > 32) return fail(RBA_ENOTSUP, "%s: MXFP4 caches support Hq/Hkv <= 32, got %d", fn, G);
   if (B == 0) return RBA_OK;
   if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !o)
     return fail(RBA_EINVAL, "%s: q, codes, scales and o must be non-NULL", fn);

@@ -42,8 +42,22 @@ __device__ __forceinline__ int vt_pos(int x) {
   return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
-// RMAX: r.E features held per curve item (8 or 16; 1 for the table)
-template <int D, int MODE, int RMAX>
+// 8 MXFP4 codes (element 2j in the low nibble of byte j) times the block scale -> 8 bf16,
+// with the hardware FP4 conversion (v_cvt_scalef32_pk_bf16_fp4, one byte per instruction).
+__device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t codes, float sc) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3))};
+}
+// E8M0 scale byte -> 2^(byte - 127) as fp32 (byte 0, an all-zero block, reads as 0).
+__device__ __forceinline__ float e8m0(uint32_t byte) { return __uint_as_float(byte << 23); }
+
+// RMAX: r.E features held per curve item (8 or 16; 1 for the table).  FP4: MXFP4 caches (codes
+// and scales as in the 16x16 kernel below); a lane half's K fragments then cover head dims
+// (D / 2) lh + 8 c .. + 7, one or two 16-byte code loads and D / 64 scale bytes per row, and the
+// query fragments use the same dims; V rows arrive as 8-dim pieces of 4 code bytes and a scale.
+template <int D, int MODE, int RMAX, bool FP4 = false>
 __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int curve_off) {
   constexpr int VST = TK + 8;          // V^T row stride (bf16): 80-byte rows, 16-byte aligned
   constexpr int NC = D / 16;           // K = 16 chunks of the head dim
@@ -91,16 +105,41 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
   const int ntiles = w_end > w_beg ? (w_end - w_beg + TK - 1) / TK : 0;
 
   // ---- registers of the tile in flight: K as MFMA A-operand fragments, V as row pieces ---
-  u32x4 kreg[NC], vreg[NVI][4];
+  u32x4 kreg[FP4 ? 1 : NC], vreg[NVI][FP4 ? 1 : 4];
+  // FP4: a lane half's D / 4 code bytes and D / 64 scale bytes per K row, 4 code bytes and a
+  // scale byte per V piece
+  constexpr int NKB = FP4 ? D / 64 : 1;   // 16-byte code loads (and scale blocks) per K row
+  u32x4 kc[NKB];
+  uint32_t ksb[NKB], vc[NVI][4], vsb[NVI][4];
+  constexpr int CB = D / 2, SB = D / 32;
+  const size_t crow = static_cast<size_t>(a.Hkv) * CB, srow = static_cast<size_t>(a.Hkv) * SB;
+  const size_t cbatch = paged ? 0 : static_cast<size_t>(b) * a.L_max;
+  const uint8_t* kcb = reinterpret_cast<const uint8_t*>(a.k) + (cbatch * a.Hkv + hkv) * CB;
+  const uint8_t* vcb = reinterpret_cast<const uint8_t*>(a.v) + (cbatch * a.Hkv + hkv) * CB;
+  const uint8_t* ksp = FP4 ? a.k_scale + (cbatch * a.Hkv + hkv) * SB : nullptr;
+  const uint8_t* vsp = FP4 ? a.v_scale + (cbatch * a.Hkv + hkv) * SB : nullptr;
   auto load_tile = [&](int tk0) {
     const int key = tk0 + ln;
     // paged: one table read per lane (its K row); the V rows take theirs from the K lanes
     const int prow = paged ? (key < w_end ? pool_row(key) : 0) : key;
-    const uint16_t* kp = kbase + static_cast<size_t>(prow) * kv_row + 8 * lh;
+    if constexpr (FP4) {
+      const uint8_t* kp = kcb + static_cast<size_t>(prow) * crow + (D / 4) * lh;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      kreg[c] = u32x4{0u, 0u, 0u, 0u};
-      if (key < w_end) kreg[c] = ld16(kp + 16 * c);
+      for (int u = 0; u < NKB; ++u) {
+        kc[u] = u32x4{0u, 0u, 0u, 0u};
+        ksb[u] = 0u;
+        if (key < w_end) {
+          kc[u] = ld16(kp + 16 * u);
+          ksb[u] = ksp[static_cast<size_t>(prow) * srow + NKB * lh + u];
+        }
+      }
+    } else {
+      const uint16_t* kp = kbase + static_cast<size_t>(prow) * kv_row + 8 * lh;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        kreg[c] = u32x4{0u, 0u, 0u, 0u};
+        if (key < w_end) kreg[c] = ld16(kp + 16 * c);
+      }
     }
 #pragma unroll
     for (int it = 0; it < NVI; ++it) {
@@ -111,19 +150,28 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
       for (int s = 0; s < 4; ++s) {
         const int kk = tk0 + 4 * kg + s;
         const int vrow = paged ? __shfl(prow, 4 * kg + s, 64) : kk;
-        vreg[it][s] = u32x4{0u, 0u, 0u, 0u};
-        if (kk < w_end) vreg[it][s] = ld16(vbase + static_cast<size_t>(vrow) * kv_row + 8 * dg);
+        if constexpr (FP4) {
+          vc[it][s] = 0u;
+          vsb[it][s] = 0u;
+          if (kk < w_end) {
+            vc[it][s] = *reinterpret_cast<const uint32_t*>(vcb + static_cast<size_t>(vrow) * crow + 4 * dg);
+            vsb[it][s] = vsp[static_cast<size_t>(vrow) * srow + (dg >> 2)];
+          }
+        } else {
+          vreg[it][s] = u32x4{0u, 0u, 0u, 0u};
+          if (kk < w_end) vreg[it][s] = ld16(vbase + static_cast<size_t>(vrow) * kv_row + 8 * dg);
+        }
       }
     }
   };
 
   bf16x8 qf[NC];
   {
-    const uint16_t* qp = a.q + (static_cast<size_t>(b) * a.Hq + (col_live ? h : 0)) * D + 8 * lh;
+    const uint16_t* qp = a.q + (static_cast<size_t>(b) * a.Hq + (col_live ? h : 0)) * D + (FP4 ? (D / 2) * lh : 8 * lh);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (col_live) v = ld16(qp + 16 * c);
+      if (col_live) v = ld16(qp + (FP4 ? 8 * c : 16 * c));
       qf[c] = as_bf16x8(v);
     }
   }
@@ -216,8 +264,14 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
     f32x16 sacc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+    if constexpr (FP4) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) sacc = mfma32(as_bf16x8(kreg[c]), qf[c], sacc);
+      for (int c = 0; c < NC; ++c)
+        sacc = mfma32(as_bf16x8(fp4x8_to_bf16(kc[c / 4][c % 4], e8m0(ksb[c / 4]))), qf[c], sacc);
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sacc = mfma32(as_bf16x8(kreg[c]), qf[c], sacc);
+    }
     // V of this tile -> LDS, transposed (the previous tile's reads of this buffer are done)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -228,12 +282,18 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
       const int kg = item & 7;
       const int dg = item >> 3;
       const int pos = vt_pos(4 * kg);
+      u32x4 rows[4];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        if constexpr (FP4) rows[s4] = fp4x8_to_bf16(vc[it][s4], e8m0(vsb[it][s4]));
+        else rows[s4] = vreg[it][s4];
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int w = e >> 1;
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t p01 = __builtin_amdgcn_perm(vreg[it][1][w], vreg[it][0][w], sel);
-        const uint32_t p23 = __builtin_amdgcn_perm(vreg[it][3][w], vreg[it][2][w], sel);
+        const uint32_t p01 = __builtin_amdgcn_perm(rows[1][w], rows[0][w], sel);
+        const uint32_t p23 = __builtin_amdgcn_perm(rows[3][w], rows[2][w], sel);
         st8(vt + (8 * dg + e) * VST + pos, u32x2{p01, p23});
       }
     }
@@ -352,16 +412,6 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
 //     elements in the order the scores already sit in (element j of lane group g is row
 //     16 (j / 4) + 4 g + j % 4), so P is packed in place; V^T is stored in LDS with the rows
 //     permuted to that order, one 16-byte read per lane.
-// 8 MXFP4 codes (element 2j in the low nibble of byte j) times the block scale -> 8 bf16,
-// with the hardware FP4 conversion (v_cvt_scalef32_pk_bf16_fp4, one byte per instruction).
-__device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t codes, float sc) {
-  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3))};
-}
-// E8M0 scale byte -> 2^(byte - 127) as fp32 (byte 0, an all-zero block, reads as 0).
-__device__ __forceinline__ float e8m0(uint32_t byte) { return __uint_as_float(byte << 23); }
 
 // FP4: the caches hold MXFP4 codes (a.k / a.v: D / 2 bytes per row and kv head) and E8M0
 // block scales (a.k_scale / a.v_scale: D / 32 bytes); the tiles in flight are the packed bytes
@@ -743,10 +793,9 @@ hipError_t launch_d(DecodeArgs a, hipStream_t s) {
   const int total = curve_off + (MODE == 2 ? a.G * a.R * 4 : 0) + (MODE != 0 ? 4 * 2 * a.G * TK * 4 : 0);
   if (total > 160 * 1024) return hipErrorInvalidValue;
   // groups of up to 16 query heads: the 16x16 MFMA kernel (two tiles in flight per wave)
-  // (FP4 caches: the 16x16 kernel only; the C ABI rejects larger groups)
-  const bool narrow = FP4 || a.G <= 16;
+  const bool narrow = a.G <= 16;
   const void* fn = narrow ? reinterpret_cast<const void*>(&decode16_kernel<D, MODE, RMAX, FP4>)
-                          : reinterpret_cast<const void*>(&decode_bf16_kernel<D, MODE, RMAX>);
+                          : reinterpret_cast<const void*>(&decode_bf16_kernel<D, MODE, RMAX, FP4>);
   {
     const hipError_t e = set_max_lds(fn, total, s);
     if (e != hipSuccess) return e;
@@ -754,7 +803,7 @@ hipError_t launch_d(DecodeArgs a, hipStream_t s) {
   if (narrow)
     hipLaunchKernelGGL((decode16_kernel<D, MODE, RMAX, FP4>), grid, dim3(256), total, s, a, curve_off);
   else
-    hipLaunchKernelGGL((decode_bf16_kernel<D, MODE, RMAX>), grid, dim3(256), total, s, a, curve_off);
+    hipLaunchKernelGGL((decode_bf16_kernel<D, MODE, RMAX, FP4>), grid, dim3(256), total, s, a, curve_off);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(a.B * a.Hq), dim3(D), 0, s, a);

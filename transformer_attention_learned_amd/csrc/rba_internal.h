@@ -194,7 +194,7 @@ hipError_t launch_bwd_f32(const BwdF32Args& a, hipStream_t s);
 int bwd_lds_bytes(int D, int mode, int bias_range, int R);
 hipError_t launch_attn_f32(const F32Args& a, hipStream_t s);
 hipError_t launch_decode_bf16(DecodeArgs a, int D, int mode, hipStream_t s);
-// Decode over MXFP4 caches (D = 64 or 128, G <= 16) and the MXFP4 quantiser of bf16 rows
+// Decode over MXFP4 caches (D = 64 or 128, G <= 32) and the MXFP4 quantiser of bf16 rows
 // (nblk blocks of 32 elements: 16 code bytes and one scale byte each).
 hipError_t launch_decode_fp4(DecodeArgs a, int D, int mode, hipStream_t s);
 hipError_t launch_quantize_fp4(const uint16_t* x, uint8_t* codes, uint8_t* scales, long long nblk, hipStream_t s);
