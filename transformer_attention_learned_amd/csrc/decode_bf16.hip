@@ -53,6 +53,15 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t codes, float sc) {
 // E8M0 scale byte -> 2^(byte - 127) as fp32 (byte 0, an all-zero block, reads as 0).
 __device__ __forceinline__ float e8m0(uint32_t byte) { return __uint_as_float(byte << 23); }
 
+// V items of a tile: 4 cache rows (keys 4 kg .. + 3, kg = lane % 8) x 8 head dims (8 dg .. + 7).
+// Item it of lane l covers dims group dg: (l + 64 it) / 8 in general; with MXFP4 caches and two
+// items per lane, 2 (l / 8) + it, so that the lane's two items are adjacent dims of the same rows
+// (one 8-byte code load and one scale byte per row instead of two of each).
+template <bool FP4, int NVI>
+__device__ __forceinline__ int v_item_dg(int lane, int it) {
+  return (FP4 && NVI == 2) ? 2 * (lane >> 3) + it : (lane + 64 * it) >> 3;
+}
+
 // RMAX: r.E features held per curve item (8 or 16; 1 for the table).  FP4: MXFP4 caches (codes
 // and scales as in the 16x16 kernel below); a lane half's K fragments then cover head dims
 // (D / 2) lh + 8 c .. + 7, one or two 16-byte code loads and D / 64 scale bytes per row, and the
@@ -141,6 +150,25 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
         if (key < w_end) kreg[c] = ld16(kp + 16 * c);
       }
     }
+    if constexpr (FP4 && NVI == 2) {
+      // the lane's two V items are dims 16 (l / 8) .. + 15 of the same 4 rows: one 8-byte code
+      // load and one scale byte per row (both halves lie in one 32-dim scale block)
+      const int kg = lane & 7;
+      const int dg0 = v_item_dg<FP4, NVI>(lane, 0);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int kk = tk0 + 4 * kg + s;
+        const int vrow = paged ? __shfl(prow, 4 * kg + s, 64) : kk;
+        vc[0][s] = vc[1][s] = 0u;
+        vsb[0][s] = vsb[1][s] = 0u;
+        if (kk < w_end) {
+          const u32x2 w2 = ld8(vcb + static_cast<size_t>(vrow) * crow + 4 * dg0);
+          vc[0][s] = w2[0];
+          vc[1][s] = w2[1];
+          vsb[0][s] = vsb[1][s] = vsp[static_cast<size_t>(vrow) * srow + (dg0 >> 2)];
+        }
+      }
+    } else {
 #pragma unroll
     for (int it = 0; it < NVI; ++it) {
       const int item = lane + 64 * it;
@@ -162,6 +190,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
           if (kk < w_end) vreg[it][s] = ld16(vbase + static_cast<size_t>(vrow) * kv_row + 8 * dg);
         }
       }
+    }
     }
   };
 
@@ -278,9 +307,8 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int it = 0; it < NVI; ++it) {
-      const int item = lane + 64 * it;
-      const int kg = item & 7;
-      const int dg = item >> 3;
+      const int kg = lane & 7;
+      const int dg = v_item_dg<FP4, NVI>(lane, it);
       const int pos = vt_pos(4 * kg);
       u32x4 rows[4];
 #pragma unroll
@@ -504,6 +532,26 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
         }
       }
     }
+    if constexpr (FP4 && NVI == 2) {
+      // the lane's two V items are dims 16 (l / 8) .. + 15 of the same 4 rows: one 8-byte code
+      // load and one scale byte per row (both halves lie in one 32-dim scale block)
+      const int kg = lane & 7;
+      const int dg0 = v_item_dg<FP4, NVI>(lane, 0);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int kk = tk0 + 4 * kg + s4;
+        int vrow = kk;
+        if (paged) vrow = __shfl(prow32, 4 * kg + s4, 64);
+        vc[set][0][s4] = vc[set][1][s4] = 0u;
+        vsb[set][0][s4] = vsb[set][1][s4] = 0u;
+        if (kk < w_end) {
+          const u32x2 w2 = ld8(vcb + static_cast<size_t>(vrow) * crow + 4 * dg0);
+          vc[set][0][s4] = w2[0];
+          vc[set][1][s4] = w2[1];
+          vsb[set][0][s4] = vsb[set][1][s4] = vsp[static_cast<size_t>(vrow) * srow + (dg0 >> 2)];
+        }
+      }
+    } else {
 #pragma unroll
     for (int it = 0; it < NVI; ++it) {
       const int item = lane + 64 * it;
@@ -526,6 +574,7 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
           if (kk < w_end) vreg[set][it][s4] = ld16(vbase + static_cast<size_t>(vrow) * kv_row + 8 * dg);
         }
       }
+    }
     }
   };
 
@@ -636,9 +685,8 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int it = 0; it < NVI; ++it) {
-      const int item = lane + 64 * it;
-      const int kg = item & 7;
-      const int dg = item >> 3;
+      const int kg = lane & 7;
+      const int dg = v_item_dg<FP4, NVI>(lane, it);
       const int pos = vt_pos16(4 * kg);
       if constexpr (FP4) {
         u32x4 rows[4];
