@@ -24,6 +24,7 @@ from paged_pool import logical_rows, paginate
 pytestmark = pytest.mark.gpu
 
 BF16_MAX_ABS, BF16_REL_L2 = 2e-2, 5e-3
+BF16_LSE_MAX_ABS = 5e-3   # lse: the row sum of bf16-rounded probabilities, within 2^-8 of ln l
 
 
 def _say(msg):
@@ -101,7 +102,10 @@ def _check_decode(w: Workload, kv_len, batches=None):
         max_abs = float(np.abs(g - r).max())
         rel = float(np.linalg.norm(g - r) / np.linalg.norm(r))
         _say(f"    parity fp4 {name}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
-        assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, (name, max_abs, rel)
+        if name.endswith("lse"):
+            assert max_abs <= BF16_LSE_MAX_ABS, (name, max_abs)
+        else:
+            assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, (name, max_abs, rel)
 
 
 CASES = [
@@ -203,7 +207,10 @@ def _check_paged(w: Workload, lens, page_size):
         max_abs = float(np.abs(g - r).max())
         rel = float(np.linalg.norm(g - r) / np.linalg.norm(r))
         _say(f"    parity fp4 paged {name}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
-        assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, (name, max_abs, rel)
+        if name.endswith("lse"):
+            assert max_abs <= BF16_LSE_MAX_ABS, (name, max_abs)
+        else:
+            assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, (name, max_abs, rel)
 
 
 PAGED_CASES = [

@@ -21,6 +21,7 @@ from paged_pool import paginate
 pytestmark = pytest.mark.gpu
 
 BF16_MAX_ABS, BF16_REL_L2 = 2e-2, 5e-3
+BF16_LSE_MAX_ABS = 5e-3   # lse: the row sum of bf16-rounded probabilities, within 2^-8 of ln l
 
 
 def _say(msg):
@@ -69,7 +70,10 @@ def _check(w, lens, page_size, n_extra=3):
         max_abs = float(np.abs(g - r).max())
         rel = float(np.linalg.norm(g - r) / np.linalg.norm(r))
         _say(f"    parity paged {name}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
-        assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, (name, max_abs, rel)
+        if name.endswith("lse"):
+            assert max_abs <= BF16_LSE_MAX_ABS, (name, max_abs)
+        else:
+            assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, (name, max_abs, rel)
 
 
 def _w(**kw):

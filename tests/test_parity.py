@@ -22,6 +22,10 @@ from transformer_attention_learned_amd.workloads import WORKLOADS, Workload, mak
 pytestmark = pytest.mark.gpu
 
 BF16_MAX_ABS, BF16_REL_L2 = 2e-2, 5e-3
+# bf16 log-sum-exp: the row sum adds the bf16-rounded probabilities (each within the bf16 unit
+# roundoff 2^-8 = 3.9e-3 relative), so ln l is off by at most 3.9e-3 when one term dominates;
+# fp32 rounding and the bias's residual add under 1e-4
+BF16_LSE_MAX_ABS = 5e-3
 F32_TOL = 1e-5
 
 
@@ -58,18 +62,19 @@ def assert_parity(got, ref, dtype, what=""):
 
 
 def assert_lse(got, ref, dtype, what=""):
-    """The log-sum-exp is held to the same bar as the output.
+    """The log-sum-exp, in natural log units, to an absolute bar (its values are about 6, so a
+    relative L2 bar would say little).
 
-    On the bf16 path the row sum adds the bf16-rounded probabilities (the same
-    ones the P.V product uses), so lse carries errors of order 2^-9 (about 2e-3
-    in natural log units).
+    On the bf16 path the row sum adds the bf16-rounded probabilities (the same ones the P.V
+    product uses), each within 2^-8 relative, so lse is off by at most about 3.9e-3; the bar is
+    BF16_LSE_MAX_ABS = 5e-3.  fp32: F32_TOL.
     """
     max_abs, rel = _errs(got, ref)
     _say(f"    lse {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
     if dtype == "f32":
         assert max_abs <= F32_TOL, (what, max_abs)
     else:
-        assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, (what, max_abs, rel)
+        assert max_abs <= BF16_LSE_MAX_ABS, (what, max_abs)
 
 
 def _t2np(t):
