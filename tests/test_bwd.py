@@ -148,6 +148,11 @@ SWEEP = [
     dict(S=400, mode="rproj_shared", R=5, bias_range=77, D=64),
     dict(S=1000, temp_len=100), dict(S=333, mode="table", bias_range=100, temp_len=2),
     dict(S=600, window=300, temp_len=64, mode="rproj_shared", R=8),
+    # table mode with GQA groups of several heads (the dk/dv kernel stages each head's row as
+    # its walk reaches it), with a window and a temperature, and with 4,200 distances
+    dict(S=333, mode="table", bias_range=100, Hq=8, Hkv=2),
+    dict(S=500, mode="table", window=200, bias_range=150, Hq=4, Hkv=1, temp_len=64),
+    dict(S=300, mode="table", bias_range=4200, Hq=8, Hkv=1, D=64),
 ]
 
 

@@ -148,19 +148,34 @@ typedef __attribute__((address_space(3))) float lds_float;
 
 // r fragment (B operand) of query row `row`: EW = 16: features 0..7 in both lane halves;
 // EW = 32: features 8 lh .. 8 lh + 7; zero past R and for rows at or past S.
+// Split into the loads (unconditional, inside the row: the feature index is clamped, so that no
+// load sits in a branch of its own and is waited for before the next one is issued) and the
+// packing, which masks the features past R and rows at or past S.
 template <int EW>
-__device__ __forceinline__ bf16x8 r_frag(const BwdArgs& a, int b, int h, int row, int lh) {
+__device__ __forceinline__ void r_load(const BwdArgs& a, int b, int h, int row, int lh, uint32_t (&x)[8]) {
+  const int f0 = (EW == 32) ? 8 * lh : 0;
+  const uint16_t* rp = a.r + ((static_cast<size_t>(b) * a.S + (row < a.S ? row : 0)) * a.Hq + h) * a.R;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = rp[min(f0 + e, a.R - 1)];
+}
+template <int EW>
+__device__ __forceinline__ bf16x8 r_pack(const BwdArgs& a, int row, int lh, const uint32_t (&x)[8]) {
   const int f0 = (EW == 32) ? 8 * lh : 0;
   uint32_t w[4];
-  const uint16_t* rp = a.r + ((static_cast<size_t>(b) * a.S + (row < a.S ? row : 0)) * a.Hq + h) * a.R;
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const int f = f0 + 2 * jj;
-    const uint32_t lo = (row < a.S && f < a.R) ? rp[f] : 0u;
-    const uint32_t hi = (row < a.S && f + 1 < a.R) ? rp[f + 1] : 0u;
+    const uint32_t lo = (row < a.S && f < a.R) ? x[2 * jj] : 0u;
+    const uint32_t hi = (row < a.S && f + 1 < a.R) ? x[2 * jj + 1] : 0u;
     w[jj] = lo | (hi << 16);
   }
   return as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+}
+template <int EW>
+__device__ __forceinline__ bf16x8 r_frag(const BwdArgs& a, int b, int h, int row, int lh) {
+  uint32_t x[8];
+  r_load<EW>(a, b, h, row, lh, x);
+  return r_pack<EW>(a, row, lh, x);
 }
 
 // E rows of a block whose distances are c - 31 + l (block 0) and c + 1 + l (block 1) for the
@@ -610,30 +625,73 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
 }
 
 // ---- dk, dv: key-parallel ------------------------------------------------------------------------
+// One workgroup = 4 waves x 32 keys of one kv head, walking (query head of the group, 32-row query
+// tile) steps, head-major.  The forward's structure with the roles of queries and keys swapped:
+// K and V stay in registers as B operands, and each step's q and dout rows go straight from
+// global memory into a 3-slot LDS ring (16-byte chunks, swizzled so that both the row reads of
+// the score products and the transposing reads of the gradient products are free of bank
+// conflicts), with the step's per-row values (lse, rowsum, temperature) beside them, two steps
+// ahead.  Per step a wave turns the scores S = Q K^T and dP = dO V^T it formed at the end of the
+// previous step into P and dZ, accumulates dV^T += dO^T P and dK^T += Q^T dZ, and forms the next
+// step's scores; one barrier per step.
+constexpr int KV_ROWS = 32;   // query rows per step
+constexpr int KV_NBUF = 3;    // ring slots
+
 template <int D>
 struct DkvLayout {
-  static constexpr int TILES = (2 * BN * (D + 8) + 2 * D * (BN + 8)) * 2 + 4 * BN * 4;
-  // table mode: the head's table row; r.E: a curve buffer per wave
+  static constexpr int ROW_B = 2 * D;                  // bytes per tile row
+  static constexpr int TILE_B = KV_ROWS * ROW_B;       // q or dout tile
+  static constexpr int REC_B = 4 * KV_ROWS * 4;        // per-row lse2, rowsum, c_qk tau, tau
+  static constexpr int SLOT_B = 2 * TILE_B + REC_B;
+  static constexpr int RING_B = KV_NBUF * SLOT_B;
+  // table mode: two head slots of the zero-padded table row; r.E: a curve buffer per wave
   static int bytes(int mode, int Rb) {
-    return TILES + (mode == 1 ? (Rb + 2 * PADT) * 4 : 0) + (mode == 2 ? DKV_WAVES * CURVE_BYTES_KV : 0);
+    return RING_B + (mode == 1 ? 2 * (Rb + 2 * PADT) * 4 : 0) + (mode == 2 ? DKV_WAVES * CURVE_BYTES_KV : 0);
   }
 };
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at dst + 16 l
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
+}
+// LDS transpose read: within each group of 16 lanes, lane i receives 16-bit element i % 4 of the
+// 8-byte pieces addressed by lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4
+__device__ __forceinline__ u32x2 tr_read(const void* p) {
+  const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+  return __builtin_bit_cast(u32x2, x);
+}
+
+// XOR applied to the 16-byte chunk index of tile row r.  Row reads (16 lanes, rows r .. r + 15
+// at one logical chunk) need distinct values over any 16 consecutive rows; a transposing read
+// (16 lanes, 4 rows x 32 bytes: rows 4 k .. 4 k + 3, logical chunks 2 m, 2 m + 1) needs the four
+// rows' values to differ above bit 0.  D = 128 (256-byte rows, one row spans the 64 banks): row
+// bits 0-1 to chunk bits 2-3, bits 2-3 to bits 0-1.  D = 64 (128-byte rows, two rows per bank
+// line, row bit 0 selecting the half): row bit 1 to chunk bit 2, bits 2-3 to bits 0-1.
+template <int D>
+__device__ __forceinline__ int tile_sw(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
 
 template <int D, int MODE, int EW>
 __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using L = DkvLayout<D>;
-  constexpr int QST = D + 8;
-  constexpr int TST = BN + 8;
   constexpr int NC = D / 16;
   constexpr int NDB = D / 32;
   constexpr int NT = 64 * DKV_WAVES;
+  constexpr int ROW_B = L::ROW_B;
+  constexpr int TILE_B = L::TILE_B;
+  constexpr int SLOT_B = L::SLOT_B;
+  constexpr int CPR = ROW_B / 16;                     // chunks per row
+  constexpr int RPI = 64 / CPR;                       // rows per direct-load instruction
+  constexpr int NIT = KV_ROWS / RPI / DKV_WAVES;      // instructions per wave and tile
+  static_assert(NIT >= 1 && NIT * RPI * DKV_WAVES == KV_ROWS, "tile rows split evenly over the waves");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* Qs = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* dOs = Qs + BN * QST;
-  uint16_t* Qt = dOs + BN * QST;
-  uint16_t* dOt = Qt + D * TST;
-  float* rowp = reinterpret_cast<float*>(dOt + D * TST);   // [4][BN]: lse2, rowsum, c_qk*tau, tau
-  float* tabs = reinterpret_cast<float*>(smem + L::TILES);  // table mode: [PADT + Rb + PADT]
+  const int Rb = a.bias_range;
+  const int TROW = Rb + 2 * PADT;
+  float* tabs = reinterpret_cast<float*>(smem + L::RING_B);   // table mode: 2 x [PADT + Rb + PADT]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -649,14 +707,16 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
 
   const int S = a.S;
   const int W = a.window;
-  const int Rb = a.bias_range;
+  const int G = a.G;
   const int j_lo = kt * (32 * DKV_WAVES);
   const int j0w = j_lo + 32 * wave;
   const bool wave_live = j0w < S;
   const int key = j0w + ln;
   const bool key_ok = key < S;
+  const float inv_scale = 1.f / a.scale;   // bias in units of the raw score q.k
 
   const size_t q_row = static_cast<size_t>(a.Hq) * D;
+  const int q_row_b = a.Hq * D * 2;
   const size_t kv_row = static_cast<size_t>(a.Hkv) * D;
   const size_t koff = (static_cast<size_t>(b) * S + (key_ok ? key : 0)) * kv_row + static_cast<size_t>(hkv) * D;
 
@@ -664,7 +724,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   // of the row are written); key n reads row m at t = 31 + m - n, which for element i (query
   // m = 8 g + 4 lh + k) is 320 g + 41 k + 160 lh + 31 - n: one base register per lane and
   // immediate offsets, and each half-wave reads 32 consecutive dwords of one row
-  float* cbuf = (MODE == 2) ? reinterpret_cast<float*>(smem + L::TILES) + wave * (CURVE_BYTES_KV / 4) : nullptr;
+  float* cbuf = (MODE == 2) ? reinterpret_cast<float*>(smem + L::RING_B) + wave * (CURVE_BYTES_KV / 4) : nullptr;
   const lds_float* crd = nullptr;
   if (MODE == 2) {
     crd = (const lds_float*)(cbuf + 160 * lh + 31 - ln);
@@ -690,190 +750,292 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
     dvacc[db] = zero16();
   }
 
+  // steps: (query head hh of the group, query tile t_begin + t), t < ntiles
   const int last_key = min(S, j_lo + 32 * DKV_WAVES) - 1;
   const int i_last = W ? min(S - 1, last_key + W - 1) : S - 1;
-  const int t_begin = j_lo / BN;
-  const int t_end = i_last / BN;
+  const int t_begin = j_lo / KV_ROWS;
+  const int ntiles = i_last / KV_ROWS - t_begin + 1;
+  const int nsteps = G * ntiles;
+  // the wave's tiles within a head: from the tile of its first key to that of its keys' last
+  // visible query row
+  const int w_lo = wave;
+  const int w_hi = (W ? min(S - 1, j0w + 31 + W - 1) : S - 1) / KV_ROWS - t_begin;
 
-  // (head, query tile) steps in one sequence, so the next step's Q / dO rows and per-row
-  // values are loaded into registers while the current step is used
-  const int ntiles = t_end - t_begin + 1;
-  const int nsteps = ntiles > 0 ? a.G * ntiles : 0;
-  constexpr int QIT = (row_items<D>() + NT - 1) / NT;
-  u32x4 qpre[QIT][4], dpre[QIT][4];
-  float lpre = 0.f, spre = 0.f, tpre = 1.f;
-  auto load_step = [&](int st) {
-    const int h = hkv * a.G + st / ntiles;
-    const int qt0 = (t_begin + st % ntiles) * BN;
-    load_rows<D, QIT>(a.q + static_cast<size_t>(b) * S * q_row + static_cast<size_t>(h) * D, q_row, qt0, S,
-                      qpre, tid, NT);
-    load_rows<D, QIT>(a.dout + static_cast<size_t>(b) * S * q_row + static_cast<size_t>(h) * D, q_row, qt0, S,
-                      dpre, tid, NT);
-    if (tid < BN) {
-      const int rr = qt0 + tid;
-      const bool ok = rr < S;
-      const size_t lrow = (static_cast<size_t>(b) * a.Hq + h) * S + (ok ? rr : 0);
-      lpre = ok ? a.lse[lrow] * kLog2e : INFINITY;
-      spre = ok ? a.dsum[lrow] : 0.f;
-      tpre = temp_factor(visible_keys(rr, W), a.temp_len, a.temp_inv_log2);
+  auto step_head = [&](int js) { return js / ntiles; };
+  auto step_row0 = [&](int js) { return (t_begin + js - (js / ntiles) * ntiles) * KV_ROWS; };
+  auto step_on = [&](int js) {
+    const int t = js - (js / ntiles) * ntiles;
+    return wave_live && js < nsteps && t >= w_lo && t <= w_hi;
+  };
+  // element (query m, key n) of a step lies at distance c + m - n, c = its first row - j0w
+  auto step_inband = [&](int js) { return MODE != 0 && step_row0(js) - j0w - 31 < a.bias_range; };
+  auto step_edge = [&](int js) {
+    const int i0 = step_row0(js);
+    const int c = i0 - j0w;
+    return (c - 31 < 0) || (W && c + 31 >= W) || (i0 + KV_ROWS > S);
+  };
+
+  // direct loads: instruction k of this wave fills rows RPI (NIT wave + k) .. + RPI - 1
+  int voff[NIT];
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int r = RPI * (NIT * wave + k) + lane / CPR;
+    voff[k] = r * q_row_b + 16 * ((lane % CPR) ^ tile_sw<D>(r));
+  }
+  auto dma_tile = [&](int js, unsigned char* slot) __attribute__((always_inline)) {
+    const int h = hkv * G + step_head(js);
+    const int i0 = step_row0(js);
+    const int rows = min(S - i0, KV_ROWS);
+    const int nrec = (rows - 1) * q_row_b + ROW_B;   // rows past S read as zeros
+    const size_t off = (static_cast<size_t>(b) * S + i0) * q_row + static_cast<size_t>(h) * D;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + off, nrec);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dout + off, nrec);
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+      dma16(rq, slot + (NIT * wave + k) * 1024, voff[k]);
+      dma16(rd, slot + TILE_B + (NIT * wave + k) * 1024, voff[k]);
     }
   };
-  if (nsteps > 0) load_step(0);
-
-  for (int st = 0; st < nsteps; ++st) {
-    const int hh = st / ntiles;
-    const int h = hkv * a.G + hh;
-    const int qt0 = (t_begin + st % ntiles) * BN;
-    __syncthreads();   // the previous step's LDS reads are complete
-    store_rows<D, QIT>(qpre, Qs, Qt, tid, NT);
-    store_rows<D, QIT>(dpre, dOs, dOt, tid, NT);
-    if (tid < BN) {
-      rowp[tid] = lpre;
-      rowp[BN + tid] = spre;
-      rowp[2 * BN + tid] = a.c_qk * tpre;
-      rowp[3 * BN + tid] = tpre;
-    }
-    if (MODE == 1 && st % ntiles == 0) {   // a new head: its table row, zero-padded
-      const float* tp = a.table + static_cast<size_t>(h) * Rb;
-      for (int x = tid; x < Rb + 2 * PADT; x += NT) {
-        const int d = x - PADT;
-        tabs[x] = (d >= 0 && d < Rb) ? tp[d] * kLog2e : 0.f;
+  // per-row values of a step, through lanes 0..31 of wave 0: loaded a step ahead and used only
+  // when stored after the next barrier (so that no wait for them stalls the step); rows past S
+  // get lse = +inf (P = 0)
+  float rec_l = INFINITY, rec_s = 0.f;
+  int rec_row = 0;
+  auto rec_load = [&](int js) __attribute__((always_inline)) {
+    if (wave == 0 && lh == 0) {
+      const int h = hkv * G + step_head(js);
+      rec_row = step_row0(js) + ln;
+      rec_l = INFINITY;
+      rec_s = 0.f;
+      if (rec_row < S) {
+        const size_t lrow = (static_cast<size_t>(b) * a.Hq + h) * S + rec_row;
+        rec_l = a.lse[lrow];
+        rec_s = a.dsum[lrow];
       }
     }
-    __syncthreads();
-    if (st + 1 < nsteps) load_step(st + 1);
-    if (!wave_live) continue;
-    // r.E: the head's converted E rows at distance 0
-    const uint16_t* e2h = (MODE == 2)
-        ? a.e2 + (static_cast<size_t>(a.e_hs ? h : 0) * (Rb + 2 * kE2Pad + 1) + kE2Pad) * EW
-        : nullptr;
+  };
+  auto rec_store = [&](unsigned char* slot) __attribute__((always_inline)) {
+    if (wave == 0 && lh == 0) {
+      float* rp = reinterpret_cast<float*>(slot + 2 * TILE_B);
+      const float tq = temp_factor(visible_keys(rec_row, W), a.temp_len, a.temp_inv_log2);
+      rp[ln] = rec_l * kLog2e;
+      rp[KV_ROWS + ln] = rec_s;
+      rp[2 * KV_ROWS + ln] = a.c_qk * tq;
+      rp[3 * KV_ROWS + ln] = tq;
+    }
+  };
+  // table mode: head hh's row (in units of the raw score), zero-padded, into slot hh % 2
+  auto stage_table = [&](int hh) __attribute__((always_inline)) {
+    float* tab = tabs + (hh & 1) * TROW;
+    const float* tp = a.table + static_cast<size_t>(hkv * G + hh) * Rb;
+    for (int x = tid; x < TROW; x += NT) {
+      const int d = x - PADT;
+      tab[x] = (d >= 0 && d < Rb) ? tp[d] * inv_scale : 0.f;
+    }
+  };
 
-#pragma unroll 1
-    for (int qb = 0; qb < 2; ++qb) {
-      const int i0b = qt0 + 32 * qb;
-      const int c = i0b - j0w;                  // delta = c + m - n
-      bool on = (c + 31 >= 0) && (i0b < S);
-      if (W) on = on && (c - 31 < W);
-      if (!on) continue;
-      const bool inband = (MODE != 0) && (c - 31 < Rb);
+  // fragment addresses within a slot: rows of the score products (A = q or dout rows, lane ln
+  // reads row ln, chunk 2 c + lh) and the transposing reads of the gradient products (A = q^T
+  // or dout^T: lane (ln = head-dim row, lh) gets queries 4 lh .. 4 lh + 3 from its "lo" read
+  // and 8 + the same from its "hi" read, 16 more queries at + 16 rows)
+  int qaddr[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) qaddr[c] = ln * ROW_B + 16 * ((2 * c + lh) ^ tile_sw<D>(ln));
+  int taddr[2][NDB];
+  {
+    const int t16 = lane & 15, j = t16 >> 2, q = t16 & 3, gq = (lane >> 4) & 1;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int r = 4 * lh + j + 8 * x;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        taddr[x][db] = r * ROW_B + 16 * ((4 * db + 2 * gq + (q >> 1)) ^ tile_sw<D>(r)) + 8 * (q & 1);
+    }
+  }
+  auto t_frag = [&](const unsigned char* base, int db, int kk) __attribute__((always_inline)) -> bf16x8 {
+    const u32x2 lo = tr_read(base + taddr[0][db] + 16 * ROW_B * kk);
+    const u32x2 hi = tr_read(base + taddr[1][db] + 16 * ROW_B * kk);
+    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+  };
 
-      // r.E bias of element (query m, key ln) at distance c + m - ln: the block's E rows and r
-      // of its query rows (B operand column ln = query i0b + ln), requested before the score
-      // MFMAs
-      u32x4 eb[2][EW / 16];
-      bf16x8 rq = {};
-      if (MODE == 2 && inband) {
-        e_rows<EW>(e2h, c, ln, lh, eb);
-        rq = r_frag<EW>(a, b, h, i0b + ln, lh);
-      }
+  const uint16_t* e2b = (MODE == 2) ? a.e2 + kE2Pad * EW : nullptr;
+  auto e_load = [&](int js, u32x4 (&eb)[2][EW / 16], uint32_t (&rx)[8]) __attribute__((always_inline)) {
+    const int h = hkv * G + step_head(js);
+    const int i0 = step_row0(js);
+    e_rows<EW>(e2b + static_cast<size_t>(a.e_hs ? h : 0) * (Rb + 2 * kE2Pad + 1) * EW, i0 - j0w, ln, lh, eb);
+    r_load<EW>(a, b, h, i0 + ln, lh, rx);
+  };
 
-      // operands read one step ahead of the MFMAs that use them
-      f32x16 sacc = zero16(), pacc = zero16();
-      const uint16_t* qr = Qs + (32 * qb + ln) * QST + 8 * lh;
-      const uint16_t* dr_ = dOs + (32 * qb + ln) * QST + 8 * lh;
-      bf16x8 qa = as_bf16x8(ld16(qr)), da = as_bf16x8(ld16(dr_));
+  // S (plus the bias, in units of q.k) and dP of a step
+  auto scores = [&](int js, const unsigned char* slot, f32x16& sacc, f32x16& pacc, const u32x4 (&eb)[2][EW / 16],
+                    const uint32_t (&rx)[8]) __attribute__((always_inline)) {
+    const int c = step_row0(js) - j0w;
+    const bool ib = step_inband(js);
+    sacc = zero16();
+    pacc = zero16();
+    if (MODE == 1 && ib) {
+      // distances c + m - ln lie in [-31, Rb + 62]: inside the zero-padded row
+      const float* tb = tabs + (step_head(js) & 1) * TROW + PADT + c - ln;
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        bf16x8 qn = qa, dn = da;
-        if (cc + 1 < NC) {
-          qn = as_bf16x8(ld16(qr + 16 * (cc + 1)));
-          dn = as_bf16x8(ld16(dr_ + 16 * (cc + 1)));
-        }
-        sacc = mfma32(qa, kf[cc], sacc);
-        pacc = mfma32(da, vf[cc], pacc);
-        qa = qn;
-        da = dn;
+      for (int i = 0; i < 16; ++i) sacc[i] = tb[out_row(i, lh)];
+    }
+    bf16x8 qa = as_bf16x8(ld16(slot + qaddr[0])), da = as_bf16x8(ld16(slot + TILE_B + qaddr[0]));
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      bf16x8 qn = qa, dn = da;
+      if (cc + 1 < NC) {
+        qn = as_bf16x8(ld16(slot + qaddr[cc + 1]));
+        dn = as_bf16x8(ld16(slot + TILE_B + qaddr[cc + 1]));
       }
-      // bias (log2 units) per element, before the temperature
-      float bias[16];
+      sacc = mfma32(qa, kf[cc], sacc);
+      pacc = mfma32(da, vf[cc], pacc);
+      qa = qn;
+      da = dn;
+    }
+    if (MODE == 2 && ib) {
+      f32x16 clo, chi;
+      curve_mfma<EW>(eb, r_pack<EW>(a, step_row0(js) + ln, lh, rx), clo, chi);
+      curve_write(cbuf + CURVE_ROWS_KV * ln, ln, lh, clo, chi);
+      wave_sync_lds();
 #pragma unroll
-      for (int i = 0; i < 16; ++i) bias[i] = 0.f;
-      if (MODE == 1 && inband) {
-        // distances c + m - ln lie in [-31, Rb + 62]: inside the zero-padded row
-        const float* tb = tabs + PADT + c - ln;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) bias[i] = tb[out_row(i, lh)];
-      }
-      if (MODE == 2 && inband) {
-        f32x16 clo, chi;
-        curve_mfma<EW>(eb, rq, clo, chi);
-        curve_write(cbuf + CURVE_ROWS_KV * ln, ln, lh, clo, chi);
-        wave_sync_lds();
-#pragma unroll
-        for (int i = 0; i < 16; ++i) bias[i] = crd[320 * (i >> 2) + 41 * (i & 3)] * kLog2e;
-        wave_sync_lds();   // the next block's writes follow these reads
-      }
-      // P into sacc, dZ = tau * P * (dP - rowsum) into pacc (in place); per row: lse (log2
-      // units), rowsum, c_qk * tau and tau (tau = 1 without a temperature).  Interior and
-      // edge blocks get separate loops so that no branch sits inside the element loop.
-      const bool edge = (c - 31 < 0) || (W && c + 31 >= W);
+      for (int i = 0; i < 16; ++i) sacc[i] = fmaf(crd[320 * (i >> 2) + 41 * (i & 3)], inv_scale, sacc[i]);
+      wave_sync_lds();   // the next step's writes follow these reads
+    }
+  };
+  // P and dZ = tau * P * (dP - rowsum), rounded to bf16 as the B operands of the gradient
+  // products; per row: lse (log2 units), rowsum, c_qk * tau, tau.  Interior and edge steps get
+  // separate loops so that no branch sits inside the element loop.
+  auto probs = [&](int js, const unsigned char* slot, f32x16& sacc, f32x16& pacc, bf16x8 (&pf)[2],
+                   bf16x8 (&dzf)[2]) __attribute__((always_inline)) {
+    const float* rp = reinterpret_cast<const float*>(slot + 2 * TILE_B);
+    if (step_edge(js)) {
+      const int i0 = step_row0(js);
+      const int c = i0 - j0w;
       const int wlim = W ? W : 0x7fffffff;
-      if (edge) {
+      const int mlim = S - i0;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int m0 = 32 * qb + 8 * g4 + 4 * lh;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(rowp + m0);
-          const f32x4 s4 = *reinterpret_cast<const f32x4*>(rowp + BN + m0);
-          const f32x4 c4 = *reinterpret_cast<const f32x4*>(rowp + 2 * BN + m0);
-          const f32x4 t4 = *reinterpret_cast<const f32x4*>(rowp + 3 * BN + m0);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int m0 = 8 * g4 + 4 * lh;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(rp + m0);
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(rp + KV_ROWS + m0);
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(rp + 2 * KV_ROWS + m0);
+        const f32x4 t4 = *reinterpret_cast<const f32x4*>(rp + 3 * KV_ROWS + m0);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int i = 4 * g4 + u;
-            const int d = c + out_row(i, lh) - ln;
-            const float p = fast_exp2(fmaf(bias[i], t4[u], fmaf(sacc[i], c4[u], -l4[u])));
-            const float pm = ((d >= 0) & (d < wlim)) ? p : 0.f;
-            pacc[i] = pm * (pacc[i] - s4[u]) * t4[u];
-            sacc[i] = pm;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int m0 = 32 * qb + 8 * g4 + 4 * lh;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(rowp + m0);
-          const f32x4 s4 = *reinterpret_cast<const f32x4*>(rowp + BN + m0);
-          const f32x4 c4 = *reinterpret_cast<const f32x4*>(rowp + 2 * BN + m0);
-          const f32x4 t4 = *reinterpret_cast<const f32x4*>(rowp + 3 * BN + m0);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int i = 4 * g4 + u;
-            const float p = fast_exp2(fmaf(bias[i], t4[u], fmaf(sacc[i], c4[u], -l4[u])));
-            pacc[i] = p * (pacc[i] - s4[u]) * t4[u];
-            sacc[i] = p;
-          }
+        for (int u = 0; u < 4; ++u) {
+          const int i = 4 * g4 + u;
+          const int d = c + m0 + u - ln;
+          const float p = fast_exp2(fmaf(sacc[i], c4[u], -l4[u]));
+          const float pm = ((d >= 0) & (d < wlim) & (m0 + u < mlim)) ? p : 0.f;
+          pacc[i] = pm * (pacc[i] - s4[u]) * t4[u];
+          sacc[i] = pm;
         }
       }
-      bf16x8 pf[2], dzf[2];
+    } else {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        uint32_t w[4], x[4];
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int m0 = 8 * g4 + 4 * lh;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(rp + m0);
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(rp + KV_ROWS + m0);
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(rp + 2 * KV_ROWS + m0);
+        const f32x4 t4 = *reinterpret_cast<const f32x4*>(rp + 3 * KV_ROWS + m0);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          w[jj] = pack_bf16x2(sacc[8 * kk + 2 * jj], sacc[8 * kk + 2 * jj + 1]);
-          x[jj] = pack_bf16x2(pacc[8 * kk + 2 * jj], pacc[8 * kk + 2 * jj + 1]);
-        }
-        pf[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
-        dzf[kk] = as_bf16x8(u32x4{x[0], x[1], x[2], x[3]});
-      }
-      // dV^T += dO^T P,  dK^T += Q^T dZ
-      {
-        const int off0 = ln * TST + 32 * qb + 8 * lh;
-        bf16x8 oa = as_bf16x8(ld16(dOt + off0)), qt = as_bf16x8(ld16(Qt + off0));
-#pragma unroll
-        for (int x = 0; x < 2 * NDB; ++x) {
-          bf16x8 on = oa, qn = qt;
-          if (x + 1 < 2 * NDB) {
-            const int off = off0 + 32 * ((x + 1) >> 1) * TST + 16 * ((x + 1) & 1);
-            on = as_bf16x8(ld16(dOt + off));
-            qn = as_bf16x8(ld16(Qt + off));
-          }
-          dvacc[x >> 1] = mfma32(oa, pf[x & 1], dvacc[x >> 1]);
-          dkacc[x >> 1] = mfma32(qt, dzf[x & 1], dkacc[x >> 1]);
-          oa = on;
-          qt = qn;
+        for (int u = 0; u < 4; ++u) {
+          const int i = 4 * g4 + u;
+          const float p = fast_exp2(fmaf(sacc[i], c4[u], -l4[u]));
+          pacc[i] = p * (pacc[i] - s4[u]) * t4[u];
+          sacc[i] = p;
         }
       }
     }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      uint32_t w[4], x[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        w[jj] = pack_bf16x2(sacc[8 * kk + 2 * jj], sacc[8 * kk + 2 * jj + 1]);
+        x[jj] = pack_bf16x2(pacc[8 * kk + 2 * jj], pacc[8 * kk + 2 * jj + 1]);
+      }
+      pf[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+      dzf[kk] = as_bf16x8(u32x4{x[0], x[1], x[2], x[3]});
+    }
+  };
+  // dV^T += dO^T P,  dK^T += Q^T dZ
+  auto grads = [&](const unsigned char* slot, const bf16x8 (&pf)[2],
+                   const bf16x8 (&dzf)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < 2 * NDB; ++x) {
+      const bf16x8 oa = t_frag(slot + TILE_B, x >> 1, x & 1);
+      const bf16x8 qt = t_frag(slot, x >> 1, x & 1);
+      dvacc[x >> 1] = mfma32(oa, pf[x & 1], dvacc[x >> 1]);
+      dkacc[x >> 1] = mfma32(qt, dzf[x & 1], dkacc[x >> 1]);
+    }
+  };
+
+  // prologue: the first two steps' tiles and row values, the first step's scores
+  if (MODE == 1) {
+    stage_table(0);
+    if (ntiles == 1 && G > 1) stage_table(1);
+  }
+  rec_load(0);
+  dma_tile(0, smem);
+  if (nsteps > 1) dma_tile(1, smem + SLOT_B);
+  rec_store(smem);
+  if (nsteps > 1) rec_load(1);
+  u32x4 eb[2][EW / 16];
+  uint32_t rx[8];
+  if (MODE == 2 && step_on(0) && step_inband(0)) e_load(0, eb, rx);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's direct loads have landed
+  __syncthreads();
+  f32x16 sa, pa;
+  if (step_on(0)) scores(0, smem, sa, pa, eb, rx);
+
+  // step js: P, dZ and the gradient products of js (its row values and tiles in slot js % 3), then
+  // the scores of js + 1 (slot (js + 1) % 3) into the same registers; the tiles of js + 2 go to
+  // the slot js - 1 used.  The slots are passed as restrict pointers: the compiler then knows
+  // that the direct loads into ds do not alias the reads of cs and ns and adds no wait for them.
+  auto iteration_body = [&](int js, const unsigned char* __restrict__ cs, unsigned char* __restrict__ ns,
+                            unsigned char* __restrict__ ds, auto inner_c) __attribute__((always_inline)) {
+    constexpr bool INNER = decltype(inner_c)::value;   // js + 2 < nsteps is known
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    rec_store(ns);
+    u32x4 e[2][EW / 16];
+    uint32_t x[8];
+    if (MODE == 2 && step_on(js + 1) && step_inband(js + 1)) e_load(js + 1, e, x);
+    if (MODE == 1 && (INNER || js + 2 < nsteps) && (js + 2) % ntiles == 0) stage_table((js + 2) / ntiles);
+    // the bias operands are requested before the tiles of js + 2, so that the waits for them
+    // (vector-memory counts retire in order) do not wait for the tiles
+    __builtin_amdgcn_sched_barrier(0);
+    if (INNER || js + 2 < nsteps) {
+      dma_tile(js + 2, ds);
+      rec_load(js + 2);
+    }
+    if (step_on(js)) {
+      bf16x8 pf[2], dzf[2];
+      probs(js, cs, sa, pa, pf, dzf);
+      grads(cs, pf, dzf);
+    }
+    if (step_on(js + 1)) scores(js + 1, ns, sa, pa, e, x);
+  };
+  using true_t = std::integral_constant<bool, true>;
+  using false_t = std::integral_constant<bool, false>;
+  auto iteration = [&](int js, int sl, auto inner_c) __attribute__((always_inline)) {
+    iteration_body(js, smem + sl * SLOT_B, smem + ((sl + 1) % KV_NBUF) * SLOT_B, smem + ((sl + 2) % KV_NBUF) * SLOT_B,
+                   inner_c);
+  };
+  int js = 0;
+  for (; js + 4 < nsteps; js += 3) {
+    iteration(js, 0, true_t{});
+    iteration(js + 1, 1, true_t{});
+    iteration(js + 2, 2, true_t{});
+  }
+  for (; js + 1 < nsteps; ++js) iteration(js, js % KV_NBUF, false_t{});
+  if (nsteps > 1) __syncthreads();   // the last step's row values, stored after the previous barrier
+  if (step_on(js)) {
+    const unsigned char* cs = smem + (js % KV_NBUF) * SLOT_B;
+    bf16x8 pf[2], dzf[2];
+    probs(js, cs, sa, pa, pf, dzf);
+    grads(cs, pf, dzf);
   }
 
   if (!wave_live || !key_ok) return;
