@@ -51,19 +51,12 @@ namespace rba {
 
 namespace {
 
-constexpr int BN = 64;        // keys per tile (dq kernel), query rows per tile (dk/dv kernel)
 constexpr int PADT = 64;      // zero distances staged on each side of a table row
 constexpr int PADE = 64;      // zero distances staged on each side of E
 constexpr int GST = 64 + 8;   // G row stride (bf16): row = query, 64 distances
 constexpr int GTS = 32 + 8;   // G^T row stride (bf16): row = distance, 32 queries
 constexpr int DQ_WAVES = 4;
 constexpr int DKV_WAVES = 4;
-
-// Position of key (or query) x of a 64-row tile inside a transposed LDS row: bits 2 and 3
-// swapped, so the 8 rows one lane half feeds to an MFMA over 16 rows are contiguous.
-__device__ __forceinline__ int vt_pos(int x) {
-  return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
-}
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -80,58 +73,6 @@ __device__ __forceinline__ f32x16 zero16() {
 
 // Row of element i of a 32x32 MFMA output in lane half lh.
 __device__ __forceinline__ int out_row(int i, int lh) { return 8 * (i >> 2) + 4 * lh + (i & 3); }
-
-// Rows [r0, r0 + 64) of a [.., ld]-strided bf16 tensor (D columns), in items of 4 rows x 8
-// columns: load_rows fetches a thread's items into registers (rows >= nrows read as zero),
-// store_rows writes them to LDS twice: row-major (stride D + 8) and, if tr != nullptr,
-// transposed with the row permutation vt_pos (stride 64 + 8).  Split so that the loads of
-// the next tile are in flight while the current one is used.
-template <int D>
-constexpr int row_items() { return (BN / 4) * (D / 8); }
-
-template <int D, int NIT>
-__device__ __forceinline__ void load_rows(const uint16_t* base, size_t ld, int r0, int nrows,
-                                          u32x4 (&pre)[NIT][4], int t, int nt) {
-#pragma unroll
-  for (int k = 0; k < NIT; ++k) {
-    const int it = t + k * nt;
-    const int rg = it % (BN / 4);
-    const int dg = it / (BN / 4);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int row = r0 + 4 * rg + s;
-      pre[k][s] = u32x4{0u, 0u, 0u, 0u};
-      if (it < row_items<D>() && row < nrows) pre[k][s] = ld16(base + static_cast<size_t>(row) * ld + 8 * dg);
-    }
-  }
-}
-
-template <int D, int NIT>
-__device__ __forceinline__ void store_rows(const u32x4 (&pre)[NIT][4], uint16_t* rm, uint16_t* tr,
-                                           int t, int nt) {
-#pragma unroll
-  for (int k = 0; k < NIT; ++k) {
-    const int it = t + k * nt;
-    if (it >= row_items<D>()) continue;
-    const int rg = it % (BN / 4);
-    const int dg = it / (BN / 4);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) st16(rm + (4 * rg + s) * (D + 8) + 8 * dg, pre[k][s]);
-    if (tr) {
-      const int pos = vt_pos(4 * rg);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        const int sh = (e & 1) * 16;
-        const uint32_t x0 = (pre[k][0][w] >> sh) & 0xffffu;
-        const uint32_t x1 = (pre[k][1][w] >> sh) & 0xffffu;
-        const uint32_t x2 = (pre[k][2][w] >> sh) & 0xffffu;
-        const uint32_t x3 = (pre[k][3][w] >> sh) & 0xffffu;
-        st8(tr + (8 * dg + e) * (BN + 8) + pos, u32x2{x0 | (x1 << 16), x2 | (x3 << 16)});
-      }
-    }
-  }
-}
 
 // ---- input-dependent bias, formed per 32 x 32 block (shared by the dq and dk/dv kernels) -------
 // The E rows of a block come from the converted copy (kE2Pad zero distances on each side, EW =
@@ -267,19 +208,101 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, float* zero_ptr
     zero_ptr[idx] = 0.f;
 }
 
+// ---- tile ring shared by the dq and dk/dv kernels --------------------------------------------------
+// Each step streams 32 rows of two bf16 tensors (K and V in the dq kernel, q and dout in the dk/dv
+// kernel) straight from global memory into a 3-slot LDS ring: rows of 2 D bytes in 16-byte chunks,
+// chunk index XOR-swizzled per row (tile_sw), each wave issuing its share of the 1 KB direct-load
+// instructions.  The score products read tile rows (A operand, 16 bytes per lane), the gradient
+// products read the tile transposed (ds_read_b64_tr_b16).
+constexpr int TROWS = 32;   // rows per step
+constexpr int NBUF = 3;     // ring slots
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at dst + 16 l
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
+}
+// LDS transpose read: within each group of 16 lanes, lane i receives 16-bit element i % 4 of the
+// 8-byte pieces addressed by lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4
+__device__ __forceinline__ u32x2 tr_read(const void* p) {
+  const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+  return __builtin_bit_cast(u32x2, x);
+}
+
+// XOR applied to the 16-byte chunk index of tile row r.  Row reads (16 lanes, rows r .. r + 15
+// at one logical chunk) need distinct values over any 16 consecutive rows; a transposing read
+// (16 lanes, 4 rows x 32 bytes: rows 4 k .. 4 k + 3, logical chunks 2 m, 2 m + 1) needs the four
+// rows' values to differ above bit 0.  D = 128 (256-byte rows, one row spans the 64 banks): row
+// bits 0-1 to chunk bits 2-3, bits 2-3 to bits 0-1.  D = 64 (128-byte rows, two rows per bank
+// line, row bit 0 selecting the half): row bit 1 to chunk bit 2, bits 2-3 to bits 0-1.
+template <int D>
+__device__ __forceinline__ int tile_sw(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// Per-lane addresses within a tile.  Direct loads: instruction k of wave w fills rows
+// RPI (NIT w + k) .. + RPI - 1 (RPI = 1024 / (2 D) rows per instruction); voff is the lane's byte
+// offset in global memory (row stride row_b).  Row reads: lane ln reads row ln, logical chunk
+// 2 c + lh.  Transposing reads of 16 rows x 32 columns (the A operand of a gradient product over
+// 16 rows): lane (ln = column within 32, lh) gets rows 4 lh .. 4 lh + 3 from its "lo" read and 8 +
+// the same from its "hi" read (16 more rows at + 16 rows), the row order in which a 32x32 MFMA
+// output lane half holds its rows, so the product's B operand is the output packed as it is.
+template <int D, int NIT>
+struct TileAddr {
+  static constexpr int ROW_B = 2 * D;
+  static constexpr int CPR = ROW_B / 16;
+  static constexpr int RPI = 64 / CPR;
+  int voff[NIT];
+  int raddr[D / 16];
+  int taddr[2][D / 32];
+  __device__ __forceinline__ TileAddr(int lane, int wave, int row_b) {
+    const int ln = lane & 31, lh = lane >> 5;
+#pragma unroll
+    for (int k = 0; k < NIT; ++k) {
+      const int r = RPI * (NIT * wave + k) + lane / CPR;
+      voff[k] = r * row_b + 16 * ((lane % CPR) ^ tile_sw<D>(r));
+    }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) raddr[c] = ln * ROW_B + 16 * ((2 * c + lh) ^ tile_sw<D>(ln));
+    const int t16 = lane & 15, j = t16 >> 2, q = t16 & 3, gq = (lane >> 4) & 1;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int r = 4 * lh + j + 8 * x;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        taddr[x][db] = r * ROW_B + 16 * ((4 * db + 2 * gq + (q >> 1)) ^ tile_sw<D>(r)) + 8 * (q & 1);
+    }
+  }
+  // A operand of a gradient product: head-dim rows 32 db + ln, tile rows 16 kk + the above
+  __device__ __forceinline__ bf16x8 tfrag(const unsigned char* tile, int db, int kk) const {
+    const u32x2 lo = tr_read(tile + taddr[0][db] + 16 * ROW_B * kk);
+    const u32x2 hi = tr_read(tile + taddr[1][db] + 16 * ROW_B * kk);
+    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+  }
+};
+
 // ---- dq (+ dr, dE, dtable): query-parallel -----------------------------------------------------
-// LDS: K, V, K^T tiles; per wave the skewed dZ buffers; the table row (table mode) or E staged
-// curve-major for the dr MFMA (r.E).
+// One workgroup = 4 waves x 32 query rows of one head, walking the kv head's 32-key tiles (K and
+// V through the ring).  The forward's transposed layout: S^T = K Q^T, so each lane owns one query
+// row and its lse, rowsum and temperature are scalars; Q^T and dO^T stay in registers as B
+// operands.  Per step a wave turns the S^T and dP^T it formed at the end of the previous step
+// into dZ^T, accumulates dQ^T += K^T dZ^T (K^T from transposing reads of the K tile) and the
+// bias-parameter gradients of in-band steps, and forms the next step's scores; one barrier per
+// step.  LDS besides the ring: per wave the skewed dZ buffers and the curves (r.E); the table row
+// (table mode) or E staged curve-major for the dr MFMA (r.E).
 template <int D, int MODE>
 struct DqLayout {
-  static constexpr int KST = D + 8;
-  static constexpr int TST = BN + 8;
-  static constexpr int TILE_BYTES = (2 * BN * KST + D * TST) * 2;
+  static constexpr int ROW_B = 2 * D;
+  static constexpr int TILE_B = TROWS * ROW_B;   // K or V tile
+  static constexpr int SLOT_B = 2 * TILE_B;
+  static constexpr int RING_B = NBUF * SLOT_B;
   static constexpr int G_BYTES = (MODE == 2) ? 32 * GST * 2 : 0;
   static constexpr int GT_BYTES = (MODE != 0) ? 64 * GTS * 2 : 0;
-  static constexpr int C_BYTES = (MODE == 2) ? CURVE_BYTES_DQ : 0;   // the block's curves (fp32)
+  static constexpr int C_BYTES = (MODE == 2) ? CURVE_BYTES_DQ : 0;   // the step's curves (fp32)
   static constexpr int WAVE_BYTES = G_BYTES + GT_BYTES + C_BYTES;
-  static constexpr int FIXED = TILE_BYTES + DQ_WAVES * WAVE_BYTES;
+  static constexpr int FIXED = RING_B + DQ_WAVES * WAVE_BYTES;
   static int bytes(int Rb, int R) {
     int n = FIXED;
     if (MODE == 1) n += (Rb + 2 * PADT) * 4;
@@ -293,14 +316,13 @@ struct DqLayout {
 template <int D, int MODE, int EW>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles, int longest_first) {
   using L = DqLayout<D, MODE>;
-  constexpr int KST = L::KST;
-  constexpr int TST = L::TST;
   constexpr int NC = D / 16;
   constexpr int NDB = D / 32;
+  constexpr int TILE_B = L::TILE_B;
+  constexpr int SLOT_B = L::SLOT_B;
+  constexpr int NIT = TROWS / (64 / (L::ROW_B / 16)) / DQ_WAVES;   // direct loads per wave and tile
+  static_assert(NIT >= 1 && NIT * (64 / (L::ROW_B / 16)) * DQ_WAVES == TROWS, "tile rows split evenly");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* Vs = Ks + BN * KST;
-  uint16_t* Kt = Vs + BN * KST;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -308,10 +330,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
   const int ln = lane & 31;
   const int lh = lane >> 5;
 
-  unsigned char* wsp = smem + L::TILE_BYTES + wave * L::WAVE_BYTES;
+  unsigned char* wsp = smem + L::RING_B + wave * L::WAVE_BYTES;
   uint16_t* Gs = reinterpret_cast<uint16_t*>(wsp);
   uint16_t* GTs = reinterpret_cast<uint16_t*>(wsp + L::G_BYTES);
-  float* cbuf = reinterpret_cast<float*>(wsp + L::G_BYTES + L::GT_BYTES);   // r.E: the block's curves
+  float* cbuf = reinterpret_cast<float*>(wsp + L::G_BYTES + L::GT_BYTES);   // r.E: the step's curves
   float* tabs = reinterpret_cast<float*>(smem + L::FIXED);                 // table mode
   uint16_t* ef = reinterpret_cast<uint16_t*>(smem + L::FIXED);             // r.E
 
@@ -332,15 +354,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
   const int row = i0 + ln;
   const bool row_ok = row < S;
 
+  // steps: the kv head's 32-key tiles t_begin + js, js < nsteps, that the workgroup's rows see;
+  // the wave's own tiles are w_lo .. w_hi
   const int wg_last = min(S, wg_i0 + 32 * DQ_WAVES) - 1;
   const int kmin = W ? max(0, wg_i0 - W + 1) : 0;
-  const int t_begin = kmin / BN;
-  const int t_end = wg_last / BN;
+  const int t_begin = kmin / TROWS;
+  const int nsteps = wg_last / TROWS - t_begin + 1;
+  const int w_lo = (W ? max(0, i0 - W + 1) : 0) / TROWS - t_begin;
+  const int w_hi = min(S - 1, i0 + 31) / TROWS - t_begin;
 
   const size_t q_row = static_cast<size_t>(a.Hq) * D;
   const size_t kv_row = static_cast<size_t>(a.Hkv) * D;
-  const uint16_t* kbase = a.k + static_cast<size_t>(b) * S * kv_row + static_cast<size_t>(hkv) * D;
-  const uint16_t* vbase = a.v + static_cast<size_t>(b) * S * kv_row + static_cast<size_t>(hkv) * D;
+  const int kv_row_b = a.Hkv * D * 2;
   const size_t qoff = (static_cast<size_t>(b) * S + (row_ok ? row : 0)) * q_row + static_cast<size_t>(h) * D;
   const float* Eh = (MODE == 2) ? a.E + static_cast<size_t>(h) * a.e_hs : nullptr;
   // r.E: the head's converted E rows at distance 0, the lane's r fragment (its own query row),
@@ -361,7 +386,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
     asm volatile("" : "+v"(crd));   // one base register, immediate offsets for the reads
   }
 
-  // bias parameters of the head in LDS (made visible by the first barrier of the tile loop)
+  // bias parameters of the head in LDS (made visible by the first barrier)
   if (MODE == 1) {
     const float* tp = a.table + static_cast<size_t>(h) * Rb;
     for (int x = tid; x < Rb + 2 * PADT; x += 256) {
@@ -420,7 +445,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
       }
       rA[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
     }
-    // zero the skewed buffers once: every in-band block writes the same set of positions
+    // zero the skewed buffers once: every in-band step writes the same set of positions
     for (int x = lane; x < (L::G_BYTES + L::GT_BYTES) / 16; x += 64)
       st16(reinterpret_cast<unsigned char*>(Gs) + 16 * x, u32x4{0u, 0u, 0u, 0u});
   }
@@ -432,175 +457,187 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
   float* dEh = (MODE == 2) ? a.dE + static_cast<size_t>(h) * a.e_hs : nullptr;
   float* dtab = (MODE == 1) ? a.dtable + static_cast<size_t>(h) * Rb : nullptr;
 
-  // K / V tiles: the next tile's rows are loaded into registers while the current one is used
-  constexpr int KIT = (row_items<D>() + 255) / 256;
-  constexpr int NCH = BN * (D / 8);
-  constexpr int VIT = (NCH + 255) / 256;
-  u32x4 kpre[KIT][4], vpre[VIT];
-  auto load_kv = [&](int tk0) {
-    load_rows<D, KIT>(kbase, kv_row, tk0, S, kpre, tid, 256);
+  const TileAddr<D, NIT> ta(lane, wave, kv_row_b);
+  const uint16_t* kbase = a.k + static_cast<size_t>(b) * S * kv_row + static_cast<size_t>(hkv) * D;
+  const uint16_t* vbase = a.v + static_cast<size_t>(b) * S * kv_row + static_cast<size_t>(hkv) * D;
+  auto dma_tile = [&](int js, unsigned char* slot) __attribute__((always_inline)) {
+    const int k0 = (t_begin + js) * TROWS;
+    const int rows = min(S - k0, TROWS);
+    const int nrec = (rows - 1) * kv_row_b + L::ROW_B;   // keys past S read as zeros
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + static_cast<size_t>(k0) * kv_row, nrec);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + static_cast<size_t>(k0) * kv_row, nrec);
 #pragma unroll
-    for (int q = 0; q < VIT; ++q) {
-      const int x = tid + 256 * q;
-      const int rr = x / (D / 8);
-      const int ch = x % (D / 8);
-      vpre[q] = u32x4{0u, 0u, 0u, 0u};
-      if (x < NCH && tk0 + rr < S) vpre[q] = ld16(vbase + static_cast<size_t>(tk0 + rr) * kv_row + 8 * ch);
+    for (int k = 0; k < NIT; ++k) {
+      dma16(rk, slot + (NIT * wave + k) * 1024, ta.voff[k]);
+      dma16(rv, slot + TILE_B + (NIT * wave + k) * 1024, ta.voff[k]);
     }
   };
-  auto store_kv = [&]() {
-    store_rows<D, KIT>(kpre, Ks, Kt, tid, 256);
+  // element (key m, query n) of a step lies at distance c + n - m, c = i0 - its first key
+  auto step_c = [&](int js) { return i0 - (t_begin + js) * TROWS; };
+  auto step_on = [&](int js) { return wave_live && js < nsteps && js >= w_lo && js <= w_hi; };
+  auto step_inband = [&](int js) { return MODE != 0 && step_c(js) - 31 < Rb; };
+
+  // S^T (log2 units, with the bias) and dP^T of a step
+  auto scores = [&](int js, const unsigned char* slot, f32x16& sacc, f32x16& pacc,
+                    const u32x4 (&eb)[2][EW / 16]) __attribute__((always_inline)) {
+    const int c = step_c(js);
+    const bool ib = step_inband(js);
+    sacc = zero16();
+    pacc = zero16();
+    bf16x8 kf = as_bf16x8(ld16(slot + ta.raddr[0])), vf = as_bf16x8(ld16(slot + TILE_B + ta.raddr[0]));
 #pragma unroll
-    for (int q = 0; q < VIT; ++q) {
-      const int x = tid + 256 * q;
-      if (x < NCH) st16(Vs + (x / (D / 8)) * KST + 8 * (x % (D / 8)), vpre[q]);
+    for (int cc = 0; cc < NC; ++cc) {
+      bf16x8 kn = kf, vn = vf;
+      if (cc + 1 < NC) {
+        kn = as_bf16x8(ld16(slot + ta.raddr[cc + 1]));
+        vn = as_bf16x8(ld16(slot + TILE_B + ta.raddr[cc + 1]));
+      }
+      sacc = mfma32(kf, qf[cc], sacc);
+      pacc = mfma32(vf, dof[cc], pacc);
+      kf = kn;
+      vf = vn;
+    }
+    // log2-domain logits tau * (scale log2(e) q.k + log2(e) beta)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] *= cq;
+    if (MODE == 1 && ib) {
+      // distances c + ln - m lie in [-31, Rb + 62]: inside the zero-padded row
+      const float* tb = tabs + PADT + c + ln;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = fmaf(tb[-out_row(i, lh)], tq, sacc[i]);
+    }
+    if (MODE == 2 && ib) {
+      // curves of the wave's 32 rows over the step's distances c - 31 .. c + 32, fp32; key
+      // m = 8 g + 4 lh + k of row n at distance c + n - m, entry t = 31 + n - m of row n
+      f32x16 clo, chi;
+      curve_mfma<EW>(eb, rf, clo, chi);
+      curve_write(crow_w, ln, lh, clo, chi);
+      wave_sync_lds();
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = fmaf(crd[27 - 8 * (i >> 2) - (i & 3)], cb, sacc[i]);
+      wave_sync_lds();   // the next step's writes follow these reads
     }
   };
-  if (t_begin <= t_end) load_kv(t_begin * BN);
-
-  for (int t = t_begin; t <= t_end; ++t) {
-    const int tk0 = t * BN;
-    __syncthreads();   // the previous tile's LDS reads are complete
-    store_kv();
-    __syncthreads();
-    if (t < t_end) load_kv(tk0 + BN);
-    if (!wave_live) continue;
-
-#pragma unroll 1
-    for (int kb = 0; kb < 2; ++kb) {
-      const int kb0 = tk0 + 32 * kb;
-      const int c = i0 - kb0;                    // delta = c + n - m
-      bool on = (c + 31 >= 0) && (kb0 < S);
-      if (W) on = on && (c - 31 < W);
-      if (!on) continue;
-      const bool inband = (MODE != 0) && (c - 31 < Rb);
-
-      // r.E bias: the block's E rows, requested before the score MFMAs
-      u32x4 eb[2][EW / 16];
-      if (MODE == 2 && inband) e_rows<EW>(e2h, c, ln, lh, eb);
-
-      // operands read one step ahead of the MFMAs that use them
-      f32x16 sacc = zero16(), pacc = zero16();
-      const uint16_t* kr = Ks + (32 * kb + ln) * KST + 8 * lh;
-      const uint16_t* vr = Vs + (32 * kb + ln) * KST + 8 * lh;
-      bf16x8 kf = as_bf16x8(ld16(kr)), vf = as_bf16x8(ld16(vr));
+  // dS^T = P * (dP - rowsum) (the temperature factor of dZ = tau dS is applied to the accumulated
+  // dq and to the bias-gradient inputs), dQ^T += K^T dS^T, and the bias-parameter gradients
+  auto grads = [&](int js, const unsigned char* slot, const f32x16& sacc,
+                   const f32x16& pacc) __attribute__((always_inline)) {
+    const int c = step_c(js);
+    float dz[16];
+    const bool edge = (c - 31 < 0) || (W && c + 31 >= W);
+    if (edge) {
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        bf16x8 kn = kf, vn = vf;
-        if (cc + 1 < NC) {
-          kn = as_bf16x8(ld16(kr + 16 * (cc + 1)));
-          vn = as_bf16x8(ld16(vr + 16 * (cc + 1)));
+      for (int i = 0; i < 16; ++i) {
+        const int d = c + ln - out_row(i, lh);
+        const bool vis = (d >= 0) & ((W == 0) | (d < W));
+        const float p = fast_exp2(sacc[i] - lse2);
+        dz[i] = (vis ? p : 0.f) * (pacc[i] - dsum);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dz[i] = fast_exp2(sacc[i] - lse2) * (pacc[i] - dsum);
+    }
+    bf16x8 dzf[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      uint32_t w[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) w[jj] = pack_bf16x2(dz[8 * kk + 2 * jj], dz[8 * kk + 2 * jj + 1]);
+      dzf[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+    }
+#pragma unroll
+    for (int x = 0; x < 2 * NDB; ++x) dqacc[x >> 1] = mfma32(ta.tfrag(slot, x >> 1, x & 1), dzf[x & 1], dqacc[x >> 1]);
+
+    if (MODE != 0 && step_inband(js)) {
+      // skewed dZ: G^T[dist][query] (and G[query][dist]) with dist = n - m + 32 over the
+      // window c - 32 .. c + 31
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int dp = ln - out_row(i, lh) + 32;
+        const uint16_t v16 = f32_to_bf16(dz[i] * tq);
+        GTs[dp * GTS + ln] = v16;
+        if (MODE == 2) Gs[ln * GST + dp] = v16;
+      }
+      wave_sync_lds();
+      // dE (dtable): D[f][dist] = sum_i r^T[f][i] G[i][dist], 32 distances per MFMA pair
+#pragma unroll
+      for (int dbp = 0; dbp < 2; ++dbp) {
+        f32x16 acc = zero16();
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 gt = as_bf16x8(ld16(GTs + (32 * dbp + ln) * GTS + 16 * kk + 8 * lh));
+          acc = mfma32(rA[kk], gt, acc);
         }
-        sacc = mfma32(kf, qf[cc], sacc);
-        pacc = mfma32(vf, dof[cc], pacc);
-        kf = kn;
-        vf = vn;
-      }
-      // log2-domain logits tau * (scale log2(e) q.k + log2(e) beta)
+        const int dist = c - 32 + 32 * dbp + ln;
+        if (dist >= 0 && dist < Rb) {
+          if (MODE == 1) {
+            if (lh == 0) atomicAdd(dtab + dist, acc[0]);
+          } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] *= cq;
-      if (MODE == 1 && inband) {
-        // distances c + ln - m lie in [-31, Rb + 62]: inside the zero-padded row
-        const float* tb = tabs + PADT + c + ln;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = fmaf(tb[-out_row(i, lh)], tq, sacc[i]);
-      }
-      if (MODE == 2 && inband) {
-        // curves of the wave's 32 rows over the block's distances c - 31 .. c + 32, fp32; key
-        // m = 8 g + 4 lh + k of row n at distance c + n - m, entry t = 31 + n - m of row n
-        f32x16 clo, chi;
-        curve_mfma<EW>(eb, rf, clo, chi);
-        curve_write(crow_w, ln, lh, clo, chi);
-        wave_sync_lds();
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = fmaf(crd[27 - 8 * (i >> 2) - (i & 3)], cb, sacc[i]);
-        wave_sync_lds();   // the next block's writes follow these reads
-      }
-      // P and dS = P * (dP - rowsum); the temperature factor of dZ = tau dS is applied to the
-      // accumulated dq and to the bias-gradient inputs
-      float dz[16];
-      const bool edge = (c - 31 < 0) || (W && c + 31 >= W);
-      if (edge) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int d = c + ln - out_row(i, lh);
-          const bool vis = (d >= 0) & ((W == 0) | (d < W));
-          const float p = fast_exp2(sacc[i] - lse2);
-          dz[i] = (vis ? p : 0.f) * (pacc[i] - dsum);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) dz[i] = fast_exp2(sacc[i] - lse2) * (pacc[i] - dsum);
-      }
-      bf16x8 dzf[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        uint32_t w[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) w[jj] = pack_bf16x2(dz[8 * kk + 2 * jj], dz[8 * kk + 2 * jj + 1]);
-        dzf[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
-      }
-      // dQ^T += K^T dS^T
-      {
-        const uint16_t* ktr = Kt + ln * TST + 32 * kb + 8 * lh;
-        bf16x8 kt = as_bf16x8(ld16(ktr));
-#pragma unroll
-        for (int x = 0; x < 2 * NDB; ++x) {
-          bf16x8 kn = kt;
-          if (x + 1 < 2 * NDB) kn = as_bf16x8(ld16(ktr + 32 * ((x + 1) >> 1) * TST + 16 * ((x + 1) & 1)));
-          dqacc[x >> 1] = mfma32(kt, dzf[x & 1], dqacc[x >> 1]);
-          kt = kn;
-        }
-      }
-
-      if (MODE != 0 && inband) {
-        // skewed dZ: G^T[dist][query] (and G[query][dist]) with dist = n - m + 32 over the
-        // window c - 32 .. c + 31
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int dp = ln - out_row(i, lh) + 32;
-          const uint16_t v16 = f32_to_bf16(dz[i] * tq);
-          GTs[dp * GTS + ln] = v16;
-          if (MODE == 2) Gs[ln * GST + dp] = v16;
-        }
-        wave_sync_lds();
-        // dE (dtable): D[f][dist] = sum_i r^T[f][i] G[i][dist], 32 distances per MFMA pair
-#pragma unroll
-        for (int dbp = 0; dbp < 2; ++dbp) {
-          f32x16 acc = zero16();
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8 gt = as_bf16x8(ld16(GTs + (32 * dbp + ln) * GTS + 16 * kk + 8 * lh));
-            acc = mfma32(rA[kk], gt, acc);
-          }
-          const int dist = c - 32 + 32 * dbp + ln;
-          if (dist >= 0 && dist < Rb) {
-            if (MODE == 1) {
-              if (lh == 0) atomicAdd(dtab + dist, acc[0]);
-            } else {
-#pragma unroll
-              for (int i = 0; i < 8; ++i) {
-                const int f = out_row(i, lh);
-                if (f < a.R) atomicAdd(dEh + static_cast<size_t>(f) * Rb + dist, acc[i]);
-              }
+            for (int i = 0; i < 8; ++i) {
+              const int f = out_row(i, lh);
+              if (f < a.R) atomicAdd(dEh + static_cast<size_t>(f) * Rb + dist, acc[i]);
             }
           }
         }
-        if (MODE == 2) {
-          // dr^T[f][query] += sum_dist E[f][dist] G^T[dist][query], 16 distances per MFMA
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const int d0 = c - 32 + 16 * kk + 8 * lh;
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (ln < a.R) x = ld16(ef + ln * efs + PADE + d0);
-            const bf16x8 gf = as_bf16x8(ld16(Gs + ln * GST + 16 * kk + 8 * lh));
-            dracc = mfma32(as_bf16x8(x), gf, dracc);
-          }
-        }
-        wave_sync_lds();
       }
+      if (MODE == 2) {
+        // dr^T[f][query] += sum_dist E[f][dist] G^T[dist][query], 16 distances per MFMA
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int d0 = c - 32 + 16 * kk + 8 * lh;
+          u32x4 x = {0u, 0u, 0u, 0u};
+          if (ln < a.R) x = ld16(ef + ln * efs + PADE + d0);
+          const bf16x8 gf = as_bf16x8(ld16(Gs + ln * GST + 16 * kk + 8 * lh));
+          dracc = mfma32(as_bf16x8(x), gf, dracc);
+        }
+      }
+      wave_sync_lds();
     }
+  };
+
+  // prologue: the first two steps' tiles, the first step's scores
+  dma_tile(0, smem);
+  if (nsteps > 1) dma_tile(1, smem + SLOT_B);
+  u32x4 eb[2][EW / 16];
+  if (MODE == 2 && step_on(0) && step_inband(0)) e_rows<EW>(e2h, step_c(0), ln, lh, eb);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's direct loads have landed
+  __syncthreads();
+  f32x16 sa, pa;
+  if (step_on(0)) scores(0, smem, sa, pa, eb);
+
+  // step js: the gradients of js (tiles in slot js % 3), then the scores of js + 1 (slot
+  // (js + 1) % 3) into the same registers; the tiles of js + 2 go to the slot js - 1 used.  The
+  // slots are passed as restrict pointers: the compiler then knows that the direct loads into ds
+  // do not alias the reads of cs and ns and adds no wait for them.
+  auto iteration_body = [&](int js, const unsigned char* __restrict__ cs, const unsigned char* __restrict__ ns,
+                            unsigned char* __restrict__ ds, auto inner_c) __attribute__((always_inline)) {
+    constexpr bool INNER = decltype(inner_c)::value;   // js + 2 < nsteps is known
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    u32x4 e[2][EW / 16];
+    if (MODE == 2 && step_on(js + 1) && step_inband(js + 1)) e_rows<EW>(e2h, step_c(js + 1), ln, lh, e);
+    // the E rows are requested before the tiles of js + 2, so that the wait for them
+    // (vector-memory counts retire in order) does not wait for the tiles
+    __builtin_amdgcn_sched_barrier(0);
+    if (INNER || js + 2 < nsteps) dma_tile(js + 2, ds);
+    if (step_on(js)) grads(js, cs, sa, pa);
+    if (step_on(js + 1)) scores(js + 1, ns, sa, pa, e);
+  };
+  using true_t = std::integral_constant<bool, true>;
+  using false_t = std::integral_constant<bool, false>;
+  auto iteration = [&](int js, int sl, auto inner_c) __attribute__((always_inline)) {
+    iteration_body(js, smem + sl * SLOT_B, smem + ((sl + 1) % NBUF) * SLOT_B, smem + ((sl + 2) % NBUF) * SLOT_B,
+                   inner_c);
+  };
+  int js = 0;
+  for (; js + 4 < nsteps; js += 3) {
+    iteration(js, 0, true_t{});
+    iteration(js + 1, 1, true_t{});
+    iteration(js + 2, 2, true_t{});
   }
+  for (; js + 1 < nsteps; ++js) iteration(js, js % NBUF, false_t{});
+  if (step_on(js)) grads(js, smem + (js % NBUF) * SLOT_B, sa, pa);
 
   if (!wave_live || !row_ok) return;
   uint16_t* dqp = a.dq + qoff;
@@ -634,46 +671,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
 // ahead.  Per step a wave turns the scores S = Q K^T and dP = dO V^T it formed at the end of the
 // previous step into P and dZ, accumulates dV^T += dO^T P and dK^T += Q^T dZ, and forms the next
 // step's scores; one barrier per step.
-constexpr int KV_ROWS = 32;   // query rows per step
-constexpr int KV_NBUF = 3;    // ring slots
-
 template <int D>
 struct DkvLayout {
   static constexpr int ROW_B = 2 * D;                  // bytes per tile row
-  static constexpr int TILE_B = KV_ROWS * ROW_B;       // q or dout tile
-  static constexpr int REC_B = 4 * KV_ROWS * 4;        // per-row lse2, rowsum, c_qk tau, tau
+  static constexpr int TILE_B = TROWS * ROW_B;       // q or dout tile
+  static constexpr int REC_B = 4 * TROWS * 4;        // per-row lse2, rowsum, c_qk tau, tau
   static constexpr int SLOT_B = 2 * TILE_B + REC_B;
-  static constexpr int RING_B = KV_NBUF * SLOT_B;
+  static constexpr int RING_B = NBUF * SLOT_B;
   // table mode: two head slots of the zero-padded table row; r.E: a curve buffer per wave
   static int bytes(int mode, int Rb) {
     return RING_B + (mode == 1 ? 2 * (Rb + 2 * PADT) * 4 : 0) + (mode == 2 ? DKV_WAVES * CURVE_BYTES_KV : 0);
   }
 };
-
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at dst + 16 l
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
-}
-// LDS transpose read: within each group of 16 lanes, lane i receives 16-bit element i % 4 of the
-// 8-byte pieces addressed by lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4
-__device__ __forceinline__ u32x2 tr_read(const void* p) {
-  const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
-  return __builtin_bit_cast(u32x2, x);
-}
-
-// XOR applied to the 16-byte chunk index of tile row r.  Row reads (16 lanes, rows r .. r + 15
-// at one logical chunk) need distinct values over any 16 consecutive rows; a transposing read
-// (16 lanes, 4 rows x 32 bytes: rows 4 k .. 4 k + 3, logical chunks 2 m, 2 m + 1) needs the four
-// rows' values to differ above bit 0.  D = 128 (256-byte rows, one row spans the 64 banks): row
-// bits 0-1 to chunk bits 2-3, bits 2-3 to bits 0-1.  D = 64 (128-byte rows, two rows per bank
-// line, row bit 0 selecting the half): row bit 1 to chunk bit 2, bits 2-3 to bits 0-1.
-template <int D>
-__device__ __forceinline__ int tile_sw(int r) {
-  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
-}
 
 template <int D, int MODE, int EW>
 __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) {
@@ -686,8 +695,8 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   constexpr int SLOT_B = L::SLOT_B;
   constexpr int CPR = ROW_B / 16;                     // chunks per row
   constexpr int RPI = 64 / CPR;                       // rows per direct-load instruction
-  constexpr int NIT = KV_ROWS / RPI / DKV_WAVES;      // instructions per wave and tile
-  static_assert(NIT >= 1 && NIT * RPI * DKV_WAVES == KV_ROWS, "tile rows split evenly over the waves");
+  constexpr int NIT = TROWS / RPI / DKV_WAVES;      // instructions per wave and tile
+  static_assert(NIT >= 1 && NIT * RPI * DKV_WAVES == TROWS, "tile rows split evenly over the waves");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int Rb = a.bias_range;
   const int TROW = Rb + 2 * PADT;
@@ -753,16 +762,16 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   // steps: (query head hh of the group, query tile t_begin + t), t < ntiles
   const int last_key = min(S, j_lo + 32 * DKV_WAVES) - 1;
   const int i_last = W ? min(S - 1, last_key + W - 1) : S - 1;
-  const int t_begin = j_lo / KV_ROWS;
-  const int ntiles = i_last / KV_ROWS - t_begin + 1;
+  const int t_begin = j_lo / TROWS;
+  const int ntiles = i_last / TROWS - t_begin + 1;
   const int nsteps = G * ntiles;
   // the wave's tiles within a head: from the tile of its first key to that of its keys' last
   // visible query row
   const int w_lo = wave;
-  const int w_hi = (W ? min(S - 1, j0w + 31 + W - 1) : S - 1) / KV_ROWS - t_begin;
+  const int w_hi = (W ? min(S - 1, j0w + 31 + W - 1) : S - 1) / TROWS - t_begin;
 
   auto step_head = [&](int js) { return js / ntiles; };
-  auto step_row0 = [&](int js) { return (t_begin + js - (js / ntiles) * ntiles) * KV_ROWS; };
+  auto step_row0 = [&](int js) { return (t_begin + js - (js / ntiles) * ntiles) * TROWS; };
   auto step_on = [&](int js) {
     const int t = js - (js / ntiles) * ntiles;
     return wave_live && js < nsteps && t >= w_lo && t <= w_hi;
@@ -772,28 +781,22 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   auto step_edge = [&](int js) {
     const int i0 = step_row0(js);
     const int c = i0 - j0w;
-    return (c - 31 < 0) || (W && c + 31 >= W) || (i0 + KV_ROWS > S);
+    return (c - 31 < 0) || (W && c + 31 >= W) || (i0 + TROWS > S);
   };
 
-  // direct loads: instruction k of this wave fills rows RPI (NIT wave + k) .. + RPI - 1
-  int voff[NIT];
-#pragma unroll
-  for (int k = 0; k < NIT; ++k) {
-    const int r = RPI * (NIT * wave + k) + lane / CPR;
-    voff[k] = r * q_row_b + 16 * ((lane % CPR) ^ tile_sw<D>(r));
-  }
+  const TileAddr<D, NIT> ta(lane, wave, q_row_b);
   auto dma_tile = [&](int js, unsigned char* slot) __attribute__((always_inline)) {
     const int h = hkv * G + step_head(js);
     const int i0 = step_row0(js);
-    const int rows = min(S - i0, KV_ROWS);
+    const int rows = min(S - i0, TROWS);
     const int nrec = (rows - 1) * q_row_b + ROW_B;   // rows past S read as zeros
     const size_t off = (static_cast<size_t>(b) * S + i0) * q_row + static_cast<size_t>(h) * D;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + off, nrec);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.dout + off, nrec);
 #pragma unroll
     for (int k = 0; k < NIT; ++k) {
-      dma16(rq, slot + (NIT * wave + k) * 1024, voff[k]);
-      dma16(rd, slot + TILE_B + (NIT * wave + k) * 1024, voff[k]);
+      dma16(rq, slot + (NIT * wave + k) * 1024, ta.voff[k]);
+      dma16(rd, slot + TILE_B + (NIT * wave + k) * 1024, ta.voff[k]);
     }
   };
   // per-row values of a step, through lanes 0..31 of wave 0: loaded a step ahead and used only
@@ -819,9 +822,9 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
       float* rp = reinterpret_cast<float*>(slot + 2 * TILE_B);
       const float tq = temp_factor(visible_keys(rec_row, W), a.temp_len, a.temp_inv_log2);
       rp[ln] = rec_l * kLog2e;
-      rp[KV_ROWS + ln] = rec_s;
-      rp[2 * KV_ROWS + ln] = a.c_qk * tq;
-      rp[3 * KV_ROWS + ln] = tq;
+      rp[TROWS + ln] = rec_s;
+      rp[2 * TROWS + ln] = a.c_qk * tq;
+      rp[3 * TROWS + ln] = tq;
     }
   };
   // table mode: head hh's row (in units of the raw score), zero-padded, into slot hh % 2
@@ -832,30 +835,6 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
       const int d = x - PADT;
       tab[x] = (d >= 0 && d < Rb) ? tp[d] * inv_scale : 0.f;
     }
-  };
-
-  // fragment addresses within a slot: rows of the score products (A = q or dout rows, lane ln
-  // reads row ln, chunk 2 c + lh) and the transposing reads of the gradient products (A = q^T
-  // or dout^T: lane (ln = head-dim row, lh) gets queries 4 lh .. 4 lh + 3 from its "lo" read
-  // and 8 + the same from its "hi" read, 16 more queries at + 16 rows)
-  int qaddr[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) qaddr[c] = ln * ROW_B + 16 * ((2 * c + lh) ^ tile_sw<D>(ln));
-  int taddr[2][NDB];
-  {
-    const int t16 = lane & 15, j = t16 >> 2, q = t16 & 3, gq = (lane >> 4) & 1;
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int r = 4 * lh + j + 8 * x;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        taddr[x][db] = r * ROW_B + 16 * ((4 * db + 2 * gq + (q >> 1)) ^ tile_sw<D>(r)) + 8 * (q & 1);
-    }
-  }
-  auto t_frag = [&](const unsigned char* base, int db, int kk) __attribute__((always_inline)) -> bf16x8 {
-    const u32x2 lo = tr_read(base + taddr[0][db] + 16 * ROW_B * kk);
-    const u32x2 hi = tr_read(base + taddr[1][db] + 16 * ROW_B * kk);
-    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
   };
 
   const uint16_t* e2b = (MODE == 2) ? a.e2 + kE2Pad * EW : nullptr;
@@ -879,13 +858,13 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = tb[out_row(i, lh)];
     }
-    bf16x8 qa = as_bf16x8(ld16(slot + qaddr[0])), da = as_bf16x8(ld16(slot + TILE_B + qaddr[0]));
+    bf16x8 qa = as_bf16x8(ld16(slot + ta.raddr[0])), da = as_bf16x8(ld16(slot + TILE_B + ta.raddr[0]));
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       bf16x8 qn = qa, dn = da;
       if (cc + 1 < NC) {
-        qn = as_bf16x8(ld16(slot + qaddr[cc + 1]));
-        dn = as_bf16x8(ld16(slot + TILE_B + qaddr[cc + 1]));
+        qn = as_bf16x8(ld16(slot + ta.raddr[cc + 1]));
+        dn = as_bf16x8(ld16(slot + TILE_B + ta.raddr[cc + 1]));
       }
       sacc = mfma32(qa, kf[cc], sacc);
       pacc = mfma32(da, vf[cc], pacc);
@@ -917,9 +896,9 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
       for (int g4 = 0; g4 < 4; ++g4) {
         const int m0 = 8 * g4 + 4 * lh;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(rp + m0);
-        const f32x4 s4 = *reinterpret_cast<const f32x4*>(rp + KV_ROWS + m0);
-        const f32x4 c4 = *reinterpret_cast<const f32x4*>(rp + 2 * KV_ROWS + m0);
-        const f32x4 t4 = *reinterpret_cast<const f32x4*>(rp + 3 * KV_ROWS + m0);
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(rp + TROWS + m0);
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(rp + 2 * TROWS + m0);
+        const f32x4 t4 = *reinterpret_cast<const f32x4*>(rp + 3 * TROWS + m0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int i = 4 * g4 + u;
@@ -935,9 +914,9 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
       for (int g4 = 0; g4 < 4; ++g4) {
         const int m0 = 8 * g4 + 4 * lh;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(rp + m0);
-        const f32x4 s4 = *reinterpret_cast<const f32x4*>(rp + KV_ROWS + m0);
-        const f32x4 c4 = *reinterpret_cast<const f32x4*>(rp + 2 * KV_ROWS + m0);
-        const f32x4 t4 = *reinterpret_cast<const f32x4*>(rp + 3 * KV_ROWS + m0);
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(rp + TROWS + m0);
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(rp + 2 * TROWS + m0);
+        const f32x4 t4 = *reinterpret_cast<const f32x4*>(rp + 3 * TROWS + m0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int i = 4 * g4 + u;
@@ -964,8 +943,8 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
                    const bf16x8 (&dzf)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int x = 0; x < 2 * NDB; ++x) {
-      const bf16x8 oa = t_frag(slot + TILE_B, x >> 1, x & 1);
-      const bf16x8 qt = t_frag(slot, x >> 1, x & 1);
+      const bf16x8 oa = ta.tfrag(slot + TILE_B, x >> 1, x & 1);
+      const bf16x8 qt = ta.tfrag(slot, x >> 1, x & 1);
       dvacc[x >> 1] = mfma32(oa, pf[x & 1], dvacc[x >> 1]);
       dkacc[x >> 1] = mfma32(qt, dzf[x & 1], dkacc[x >> 1]);
     }
@@ -1020,7 +999,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   using true_t = std::integral_constant<bool, true>;
   using false_t = std::integral_constant<bool, false>;
   auto iteration = [&](int js, int sl, auto inner_c) __attribute__((always_inline)) {
-    iteration_body(js, smem + sl * SLOT_B, smem + ((sl + 1) % KV_NBUF) * SLOT_B, smem + ((sl + 2) % KV_NBUF) * SLOT_B,
+    iteration_body(js, smem + sl * SLOT_B, smem + ((sl + 1) % NBUF) * SLOT_B, smem + ((sl + 2) % NBUF) * SLOT_B,
                    inner_c);
   };
   int js = 0;
@@ -1029,10 +1008,10 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
     iteration(js + 1, 1, true_t{});
     iteration(js + 2, 2, true_t{});
   }
-  for (; js + 1 < nsteps; ++js) iteration(js, js % KV_NBUF, false_t{});
+  for (; js + 1 < nsteps; ++js) iteration(js, js % NBUF, false_t{});
   if (nsteps > 1) __syncthreads();   // the last step's row values, stored after the previous barrier
   if (step_on(js)) {
-    const unsigned char* cs = smem + (js % KV_NBUF) * SLOT_B;
+    const unsigned char* cs = smem + (js % NBUF) * SLOT_B;
     bf16x8 pf[2], dzf[2];
     probs(js, cs, sa, pa, pf, dzf);
     grads(cs, pf, dzf);
