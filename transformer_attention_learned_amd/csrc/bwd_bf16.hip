@@ -314,7 +314,7 @@ struct DqLayout {
 };
 
 template <int D, int MODE, int EW>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles, int longest_first) {
+__global__ __launch_bounds__(256, (MODE == 0 || (MODE == 1 && D == 64)) ? 2 : 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles, int longest_first) {
   using L = DqLayout<D, MODE>;
   constexpr int NC = D / 16;
   constexpr int NDB = D / 32;
@@ -770,22 +770,31 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   const int w_lo = wave;
   const int w_hi = (W ? min(S - 1, j0w + 31 + W - 1) : S - 1) / TROWS - t_begin;
 
-  auto step_head = [&](int js) { return js / ntiles; };
-  auto step_row0 = [&](int js) { return (t_begin + js - (js / ntiles) * ntiles) * TROWS; };
-  auto step_on = [&](int js) {
-    const int t = js - (js / ntiles) * ntiles;
-    return wave_live && js < nsteps && t >= w_lo && t <= w_hi;
+  // a step's position (head hh, tile t), advanced one step at a time (no divisions per step);
+  // hh == G past the last step
+  struct Pos {
+    int hh, t;
   };
+  auto pos_next = [&](Pos p) {
+    if (++p.t == ntiles) {
+      p.t = 0;
+      ++p.hh;
+    }
+    return p;
+  };
+  auto step_head = [&](Pos p) { return p.hh; };
+  auto step_row0 = [&](Pos p) { return (t_begin + p.t) * TROWS; };
+  auto step_on = [&](Pos p) { return wave_live && p.hh < G && p.t >= w_lo && p.t <= w_hi; };
   // element (query m, key n) of a step lies at distance c + m - n, c = its first row - j0w
-  auto step_inband = [&](int js) { return MODE != 0 && step_row0(js) - j0w - 31 < a.bias_range; };
-  auto step_edge = [&](int js) {
+  auto step_inband = [&](Pos js) { return MODE != 0 && step_row0(js) - j0w - 31 < a.bias_range; };
+  auto step_edge = [&](Pos js) {
     const int i0 = step_row0(js);
     const int c = i0 - j0w;
     return (c - 31 < 0) || (W && c + 31 >= W) || (i0 + TROWS > S);
   };
 
   const TileAddr<D, NIT> ta(lane, wave, q_row_b);
-  auto dma_tile = [&](int js, unsigned char* slot) __attribute__((always_inline)) {
+  auto dma_tile = [&](Pos js, unsigned char* slot) __attribute__((always_inline)) {
     const int h = hkv * G + step_head(js);
     const int i0 = step_row0(js);
     const int rows = min(S - i0, TROWS);
@@ -804,7 +813,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   // get lse = +inf (P = 0)
   float rec_l = INFINITY, rec_s = 0.f;
   int rec_row = 0;
-  auto rec_load = [&](int js) __attribute__((always_inline)) {
+  auto rec_load = [&](Pos js) __attribute__((always_inline)) {
     if (wave == 0 && lh == 0) {
       const int h = hkv * G + step_head(js);
       rec_row = step_row0(js) + ln;
@@ -838,7 +847,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   };
 
   const uint16_t* e2b = (MODE == 2) ? a.e2 + kE2Pad * EW : nullptr;
-  auto e_load = [&](int js, u32x4 (&eb)[2][EW / 16], uint32_t (&rx)[8]) __attribute__((always_inline)) {
+  auto e_load = [&](Pos js, u32x4 (&eb)[2][EW / 16], uint32_t (&rx)[8]) __attribute__((always_inline)) {
     const int h = hkv * G + step_head(js);
     const int i0 = step_row0(js);
     e_rows<EW>(e2b + static_cast<size_t>(a.e_hs ? h : 0) * (Rb + 2 * kE2Pad + 1) * EW, i0 - j0w, ln, lh, eb);
@@ -846,7 +855,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   };
 
   // S (plus the bias, in units of q.k) and dP of a step
-  auto scores = [&](int js, const unsigned char* slot, f32x16& sacc, f32x16& pacc, const u32x4 (&eb)[2][EW / 16],
+  auto scores = [&](Pos js, const unsigned char* slot, f32x16& sacc, f32x16& pacc, const u32x4 (&eb)[2][EW / 16],
                     const uint32_t (&rx)[8]) __attribute__((always_inline)) {
     const int c = step_row0(js) - j0w;
     const bool ib = step_inband(js);
@@ -884,7 +893,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   // P and dZ = tau * P * (dP - rowsum), rounded to bf16 as the B operands of the gradient
   // products; per row: lse (log2 units), rowsum, c_qk * tau, tau.  Interior and edge steps get
   // separate loops so that no branch sits inside the element loop.
-  auto probs = [&](int js, const unsigned char* slot, f32x16& sacc, f32x16& pacc, bf16x8 (&pf)[2],
+  auto probs = [&](Pos js, const unsigned char* slot, f32x16& sacc, f32x16& pacc, bf16x8 (&pf)[2],
                    bf16x8 (&dzf)[2]) __attribute__((always_inline)) {
     const float* rp = reinterpret_cast<const float*>(slot + 2 * TILE_B);
     if (step_edge(js)) {
@@ -955,65 +964,71 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
     stage_table(0);
     if (ntiles == 1 && G > 1) stage_table(1);
   }
-  rec_load(0);
-  dma_tile(0, smem);
-  if (nsteps > 1) dma_tile(1, smem + SLOT_B);
+  Pos p0 = {0, 0};
+  Pos p1 = pos_next(p0);
+  Pos p2 = pos_next(p1);
+  rec_load(p0);
+  dma_tile(p0, smem);
+  if (nsteps > 1) dma_tile(p1, smem + SLOT_B);
   rec_store(smem);
-  if (nsteps > 1) rec_load(1);
+  if (nsteps > 1) rec_load(p1);
   u32x4 eb[2][EW / 16];
   uint32_t rx[8];
-  if (MODE == 2 && step_on(0) && step_inband(0)) e_load(0, eb, rx);
+  if (MODE == 2 && step_on(p0) && step_inband(p0)) e_load(p0, eb, rx);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's direct loads have landed
   __syncthreads();
   f32x16 sa, pa;
-  if (step_on(0)) scores(0, smem, sa, pa, eb, rx);
+  if (step_on(p0)) scores(p0, smem, sa, pa, eb, rx);
 
   // step js: P, dZ and the gradient products of js (its row values and tiles in slot js % 3), then
   // the scores of js + 1 (slot (js + 1) % 3) into the same registers; the tiles of js + 2 go to
   // the slot js - 1 used.  The slots are passed as restrict pointers: the compiler then knows
   // that the direct loads into ds do not alias the reads of cs and ns and adds no wait for them.
-  auto iteration_body = [&](int js, const unsigned char* __restrict__ cs, unsigned char* __restrict__ ns,
+  auto iteration_body = [&](const unsigned char* __restrict__ cs, unsigned char* __restrict__ ns,
                             unsigned char* __restrict__ ds, auto inner_c) __attribute__((always_inline)) {
-    constexpr bool INNER = decltype(inner_c)::value;   // js + 2 < nsteps is known
+    constexpr bool INNER = decltype(inner_c)::value;   // step js + 2 exists
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     rec_store(ns);
     u32x4 e[2][EW / 16];
     uint32_t x[8];
-    if (MODE == 2 && step_on(js + 1) && step_inband(js + 1)) e_load(js + 1, e, x);
-    if (MODE == 1 && (INNER || js + 2 < nsteps) && (js + 2) % ntiles == 0) stage_table((js + 2) / ntiles);
+    if (MODE == 2 && step_on(p1) && step_inband(p1)) e_load(p1, e, x);
+    if (MODE == 1 && (INNER || p2.hh < G) && p2.t == 0) stage_table(p2.hh);
     // the bias operands are requested before the tiles of js + 2, so that the waits for them
     // (vector-memory counts retire in order) do not wait for the tiles
     __builtin_amdgcn_sched_barrier(0);
-    if (INNER || js + 2 < nsteps) {
-      dma_tile(js + 2, ds);
-      rec_load(js + 2);
+    if (INNER || p2.hh < G) {
+      dma_tile(p2, ds);
+      rec_load(p2);
     }
-    if (step_on(js)) {
+    if (step_on(p0)) {
       bf16x8 pf[2], dzf[2];
-      probs(js, cs, sa, pa, pf, dzf);
+      probs(p0, cs, sa, pa, pf, dzf);
       grads(cs, pf, dzf);
     }
-    if (step_on(js + 1)) scores(js + 1, ns, sa, pa, e, x);
+    if (step_on(p1)) scores(p1, ns, sa, pa, e, x);
+    p0 = p1;
+    p1 = p2;
+    p2 = pos_next(p2);
   };
   using true_t = std::integral_constant<bool, true>;
   using false_t = std::integral_constant<bool, false>;
-  auto iteration = [&](int js, int sl, auto inner_c) __attribute__((always_inline)) {
-    iteration_body(js, smem + sl * SLOT_B, smem + ((sl + 1) % NBUF) * SLOT_B, smem + ((sl + 2) % NBUF) * SLOT_B,
+  auto iteration = [&](int sl, auto inner_c) __attribute__((always_inline)) {
+    iteration_body(smem + sl * SLOT_B, smem + ((sl + 1) % NBUF) * SLOT_B, smem + ((sl + 2) % NBUF) * SLOT_B,
                    inner_c);
   };
   int js = 0;
   for (; js + 4 < nsteps; js += 3) {
-    iteration(js, 0, true_t{});
-    iteration(js + 1, 1, true_t{});
-    iteration(js + 2, 2, true_t{});
+    iteration(0, true_t{});
+    iteration(1, true_t{});
+    iteration(2, true_t{});
   }
-  for (; js + 1 < nsteps; ++js) iteration(js, js % NBUF, false_t{});
+  for (; js + 1 < nsteps; ++js) iteration(js % NBUF, false_t{});
   if (nsteps > 1) __syncthreads();   // the last step's row values, stored after the previous barrier
-  if (step_on(js)) {
+  if (step_on(p0)) {
     const unsigned char* cs = smem + (js % NBUF) * SLOT_B;
     bf16x8 pf[2], dzf[2];
-    probs(js, cs, sa, pa, pf, dzf);
+    probs(p0, cs, sa, pa, pf, dzf);
     grads(cs, pf, dzf);
   }
 
