@@ -21,10 +21,13 @@
 //     32 x 32 block forms the curves of its 32 query rows over its 64 distances with MFMAs over
 //     the features (fp32 results), writes them to a wave-private LDS buffer and reads its
 //     diagonal back, so the bias reaches the recomputed logits with fp32 accuracy.
+//   * both main kernels stream their 32-row tiles (K and V, or q and dout) through a 3-slot LDS
+//     ring filled by direct-to-LDS loads two steps ahead, one barrier per step; the gradient
+//     products read the tiles transposed (ds_read_b64_tr_b16), so no transposed copy is stored.
 //   * bwd_dq: one workgroup = 4 waves x 32 query rows of one head (the forward's transposed
 //     layout: S^T = K Q^T, so each lane owns one query row and its lse, rowsum and temperature
-//     are scalars).  Per 32 x 32 block it recomputes S^T and dP^T = V dO^T, forms dZ^T and
-//     accumulates dQ^T += K^T dZ^T (K^T in LDS with the key permutation of the forward's V^T).
+//     are scalars).  Per 32-key step it recomputes S^T and dP^T = V dO^T, forms dZ^T and
+//     accumulates dQ^T += K^T dZ^T.
 //     A lane's 16 bias values lie on its own query row's curve (the forward's skewed curve
 //     buffer layout).  In-band blocks also write dZ into two wave-private skewed buffers,
 //     G[query][distance] and its transpose, over the block's 64-distance window; then
@@ -35,8 +38,8 @@
 //     with r replaced by a ones row.
 //   * bwd_dkdv: one workgroup = 4 waves x 32 keys of one kv head, looping over the group's
 //     query heads and the query tiles that see its keys.  Untransposed layout S = Q K^T (each
-//     lane owns one key), K and V held in registers as B operands; Q, dO and their transposes
-//     in LDS; per-row lse, rowsum and temperature from LDS.  dV^T += dO^T P and dK^T += Q^T dZ
+//     lane owns one key), K and V held in registers as B operands; per-row lse, rowsum and
+//     temperature from LDS, beside the step's tiles.  dV^T += dO^T P and dK^T += Q^T dZ
 //     take P and dZ straight from the registers the score MFMAs left them in.  The bias comes
 //     from the table row staged in LDS, or from the block's curves (the B operand of their MFMA
 //     is r of the block's 32 query rows; a lane reads its key's value from each of the 16 rows
