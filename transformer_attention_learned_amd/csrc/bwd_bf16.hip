@@ -317,7 +317,7 @@ struct DqLayout {
 };
 
 template <int D, int MODE, int EW>
-__global__ __launch_bounds__(256, (MODE == 0 || (MODE == 1 && D == 64)) ? 2 : 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles, int longest_first) {
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles, int longest_first) {
   using L = DqLayout<D, MODE>;
   constexpr int NC = D / 16;
   constexpr int NDB = D / 32;
