@@ -153,6 +153,13 @@ SWEEP = [
     dict(S=333, mode="table", bias_range=100, Hq=8, Hkv=2),
     dict(S=500, mode="table", window=200, bias_range=150, Hq=4, Hkv=1, temp_len=64),
     dict(S=300, mode="table", bias_range=4200, Hq=8, Hkv=1, D=64),
+    # the tile rings at their smallest: one 32-row tile per head (the dk/dv kernel's head, and
+    # with it the staged table row, changes every step), two tiles, a window narrower than a tile
+    dict(S=20, mode="table", bias_range=30, Hq=4, Hkv=1),
+    dict(S=40, mode="table", window=8, bias_range=16, Hq=8, Hkv=2),
+    dict(S=33, mode="rproj", window=5, bias_range=40, Hq=4, Hkv=1),
+    dict(S=96, mode="none", window=40, Hq=3, Hkv=1, D=64),
+    dict(S=70, mode="rproj", R=16, D=64, Hq=4, Hkv=2, temp_len=16),
 ]
 
 
