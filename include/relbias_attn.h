@@ -305,7 +305,11 @@ size_t relbias_attn_bwd_workspace_size(int B, int S, int Hq, int mode, int bias_
  *
  *   dtype       RBA_BF16 (D in {64, 128}; MFMA kernels) or RBA_F32 (D in {32, 64, 128};
  *               vector-ALU kernels, fp32 throughout); every tensor below of that dtype
- *               unless stated.
+ *               unless stated.  The bf16 kernels stage the bias parameters in LDS, which
+ *               bounds bias_range: table up to 14016 distances (D = 128) or 17088 (D = 64);
+ *               r.E up to 3456 with R = 8 and 1664 with R = 16 at D = 128 (4992 and 2432 at
+ *               D = 64; more for smaller R); past that the call returns RBA_ENOTSUP.  The fp32
+ *               kernels read the bias parameters from global memory and have no such bound.
  *   q, k, v, window, bias_range, mode, table, r, E, R, scale, temp_len, shapes:
  *               exactly as passed to relbias_attn_fwd.
  *   o           [B, S, Hq, D]: the forward's output.

@@ -251,6 +251,11 @@ def _bwd(lib, **kw):
     (dict(ws=P + 4), EINVAL, "16-byte"),
     (dict(temp_len=1), EINVAL, "temp_len"),
     (dict(B=-1), EINVAL, "B="),
+    # bias parameters staged in LDS: one distance past what the bf16 kernels hold
+    (dict(mode=1, table=P, dtable=P, bias_range=14017), ENOTSUP, "LDS"),
+    (dict(mode=1, table=P, dtable=P, bias_range=17089, D=64), ENOTSUP, "LDS"),
+    (dict(mode=2, r=P, E=P, R=16, dr=P, dE=P, bias_range=1665), ENOTSUP, "LDS"),
+    (dict(mode=2, r=P, E=P, R=8, dr=P, dE=P, bias_range=3457), ENOTSUP, "LDS"),
 ])
 def test_bwd_rejects(lib, kw, code, needle):
     assert _bwd(lib, **kw) == code
