@@ -487,18 +487,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
     const bool ib = step_inband(js);
     sacc = zero16();
     pacc = zero16();
-    bf16x8 kf = as_bf16x8(ld16(slot + ta.raddr[0])), vf = as_bf16x8(ld16(slot + TILE_B + ta.raddr[0]));
+    // fragments in groups of two head-dim chunks (four 16-byte reads), the next group's reads
+    // issued before the current group's MFMAs (scheduling barriers pin the order; left to
+    // itself the compiler keeps one fragment in flight and each MFMA waits out its read)
+    bf16x8 fk[2][2], fv[2][2];
+    auto rd = [&](int gi, int par) __attribute__((always_inline)) {
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      bf16x8 kn = kf, vn = vf;
-      if (cc + 1 < NC) {
-        kn = as_bf16x8(ld16(slot + ta.raddr[cc + 1]));
-        vn = as_bf16x8(ld16(slot + TILE_B + ta.raddr[cc + 1]));
+      for (int c = 0; c < 2; ++c) {
+        fk[par][c] = as_bf16x8(ld16(slot + ta.raddr[2 * gi + c]));
+        fv[par][c] = as_bf16x8(ld16(slot + TILE_B + ta.raddr[2 * gi + c]));
       }
-      sacc = mfma32(kf, qf[cc], sacc);
-      pacc = mfma32(vf, dof[cc], pacc);
-      kf = kn;
-      vf = vn;
+    };
+    rd(0, 0);
+#pragma unroll
+    for (int gi = 0; gi < NC / 2; ++gi) {
+      if (gi + 1 < NC / 2) rd(gi + 1, (gi + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        sacc = mfma32(fk[gi & 1][c], qf[2 * gi + c], sacc);
+        pacc = mfma32(fv[gi & 1][c], dof[2 * gi + c], pacc);
+      }
     }
     // log2-domain logits tau * (scale log2(e) q.k + log2(e) beta)
 #pragma unroll
@@ -548,8 +557,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
       for (int jj = 0; jj < 4; ++jj) w[jj] = pack_bf16x2(dz[8 * kk + 2 * jj], dz[8 * kk + 2 * jj + 1]);
       dzf[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
     }
+    bf16x8 kt[2];
+    kt[0] = ta.tfrag(slot, 0, 0);
 #pragma unroll
-    for (int x = 0; x < 2 * NDB; ++x) dqacc[x >> 1] = mfma32(ta.tfrag(slot, x >> 1, x & 1), dzf[x & 1], dqacc[x >> 1]);
+    for (int x = 0; x < 2 * NDB; ++x) {
+      // the next product's transposing reads are issued before this product (as in the
+      // scores: otherwise each MFMA waits out its own reads)
+      if (x + 1 < 2 * NDB) kt[(x + 1) & 1] = ta.tfrag(slot, (x + 1) >> 1, (x + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      dqacc[x >> 1] = mfma32(kt[x & 1], dzf[x & 1], dqacc[x >> 1]);
+    }
 
     if (MODE != 0 && step_inband(js)) {
       // skewed dZ: G^T[dist][query] (and G[query][dist]) with dist = n - m + 32 over the
@@ -870,18 +887,27 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = tb[out_row(i, lh)];
     }
-    bf16x8 qa = as_bf16x8(ld16(slot + ta.raddr[0])), da = as_bf16x8(ld16(slot + TILE_B + ta.raddr[0]));
+    // fragments in groups of two head-dim chunks (four 16-byte reads), the next group's reads
+    // issued before the current group's MFMAs (scheduling barriers pin the order; left to
+    // itself the compiler keeps one fragment in flight and each MFMA waits out its read)
+    bf16x8 fq[2][2], fd[2][2];
+    auto rd = [&](int gi, int par) __attribute__((always_inline)) {
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      bf16x8 qn = qa, dn = da;
-      if (cc + 1 < NC) {
-        qn = as_bf16x8(ld16(slot + ta.raddr[cc + 1]));
-        dn = as_bf16x8(ld16(slot + TILE_B + ta.raddr[cc + 1]));
+      for (int c = 0; c < 2; ++c) {
+        fq[par][c] = as_bf16x8(ld16(slot + ta.raddr[2 * gi + c]));
+        fd[par][c] = as_bf16x8(ld16(slot + TILE_B + ta.raddr[2 * gi + c]));
       }
-      sacc = mfma32(qa, kf[cc], sacc);
-      pacc = mfma32(da, vf[cc], pacc);
-      qa = qn;
-      da = dn;
+    };
+    rd(0, 0);
+#pragma unroll
+    for (int gi = 0; gi < NC / 2; ++gi) {
+      if (gi + 1 < NC / 2) rd(gi + 1, (gi + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        sacc = mfma32(fq[gi & 1][c], kf[2 * gi + c], sacc);
+        pacc = mfma32(fd[gi & 1][c], vf[2 * gi + c], pacc);
+      }
     }
     if (MODE == 2 && ib) {
       f32x16 clo, chi;
@@ -953,12 +979,19 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   // dV^T += dO^T P,  dK^T += Q^T dZ
   auto grads = [&](const unsigned char* slot, const bf16x8 (&pf)[2],
                    const bf16x8 (&dzf)[2]) __attribute__((always_inline)) {
+    // the next pair's transposing reads are issued before this pair's products (as in the scores)
+    bf16x8 oa[2], qt[2];
+    oa[0] = ta.tfrag(slot + TILE_B, 0, 0);
+    qt[0] = ta.tfrag(slot, 0, 0);
 #pragma unroll
     for (int x = 0; x < 2 * NDB; ++x) {
-      const bf16x8 oa = ta.tfrag(slot + TILE_B, x >> 1, x & 1);
-      const bf16x8 qt = ta.tfrag(slot, x >> 1, x & 1);
-      dvacc[x >> 1] = mfma32(oa, pf[x & 1], dvacc[x >> 1]);
-      dkacc[x >> 1] = mfma32(qt, dzf[x & 1], dkacc[x >> 1]);
+      if (x + 1 < 2 * NDB) {
+        oa[(x + 1) & 1] = ta.tfrag(slot + TILE_B, (x + 1) >> 1, (x + 1) & 1);
+        qt[(x + 1) & 1] = ta.tfrag(slot, (x + 1) >> 1, (x + 1) & 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dvacc[x >> 1] = mfma32(oa[x & 1], pf[x & 1], dvacc[x >> 1]);
+      dkacc[x >> 1] = mfma32(qt[x & 1], dzf[x & 1], dkacc[x >> 1]);
     }
   };
 
