@@ -481,91 +481,124 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
   auto step_inband = [&](int js) { return MODE != 0 && step_c(js) - 31 < Rb; };
 
   // S^T (log2 units, with the bias) and dP^T of a step
+  // S^T and dP^T of a step, and P (in place of S).  The S chain is issued first and the dP chain
+  // second, with the vector work on S (scale, bias, exp) in groups between the dP products: a wave
+  // runs alone on its SIMD, so its vector work overlaps MFMAs only when interleaved with its own.
+  // The r.E curves' MFMAs go ahead of the S chain, so that their results are ready when the
+  // curve buffer is written.  Fragments in groups of two head-dim chunks (four 16-byte reads),
+  // the next group's reads issued before the current group's MFMAs (scheduling barriers pin the
+  // order; left to itself the compiler keeps one fragment in flight and each MFMA waits out its
+  // read).
   auto scores = [&](int js, const unsigned char* slot, f32x16& sacc, f32x16& pacc,
                     const u32x4 (&eb)[2][EW / 16]) __attribute__((always_inline)) {
     const int c = step_c(js);
     const bool ib = step_inband(js);
     sacc = zero16();
     pacc = zero16();
-    // fragments in groups of two head-dim chunks (four 16-byte reads), the next group's reads
-    // issued before the current group's MFMAs (scheduling barriers pin the order; left to
-    // itself the compiler keeps one fragment in flight and each MFMA waits out its read)
-    bf16x8 fk[2][2], fv[2][2];
-    auto rd = [&](int gi, int par) __attribute__((always_inline)) {
+    f32x16 clo, chi;
+    if (MODE == 2 && ib) curve_mfma<EW>(eb, rf, clo, chi);
+    constexpr int NG = NC / 2;   // fragment groups per chain
+    bf16x8 fr[2][2];
+    // group q < NG: K chunks 2q, 2q + 1; group NG + q: the same V chunks
+    auto rd = [&](int q) __attribute__((always_inline)) {
+      const unsigned char* t = slot + (q >= NG ? TILE_B : 0);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        fk[par][c] = as_bf16x8(ld16(slot + ta.raddr[2 * gi + c]));
-        fv[par][c] = as_bf16x8(ld16(slot + TILE_B + ta.raddr[2 * gi + c]));
-      }
+      for (int u = 0; u < 2; ++u) fr[q & 1][u] = as_bf16x8(ld16(t + ta.raddr[2 * (q % NG) + u]));
     };
-    rd(0, 0);
+    rd(0);
 #pragma unroll
-    for (int gi = 0; gi < NC / 2; ++gi) {
-      if (gi + 1 < NC / 2) rd(gi + 1, (gi + 1) & 1);
+    for (int q = 0; q < NG; ++q) {
+      rd(q + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        sacc = mfma32(fk[gi & 1][c], qf[2 * gi + c], sacc);
-        pacc = mfma32(fv[gi & 1][c], dof[2 * gi + c], pacc);
-      }
+      for (int u = 0; u < 2; ++u) sacc = mfma32(fr[q & 1][u], qf[2 * q + u], sacc);
     }
-    // log2-domain logits tau * (scale log2(e) q.k + log2(e) beta)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[i] *= cq;
+    // bias of the step in units of the log2-domain logit, fetched while the S chain runs
+    float bv[16];
+    float bm = 0.f;
     if (MODE == 1 && ib) {
       // distances c + ln - m lie in [-31, Rb + 62]: inside the zero-padded row
       const float* tb = tabs + PADT + c + ln;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = fmaf(tb[-out_row(i, lh)], tq, sacc[i]);
+      for (int i = 0; i < 16; ++i) bv[i] = tb[-out_row(i, lh)];
+      bm = tq;
     }
     if (MODE == 2 && ib) {
       // curves of the wave's 32 rows over the step's distances c - 31 .. c + 32, fp32; key
       // m = 8 g + 4 lh + k of row n at distance c + n - m, entry t = 31 + n - m of row n
-      f32x16 clo, chi;
-      curve_mfma<EW>(eb, rf, clo, chi);
       curve_write(crow_w, ln, lh, clo, chi);
       wave_sync_lds();
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = fmaf(crd[27 - 8 * (i >> 2) - (i & 3)], cb, sacc[i]);
+      for (int i = 0; i < 16; ++i) bv[i] = crd[27 - 8 * (i >> 2) - (i & 3)];
       wave_sync_lds();   // the next step's writes follow these reads
+      bm = cb;
     }
-  };
-  // dS^T = P * (dP - rowsum) (the temperature factor of dZ = tau dS is applied to the accumulated
-  // dq and to the bias-gradient inputs), dQ^T += K^T dS^T, and the bias-parameter gradients
-  auto grads = [&](int js, const unsigned char* slot, const f32x16& sacc,
-                   const f32x16& pacc) __attribute__((always_inline)) {
-    const int c = step_c(js);
-    float dz[16];
-    const bool edge = (c - 31 < 0) || (W && c + 31 >= W);
-    if (edge) {
+    // dP chain; P = exp2(tau (scale log2(e) q.k + log2(e) beta) - lse2), EPG elements per group
+    constexpr int EPG = 16 / NG;
+    auto chain = [&](auto bias_c) __attribute__((always_inline)) {
+      constexpr bool BIAS = decltype(bias_c)::value;
+#pragma unroll
+      for (int q = 0; q < NG; ++q) {
+        if (q + 1 < NG) rd(NG + q + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) pacc = mfma32(fr[(NG + q) & 1][u], dof[2 * q + u], pacc);
+#pragma unroll
+        for (int e = 0; e < EPG; ++e) {
+          const int i = EPG * q + e;
+          float x = sacc[i] * cq;
+          if constexpr (BIAS) x = fmaf(bv[i], bm, x);
+          sacc[i] = fast_exp2(x - lse2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (MODE != 0 && ib) chain(std::true_type{});
+    else chain(std::false_type{});
+    if ((c - 31 < 0) || (W && c + 31 >= W)) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int d = c + ln - out_row(i, lh);
         const bool vis = (d >= 0) & ((W == 0) | (d < W));
-        const float p = fast_exp2(sacc[i] - lse2);
-        dz[i] = (vis ? p : 0.f) * (pacc[i] - dsum);
+        sacc[i] = vis ? sacc[i] : 0.f;
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dz[i] = fast_exp2(sacc[i] - lse2) * (pacc[i] - dsum);
     }
+  };
+  // dZ^T = P (dP - rowsum) and dQ^T += K^T dZ^T.  The first key chunk's dZ (output groups 0
+  // and 1) is formed first; its products then run beside the second chunk's dZ.
+  auto grads = [&](int js, const unsigned char* slot, const f32x16& pf32,
+                   const f32x16& pacc) __attribute__((always_inline)) {
+    const int c = step_c(js);
+    float dz[16];
     bf16x8 dzf[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    auto pack = [&](int kk) __attribute__((always_inline)) {
       uint32_t w[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) w[jj] = pack_bf16x2(dz[8 * kk + 2 * jj], dz[8 * kk + 2 * jj + 1]);
       dzf[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
-    }
+    };
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dz[i] = pf32[i] * (pacc[i] - dsum);
+    pack(0);
+    constexpr int EPX = 8 / NDB;   // second-chunk elements per first-chunk product
     bf16x8 kt[2];
     kt[0] = ta.tfrag(slot, 0, 0);
 #pragma unroll
     for (int x = 0; x < 2 * NDB; ++x) {
       // the next product's transposing reads are issued before this product (as in the
       // scores: otherwise each MFMA waits out its own reads)
-      if (x + 1 < 2 * NDB) kt[(x + 1) & 1] = ta.tfrag(slot, (x + 1) >> 1, (x + 1) & 1);
+      if (x + 1 < 2 * NDB) kt[(x + 1) & 1] = ta.tfrag(slot, (x + 1) % NDB, (x + 1) / NDB);
       __builtin_amdgcn_sched_barrier(0);
-      dqacc[x >> 1] = mfma32(kt[x & 1], dzf[x & 1], dqacc[x >> 1]);
+      dqacc[x % NDB] = mfma32(kt[x & 1], dzf[x / NDB], dqacc[x % NDB]);
+      if (x < NDB) {
+#pragma unroll
+        for (int e = 0; e < EPX; ++e) {
+          const int i = 8 + EPX * x + e;
+          dz[i] = pf32[i] * (pacc[i] - dsum);
+        }
+        if (x == NDB - 1) pack(1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     if (MODE != 0 && step_inband(js)) {
