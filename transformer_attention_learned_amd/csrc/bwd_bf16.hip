@@ -290,10 +290,10 @@ struct TileAddr {
 // One workgroup = 4 waves x 32 query rows of one head, walking the kv head's 32-key tiles (K and
 // V through the ring).  The forward's transposed layout: S^T = K Q^T, so each lane owns one query
 // row and its lse, rowsum and temperature are scalars; Q^T and dO^T stay in registers as B
-// operands.  Per step a wave turns the S^T and dP^T it formed at the end of the previous step
+// operands.  Per step a wave turns the P^T and dP^T it formed at the end of the previous step
 // into dZ^T, accumulates dQ^T += K^T dZ^T (K^T from transposing reads of the K tile) and the
-// bias-parameter gradients of in-band steps, and forms the next step's scores; one barrier per
-// step.  LDS besides the ring: per wave the skewed dZ buffers and the curves (r.E); the table row
+// bias-parameter gradients of in-band steps, and forms the next step's S^T, dP^T and P^T; one
+// barrier per step.  LDS besides the ring: per wave the skewed dZ buffers and the curves (r.E); the table row
 // (table mode) or E staged curve-major for the dr MFMA (r.E).
 template <int D, int MODE>
 struct DqLayout {
@@ -721,9 +721,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
 // global memory into a 3-slot LDS ring (16-byte chunks, swizzled so that both the row reads of
 // the score products and the transposing reads of the gradient products are free of bank
 // conflicts), with the step's per-row values (lse, rowsum, temperature) beside them, two steps
-// ahead.  Per step a wave turns the scores S = Q K^T and dP = dO V^T it formed at the end of the
-// previous step into P and dZ, accumulates dV^T += dO^T P and dK^T += Q^T dZ, and forms the next
-// step's scores; one barrier per step.
+// ahead.  Per step a wave turns the P and dP = dO V^T it formed at the end of the previous step
+// into dZ, accumulates dV^T += dO^T P and dK^T += Q^T dZ, and forms the next step's
+// S = Q K^T, dP and P; one barrier per step.
 template <int D>
 struct DkvLayout {
   static constexpr int ROW_B = 2 * D;                  // bytes per tile row
@@ -861,9 +861,9 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
       dma16(rd, slot + TILE_B + (NIT * wave + k) * 1024, ta.voff[k]);
     }
   };
-  // per-row values of a step, through lanes 0..31 of wave 0: loaded a step ahead and used only
-  // when stored after the next barrier (so that no wait for them stalls the step); rows past S
-  // get lse = +inf (P = 0)
+  // per-row values of a step, through lanes 0..31 of wave 0: requested with the step's tiles (two
+  // steps ahead) and stored beside them at the end of that iteration, ahead of the barrier that
+  // publishes both; rows past S get lse = +inf (P = 0)
   float rec_l = INFINITY, rec_s = 0.f;
   int rec_row = 0;
   auto rec_load = [&](Pos js) __attribute__((always_inline)) {
@@ -907,11 +907,20 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
     r_load<EW>(a, b, h, i0 + ln, lh, rx);
   };
 
-  // S (plus the bias, in units of q.k) and dP of a step
+  // S (plus the bias, in units of q.k), dP and P of a step (P in place of S).  The S chain is
+  // issued first and the dP chain second, with the vector work on S (bias, exp) in groups between
+  // the dP products: a wave runs alone on its SIMD, so its vector work overlaps MFMAs only when
+  // interleaved with its own.  The r.E curves' MFMAs go ahead of the S chain.  Per row: lse
+  // (log2 units) and c_qk * tau from the step's row values.  Fragments in groups of two head-dim
+  // chunks (four 16-byte reads), the next group's reads issued before the current group's MFMAs
+  // (scheduling barriers pin the order; left to itself the compiler keeps one fragment in flight
+  // and each MFMA waits out its read).
   auto scores = [&](Pos js, const unsigned char* slot, f32x16& sacc, f32x16& pacc, const u32x4 (&eb)[2][EW / 16],
                     const uint32_t (&rx)[8]) __attribute__((always_inline)) {
-    const int c = step_row0(js) - j0w;
+    const int i0 = step_row0(js);
+    const int c = i0 - j0w;
     const bool ib = step_inband(js);
+    const float* rp = reinterpret_cast<const float*>(slot + 2 * TILE_B);
     sacc = zero16();
     pacc = zero16();
     if (MODE == 1 && ib) {
@@ -920,111 +929,120 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = tb[out_row(i, lh)];
     }
-    // fragments in groups of two head-dim chunks (four 16-byte reads), the next group's reads
-    // issued before the current group's MFMAs (scheduling barriers pin the order; left to
-    // itself the compiler keeps one fragment in flight and each MFMA waits out its read)
-    bf16x8 fq[2][2], fd[2][2];
-    auto rd = [&](int gi, int par) __attribute__((always_inline)) {
+    f32x16 clo, chi;
+    if (MODE == 2 && ib) curve_mfma<EW>(eb, r_pack<EW>(a, i0 + ln, lh, rx), clo, chi);
+    constexpr int NG = NC / 2;   // fragment groups per chain
+    bf16x8 fr[2][2];
+    // group q < NG: q chunks 2q, 2q + 1; group NG + q: the same dout chunks
+    auto rd = [&](int q) __attribute__((always_inline)) {
+      const unsigned char* t = slot + (q >= NG ? TILE_B : 0);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        fq[par][c] = as_bf16x8(ld16(slot + ta.raddr[2 * gi + c]));
-        fd[par][c] = as_bf16x8(ld16(slot + TILE_B + ta.raddr[2 * gi + c]));
-      }
+      for (int u = 0; u < 2; ++u) fr[q & 1][u] = as_bf16x8(ld16(t + ta.raddr[2 * (q % NG) + u]));
     };
-    rd(0, 0);
+    rd(0);
 #pragma unroll
-    for (int gi = 0; gi < NC / 2; ++gi) {
-      if (gi + 1 < NC / 2) rd(gi + 1, (gi + 1) & 1);
+    for (int q = 0; q < NG; ++q) {
+      rd(q + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        sacc = mfma32(fq[gi & 1][c], kf[2 * gi + c], sacc);
-        pacc = mfma32(fd[gi & 1][c], vf[2 * gi + c], pacc);
-      }
+      for (int u = 0; u < 2; ++u) sacc = mfma32(fr[q & 1][u], kf[2 * q + u], sacc);
+      // the curves are written halfway through the S chain, once their MFMAs have finished
+      if (MODE == 2 && q == NG / 2 - 1 && ib) curve_write(cbuf + CURVE_ROWS_KV * ln, ln, lh, clo, chi);
     }
+    // rows 8 g + 4 lh .. + 3 of element group g
+    f32x4 l4[4], c4[4];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      l4[g4] = *reinterpret_cast<const f32x4*>(rp + 8 * g4 + 4 * lh);
+      c4[g4] = *reinterpret_cast<const f32x4*>(rp + 2 * TROWS + 8 * g4 + 4 * lh);
+    }
+    float bv[16];
     if (MODE == 2 && ib) {
-      f32x16 clo, chi;
-      curve_mfma<EW>(eb, r_pack<EW>(a, step_row0(js) + ln, lh, rx), clo, chi);
-      curve_write(cbuf + CURVE_ROWS_KV * ln, ln, lh, clo, chi);
       wave_sync_lds();
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = fmaf(crd[320 * (i >> 2) + 41 * (i & 3)], inv_scale, sacc[i]);
+      for (int i = 0; i < 16; ++i) bv[i] = crd[320 * (i >> 2) + 41 * (i & 3)];
       wave_sync_lds();   // the next step's writes follow these reads
     }
-  };
-  // P and dZ = tau * P * (dP - rowsum), rounded to bf16 as the B operands of the gradient
-  // products; per row: lse (log2 units), rowsum, c_qk * tau, tau.  Interior and edge steps get
-  // separate loops so that no branch sits inside the element loop.
-  auto probs = [&](Pos js, const unsigned char* slot, f32x16& sacc, f32x16& pacc, bf16x8 (&pf)[2],
-                   bf16x8 (&dzf)[2]) __attribute__((always_inline)) {
-    const float* rp = reinterpret_cast<const float*>(slot + 2 * TILE_B);
+    constexpr int EPG = 16 / NG;   // elements per dP group
+    auto chain = [&](auto bias_c) __attribute__((always_inline)) {
+      constexpr bool BIAS = decltype(bias_c)::value;
+#pragma unroll
+      for (int q = 0; q < NG; ++q) {
+        if (q + 1 < NG) rd(NG + q + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) pacc = mfma32(fr[(NG + q) & 1][u], vf[2 * q + u], pacc);
+#pragma unroll
+        for (int e = 0; e < EPG; ++e) {
+          const int i = EPG * q + e;
+          float x = sacc[i];
+          if constexpr (BIAS) x = fmaf(bv[i], inv_scale, x);
+          sacc[i] = fast_exp2(fmaf(x, c4[i >> 2][i & 3], -l4[i >> 2][i & 3]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (MODE == 2 && ib) chain(std::true_type{});
+    else chain(std::false_type{});
     if (step_edge(js)) {
-      const int i0 = step_row0(js);
-      const int c = i0 - j0w;
       const int wlim = W ? W : 0x7fffffff;
       const int mlim = S - i0;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int m0 = 8 * g4 + 4 * lh;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(rp + m0);
-        const f32x4 s4 = *reinterpret_cast<const f32x4*>(rp + TROWS + m0);
-        const f32x4 c4 = *reinterpret_cast<const f32x4*>(rp + 2 * TROWS + m0);
-        const f32x4 t4 = *reinterpret_cast<const f32x4*>(rp + 3 * TROWS + m0);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = 4 * g4 + u;
-          const int d = c + m0 + u - ln;
-          const float p = fast_exp2(fmaf(sacc[i], c4[u], -l4[u]));
-          const float pm = ((d >= 0) & (d < wlim) & (m0 + u < mlim)) ? p : 0.f;
-          pacc[i] = pm * (pacc[i] - s4[u]) * t4[u];
-          sacc[i] = pm;
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int m = out_row(i, lh);
+        const int d = c + m - ln;
+        sacc[i] = ((d >= 0) & (d < wlim) & (m < mlim)) ? sacc[i] : 0.f;
       }
-    } else {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int m0 = 8 * g4 + 4 * lh;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(rp + m0);
-        const f32x4 s4 = *reinterpret_cast<const f32x4*>(rp + TROWS + m0);
-        const f32x4 c4 = *reinterpret_cast<const f32x4*>(rp + 2 * TROWS + m0);
-        const f32x4 t4 = *reinterpret_cast<const f32x4*>(rp + 3 * TROWS + m0);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = 4 * g4 + u;
-          const float p = fast_exp2(fmaf(sacc[i], c4[u], -l4[u]));
-          pacc[i] = p * (pacc[i] - s4[u]) * t4[u];
-          sacc[i] = p;
-        }
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      uint32_t w[4], x[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        w[jj] = pack_bf16x2(sacc[8 * kk + 2 * jj], sacc[8 * kk + 2 * jj + 1]);
-        x[jj] = pack_bf16x2(pacc[8 * kk + 2 * jj], pacc[8 * kk + 2 * jj + 1]);
-      }
-      pf[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
-      dzf[kk] = as_bf16x8(u32x4{x[0], x[1], x[2], x[3]});
     }
   };
-  // dV^T += dO^T P,  dK^T += Q^T dZ
-  auto grads = [&](const unsigned char* slot, const bf16x8 (&pf)[2],
-                   const bf16x8 (&dzf)[2]) __attribute__((always_inline)) {
-    // the next pair's transposing reads are issued before this pair's products (as in the scores)
-    bf16x8 oa[2], qt[2];
-    oa[0] = ta.tfrag(slot + TILE_B, 0, 0);
-    qt[0] = ta.tfrag(slot, 0, 0);
+  // dZ = tau * P * (dP - rowsum) and the gradient products dV^T += dO^T P, dK^T += Q^T dZ, with
+  // P and dZ rounded to bf16 as their B operands: the dV products (P alone) run beside the dZ
+  // work, then the dK products.  The next product's transposing reads are issued before this
+  // product (as in the scores).
+  auto grads = [&](const unsigned char* slot, const f32x16& pr, f32x16& pacc) __attribute__((always_inline)) {
+    const float* rp = reinterpret_cast<const float*>(slot + 2 * TILE_B);
+    bf16x8 pf[2], dzf[2];
+    auto pack = [&](const f32x16& v, bf16x8 (&f)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int x = 0; x < 2 * NDB; ++x) {
-      if (x + 1 < 2 * NDB) {
-        oa[(x + 1) & 1] = ta.tfrag(slot + TILE_B, (x + 1) >> 1, (x + 1) & 1);
-        qt[(x + 1) & 1] = ta.tfrag(slot, (x + 1) >> 1, (x + 1) & 1);
+      for (int kk = 0; kk < 2; ++kk) {
+        uint32_t w[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) w[jj] = pack_bf16x2(v[8 * kk + 2 * jj], v[8 * kk + 2 * jj + 1]);
+        f[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+      }
+    };
+    pack(pr, pf);
+    f32x4 s4[4], t4[4];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      s4[g4] = *reinterpret_cast<const f32x4*>(rp + TROWS + 8 * g4 + 4 * lh);
+      t4[g4] = *reinterpret_cast<const f32x4*>(rp + 3 * TROWS + 8 * g4 + 4 * lh);
+    }
+    constexpr int NX = 2 * NDB;    // products per gradient
+    constexpr int EPX = 16 / NX;   // dZ elements per dV product
+    // product y < NX: dV, head-dim block y / 2 over query rows 16 (y % 2) ..; then dK
+    auto tr = [&](int y) __attribute__((always_inline)) {
+      return y < NX ? ta.tfrag(slot + TILE_B, y >> 1, y & 1) : ta.tfrag(slot, (y - NX) >> 1, y & 1);
+    };
+    bf16x8 fa[2];
+    fa[0] = tr(0);
+#pragma unroll
+    for (int y = 0; y < 2 * NX; ++y) {
+      if (y + 1 < 2 * NX) fa[(y + 1) & 1] = tr(y + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (y < NX) {
+        dvacc[y >> 1] = mfma32(fa[y & 1], pf[y & 1], dvacc[y >> 1]);
+#pragma unroll
+        for (int e = 0; e < EPX; ++e) {
+          const int i = EPX * y + e;
+          pacc[i] = pr[i] * (pacc[i] - s4[i >> 2][i & 3]) * t4[i >> 2][i & 3];
+        }
+        if (y == NX - 1) pack(pacc, dzf);
+      } else {
+        const int x = y - NX;
+        dkacc[x >> 1] = mfma32(fa[y & 1], dzf[x & 1], dkacc[x >> 1]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      dvacc[x >> 1] = mfma32(oa[x & 1], pf[x & 1], dvacc[x >> 1]);
-      dkacc[x >> 1] = mfma32(qt[x & 1], dzf[x & 1], dkacc[x >> 1]);
     }
   };
 
@@ -1040,7 +1058,10 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   dma_tile(p0, smem);
   if (nsteps > 1) dma_tile(p1, smem + SLOT_B);
   rec_store(smem);
-  if (nsteps > 1) rec_load(p1);
+  if (nsteps > 1) {
+    rec_load(p1);
+    rec_store(smem + SLOT_B);
+  }
   u32x4 eb[2][EW / 16];
   uint32_t rx[8];
   if (MODE == 2 && step_on(p0) && step_inband(p0)) e_load(p0, eb, rx);
@@ -1049,33 +1070,29 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   f32x16 sa, pa;
   if (step_on(p0)) scores(p0, smem, sa, pa, eb, rx);
 
-  // step js: P, dZ and the gradient products of js (its row values and tiles in slot js % 3), then
-  // the scores of js + 1 (slot (js + 1) % 3) into the same registers; the tiles of js + 2 go to
-  // the slot js - 1 used.  The slots are passed as restrict pointers: the compiler then knows
-  // that the direct loads into ds do not alias the reads of cs and ns and adds no wait for them.
-  auto iteration_body = [&](const unsigned char* __restrict__ cs, unsigned char* __restrict__ ns,
+  // step js: dZ and the gradient products of js (its row values and tiles in slot js % 3, P and
+  // dP in registers), then the scores and P of js + 1 (slot (js + 1) % 3) into the same
+  // registers; the tiles and row values of js + 2 go to the slot js - 1 used.  The slots are
+  // passed as restrict pointers: the compiler then knows that the direct loads into ds do not
+  // alias the reads of cs and ns and adds no wait for them.
+  auto iteration_body = [&](const unsigned char* __restrict__ cs, const unsigned char* __restrict__ ns,
                             unsigned char* __restrict__ ds, auto inner_c) __attribute__((always_inline)) {
     constexpr bool INNER = decltype(inner_c)::value;   // step js + 2 exists
+    const bool more = INNER || p2.hh < G;
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    rec_store(ns);
     u32x4 e[2][EW / 16];
     uint32_t x[8];
     if (MODE == 2 && step_on(p1) && step_inband(p1)) e_load(p1, e, x);
-    if (MODE == 1 && (INNER || p2.hh < G) && p2.t == 0) stage_table(p2.hh);
-    // the bias operands are requested before the tiles of js + 2, so that the waits for them
-    // (vector-memory counts retire in order) do not wait for the tiles
+    if (MODE == 1 && more && p2.t == 0) stage_table(p2.hh);
+    if (more) rec_load(p2);
+    // the bias operands and row values are requested before the tiles of js + 2, so that the
+    // waits for them (vector-memory counts retire in order) do not wait for the tiles
     __builtin_amdgcn_sched_barrier(0);
-    if (INNER || p2.hh < G) {
-      dma_tile(p2, ds);
-      rec_load(p2);
-    }
-    if (step_on(p0)) {
-      bf16x8 pf[2], dzf[2];
-      probs(p0, cs, sa, pa, pf, dzf);
-      grads(cs, pf, dzf);
-    }
+    if (more) dma_tile(p2, ds);
+    if (step_on(p0)) grads(cs, sa, pa);
     if (step_on(p1)) scores(p1, ns, sa, pa, e, x);
+    if (more) rec_store(ds);
     p0 = p1;
     p1 = p2;
     p2 = pos_next(p2);
@@ -1093,13 +1110,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
     iteration(2, true_t{});
   }
   for (; js + 1 < nsteps; ++js) iteration(js % NBUF, false_t{});
-  if (nsteps > 1) __syncthreads();   // the last step's row values, stored after the previous barrier
-  if (step_on(p0)) {
-    const unsigned char* cs = smem + (js % NBUF) * SLOT_B;
-    bf16x8 pf[2], dzf[2];
-    probs(p0, cs, sa, pa, pf, dzf);
-    grads(cs, pf, dzf);
-  }
+  if (step_on(p0)) grads(smem + (js % NBUF) * SLOT_B, sa, pa);
 
   if (!wave_live || !key_ok) return;
   uint16_t* dkp = a.dk + koff;
