@@ -210,6 +210,27 @@ def test_bwd_deterministic_dq_dk_dv():
         assert torch.equal(g1[n], g2[n]), n
 
 
+@pytest.mark.parametrize("R,D", [(8, 128), (16, 64)])
+def test_bwd_r_load_paths(R, D):
+    """With R = 8 or 16 and r 16-byte aligned, a lane reads its row's 8 features of r in one
+    16-byte load; an r two bytes past such a boundary takes the 2-byte loads.  The features,
+    hence the gradients, are the same either way (dE up to the order of its atomics)."""
+    w = small(S=300, R=R, D=D, window=128, bias_range=160, Hq=4, Hkv=2)
+    inp = make_inputs(w, device="cuda")
+    dout = _dout(w, inp["q"])
+    r = inp["r"]
+    assert r.data_ptr() % 16 == 0
+    buf = torch.empty(r.numel() + 8, dtype=r.dtype, device=r.device)
+    r_off = buf[1:1 + r.numel()].view(r.shape)
+    r_off.copy_(r)
+    assert r_off.data_ptr() % 16 == 2
+    g0 = run_bwd(w, inp, dout)
+    g1 = run_bwd(w, dict(inp, r=r_off), dout)
+    for n in ("dq", "dk", "dv", "dr"):
+        assert torch.equal(g0[n], g1[n]), n
+    torch.testing.assert_close(g0["dE"], g1["dE"], rtol=1e-5, atol=1e-6)
+
+
 # fp32 backward: the vector-ALU kernels against the same oracle at the fp32 bar
 F32_SWEEP = [
     dict(S=1), dict(S=33), dict(S=200), dict(S=200, mode="none"),

@@ -92,34 +92,52 @@ typedef __attribute__((address_space(3))) float lds_float;
 
 // r fragment (B operand) of query row `row`: EW = 16: features 0..7 in both lane halves;
 // EW = 32: features 8 lh .. 8 lh + 7; zero past R and for rows at or past S.
-// Split into the loads (unconditional, inside the row: the feature index is clamped, so that no
-// load sits in a branch of its own and is waited for before the next one is issued) and the
-// packing, which masks the features past R and rows at or past S.
+// Split into the loads and the packing, which masks the features past R and rows at or past S.
+// With R = EW / 2 and r 16-byte aligned (rvec) a lane's 8 features are one 16-byte load, kept
+// packed in pairs in x[0..3]; otherwise 8 two-byte loads, unconditional and inside the row (the
+// feature index is clamped, so that no load sits in a branch of its own and is waited for
+// before the next one is issued).
 template <int EW>
-__device__ __forceinline__ void r_load(const BwdArgs& a, int b, int h, int row, int lh, uint32_t (&x)[8]) {
-  const int f0 = (EW == 32) ? 8 * lh : 0;
-  const uint16_t* rp = a.r + ((static_cast<size_t>(b) * a.S + (row < a.S ? row : 0)) * a.Hq + h) * a.R;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = rp[min(f0 + e, a.R - 1)];
+__device__ __forceinline__ bool r_vec(const BwdArgs& a) {
+  return a.R == EW / 2 && (reinterpret_cast<uintptr_t>(a.r) & 15) == 0;
 }
 template <int EW>
-__device__ __forceinline__ bf16x8 r_pack(const BwdArgs& a, int row, int lh, const uint32_t (&x)[8]) {
+__device__ __forceinline__ void r_load(const BwdArgs& a, bool rvec, int b, int h, int row, int lh,
+                                       uint32_t (&x)[8]) {
+  const int f0 = (EW == 32) ? 8 * lh : 0;
+  const uint16_t* rp = a.r + ((static_cast<size_t>(b) * a.S + (row < a.S ? row : 0)) * a.Hq + h) * a.R;
+  if (rvec) {
+    const u32x4 v = ld16(rp + f0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = v[k];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = rp[min(f0 + e, a.R - 1)];
+  }
+}
+template <int EW>
+__device__ __forceinline__ bf16x8 r_pack(const BwdArgs& a, bool rvec, int row, int lh, const uint32_t (&x)[8]) {
   const int f0 = (EW == 32) ? 8 * lh : 0;
   uint32_t w[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
-    const int f = f0 + 2 * jj;
-    const uint32_t lo = (row < a.S && f < a.R) ? x[2 * jj] : 0u;
-    const uint32_t hi = (row < a.S && f + 1 < a.R) ? x[2 * jj + 1] : 0u;
-    w[jj] = lo | (hi << 16);
+    if (rvec) {
+      w[jj] = row < a.S ? x[jj] : 0u;
+    } else {
+      const int f = f0 + 2 * jj;
+      const uint32_t lo = (row < a.S && f < a.R) ? x[2 * jj] : 0u;
+      const uint32_t hi = (row < a.S && f + 1 < a.R) ? x[2 * jj + 1] : 0u;
+      w[jj] = lo | (hi << 16);
+    }
   }
   return as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
 }
 template <int EW>
 __device__ __forceinline__ bf16x8 r_frag(const BwdArgs& a, int b, int h, int row, int lh) {
   uint32_t x[8];
-  r_load<EW>(a, b, h, row, lh, x);
-  return r_pack<EW>(a, row, lh, x);
+  const bool rvec = r_vec<EW>(a);
+  r_load<EW>(a, rvec, b, h, row, lh, x);
+  return r_pack<EW>(a, rvec, row, lh, x);
 }
 
 // E rows of a block whose distances are c - 31 + l (block 0) and c + 1 + l (block 1) for the
@@ -900,11 +918,12 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   };
 
   const uint16_t* e2b = (MODE == 2) ? a.e2 + kE2Pad * EW : nullptr;
+  const bool rvec = r_vec<EW>(a);
   auto e_load = [&](Pos js, u32x4 (&eb)[2][EW / 16], uint32_t (&rx)[8]) __attribute__((always_inline)) {
     const int h = hkv * G + step_head(js);
     const int i0 = step_row0(js);
     e_rows<EW>(e2b + static_cast<size_t>(a.e_hs ? h : 0) * (Rb + 2 * kE2Pad + 1) * EW, i0 - j0w, ln, lh, eb);
-    r_load<EW>(a, b, h, i0 + ln, lh, rx);
+    r_load<EW>(a, rvec, b, h, i0 + ln, lh, rx);
   };
 
   // S (plus the bias, in units of q.k), dP and P of a step (P in place of S).  The S chain is
@@ -930,7 +949,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
       for (int i = 0; i < 16; ++i) sacc[i] = tb[out_row(i, lh)];
     }
     f32x16 clo, chi;
-    if (MODE == 2 && ib) curve_mfma<EW>(eb, r_pack<EW>(a, i0 + ln, lh, rx), clo, chi);
+    if (MODE == 2 && ib) curve_mfma<EW>(eb, r_pack<EW>(a, rvec, i0 + ln, lh, rx), clo, chi);
     constexpr int NG = NC / 2;   // fragment groups per chain
     bf16x8 fr[2][2];
     // group q < NG: q chunks 2q, 2q + 1; group NG + q: the same dout chunks
