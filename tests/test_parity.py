@@ -327,6 +327,17 @@ def test_decode_small(kw):
     check_decode(w, kv_len)
 
 
+# Waves of five 32-row tiles (32 sequences x 8 kv heads make the split give each wave 160 rows)
+# with the bias range covering the last seven waves: on contiguous caches the curves of a wave's
+# first four tiles are formed up front and those of later in-band tiles one tile ahead, and a
+# wave's last tile is ragged.  Checked on a few sequences.
+@pytest.mark.parametrize("mode", ["rproj", "table"])
+def test_decode_late_curves(mode):
+    w = Workload(name=f"dec_late_{mode}", kind="decode", dtype="bf16", B=32, Hq=16, Hkv=8, D=128,
+                 S=4200, window=0, bias_range=1024, mode=mode, R=8, seed=21)
+    check_decode(w, 4100, batches=[0, 17, 31])
+
+
 @pytest.mark.parametrize("kw", [dict(mode="rproj", window=0), dict(mode="table", window=20),
                                 dict(mode="rproj_shared", window=40, logit_scale="inv_d"),
                                 dict(mode="rproj", window=0, temp_len=16)],

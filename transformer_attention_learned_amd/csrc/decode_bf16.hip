@@ -20,6 +20,7 @@
 //     workgroup writes an unnormalised partial that a second kernel combines.
 
 #include <mutex>
+#include <type_traits>
 
 #include "relbias_attn.h"
 #include "rba_device.h"
@@ -446,7 +447,13 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
 // (a quarter of the registers of bf16 rows) and are widened to bf16 where the MFMAs use them.
 // A lane's K fragment then covers head dims (D / 4) g + 8 c .. + 7 (one 16-byte load per row at
 // D = 128, 8 bytes at D = 64, and a single scale), so the query fragments use the same dims.
-template <int D, int MODE, int RMAX, bool FP4>
+// CONTIG: contiguous bf16 caches.  Loads complete in issue order, so a wait for any load also
+// waits for every tile requested before it; here the tile loop keeps the next tile in flight
+// during each wait: every K / V load is issued unconditionally (buffer resources that read zeros
+// past the wave's last row, so the compiler counts the loads in flight exactly), and the bias
+// curves of the wave's first four tiles (every tile of a 512-row window) are formed up front
+// from inputs requested ahead of the first tiles, so that no curve load follows a tile.
+template <int D, int MODE, int RMAX, bool FP4, bool CONTIG = false>
 __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curve_off) {
   constexpr int VST = TK + 8;          // V^T row stride (bf16)
   constexpr int NC = D / 32;           // K = 32 chunks of the head dim
@@ -457,7 +464,7 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile bases stay scalar
   const int n16 = lane & 15;           // head column
   const int g = lane >> 4;             // row group
   const int split = blockIdx.x;
@@ -467,7 +474,7 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
   const bool col_live = n16 < G;
 
   const size_t kv_row = static_cast<size_t>(a.Hkv) * D;
-  const bool paged = a.block_table != nullptr;
+  const bool paged = !CONTIG && a.block_table != nullptr;
   const int kv_len = paged ? min(max(a.kv_lens[b], 0), a.kv_len) : a.kv_len;
   const int key_begin = paged ? (a.window ? max(0, kv_len - a.window) : 0) : a.key_begin;
   // context-length temperature of this sequence's query, on q.k and bias alike
@@ -502,6 +509,30 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
   const uint8_t* ksp = FP4 ? a.k_scale + (cbatch * a.Hkv + hkv) * SB : nullptr;
   const uint8_t* vsp = FP4 ? a.v_scale + (cbatch * a.Hkv + hkv) * SB : nullptr;
   auto load_tile = [&](int set, int tk0) {
+    if constexpr (CONTIG) {
+      // rows tk0 .. tk0 + 31 through buffer resources over the tile's existing rows: the
+      // resource ends at the last row's 2 D bytes, so every chunk of a row at or past w_end
+      // reads as zeros (a row is row_b >= 2 D bytes from the next), and a tile wholly past
+      // w_end has an empty resource (no memory access)
+      const int row_b = a.Hkv * D * 2;
+      const int left = w_end - tk0;
+      const int nrows = left <= 0 ? 0 : (left < TK ? left : TK);
+      const int nbytes = nrows > 0 ? (nrows - 1) * row_b + D * 2 : 0;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + static_cast<size_t>(tk0) * kv_row, nbytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + static_cast<size_t>(tk0) * kv_row, nbytes);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) kreg[set][kb][c] = buf_ld16(rk, (16 * kb + n16) * row_b + 2 * (8 * g + 32 * c));
+#pragma unroll
+      for (int it = 0; it < NVI; ++it) {
+        const int kg = lane & 7;
+        const int dg = v_item_dg<FP4, NVI>(lane, it);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) vreg[set][it][s4] = buf_ld16(rv, (4 * kg + s4) * row_b + 16 * dg);
+      }
+      return;
+    }
     // K rows tk0 + 16 kb + (l % 16); paged: one table read per lane and row block, and lane
     // l < 32 keeps the pool row of cache row tk0 + l for the V loads below
     int prow32 = 0;
@@ -578,27 +609,17 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
     }
   };
 
-  bf16x8 qf[NC];
-  {
-    const uint16_t* qp = a.q + (static_cast<size_t>(b) * a.Hq + hkv * G + (col_live ? n16 : 0)) * D + (FP4 ? EPL * g : 8 * g);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (col_live) v = ld16(qp + (FP4 ? 8 * c : 32 * c));
-      qf[c] = as_bf16x8(v);
-    }
-  }
-  if (ntiles > 0) load_tile(0, w_beg);
-  if (ntiles > 1) load_tile(1, w_beg + TK);
-
-  // ---- bias curves per tile, as in the 32x32 kernel ---------------------------------------
+  // ---- bias curves per tile, as in the 32x32 kernel -----------------------------------------
   float* rs = reinterpret_cast<float*>(smem + curve_off);                  // [G][R] (r.E)
-  float* cbuf = rs + (MODE == 2 ? G * a.R : 0) + wave * 2 * G * TK;         // [2][G][TK]
-  if (MODE == 2) {
+  // per wave a ring of tile curves [NSLOT][G][TK] (CONTIG: the up-front curves of the first
+  // NSLOT tiles, then the later in-band tiles in turn)
+  constexpr int NSLOT = CONTIG ? 4 : 2;
+  float* cbuf = rs + (MODE == 2 ? G * a.R : 0) + wave * NSLOT * G * TK;
+  auto stage_r = [&]() {
     for (int i = tid; i < G * a.R; i += 256)
       rs[i] = bf16_to_f32(a.r[(static_cast<size_t>(b) * a.Hq + hkv * G) * a.R + i]);
     __syncthreads();
-  }
+  };
   const int n_items = G * TK;
   auto tile_in_band = [&](int tk0) { return MODE != 0 && qpos - (tk0 + TK - 1) < a.bias_range; };
   auto item_geo = [&](int tk0, int item, int& n, int& d, bool& live) {
@@ -624,7 +645,38 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
       }
     }
   };
-  auto finish_items = [&](int tk0, int base, const float (&e)[2][RMAX], float* dst) {
+  // CONTIG: the same values through one buffer resource over the group's table rows or E
+  // slabs (heads hkv G .. hkv G + G - 1): a lane's offset is its item's (head, distance), the
+  // feature's offset is scalar (clamped to feature R - 1), and an item that is not live reads
+  // zeros from an offset past the resource, so no load sits behind a per-lane branch.  The
+  // launcher guarantees that the resource's extent fits 31 bits.
+  const __amdgpu_buffer_rsrc_t e_rsrc = [&]() {
+    if (MODE == 1)
+      return make_rsrc(a.table + static_cast<size_t>(hkv) * G * a.bias_range, G * a.bias_range * 4);
+    const long long hs = a.e_hs;
+    return make_rsrc(a.E + static_cast<size_t>(hkv) * G * hs,
+                     static_cast<int>(((G - 1) * hs + static_cast<long long>(a.R) * a.bias_range) * 4));
+  }();
+  auto fetch_items_buf = [&](int tk0, int base, float (&e)[2][RMAX]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      int n, d;
+      bool live;
+      item_geo(tk0, base + lane + 64 * u, n, d, live);
+      const int voff = live ? 4 * static_cast<int>((MODE == 1 ? static_cast<long long>(a.bias_range) : a.e_hs) * n + d)
+                            : 0x7FFFFFF0;
+      if (MODE == 1) {
+        e[u][0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(e_rsrc, voff, 0, 0));
+      } else {
+#pragma unroll
+        for (int f = 0; f < RMAX; ++f) {
+          const int soff = 4 * (f < a.R ? f : a.R - 1) * a.bias_range;
+          e[u][f] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(e_rsrc, voff, soff, 0));
+        }
+      }
+    }
+  };
+  auto finish_items = [&](int tk0, int base, const float (&e)[2][RMAX], float* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int item = base + lane + 64 * u;
@@ -643,14 +695,85 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
     }
   };
   // (the inputs are fetched where they are used: registers go to the tiles in flight)
-  auto curve_tile = [&](int tk0, float* dst) {
-    for (int base = 0; base < n_items; base += 128) {
+  // CONTIG: the same with a static trip count (n_items <= 256: G <= 8): a loop of unknown trip
+  // count around loads makes the compiler's counts of loads in flight unknown after it, and
+  // every later wait for a tile would then wait for all loads
+  auto curve_tile_static = [&](int tk0, float* dst, int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (k >= k0 && 128 * k < n_items) {
+        float e[2][RMAX];
+        fetch_items_buf(tk0, 128 * k, e);
+        finish_items(tk0, 128 * k, e, dst);
+      }
+    }
+  };
+  auto curve_tile = [&](int tk0, float* dst, int base0) {
+    for (int base = base0; base < n_items; base += 128) {
       float e[2][RMAX];
       fetch_items(tk0, base, e);
       finish_items(tk0, base, e, dst);
     }
   };
-  if (ntiles > 0 && tile_in_band(w_beg)) curve_tile(w_beg, cbuf);
+  bf16x8 qf[NC];
+  if constexpr (CONTIG) {
+    // r (one entry per thread, G R <= 128) and the curve inputs of the wave's first NPRE tiles
+    // (their first 128 items each) are requested first, while no tile registers are live, then
+    // the query rows and the first two tiles; the curves are formed while those are in flight,
+    // and the tile loop then waits for no curve input of these tiles
+    constexpr int NPRE = (MODE == 2 && RMAX > 8) ? 2 : NSLOT;
+    uint32_t r_raw = 0;
+    if (MODE == 2) {
+      const __amdgpu_buffer_rsrc_t r_rsrc =
+          make_rsrc(a.r + (static_cast<size_t>(b) * a.Hq + hkv * G) * a.R, G * a.R * 2);
+      r_raw = __builtin_amdgcn_raw_buffer_load_b16(r_rsrc, tid < G * a.R ? 2 * tid : 0x7FFFFFF0, 0, 0);
+    }
+    float ep[NPRE][2][RMAX];
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i)
+      if (i < ntiles && tile_in_band(w_beg + i * TK)) fetch_items_buf(w_beg + i * TK, 0, ep[i]);
+  {
+    const uint16_t* qp = a.q + (static_cast<size_t>(b) * a.Hq + hkv * G + (col_live ? n16 : 0)) * D + (FP4 ? EPL * g : 8 * g);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (col_live) v = ld16(qp + (FP4 ? 8 * c : 32 * c));
+      qf[c] = as_bf16x8(v);
+    }
+  }
+    load_tile(0, w_beg);
+    load_tile(1, w_beg + TK);
+    if (MODE == 2) {
+      if (tid < G * a.R) rs[tid] = bf16_to_f32(static_cast<uint16_t>(r_raw));
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < NSLOT; ++i) {
+      if (i < ntiles && tile_in_band(w_beg + i * TK)) {
+        float* dst = cbuf + i * G * TK;
+        if (i < NPRE) {
+          finish_items(w_beg + i * TK, 0, ep[i < NPRE ? i : 0], dst);
+          curve_tile_static(w_beg + i * TK, dst, 1);
+        } else {
+          curve_tile_static(w_beg + i * TK, dst, 0);
+        }
+      }
+    }
+  } else {
+  {
+    const uint16_t* qp = a.q + (static_cast<size_t>(b) * a.Hq + hkv * G + (col_live ? n16 : 0)) * D + (FP4 ? EPL * g : 8 * g);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (col_live) v = ld16(qp + (FP4 ? 8 * c : 32 * c));
+      qf[c] = as_bf16x8(v);
+    }
+  }
+    if (ntiles > 0) load_tile(0, w_beg);
+    if (ntiles > 1) load_tile(1, w_beg + TK);
+    if (MODE == 2) stage_r();
+    if (ntiles > 0 && tile_in_band(w_beg)) curve_tile(w_beg, cbuf, 0);
+  }
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 oacc[NDB];
@@ -662,7 +785,10 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
   // V^T position of tile row k: 8 (k % 16 / 4) + 4 (k / 16) + k % 4
   auto vt_pos16 = [](int k) { return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3); };
 
-  auto process = [&](int t, int set) {
+  // LATE: this call may form the next tile's curve (always outside CONTIG; in CONTIG only in
+  // the second phase of the tile loop below)
+  auto process = [&](int t, int set, auto late_c) {
+    constexpr bool LATE = decltype(late_c)::value;
     const int tk0 = w_beg + t * TK;
     // S^T of the two 16-row blocks
     f32x4 sacc[2];
@@ -711,12 +837,16 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
         }
       }
     }
-    // this set's registers are free: the tile two ahead goes in flight
-    if (t + 2 < ntiles) load_tile(set, tk0 + 2 * TK);
+    // this set's registers are free: the tile two ahead goes in flight (CONTIG: always issued,
+    // empty past the wave's rows)
+    if constexpr (CONTIG)
+      load_tile(set, tk0 + 2 * TK);
+    else if (t + 2 < ntiles)
+      load_tile(set, tk0 + 2 * TK);
 
     // logits (log2 units), bias of in-band rows, mask beyond this wave's rows
     const bool in_band = tile_in_band(tk0);
-    const float* cv = cbuf + (t & 1) * G * TK + (col_live ? n16 : 0) * TK + 4 * g;
+    const float* cv = cbuf + (t & (NSLOT - 1)) * G * TK + (col_live ? n16 : 0) * TK + 4 * g;
     float mx = NEG_INF;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -759,11 +889,51 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
       const bf16x8 vf = as_bf16x8(ld16(vt + (16 * db + n16) * VST + 8 * g));
       oacc[db] = mfma16(vf, pf, oacc[db]);
     }
-    if (t + 1 < ntiles && tile_in_band(tk0 + TK)) curve_tile(tk0 + TK, cbuf + ((t + 1) & 1) * G * TK);
+    // the curve of the next tile (CONTIG: only past the up-front ones; its inputs then wait
+    // behind the tile just requested)
+    if (LATE && (!CONTIG || t + 1 >= NSLOT) && t + 1 < ntiles && tile_in_band(tk0 + TK)) {
+      float* dst = cbuf + ((t + 1) & (NSLOT - 1)) * G * TK;
+      if constexpr (CONTIG)
+        curve_tile_static(tk0 + TK, dst, 0);
+      else
+        curve_tile(tk0 + TK, dst, 0);
+    }
   };
-  for (int t = 0; t < ntiles; t += 2) {   // two register sets: the unroll keeps their indices static
-    process(t, 0);
-    if (t + 1 < ntiles) process(t + 1, 1);
+  // two register sets: the unroll keeps their indices static
+  using late_t = std::integral_constant<bool, true>;
+  using early_t = std::integral_constant<bool, false>;
+  if constexpr (CONTIG) {
+    // Phase 1, tiles [0, t1): every curve they need was formed up front (tiles < NSLOT) or
+    // none is (out of band), so its loop body has fixed load counts and no curve loads.  In-band
+    // tiles are a suffix of the wave's tiles; t1 is the first in-band tile at or past NSLOT,
+    // rounded down to even (tile t uses register set t % 2).  Phase 2, the in-band tiles past
+    // the up-front ones (only where the bias range covers more than 4 of a wave's tiles), forms
+    // each tile's curve during the tile before, as the general kernel does.
+    int tb = ntiles;
+    if (MODE != 0) {
+      const int x = qpos - a.bias_range - w_beg - TK + 2;   // tile t in band iff t TK >= x
+      tb = x <= 0 ? 0 : (x + TK - 1) / TK;
+    }
+    const int t1 = min(ntiles, max(NSLOT, tb)) & ~1;
+    int t = 0;
+    for (; t < t1; t += 2) {
+      process(t, 0, early_t{});
+      process(t + 1, 1, early_t{});
+    }
+    if (t < ntiles) {
+      if (t >= NSLOT && tile_in_band(w_beg + t * TK))
+        curve_tile_static(w_beg + t * TK, cbuf + (t & (NSLOT - 1)) * G * TK, 0);
+      for (; t + 1 < ntiles; t += 2) {
+        process(t, 0, late_t{});
+        process(t + 1, 1, late_t{});
+      }
+      if (t < ntiles) process(t, 0, late_t{});
+    }
+  } else {
+    for (int t = 0; t < ntiles; t += 2) {
+      process(t, 0, late_t{});
+      if (t + 1 < ntiles) process(t + 1, 1, late_t{});
+    }
   }
 
   // ---- merge the 4 waves through LDS (reusing the V^T area) ---------------------------
@@ -838,17 +1008,27 @@ hipError_t launch_d(DecodeArgs a, hipStream_t s) {
   const int merge = 4 * a.G * (D + 2) * 4;
   const int curve_off = ((VT_ALL > merge ? VT_ALL : merge) + 15) / 16 * 16;
   // after the V^T tiles / merge buffer: r [G][R] (r.E), then per wave two tile curves [G][TK]
-  const int total = curve_off + (MODE == 2 ? a.G * a.R * 4 : 0) + (MODE != 0 ? 4 * 2 * a.G * TK * 4 : 0);
+  const bool narrow = a.G <= 16;
+  // contiguous bf16 caches and groups of up to 8 query heads: the 16x16 kernel with fixed load
+  // counts per tile and up-front curves (its curve inputs read through one buffer resource,
+  // whose extent must fit 31 bits)
+  const long long e_extent = MODE == 1 ? 4LL * a.G * a.bias_range
+                                       : 4LL * ((a.G - 1) * a.e_hs + static_cast<long long>(a.R) * a.bias_range);
+  const bool contig = a.G <= 8 && !FP4 && a.block_table == nullptr && e_extent < (1LL << 31);
+  const int nslot = contig ? 4 : 2;   // tile curves per wave
+  const int total = curve_off + (MODE == 2 ? a.G * a.R * 4 : 0) + (MODE != 0 ? 4 * nslot * a.G * TK * 4 : 0);
   if (total > 160 * 1024) return hipErrorInvalidValue;
   // groups of up to 16 query heads: the 16x16 MFMA kernel (two tiles in flight per wave)
-  const bool narrow = a.G <= 16;
-  const void* fn = narrow ? reinterpret_cast<const void*>(&decode16_kernel<D, MODE, RMAX, FP4>)
-                          : reinterpret_cast<const void*>(&decode_bf16_kernel<D, MODE, RMAX, FP4>);
+  const void* fn = contig ? reinterpret_cast<const void*>(&decode16_kernel<D, MODE, RMAX, false, true>)
+                   : narrow ? reinterpret_cast<const void*>(&decode16_kernel<D, MODE, RMAX, FP4>)
+                            : reinterpret_cast<const void*>(&decode_bf16_kernel<D, MODE, RMAX, FP4>);
   {
     const hipError_t e = set_max_lds(fn, total, s);
     if (e != hipSuccess) return e;
   }
-  if (narrow)
+  if (contig)
+    hipLaunchKernelGGL((decode16_kernel<D, MODE, RMAX, false, true>), grid, dim3(256), total, s, a, curve_off);
+  else if (narrow)
     hipLaunchKernelGGL((decode16_kernel<D, MODE, RMAX, FP4>), grid, dim3(256), total, s, a, curve_off);
   else
     hipLaunchKernelGGL((decode_bf16_kernel<D, MODE, RMAX, FP4>), grid, dim3(256), total, s, a, curve_off);
