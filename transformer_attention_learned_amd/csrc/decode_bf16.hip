@@ -447,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
 // (a quarter of the registers of bf16 rows) and are widened to bf16 where the MFMAs use them.
 // A lane's K fragment then covers head dims (D / 4) g + 8 c .. + 7 (one 16-byte load per row at
 // D = 128, 8 bytes at D = 64, and a single scale), so the query fragments use the same dims.
-// CONTIG: contiguous bf16 caches.  Loads complete in issue order, so a wait for any load also
+// CONTIG: contiguous caches (bf16 or MXFP4).  Loads complete in issue order, so a wait for any load also
 // waits for every tile requested before it; here the tile loop keeps the next tile in flight
 // during each wait: every K / V load is issued unconditionally (buffer resources that read zeros
 // past the wave's last row, so the compiler counts the loads in flight exactly), and the bias
@@ -498,7 +498,8 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
   u32x4 kreg[2][2][FP4 ? 1 : NC], vreg[2][NVI][FP4 ? 1 : 4];
   // FP4: 16 code bytes and the scale byte per K row, 4 code bytes and a scale byte per V row
   u32x4 kc[2][2];
-  uint32_t ksb[2][2], vc[2][NVI][4], vsb[2][NVI][4];
+  uint32_t vc[2][NVI][4];
+  uint8_t ksb[2][2], vsb[2][NVI][4];   // scale bytes, widened where they are used
   constexpr int CB = D / 2, SB = D / 32;
   constexpr int EPL = D / 4;   // FP4: head-dim elements of a lane's K fragment (D = 64 or 128)
   static_assert(!FP4 || EPL == 16 || EPL == 32, "MXFP4 caches: head_dim 64 or 128");
@@ -514,9 +515,54 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
       // resource ends at the last row's 2 D bytes, so every chunk of a row at or past w_end
       // reads as zeros (a row is row_b >= 2 D bytes from the next), and a tile wholly past
       // w_end has an empty resource (no memory access)
-      const int row_b = a.Hkv * D * 2;
       const int left = w_end - tk0;
       const int nrows = left <= 0 ? 0 : (left < TK ? left : TK);
+      if constexpr (FP4) {
+        // codes (crow bytes per row, CB of this kv head) and scale bytes (srow, SB) likewise
+        const int crow_i = static_cast<int>(crow), srow_i = static_cast<int>(srow);
+        const int cbytes = nrows > 0 ? (nrows - 1) * crow_i + CB : 0;
+        const int sbytes = nrows > 0 ? (nrows - 1) * srow_i + SB : 0;
+        const __amdgpu_buffer_rsrc_t rkc = make_rsrc(kcb + static_cast<size_t>(tk0) * crow, cbytes);
+        const __amdgpu_buffer_rsrc_t rks = make_rsrc(ksp + static_cast<size_t>(tk0) * srow, sbytes);
+        const __amdgpu_buffer_rsrc_t rvc = make_rsrc(vcb + static_cast<size_t>(tk0) * crow, cbytes);
+        const __amdgpu_buffer_rsrc_t rvs = make_rsrc(vsp + static_cast<size_t>(tk0) * srow, sbytes);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int r = 16 * kb + n16;
+          if constexpr (EPL == 32) {
+            kc[set][kb] = buf_ld16(rkc, r * crow_i + (EPL / 2) * g);
+          } else {
+            const u32x2 w2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rkc, r * crow_i + (EPL / 2) * g, 0, 0));
+            kc[set][kb] = u32x4{w2[0], w2[1], 0u, 0u};
+          }
+          ksb[set][kb] = __builtin_amdgcn_raw_buffer_load_b8(rks, r * srow_i + (EPL * g) / 32, 0, 0);
+        }
+        const int kg = lane & 7;
+        if constexpr (NVI == 2) {
+          const int dg0 = v_item_dg<FP4, NVI>(lane, 0);
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) {
+            const int r = 4 * kg + s4;
+            const u32x2 w2 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvc, r * crow_i + 4 * dg0, 0, 0));
+            vc[set][0][s4] = w2[0];
+            vc[set][1][s4] = w2[1];
+            vsb[set][0][s4] = vsb[set][1][s4] = __builtin_amdgcn_raw_buffer_load_b8(rvs, r * srow_i + (dg0 >> 2), 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int it = 0; it < NVI; ++it) {
+            const int dg = v_item_dg<FP4, NVI>(lane, it);
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+              const int r = 4 * kg + s4;
+              vc[set][it][s4] = __builtin_amdgcn_raw_buffer_load_b32(rvc, r * crow_i + 4 * dg, 0, 0);
+              vsb[set][it][s4] = __builtin_amdgcn_raw_buffer_load_b8(rvs, r * srow_i + (dg >> 2), 0, 0);
+            }
+          }
+        }
+        return;
+      }
+      const int row_b = a.Hkv * D * 2;
       const int nbytes = nrows > 0 ? (nrows - 1) * row_b + D * 2 : 0;
       const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + static_cast<size_t>(tk0) * kv_row, nbytes);
       const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + static_cast<size_t>(tk0) * kv_row, nbytes);
@@ -732,6 +778,9 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
 #pragma unroll
     for (int i = 0; i < NPRE; ++i)
       if (i < ntiles && tile_in_band(w_beg + i * TK)) fetch_items_buf(w_beg + i * TK, 0, ep[i]);
+    // keeps the compiler from moving those loads below the tile loads (loads may be reordered
+    // freely, and it would sink them to their use)
+    asm volatile("" ::: "memory");
   {
     const uint16_t* qp = a.q + (static_cast<size_t>(b) * a.Hq + hkv * G + (col_live ? n16 : 0)) * D + (FP4 ? EPL * g : 8 * g);
 #pragma unroll
@@ -1009,17 +1058,17 @@ hipError_t launch_d(DecodeArgs a, hipStream_t s) {
   const int curve_off = ((VT_ALL > merge ? VT_ALL : merge) + 15) / 16 * 16;
   // after the V^T tiles / merge buffer: r [G][R] (r.E), then per wave two tile curves [G][TK]
   const bool narrow = a.G <= 16;
-  // contiguous bf16 caches and groups of up to 8 query heads: the 16x16 kernel with fixed load
+  // contiguous caches (bf16 or MXFP4) and groups of up to 8 query heads: the 16x16 kernel with fixed load
   // counts per tile and up-front curves (its curve inputs read through one buffer resource,
   // whose extent must fit 31 bits)
   const long long e_extent = MODE == 1 ? 4LL * a.G * a.bias_range
                                        : 4LL * ((a.G - 1) * a.e_hs + static_cast<long long>(a.R) * a.bias_range);
-  const bool contig = a.G <= 8 && !FP4 && a.block_table == nullptr && e_extent < (1LL << 31);
+  const bool contig = a.G <= 8 && a.block_table == nullptr && e_extent < (1LL << 31);
   const int nslot = contig ? 4 : 2;   // tile curves per wave
   const int total = curve_off + (MODE == 2 ? a.G * a.R * 4 : 0) + (MODE != 0 ? 4 * nslot * a.G * TK * 4 : 0);
   if (total > 160 * 1024) return hipErrorInvalidValue;
   // groups of up to 16 query heads: the 16x16 MFMA kernel (two tiles in flight per wave)
-  const void* fn = contig ? reinterpret_cast<const void*>(&decode16_kernel<D, MODE, RMAX, false, true>)
+  const void* fn = contig ? reinterpret_cast<const void*>(&decode16_kernel<D, MODE, RMAX, FP4, true>)
                    : narrow ? reinterpret_cast<const void*>(&decode16_kernel<D, MODE, RMAX, FP4>)
                             : reinterpret_cast<const void*>(&decode_bf16_kernel<D, MODE, RMAX, FP4>);
   {
@@ -1027,7 +1076,7 @@ hipError_t launch_d(DecodeArgs a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (contig)
-    hipLaunchKernelGGL((decode16_kernel<D, MODE, RMAX, false, true>), grid, dim3(256), total, s, a, curve_off);
+    hipLaunchKernelGGL((decode16_kernel<D, MODE, RMAX, FP4, true>), grid, dim3(256), total, s, a, curve_off);
   else if (narrow)
     hipLaunchKernelGGL((decode16_kernel<D, MODE, RMAX, FP4>), grid, dim3(256), total, s, a, curve_off);
   else
