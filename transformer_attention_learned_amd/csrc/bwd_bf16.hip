@@ -101,32 +101,35 @@ template <int EW>
 __device__ __forceinline__ bool r_vec(const BwdArgs& a) {
   return a.R == EW / 2 && (reinterpret_cast<uintptr_t>(a.r) & 15) == 0;
 }
+// The two load forms keep separate storage: with one array written in either form the compiler
+// placed it in scratch memory, and the store there waited for every load in flight.
+struct RRaw {
+  u32x4 v;          // the 16-byte form: features in pairs
+  uint32_t s[8];    // the two-byte form: one feature each
+};
 template <int EW>
-__device__ __forceinline__ void r_load(const BwdArgs& a, bool rvec, int b, int h, int row, int lh,
-                                       uint32_t (&x)[8]) {
+__device__ __forceinline__ void r_load(const BwdArgs& a, bool rvec, int b, int h, int row, int lh, RRaw& x) {
   const int f0 = (EW == 32) ? 8 * lh : 0;
   const uint16_t* rp = a.r + ((static_cast<size_t>(b) * a.S + (row < a.S ? row : 0)) * a.Hq + h) * a.R;
   if (rvec) {
-    const u32x4 v = ld16(rp + f0);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) x[k] = v[k];
+    x.v = ld16(rp + f0);
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = rp[min(f0 + e, a.R - 1)];
+    for (int e = 0; e < 8; ++e) x.s[e] = rp[min(f0 + e, a.R - 1)];
   }
 }
 template <int EW>
-__device__ __forceinline__ bf16x8 r_pack(const BwdArgs& a, bool rvec, int row, int lh, const uint32_t (&x)[8]) {
+__device__ __forceinline__ bf16x8 r_pack(const BwdArgs& a, bool rvec, int row, int lh, const RRaw& x) {
   const int f0 = (EW == 32) ? 8 * lh : 0;
   uint32_t w[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     if (rvec) {
-      w[jj] = row < a.S ? x[jj] : 0u;
+      w[jj] = row < a.S ? x.v[jj] : 0u;
     } else {
       const int f = f0 + 2 * jj;
-      const uint32_t lo = (row < a.S && f < a.R) ? x[2 * jj] : 0u;
-      const uint32_t hi = (row < a.S && f + 1 < a.R) ? x[2 * jj + 1] : 0u;
+      const uint32_t lo = (row < a.S && f < a.R) ? x.s[2 * jj] : 0u;
+      const uint32_t hi = (row < a.S && f + 1 < a.R) ? x.s[2 * jj + 1] : 0u;
       w[jj] = lo | (hi << 16);
     }
   }
@@ -134,7 +137,7 @@ __device__ __forceinline__ bf16x8 r_pack(const BwdArgs& a, bool rvec, int row, i
 }
 template <int EW>
 __device__ __forceinline__ bf16x8 r_frag(const BwdArgs& a, int b, int h, int row, int lh) {
-  uint32_t x[8];
+  RRaw x;
   const bool rvec = r_vec<EW>(a);
   r_load<EW>(a, rvec, b, h, row, lh, x);
   return r_pack<EW>(a, rvec, row, lh, x);
@@ -919,7 +922,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
 
   const uint16_t* e2b = (MODE == 2) ? a.e2 + kE2Pad * EW : nullptr;
   const bool rvec = r_vec<EW>(a);
-  auto e_load = [&](Pos js, u32x4 (&eb)[2][EW / 16], uint32_t (&rx)[8]) __attribute__((always_inline)) {
+  auto e_load = [&](Pos js, u32x4 (&eb)[2][EW / 16], RRaw& rx) __attribute__((always_inline)) {
     const int h = hkv * G + step_head(js);
     const int i0 = step_row0(js);
     e_rows<EW>(e2b + static_cast<size_t>(a.e_hs ? h : 0) * (Rb + 2 * kE2Pad + 1) * EW, i0 - j0w, ln, lh, eb);
@@ -935,7 +938,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   // (scheduling barriers pin the order; left to itself the compiler keeps one fragment in flight
   // and each MFMA waits out its read).
   auto scores = [&](Pos js, const unsigned char* slot, f32x16& sacc, f32x16& pacc, const u32x4 (&eb)[2][EW / 16],
-                    const uint32_t (&rx)[8]) __attribute__((always_inline)) {
+                    const RRaw& rx) __attribute__((always_inline)) {
     const int i0 = step_row0(js);
     const int c = i0 - j0w;
     const bool ib = step_inband(js);
@@ -1082,7 +1085,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
     rec_store(smem + SLOT_B);
   }
   u32x4 eb[2][EW / 16];
-  uint32_t rx[8];
+  RRaw rx;
   if (MODE == 2 && step_on(p0) && step_inband(p0)) e_load(p0, eb, rx);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's direct loads have landed
   __syncthreads();
@@ -1101,7 +1104,7 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     u32x4 e[2][EW / 16];
-    uint32_t x[8];
+    RRaw x;
     if (MODE == 2 && step_on(p1) && step_inband(p1)) e_load(p1, e, x);
     if (MODE == 1 && more && p2.t == 0) stage_table(p2.hh);
     if (more) rec_load(p2);
