@@ -413,18 +413,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
   // bias parameters of the head in LDS (made visible by the first barrier)
   if (MODE == 1) {
     const float* tp = a.table + static_cast<size_t>(h) * Rb;
-    for (int x = tid; x < Rb + 2 * PADT; x += 256) {
-      const int d = x - PADT;
-      tabs[x] = (d >= 0 && d < Rb) ? tp[d] * kLog2e : 0.f;
-    }
+    stage_batched(tid, 256, Rb + 2 * PADT,
+        [&](int x) { return __float_as_uint(tp[min(max(x - PADT, 0), Rb - 1)]); },
+        [&](int x, uint32_t w) {
+          const int d = x - PADT;
+          const uint32_t keep = (d >= 0 && d < Rb) ? ~0u : 0u;
+          tabs[x] = __uint_as_float(__float_as_uint(__uint_as_float(w) * kLog2e) & keep);
+        });
   }
   const int efs = L::ef_stride(Rb);
   if (MODE == 2) {
-    for (int x = tid; x < a.R * efs; x += 256) {
-      const int f = x / efs;
-      const int d = x - f * efs - PADE;
-      ef[x] = (d >= 0 && d < Rb) ? f32_to_bf16(Eh[static_cast<size_t>(f) * Rb + d]) : static_cast<uint16_t>(0);
-    }
+    stage_batched(tid, 256, a.R * efs,
+        [&](int x) {
+          const int f = x / efs;
+          const int d = x - f * efs - PADE;
+          return __float_as_uint(Eh[static_cast<size_t>(f) * Rb + min(max(d, 0), Rb - 1)]);
+        },
+        [&](int x, uint32_t w) {
+          const int f = x / efs;
+          const int d = x - f * efs - PADE;
+          const uint32_t keep = (d >= 0 && d < Rb) ? 0xFFFFu : 0u;
+          ef[x] = static_cast<uint16_t>(f32_to_bf16(__uint_as_float(w)) & keep);
+        });
   }
 
   // Q^T and dO^T fragments (B operands): lane (n = ln, lh) holds x[row][16c + 8lh .. +7]
@@ -451,23 +461,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdArgs a, int n_qtiles,
   if (MODE != 0) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      uint32_t w[4];
+      // all 8 loads issued before any is used (clamped inside the rows, masked afterwards as
+      // integers, so that none sits behind its own branch)
+      uint32_t xr[8];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        uint32_t pr[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int rr = i0 + 16 * kk + 8 * lh + 2 * jj + u;
-          uint32_t x = 0u;
-          if (rr < S) {
-            if (MODE == 1) x = (ln == 0) ? 0x3f80u : 0u;   // bf16 1.0
-            else if (ln < a.R) x = a.r[((static_cast<size_t>(b) * S + rr) * a.Hq + h) * a.R + ln];
-          }
-          pr[u] = x;
+      for (int e = 0; e < 8; ++e) {
+        const int rr = i0 + 16 * kk + 8 * lh + e;
+        if (MODE == 1) {
+          xr[e] = (rr < S && ln == 0) ? 0x3f80u : 0u;   // bf16 1.0
+        } else {
+          const uint32_t raw = a.r[((static_cast<size_t>(b) * S + min(rr, S - 1)) * a.Hq + h) * a.R + min(ln, a.R - 1)];
+          xr[e] = raw & ((rr < S && ln < a.R) ? 0xFFFFu : 0u);
         }
-        w[jj] = pr[0] | (pr[1] << 16);
       }
-      rA[kk] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+      rA[kk] = as_bf16x8(u32x4{xr[0] | (xr[1] << 16), xr[2] | (xr[3] << 16), xr[4] | (xr[5] << 16), xr[6] | (xr[7] << 16)});
     }
     // zero the skewed buffers once: every in-band step writes the same set of positions
     for (int x = lane; x < (L::G_BYTES + L::GT_BYTES) / 16; x += 64)
@@ -914,10 +921,13 @@ __global__ __launch_bounds__(64 * DKV_WAVES, 1) void bwd_dkdv_kernel(BwdArgs a) 
   auto stage_table = [&](int hh) __attribute__((always_inline)) {
     float* tab = tabs + (hh & 1) * TROW;
     const float* tp = a.table + static_cast<size_t>(hkv * G + hh) * Rb;
-    for (int x = tid; x < TROW; x += NT) {
-      const int d = x - PADT;
-      tab[x] = (d >= 0 && d < Rb) ? tp[d] * inv_scale : 0.f;
-    }
+    stage_batched(tid, NT, TROW,
+        [&](int x) { return __float_as_uint(tp[min(max(x - PADT, 0), Rb - 1)]); },
+        [&](int x, uint32_t w) {
+          const int d = x - PADT;
+          const uint32_t keep = (d >= 0 && d < Rb) ? ~0u : 0u;
+          tab[x] = __uint_as_float(__float_as_uint(__uint_as_float(w) * inv_scale) & keep);
+        });
   };
 
   const uint16_t* e2b = (MODE == 2) ? a.e2 + kE2Pad * EW : nullptr;

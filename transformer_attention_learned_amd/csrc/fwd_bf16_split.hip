@@ -196,21 +196,33 @@ __global__ __launch_bounds__(NT, 2) void fwd_split_kernel(FwdArgs a, const uint1
     else __builtin_amdgcn_s_waitcnt(0x0F72);            // vmcnt(2)
   };
 
+  // tiles 0 and 1 in flight first (HBM), then the query rows
+  dma_tile(0, smem);
+  if (nsteps > 1) dma_tile(1, smem + BUF_BYTES);
   // ---- table rows of the group (MODE 1), in accumulator units, PAD zero distances each side
+  // (requested behind the first two tiles, whose latency their first wait then overlaps)
   const int Rp = Rb + 2 * PAD;
   if (MODE == 1) {
     float* tab = reinterpret_cast<float*>(smem + TILE_BYTES);
     const float* tg = a.table + static_cast<size_t>(hg) * 4 * Rb;
-    for (int i = tid; i < 4 * Rp; i += NT) {
-      const int hw = static_cast<int>(i >= Rp) + static_cast<int>(i >= 2 * Rp) + static_cast<int>(i >= 3 * Rp);
-      const int d = i - hw * Rp - PAD;
-      tab[i] = (d >= 0 && d < Rb) ? tg[hw * Rb + d] * inv_scale : 0.f;
-    }
+    auto dist = [&](int i, int& hw) {
+      hw = static_cast<int>(i >= Rp) + static_cast<int>(i >= 2 * Rp) + static_cast<int>(i >= 3 * Rp);
+      return i - hw * Rp - PAD;
+    };
+    stage_batched(tid, NT, 4 * Rp,
+        [&](int i) {
+          int hw;
+          const int d = dist(i, hw);
+          return __float_as_uint(tg[hw * Rb + min(max(d, 0), Rb - 1)]);
+        },
+        [&](int i, uint32_t w) {
+          int hw;
+          const int d = dist(i, hw);
+          const uint32_t keep = (d >= 0 && d < Rb) ? ~0u : 0u;
+          tab[i] = __uint_as_float(__float_as_uint(__uint_as_float(w) * inv_scale) & keep);
+        });
   }
 
-  // tiles 0 and 1 in flight first (HBM), then the query rows
-  dma_tile(0, smem);
-  if (nsteps > 1) dma_tile(1, smem + BUF_BYTES);
 
   bf16x8 qf[NC];
   {

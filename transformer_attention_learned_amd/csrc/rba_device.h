@@ -88,4 +88,22 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Fills entries [0, n) of a staging buffer, thread t taking t, t + nt, t + 2 nt, ...: in
+// batches of 8, all of a batch's loads are issued before any is used (a loop of one load and its
+// store per entry waits out one memory round trip per entry).  Indices past n are clamped to
+// n - 1 (that entry is loaded and stored again with the same value), so that neither the loads
+// nor the stores sit behind a branch the compiler could sink a load into.  load(x) returns the
+// raw 32-bit word of entry x from an address valid for any x in [0, n); store(x, w) writes
+// entry x from that word (masks as integer operations, for the same reason).
+template <typename LoadF, typename StoreF>
+__device__ __forceinline__ void stage_batched(int tid, int nt, int n, LoadF load, StoreF store) {
+  for (int x0 = tid; x0 < n; x0 += 8 * nt) {
+    uint32_t w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w[u] = load(min(x0 + u * nt, n - 1));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) store(min(x0 + u * nt, n - 1), w[u]);
+  }
+}
+
 }  // namespace rba
