@@ -94,7 +94,12 @@ __global__ void e2_convert_kernel(const float* __restrict__ E, long long e_hs, i
   const int f0 = 8 * blockIdx.z;
   const int d = p - PAD;
   const bool live = d >= 0 && d < Rb;
-  const float* eh = E + h * e_hs + static_cast<long long>(f0) * Rb + d;
+  // all 8 loads issued unconditionally (distance and feature clamped into range) and masked
+  // afterwards as integers, so that none waits behind its own branch
+  const float* eh = E + h * e_hs + min(max(d, 0), Rb - 1);
+  uint32_t raw[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) raw[q] = __float_as_uint(eh[static_cast<long long>(min(f0 + q, R - 1)) * Rb]);
   uint32_t whi[4], wlo[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -102,7 +107,8 @@ __global__ void e2_convert_kernel(const float* __restrict__ E, long long e_hs, i
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int f = f0 + 2 * k + u;
-      const float x = (live && f < R) ? eh[static_cast<long long>(2 * k + u) * Rb] * inv_scale : 0.f;
+      const uint32_t keep = (live && f < R) ? ~0u : 0u;
+      const float x = __uint_as_float(__float_as_uint(__uint_as_float(raw[2 * k + u]) * inv_scale) & keep);
       hb[u] = f32_to_bf16(x);
       lb[u] = f32_to_bf16(x - bf16_to_f32(hb[u]));
     }
