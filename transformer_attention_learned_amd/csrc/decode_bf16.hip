@@ -447,13 +447,16 @@ __global__ __launch_bounds__(256, 2) void decode_bf16_kernel(DecodeArgs a, int c
 // (a quarter of the registers of bf16 rows) and are widened to bf16 where the MFMAs use them.
 // A lane's K fragment then covers head dims (D / 4) g + 8 c .. + 7 (one 16-byte load per row at
 // D = 128, 8 bytes at D = 64, and a single scale), so the query fragments use the same dims.
-// CONTIG: contiguous caches (bf16 or MXFP4).  Loads complete in issue order, so a wait for any load also
-// waits for every tile requested before it; here the tile loop keeps the next tile in flight
-// during each wait: every K / V load is issued unconditionally (buffer resources that read zeros
-// past the wave's last row, so the compiler counts the loads in flight exactly), and the bias
-// curves of the wave's first four tiles (every tile of a 512-row window) are formed up front
-// from inputs requested ahead of the first tiles, so that no curve load follows a tile.
-template <int D, int MODE, int RMAX, bool FP4, bool CONTIG = false>
+// PIPE: the pipelined tile loop, for contiguous caches or (PAGED) page pools, bf16 or MXFP4.
+// Loads complete in issue order, so a wait for any load also waits for every tile requested
+// before it; here the tile loop keeps the next tile in flight during each wait: every K / V
+// load is issued unconditionally (contiguous: buffer resources that read zeros past the wave's
+// last row; paged: rows clamped into the sequence, masked in the logits), so the compiler
+// counts the loads in flight exactly; page entries are requested a tile ahead of the tile that
+// uses them, before the tile two ahead; and the bias curves of the wave's first four tiles
+// (every tile of a 512-row window) are formed up front from inputs requested ahead of the first
+// tiles, so that no curve load follows a tile.
+template <int D, int MODE, int RMAX, bool FP4, bool PIPE = false, bool PAGED = false>
 __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curve_off) {
   constexpr int VST = TK + 8;          // V^T row stride (bf16)
   constexpr int NC = D / 32;           // K = 32 chunks of the head dim
@@ -474,7 +477,7 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
   const bool col_live = n16 < G;
 
   const size_t kv_row = static_cast<size_t>(a.Hkv) * D;
-  const bool paged = !CONTIG && a.block_table != nullptr;
+  const bool paged = PIPE ? PAGED : a.block_table != nullptr;
   const int kv_len = paged ? min(max(a.kv_lens[b], 0), a.kv_len) : a.kv_len;
   const int key_begin = paged ? (a.window ? max(0, kv_len - a.window) : 0) : a.key_begin;
   // context-length temperature of this sequence's query, on q.k and bias alike
@@ -509,8 +512,81 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
   const uint8_t* vcb = reinterpret_cast<const uint8_t*>(a.v) + (cbatch * a.Hkv + hkv) * CB;
   const uint8_t* ksp = FP4 ? a.k_scale + (cbatch * a.Hkv + hkv) * SB : nullptr;
   const uint8_t* vsp = FP4 ? a.v_scale + (cbatch * a.Hkv + hkv) * SB : nullptr;
+  // PIPE && PAGED: page entries of the K rows (rows 16 kb + l % 16) of the tile a register set
+  // receives next, requested a tile ahead (keys clamped into the sequence: valid table entries)
+  int pgv[2][2] = {{0, 0}, {0, 0}};
+  auto key_clamp = [&](int key) { return max(0, min(key, w_end - 1)); };
+  auto fetch_pages = [&](int set, int tk0) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) pgv[set][kb] = bt[key_clamp(tk0 + 16 * kb + n16) / a.page_size];
+  };
   auto load_tile = [&](int set, int tk0) {
-    if constexpr (CONTIG) {
+    if constexpr (PIPE && PAGED) {
+      // pool rows of this lane's K rows, and of its V rows from the lanes holding them (lane
+      // l < 32 holds row tk0 + l); rows past the wave's end read its last row (masked later)
+      int prow[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int pg = min(max(pgv[set][kb], 0), a.num_pages - 1);
+        prow[kb] = pg * a.page_size + key_clamp(tk0 + 16 * kb + n16) % a.page_size;
+      }
+      const int prow32 = prow[g & 1];
+      if constexpr (FP4) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint8_t* kp = kcb + static_cast<size_t>(prow[kb]) * crow + (EPL / 2) * g;
+          if constexpr (EPL == 32) {
+            kc[set][kb] = ld16(kp);
+          } else {
+            const u32x2 w2 = ld8(kp);
+            kc[set][kb] = u32x4{w2[0], w2[1], 0u, 0u};
+          }
+          ksb[set][kb] = ksp[static_cast<size_t>(prow[kb]) * srow + (EPL * g) / 32];
+        }
+        const int kg = lane & 7;
+        if constexpr (NVI == 2) {
+          const int dg0 = v_item_dg<FP4, NVI>(lane, 0);
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) {
+            const int vrow = __shfl(prow32, 4 * kg + s4, 64);
+            const u32x2 w2 = ld8(vcb + static_cast<size_t>(vrow) * crow + 4 * dg0);
+            vc[set][0][s4] = w2[0];
+            vc[set][1][s4] = w2[1];
+            vsb[set][0][s4] = vsb[set][1][s4] = vsp[static_cast<size_t>(vrow) * srow + (dg0 >> 2)];
+          }
+        } else {
+#pragma unroll
+          for (int it = 0; it < NVI; ++it) {
+            const int dg = v_item_dg<FP4, NVI>(lane, it);
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+              const int vrow = __shfl(prow32, 4 * kg + s4, 64);
+              vc[set][it][s4] = *reinterpret_cast<const uint32_t*>(vcb + static_cast<size_t>(vrow) * crow + 4 * dg);
+              vsb[set][it][s4] = vsp[static_cast<size_t>(vrow) * srow + (dg >> 2)];
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const uint16_t* kp = kbase + static_cast<size_t>(prow[kb]) * kv_row + 8 * g;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) kreg[set][kb][c] = ld16(kp + 32 * c);
+        }
+#pragma unroll
+        for (int it = 0; it < NVI; ++it) {
+          const int kg = lane & 7;
+          const int dg = v_item_dg<FP4, NVI>(lane, it);
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) {
+            const int vrow = __shfl(prow32, 4 * kg + s4, 64);
+            vreg[set][it][s4] = ld16(vbase + static_cast<size_t>(vrow) * kv_row + 8 * dg);
+          }
+        }
+      }
+      return;
+    }
+    if constexpr (PIPE) {
       // rows tk0 .. tk0 + 31 through buffer resources over the tile's existing rows: the
       // resource ends at the last row's 2 D bytes, so every chunk of a row at or past w_end
       // reads as zeros (a row is row_b >= 2 D bytes from the next), and a tile wholly past
@@ -657,9 +733,9 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
 
   // ---- bias curves per tile, as in the 32x32 kernel -----------------------------------------
   float* rs = reinterpret_cast<float*>(smem + curve_off);                  // [G][R] (r.E)
-  // per wave a ring of tile curves [NSLOT][G][TK] (CONTIG: the up-front curves of the first
+  // per wave a ring of tile curves [NSLOT][G][TK] (PIPE: the up-front curves of the first
   // NSLOT tiles, then the later in-band tiles in turn)
-  constexpr int NSLOT = CONTIG ? 4 : 2;
+  constexpr int NSLOT = PIPE ? 4 : 2;
   float* cbuf = rs + (MODE == 2 ? G * a.R : 0) + wave * NSLOT * G * TK;
   auto stage_r = [&]() {
     for (int i = tid; i < G * a.R; i += 256)
@@ -691,7 +767,7 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
       }
     }
   };
-  // CONTIG: the same values through one buffer resource over the group's table rows or E
+  // PIPE: the same values through one buffer resource over the group's table rows or E
   // slabs (heads hkv G .. hkv G + G - 1): a lane's offset is its item's (head, distance), the
   // feature's offset is scalar (clamped to feature R - 1), and an item that is not live reads
   // zeros from an offset past the resource, so no load sits behind a per-lane branch.  The
@@ -741,7 +817,7 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
     }
   };
   // (the inputs are fetched where they are used: registers go to the tiles in flight)
-  // CONTIG: the same with a static trip count (n_items <= 256: G <= 8): a loop of unknown trip
+  // PIPE: the same with a static trip count (n_items <= 256: G <= 8): a loop of unknown trip
   // count around loads makes the compiler's counts of loads in flight unknown after it, and
   // every later wait for a tile would then wait for all loads
   auto curve_tile_static = [&](int tk0, float* dst, int k0) __attribute__((always_inline)) {
@@ -762,12 +838,18 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
     }
   };
   bf16x8 qf[NC];
-  if constexpr (CONTIG) {
+  if constexpr (PIPE) {
     // r (one entry per thread, G R <= 128) and the curve inputs of the wave's first NPRE tiles
     // (their first 128 items each) are requested first, while no tile registers are live, then
     // the query rows and the first two tiles; the curves are formed while those are in flight,
     // and the tile loop then waits for no curve input of these tiles
     constexpr int NPRE = (MODE == 2 && RMAX > 8) ? 2 : NSLOT;
+    // page pools: the page entries of the first two tiles first (their rows' addresses wait
+    // for them)
+    if constexpr (PAGED) {
+      fetch_pages(0, w_beg);
+      fetch_pages(1, w_beg + TK);
+    }
     uint32_t r_raw = 0;
     if (MODE == 2) {
       const __amdgpu_buffer_rsrc_t r_rsrc =
@@ -792,6 +874,7 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
   }
     load_tile(0, w_beg);
     load_tile(1, w_beg + TK);
+    if constexpr (PAGED) fetch_pages(0, w_beg + 2 * TK);   // for the first tile loop step
     if (MODE == 2) {
       if (tid < G * a.R) rs[tid] = bf16_to_f32(static_cast<uint16_t>(r_raw));
       __syncthreads();
@@ -834,7 +917,7 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
   // V^T position of tile row k: 8 (k % 16 / 4) + 4 (k / 16) + k % 4
   auto vt_pos16 = [](int k) { return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3); };
 
-  // LATE: this call may form the next tile's curve (always outside CONTIG; in CONTIG only in
+  // LATE: this call may form the next tile's curve (always outside PIPE; in PIPE only in
   // the second phase of the tile loop below)
   auto process = [&](int t, int set, auto late_c) {
     constexpr bool LATE = decltype(late_c)::value;
@@ -886,12 +969,16 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
         }
       }
     }
-    // this set's registers are free: the tile two ahead goes in flight (CONTIG: always issued,
+    // this set's registers are free: the tile two ahead goes in flight (PIPE: always issued,
     // empty past the wave's rows)
-    if constexpr (CONTIG)
+    if constexpr (PIPE) {
+      // page pools: the next tile's page entries first, so that their wait (in the next call)
+      // leaves this tile in flight
+      if constexpr (PAGED) fetch_pages(1 - set, tk0 + 3 * TK);
       load_tile(set, tk0 + 2 * TK);
-    else if (t + 2 < ntiles)
+    } else if (t + 2 < ntiles) {
       load_tile(set, tk0 + 2 * TK);
+    }
 
     // logits (log2 units), bias of in-band rows, mask beyond this wave's rows
     const bool in_band = tile_in_band(tk0);
@@ -938,11 +1025,11 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
       const bf16x8 vf = as_bf16x8(ld16(vt + (16 * db + n16) * VST + 8 * g));
       oacc[db] = mfma16(vf, pf, oacc[db]);
     }
-    // the curve of the next tile (CONTIG: only past the up-front ones; its inputs then wait
+    // the curve of the next tile (PIPE: only past the up-front ones; its inputs then wait
     // behind the tile just requested)
-    if (LATE && (!CONTIG || t + 1 >= NSLOT) && t + 1 < ntiles && tile_in_band(tk0 + TK)) {
+    if (LATE && (!PIPE || t + 1 >= NSLOT) && t + 1 < ntiles && tile_in_band(tk0 + TK)) {
       float* dst = cbuf + ((t + 1) & (NSLOT - 1)) * G * TK;
-      if constexpr (CONTIG)
+      if constexpr (PIPE)
         curve_tile_static(tk0 + TK, dst, 0);
       else
         curve_tile(tk0 + TK, dst, 0);
@@ -951,7 +1038,7 @@ __global__ __launch_bounds__(256, 2) void decode16_kernel(DecodeArgs a, int curv
   // two register sets: the unroll keeps their indices static
   using late_t = std::integral_constant<bool, true>;
   using early_t = std::integral_constant<bool, false>;
-  if constexpr (CONTIG) {
+  if constexpr (PIPE) {
     // Phase 1, tiles [0, t1): every curve they need was formed up front (tiles < NSLOT) or
     // none is (out of band), so its loop body has fixed load counts and no curve loads.  In-band
     // tiles are a suffix of the wave's tiles; t1 is the first in-band tile at or past NSLOT,
@@ -1058,25 +1145,29 @@ hipError_t launch_d(DecodeArgs a, hipStream_t s) {
   const int curve_off = ((VT_ALL > merge ? VT_ALL : merge) + 15) / 16 * 16;
   // after the V^T tiles / merge buffer: r [G][R] (r.E), then per wave two tile curves [G][TK]
   const bool narrow = a.G <= 16;
-  // contiguous caches (bf16 or MXFP4) and groups of up to 8 query heads: the 16x16 kernel with fixed load
-  // counts per tile and up-front curves (its curve inputs read through one buffer resource,
-  // whose extent must fit 31 bits)
+  // groups of up to 8 query heads: the 16x16 kernel with the pipelined tile loop (fixed load
+  // counts per tile, up-front curves; contiguous caches or page pools), its curve inputs read
+  // through one buffer resource, whose extent must fit 31 bits
   const long long e_extent = MODE == 1 ? 4LL * a.G * a.bias_range
                                        : 4LL * ((a.G - 1) * a.e_hs + static_cast<long long>(a.R) * a.bias_range);
-  const bool contig = a.G <= 8 && a.block_table == nullptr && e_extent < (1LL << 31);
-  const int nslot = contig ? 4 : 2;   // tile curves per wave
+  const bool pipe = a.G <= 8 && e_extent < (1LL << 31);
+  const bool pool = a.block_table != nullptr;
+  const int nslot = pipe ? 4 : 2;   // tile curves per wave
   const int total = curve_off + (MODE == 2 ? a.G * a.R * 4 : 0) + (MODE != 0 ? 4 * nslot * a.G * TK * 4 : 0);
   if (total > 160 * 1024) return hipErrorInvalidValue;
   // groups of up to 16 query heads: the 16x16 MFMA kernel (two tiles in flight per wave)
-  const void* fn = contig ? reinterpret_cast<const void*>(&decode16_kernel<D, MODE, RMAX, FP4, true>)
+  const void* fn = pipe ? (pool ? reinterpret_cast<const void*>(&decode16_kernel<D, MODE, RMAX, FP4, true, true>)
+                                : reinterpret_cast<const void*>(&decode16_kernel<D, MODE, RMAX, FP4, true, false>))
                    : narrow ? reinterpret_cast<const void*>(&decode16_kernel<D, MODE, RMAX, FP4>)
                             : reinterpret_cast<const void*>(&decode_bf16_kernel<D, MODE, RMAX, FP4>);
   {
     const hipError_t e = set_max_lds(fn, total, s);
     if (e != hipSuccess) return e;
   }
-  if (contig)
-    hipLaunchKernelGGL((decode16_kernel<D, MODE, RMAX, FP4, true>), grid, dim3(256), total, s, a, curve_off);
+  if (pipe && pool)
+    hipLaunchKernelGGL((decode16_kernel<D, MODE, RMAX, FP4, true, true>), grid, dim3(256), total, s, a, curve_off);
+  else if (pipe)
+    hipLaunchKernelGGL((decode16_kernel<D, MODE, RMAX, FP4, true, false>), grid, dim3(256), total, s, a, curve_off);
   else if (narrow)
     hipLaunchKernelGGL((decode16_kernel<D, MODE, RMAX, FP4>), grid, dim3(256), total, s, a, curve_off);
   else
