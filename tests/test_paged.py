@@ -95,6 +95,13 @@ CASES = [
     (dict(B=3, S=5000, bias_range=1024, Hq=32, Hkv=8), [5000, 4097, 1025], 128),
     # context-length temperature follows each sequence's own length
     (dict(S=3000, temp_len=256), [3000, 2000, 257, 100], 64),
+    # waves of five 32-row tiles (32 sequences x 8 kv heads) with the bias range covering the
+    # last waves: curves of in-band tiles past a wave's fourth are formed one tile ahead, page
+    # entries are read a tile ahead, lengths end inside a tile
+    (dict(B=32, Hq=16, Hkv=8, S=4200, bias_range=1024),
+     [4100, 4099, 4064, 3000, 1025, 1024, 700, 33] * 4, 64),
+    (dict(B=32, Hq=16, Hkv=8, S=4200, bias_range=1024, mode="table"),
+     [4100, 3333, 2048, 4031] * 8, 16),
 ]
 
 
