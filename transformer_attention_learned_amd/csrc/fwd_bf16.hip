@@ -113,15 +113,31 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(FwdArgs 
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int row = i0 + 32 * qb + ln;
-      const uint16_t* rp = a.r + ((static_cast<size_t>(b) * S + row) * a.Hq + h) * a.R;
+      // every load issued (row and feature clamped into range) before any is used, masked
+      // afterwards as integers: no load waits behind its own branch
+      const uint16_t* rp = a.r + ((static_cast<size_t>(b) * S + min(row, S - 1)) * a.Hq + h) * a.R;
+      if ((a.R == 8 || a.R == 16) && (reinterpret_cast<uintptr_t>(a.r) & 15) == 0) {
+        // R = 8 or 16, r 16-byte aligned: a lane's features are one or two 16-byte loads
+#pragma unroll
+        for (int fc = 0; fc < NFC; ++fc) {
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (8 * fc < a.R) v = ld16(rp + 8 * fc);
+          const uint32_t keep = row < S ? ~0u : 0u;
+          rf[qb][fc] = as_bf16x8(u32x4{v[0] & keep, v[1] & keep, v[2] & keep, v[3] & keep});
+        }
+        continue;
+      }
+      uint32_t raw[8 * NFC];
+#pragma unroll
+      for (int f = 0; f < 8 * NFC; ++f) raw[f] = rp[min(f, a.R - 1)];
 #pragma unroll
       for (int fc = 0; fc < NFC; ++fc) {
         uint32_t w[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int f0 = 8 * fc + 2 * jj;
-          uint32_t lo = (row < S && f0 < a.R) ? rp[f0] : 0u;
-          uint32_t hi = (row < S && f0 + 1 < a.R) ? rp[f0 + 1] : 0u;
+          const uint32_t lo = raw[f0] & ((row < S && f0 < a.R) ? 0xFFFFu : 0u);
+          const uint32_t hi = raw[f0 + 1] & ((row < S && f0 + 1 < a.R) ? 0xFFFFu : 0u);
           w[jj] = lo | (hi << 16);
         }
         rf[qb][fc] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
@@ -250,10 +266,19 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(FwdArgs 
           for (int half = 0; half < 2; ++half) {
             const int d0 = c - 31 + 32 * half;
             const int dl = d0 + ln;              // A-operand row: distance d0 + ln
+            const bool dok = dl >= 0 && dl < a.bias_range;
+            // the block's E values all requested (distance and feature clamped into range)
+            // before any is used, masked afterwards as integers
+            const float* ep = Eh + min(max(dl, 0), a.bias_range - 1);
+            uint32_t raw[8 * NFC];
+#pragma unroll
+            for (int f = 0; f < 8 * NFC; ++f) raw[f] = __float_as_uint(ep[static_cast<size_t>(min(f, a.R - 1)) * a.bias_range]);
             f32x16 cacc;
 #pragma unroll
             for (int i = 0; i < 16; ++i) cacc[i] = 0.f;
-            for (int fc = 0; fc < nfc; ++fc) {
+#pragma unroll
+            for (int fc = 0; fc < NFC; ++fc) {
+              if (fc >= nfc) break;
               uint32_t w[4];
 #pragma unroll
               for (int jj = 0; jj < 4; ++jj) {
@@ -261,8 +286,8 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void fwd_bf16_kernel(FwdArgs 
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                   const int f = 8 * fc + 2 * jj + u;
-                  float e = 0.f;
-                  if (f < a.R && dl >= 0 && dl < a.bias_range) e = Eh[static_cast<size_t>(f) * a.bias_range + dl] * kLog2e;
+                  const uint32_t keep = (f < a.R && dok) ? ~0u : 0u;
+                  const float e = __uint_as_float(__float_as_uint(__uint_as_float(raw[f]) * kLog2e) & keep);
                   const float hi = bf16_to_f32(f32_to_bf16(e));
                   e2[u] = lh ? (e - hi) : e;      // lane half 1 feeds the low part
                 }
