@@ -22,10 +22,14 @@ namespace {
 constexpr int TK = 64;
 constexpr int NW = 4;   // waves per workgroup, splitting each tile's keys
 
+constexpr int NDS = 2 * TK;   // distances a tile's pairs span (64 rows x TK keys)
+constexpr int RMAX_F32 = 16;
+
 template <int D>
 constexpr int f32_lds_floats() {
-  // K and V tiles during the key loop; the merge buffers after it
-  return std::max(2 * TK * (D + 1), 2 * NW * 64 + (NW - 1) * 64 * 33);
+  // K and V tiles and the tile's bias parameters (table entries or E rows over its distance
+  // span) during the key loop; the merge buffers after it
+  return std::max(2 * TK * (D + 1) + RMAX_F32 * NDS, 2 * NW * 64 + (NW - 1) * 64 * 33);
 }
 
 template <int D>
@@ -33,6 +37,7 @@ __global__ __launch_bounds__(64 * NW) void attn_f32_kernel(F32Args a) {
   __shared__ float sm[f32_lds_floats<D>()];
   float (*Kt)[D + 1] = reinterpret_cast<float (*)[D + 1]>(sm);
   float (*Vt)[D + 1] = reinterpret_cast<float (*)[D + 1]>(sm + TK * (D + 1));
+  float* bs = sm + 2 * TK * (D + 1);   // [R][NDS] E rows, or [NDS] table entries, of the tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -74,15 +79,41 @@ __global__ __launch_bounds__(64 * NW) void attn_f32_kernel(F32Args a) {
   const float* kb = a.k + static_cast<size_t>(b) * a.kv_rows * kv_row + static_cast<size_t>(g) * D;
   const float* vb = a.v + static_cast<size_t>(b) * a.kv_rows * kv_row + static_cast<size_t>(g) * D;
 
+  const int nb = a.mode == 2 ? a.R : 1;   // bias parameters per distance
+  const float* bsrc = a.mode == 2 ? a.E + static_cast<size_t>(h) * a.e_hs
+                                  : (a.mode == 1 ? a.table + static_cast<size_t>(h) * a.bias_range : nullptr);
   for (int t0 = kbeg; t0 <= kend; t0 += TK) {
     __syncthreads();
-    for (int idx = tid; idx < TK * D; idx += 64 * NW) {
-      const int row = idx / D, d = idx % D;
-      const int key = t0 + row;
-      const bool ok = key <= kend;
-      Kt[row][d] = ok ? kb[static_cast<size_t>(key) * kv_row + d] : 0.f;
-      Vt[row][d] = ok ? vb[static_cast<size_t>(key) * kv_row + d] : 0.f;
-    }
+    // the tile's K and V rows and its bias parameters, each with 8 loads in flight per thread
+    // (rows past kend read row kend and are stored as zero)
+    auto load_kv = [&](const float* base) {
+      return [=](int idx) {
+        const int key = min(t0 + idx / D, kend);
+        return __float_as_uint(base[static_cast<size_t>(key) * kv_row + idx % D]);
+      };
+    };
+    auto store_kv = [&](float (*tile)[D + 1]) {
+      return [=](int idx, uint32_t w) {
+        const int row = idx / D;
+        tile[row][idx % D] = __uint_as_float(w & ((t0 + row <= kend) ? ~0u : 0u));
+      };
+    };
+    stage_batched(tid, 64 * NW, TK * D, load_kv(kb), store_kv(Kt));
+    stage_batched(tid, 64 * NW, TK * D, load_kv(vb), store_kv(Vt));
+    // distances dmin .. dmin + NDS - 1 cover every pair of this tile; entries outside
+    // [0, bias_range) are zero (and never read)
+    const int dmin = pos_lo - (t0 + TK - 1);
+    if (a.mode != 0 && a.bias_range > 0)
+      stage_batched(tid, 64 * NW, nb * NDS,
+          [&](int x) {
+            const int f = x / NDS;
+            const int d = min(max(dmin + x - f * NDS, 0), a.bias_range - 1);
+            return __float_as_uint(bsrc[static_cast<size_t>(f) * a.bias_range + d]);
+          },
+          [&](int x, uint32_t w) {
+            const int d = dmin + x - (x / NDS) * NDS;
+            bs[x] = __uint_as_float(w & ((d >= 0 && d < a.bias_range) ? ~0u : 0u));
+          });
     __syncthreads();
     if (!live) continue;
     const int n = min(TK, kend - t0 + 1);
@@ -95,14 +126,14 @@ __global__ __launch_bounds__(64 * NW) void attn_f32_kernel(F32Args a) {
       for (int d = 0; d < D; ++d) sp[d & 3] = fmaf(qv[d], Kt[jj][d], sp[d & 3]);
       float s = ((sp[0] + sp[1]) + (sp[2] + sp[3])) * a.scale;
       if (a.mode != 0 && delta < a.bias_range) {
+        const float* bd = bs + (delta - (pos_lo - (t0 + TK - 1)));
         if (a.mode == 1) {
-          s += a.table[static_cast<size_t>(h) * a.bias_range + delta];
+          s += bd[0];
         } else {
-          const float* Eh = a.E + static_cast<size_t>(h) * a.e_hs + delta;
           float bsum = 0.f;
 #pragma unroll
-          for (int f = 0; f < 16; ++f)
-            if (f < a.R) bsum = fmaf(rv[f], Eh[static_cast<size_t>(f) * a.bias_range], bsum);
+          for (int f = 0; f < RMAX_F32; ++f)
+            if (f < a.R) bsum = fmaf(rv[f], bd[f * NDS], bsum);
           s += bsum;
         }
       }
