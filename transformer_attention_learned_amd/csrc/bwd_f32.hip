@@ -34,8 +34,11 @@ constexpr int tile_floats() { return T * (D + 1); }
 
 // LDS floats of both main kernels: four row tiles (q, dout, k, v), the P and dZ blocks, the
 // query tile's r coefficients and its per-row lse, rowsum and temperature.
+constexpr int NBD = 2 * T;  // distances a block's pairs span (63), padded
+constexpr int RB_MAX = 16;   // bias parameters per distance (E rows; 1 for the table)
+
 template <int D>
-constexpr int bwd_f32_lds_floats() { return 4 * tile_floats<D>() + 2 * T * (T + 1) + T * RS + 3 * T; }
+constexpr int bwd_f32_lds_floats() { return 4 * tile_floats<D>() + 2 * T * (T + 1) + T * RS + 3 * T + RB_MAX * NBD; }
 
 // One wave per (batch, row, head): rowsum(dout * o) into dsum [B, Hq, S]; the first workgroups
 // also clear dtable / dE, which the query-parallel kernel accumulates into.
@@ -77,6 +80,8 @@ struct Block {
   float* lse_s; // [T]
   float* dsum_s;
   float* tau_s;
+  float* Bs;    // [R][NBD] E rows (MODE 2) or [NBD] table entries (MODE 1) over the block's
+                // distances i0 - j0 - 31 ..
 
   __device__ explicit Block(float* sm) {
     Qs = sm;
@@ -89,15 +94,40 @@ struct Block {
     lse_s = rS + T * RS;
     dsum_s = lse_s + T;
     tau_s = dsum_s + T;
+    Bs = tau_s + T;
   }
 
   // rows r0 .. r0 + 31 of a [B, S, H, D] tensor (head h of batch b) into dst, zero past S
+  // (8 loads in flight per thread: rows past S read row S - 1 and are stored as zero)
   __device__ static void load_rows(float* dst, const float* src, const BwdF32Args& a, int b, int h, int H, int r0) {
-    for (int idx = threadIdx.x; idx < T * D; idx += NTH) {
-      const int rr = idx / D, d = idx - rr * D;
-      const int row = r0 + rr;
-      dst[rr * (D + 1) + d] = row < a.S ? src[((static_cast<size_t>(b) * a.S + row) * H + h) * D + d] : 0.f;
-    }
+    stage_batched(threadIdx.x, NTH, T * D,
+        [&](int idx) {
+          const int rr = idx / D;
+          return __float_as_uint(src[((static_cast<size_t>(b) * a.S + min(r0 + rr, a.S - 1)) * H + h) * D + idx - rr * D]);
+        },
+        [&](int idx, uint32_t w) {
+          const int rr = idx / D;
+          dst[rr * (D + 1) + idx - rr * D] = __uint_as_float(w & ((r0 + rr < a.S) ? ~0u : 0u));
+        });
+  }
+
+  // the bias parameters over the distances of block (i0.., j0..): dmin = i0 - j0 - 31 ..
+  // dmin + 62, table entries (MODE 1) or the R rows of E (MODE 2), with 8 loads in flight per
+  // thread; entries outside [0, bias_range) are zero and never read
+  __device__ void load_bias(const BwdF32Args& a, int h, int i0, int j0) {
+    if (MODE == 0 || a.bias_range <= 0) return;
+    const int dmin = i0 - j0 - (T - 1);
+    const float* src = MODE == 2 ? a.E + static_cast<size_t>(h) * a.e_hs : a.table + static_cast<size_t>(h) * a.bias_range;
+    stage_batched(threadIdx.x, NTH, (MODE == 2 ? a.R : 1) * NBD,
+        [&](int x) {
+          const int f = x / NBD;
+          const int d = min(max(dmin + x - f * NBD, 0), a.bias_range - 1);
+          return __float_as_uint(src[static_cast<size_t>(f) * a.bias_range + d]);
+        },
+        [&](int x, uint32_t w) {
+          const int d = dmin + x - (x / NBD) * NBD;
+          Bs[x] = __uint_as_float(w & ((d >= 0 && d < a.bias_range) ? ~0u : 0u));
+        });
   }
 
   // the query side of a block: q, dout, lse, rowsum, temperature (and r) of rows i0 .. i0 + 31
@@ -135,7 +165,7 @@ struct Block {
     const int i = i0 + ii;
     const float* qr = Qs + ii * (D + 1);
     const float* dr_ = dOs + ii * (D + 1);
-    const float* eh = (MODE == 2) ? a.E + static_cast<size_t>(h) * a.e_hs : nullptr;
+    const float* bd0 = Bs - (i0 - j0 - (T - 1));   // bias parameters at distance 0
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int jj = 4 * (t & 7) + p;
@@ -153,10 +183,10 @@ struct Block {
           dp = fmaf(dr_[d], vr[d], dp);
         }
         float beta = 0.f;
-        if (MODE == 1 && delta < a.bias_range) beta = a.table[static_cast<size_t>(h) * a.bias_range + delta];
+        if (MODE == 1 && delta < a.bias_range) beta = bd0[delta];
         if (MODE == 2 && delta < a.bias_range) {
 #pragma unroll 1
-          for (int f = 0; f < a.R; ++f) beta = fmaf(rS[ii * RS + f], eh[static_cast<size_t>(f) * a.bias_range + delta], beta);
+          for (int f = 0; f < a.R; ++f) beta = fmaf(rS[ii * RS + f], bd0[f * NBD + delta], beta);
         }
         const float tau = tau_s[ii];
         P = expf(tau * fmaf(a.scale, s, beta) - lse_s[ii]);
@@ -191,7 +221,6 @@ __global__ __launch_bounds__(NTH) void bwd_f32_dq(BwdF32Args a) {
 #pragma unroll
   for (int u = 0; u < NU; ++u) acc[u] = 0.f;
   float racc[2] = {0.f, 0.f};   // dr of row ii at features t % 8 and t % 8 + 8
-  const float* eh = (MODE == 2) ? a.E + static_cast<size_t>(h) * a.e_hs : nullptr;
   float* dEh = (MODE == 2) ? a.dE + static_cast<size_t>(h) * a.e_hs : nullptr;
 
   const int row_last = min(a.S, i0 + T) - 1;
@@ -199,6 +228,7 @@ __global__ __launch_bounds__(NTH) void bwd_f32_dq(BwdF32Args a) {
   for (int j0 = kmin / T * T; j0 <= row_last; j0 += T) {
     __syncthreads();   // the previous block's reads are done
     blk.load_keys(a, b, g, j0);
+    blk.load_bias(a, h, i0, j0);
     __syncthreads();
     blk.probs(a, h, i0, j0);
     __syncthreads();
@@ -212,6 +242,7 @@ __global__ __launch_bounds__(NTH) void bwd_f32_dq(BwdF32Args a) {
       acc[u] += sacc;
     }
     if (MODE == 2) {
+      const float* bd0 = blk.Bs - (i0 - j0 - (T - 1));   // E rows at distance 0
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
         const int f = (t & 7) + 8 * w;
@@ -220,7 +251,7 @@ __global__ __launch_bounds__(NTH) void bwd_f32_dq(BwdF32Args a) {
 #pragma unroll 4
           for (int jj = 0; jj < T; ++jj) {
             const int delta = i - (j0 + jj);
-            if (delta >= 0 && delta < a.bias_range) s = fmaf(zr[jj], eh[static_cast<size_t>(f) * a.bias_range + delta], s);
+            if (delta >= 0 && delta < a.bias_range) s = fmaf(zr[jj], bd0[f * NBD + delta], s);
           }
           racc[w] += s;
         }
@@ -300,6 +331,7 @@ __global__ __launch_bounds__(NTH) void bwd_f32_dkdv(BwdF32Args a) {
     for (int i0 = j0; i0 <= row_end; i0 += T) {
       __syncthreads();   // the previous block's reads are done
       blk.load_queries(a, b, h, i0);
+      blk.load_bias(a, h, i0, j0);
       __syncthreads();
       blk.probs(a, h, i0, j0);
       __syncthreads();
