@@ -240,6 +240,10 @@ F32_SWEEP = [
          logit_scale="inv_d"),
     dict(S=300, temp_len=64, window=150, bias_range=100), dict(S=200, e_std=1.0),
     dict(S=120, bias_range=1),
+    # the block's staged distances straddle the end of the range (33) with 16 E rows, and a
+    # table longer than the sequence
+    dict(S=161, R=16, bias_range=33, window=90, e_std=1.0),
+    dict(S=100, mode="table", bias_range=300),
 ]
 
 
